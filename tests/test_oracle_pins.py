@@ -1,0 +1,284 @@
+"""Pins that tie the CPU oracle to the pages and to mathematics.
+
+None of these compares the oracle with itself: each checks it against a
+worked example (tests/golden), a library routine it must agree with, a closed
+form, or an invariant the definition implies.  A dropped term, a wrong sign, a
+swapped nibble or a transposed operand fails at least one of them.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth_inputs as si
+
+BF16, FP16 = oracle.BF16, oracle.FP16
+
+
+def bf16_bits(x):
+    return torch.tensor(np.asarray(x, dtype=np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def f16_bits(x):
+    return np.asarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def load(golden_dir, name):
+    with open(os.path.join(golden_dir, name)) as f:
+        return json.load(f)
+
+
+# -- 16-bit float conversions vs library routines ------------------------------
+
+def test_bf16_widen_all_patterns_match_torch():
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = oracle.bf16_to_f32(allbits)
+    ref = torch.from_numpy(allbits.view(np.int16).copy()).view(torch.bfloat16).float().numpy()
+    same = (ours.view(np.uint32) == ref.view(np.uint32)) | (np.isnan(ours) & np.isnan(ref))
+    assert same.all()
+
+
+def test_f16_widen_all_patterns_match_numpy():
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = oracle.f16_to_f32(allbits)
+    ref = allbits.view(np.float16).astype(np.float32)
+    same = (ours.view(np.uint32) == ref.view(np.uint32)) | (np.isnan(ours) & np.isnan(ref))
+    assert same.all()
+
+
+def _rounding_cases(rng):
+    x = rng.standard_normal(20000).astype(np.float32) * np.float32(3.0)
+    # exact ties for bf16: low 16 bits == 0x8000 with both parities of the kept lsb
+    ties = (rng.integers(0x3F000000, 0x47000000, 4000, dtype=np.uint32) & ~np.uint32(0xFFFF)) | np.uint32(0x8000)
+    # fp16 ties: values k + 0.5 ulp in several binades, incl. subnormal range
+    f16 = np.arange(1, 65504, 97, dtype=np.float32)
+    halfway = np.concatenate([f16 + 0.5, (f16 + 0.5) * np.float32(2.0 ** -14), (f16 + 0.5) * np.float32(2.0 ** -24)])
+    big = np.array([65504, 65519, 65520, 65536, 1e9, -65520, 6e-8, 2.9e-8, 3.0e-8, 0.0, -0.0], dtype=np.float32)
+    return np.concatenate([x, ties.view(np.float32), halfway.astype(np.float32), big, -x[:1000]])
+
+
+def test_f32_to_bf16_matches_torch_rne():
+    x = _rounding_cases(np.random.default_rng(1))
+    ours = oracle.f32_to_bf16(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert (ours == ref).all()
+
+
+def test_f32_to_f16_matches_numpy_rne():
+    x = _rounding_cases(np.random.default_rng(2))
+    ours = oracle.f32_to_f16(x)
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    assert (ours == ref).all()
+
+
+# -- nibble packing (worked bytes from the stated byte formula) ---------------
+
+def test_pack_worked_bytes():
+    assert oracle.pack4([[1, 2]]).tolist() == [[0x21]]          # low nibble = even k
+    assert oracle.unpack4(np.array([[0xA5]], np.uint8)).tolist() == [[5, 10]]
+
+
+def test_pack_unpack_all_bytes_round_trip():
+    b = np.arange(256, dtype=np.uint8).reshape(2, 128)
+    assert (oracle.pack4(oracle.unpack4(b)) == b).all()
+    q = np.random.default_rng(3).integers(0, 16, (7, 64))
+    assert (oracle.unpack4(oracle.pack4(q)) == q).all()
+
+
+# -- dequantization -------------------------------------------------------------
+
+def test_e1_dequant_and_gemm(golden_dir):
+    e = load(golden_dir, "e1_w4_groupwise.json")
+    packed = oracle.pack4(e["codes"])
+    assert packed.tolist() == e["packed"]
+    s, z = bf16_bits(e["scale"]), bf16_bits(e["zero"])
+    W = oracle.dequant4(packed, s, z, e["group"], BF16)
+    assert W.tolist() == e["W"]
+    A = bf16_bits(e["A"])
+    assert oracle.gemm_w4(A, packed, s, z, e["group"], BF16).tolist() == e["C"]
+    b = f16_bits(e["bias"])
+    C = oracle.gemm_w4(A, packed, s, z, e["group"], BF16, bias=b, bias_dtype=FP16)
+    assert C.tolist() == e["C_bias"]
+    # the same numbers through fp16 activations/scales
+    W16 = oracle.dequant4(packed, f16_bits(e["scale"]), f16_bits(e["zero"]), e["group"], FP16)
+    assert W16.tolist() == e["W"]
+
+
+def test_e2_w8_dequant_and_gemm(golden_dir):
+    e = load(golden_dir, "e2_w8_perchannel.json")
+    codes = np.array(e["codes"], dtype=np.int8)
+    assert codes.view(np.uint8).tolist() == e["bytes"]
+    s = f16_bits(e["scale"])
+    assert oracle.dequant8(codes, s, -1, FP16).tolist() == e["W"]
+    assert oracle.dequant8(codes, s, codes.shape[1], FP16).tolist() == e["W"]  # group = K
+    C = oracle.gemm_w8(f16_bits(e["A"]), codes, s, -1, FP16)
+    assert C.tolist() == e["C"]
+
+
+def test_dequant_identity_grid():
+    # scale 1, zero 8 turns the rule into w = q exactly
+    q = np.random.default_rng(4).integers(0, 16, (8, 128))
+    W = oracle.dequant4(oracle.pack4(q), bf16_bits(np.ones((8, 2))), bf16_bits(np.full((8, 2), 8.0)), 64)
+    assert (W == q).all()
+
+
+@pytest.mark.parametrize("j", [0, 3, 7])
+def test_quantizer_extremes_identity(j):
+    # scale = (max - min) / 15 and zero = min + 8 * scale put q = 0 on the
+    # group minimum and q = 15 on the group maximum.  Dyadic min/max keep
+    # every quantity exact in bf16.
+    wmin = -1.0 + 0.25 * j
+    scale = 2.0 ** -j
+    wmax = wmin + 15 * scale
+    zero = wmin + 8 * scale
+    q = np.array([[0, 15] * 32])
+    W = oracle.dequant4(oracle.pack4(q), bf16_bits([[scale]]), bf16_bits([[zero]]), 64)
+    assert W[0, 0] == wmin and W[0, 1] == wmax
+
+
+def test_group_indexing_closed_form():
+    # constant code c and A = 1: C[n] = sum_g group * ((c - 8) * s[n, g] + z[n, g])
+    rng = np.random.default_rng(5)
+    n, k, g, c = 5, 512, 64, 11
+    s = (rng.integers(1, 64, (n, k // g)) / 64.0).astype(np.float32)
+    z = (rng.integers(-32, 33, (n, k // g)) / 64.0).astype(np.float32)
+    packed = oracle.pack4(np.full((n, k), c))
+    C = oracle.gemm_w4(bf16_bits(np.ones((1, k))), packed, bf16_bits(s), bf16_bits(z), g)
+    expect = (g * ((c - 8) * s.astype(np.float64) + z)).sum(axis=1)
+    assert np.array_equal(C[0], expect)
+
+
+def test_dequant_rounds_once_in_fp32():
+    # (q - 8) * s is exact in fp32; only the add of the zero rounds, to nearest even.
+    rng = np.random.default_rng(6)
+    n, k, g = 64, 256, 64
+    p = si.w4_problem(1, n, k, g)
+    W = oracle.dequant4(p.packed, p.scale, p.zero, g)
+    q = oracle.unpack4(p.packed).astype(np.float64)
+    s = np.repeat(torch.from_numpy(p.scale.view(np.int16).copy()).view(torch.bfloat16).double().numpy(), g, axis=1)
+    z = np.repeat(torch.from_numpy(p.zero.view(np.int16).copy()).view(torch.bfloat16).double().numpy(), g, axis=1)
+    exact = (q - 8.0) * s + z                  # exact in double
+    assert np.array_equal(W, exact.astype(np.float32))   # numpy's cast is RNE
+    del rng
+
+
+# -- GEMM brute force against a library matmul -----------------------------------
+
+@pytest.mark.parametrize("m,n,k,g", [(1, 16, 64, 64), (3, 40, 128, 64), (7, 64, 256, 128), (5, 33, 192, 64)])
+@pytest.mark.parametrize("dtype", [BF16, FP16])
+def test_w4_gemm_vs_numpy_matmul(m, n, k, g, dtype):
+    p = si.w4_problem(m, n, k, g, tag="pin", dtype=dtype, bias_dtype=FP16)
+    W = oracle.dequant4(p.packed, p.scale, p.zero, g, dtype).astype(np.float64)
+    conv = oracle.bf16_to_f32 if dtype == BF16 else oracle.f16_to_f32
+    A = conv(p.A).astype(np.float64)
+    bias = oracle.f16_to_f32(p.bias).astype(np.float64)
+    ref = A @ W.T + bias
+    C = oracle.gemm_w4(p.A, p.packed, p.scale, p.zero, g, dtype, p.bias, FP16)
+    np.testing.assert_allclose(C, ref, rtol=1e-12, atol=1e-12)
+    rows = np.array([0, m - 1, m // 2]); cols = np.array([n - 1, 0, n // 3])
+    at = oracle.gemm_w4_at(p.A, p.packed, p.scale, p.zero, g, rows, cols, dtype, p.bias, FP16)
+    np.testing.assert_allclose(at, ref[rows, cols], rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 16, 64), (4, 24, 96), (9, 8, 256)])
+def test_w8_gemm_vs_numpy_matmul(m, n, k):
+    p = si.w8_problem(m, n, k, -1, tag="pin", bias_dtype=FP16)
+    W = oracle.dequant8(p.codes, p.scale, -1, FP16).astype(np.float64)
+    A = oracle.f16_to_f32(p.A).astype(np.float64)
+    ref = A @ W.T + oracle.f16_to_f32(p.bias)
+    C = oracle.gemm_w8(p.A, p.codes, p.scale, -1, FP16, p.bias, FP16)
+    np.testing.assert_allclose(C, ref, rtol=1e-12, atol=1e-12)
+    # signed codes: the weight is the code times the scale, sign included
+    s = oracle.f16_to_f32(p.scale).astype(np.float64)
+    assert np.array_equal(W, p.codes.astype(np.float64) * s[:, None])
+
+
+def test_w4_exact_inputs_are_exact():
+    p = si.w4_exact_problem(3, 32, 256, 64, seed=7, bias_dtype=FP16)
+    C = oracle.gemm_w4(p.A, p.packed, p.scale, p.zero, 64, BF16, p.bias, FP16)
+    assert np.array_equal(C * 4, np.round(C * 4))     # multiples of 1/4
+    assert np.abs(C).max() < 2 ** 17
+
+
+# -- MoE ---------------------------------------------------------------------
+
+def test_route_one_hot_and_ties():
+    lg = np.zeros((3, 8), np.float32)
+    lg[0, 5] = 4.0; lg[0, 2] = 3.0
+    lg[1, :] = 1.0                                   # all tied: lowest ids first
+    lg[2, 7] = 2.0; lg[2, 1] = 2.0; lg[2, 0] = -1.0
+    ids, w = oracle.moe_route(lg, 2)
+    assert ids.tolist() == [[5, 2], [0, 1], [1, 7]]
+    np.testing.assert_allclose(w[0], [np.exp(1) / (np.exp(1) + 1), 1 / (np.exp(1) + 1)], rtol=1e-15)
+    np.testing.assert_allclose(w[1], [0.5, 0.5], rtol=0)
+    np.testing.assert_allclose(w[2], [0.5, 0.5], rtol=0)
+
+
+def test_route_weights_are_renormalised_softmax():
+    lg = np.random.default_rng(8).standard_normal((50, 16)).astype(np.float32)
+    ids, w = oracle.moe_route(lg, 4)
+    np.testing.assert_allclose(w.sum(1), 1.0, rtol=1e-14)
+    sm = torch.softmax(torch.from_numpy(lg).double(), dim=1).numpy()
+    top = np.take_along_axis(sm, ids.astype(np.int64), 1)
+    np.testing.assert_allclose(w, top / top.sum(1, keepdims=True), rtol=1e-12)
+    assert (np.diff(np.take_along_axis(lg, ids.astype(np.int64), 1), axis=1) <= 0).all()
+    ids1, w1 = oracle.moe_route(lg, 1)
+    assert (w1 == 1.0).all() and (ids1[:, 0] == lg.argmax(1)).all()
+
+
+def _dense_swiglu(xf, W1, W2, inter):
+    h = xf @ W1.T
+    gate, up = h[:, :inter], h[:, inter:]
+    a = gate / (1.0 + np.exp(-gate)) * up
+    return a @ W2.T
+
+
+def _conv(bits, dtype):
+    return (oracle.bf16_to_f32(bits) if dtype == BF16 else oracle.f16_to_f32(bits)).astype(np.float64)
+
+
+def test_moe_identical_experts_equal_dense_ffn():
+    p = si.moe_problem(6, 64, 64, 4, 2, group=64, tag="pin-moe")
+    for arr in (p.w1, p.s1, p.z1, p.w2, p.s2, p.z2):
+        arr[1:] = arr[0]
+    out, _, _ = oracle.moe(p.x, p.logits, p.w1, p.s1, p.z1, p.w2, p.s2, p.z2, 2, 64)
+    W1 = oracle.dequant4(p.w1[0], p.s1[0], p.z1[0], 64).astype(np.float64)
+    W2 = oracle.dequant4(p.w2[0], p.s2[0], p.z2[0], 64).astype(np.float64)
+    ref = _dense_swiglu(_conv(p.x, BF16), W1, W2, 64)
+    np.testing.assert_allclose(out, ref, rtol=1e-10, atol=1e-10)
+
+
+def test_moe_brute_force_tiny():
+    p = si.moe_problem(4, 64, 64, 4, 2, group=64, tag="pin-moe2")
+    out, ids, w = oracle.moe(p.x, p.logits, p.w1, p.s1, p.z1, p.w2, p.s2, p.z2, 2, 64)
+    xf = _conv(p.x, BF16)
+    ref = np.zeros_like(out)
+    for e in range(4):
+        W1 = oracle.dequant4(p.w1[e], p.s1[e], p.z1[e], 64).astype(np.float64)
+        W2 = oracle.dequant4(p.w2[e], p.s2[e], p.z2[e], 64).astype(np.float64)
+        ye = _dense_swiglu(xf, W1, W2, 64)
+        for t in range(4):
+            for j in range(2):
+                if ids[t, j] == e:
+                    ref[t] += w[t, j] * ye[t]
+    np.testing.assert_allclose(out, ref, rtol=1e-10, atol=1e-10)
+
+
+def test_moe_expert_permutation_invariance():
+    p = si.moe_problem(5, 64, 64, 4, 2, group=64, tag="pin-moe3")
+    out, _, _ = oracle.moe(p.x, p.logits, p.w1, p.s1, p.z1, p.w2, p.s2, p.z2, 2, 64)
+    perm = np.array([2, 0, 3, 1])
+    out2, _, _ = oracle.moe(p.x, p.logits[:, perm], p.w1[perm], p.s1[perm], p.z1[perm],
+                            p.w2[perm], p.s2[perm], p.z2[perm], 2, 64)
+    np.testing.assert_allclose(out, out2, rtol=1e-13, atol=1e-13)
+
+
+def test_moe_token_subset_matches_full():
+    p = si.moe_problem(6, 64, 128, 4, 3, group=64, tag="pin-moe4")
+    full, _, _ = oracle.moe(p.x, p.logits, p.w1, p.s1, p.z1, p.w2, p.s2, p.z2, 3, 64)
+    part, _, _ = oracle.moe(p.x, p.logits, p.w1, p.s1, p.z1, p.w2, p.s2, p.z2, 3, 64, tokens=[4, 1])
+    np.testing.assert_array_equal(part, full[[4, 1]])
