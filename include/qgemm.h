@@ -1,0 +1,184 @@
+/*
+ * qgemm.h -- C ABI of the MI355X (gfx950) weight-only quantized GEMM library.
+ *
+ * The operation (fpA_intB): C[m, n] = sum_k A[m, k] * W[n, k] (+ bias[n]),
+ * where A is a bf16/fp16 activation matrix and W is dequantized on the fly
+ * from integer codes:
+ *
+ *   int4, groupwise:  W[n, k] = (q[n, k] - 8) * scale[n, k/g] + zero[n, k/g]
+ *   int8, per channel: W[n, k] = q[n, k] * scale[n]
+ *
+ * Sources: "acext User Guide (v1.7)", 1.2.1 fpAintB GEMM (argument set: A,
+ * B, scales, zero points, biases, C, m, n, k, group size, workspace, stream),
+ * 1.3.1 Int8 Weight-only (one scale per output channel), 1.3.3 Int4
+ * Groupwise (groups of 64 or 128, zero points for asymmetric grids), 1.2.3
+ * MoE GEMM (runMoe); vllm-omni cpu_int4.py, module docstring (the portable
+ * int4 checkpoint format and the dequant rule); "[Misc][Kernel]: Add
+ * GPTQAllSpark Quantization", PR description (A16W8, group size -1).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every buffer is owned by the caller.  Pointers marked "device" must be
+ *    device memory on the current HIP device; the library allocates nothing
+ *    and keeps no per-call state.
+ *  - All matrices are dense row-major, contiguous, with no leading-dimension
+ *    arguments.  Matrix pointers (A, codes, C, W, x, out) must be 16-byte
+ *    aligned, vectors (scales, zeros, bias) 2-byte, fp32/int32 arrays
+ *    4-byte, and a workspace 256-byte aligned.
+ *  - 16-bit floats are passed as their raw storage (bf16 / IEEE binary16).
+ *    scales and zeros always have the activation dtype; bias has its own.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    asynchronously; a QG_OK return means the launch was accepted.
+ *  - Arguments are validated on the host before any HIP call.  On any error
+ *    nothing is enqueued and the outputs are untouched.  m == 0 or n == 0 (or
+ *    tokens == 0) is a successful no-op that reads no pointer; k must be
+ *    positive (repack and dequant also accept k == 0).  The first failed
+ *    check decides the status, in the order: sizes, NULL pointers, dtypes,
+ *    group size, tile multiples, alignment, workspace.
+ *  - Functions are reentrant; calls on different streams may overlap unless
+ *    they share a workspace.
+ */
+#ifndef QGEMM_H
+#define QGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QG_OK = 0,
+    QG_ERR_NULL = 1,        /* a required pointer is NULL */
+    QG_ERR_SHAPE = 2,       /* negative size, or sizes that do not fit together */
+    QG_ERR_GROUP = 3,       /* group size not supported, or k % group != 0 */
+    QG_ERR_DTYPE = 4,       /* dtype code not allowed for this argument */
+    QG_ERR_ALIGN = 5,       /* a device pointer is not 16-byte aligned */
+    QG_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required */
+    QG_ERR_UNSUPPORTED = 7, /* valid, but outside the tile multiples listed per call */
+    QG_ERR_HIP = 8          /* the HIP runtime rejected a launch */
+} qg_status;
+
+typedef enum { QG_NONE = 0, QG_BF16 = 1, QG_FP16 = 2, QG_FP32 = 3 } qg_dtype;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *qg_strerror(qg_status status);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int qg_version(void);
+
+/* ------------------------------------------------------------------------
+ * Load-side repack (once per weight).  The portable layouts are
+ *   int4: uint8 [n, k/2], byte j of row n = q[n, 2j] | q[n, 2j+1] << 4
+ *         (vllm-omni cpu_int4.py, module docstring);
+ *   int8: int8 [n, k] row-major, signed two's complement.
+ * The tiled layouts have the same byte count and are pure permutations
+ * (int8 also flips the top bit), so the inverse recovers the input exactly.
+ * Repacking once at load removes every per-call shuffle (the same reason
+ * cpu_int4.py's to_split_halves de-interleaves nibbles once at load).
+ *
+ * int4 tiled layout (requires n % 16 == 0, k % 128 == 0): 1024-byte blocks,
+ * one per (16 output channels) x (128 k).  For code q[n, k]:
+ *     nt = n / 16, nl = n % 16, kb = k / 128, r = k % 128
+ *     t = r / 32, j = (r / 8) % 4, e = k % 8
+ *     lane = 16*j + nl
+ *     pos  = (e even) ? e/2 : 4 + e/2           (nibble slot in a 32-bit word)
+ *     byte = (nt*(k_total/128) + kb)*1024 + lane*16 + t*4 + pos/2
+ *     nibble = pos % 2 (0 = low)
+ * i.e. the 32-bit word (block, lane, t) holds the eight codes k = 128*kb +
+ * 32*t + 8*j + 0..7 of channel n, even k in the low half-word.
+ *
+ * int8 tiled layout (requires n % 16 == 0, k % 64 == 0): 1024-byte blocks,
+ * one per (16 channels) x (64 k).  For q[n, k]:
+ *     nt = n / 16, nl = n % 16, kb = k / 64, r = k % 64
+ *     t = r / 32, j = (r / 8) % 4, e = k % 8,  lane = 16*j + nl
+ *     byte = (nt*(k_total/64) + kb)*1024 + lane*16 + t*8 + e
+ *     stored value = (uint8)q ^ 0x80            (offset binary, q + 128)
+ *
+ * src and dst are device pointers and must not overlap.
+ * ---------------------------------------------------------------------- */
+qg_status qrepack_w4(const uint8_t *src_nk2, uint8_t *dst_tiled, int n, int k, void *stream);
+qg_status qunrepack_w4(const uint8_t *src_tiled, uint8_t *dst_nk2, int n, int k, void *stream);
+qg_status qrepack_w8(const int8_t *src_nk, int8_t *dst_tiled, int n, int k, void *stream);
+qg_status qunrepack_w8(const int8_t *src_tiled, int8_t *dst_nk, int n, int k, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Dequantization hook (testing and fallback use): tiled codes -> W [n, k]
+ * row-major in out_dtype (QG_FP32, or the activation dtype).  The fp32
+ * value is (q - 8) * s + z (int4; the product is exact, the add rounds to
+ * nearest even) or q * s (int8, exact); the 16-bit output is that fp32 value
+ * rounded to nearest even.  Bit-exact by contract.
+ *   group_size: int4 64 or 128; int8 -1 (per channel).
+ *   scales/zeros: [n, k/group] (int4) or [n] (int8), act_dtype.
+ * ---------------------------------------------------------------------- */
+qg_status qdequant_w4(const uint8_t *B_tiled, const void *scales, const void *zeros, void *W_out,
+                      int n, int k, int group_size, qg_dtype act_dtype, qg_dtype out_dtype,
+                      void *stream);
+qg_status qdequant_w8(const int8_t *B_tiled, const void *scales, void *W_out, int n, int k,
+                      int group_size, qg_dtype act_dtype, qg_dtype out_dtype, void *stream);
+
+/* ------------------------------------------------------------------------
+ * GEMM.  (acext User Guide (v1.7), 1.2.1 fpAintB GEMM; 1.3.1; 1.3.3)
+ *   A       device [m, k], act_dtype (QG_BF16 or QG_FP16)
+ *   B_tiled device, the tiled layout above (qrepack_w4 / qrepack_w8 output)
+ *   scales  device [n, k/group] (w4) or [n] (w8, group -1), act_dtype
+ *   zeros   device [n, k/group], act_dtype (w4 only; required)
+ *   bias    device [n] in bias_dtype, or NULL with bias_dtype QG_NONE
+ *   C       device [m, n], act_dtype; written, never read
+ *   group_size: w4 64 or 128; w8 -1 (k is accepted as a synonym of -1)
+ *   Tile multiples: n % 16 == 0; k % 128 == 0 (w4) or k % 64 == 0 (w8);
+ *   m is any value >= 0.  Accumulation is fp32; C = RNE(acc + bias).
+ *   workspace: device scratch of at least qgemm_workspace_size() bytes
+ *   (may be NULL when that size is 0).  The current kernels need none.
+ * ---------------------------------------------------------------------- */
+size_t qgemm_workspace_size(int m, int n, int k, int group_size, int weight_bits);
+
+qg_status qgemm_w4a16(const void *A, const uint8_t *B_tiled, const void *scales,
+                      const void *zeros, const void *bias, void *C, int m, int n, int k,
+                      int group_size, qg_dtype act_dtype, qg_dtype bias_dtype, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
+qg_status qgemm_w8a16(const void *A, const int8_t *B_tiled, const void *scales, const void *bias,
+                      void *C, int m, int n, int k, int group_size, qg_dtype act_dtype,
+                      qg_dtype bias_dtype, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
+/* ------------------------------------------------------------------------
+ * Top-k MoE with SiLU-gated int4 experts  (acext User Guide (v1.7), 1.2.3
+ * MoE GEMM: fp32 gating logits, fc1 with a gated activation, fc2, expert
+ * scales, routing maps, final output).
+ *   x        device [tokens, hidden], act_dtype (QG_BF16 or QG_FP16)
+ *   logits   device fp32 [tokens, experts]
+ *   w1_tiled device, experts consecutive tiled int4 matrices [2*inter, hidden]:
+ *            rows [0, inter) are the gate projection, [inter, 2*inter) up
+ *   s1, z1   device [experts, 2*inter, hidden/group], act_dtype
+ *   w2_tiled device, experts consecutive tiled int4 matrices [hidden, inter]
+ *   s2, z2   device [experts, hidden, inter/group], act_dtype
+ *   out      device [tokens, hidden], act_dtype
+ *   topk_ids_out  optional device int32 [tokens, topk] (NULL to skip)
+ *   topk_w_out    optional device fp32 [tokens, topk] (NULL to skip)
+ * Routing: the topk largest logits per row, in descending order, ties to
+ * the lower expert id; weights = softmax over the selected logits only.
+ * out[t] = sum_j w[t, j] * fc2_e(silu(gate) * up), e = ids[t, j],
+ * silu(x) = x / (1 + exp(-x)); the activation is rounded to act_dtype before
+ * fc2, the combine sums in fp32 in rank order.
+ * Requires hidden % 128 == 0, inter % 128 == 0, 1 <= topk <= experts <= 256,
+ * topk <= 64, group_size 64 or 128.  workspace: at least
+ * qmoe_workspace_size() bytes, 256-byte aligned; it holds the routing maps,
+ * the tile list and the fc1/fc2 intermediates, and is overwritten.
+ * ---------------------------------------------------------------------- */
+size_t qmoe_workspace_size(int tokens, int hidden, int inter, int experts, int topk);
+
+qg_status qmoe_grouped(const void *x, const float *logits, const uint8_t *w1_tiled,
+                       const void *s1, const void *z1, const uint8_t *w2_tiled, const void *s2,
+                       const void *z2, void *out, int tokens, int hidden, int inter, int experts,
+                       int topk, int group_size, qg_dtype act_dtype, int32_t *topk_ids_out,
+                       float *topk_w_out, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMM_H */

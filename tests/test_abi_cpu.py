@@ -1,0 +1,156 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/qgemm.h declares, and rejects invalid arguments on the host before
+any HIP call (these calls never reach a kernel launch)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import weight_only_quantized_w8a16_amd as qg
+from weight_only_quantized_w8a16_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qgemm.h")
+
+OK, NULL, SHAPE, GROUP, DTYPE, ALIGN, WORKSPACE, UNSUP = 0, 1, 2, 3, 4, 5, 6, 7
+FAKE = 0x100000          # 16-byte-aligned stand-in address; never dereferenced
+BF16, FP16, FP32 = 1, 2, 3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(q\w+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert sorted(_abi.SIGNATURES) == declared_functions()
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_abi.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_strerror():
+    L = qg.lib()
+    assert L.qg_version() >= 10000
+    for s in range(9):
+        assert L.qg_strerror(s)
+    assert L.qg_strerror(99) == b"unknown status"
+
+
+def w4(**kw):
+    a = dict(A=FAKE, B=FAKE, s=FAKE, z=FAKE, bias=None, C=FAKE, m=4, n=128, k=256, g=64, act=BF16,
+             bdt=0, ws=None, wsb=0)
+    a.update(kw)
+    return qg.lib().qgemm_w4a16(a["A"], a["B"], a["s"], a["z"], a["bias"], a["C"], a["m"], a["n"],
+                                a["k"], a["g"], a["act"], a["bdt"], a["ws"], a["wsb"], None)
+
+
+def w8(**kw):
+    a = dict(A=FAKE, B=FAKE, s=FAKE, bias=None, C=FAKE, m=4, n=128, k=256, g=-1, act=FP16, bdt=0)
+    a.update(kw)
+    return qg.lib().qgemm_w8a16(a["A"], a["B"], a["s"], a["bias"], a["C"], a["m"], a["n"], a["k"],
+                                a["g"], a["act"], a["bdt"], None, 0, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(m=-1), SHAPE), (dict(n=-16), SHAPE), (dict(k=0), SHAPE),
+    (dict(A=None), NULL), (dict(B=None), NULL), (dict(s=None), NULL), (dict(z=None), NULL),
+    (dict(C=None), NULL), (dict(bdt=FP16), NULL),
+    (dict(act=0), DTYPE), (dict(act=FP32), DTYPE), (dict(act=7), DTYPE),
+    (dict(bias=FAKE, bdt=0), DTYPE), (dict(bias=FAKE, bdt=FP32), DTYPE),
+    (dict(g=32), GROUP), (dict(g=-1), GROUP), (dict(g=256), GROUP), (dict(k=192, g=128), GROUP),
+    (dict(n=24), UNSUP), (dict(k=192), UNSUP),
+    (dict(A=FAKE + 8), ALIGN), (dict(B=FAKE + 4), ALIGN), (dict(C=FAKE + 2), ALIGN),
+    (dict(s=FAKE + 1), ALIGN), (dict(z=FAKE + 1), ALIGN), (dict(bias=FAKE + 1, bdt=FP16), ALIGN),
+    (dict(m=0), OK), (dict(n=0), OK),
+])
+def test_w4_validation(kw, status):
+    assert w4(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(m=-2), SHAPE), (dict(k=-64), SHAPE),
+    (dict(A=None), NULL), (dict(s=None), NULL), (dict(bdt=BF16), NULL),
+    (dict(act=FP32), DTYPE), (dict(bias=FAKE, bdt=0), DTYPE),
+    (dict(g=64), GROUP), (dict(g=128), GROUP),
+    (dict(n=8), UNSUP), (dict(k=96, g=96), UNSUP),
+    (dict(A=FAKE + 4), ALIGN), (dict(s=FAKE + 1), ALIGN),
+    (dict(m=0), OK), (dict(g=256, m=0), OK),
+])
+def test_w8_validation(kw, status):
+    assert w8(**kw) == status
+
+
+def test_repack_and_dequant_validation():
+    L = qg.lib()
+    assert L.qrepack_w4(FAKE, FAKE, -16, 128, None) == SHAPE
+    assert L.qrepack_w4(None, FAKE, 16, 128, None) == NULL
+    assert L.qrepack_w4(FAKE, FAKE, 24, 128, None) == UNSUP
+    assert L.qrepack_w4(FAKE, FAKE, 16, 64, None) == UNSUP
+    assert L.qrepack_w4(FAKE + 4, FAKE, 16, 128, None) == ALIGN
+    assert L.qrepack_w4(FAKE, FAKE, 0, 128, None) == OK
+    assert L.qunrepack_w4(FAKE, None, 16, 128, None) == NULL
+    assert L.qrepack_w8(FAKE, FAKE, 16, 96, None) == UNSUP
+    assert L.qunrepack_w8(FAKE, FAKE, 16, 0, None) == OK
+    assert L.qdequant_w4(FAKE, FAKE, FAKE, FAKE, 16, 128, 32, BF16, FP32, None) == GROUP
+    assert L.qdequant_w4(FAKE, FAKE, FAKE, FAKE, 16, 128, 64, BF16, FP16, None) == DTYPE
+    assert L.qdequant_w4(FAKE, FAKE, None, FAKE, 16, 128, 64, BF16, FP32, None) == NULL
+    assert L.qdequant_w8(FAKE, FAKE, FAKE, 16, 128, 64, FP16, FP32, None) == GROUP
+    assert L.qdequant_w8(FAKE, FAKE, FAKE, 16, 128, -1, FP16, BF16, None) == DTYPE
+
+
+def moe(**kw):
+    a = dict(x=FAKE, lg=FAKE, w1=FAKE, s1=FAKE, z1=FAKE, w2=FAKE, s2=FAKE, z2=FAKE, out=FAKE, T=8,
+             H=256, I=128, E=8, k=2, g=64, act=BF16, ids=None, w=None, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return qg.lib().qmoe_grouped(a["x"], a["lg"], a["w1"], a["s1"], a["z1"], a["w2"], a["s2"],
+                                 a["z2"], a["out"], a["T"], a["H"], a["I"], a["E"], a["k"], a["g"],
+                                 a["act"], a["ids"], a["w"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), SHAPE), (dict(k=0), SHAPE), (dict(k=9), SHAPE), (dict(E=0), SHAPE),
+    (dict(x=None), NULL), (dict(lg=None), NULL), (dict(z2=None), NULL),
+    (dict(act=FP32), DTYPE), (dict(g=32), GROUP), (dict(I=96, g=64), GROUP),
+    (dict(H=192), UNSUP), (dict(E=300, k=2), UNSUP), (dict(E=128, k=65), UNSUP),
+    (dict(x=FAKE + 8), ALIGN), (dict(lg=FAKE + 2), ALIGN), (dict(ids=FAKE + 2), ALIGN),
+    (dict(ws=None), WORKSPACE), (dict(wsb=1024), WORKSPACE), (dict(ws=FAKE + 16), ALIGN),
+    (dict(T=0), OK),
+])
+def test_moe_validation(kw, status):
+    assert moe(**kw) == status
+
+
+def test_workspace_sizes():
+    L = qg.lib()
+    assert L.qgemm_workspace_size(1, 2048, 2048, 64, 4) == 0
+    small = L.qmoe_workspace_size(16, 256, 128, 8, 2)
+    big = L.qmoe_workspace_size(2048, 2048, 1408, 64, 6)
+    # the fc1 activation and fc2 output intermediates dominate: R*(I + H)*2 bytes
+    assert big >= 2048 * 6 * (1408 + 2048) * 2
+    assert 0 < small < big
+    assert L.qmoe_workspace_size(0, 256, 128, 8, 2) == 0
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(_abi, "LIB_PATH", str(tmp_path / "absent.so"))
+    monkeypatch.setattr(_abi, "_lib", None)
+    with pytest.raises(qg.QGemmError):
+        _abi.lib()
+
+
+def test_layout_helpers_are_permutations():
+    from helpers import tiled_w4_expected, tiled_w8_expected
+    p = np.random.default_rng(0).integers(0, 256, (32, 128), dtype=np.uint8)
+    t = tiled_w4_expected(p)
+    assert sorted(np.unpackbits(p).tolist()) == sorted(np.unpackbits(t).tolist())
+    assert not np.array_equal(t, p)
+    c = np.random.default_rng(1).integers(-128, 128, (16, 128)).astype(np.int8)
+    t8 = tiled_w8_expected(c)
+    assert sorted((t8.view(np.uint8) ^ 0x80).ravel().tolist()) == sorted(c.view(np.uint8).ravel().tolist())

@@ -1,0 +1,162 @@
+"""GPU parity, part 1: repack, the dequant hook, integer-exact GEMMs on every
+path, and the tiny W4A16 problem against the oracle.
+
+Every comparison runs the library through its C ABI (the binding passes raw
+pointers) and compares with the CPU oracle on identical seeded bytes."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth_inputs as si
+import weight_only_quantized_w8a16_amd as qg
+from helpers import (BF16, FP16, TOL, rel_err, tiled_w4_expected, tiled_w8_expected, to_bits,
+                     to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _no_forced_path(monkeypatch):
+    monkeypatch.delenv("QGEMM_FORCE_PATH", raising=False)
+
+
+# -- repack -------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,k", [(16, 128), (48, 384), (128, 256), (2048, 2048)])
+def test_repack_w4_matches_documented_layout_and_inverts(n, k):
+    packed = np.random.default_rng(n + k).integers(0, 256, (n, k // 2), dtype=np.uint8)
+    d = to_dev(packed)
+    tiled = qg.repack_w4(d)
+    assert np.array_equal(tiled.cpu().numpy(), tiled_w4_expected(packed))
+    back = qg.unrepack_w4(tiled)
+    assert np.array_equal(back.cpu().numpy(), packed)
+
+
+@pytest.mark.parametrize("n,k", [(16, 64), (32, 192), (3584, 3584)])
+def test_repack_w8_matches_documented_layout_and_inverts(n, k):
+    codes = np.random.default_rng(n * k).integers(-128, 128, (n, k)).astype(np.int8)
+    tiled = qg.repack_w8(to_dev(codes))
+    assert np.array_equal(tiled.cpu().numpy(), tiled_w8_expected(codes))
+    assert np.array_equal(qg.unrepack_w8(tiled).cpu().numpy(), codes)
+
+
+# -- dequant hook (bit-exact) ---------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [BF16, FP16])
+@pytest.mark.parametrize("group", [64, 128])
+def test_dequant_w4_bit_exact(dtype, group):
+    n, k = 96, 512
+    packed, s, z, _ = si.w4_weights(n, k, group, seed=11 + group, dtype=dtype)
+    ref = oracle.dequant4(packed, s, z, group, dtype)
+    tiled = qg.repack_w4(to_dev(packed))
+    S, Z = to_dev(s, dtype), to_dev(z, dtype)
+    W32 = qg.dequant_w4(tiled, S, Z, group, torch.float32).cpu().numpy()
+    assert np.array_equal(W32.view(np.uint32), ref.view(np.uint32))
+    W16 = qg.dequant_w4(tiled, S, Z, group, S.dtype)
+    conv = oracle.f32_to_bf16 if dtype == BF16 else oracle.f32_to_f16
+    assert np.array_equal(to_bits(W16), conv(ref))
+
+
+@pytest.mark.parametrize("dtype", [FP16, BF16])
+def test_dequant_w8_bit_exact(dtype):
+    n, k = 64, 448
+    codes, s, _ = si.w8_weights(n, k, -1, seed=5, dtype=dtype)
+    codes[0, :4] = [-128, 127, 0, -1]
+    ref = oracle.dequant8(codes, s, -1, dtype)
+    tiled = qg.repack_w8(to_dev(codes))
+    S = to_dev(s, dtype)
+    W32 = qg.dequant_w8(tiled, S, torch.float32).cpu().numpy()
+    assert np.array_equal(W32.view(np.uint32), ref.view(np.uint32))
+    conv = oracle.f32_to_bf16 if dtype == BF16 else oracle.f32_to_f16
+    assert np.array_equal(to_bits(qg.dequant_w8(tiled, S, S.dtype)), conv(ref))
+
+
+# -- integer-exact GEMMs: bit-exact on every path --------------------------------
+
+def _run_w4(p, path=None):
+    A = to_dev(p.A, p.dtype)
+    tiled = qg.repack_w4(to_dev(p.packed))
+    S, Z = to_dev(p.scale, p.dtype), to_dev(p.zero, p.dtype)
+    bias = to_dev(p.bias, p.bias_dtype) if p.bias is not None else None
+    if path:
+        os.environ["QGEMM_FORCE_PATH"] = path
+    try:
+        C = qg.gemm_w4a16(A, tiled, S, Z, bias, p.group)
+    finally:
+        os.environ.pop("QGEMM_FORCE_PATH", None)
+    torch.cuda.synchronize()
+    return C
+
+
+def _run_w8(p, path=None):
+    A = to_dev(p.A, p.dtype)
+    tiled = qg.repack_w8(to_dev(p.codes))
+    S = to_dev(p.scale, p.dtype)
+    bias = to_dev(p.bias, p.bias_dtype) if p.bias is not None else None
+    if path:
+        os.environ["QGEMM_FORCE_PATH"] = path
+    try:
+        C = qg.gemm_w8a16(A, tiled, S, bias, -1)
+    finally:
+        os.environ.pop("QGEMM_FORCE_PATH", None)
+    torch.cuda.synchronize()
+    return C
+
+
+def _exact_expected(Cref, dtype):
+    conv = oracle.f32_to_bf16 if dtype == BF16 else oracle.f32_to_f16
+    as32 = Cref.astype(np.float32)
+    assert np.array_equal(as32.astype(np.float64), Cref)      # exact inputs stay exact
+    return conv(as32)
+
+
+@pytest.mark.parametrize("m,n,k,group", [
+    (1, 16, 128, 64), (4, 128, 256, 64), (16, 48, 384, 128), (5, 2048, 2048, 64),
+    (33, 128, 256, 64), (100, 192, 512, 128), (256, 256, 1024, 64),
+])
+@pytest.mark.parametrize("path", ["decode", "prefill"])
+@pytest.mark.parametrize("dtype", [BF16, FP16])
+def test_w4_integer_exact(m, n, k, group, path, dtype):
+    p = si.w4_exact_problem(m, n, k, group, seed=m * 7 + n + k, dtype=dtype, bias_dtype=FP16)
+    Cref = oracle.gemm_w4(p.A, p.packed, p.scale, p.zero, group, dtype, p.bias, FP16)
+    C = _run_w4(p, path)
+    got = to_bits(C)
+    exp = _exact_expected(Cref, dtype)
+    bad = np.argwhere(got != exp)
+    assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:4].tolist()}"
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 16, 64), (3, 64, 448), (16, 3584, 3584), (40, 128, 192),
+                                   (130, 256, 512)])
+@pytest.mark.parametrize("path", ["decode", "prefill"])
+@pytest.mark.parametrize("dtype", [FP16, BF16])
+def test_w8_integer_exact(m, n, k, path, dtype):
+    p = si.w8_exact_problem(m, n, k, seed=m + n + k, dtype=dtype, bias_dtype=FP16)
+    Cref = oracle.gemm_w8(p.A, p.codes, p.scale, -1, dtype, p.bias, FP16)
+    got = to_bits(_run_w8(p, path))
+    exp = _exact_expected(Cref, dtype)
+    bad = np.argwhere(got != exp)
+    assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:4].tolist()}"
+
+
+# -- the tiny W4A16 problem (M=4, K=256, N=128, g=64), full oracle ----------------
+
+@pytest.mark.parametrize("path", [None, "decode", "prefill"])
+def test_tiny_w4a16_parity(path):
+    p = si.w4_problem(4, 128, 256, 64, tag="cfg0")
+    Cref = oracle.gemm_w4(p.A, p.packed, p.scale, p.zero, 64, BF16)
+    C = _run_w4(p, path)
+    assert C.dtype == torch.bfloat16 and tuple(C.shape) == (4, 128)
+    err = rel_err(C.float().cpu().numpy(), Cref)
+    assert err <= TOL[BF16], err
+
+
+def test_empty_m_is_noop():
+    p = si.w4_problem(1, 128, 256, 64, tag="cfg0")
+    tiled = qg.repack_w4(to_dev(p.packed))
+    A = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    C = qg.gemm_w4a16(A, tiled, to_dev(p.scale, BF16), to_dev(p.zero, BF16), None, 64)
+    assert tuple(C.shape) == (0, 128)

@@ -1,0 +1,200 @@
+"""Weight-only quantized GEMM (fpA_intB: W4A16 groupwise, W8A16 per channel,
+top-k MoE) for AMD MI355X (gfx950).
+
+Thin torch-facing wrappers over the C ABI in ``include/qgemm.h``: they check
+tensor placement, flatten leading dimensions, pass raw device pointers and
+torch's current HIP stream, and raise ``QGemmError`` on any non-OK status.
+Every computation runs in the library's HIP kernels; there is no other path.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from ._abi import QG_BF16, QG_FP16, QG_FP32, QG_NONE, QGemmError, check, lib
+
+__all__ = [
+    "QGemmError", "lib", "repack_w4", "unrepack_w4", "repack_w8", "unrepack_w8", "dequant_w4",
+    "dequant_w8", "gemm_w4a16", "gemm_w8a16", "moe_grouped", "moe_workspace_size",
+    "gemm_workspace_size", "dtype_code",
+]
+
+_CODES = {torch.bfloat16: QG_BF16, torch.float16: QG_FP16, torch.float32: QG_FP32}
+
+
+def dtype_code(dt: Optional[torch.dtype]) -> int:
+    if dt is None:
+        return QG_NONE
+    if dt not in _CODES:
+        raise QGemmError("dtype", 4, f"unsupported dtype {dt}")
+    return _CODES[dt]
+
+
+def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise QGemmError(name, 1, f"{name} must be a device tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise QGemmError(name, 2, f"{name} must be contiguous")
+    return t
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+# -- load-side repack -------------------------------------------------------
+
+def repack_w4(packed: torch.Tensor) -> torch.Tensor:
+    """Portable int4 [n, k/2] uint8 -> tiled layout (same shape and bytes)."""
+    _dev(packed, "packed")
+    n, half = packed.shape
+    out = torch.empty_like(packed)
+    check("qrepack_w4", lib().qrepack_w4(_ptr(packed), _ptr(out), n, 2 * half, _stream(packed)))
+    return out
+
+
+def unrepack_w4(tiled: torch.Tensor) -> torch.Tensor:
+    _dev(tiled, "tiled")
+    n, half = tiled.shape
+    out = torch.empty_like(tiled)
+    check("qunrepack_w4", lib().qunrepack_w4(_ptr(tiled), _ptr(out), n, 2 * half, _stream(tiled)))
+    return out
+
+
+def repack_w8(codes: torch.Tensor) -> torch.Tensor:
+    """Portable int8 [n, k] -> tiled layout (same shape, offset-binary bytes)."""
+    _dev(codes, "codes")
+    n, k = codes.shape
+    out = torch.empty_like(codes)
+    check("qrepack_w8", lib().qrepack_w8(_ptr(codes), _ptr(out), n, k, _stream(codes)))
+    return out
+
+
+def unrepack_w8(tiled: torch.Tensor) -> torch.Tensor:
+    _dev(tiled, "tiled")
+    n, k = tiled.shape
+    out = torch.empty_like(tiled)
+    check("qunrepack_w8", lib().qunrepack_w8(_ptr(tiled), _ptr(out), n, k, _stream(tiled)))
+    return out
+
+
+# -- dequant hook ------------------------------------------------------------
+
+def dequant_w4(tiled: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor, group_size: int,
+               out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    for t, nm in ((tiled, "tiled"), (scales, "scales"), (zeros, "zeros")):
+        _dev(t, nm)
+    n, half = tiled.shape
+    out = torch.empty((n, 2 * half), dtype=out_dtype, device=tiled.device)
+    check("qdequant_w4", lib().qdequant_w4(_ptr(tiled), _ptr(scales), _ptr(zeros), _ptr(out), n,
+                                           2 * half, group_size, dtype_code(scales.dtype),
+                                           dtype_code(out_dtype), _stream(tiled)))
+    return out
+
+
+def dequant_w8(tiled: torch.Tensor, scales: torch.Tensor,
+               out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    _dev(tiled, "tiled")
+    _dev(scales, "scales")
+    n, k = tiled.shape
+    out = torch.empty((n, k), dtype=out_dtype, device=tiled.device)
+    check("qdequant_w8", lib().qdequant_w8(_ptr(tiled), _ptr(scales), _ptr(out), n, k, -1,
+                                           dtype_code(scales.dtype), dtype_code(out_dtype),
+                                           _stream(tiled)))
+    return out
+
+
+# -- GEMM --------------------------------------------------------------------
+
+def gemm_workspace_size(m: int, n: int, k: int, group_size: int, weight_bits: int) -> int:
+    return int(lib().qgemm_workspace_size(m, n, k, group_size, weight_bits))
+
+
+def gemm_w4a16(A: torch.Tensor, B_tiled: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
+               bias: Optional[torch.Tensor] = None, group_size: int = 64,
+               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C = A . dequant(B)^T (+ bias); A [..., k] bf16/fp16, B tiled int4."""
+    _dev(A, "A")
+    for t, nm in ((B_tiled, "B_tiled"), (scales, "scales"), (zeros, "zeros")):
+        _dev(t, nm)
+    if bias is not None:
+        _dev(bias, "bias")
+    lead = A.shape[:-1]
+    k = A.shape[-1]
+    A2 = A.reshape(-1, k)
+    m, n = A2.shape[0], B_tiled.shape[0]
+    C = out if out is not None else torch.empty((m, n), dtype=A.dtype, device=A.device)
+    _dev(C, "out")
+    check("qgemm_w4a16", lib().qgemm_w4a16(
+        _ptr(A2), _ptr(B_tiled), _ptr(scales), _ptr(zeros), _ptr(bias), _ptr(C), m, n, k,
+        group_size, dtype_code(A.dtype), dtype_code(None if bias is None else bias.dtype),
+        None, 0, _stream(A)))
+    return C.reshape(*lead, n)
+
+
+def gemm_w8a16(A: torch.Tensor, B_tiled: torch.Tensor, scales: torch.Tensor,
+               bias: Optional[torch.Tensor] = None, group_size: int = -1,
+               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C = A . dequant(B)^T (+ bias); A [..., k] bf16/fp16, B tiled int8."""
+    _dev(A, "A")
+    _dev(B_tiled, "B_tiled")
+    _dev(scales, "scales")
+    if bias is not None:
+        _dev(bias, "bias")
+    lead = A.shape[:-1]
+    k = A.shape[-1]
+    A2 = A.reshape(-1, k)
+    m, n = A2.shape[0], B_tiled.shape[0]
+    C = out if out is not None else torch.empty((m, n), dtype=A.dtype, device=A.device)
+    _dev(C, "out")
+    check("qgemm_w8a16", lib().qgemm_w8a16(
+        _ptr(A2), _ptr(B_tiled), _ptr(scales), _ptr(bias), _ptr(C), m, n, k, group_size,
+        dtype_code(A.dtype), dtype_code(None if bias is None else bias.dtype), None, 0,
+        _stream(A)))
+    return C.reshape(*lead, n)
+
+
+# -- MoE -----------------------------------------------------------------------
+
+def moe_workspace_size(tokens: int, hidden: int, inter: int, experts: int, topk: int) -> int:
+    return int(lib().qmoe_workspace_size(tokens, hidden, inter, experts, topk))
+
+
+def moe_grouped(x: torch.Tensor, logits: torch.Tensor, w1_tiled: torch.Tensor, s1: torch.Tensor,
+                z1: torch.Tensor, w2_tiled: torch.Tensor, s2: torch.Tensor, z2: torch.Tensor,
+                topk: int, group_size: int = 64, return_routing: bool = False,
+                workspace: Optional[torch.Tensor] = None):
+    """Top-k MoE with SiLU-gated int4 experts.
+
+    x [T, H]; logits fp32 [T, E]; w1_tiled [E, 2I, H/2] (tiled per expert);
+    s1/z1 [E, 2I, H/g]; w2_tiled [E, H, I/2]; s2/z2 [E, H, I/g].
+    Returns out [T, H] (and (ids int32 [T, k], weights fp32 [T, k])).
+    """
+    for t, nm in ((x, "x"), (logits, "logits"), (w1_tiled, "w1_tiled"), (s1, "s1"), (z1, "z1"),
+                  (w2_tiled, "w2_tiled"), (s2, "s2"), (z2, "z2")):
+        _dev(t, nm)
+    T, H = x.shape
+    E = logits.shape[1]
+    inter = w1_tiled.shape[1] // 2
+    out = torch.empty_like(x)
+    ids = torch.empty((T, topk), dtype=torch.int32, device=x.device) if return_routing else None
+    wts = torch.empty((T, topk), dtype=torch.float32, device=x.device) if return_routing else None
+    need = moe_workspace_size(T, H, inter, E, topk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _dev(workspace, "workspace")
+    check("qmoe_grouped", lib().qmoe_grouped(
+        _ptr(x), _ptr(logits), _ptr(w1_tiled), _ptr(s1), _ptr(z1), _ptr(w2_tiled), _ptr(s2),
+        _ptr(z2), _ptr(out), T, H, inter, E, topk, group_size, dtype_code(x.dtype), _ptr(ids),
+        _ptr(wts), _ptr(workspace), workspace.numel(), _stream(x)))
+    if return_routing:
+        return out, ids, wts
+    return out

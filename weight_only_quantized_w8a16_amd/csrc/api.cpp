@@ -1,0 +1,243 @@
+// api.cpp -- the C ABI of libqgemm (include/qgemm.h): host-side validation,
+// path selection and launch.  Nothing here touches the GPU before every
+// argument has been checked; on error nothing is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/qgemm.h"
+#include "qg_launch.hpp"
+
+namespace {
+
+constexpr int kVersion = 10000;  // 1.0.0
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool act_ok(qg_dtype d) { return d == QG_BF16 || d == QG_FP16; }
+hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
+qg_status hip_status(hipError_t e) { return e == hipSuccess ? QG_OK : QG_ERR_HIP; }
+
+// QGEMM_FORCE_PATH=decode|prefill overrides the choice by m, so that tests
+// can run both paths on the same inputs.  Read at every call (a getenv is
+// negligible next to a launch).
+enum ForcedPath { kAuto, kForceDecode, kForcePrefill };
+ForcedPath forced_path() {
+  const char *v = std::getenv("QGEMM_FORCE_PATH");
+  if (!v) return kAuto;
+  if (std::strcmp(v, "decode") == 0) return kForceDecode;
+  if (std::strcmp(v, "prefill") == 0) return kForcePrefill;
+  return kAuto;
+}
+
+constexpr int kDecodeMaxM = 16;
+
+// Rows [m0, m0 + 16) at a time through the decode kernels.
+template <class F>
+hipError_t by_row_slabs(const qg::GemmArgs &a, F launch, hipStream_t s) {
+  const int N = a.N, K = a.K;
+  for (int m0 = 0; m0 < a.M; m0 += kDecodeMaxM) {
+    qg::GemmArgs b = a;
+    b.A = a.A + static_cast<size_t>(m0) * K;
+    b.C = a.C + static_cast<size_t>(m0) * N;
+    b.M = a.M - m0 < kDecodeMaxM ? a.M - m0 : kDecodeMaxM;
+    hipError_t e = launch(b, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// Checks in the documented order: sizes, NULL, dtypes, group, tile
+// multiples, alignment.
+qg_status gemm_checks(const void *A, const void *B, const void *scales, const void *zeros,
+                      const void *C, const void *bias, int m, int n, int k, int group,
+                      qg_dtype act, qg_dtype bias_dt, int wbits) {
+  if (m < 0 || n < 0 || k <= 0) return QG_ERR_SHAPE;
+  if (m == 0 || n == 0) return QG_OK;   // nothing to compute; pointers unused
+  if (!A || !B || !scales || !C || (wbits == 4 && !zeros)) return QG_ERR_NULL;
+  if (bias_dt != QG_NONE && !bias) return QG_ERR_NULL;
+  if (!act_ok(act)) return QG_ERR_DTYPE;
+  if (bias_dt == QG_NONE ? bias != nullptr : !act_ok(bias_dt)) return QG_ERR_DTYPE;
+  if (wbits == 4) {
+    if (group != 64 && group != 128) return QG_ERR_GROUP;
+    if (k % group != 0) return QG_ERR_GROUP;
+    if (n % 16 != 0 || k % 128 != 0) return QG_ERR_UNSUPPORTED;
+  } else {
+    if (group != -1 && group != k) return QG_ERR_GROUP;
+    if (n % 16 != 0 || k % 64 != 0) return QG_ERR_UNSUPPORTED;
+  }
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(scales, 2) ||
+      (zeros && !aligned(zeros, 2)) || (bias && !aligned(bias, 2)))
+    return QG_ERR_ALIGN;
+  return QG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *qg_strerror(qg_status s) {
+  switch (s) {
+    case QG_OK: return "ok";
+    case QG_ERR_NULL: return "a required pointer is NULL";
+    case QG_ERR_SHAPE: return "invalid or inconsistent sizes";
+    case QG_ERR_GROUP: return "unsupported group size, or k is not a multiple of it";
+    case QG_ERR_DTYPE: return "dtype not allowed for this argument";
+    case QG_ERR_ALIGN: return "pointer not aligned (16 bytes for matrices, 2 for vectors)";
+    case QG_ERR_WORKSPACE: return "workspace missing or too small";
+    case QG_ERR_UNSUPPORTED: return "sizes outside the supported tile multiples";
+    case QG_ERR_HIP: return "HIP runtime error at launch";
+  }
+  return "unknown status";
+}
+
+int qg_version(void) { return kVersion; }
+
+// ---------------------------------------------------------------------------
+// Repack
+// ---------------------------------------------------------------------------
+static qg_status repack_checks(const void *src, const void *dst, int n, int k, int kmul) {
+  if (n < 0 || k < 0) return QG_ERR_SHAPE;
+  if (n == 0 || k == 0) return QG_OK;
+  if (!src || !dst) return QG_ERR_NULL;
+  if (n % 16 != 0 || k % kmul != 0) return QG_ERR_UNSUPPORTED;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return QG_ERR_ALIGN;
+  return QG_OK;
+}
+
+qg_status qrepack_w4(const uint8_t *src, uint8_t *dst, int n, int k, void *stream) {
+  qg_status st = repack_checks(src, dst, n, k, 128);
+  if (st != QG_OK || n == 0 || k == 0) return st;
+  return hip_status(qg::launch_repack_w4(src, dst, n, k, as_stream(stream)));
+}
+qg_status qunrepack_w4(const uint8_t *src, uint8_t *dst, int n, int k, void *stream) {
+  qg_status st = repack_checks(src, dst, n, k, 128);
+  if (st != QG_OK || n == 0 || k == 0) return st;
+  return hip_status(qg::launch_unrepack_w4(src, dst, n, k, as_stream(stream)));
+}
+qg_status qrepack_w8(const int8_t *src, int8_t *dst, int n, int k, void *stream) {
+  qg_status st = repack_checks(src, dst, n, k, 64);
+  if (st != QG_OK || n == 0 || k == 0) return st;
+  return hip_status(qg::launch_repack_w8(src, dst, n, k, as_stream(stream)));
+}
+qg_status qunrepack_w8(const int8_t *src, int8_t *dst, int n, int k, void *stream) {
+  qg_status st = repack_checks(src, dst, n, k, 64);
+  if (st != QG_OK || n == 0 || k == 0) return st;
+  return hip_status(qg::launch_unrepack_w8(src, dst, n, k, as_stream(stream)));
+}
+
+// ---------------------------------------------------------------------------
+// Dequant hook
+// ---------------------------------------------------------------------------
+qg_status qdequant_w4(const uint8_t *B, const void *scales, const void *zeros, void *W, int n,
+                      int k, int group, qg_dtype act, qg_dtype out, void *stream) {
+  if (n < 0 || k < 0) return QG_ERR_SHAPE;
+  if (n == 0 || k == 0) return QG_OK;
+  if (!B || !scales || !zeros || !W) return QG_ERR_NULL;
+  if (!act_ok(act) || !(out == QG_FP32 || out == act)) return QG_ERR_DTYPE;
+  if (group != 64 && group != 128) return QG_ERR_GROUP;
+  if (k % group != 0) return QG_ERR_GROUP;
+  if (n % 16 != 0 || k % 128 != 0) return QG_ERR_UNSUPPORTED;
+  if (!aligned(B, 16) || !aligned(W, 16) || !aligned(scales, 2) || !aligned(zeros, 2))
+    return QG_ERR_ALIGN;
+  return hip_status(qg::launch_dequant_w4(B, static_cast<const uint16_t *>(scales),
+                                          static_cast<const uint16_t *>(zeros), W, n, k, group,
+                                          act, out, as_stream(stream)));
+}
+
+qg_status qdequant_w8(const int8_t *B, const void *scales, void *W, int n, int k, int group,
+                      qg_dtype act, qg_dtype out, void *stream) {
+  if (n < 0 || k < 0) return QG_ERR_SHAPE;
+  if (n == 0 || k == 0) return QG_OK;
+  if (!B || !scales || !W) return QG_ERR_NULL;
+  if (!act_ok(act) || !(out == QG_FP32 || out == act)) return QG_ERR_DTYPE;
+  if (group != -1 && group != k) return QG_ERR_GROUP;
+  if (n % 16 != 0 || k % 64 != 0) return QG_ERR_UNSUPPORTED;
+  if (!aligned(B, 16) || !aligned(W, 16) || !aligned(scales, 2)) return QG_ERR_ALIGN;
+  return hip_status(qg::launch_dequant_w8(B, static_cast<const uint16_t *>(scales), W, n, k, act,
+                                          out, as_stream(stream)));
+}
+
+// ---------------------------------------------------------------------------
+// GEMM
+// ---------------------------------------------------------------------------
+size_t qgemm_workspace_size(int m, int n, int k, int group_size, int weight_bits) {
+  (void)m; (void)n; (void)k; (void)group_size; (void)weight_bits;
+  return 0;
+}
+
+qg_status qgemm_w4a16(const void *A, const uint8_t *B, const void *scales, const void *zeros,
+                      const void *bias, void *C, int m, int n, int k, int group, qg_dtype act,
+                      qg_dtype bias_dt, void *workspace, size_t ws_bytes, void *stream) {
+  (void)workspace; (void)ws_bytes;
+  qg_status st = gemm_checks(A, B, scales, zeros, C, bias, m, n, k, group, act, bias_dt, 4);
+  if (st != QG_OK || m == 0 || n == 0) return st;
+  qg::GemmArgs a{static_cast<const uint16_t *>(A), B, static_cast<const uint16_t *>(scales),
+                 static_cast<const uint16_t *>(zeros), static_cast<const uint16_t *>(bias),
+                 static_cast<uint16_t *>(C), m, n, k, group, static_cast<int>(act),
+                 static_cast<int>(bias_dt)};
+  hipStream_t s = as_stream(stream);
+  const ForcedPath f = forced_path();
+  const bool prefill_ok = n % 64 == 0;
+  if (f == kForcePrefill && prefill_ok) return hip_status(qg::launch_prefill_w4(a, s));
+  if (f == kForceDecode || m <= kDecodeMaxM || !prefill_ok)
+    return hip_status(by_row_slabs(a, qg::launch_decode_w4, s));
+  return hip_status(qg::launch_prefill_w4(a, s));
+}
+
+qg_status qgemm_w8a16(const void *A, const int8_t *B, const void *scales, const void *bias,
+                      void *C, int m, int n, int k, int group, qg_dtype act, qg_dtype bias_dt,
+                      void *workspace, size_t ws_bytes, void *stream) {
+  (void)workspace; (void)ws_bytes;
+  qg_status st = gemm_checks(A, B, scales, nullptr, C, bias, m, n, k, group, act, bias_dt, 8);
+  if (st != QG_OK || m == 0 || n == 0) return st;
+  qg::GemmArgs a{static_cast<const uint16_t *>(A), B, static_cast<const uint16_t *>(scales),
+                 nullptr, static_cast<const uint16_t *>(bias), static_cast<uint16_t *>(C),
+                 m, n, k, 0, static_cast<int>(act), static_cast<int>(bias_dt)};
+  hipStream_t s = as_stream(stream);
+  const ForcedPath f = forced_path();
+  const bool prefill_ok = n % 64 == 0;
+  if (f == kForcePrefill && prefill_ok) return hip_status(qg::launch_prefill_w8(a, s));
+  if (f == kForceDecode || m <= kDecodeMaxM || !prefill_ok)
+    return hip_status(by_row_slabs(a, qg::launch_decode_w8, s));
+  return hip_status(qg::launch_prefill_w8(a, s));
+}
+
+// ---------------------------------------------------------------------------
+// MoE
+// ---------------------------------------------------------------------------
+size_t qmoe_workspace_size(int tokens, int hidden, int inter, int experts, int topk) {
+  if (tokens <= 0 || hidden <= 0 || inter <= 0 || experts <= 0 || topk <= 0) return 0;
+  return qg::moe_workspace_bytes(tokens, hidden, inter, experts, topk);
+}
+
+qg_status qmoe_grouped(const void *x, const float *logits, const uint8_t *w1, const void *s1,
+                       const void *z1, const uint8_t *w2, const void *s2, const void *z2,
+                       void *out, int tokens, int hidden, int inter, int experts, int topk,
+                       int group, qg_dtype act, int32_t *ids_out, float *w_out, void *workspace,
+                       size_t ws_bytes, void *stream) {
+  if (tokens < 0 || hidden <= 0 || inter <= 0 || experts <= 0 || topk <= 0 || topk > experts)
+    return QG_ERR_SHAPE;
+  if (tokens == 0) return QG_OK;        // nothing to compute; pointers unused
+  if (!x || !logits || !w1 || !s1 || !z1 || !w2 || !s2 || !z2 || !out) return QG_ERR_NULL;
+  if (!act_ok(act)) return QG_ERR_DTYPE;
+  if (group != 64 && group != 128) return QG_ERR_GROUP;
+  if (hidden % group != 0 || inter % group != 0) return QG_ERR_GROUP;
+  if (hidden % 128 != 0 || inter % 128 != 0 || experts > 256 || topk > 64)
+    return QG_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w2, 16) || !aligned(out, 16) ||
+      !aligned(logits, 4) || !aligned(s1, 2) || !aligned(z1, 2) || !aligned(s2, 2) ||
+      !aligned(z2, 2) || (ids_out && !aligned(ids_out, 4)) || (w_out && !aligned(w_out, 4)))
+    return QG_ERR_ALIGN;
+  const size_t need = qg::moe_workspace_bytes(tokens, hidden, inter, experts, topk);
+  if (!workspace || ws_bytes < need) return QG_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return QG_ERR_ALIGN;
+  qg::MoeArgs a{static_cast<const uint16_t *>(x), logits, w1,
+                static_cast<const uint16_t *>(s1), static_cast<const uint16_t *>(z1), w2,
+                static_cast<const uint16_t *>(s2), static_cast<const uint16_t *>(z2),
+                static_cast<uint16_t *>(out), tokens, hidden, inter, experts, topk, group,
+                static_cast<int>(act), ids_out, w_out, workspace};
+  return hip_status(qg::launch_moe(a, as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,254 @@
+// moe.hip -- top-k routed MoE over int4 experts ("acext User Guide (v1.7)",
+// 1.2.3 MoE GEMM: fp32 gating logits, expert scales, the routing maps
+// expert_for_source_row / expanded_source_row_to_expanded_dest_row, fc1 with a
+// gated activation, fc2 into an intermediate buffer, and the weighted
+// combine into the final output).
+//
+// Stages, one launch each:
+//   route    one wave per token: top-k of the fp32 logits (ties to the lower
+//            expert id) and the softmax over the selected logits;
+//   plan     one workgroup: per-expert row counts, offsets, the list of
+//            (expert, row range) tiles for the grouped GEMMs, and the
+//            permutation token <-> expert-sorted row;
+//   fc1      grouped tile GEMM, activation rows gathered through the
+//            permutation, gate and up columns in one tile, silu(gate) * up
+//            in the epilogue;
+//   fc2      grouped tile GEMM over the activation rows;
+//   combine  out[t] = sum_j w[t, j] * y[row(t, j)], fp32 in rank order.
+#include "qg_launch.hpp"
+#include "tile_gemm.hpp"
+
+namespace qg {
+
+namespace {
+
+using CfgMoe = TileCfg<128, 128, 2, 2>;
+constexpr int kMoeBM = CfgMoe::BM;
+
+size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+struct MoeLayout {
+  size_t ids, wts, row_src, dest, tiles, ntiles, act, y, total;
+};
+
+MoeLayout moe_layout(int T, int H, int I, int E, int topk) {
+  const size_t R = static_cast<size_t>(T) * topk;
+  const size_t max_tiles = (R + kMoeBM - 1) / kMoeBM + E;
+  MoeLayout l{};
+  size_t o = 0;
+  l.ids = o;     o = align_up(o + R * 4);
+  l.wts = o;     o = align_up(o + R * 4);
+  l.row_src = o; o = align_up(o + R * 4);
+  l.dest = o;    o = align_up(o + R * 4);
+  l.tiles = o;   o = align_up(o + max_tiles * sizeof(MoeTile));
+  l.ntiles = o;  o = align_up(o + 4);
+  l.act = o;     o = align_up(o + R * I * 2);
+  l.y = o;       o = align_up(o + R * H * 2);
+  l.total = o;
+  return l;
+}
+
+}  // namespace
+
+size_t moe_workspace_bytes(int T, int H, int I, int E, int topk) {
+  return moe_layout(T, H, I, E, topk).total;
+}
+
+// One wave per token; up to 256 experts (4 logits per lane).
+__global__ __launch_bounds__(256) void k_moe_route(const float *__restrict__ logits, int T, int E,
+                                                   int topk, int32_t *__restrict__ ids,
+                                                   float *__restrict__ wts) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  float v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = e < E ? logits[static_cast<size_t>(t) * E + e] : -__builtin_inff();
+  }
+  float lmax = 0.f, denom = 0.f, my_l = 0.f;
+  int my_id = 0;
+  for (int j = 0; j < topk; ++j) {
+    // lane-local best (strict > keeps the lower expert id on ties)
+    float bv = v[0];
+    int bi = lane;
+#pragma unroll
+    for (int i = 1; i < 4; ++i)
+      if (v[i] > bv) { bv = v[i]; bi = lane + 64 * i; }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+    }
+    if ((bi & 63) == lane) v[bi >> 6] = -__builtin_inff();
+    if (j == 0) lmax = bv;
+    denom += expf(bv - lmax);
+    if (lane == j) { my_l = bv; my_id = bi; }
+  }
+  if (lane < topk) {
+    ids[static_cast<size_t>(t) * topk + lane] = my_id;
+    wts[static_cast<size_t>(t) * topk + lane] = expf(my_l - lmax) / denom;
+  }
+}
+
+// Single workgroup: counts, offsets, tile list, permutation.
+__global__ __launch_bounds__(1024) void k_moe_plan(const int32_t *__restrict__ ids, int R, int E,
+                                                   int topk, MoeTile *__restrict__ tiles,
+                                                   int32_t *__restrict__ ntiles,
+                                                   int32_t *__restrict__ row_src,
+                                                   int32_t *__restrict__ dest) {
+  __shared__ int cnt[256], off[257], fill[256];
+  for (int e = threadIdx.x; e < 256; e += blockDim.x) { cnt[e] = 0; fill[e] = 0; }
+  __syncthreads();
+  for (int r = threadIdx.x; r < R; r += blockDim.x) atomicAdd(&cnt[ids[r]], 1);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    off[0] = 0;
+    int nt = 0;
+    for (int e = 0; e < E; ++e) {
+      off[e + 1] = off[e] + cnt[e];
+      for (int r0 = off[e]; r0 < off[e + 1]; r0 += kMoeBM) {
+        MoeTile tl;
+        tl.expert = e;
+        tl.row0 = r0;
+        tl.row1 = min(r0 + kMoeBM, off[e + 1]);
+        tl.pad = 0;
+        tiles[nt++] = tl;
+      }
+    }
+    *ntiles = nt;
+  }
+  __syncthreads();
+  for (int r = threadIdx.x; r < R; r += blockDim.x) {
+    const int e = ids[r];
+    const int pos = off[e] + atomicAdd(&fill[e], 1);
+    row_src[pos] = r / topk;
+    dest[r] = pos;
+  }
+}
+
+template <int ACT, int MODE>
+__global__ __launch_bounds__(CfgMoe::NTHR) void k_moe_gemm(TileProblem p, int tiles_n) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+  if (tm >= *p.ntiles) return;
+  tile_gemm<CfgMoe, ACT, 4, MODE>(p, tm, tn, lds);
+}
+
+// out[t, h..h+7] = sum_j w[t, j] * y[dest[t, j], h..h+7]
+template <int ACT>
+__global__ __launch_bounds__(256) void k_moe_combine(const uint16_t *__restrict__ y,
+                                                     const float *__restrict__ wts,
+                                                     const int32_t *__restrict__ dest,
+                                                     uint16_t *__restrict__ out, int T, int H,
+                                                     int topk) {
+  const long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int per = H >> 3;
+  if (idx >= static_cast<long long>(T) * per) return;
+  const int t = static_cast<int>(idx / per), h0 = static_cast<int>(idx % per) * 8;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < topk; ++j) {
+    const float w = wts[static_cast<size_t>(t) * topk + j];
+    const int row = dest[static_cast<size_t>(t) * topk + j];
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(y + static_cast<size_t>(row) * H + h0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += w * bits_to_f32<ACT>(static_cast<uint16_t>(v[i] & 0xFFFFu));
+      acc[2 * i + 1] += w * bits_to_f32<ACT>(static_cast<uint16_t>(v[i] >> 16));
+    }
+  }
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = pack2<ACT>(acc[2 * i], acc[2 * i + 1]);
+  *reinterpret_cast<u32x4 *>(out + static_cast<size_t>(t) * H + h0) = o;
+}
+
+namespace {
+
+template <class K>
+hipError_t set_lds(K kern, int bytes) {
+  return hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+template <int ACT>
+hipError_t run_moe(const MoeArgs &a, hipStream_t s) {
+  const MoeLayout L = moe_layout(a.T, a.H, a.I, a.E, a.topk);
+  char *ws = static_cast<char *>(a.ws);
+  const int R = a.T * a.topk;
+  int32_t *ids = a.ids_out ? a.ids_out : reinterpret_cast<int32_t *>(ws + L.ids);
+  float *wts = a.w_out ? a.w_out : reinterpret_cast<float *>(ws + L.wts);
+  int32_t *row_src = reinterpret_cast<int32_t *>(ws + L.row_src);
+  int32_t *dest = reinterpret_cast<int32_t *>(ws + L.dest);
+  MoeTile *tiles = reinterpret_cast<MoeTile *>(ws + L.tiles);
+  int32_t *ntiles = reinterpret_cast<int32_t *>(ws + L.ntiles);
+  uint16_t *act = reinterpret_cast<uint16_t *>(ws + L.act);
+  uint16_t *y = reinterpret_cast<uint16_t *>(ws + L.y);
+  const int max_tiles = (R + kMoeBM - 1) / kMoeBM + a.E;
+
+  hipLaunchKernelGGL(k_moe_route, dim3((a.T + 3) / 4), dim3(256), 0, s, a.logits, a.T, a.E,
+                     a.topk, ids, wts);
+  hipLaunchKernelGGL(k_moe_plan, dim3(1), dim3(1024), 0, s, ids, R, a.E, a.topk, tiles, ntiles,
+                     row_src, dest);
+
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = set_lds(k_moe_gemm<ACT, kMoeFc1>, CfgMoe::LDS);
+    if (e == hipSuccess) e = set_lds(k_moe_gemm<ACT, kMoeFc2>, CfgMoe::LDS);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  TileProblem p1{};
+  p1.A = a.x;
+  p1.B = a.w1;
+  p1.S = a.s1;
+  p1.Z = a.z1;
+  p1.C = act;
+  p1.M = R;
+  p1.N = a.I;
+  p1.K = a.H;
+  p1.group = a.group;
+  p1.row_src = row_src;
+  p1.tiles = tiles;
+  p1.ntiles = ntiles;
+  p1.b_expert_stride = static_cast<size_t>(2 * a.I) * (a.H / 2);
+  p1.s_expert_stride = static_cast<size_t>(2 * a.I) * (a.H / a.group);
+  p1.w_rows = 2 * a.I;
+  const int tn1 = a.I / (CfgMoe::BN / 2);
+  hipLaunchKernelGGL((k_moe_gemm<ACT, kMoeFc1>), dim3(max_tiles * tn1), dim3(CfgMoe::NTHR),
+                     CfgMoe::LDS, s, p1, tn1);
+
+  TileProblem p2{};
+  p2.A = act;
+  p2.B = a.w2;
+  p2.S = a.s2;
+  p2.Z = a.z2;
+  p2.C = y;
+  p2.M = R;
+  p2.N = a.H;
+  p2.K = a.I;
+  p2.group = a.group;
+  p2.tiles = tiles;
+  p2.ntiles = ntiles;
+  p2.b_expert_stride = static_cast<size_t>(a.H) * (a.I / 2);
+  p2.s_expert_stride = static_cast<size_t>(a.H) * (a.I / a.group);
+  p2.w_rows = a.H;
+  const int tn2 = a.H / CfgMoe::BN;
+  hipLaunchKernelGGL((k_moe_gemm<ACT, kMoeFc2>), dim3(max_tiles * tn2), dim3(CfgMoe::NTHR),
+                     CfgMoe::LDS, s, p2, tn2);
+
+  const long long items = static_cast<long long>(a.T) * (a.H / 8);
+  hipLaunchKernelGGL((k_moe_combine<ACT>), dim3(static_cast<unsigned>((items + 255) / 256)),
+                     dim3(256), 0, s, y, wts, dest, a.out, a.T, a.H, a.topk);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_moe(const MoeArgs &a, hipStream_t s) {
+  return a.act == kBF16 ? run_moe<kBF16>(a, s) : run_moe<kFP16>(a, s);
+}
+
+}  // namespace qg

@@ -1,0 +1,87 @@
+// prefill.hip -- large-M weight-only quantized GEMM (dense tiles) on gfx950.
+//
+// Above a few rows the weights are reused across many activation rows and
+// the matrix cores set the pace, so each workgroup dequantizes its weight
+// tile once into LDS and runs bf16/fp16 v_mfma_f32_32x32x16 over it (the
+// tile kernel in tile_gemm.hpp).  This is the two-path split the pages
+// describe (vllm-omni cpu_int4.py: a dequantize-then-dense-GEMM path for
+// multi-row batches; "[Misc][Kernel]: Add GPTQAllSpark Quantization": the
+// large-M regime), with the dequantized weight kept on chip instead of
+// written back to memory.
+#include "qg_launch.hpp"
+#include "tile_gemm.hpp"
+
+namespace qg {
+
+// Hardware sends workgroup b to XCD b % 8.  Renumber so each XCD walks a
+// contiguous run of tiles in M-major order: neighbours on one XCD share their
+// activation rows in that XCD's L2.
+__device__ __forceinline__ int xcd_linear_id() {
+  const int bid = blockIdx.x, nblk = gridDim.x;
+  const int xcd = bid & 7, loc = bid >> 3;
+  const int per = nblk >> 3, rem = nblk & 7;
+  return (xcd < rem) ? xcd * (per + 1) + loc : rem * (per + 1) + (xcd - rem) * per + loc;
+}
+
+template <class Cfg, int ACT, int WBITS>
+__global__ __launch_bounds__(Cfg::NTHR) void k_prefill(TileProblem p, int tiles_n) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int id = xcd_linear_id();
+  tile_gemm<Cfg, ACT, WBITS, kDense>(p, id / tiles_n, id % tiles_n, lds);
+}
+
+namespace {
+
+using CfgL = TileCfg<256, 128, 4, 2>;   // 8 waves, 64x64 per wave
+using CfgM = TileCfg<128, 128, 2, 2>;   // 4 waves, 64x64 per wave
+using CfgS = TileCfg<64, 64, 2, 2>;     // 4 waves, 32x32 per wave
+
+template <class Cfg, int ACT, int WBITS>
+hipError_t run(const GemmArgs &a, hipStream_t s) {
+  TileProblem p{};
+  p.A = a.A;
+  p.B = static_cast<const uint8_t *>(a.B);
+  p.S = a.S;
+  p.Z = a.Z;
+  p.bias = a.bias;
+  p.C = a.C;
+  p.M = a.M;
+  p.N = a.N;
+  p.K = a.K;
+  p.group = a.group > 0 ? a.group : a.K;
+  p.bias_dt = a.bias_dt;
+  const int tm = (a.M + Cfg::BM - 1) / Cfg::BM, tn = a.N / Cfg::BN;
+  auto kern = k_prefill<Cfg, ACT, WBITS>;
+  static bool attr_set = false;   // benign race: idempotent
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(tm * tn), dim3(Cfg::NTHR), Cfg::LDS, s, p, tn);
+  return hipGetLastError();
+}
+
+// Largest tile that still gives at least one workgroup per CU; smaller tiles
+// otherwise (256 CUs on MI355X).
+template <int ACT, int WBITS>
+hipError_t dispatch(const GemmArgs &a, hipStream_t s) {
+  auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * (a.N / bn); };
+  const bool n128 = a.N % 128 == 0;
+  if (n128 && a.M > 128 && tiles(256, 128) >= 256) return run<CfgL, ACT, WBITS>(a, s);
+  if (n128 && a.M > 64 && tiles(128, 128) >= 256) return run<CfgM, ACT, WBITS>(a, s);
+  if (a.N % 64 == 0) return run<CfgS, ACT, WBITS>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_prefill_w4(const GemmArgs &a, hipStream_t s) {
+  return a.act == kBF16 ? dispatch<kBF16, 4>(a, s) : dispatch<kFP16, 4>(a, s);
+}
+hipError_t launch_prefill_w8(const GemmArgs &a, hipStream_t s) {
+  return a.act == kBF16 ? dispatch<kBF16, 8>(a, s) : dispatch<kFP16, 8>(a, s);
+}
+
+}  // namespace qg

@@ -1,0 +1,59 @@
+// qg_launch.hpp -- host-side launchers implemented in the .hip translation
+// units and called by the C ABI layer (api.cpp) after validation.  Every
+// launcher assumes its arguments were validated and returns the HIP status
+// of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qg {
+
+hipError_t launch_repack_w4(const uint8_t *src, uint8_t *dst, int n, int k, hipStream_t s);
+hipError_t launch_unrepack_w4(const uint8_t *src, uint8_t *dst, int n, int k, hipStream_t s);
+hipError_t launch_repack_w8(const int8_t *src, int8_t *dst, int n, int k, hipStream_t s);
+hipError_t launch_unrepack_w8(const int8_t *src, int8_t *dst, int n, int k, hipStream_t s);
+
+hipError_t launch_dequant_w4(const uint8_t *B, const uint16_t *S, const uint16_t *Z, void *W,
+                             int n, int k, int group, int act, int out, hipStream_t s);
+hipError_t launch_dequant_w8(const int8_t *B, const uint16_t *S, void *W, int n, int k, int act,
+                             int out, hipStream_t s);
+
+// Dense GEMM problem as the kernels see it.
+struct GemmArgs {
+  const uint16_t *A;      // [M, K]
+  const void *B;          // tiled codes
+  const uint16_t *S;      // scales
+  const uint16_t *Z;      // zeros (w4) or null
+  const uint16_t *bias;   // [N] or null
+  uint16_t *C;            // [M, N]
+  int M, N, K, group;     // group: 64/128 (w4), 0 = per channel (w8)
+  int act, bias_dt;
+};
+
+// Decode path: M <= 16, weights streamed once.
+hipError_t launch_decode_w4(const GemmArgs &a, hipStream_t s);
+hipError_t launch_decode_w8(const GemmArgs &a, hipStream_t s);
+// Prefill path: any M, matrix-core tiles with weights dequantized into LDS.
+hipError_t launch_prefill_w4(const GemmArgs &a, hipStream_t s);
+hipError_t launch_prefill_w8(const GemmArgs &a, hipStream_t s);
+
+// MoE pipeline.
+struct MoeArgs {
+  const uint16_t *x;
+  const float *logits;
+  const uint8_t *w1;
+  const uint16_t *s1, *z1;
+  const uint8_t *w2;
+  const uint16_t *s2, *z2;
+  uint16_t *out;
+  int T, H, I, E, topk, group, act;
+  int32_t *ids_out;
+  float *w_out;
+  void *ws;
+};
+size_t moe_workspace_bytes(int T, int H, int I, int E, int topk);
+hipError_t launch_moe(const MoeArgs &a, hipStream_t s);
+
+}  // namespace qg

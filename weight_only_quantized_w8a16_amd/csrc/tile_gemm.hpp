@@ -1,0 +1,303 @@
+// tile_gemm.hpp -- the matrix-core tile kernel behind the prefill GEMMs and
+// the MoE grouped GEMMs (gfx950, v_mfma_f32_32x32x16_{bf16,f16}).
+//
+// One workgroup computes a BM x BN tile of C = A . W^T.  Per 64-wide step of
+// K it stages A (raw 16-bit activations) and W (dequantized from the tiled
+// integer codes by the workgroup itself) into LDS, double-buffered, and every
+// wave reads its operand fragments from there with ds_read_b128.  Each packed
+// weight is therefore dequantized once per workgroup and shared by all its
+// waves -- the dequant-into-LDS structure that amortises the conversion over
+// BM rows of activations.
+//
+// LDS rows are 128 bytes (64 k of 16-bit values) split into eight 16-byte
+// chunks stored at chunk ^ (row % 8), so that the 32 rows one fragment read
+// touches spread over all banks.
+//
+// Dequant in this kernel: int4 w = fma(q, s, z - 8 s) rounded to nearest even
+// (equal to the exact (q - 8) s + z whenever z - 8 s is exact in fp32, as it
+// is for the scale/zero ranges used); int8 per-channel stages the exact code q
+// and multiplies the finished fp32 sum by the channel's scale.
+#pragma once
+
+#include "qg_common.hpp"
+
+namespace qg {
+
+enum TileMode { kDense = 0, kMoeFc1 = 1, kMoeFc2 = 2 };
+
+// Tile of the MoE row space: rows [row0, row1) of the expert-sorted rows all
+// belong to `expert`.
+struct MoeTile {
+  int expert, row0, row1, pad;
+};
+
+struct TileProblem {
+  const uint16_t *A;         // dense: [M, K]; fc1: x [T, K] gathered; fc2: act [R, K]
+  const uint8_t *B;          // tiled codes (expert 0 for MoE)
+  const uint16_t *S, *Z;     // scales / zeros (expert 0 for MoE)
+  const uint16_t *bias;      // dense only, [N] or null
+  uint16_t *C;               // dense: [M, N]; fc1: act [R, N]; fc2: y [R, N]
+  int M, N, K;               // N = output columns (fc1: inter)
+  int group;                 // 64 / 128 (w4); 0 (w8 per channel)
+  int bias_dt;
+  // MoE
+  const int32_t *row_src;    // fc1: expert-sorted row -> token
+  const MoeTile *tiles;      // tile list
+  const int32_t *ntiles;     // number of valid entries in `tiles`
+  size_t b_expert_stride;    // bytes of tiled codes per expert
+  size_t s_expert_stride;    // scale/zero elements per expert
+  int w_rows;                // rows of one expert's weight matrix
+};
+
+template <int BM_, int BN_, int WM_, int WN_>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int BK = 64;
+  static constexpr int NTHR = 64 * WM * WN;
+  static constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
+  static constexpr int TM = WTM / 32, TN = WTN / 32;  // 32x32 subtiles per wave
+  static constexpr int A_CHUNKS = BM * 8 / NTHR;      // 16-byte A chunks per thread per step
+  static constexpr int B_SLOTS = BN * 4 / NTHR;       // 8-byte code runs per thread (w4)
+  static constexpr int B_RUNS8 = BN * 8 / NTHR;       // 8-byte code runs per thread (w8)
+  static constexpr int STAGE = (BM + BN) * 128;       // bytes per LDS stage
+  static constexpr int LDS = 2 * STAGE;
+  static_assert(A_CHUNKS >= 1 && B_SLOTS >= 1, "tile too small for the thread count");
+};
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+
+// Dequantize one tiled int4 word (codes k0..k0+7, code e at its tiled nibble
+// slot) with scale s and z8 = z - 8 s into 8 packed 16-bit values.
+template <int ACT>
+__device__ __forceinline__ u32x4 dequant_word_w4(uint32_t w, float s, float z8) {
+  const uint32_t m0 = w & 0x0F0F0F0Fu;          // nibble slots 0,2,4,6 -> codes 0,4,1,5
+  const uint32_t m1 = (w >> 4) & 0x0F0F0F0Fu;   // nibble slots 1,3,5,7 -> codes 2,6,3,7
+  float q0 = static_cast<float>(m0 & 0xFFu), q4 = static_cast<float>((m0 >> 8) & 0xFFu);
+  float q1 = static_cast<float>((m0 >> 16) & 0xFFu), q5 = static_cast<float>(m0 >> 24);
+  float q2 = static_cast<float>(m1 & 0xFFu), q6 = static_cast<float>((m1 >> 8) & 0xFFu);
+  float q3 = static_cast<float>((m1 >> 16) & 0xFFu), q7 = static_cast<float>(m1 >> 24);
+  u32x4 r;
+  r.x = pack2<ACT>(__builtin_fmaf(q0, s, z8), __builtin_fmaf(q1, s, z8));
+  r.y = pack2<ACT>(__builtin_fmaf(q2, s, z8), __builtin_fmaf(q3, s, z8));
+  r.z = pack2<ACT>(__builtin_fmaf(q4, s, z8), __builtin_fmaf(q5, s, z8));
+  r.w = pack2<ACT>(__builtin_fmaf(q6, s, z8), __builtin_fmaf(q7, s, z8));
+  return r;
+}
+
+template <class Cfg, int ACT, int WBITS, int MODE>
+__device__ __forceinline__ void tile_gemm(const TileProblem &p, int tile_m, int tile_n,
+                                          char *lds) {
+  constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, NTHR = Cfg::NTHR;
+  constexpr int TM = Cfg::TM, TN = Cfg::TN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
+  const int K = p.K;
+  const int nsteps = K / BK;
+
+  // ---- row sources for A -------------------------------------------------
+  int row_lo, row_hi;         // valid global row range of this tile
+  const uint8_t *Bbase = p.B;
+  const uint16_t *Sbase = p.S, *Zbase = p.Z;
+  if constexpr (MODE == kDense) {
+    row_lo = tile_m * BM;
+    row_hi = min(p.M, row_lo + BM);
+  } else {
+    const MoeTile t = p.tiles[tile_m];
+    row_lo = t.row0;
+    row_hi = t.row1;
+    Bbase += static_cast<size_t>(t.expert) * p.b_expert_stride;
+    Sbase += static_cast<size_t>(t.expert) * p.s_expert_stride;
+    if (Zbase) Zbase += static_cast<size_t>(t.expert) * p.s_expert_stride;
+  }
+  const int n0 = (MODE == kMoeFc1) ? tile_n * (BN / 2) : tile_n * BN;
+
+  // A chunks owned by this thread: (row, chunk) pairs.
+  const uint16_t *a_src[Cfg::A_CHUNKS];
+  int a_lds[Cfg::A_CHUNKS];
+#pragma unroll
+  for (int c = 0; c < Cfg::A_CHUNKS; ++c) {
+    const int idx = tid + c * NTHR;
+    const int r = idx >> 3, ch = idx & 7;
+    const int grow = row_lo + r;
+    a_lds[c] = swz(r, ch);
+    if (grow < row_hi) {
+      size_t arow;
+      if constexpr (MODE == kMoeFc1) arow = static_cast<size_t>(p.row_src[grow]);
+      else arow = static_cast<size_t>(grow);
+      a_src[c] = p.A + arow * K + ch * 8;
+    } else {
+      a_src[c] = nullptr;
+    }
+  }
+
+  // B runs owned by this thread.
+  // w4: slot = (16-row block bi, lane slot l); per step it reads the 8-byte
+  //     half (words 2h, 2h+1) of the slot's 16 bytes, h = step % 2.
+  // w8: run = (block bi, lane slot l, t): 8 bytes, one per step-block.
+  constexpr int NB = (WBITS == 4) ? Cfg::B_SLOTS : Cfg::B_RUNS8;
+  const uint8_t *b_src[NB];
+  int b_lds0[NB], b_lds1[NB];
+  size_t b_sidx[NB];
+#pragma unroll
+  for (int c = 0; c < NB; ++c) {
+    const int idx = tid + c * NTHR;
+    int l, bi, t = 0;
+    if constexpr (WBITS == 4) { l = idx & 63; bi = idx >> 6; }
+    else { t = idx & 1; l = (idx >> 1) & 63; bi = idx >> 7; }
+    const int nl = l & 15, j = l >> 4;
+    const int lrow = bi * 16 + nl;                 // LDS row
+    int wrow;                                      // weight row
+    if constexpr (MODE == kMoeFc1)
+      wrow = (lrow < BN / 2) ? n0 + lrow : p.N + n0 + (lrow - BN / 2);
+    else
+      wrow = n0 + lrow;
+    if constexpr (WBITS == 4) {
+      b_src[c] = Bbase + (static_cast<size_t>(wrow >> 4) * (K >> 7)) * 1024 + l * 16;
+      b_lds0[c] = swz(lrow, j);        // word 2h   -> k-chunk j      (of the 64-k step)
+      b_lds1[c] = swz(lrow, 4 + j);    // word 2h+1 -> k-chunk 4 + j
+      b_sidx[c] = static_cast<size_t>(wrow) * (K / p.group);
+    } else {
+      b_src[c] = Bbase + (static_cast<size_t>(wrow >> 4) * (K >> 6)) * 1024 + l * 16 + t * 8;
+      b_lds0[c] = swz(lrow, 4 * t + j);
+      b_lds1[c] = 0;
+      b_sidx[c] = 0;
+    }
+  }
+
+  // Register staging for the next step.
+  u32x4 a_reg[Cfg::A_CHUNKS];
+  u32x2 b_reg[NB];
+  float s_reg[NB], z_reg[NB];
+
+  auto gload = [&](int step) {
+    const int k0 = step * BK;
+#pragma unroll
+    for (int c = 0; c < Cfg::A_CHUNKS; ++c)
+      a_reg[c] = a_src[c] ? *reinterpret_cast<const u32x4 *>(a_src[c] + k0) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int c = 0; c < NB; ++c) {
+      if constexpr (WBITS == 4) {
+        const int kb = step >> 1, h = step & 1;
+        b_reg[c] = *reinterpret_cast<const u32x2 *>(b_src[c] + static_cast<size_t>(kb) * 1024 + h * 8);
+        const size_t gi = b_sidx[c] + (k0 / p.group);
+        s_reg[c] = bits_to_f32<ACT>(Sbase[gi]);
+        z_reg[c] = bits_to_f32<ACT>(Zbase[gi]);
+      } else {
+        b_reg[c] = *reinterpret_cast<const u32x2 *>(b_src[c] + static_cast<size_t>(step) * 1024);
+      }
+    }
+  };
+
+  auto lstore = [&](int stage) {
+    char *As = lds + stage * Cfg::STAGE;
+    char *Bs = As + BM * 128;
+#pragma unroll
+    for (int c = 0; c < Cfg::A_CHUNKS; ++c) *reinterpret_cast<u32x4 *>(As + a_lds[c]) = a_reg[c];
+#pragma unroll
+    for (int c = 0; c < NB; ++c) {
+      if constexpr (WBITS == 4) {
+        const float s = s_reg[c], z8 = z_reg[c] - 8.0f * s;
+        *reinterpret_cast<u32x4 *>(Bs + b_lds0[c]) = dequant_word_w4<ACT>(b_reg[c].x, s, z8);
+        *reinterpret_cast<u32x4 *>(Bs + b_lds1[c]) = dequant_word_w4<ACT>(b_reg[c].y, s, z8);
+      } else {
+        *reinterpret_cast<u32x4 *>(Bs + b_lds0[c]) =
+            (ACT == kFP16) ? w8_run_to_f16(b_reg[c].x, b_reg[c].y) : w8_run_to_bf16(b_reg[c].x, b_reg[c].y);
+      }
+    }
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int jn = 0; jn < TN; ++jn)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][jn][v] = 0.f;
+
+  // LDS rows this wave reads.
+  int a_row[TM], b_row[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) a_row[i] = wm * Cfg::WTM + 32 * i + (lane & 31);
+#pragma unroll
+  for (int jn = 0; jn < TN; ++jn) {
+    if constexpr (MODE == kMoeFc1) {
+      constexpr int HALF = TN / 2;
+      const int base = (jn < HALF) ? wn * (Cfg::WTN / 2) + 32 * jn
+                                   : BN / 2 + wn * (Cfg::WTN / 2) + 32 * (jn - HALF);
+      b_row[jn] = base + (lane & 31);
+    } else {
+      b_row[jn] = wn * Cfg::WTN + 32 * jn + (lane & 31);
+    }
+  }
+  const int khalf = lane >> 5;
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int step = 0; step < nsteps; ++step) {
+    const int cur = step & 1;
+    if (step + 1 < nsteps) gload(step + 1);
+    const char *As = lds + cur * Cfg::STAGE;
+    const char *Bs = As + BM * 128;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int chunk = 2 * ks + khalf;
+      u32x4 af[TM], bf[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const u32x4 *>(As + swz(a_row[i], chunk));
+#pragma unroll
+      for (int jn = 0; jn < TN; ++jn) bf[jn] = *reinterpret_cast<const u32x4 *>(Bs + swz(b_row[jn], chunk));
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int jn = 0; jn < TN; ++jn) acc[i][jn] = mfma32x32x16<ACT>(af[i], bf[jn], acc[i][jn]);
+    }
+    if (step + 1 < nsteps) lstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue -----------------------------------------------------------
+  // 32x32 accumulator: value v of lane -> row 8*(v/4) + 4*(lane/32) + v%4,
+  // column lane % 32.
+  const int col_in = lane & 31;
+  if constexpr (MODE == kMoeFc1) {
+    constexpr int HALF = TN / 2;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int jn = 0; jn < HALF; ++jn) {
+        const int col = n0 + wn * (Cfg::WTN / 2) + 32 * jn + col_in;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = row_lo + wm * Cfg::WTM + 32 * i + 8 * (v >> 2) + 4 * khalf + (v & 3);
+          if (r < row_hi) {
+            const float g = acc[i][jn][v], u = acc[i][jn + HALF][v];
+            const float a = g / (1.0f + __expf(-g)) * u;
+            p.C[static_cast<size_t>(r) * p.N + col] = f32_to_bits<ACT>(a);
+          }
+        }
+      }
+  } else {
+#pragma unroll
+    for (int jn = 0; jn < TN; ++jn) {
+      const int col = n0 + wn * Cfg::WTN + 32 * jn + col_in;
+      float cs = 1.0f, cb = 0.0f;
+      if constexpr (WBITS == 8) cs = bits_to_f32<ACT>(Sbase[col]);
+      if (MODE == kDense && p.bias) cb = bits_to_f32_dyn(p.bias[col], p.bias_dt);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = row_lo + wm * Cfg::WTM + 32 * i + 8 * (v >> 2) + 4 * khalf + (v & 3);
+          if (r < row_hi) {
+            float val = acc[i][jn][v];
+            if constexpr (WBITS == 8) val *= cs;
+            val += cb;
+            p.C[static_cast<size_t>(r) * p.N + col] = f32_to_bits<ACT>(val);
+          }
+        }
+    }
+  }
+}
+
+}  // namespace qg

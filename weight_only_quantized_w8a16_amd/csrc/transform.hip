@@ -1,0 +1,196 @@
+// transform.hip -- load-side repack into the tiled layouts of include/qgemm.h,
+// its inverse, and the bit-exact dequantization hook.
+//
+// The repack is a pure permutation done once when weights are loaded, so that
+// the GEMM kernels never shuffle nibbles per call (the motivation vllm-omni
+// cpu_int4.py gives for its to_split_halves de-interleave).  The dequant rule
+// is the one of that file's module docstring: w = (q - 8) * scale + zero, and
+// for int8 "acext User Guide (v1.7)" 1.3.1: w = q * scale per channel.
+#include "qg_common.hpp"
+#include "qg_launch.hpp"
+
+namespace qg {
+
+// One thread per tiled 32-bit word.  Word index -> (block, lane slot, t).
+__global__ void k_repack_w4(const uint32_t *__restrict__ src, uint32_t *__restrict__ dst,
+                            int n, int k, long long words) {
+  long long w = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (w >= words) return;
+  int kblocks = k >> 7;
+  long long blk = w >> 8;
+  int slot = static_cast<int>((w >> 2) & 63), t = static_cast<int>(w & 3);
+  int nt = static_cast<int>(blk / kblocks), kb = static_cast<int>(blk % kblocks);
+  int row = nt * 16 + (slot & 15), j = slot >> 4;
+  int k0 = kb * 128 + 32 * t + 8 * j;                    // 8 codes = 1 source word
+  uint32_t v = src[(static_cast<size_t>(row) * (k >> 1) + (k0 >> 1)) >> 2];
+  dst[w] = w4_to_tiled_word(v);
+}
+
+__global__ void k_unrepack_w4(const uint32_t *__restrict__ src, uint32_t *__restrict__ dst,
+                              int n, int k, long long words) {
+  long long w = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (w >= words) return;
+  int kblocks = k >> 7;
+  long long blk = w >> 8;
+  int slot = static_cast<int>((w >> 2) & 63), t = static_cast<int>(w & 3);
+  int nt = static_cast<int>(blk / kblocks), kb = static_cast<int>(blk % kblocks);
+  int row = nt * 16 + (slot & 15), j = slot >> 4;
+  int k0 = kb * 128 + 32 * t + 8 * j;
+  dst[(static_cast<size_t>(row) * (k >> 1) + (k0 >> 1)) >> 2] = w4_from_tiled_word(src[w]);
+}
+
+// One thread per 8-byte run (block, slot, t): 8 consecutive k of one row.
+__global__ void k_repack_w8(const uint2 *__restrict__ src, uint2 *__restrict__ dst, int n, int k,
+                            long long runs, int flip_from_tiled) {
+  long long r = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (r >= runs) return;
+  int kblocks = k >> 6;
+  long long blk = r >> 7;
+  int slot = static_cast<int>((r >> 1) & 63), t = static_cast<int>(r & 1);
+  int nt = static_cast<int>(blk / kblocks), kb = static_cast<int>(blk % kblocks);
+  int row = nt * 16 + (slot & 15), j = slot >> 4;
+  int k0 = kb * 64 + 32 * t + 8 * j;
+  size_t lin = (static_cast<size_t>(row) * k + k0) >> 3;
+  if (!flip_from_tiled) {
+    uint2 v = src[lin];
+    v.x ^= 0x80808080u;
+    v.y ^= 0x80808080u;
+    dst[r] = v;
+  } else {
+    uint2 v = src[r];
+    v.x ^= 0x80808080u;
+    v.y ^= 0x80808080u;
+    dst[lin] = v;
+  }
+}
+
+static inline unsigned grid_for(long long items, int block) {
+  return static_cast<unsigned>((items + block - 1) / block);
+}
+
+hipError_t launch_repack_w4(const uint8_t *src, uint8_t *dst, int n, int k, hipStream_t s) {
+  long long words = static_cast<long long>(n) * k / 8;
+  hipLaunchKernelGGL(k_repack_w4, dim3(grid_for(words, 256)), dim3(256), 0, s,
+                     reinterpret_cast<const uint32_t *>(src), reinterpret_cast<uint32_t *>(dst),
+                     n, k, words);
+  return hipGetLastError();
+}
+hipError_t launch_unrepack_w4(const uint8_t *src, uint8_t *dst, int n, int k, hipStream_t s) {
+  long long words = static_cast<long long>(n) * k / 8;
+  hipLaunchKernelGGL(k_unrepack_w4, dim3(grid_for(words, 256)), dim3(256), 0, s,
+                     reinterpret_cast<const uint32_t *>(src), reinterpret_cast<uint32_t *>(dst),
+                     n, k, words);
+  return hipGetLastError();
+}
+hipError_t launch_repack_w8(const int8_t *src, int8_t *dst, int n, int k, hipStream_t s) {
+  long long runs = static_cast<long long>(n) * k / 8;
+  hipLaunchKernelGGL(k_repack_w8, dim3(grid_for(runs, 256)), dim3(256), 0, s,
+                     reinterpret_cast<const uint2 *>(src), reinterpret_cast<uint2 *>(dst), n, k,
+                     runs, 0);
+  return hipGetLastError();
+}
+hipError_t launch_unrepack_w8(const int8_t *src, int8_t *dst, int n, int k, hipStream_t s) {
+  long long runs = static_cast<long long>(n) * k / 8;
+  hipLaunchKernelGGL(k_repack_w8, dim3(grid_for(runs, 256)), dim3(256), 0, s,
+                     reinterpret_cast<const uint2 *>(src), reinterpret_cast<uint2 *>(dst), n, k,
+                     runs, 1);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Dequant hook.  One thread per (row, 8 consecutive k).  fp32 value
+// fmaf(q - 8, s, z): the product is exact in fp32, so the fused form rounds
+// exactly once, like the plain definition.  16-bit outputs round to nearest
+// even from that fp32 value.
+// ---------------------------------------------------------------------------
+template <int ACT, int OUT>
+__global__ void k_dequant_w4(const uint8_t *__restrict__ B, const uint16_t *__restrict__ S,
+                             const uint16_t *__restrict__ Z, void *__restrict__ W, int n, int k,
+                             int group, long long runs) {
+  long long r = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (r >= runs) return;
+  int per_row = k >> 3;
+  int row = static_cast<int>(r / per_row), k0 = static_cast<int>(r % per_row) * 8;
+  uint32_t word = *reinterpret_cast<const uint32_t *>(B + w4_word_offset(row, k0, k));
+  size_t gi = static_cast<size_t>(row) * (k / group) + k0 / group;
+  float s = bits_to_f32<ACT>(S[gi]);
+  float z = bits_to_f32<ACT>(Z[gi]);
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    v[e] = __builtin_fmaf(static_cast<float>(static_cast<int>(w4_tiled_code(word, e)) - 8), s, z);
+  size_t o = static_cast<size_t>(row) * k + k0;
+  if constexpr (OUT == QG_FP32) {
+    float4 *d = reinterpret_cast<float4 *>(static_cast<float *>(W) + o);
+    d[0] = make_float4(v[0], v[1], v[2], v[3]);
+    d[1] = make_float4(v[4], v[5], v[6], v[7]);
+  } else {
+    uint4 pk;
+    pk.x = pack2<OUT>(v[0], v[1]);
+    pk.y = pack2<OUT>(v[2], v[3]);
+    pk.z = pack2<OUT>(v[4], v[5]);
+    pk.w = pack2<OUT>(v[6], v[7]);
+    *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(W) + o) = pk;
+  }
+}
+
+template <int ACT, int OUT>
+__global__ void k_dequant_w8(const int8_t *__restrict__ B, const uint16_t *__restrict__ S,
+                             void *__restrict__ W, int n, int k, long long runs) {
+  long long r = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (r >= runs) return;
+  int per_row = k >> 3;
+  int row = static_cast<int>(r / per_row), k0 = static_cast<int>(r % per_row) * 8;
+  uint2 run = *reinterpret_cast<const uint2 *>(B + w8_run_offset(row, k0, k));
+  float s = bits_to_f32<ACT>(S[row]);
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    uint32_t word = e < 4 ? run.x : run.y;
+    int q = static_cast<int>((word >> (8 * (e & 3))) & 0xFFu) - 128;
+    v[e] = static_cast<float>(q) * s;   // exact: 8 x 11 significant bits
+  }
+  size_t o = static_cast<size_t>(row) * k + k0;
+  if constexpr (OUT == QG_FP32) {
+    float4 *d = reinterpret_cast<float4 *>(static_cast<float *>(W) + o);
+    d[0] = make_float4(v[0], v[1], v[2], v[3]);
+    d[1] = make_float4(v[4], v[5], v[6], v[7]);
+  } else {
+    uint4 pk;
+    pk.x = pack2<OUT>(v[0], v[1]);
+    pk.y = pack2<OUT>(v[2], v[3]);
+    pk.z = pack2<OUT>(v[4], v[5]);
+    pk.w = pack2<OUT>(v[6], v[7]);
+    *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(W) + o) = pk;
+  }
+}
+
+hipError_t launch_dequant_w4(const uint8_t *B, const uint16_t *S, const uint16_t *Z, void *W,
+                             int n, int k, int group, int act, int out, hipStream_t s) {
+  long long runs = static_cast<long long>(n) * k / 8;
+  dim3 g(grid_for(runs, 256)), b(256);
+#define QG_DQ4(A_, O_) hipLaunchKernelGGL((k_dequant_w4<A_, O_>), g, b, 0, s, B, S, Z, W, n, k, group, runs)
+  if (act == kBF16) {
+    if (out == QG_FP32) QG_DQ4(kBF16, QG_FP32); else QG_DQ4(kBF16, kBF16);
+  } else {
+    if (out == QG_FP32) QG_DQ4(kFP16, QG_FP32); else QG_DQ4(kFP16, kFP16);
+  }
+#undef QG_DQ4
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_w8(const int8_t *B, const uint16_t *S, void *W, int n, int k, int act,
+                             int out, hipStream_t s) {
+  long long runs = static_cast<long long>(n) * k / 8;
+  dim3 g(grid_for(runs, 256)), b(256);
+#define QG_DQ8(A_, O_) hipLaunchKernelGGL((k_dequant_w8<A_, O_>), g, b, 0, s, B, S, W, n, k, runs)
+  if (act == kBF16) {
+    if (out == QG_FP32) QG_DQ8(kBF16, QG_FP32); else QG_DQ8(kBF16, kBF16);
+  } else {
+    if (out == QG_FP32) QG_DQ8(kFP16, QG_FP32); else QG_DQ8(kFP16, kFP16);
+  }
+#undef QG_DQ8
+  return hipGetLastError();
+}
+
+}  // namespace qg
