@@ -1,0 +1,372 @@
+#!/usr/bin/env python3
+"""Benchmark of the weight-only quantized GEMM on one MI355X.
+
+Headline (the printed `value`): decode GEMV HBM bandwidth at M=1 over the
+W4A16 decode workload -- K=2048, group 64, bf16 activations and output,
+N in {2048, 3072, 13312} plus the tied-vocab projection N=131072.  One step
+is one GEMV per shape; `value` = algorithmic bytes of a step / step time.
+
+Secondary sections on the same JSON line:
+  sweep    every (M, N) of the decode workload, M in {1, 2, 4, 8};
+  prefill  W4A16 M=512, K=2048, N in {3072, 13312, 131072}, g in {64, 128},
+           fp16 bias: TFLOP/s against the dense bf16 matrix-core peak;
+  moe      grouped W4A16 MoE, 2048 tokens, hidden 2048, inter 1408,
+           64 experts, top-6;
+  roofline the decode kernel of the N=131072 GEMV: algorithmic bytes per
+           launch / its mean launch time (HIP events on the launch stream);
+  cpu_baseline  the CPU oracle on a bounded sample of the decode step.
+
+Inputs are seeded synthetic data generated on the host and copied to HBM
+before timing.  Memory-bound shapes rotate over enough identical weight
+copies (>= 1 GiB per shape) that no launch finds its weights in the 256 MB
+Infinity Cache or in L2.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores, TFLOP/s
+ROTATE_BYTES = 1 << 30
+
+DECODE_K, DECODE_G = 2048, 64
+DECODE_N = [2048, 3072, 13312, 131072]
+SWEEP = [(m, n) for m in (1, 2, 4, 8) for n in (2048, 3072, 13312)] + [(1, 131072)]
+PREFILL = [(512, n, g) for g in (64, 128) for n in (3072, 13312, 131072)]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def w4_bytes(m, n, k, g, bias=False):
+    """Algorithmic bytes of one W4A16 GEMM: packed codes, bf16 scales and
+    zeros, activations, output (and bias)."""
+    return n * k // 2 + 2 * 2 * n * (k // g) + 2 * m * k + 2 * m * n + (2 * n if bias else 0)
+
+
+def source_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+DECODE_SOURCES = ["weight_only_quantized_w8a16_amd/csrc/decode.hip",
+                  "weight_only_quantized_w8a16_amd/csrc/qg_common.hpp"]
+
+
+def load_traffic():
+    """HBM bytes per launch of the headline kernel from committed rocprofv3
+    counter runs, if they were taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic_decode_w4_m1_n131072.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_digest") != source_digest(DECODE_SOURCES):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+class Weights:
+    """`copies` identical device copies of one tiled W4 weight set."""
+
+    def __init__(self, torch, qg, si, n, k, g, tag, copies, bias=False):
+        packed, s, z, b = si.w4_weights(n, k, g, si.seed_of(tag, "w", n, k, g),
+                                        bias_dtype=si.FP16 if bias else si.NONE)
+        dev = "cuda"
+        base = qg.repack_w4(torch.from_numpy(packed).to(dev))
+        sc = torch.from_numpy(s.view("int16")).view(torch.bfloat16).to(dev)
+        ze = torch.from_numpy(z.view("int16")).view(torch.bfloat16).to(dev)
+        self.bias = torch.from_numpy(b.view("int16")).view(torch.float16).to(dev) if bias else None
+        self.sets = [(base, sc, ze)]
+        for _ in range(copies - 1):
+            self.sets.append((base.clone(), sc.clone(), ze.clone()))
+        self.n, self.k, self.g = n, k, g
+
+    def __getitem__(self, i):
+        return self.sets[i % len(self.sets)]
+
+
+def copies_for(nbytes):
+    return max(2, math.ceil(ROTATE_BYTES / nbytes))
+
+
+def gpu_lead(torch, ms=30.0):
+    """Queue a GPU-side wait so the host can enqueue ahead of the device:
+    the timed kernels then run back to back, without host gaps."""
+    try:
+        torch.cuda._sleep(int(ms * 1e-3 * 2.1e9))
+    except Exception:   # pragma: no cover - torch without _sleep
+        pass
+
+
+def run(args):
+    import torch
+
+    import synth_inputs as si
+    import weight_only_quantized_w8a16_amd as qg
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU (HIP device)")
+    torch.cuda.init()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device: {props.name} ({props.gcnArchName}), CUs {props.multi_processor_count}")
+
+    # ---- decode workload ------------------------------------------------------
+    t0 = time.time()
+    decode_w = {}
+    for n in DECODE_N:
+        b = w4_bytes(1, n, DECODE_K, DECODE_G)
+        decode_w[n] = Weights(torch, qg, si, n, DECODE_K, DECODE_G, "cfg1", copies_for(b))
+    acts = {m: torch.from_numpy(si.activations(m, DECODE_K, si.seed_of("cfg1", "a", m, DECODE_K))
+                                .view("int16")).view(torch.bfloat16).to(dev) for m in (1, 2, 4, 8)}
+    outs = {(m, n): torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            for (m, n) in SWEEP + [(1, n) for n in DECODE_N]}
+    torch.cuda.synchronize()
+    log(f"decode inputs ready in {time.time() - t0:.1f}s "
+        f"({sum(len(w.sets) for w in decode_w.values())} weight copies)")
+
+    def gemv(m, n, i):
+        B, S, Z = decode_w[n][i]
+        qg.gemm_w4a16(acts[m], B, S, Z, None, DECODE_G, out=outs[(m, n)])
+
+    # warmup
+    for i in range(args.warmup):
+        for n in DECODE_N:
+            gemv(1, n, i)
+    torch.cuda.synchronize()
+
+    # timed region: K steps, each one GEMV per shape; events around every
+    # launch on the launch stream (torch's current stream).
+    stream = torch.cuda.current_stream()
+    K = args.steps
+    ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(K)] for n in DECODE_N}
+    region = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    torch.cuda.synchronize()
+    gpu_lead(torch)
+    h0 = time.perf_counter()
+    region[0].record(stream)
+    for i in range(K):
+        for n in DECODE_N:
+            ev[n][i][0].record(stream)
+            gemv(1, n, args.warmup + i)
+            ev[n][i][1].record(stream)
+    region[1].record(stream)
+    torch.cuda.synchronize()
+    host_s = time.perf_counter() - h0
+    region_ms = region[0].elapsed_time(region[1])
+    per_launch_ms = {n: [a.elapsed_time(b) for a, b in ev[n]] for n in DECODE_N}
+    step_bytes = sum(w4_bytes(1, n, DECODE_K, DECODE_G) for n in DECODE_N)
+    ms_per_step = region_ms / K
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    per_shape = {}
+    for n in DECODE_N:
+        mean_ms = sum(per_launch_ms[n]) / K
+        b = w4_bytes(1, n, DECODE_K, DECODE_G)
+        per_shape[str(n)] = {"us": round(mean_ms * 1e3, 2),
+                             "GBps": round(b / (mean_ms * 1e-3) / 1e9, 1),
+                             "frac": round(b / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 3)}
+    log(f"decode M=1 step: {ms_per_step * 1e3:.1f} us on the device clock "
+        f"({host_s / K * 1e3:.1f} us host), {value:.0f} GB/s; per shape {per_shape}")
+
+    lm_ms = sum(per_launch_ms[131072]) / K
+    lm_bytes = w4_bytes(1, 131072, DECODE_K, DECODE_G)
+    achieved = lm_bytes / (lm_ms * 1e-3) / 1e9
+    traffic = load_traffic()
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic,
+                "kernel": "k_decode_w4 (M=1, N=131072, K=2048, g=64)",
+                "bytes_per_launch": lm_bytes, "mean_launch_us": round(lm_ms * 1e3, 2)}
+
+    # ---- full decode sweep (M = 1, 2, 4, 8) -----------------------------------
+    sweep = {}
+    if not args.quick:
+        reps = max(10, K // 2)
+        for (m, n) in SWEEP:
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(reps)]
+            gpu_lead(torch, 5.0)
+            for i in range(reps):
+                evs[i][0].record(stream)
+                gemv(m, n, 7 * i + m)
+                evs[i][1].record(stream)
+            torch.cuda.synchronize()
+            ms = sum(a.elapsed_time(b) for a, b in evs) / reps
+            b = w4_bytes(m, n, DECODE_K, DECODE_G)
+            sweep[f"M{m}_N{n}"] = {"us": round(ms * 1e3, 2),
+                                   "GBps": round(b / (ms * 1e-3) / 1e9, 1),
+                                   "frac": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 3)}
+        log(f"decode sweep: {sweep}")
+    del decode_w
+    torch.cuda.empty_cache()
+
+    # ---- prefill M=512 ------------------------------------------------------------
+    prefill = None
+    if not args.no_prefill:
+        A = torch.from_numpy(si.activations(512, 2048, si.seed_of("cfg3", "a", 512, 2048))
+                             .view("int16")).view(torch.bfloat16).to(dev)
+        shapes = {}
+        tot_flop, tot_ms = 0.0, 0.0
+        for (m, n, g) in PREFILL:
+            w = Weights(torch, qg, si, n, 2048, g, "cfg3", 2, bias=True)
+            C = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            for i in range(3):
+                B, S, Z = w[i]
+                qg.gemm_w4a16(A, B, S, Z, w.bias, g, out=C)
+            reps = max(10, K // 2)
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(reps)]
+            gpu_lead(torch, 5.0)
+            for i in range(reps):
+                B, S, Z = w[i]
+                evs[i][0].record(stream)
+                qg.gemm_w4a16(A, B, S, Z, w.bias, g, out=C)
+                evs[i][1].record(stream)
+            torch.cuda.synchronize()
+            ms = sum(a.elapsed_time(b) for a, b in evs) / reps
+            flop = 2.0 * m * n * 2048
+            tot_flop += flop
+            tot_ms += ms
+            shapes[f"N{n}_g{g}"] = {"us": round(ms * 1e3, 1),
+                                    "TFLOPS": round(flop / (ms * 1e-3) / 1e12, 1),
+                                    "frac": round(flop / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 3)}
+            del w, C
+        tf = tot_flop / (tot_ms * 1e-3) / 1e12
+        prefill = {"metric": "prefill TFLOPS at M=512 (W4A16, K=2048, fp16 bias)",
+                   "value": round(tf, 1), "unit": "TFLOP/s",
+                   "roofline": {"bound": "mfma", "achieved": round(tf, 1),
+                                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None},
+                   "shapes": shapes}
+        log(f"prefill: {prefill}")
+        torch.cuda.empty_cache()
+
+    # ---- MoE ------------------------------------------------------------------------
+    moe = None
+    if not args.no_moe:
+        T, H, I, E, TK, G = 2048, 2048, 1408, 64, 6, 64
+        p = si.moe_problem(T, H, I, E, TK, G, tag="cfg4")
+
+        def up16(a):
+            return torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)
+
+        x = up16(p.x)
+        lg = torch.from_numpy(p.logits).to(dev)
+        w1 = torch.stack([qg.repack_w4(torch.from_numpy(p.w1[e]).to(dev)) for e in range(E)])
+        w2 = torch.stack([qg.repack_w4(torch.from_numpy(p.w2[e]).to(dev)) for e in range(E)])
+        s1, z1, s2, z2 = (up16(a) for a in (p.s1, p.z1, p.s2, p.z2))
+        ws = torch.empty(qg.moe_workspace_size(T, H, I, E, TK), dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            qg.moe_grouped(x, lg, w1, s1, z1, w2, s2, z2, TK, G, workspace=ws)
+        reps = max(5, K // 5)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        torch.cuda.synchronize()
+        gpu_lead(torch, 5.0)
+        for i in range(reps):
+            evs[i][0].record(stream)
+            qg.moe_grouped(x, lg, w1, s1, z1, w2, s2, z2, TK, G, workspace=ws)
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        ms = sum(a.elapsed_time(b) for a, b in evs) / reps
+        flop = 2.0 * T * TK * (2 * I * H + H * I)
+        wbytes = E * (w4_bytes(0, 2 * I, H, G) + w4_bytes(0, H, I, G))
+        moe = {"config": "T=2048 H=2048 I=1408 E=64 top-6 g=64", "us": round(ms * 1e3, 1),
+               "TFLOPS": round(flop / (ms * 1e-3) / 1e12, 1),
+               "weight_GBps": round(wbytes / (ms * 1e-3) / 1e9, 1)}
+        log(f"moe: {moe}")
+        del w1, w2, ws
+        torch.cuda.empty_cache()
+
+    # ---- CPU oracle baseline -----------------------------------------------------
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        oracle.lib()
+        probs = []
+        for n in DECODE_N:
+            packed, s, z, _ = si.w4_weights(n, DECODE_K, DECODE_G,
+                                            si.seed_of("cfg1", "w", n, DECODE_K, DECODE_G))
+            probs.append((n, packed, s, z))
+        A1 = si.activations(1, DECODE_K, si.seed_of("cfg1", "a", 1, DECODE_K))
+        passes, t_cpu = 0, 0.0
+        while t_cpu < args.cpu_seconds or passes == 0:
+            c0 = time.perf_counter()
+            for (n, packed, s, z) in probs:
+                oracle.gemm_w4(A1, packed, s, z, DECODE_G)
+            t_cpu += time.perf_counter() - c0
+            passes += 1
+        cpu_val = passes * step_bytes / t_cpu / 1e9
+        cpu = {"value": round(cpu_val, 2), "unit": "GB/s", "cores": oracle.threads(),
+               "kind": "oracle",
+               "sample": f"{passes} full passes of the M=1 decode step "
+                         f"(N={DECODE_N}, K=2048, g=64) in {t_cpu:.1f}s, fp64 accumulation"}
+        log(f"cpu baseline: {cpu}")
+
+    result = {
+        "metric": "decode GEMV HBM GB/s (% of peak) at M=1; prefill TFLOPS (% MFMA peak) at M=512",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "frac_of_peak": round(value / HBM_PEAK_GBS, 4),
+        "config": {"workload": "W4A16 decode GEMV, M=1, K=2048, group 64, bf16 in/out, "
+                               "N in {2048, 3072, 13312, 131072}",
+                   "global_batch": 1, "parallelism": "none (one GPU)",
+                   "weights_rotated_bytes": ROTATE_BYTES},
+        "per_shape": per_shape,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "sweep": sweep,
+        "prefill": prefill,
+        "moe": moe,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-moe", action="store_true")
+    ap.add_argument("--quick", action="store_true", help="skip the M sweep")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only; there is no multi-GPU path to run "
+              "(the GEMM shards along N without communication, so one GPU's shard is the "
+              "kernel measured here). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    run(args)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,79 @@
+"""GPU parity, part 3: the top-k MoE against the CPU oracle.
+
+Routing ids must equal the oracle's exactly (same fp32 comparisons, ties to
+the lower expert); weights and outputs within tolerance."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth_inputs as si
+import weight_only_quantized_w8a16_amd as qg
+from helpers import BF16, FP16, TOL, rel_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run_moe(p):
+    dev = "cuda"
+    x = to_dev(p.x, p.dtype)
+    lg = torch.from_numpy(p.logits).to(dev)
+    w1 = torch.stack([qg.repack_w4(to_dev(p.w1[e])) for e in range(p.experts)])
+    w2 = torch.stack([qg.repack_w4(to_dev(p.w2[e])) for e in range(p.experts)])
+    s1, z1, s2, z2 = (to_dev(a, p.dtype) for a in (p.s1, p.z1, p.s2, p.z2))
+    out, ids, w = qg.moe_grouped(x, lg, w1, s1, z1, w2, s2, z2, p.topk, p.group,
+                                 return_routing=True)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy()
+
+
+def check(p, tokens=None, tol=TOL[BF16]):
+    out, ids, w = run_moe(p)
+    ref, rids, rw = oracle.moe(p.x, p.logits, p.w1, p.s1, p.z1, p.w2, p.s2, p.z2, p.topk,
+                               p.group, p.dtype, tokens=tokens)
+    assert np.array_equal(ids, rids)
+    np.testing.assert_allclose(w, rw, rtol=2e-6, atol=1e-7)
+    sel = np.arange(p.tokens) if tokens is None else np.asarray(tokens)
+    err = rel_err(out[sel], ref)
+    assert err <= tol, err
+    return out
+
+
+@pytest.mark.parametrize("T,H,I,E,k,g", [
+    (4, 128, 128, 4, 2, 64), (33, 256, 256, 16, 4, 64), (1, 256, 128, 8, 8, 128),
+    (64, 256, 384, 8, 1, 64), (200, 128, 128, 64, 6, 64), (130, 384, 256, 4, 2, 128),
+])
+def test_moe_small_full(T, H, I, E, k, g):
+    p = si.moe_problem(T, H, I, E, k, g, tag="moe-small")
+    check(p)
+
+
+def test_moe_fp16():
+    p = si.moe_problem(48, 256, 256, 8, 2, 64, tag="moe-f16", dtype=FP16)
+    check(p, tol=TOL[FP16] * 3)
+
+
+def test_moe_identical_experts_give_dense_ffn():
+    p = si.moe_problem(40, 256, 128, 8, 3, 64, tag="moe-same")
+    for a in (p.w1, p.s1, p.z1, p.w2, p.s2, p.z2):
+        a[1:] = a[0]
+    out, _, _ = run_moe(p)
+    ref, _, _ = oracle.moe(p.x, p.logits, p.w1, p.s1, p.z1, p.w2, p.s2, p.z2, 3, 64)
+    assert rel_err(out, ref) <= TOL[BF16]
+
+
+def test_moe_forced_routes_and_empty_experts():
+    p = si.moe_problem(16, 128, 128, 8, 2, 64, tag="moe-forced")
+    p.logits[:] = 0.0
+    p.logits[:, 5] = 3.0           # every token picks 5 first
+    p.logits[:, 2] = 2.0           # then 2; experts 0,1,3,4,6,7 receive no rows
+    out, ids, w = run_moe(p)
+    assert (ids[:, 0] == 5).all() and (ids[:, 1] == 2).all()
+    check(p)
+
+
+def test_moe_full_size_sampled_tokens():
+    # 2048 tokens, hidden 2048, inter 1408, 64 experts, top-6, g=64
+    p = si.moe_problem(2048, 2048, 1408, 64, 6, 64, tag="cfg4")
+    toks = np.unique(np.concatenate([[0, 1, 2047], np.random.default_rng(4).integers(0, 2048, 21)]))
+    check(p, tokens=toks)
