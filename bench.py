@@ -104,7 +104,7 @@ def copies_for(nbytes):
     return max(2, math.ceil(ROTATE_BYTES / nbytes))
 
 
-def gpu_lead(torch, ms=30.0):
+def gpu_lead(torch, ms=20.0):
     """Queue a GPU-side wait so the host can enqueue ahead of the device:
     the timed kernels then run back to back, without host gaps."""
     try:
@@ -151,41 +151,52 @@ def run(args):
             gemv(1, n, i)
     torch.cuda.synchronize()
 
-    # timed region: K steps, each one GEMV per shape; events around every
-    # launch on the launch stream (torch's current stream).
+    # Timed region: K steps, each one GEMV per shape, back to back on torch's
+    # current stream (the stream the library launches on), bracketed by two
+    # HIP events.  A GPU-side wait queued first lets the host run ahead, so
+    # the region holds no host gaps.
     stream = torch.cuda.current_stream()
     K = args.steps
-    ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(K)] for n in DECODE_N}
-    region = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-    torch.cuda.synchronize()
-    gpu_lead(torch)
-    h0 = time.perf_counter()
-    region[0].record(stream)
-    for i in range(K):
+
+    def timed(fn, reps, calls_per_rep=1):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        # the lead outlasts the host's enqueue time (generously 0.2 ms a call);
+        # the start event is taken when the wait ends, so it adds no time.
+        gpu_lead(torch, 2.0 + 0.2 * reps * calls_per_rep)
+        a.record(stream)
+        for i in range(reps):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+    def step(i):
         for n in DECODE_N:
-            ev[n][i][0].record(stream)
             gemv(1, n, args.warmup + i)
-            ev[n][i][1].record(stream)
-    region[1].record(stream)
-    torch.cuda.synchronize()
+
+    h0 = time.perf_counter()
+    region_ms = timed(step, K, len(DECODE_N))
     host_s = time.perf_counter() - h0
-    region_ms = region[0].elapsed_time(region[1])
-    per_launch_ms = {n: [a.elapsed_time(b) for a, b in ev[n]] for n in DECODE_N}
     step_bytes = sum(w4_bytes(1, n, DECODE_K, DECODE_G) for n in DECODE_N)
     ms_per_step = region_ms / K
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    per_shape = {}
-    for n in DECODE_N:
-        mean_ms = sum(per_launch_ms[n]) / K
-        b = w4_bytes(1, n, DECODE_K, DECODE_G)
-        per_shape[str(n)] = {"us": round(mean_ms * 1e3, 2),
-                             "GBps": round(b / (mean_ms * 1e-3) / 1e9, 1),
-                             "frac": round(b / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 3)}
-    log(f"decode M=1 step: {ms_per_step * 1e3:.1f} us on the device clock "
-        f"({host_s / K * 1e3:.1f} us host), {value:.0f} GB/s; per shape {per_shape}")
 
-    lm_ms = sum(per_launch_ms[131072]) / K
+    # Per shape: the same launches, one shape at a time, back to back; the
+    # mean launch time is the region over the launch count.
+    per_shape, launch_ms = {}, {}
+    for n in DECODE_N:
+        ms = timed(lambda i, n=n: gemv(1, n, 3 * i + 1), K) / K
+        b = w4_bytes(1, n, DECODE_K, DECODE_G)
+        launch_ms[n] = ms
+        per_shape[str(n)] = {"us": round(ms * 1e3, 2),
+                             "GBps": round(b / (ms * 1e-3) / 1e9, 1),
+                             "frac": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 3)}
+    log(f"decode M=1 step: {ms_per_step * 1e3:.1f} us on the device clock "
+        f"({host_s / K * 1e6:.0f} us host incl. the lead), {value:.0f} GB/s; "
+        f"per shape {per_shape}")
+
+    lm_ms = launch_ms[131072]
     lm_bytes = w4_bytes(1, 131072, DECODE_K, DECODE_G)
     achieved = lm_bytes / (lm_ms * 1e-3) / 1e9
     traffic = load_traffic()
@@ -200,15 +211,7 @@ def run(args):
     if not args.quick:
         reps = max(10, K // 2)
         for (m, n) in SWEEP:
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(reps)]
-            gpu_lead(torch, 5.0)
-            for i in range(reps):
-                evs[i][0].record(stream)
-                gemv(m, n, 7 * i + m)
-                evs[i][1].record(stream)
-            torch.cuda.synchronize()
-            ms = sum(a.elapsed_time(b) for a, b in evs) / reps
+            ms = timed(lambda i, m=m, n=n: gemv(m, n, 7 * i + m), reps) / reps
             b = w4_bytes(m, n, DECODE_K, DECODE_G)
             sweep[f"M{m}_N{n}"] = {"us": round(ms * 1e3, 2),
                                    "GBps": round(b / (ms * 1e-3) / 1e9, 1),
@@ -231,16 +234,11 @@ def run(args):
                 B, S, Z = w[i]
                 qg.gemm_w4a16(A, B, S, Z, w.bias, g, out=C)
             reps = max(10, K // 2)
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(reps)]
-            gpu_lead(torch, 5.0)
-            for i in range(reps):
+
+            def call(i, w=w, C=C, g=g):
                 B, S, Z = w[i]
-                evs[i][0].record(stream)
                 qg.gemm_w4a16(A, B, S, Z, w.bias, g, out=C)
-                evs[i][1].record(stream)
-            torch.cuda.synchronize()
-            ms = sum(a.elapsed_time(b) for a, b in evs) / reps
+            ms = timed(call, reps) / reps
             flop = 2.0 * m * n * 2048
             tot_flop += flop
             tot_ms += ms
@@ -276,16 +274,8 @@ def run(args):
         for _ in range(3):
             qg.moe_grouped(x, lg, w1, s1, z1, w2, s2, z2, TK, G, workspace=ws)
         reps = max(5, K // 5)
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(reps)]
-        torch.cuda.synchronize()
-        gpu_lead(torch, 5.0)
-        for i in range(reps):
-            evs[i][0].record(stream)
-            qg.moe_grouped(x, lg, w1, s1, z1, w2, s2, z2, TK, G, workspace=ws)
-            evs[i][1].record(stream)
-        torch.cuda.synchronize()
-        ms = sum(a.elapsed_time(b) for a, b in evs) / reps
+        ms = timed(lambda i: qg.moe_grouped(x, lg, w1, s1, z1, w2, s2, z2, TK, G, workspace=ws),
+                   reps, 4) / reps
         flop = 2.0 * T * TK * (2 * I * H + H * I)
         wbytes = E * (w4_bytes(0, 2 * I, H, G) + w4_bytes(0, H, I, G))
         moe = {"config": "T=2048 H=2048 I=1408 E=64 top-6 g=64", "us": round(ms * 1e3, 1),

@@ -129,3 +129,36 @@ def test_repeated_calls_are_deterministic():
     a = gpu_w4(p)
     b = gpu_w4(p)
     assert np.array_equal(a, b)
+
+
+# -- the streaming decode kernel (M <= 2 with many channel tiles) and its
+#    fallbacks: unaligned scale rows, K not a multiple of 512, bias.
+@pytest.mark.parametrize("m,n,k,g,bias", [
+    (1, 65536, 2048, 64, False), (2, 65536, 2048, 128, True), (1, 65536, 512, 64, True),
+    (2, 65536, 4096, 64, False), (1, 65536, 1152, 128, False), (3, 65536, 2048, 64, True),
+])
+def test_large_n_decode(m, n, k, g, bias):
+    p = si.w4_problem(m, n, k, g, tag="stream", bias_dtype=FP16 if bias else si.NONE)
+    C = gpu_w4(p)
+    r, c = sample_pairs(m, n, seed=n + k + g)
+    ref = oracle.gemm_w4_at(p.A, p.packed, p.scale, p.zero, g, r, c, BF16, p.bias,
+                            FP16 if bias else si.NONE)
+    assert rel_err(C[r, c], ref) <= TOL[BF16]
+
+
+def test_unaligned_scale_rows_fall_back():
+    p = si.w4_problem(1, 65536, 2048, 64, tag="unal")
+    A = to_dev(p.A, BF16)
+    tiled = qg.repack_w4(to_dev(p.packed))
+
+    def shifted(bits):
+        buf = torch.empty(bits.size + 1, dtype=torch.bfloat16, device="cuda")
+        view = buf[1:].view(bits.shape)              # 2-byte aligned, not 16
+        view.copy_(to_dev(bits, BF16))
+        return view
+    S, Z = shifted(p.scale), shifted(p.zero)
+    assert S.data_ptr() % 16 != 0
+    C = qg.gemm_w4a16(A, tiled, S, Z, None, 64).float().cpu().numpy()
+    r, c = sample_pairs(1, 65536, seed=3)
+    ref = oracle.gemm_w4_at(p.A, p.packed, p.scale, p.zero, 64, r, c)
+    assert rel_err(C[r, c], ref) <= TOL[BF16]

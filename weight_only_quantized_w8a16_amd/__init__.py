@@ -35,7 +35,7 @@ def dtype_code(dt: Optional[torch.dtype]) -> int:
 def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise QGemmError(name, 1, f"{name} must be a device tensor (got {t.device})")
     if not t.is_contiguous():
         raise QGemmError(name, 2, f"{name} must be contiguous")
@@ -43,11 +43,17 @@ def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
 
 
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
+
+
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 def _stream(t: torch.Tensor):
-    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+    """Raw handle of torch's current stream on t's device (a hipStream_t)."""
+    if _raw_stream is not None:
+        return _raw_stream(t.get_device())
+    return torch.cuda.current_stream(t.device).cuda_stream
 
 
 # -- load-side repack -------------------------------------------------------

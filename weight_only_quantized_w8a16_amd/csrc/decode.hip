@@ -29,11 +29,14 @@ namespace qg {
 namespace {
 
 // Activation fragment of v_mfma_f32_16x16x32: row m = lane % 16 holds the
-// eight values k0 + 8 * (lane / 16) + 0..7.  Rows >= M are zero.
+// eight values k0 + 8 * (lane / 16) + 0..7.  Rows >= M read row M - 1 (no
+// divergent branch) and are zeroed.
 __device__ __forceinline__ u32x4 load_afrag(const uint16_t *__restrict__ A, int M, int K, int m,
                                             int k) {
-  if (m < M) return *reinterpret_cast<const u32x4 *>(A + static_cast<size_t>(m) * K + k);
-  return u32x4{0u, 0u, 0u, 0u};
+  const int row = m < M ? m : M - 1;
+  const u32x4 v = *reinterpret_cast<const u32x4 *>(A + static_cast<size_t>(row) * K + k);
+  const uint32_t keep = m < M ? 0xFFFFFFFFu : 0u;
+  return u32x4{v.x & keep, v.y & keep, v.z & keep, v.w & keep};
 }
 
 // Sum the per-wave partials in LDS, add bias, round, store rows < M.
@@ -56,10 +59,52 @@ __device__ __forceinline__ void reduce_store(float *red, int nwaves, const uint1
   }
 }
 
+// A chunk's NG consecutive 16-bit scale (or zero) values of one row, kept as
+// packed words until use: one vector load when the row offset is aligned to
+// it, else one load per value.
+template <int NG>
+struct Groups {
+  static constexpr int W = (NG + 1) / 2;
+  uint32_t w[W];
+};
+
+template <int NG, bool VEC>
+__device__ __forceinline__ Groups<NG> load_groups(const uint16_t *__restrict__ p) {
+  Groups<NG> g;
+  if constexpr (VEC && NG == 8) {
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(p);
+    g.w[0] = v.x; g.w[1] = v.y; g.w[2] = v.z; g.w[3] = v.w;
+  } else if constexpr (VEC && NG == 4) {
+    const u32x2 v = *reinterpret_cast<const u32x2 *>(p);
+    g.w[0] = v.x; g.w[1] = v.y;
+  } else if constexpr (VEC && NG == 2) {
+    g.w[0] = *reinterpret_cast<const uint32_t *>(p);
+  } else {
+#pragma unroll
+    for (int i = 0; i < Groups<NG>::W; ++i) {
+      const uint32_t lo = p[2 * i];
+      const uint32_t hi = (2 * i + 1 < NG) ? p[2 * i + 1] : 0u;
+      g.w[i] = lo | (hi << 16);
+    }
+  }
+  return g;
+}
+
+template <int ACT, int NG>
+__device__ __forceinline__ float group_value(const Groups<NG> &g, int i) {
+  const uint32_t w = g.w[i >> 1];
+  return bits_to_f32<ACT>(static_cast<uint16_t>((i & 1) ? (w >> 16) : (w & 0xFFFFu)));
+}
+
 }  // namespace
 
-template <int ACT, int G, int BPW, int NT>
-__global__ __launch_bounds__(512) void k_decode_w4(const uint16_t *__restrict__ A,
+// Launch bounds follow the plan: BPW 1 runs up to 16 waves, BPW 2 up to 8,
+// BPW 4 up to 4, so the register budget grows with the chunk size.
+template <int BPW>
+constexpr int decode_threads() { return BPW == 1 ? 1024 : (BPW == 2 ? 512 : 256); }
+
+template <int ACT, int G, int BPW, int NT, bool VEC>
+__global__ __launch_bounds__(decode_threads<BPW>()) void k_decode_w4(const uint16_t *__restrict__ A,
                                                    const u32x4 *__restrict__ Bt,
                                                    const uint16_t *__restrict__ S,
                                                    const uint16_t *__restrict__ Z,
@@ -99,19 +144,22 @@ __global__ __launch_bounds__(512) void k_decode_w4(const uint16_t *__restrict__ 
         for (int tt = 0; tt < TPG; ++tt) d = mfma16x16x32<ACT>(af[b][h * TPG + tt], ones, d);
         sg[b * GPB + h] = d;
       }
+    // Issue every weight and scale load of the NT tiles before any math, so
+    // the workgroup pays one memory round trip per chunk, not one per tile.
+    u32x4 bw[NT][BPW];
+    Groups<NG> sv[NT], zv[NT];
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
       const int nt = nt0 + i;
-      u32x4 bw[BPW];
 #pragma unroll
-      for (int b = 0; b < BPW; ++b) bw[b] = Bt[(static_cast<size_t>(nt) * nb + kb0 + b) * 64 + lane];
+      for (int b = 0; b < BPW; ++b)
+        bw[i][b] = __builtin_nontemporal_load(&Bt[(static_cast<size_t>(nt) * nb + kb0 + b) * 64 + lane]);
       const size_t srow = static_cast<size_t>(nt * 16 + nl) * ngroups + kb0 * GPB;
-      float sv[NG], zv[NG];
+      sv[i] = load_groups<NG, VEC>(S + srow);
+      zv[i] = load_groups<NG, VEC>(Z + srow);
+    }
 #pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        sv[g] = bits_to_f32<ACT>(S[srow + g]);
-        zv[g] = bits_to_f32<ACT>(Z[srow + g]);
-      }
+    for (int i = 0; i < NT; ++i) {
 #pragma unroll
       for (int b = 0; b < BPW; ++b)
 #pragma unroll
@@ -120,11 +168,11 @@ __global__ __launch_bounds__(512) void k_decode_w4(const uint16_t *__restrict__ 
 #pragma unroll
           for (int tt = 0; tt < TPG; ++tt) {
             const int t = h * TPG + tt;
-            d = mfma16x16x32<ACT>(af[b][t], w4_word_to_operand<ACT>(bw[b][t]), d);
+            d = mfma16x16x32<ACT>(af[b][t], w4_word_to_operand<ACT>(bw[i][b][t]), d);
           }
           const int g = b * GPB + h;
-          const float s = sv[g];
-          const float zc = zv[g] - kOff * s;
+          const float s = group_value<ACT, NG>(sv[i], g);
+          const float zc = group_value<ACT, NG>(zv[i], g) - kOff * s;
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[i][r] += s * d[r] + zc * sg[g][r];
         }
@@ -140,7 +188,7 @@ __global__ __launch_bounds__(512) void k_decode_w4(const uint16_t *__restrict__ 
 }
 
 template <int ACT, int BPW, int NT>
-__global__ __launch_bounds__(512) void k_decode_w8(const uint16_t *__restrict__ A,
+__global__ __launch_bounds__(decode_threads<BPW>()) void k_decode_w8(const uint16_t *__restrict__ A,
                                                    const u32x4 *__restrict__ Bt,
                                                    const uint16_t *__restrict__ S,
                                                    const uint16_t *__restrict__ bias, int bias_dt,
@@ -162,21 +210,22 @@ __global__ __launch_bounds__(512) void k_decode_w8(const uint16_t *__restrict__ 
     for (int b = 0; b < BPW; ++b)
 #pragma unroll
       for (int t = 0; t < 2; ++t) af[b][t] = load_afrag(A, M, K, nl, (kb0 + b) * 64 + 32 * t + 8 * j);
+    u32x4 bw[NT][BPW];
 #pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      const int nt = nt0 + i;
-      u32x4 bw[BPW];
+    for (int i = 0; i < NT; ++i)
 #pragma unroll
-      for (int b = 0; b < BPW; ++b) bw[b] = Bt[(static_cast<size_t>(nt) * nb + kb0 + b) * 64 + lane];
+      for (int b = 0; b < BPW; ++b)
+        bw[i][b] = __builtin_nontemporal_load(&Bt[(static_cast<size_t>(nt0 + i) * nb + kb0 + b) * 64 + lane]);
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
 #pragma unroll
       for (int b = 0; b < BPW; ++b)
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          u32x4 op = (ACT == kFP16) ? w8_run_to_f16(bw[b][2 * t], bw[b][2 * t + 1])
-                                    : w8_run_to_bf16(bw[b][2 * t], bw[b][2 * t + 1]);
+          u32x4 op = (ACT == kFP16) ? w8_run_to_f16(bw[i][b][2 * t], bw[i][b][2 * t + 1])
+                                    : w8_run_to_bf16(bw[i][b][2 * t], bw[i][b][2 * t + 1]);
           acc[i] = mfma16x16x32<ACT>(af[b][t], op, acc[i]);
         }
-    }
   }
   constexpr int PER = NT * 256;
 #pragma unroll
@@ -185,6 +234,137 @@ __global__ __launch_bounds__(512) void k_decode_w8(const uint16_t *__restrict__ 
     for (int r = 0; r < 4; ++r) red[wave * PER + i * 256 + r * 64 + lane] = acc[i][r];
   __syncthreads();
   reduce_store<ACT, NT>(red, nwaves, bias, bias_dt, S, C, M, N, nt0);
+}
+
+// ---------------------------------------------------------------------------
+// Streaming variant for many channel tiles (large N).  Each wave owns whole
+// tiles of 16 channels over all of K, and consecutive waves of the grid take
+// consecutive tiles, so at any moment the running waves sweep one contiguous
+// window of the tiled weights -- the access pattern that streams best from
+// HBM.  The activations (rows < M) and their per-group sums S_g live in LDS,
+// written once per workgroup; no cross-wave reduction is needed.  K is walked
+// in segments of SEG 128-k blocks whose codes are loaded together.
+// ---------------------------------------------------------------------------
+// R: accumulator rows per lane that can hold a live output (lane rows are
+// m = 4 * (lane / 16) + r): M = 1 needs r = 0 only, M = 2 r < 2.  Only the
+// live rows get the per-group scale update, which is most of the VALU work.
+template <int ACT, int G, int SEG, int R>
+__global__ __launch_bounds__(256) void k_decode_w4_stream(const uint16_t *__restrict__ A,
+                                                          const u32x4 *__restrict__ Bt,
+                                                          const uint16_t *__restrict__ S,
+                                                          const uint16_t *__restrict__ Z,
+                                                          const uint16_t *__restrict__ bias,
+                                                          int bias_dt, uint16_t *__restrict__ C,
+                                                          int M, int N, int K) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  constexpr int GPB = 128 / G;           // groups per block
+  constexpr int TPG = 4 / GPB;           // MFMA steps per group
+  constexpr int NGS = SEG * GPB;         // groups per segment
+  constexpr float kOff = w4_operand_offset<ACT>() + 8.0f;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nl = lane & 15, j = lane >> 4;
+  const int nb = K >> 7, ngroups = K / G, ntiles = N >> 4;
+  const int arow = 2 * K + 16;           // padded LDS row (bytes)
+  const int Mr = M < 16 ? M : 16;
+  float *sS = reinterpret_cast<float *>(lds + Mr * arow);   // [ngroups][16]
+
+  // Activation rows -> LDS (16-byte chunks), then S[g][m] = sum of a group.
+  for (int c = threadIdx.x; c < Mr * (K >> 3); c += blockDim.x) {
+    const int m = c / (K >> 3), k8 = c % (K >> 3);
+    *reinterpret_cast<u32x4 *>(lds + m * arow + k8 * 16) =
+        *reinterpret_cast<const u32x4 *>(A + static_cast<size_t>(m) * K + k8 * 8);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < ngroups * 16; e += blockDim.x) {
+    const int g = e >> 4, m = e & 15;
+    float acc = 0.f;
+    if (m < Mr) {
+      const uint16_t *row = reinterpret_cast<const uint16_t *>(lds + m * arow) + g * G;
+      for (int i = 0; i < G; ++i) acc += bits_to_f32<ACT>(row[i]);
+    }
+    sS[e] = acc;
+  }
+  __syncthreads();
+
+  const bool active = nl < Mr;           // this lane's activation row exists
+  const char *arow_p = lds + (active ? nl : 0) * arow + 16 * j;
+  const int total_waves = gridDim.x * (blockDim.x >> 6);
+  const int nseg = nb / SEG;
+  static_assert(R == 1 || R == 2, "streaming decode serves M <= 2");
+
+  // Codes and scales of one (tile, segment) item; all of an item's loads are
+  // issued together, then consumed.
+  struct Item {
+    u32x4 bw[SEG];
+    uint32_t sw[(NGS + 1) / 2], zw[(NGS + 1) / 2];
+  };
+  auto fetch = [&](int tile, int seg, Item &it) {
+    const int kb0 = seg * SEG;
+#pragma unroll
+    for (int b = 0; b < SEG; ++b)
+      it.bw[b] = __builtin_nontemporal_load(&Bt[(static_cast<size_t>(tile) * nb + kb0 + b) * 64 + lane]);
+    const size_t off = static_cast<size_t>(tile * 16 + nl) * ngroups + kb0 * GPB;
+    if constexpr (NGS >= 8) {
+#pragma unroll
+      for (int q = 0; q < NGS / 8; ++q) {
+        const u32x4 a = *reinterpret_cast<const u32x4 *>(S + off + 8 * q);
+        const u32x4 b = *reinterpret_cast<const u32x4 *>(Z + off + 8 * q);
+        it.sw[4 * q] = a.x; it.sw[4 * q + 1] = a.y; it.sw[4 * q + 2] = a.z; it.sw[4 * q + 3] = a.w;
+        it.zw[4 * q] = b.x; it.zw[4 * q + 1] = b.y; it.zw[4 * q + 2] = b.z; it.zw[4 * q + 3] = b.w;
+      }
+    } else if constexpr (NGS == 4) {
+      const u32x2 a = *reinterpret_cast<const u32x2 *>(S + off);
+      const u32x2 b = *reinterpret_cast<const u32x2 *>(Z + off);
+      it.sw[0] = a.x; it.sw[1] = a.y; it.zw[0] = b.x; it.zw[1] = b.y;
+    } else {
+      it.sw[0] = *reinterpret_cast<const uint32_t *>(S + off);
+      it.zw[0] = *reinterpret_cast<const uint32_t *>(Z + off);
+    }
+  };
+
+  for (int tile = blockIdx.x * (blockDim.x >> 6) + wave; tile < ntiles; tile += total_waves) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int seg = 0; seg < nseg; ++seg) {
+      Item cur;
+      fetch(tile, seg, cur);
+      const int kb0 = seg * SEG;
+#pragma unroll
+      for (int b = 0; b < SEG; ++b)
+#pragma unroll
+        for (int h = 0; h < GPB; ++h) {
+          f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int tt = 0; tt < TPG; ++tt) {
+            const int t = h * TPG + tt;
+            const int k = (kb0 + b) * 128 + 32 * t;          // + 8 j via arow_p
+            u32x4 af = {0u, 0u, 0u, 0u};
+            if (active) af = *reinterpret_cast<const u32x4 *>(arow_p + 2 * k);
+            d = mfma16x16x32<ACT>(af, w4_word_to_operand<ACT>(cur.bw[b][t]), d);
+          }
+          const int gl = b * GPB + h, g = kb0 * GPB + gl;
+          const uint32_t swd = cur.sw[gl >> 1], zwd = cur.zw[gl >> 1];
+          const float sc = bits_to_f32<ACT>(static_cast<uint16_t>((gl & 1) ? (swd >> 16) : (swd & 0xFFFFu)));
+          const float zc = bits_to_f32<ACT>(static_cast<uint16_t>((gl & 1) ? (zwd >> 16) : (zwd & 0xFFFFu))) - kOff * sc;
+          if constexpr (R == 1) {
+            acc[0] += sc * d[0] + zc * sS[g * 16 + 4 * j];
+          } else {
+            const f32x2 sg = *reinterpret_cast<const f32x2 *>(sS + g * 16 + 4 * j);
+            acc[0] += sc * d[0] + zc * sg[0];
+            acc[1] += sc * d[1] + zc * sg[1];
+          }
+        }
+    }
+    const int n = tile * 16 + nl;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int m = 4 * j + r;
+      if (m < M) {
+        float v = acc[r];
+        if (bias) v += bits_to_f32_dyn(bias[n], bias_dt);
+        C[static_cast<size_t>(m) * N + n] = f32_to_bits<ACT>(v);
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -197,46 +377,78 @@ struct DecodePlan {
 };
 
 // K is cut into chunks of `bpw` blocks shared out over `waves` waves; each
-// workgroup owns `nt` tiles of 16 channels.  Small N: thin chunks and many
-// waves, so that every byte is requested at once; large N: fat chunks and
-// several tiles per workgroup, so activation fragments are reused.
-DecodePlan plan_decode(int nb, int ntiles, int max_bpw) {
+// workgroup owns `nt` tiles of 16 channels.  Measured on MI355X at K = 2048:
+// two blocks per chunk (eight waves) beats one or four at every N, and two
+// tiles per workgroup pays off once there are a few hundred tiles.
+DecodePlan plan_decode(int nb, int ntiles) {
   DecodePlan p{1, 1, 1};
-  int bpw = ntiles >= 2048 ? 4 : (ntiles >= 512 ? 2 : 1);
-  if (bpw > max_bpw) bpw = max_bpw;
-  while (bpw > 1 && nb % bpw != 0) bpw >>= 1;
-  p.bpw = bpw;
-  const int nchunks = nb / bpw;
-  p.waves = nchunks < 8 ? nchunks : 8;
-  int nt = ntiles >= 4096 ? 4 : (ntiles >= 2048 ? 2 : 1);
-  while (nt > 1 && ntiles % nt != 0) nt >>= 1;
-  p.nt = nt;
+  p.bpw = nb % 2 == 0 ? 2 : 1;
+  const int nchunks = nb / p.bpw;
+  const int max_waves = 16 / p.bpw;
+  p.waves = nchunks < max_waves ? nchunks : max_waves;
+  p.nt = (ntiles >= 512 && ntiles % 2 == 0) ? 2 : 1;
   return p;
+}
+
+template <int ACT, int G, int R>
+hipError_t launch_stream(const GemmArgs &a, hipStream_t s) {
+  constexpr int SEG = 4;
+  const int ntiles = a.N >> 4;
+  const size_t lds = static_cast<size_t>(a.M) * (2 * a.K + 16) + static_cast<size_t>(a.K / G) * 64;
+  auto kern = k_decode_w4_stream<ACT, G, SEG, R>;
+  // One resident pass: 4 workgroups of 4 waves per CU on 256 CUs.
+  int grid = (ntiles + 3) / 4;
+  if (grid > 1024) grid = 1024;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, s, a.A, static_cast<const u32x4 *>(a.B),
+                     a.S, a.Z, a.bias, a.bias_dt, a.C, a.M, a.N, a.K);
+  return hipGetLastError();
+}
+
+template <int ACT, int G>
+hipError_t launch_stream_m(const GemmArgs &a, hipStream_t s) {
+  return a.M == 1 ? launch_stream<ACT, G, 1>(a, s) : launch_stream<ACT, G, 2>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_decode_w4(const GemmArgs &a, hipStream_t s) {
   const int nb = a.K >> 7, ntiles = a.N >> 4;
-  DecodePlan p = plan_decode(nb, ntiles, 4);
+  // Streaming kernel: one or two rows, many tiles, K a multiple of 512,
+  // scale rows 16-byte aligned, activations that fit in LDS.
+  const bool aligned16 =
+      ((reinterpret_cast<uintptr_t>(a.S) | reinterpret_cast<uintptr_t>(a.Z)) & 15) == 0 &&
+      ((a.K / a.group) % 8) == 0;
+  const bool fits = static_cast<size_t>(a.M) * (2 * static_cast<size_t>(a.K) + 16) +
+                        static_cast<size_t>(a.K / a.group) * 64 <= 64 * 1024;
+  if (a.M <= 2 && ntiles >= 4096 && aligned16 && fits && nb % 4 == 0) {
+    if (a.act == kBF16)
+      return a.group == 64 ? launch_stream_m<kBF16, 64>(a, s) : launch_stream_m<kBF16, 128>(a, s);
+    return a.group == 64 ? launch_stream_m<kFP16, 64>(a, s) : launch_stream_m<kFP16, 128>(a, s);
+  }
+  DecodePlan p = plan_decode(nb, ntiles);
   dim3 grid(ntiles / p.nt), block(64 * p.waves);
   size_t lds = static_cast<size_t>(p.waves) * p.nt * 256 * sizeof(float);
   const u32x4 *B = static_cast<const u32x4 *>(a.B);
-#define QG_DEC4(ACT_, G_, BPW_, NT_)                                                          \
-  hipLaunchKernelGGL((k_decode_w4<ACT_, G_, BPW_, NT_>), grid, block, lds, s, a.A, B, a.S, a.Z, \
-                     a.bias, a.bias_dt, a.C, a.M, a.N, a.K)
+  // Vector scale loads need the scale/zero bases aligned to a chunk's worth
+  // of groups (the row offsets are multiples of it by construction).
+  const int ng = p.bpw * (128 / a.group);
+  const uintptr_t amask = static_cast<uintptr_t>(2 * ng - 1);
+  const bool vec = ((reinterpret_cast<uintptr_t>(a.S) | reinterpret_cast<uintptr_t>(a.Z)) & amask) == 0;
+#define QG_DEC4(ACT_, G_, BPW_, NT_)                                                            \
+  do {                                                                                          \
+    if (vec)                                                                                    \
+      hipLaunchKernelGGL((k_decode_w4<ACT_, G_, BPW_, NT_, true>), grid, block, lds, s, a.A, B, \
+                         a.S, a.Z, a.bias, a.bias_dt, a.C, a.M, a.N, a.K);                      \
+    else                                                                                        \
+      hipLaunchKernelGGL((k_decode_w4<ACT_, G_, BPW_, NT_, false>), grid, block, lds, s, a.A,   \
+                         B, a.S, a.Z, a.bias, a.bias_dt, a.C, a.M, a.N, a.K);                   \
+  } while (0)
 #define QG_DEC4_NT(ACT_, G_, BPW_)                   \
-  switch (p.nt) {                                    \
-    case 4: QG_DEC4(ACT_, G_, BPW_, 4); break;       \
-    case 2: QG_DEC4(ACT_, G_, BPW_, 2); break;       \
-    default: QG_DEC4(ACT_, G_, BPW_, 1); break;      \
-  }
+  if (p.nt == 2) QG_DEC4(ACT_, G_, BPW_, 2);         \
+  else QG_DEC4(ACT_, G_, BPW_, 1);
 #define QG_DEC4_BPW(ACT_, G_)                        \
-  switch (p.bpw) {                                   \
-    case 4: QG_DEC4_NT(ACT_, G_, 4); break;          \
-    case 2: QG_DEC4_NT(ACT_, G_, 2); break;          \
-    default: QG_DEC4_NT(ACT_, G_, 1); break;         \
-  }
+  if (p.bpw == 2) { QG_DEC4_NT(ACT_, G_, 2) }        \
+  else { QG_DEC4_NT(ACT_, G_, 1) }
   if (a.act == kBF16) {
     if (a.group == 64) { QG_DEC4_BPW(kBF16, 64); } else { QG_DEC4_BPW(kBF16, 128); }
   } else {
@@ -250,7 +462,7 @@ hipError_t launch_decode_w4(const GemmArgs &a, hipStream_t s) {
 
 hipError_t launch_decode_w8(const GemmArgs &a, hipStream_t s) {
   const int nb = a.K >> 6, ntiles = a.N >> 4;
-  DecodePlan p = plan_decode(nb, ntiles, 4);
+  DecodePlan p = plan_decode(nb, ntiles);
   dim3 grid(ntiles / p.nt), block(64 * p.waves);
   size_t lds = static_cast<size_t>(p.waves) * p.nt * 256 * sizeof(float);
   const u32x4 *B = static_cast<const u32x4 *>(a.B);
@@ -258,17 +470,11 @@ hipError_t launch_decode_w8(const GemmArgs &a, hipStream_t s) {
   hipLaunchKernelGGL((k_decode_w8<ACT_, BPW_, NT_>), grid, block, lds, s, a.A, B, a.S, a.bias, \
                      a.bias_dt, a.C, a.M, a.N, a.K)
 #define QG_DEC8_NT(ACT_, BPW_)                       \
-  switch (p.nt) {                                    \
-    case 4: QG_DEC8(ACT_, BPW_, 4); break;           \
-    case 2: QG_DEC8(ACT_, BPW_, 2); break;           \
-    default: QG_DEC8(ACT_, BPW_, 1); break;          \
-  }
+  if (p.nt == 2) QG_DEC8(ACT_, BPW_, 2);             \
+  else QG_DEC8(ACT_, BPW_, 1);
 #define QG_DEC8_BPW(ACT_)                            \
-  switch (p.bpw) {                                   \
-    case 4: QG_DEC8_NT(ACT_, 4); break;              \
-    case 2: QG_DEC8_NT(ACT_, 2); break;              \
-    default: QG_DEC8_NT(ACT_, 1); break;             \
-  }
+  if (p.bpw == 2) { QG_DEC8_NT(ACT_, 2) }            \
+  else { QG_DEC8_NT(ACT_, 1) }
   if (a.act == kBF16) { QG_DEC8_BPW(kBF16); } else { QG_DEC8_BPW(kFP16); }
 #undef QG_DEC8_BPW
 #undef QG_DEC8_NT
