@@ -160,3 +160,25 @@ def test_empty_m_is_noop():
     A = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
     C = qg.gemm_w4a16(A, tiled, to_dev(p.scale, BF16), to_dev(p.zero, BF16), None, 64)
     assert tuple(C.shape) == (0, 128)
+
+
+# -- every prefill tile configuration, forced, on ragged M: bit-exact --------------
+
+@pytest.mark.parametrize("tile", ["X", "L", "M", "S"])
+@pytest.mark.parametrize("m", [1, 77, 300])
+def test_prefill_tiles_integer_exact(tile, m, monkeypatch):
+    n, k, group = 512, 640, 128
+    p = si.w4_exact_problem(m, n, k, group, seed=m + 3, dtype=BF16, bias_dtype=FP16)
+    Cref = oracle.gemm_w4(p.A, p.packed, p.scale, p.zero, group, BF16, p.bias, FP16)
+    monkeypatch.setenv("QGEMM_PREFILL_TILE", tile)
+    got = to_bits(_run_w4(p, "prefill"))
+    assert np.array_equal(got, _exact_expected(Cref, BF16))
+
+
+@pytest.mark.parametrize("tile", ["X", "L", "M", "S"])
+def test_prefill_tiles_w8_integer_exact(tile, monkeypatch):
+    p = si.w8_exact_problem(200, 256, 576, seed=9, dtype=FP16, bias_dtype=FP16)
+    Cref = oracle.gemm_w8(p.A, p.codes, p.scale, -1, FP16, p.bias, FP16)
+    monkeypatch.setenv("QGEMM_PREFILL_TILE", tile)
+    got = to_bits(_run_w8(p, "prefill"))
+    assert np.array_equal(got, _exact_expected(Cref, FP16))

@@ -8,6 +8,9 @@
 // multi-row batches; "[Misc][Kernel]: Add GPTQAllSpark Quantization": the
 // large-M regime), with the dequantized weight kept on chip instead of
 // written back to memory.
+#include <cstdlib>
+#include <string>
+
 #include "qg_launch.hpp"
 #include "tile_gemm.hpp"
 
@@ -32,6 +35,7 @@ __global__ __launch_bounds__(Cfg::NTHR) void k_prefill(TileProblem p, int tiles_
 
 namespace {
 
+using CfgX = TileCfg<256, 256, 2, 4>;   // 8 waves, 128x64 per wave
 using CfgL = TileCfg<256, 128, 4, 2>;   // 8 waves, 64x64 per wave
 using CfgM = TileCfg<128, 128, 2, 2>;   // 4 waves, 64x64 per wave
 using CfgS = TileCfg<64, 64, 2, 2>;     // 4 waves, 32x32 per wave
@@ -63,16 +67,25 @@ hipError_t run(const GemmArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Largest tile that still gives at least one workgroup per CU; smaller tiles
-// otherwise (256 CUs on MI355X).
+// Tile choice, from on-device sweeps at K = 2048: the biggest tile (fewest
+// LDS bytes per matrix-core instruction) once there are enough tiles to give
+// every CU about two; smaller tiles when the problem would leave CUs idle.
+// QGEMM_PREFILL_TILE=X|L|M|S forces one (tests and tuning).
 template <int ACT, int WBITS>
 hipError_t dispatch(const GemmArgs &a, hipStream_t s) {
   auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * (a.N / bn); };
-  const bool n128 = a.N % 128 == 0;
+  const bool n256 = a.N % 256 == 0, n128 = a.N % 128 == 0;
+  if (const char *o = std::getenv("QGEMM_PREFILL_TILE")) {
+    const std::string c(o);
+    if (c == "X" && n256) return run<CfgX, ACT, WBITS>(a, s);
+    if (c == "L" && n128) return run<CfgL, ACT, WBITS>(a, s);
+    if (c == "M" && n128) return run<CfgM, ACT, WBITS>(a, s);
+    if (c == "S") return run<CfgS, ACT, WBITS>(a, s);
+  }
+  if (n256 && a.M > 128 && tiles(256, 256) >= 400) return run<CfgX, ACT, WBITS>(a, s);
   if (n128 && a.M > 128 && tiles(256, 128) >= 256) return run<CfgL, ACT, WBITS>(a, s);
   if (n128 && a.M > 64 && tiles(128, 128) >= 256) return run<CfgM, ACT, WBITS>(a, s);
-  if (a.N % 64 == 0) return run<CfgS, ACT, WBITS>(a, s);
-  return hipErrorInvalidValue;
+  return run<CfgS, ACT, WBITS>(a, s);
 }
 
 }  // namespace

@@ -10,8 +10,9 @@
 // BM rows of activations.
 //
 // LDS rows are 128 bytes (64 k of 16-bit values) split into eight 16-byte
-// chunks stored at chunk ^ (row % 8), so that the 32 rows one fragment read
-// touches spread over all banks.
+// chunks stored at chunk ^ (row % 8), so that the rows one fragment read
+// touches spread over the banks (measured on gfx950: unswizzled rows run
+// about 3x slower; this placement and chunk ^ ((row / 2) % 8) are within 1%).
 //
 // Dequant in this kernel: int4 w = fma(q, s, z - 8 s) rounded to nearest even
 // (equal to the exact (q - 8) s + z whenever z - 8 s is exact in fp32, as it
@@ -49,9 +50,12 @@ struct TileProblem {
   int w_rows;                // rows of one expert's weight matrix
 };
 
-template <int BM_, int BN_, int WM_, int WN_>
+// INTERLEAVE: 0 = run the stage's matrix-core work, then dequantize the next
+// stage; > 0 = interleave them, with up to that many VALU instructions after
+// each MFMA.
+template <int BM_, int BN_, int WM_, int WN_, int INTERLEAVE_ = 0>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, INTERLEAVE = INTERLEAVE_;
   static constexpr int BK = 64;
   static constexpr int NTHR = 64 * WM * WN;
   static constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
@@ -111,23 +115,27 @@ __device__ __forceinline__ void tile_gemm(const TileProblem &p, int tile_m, int 
   }
   const int n0 = (MODE == kMoeFc1) ? tile_n * (BN / 2) : tile_n * BN;
 
-  // A chunks owned by this thread: (row, chunk) pairs.
+  // A chunks owned by this thread: (row, chunk) pairs.  Rows past the tile's
+  // end read the tile's first row and are masked to zero, so the loads stay
+  // branch-free (a divergent branch around a load makes the wait-count
+  // insertion fall back to draining every outstanding load, which would undo
+  // the prefetch).
   const uint16_t *a_src[Cfg::A_CHUNKS];
+  uint32_t a_keep[Cfg::A_CHUNKS];
   int a_lds[Cfg::A_CHUNKS];
 #pragma unroll
   for (int c = 0; c < Cfg::A_CHUNKS; ++c) {
     const int idx = tid + c * NTHR;
     const int r = idx >> 3, ch = idx & 7;
     const int grow = row_lo + r;
+    const bool live = grow < row_hi;
     a_lds[c] = swz(r, ch);
-    if (grow < row_hi) {
-      size_t arow;
-      if constexpr (MODE == kMoeFc1) arow = static_cast<size_t>(p.row_src[grow]);
-      else arow = static_cast<size_t>(grow);
-      a_src[c] = p.A + arow * K + ch * 8;
-    } else {
-      a_src[c] = nullptr;
-    }
+    a_keep[c] = live ? 0xFFFFFFFFu : 0u;
+    const int srow = live ? grow : row_lo;
+    size_t arow;
+    if constexpr (MODE == kMoeFc1) arow = static_cast<size_t>(p.row_src[srow]);
+    else arow = static_cast<size_t>(srow);
+    a_src[c] = p.A + arow * K + ch * 8;
   }
 
   // B runs owned by this thread.
@@ -164,44 +172,51 @@ __device__ __forceinline__ void tile_gemm(const TileProblem &p, int tile_m, int 
     }
   }
 
-  // Register staging for the next step.
-  u32x4 a_reg[Cfg::A_CHUNKS];
-  u32x2 b_reg[NB];
-  float s_reg[NB], z_reg[NB];
+  // Register staging: two sets, so the global loads of step s + 2 are issued
+  // while step s computes and step s + 1 waits in the other set -- two steps
+  // of matrix-core work to hide the memory latency.
+  struct Regs {
+    u32x4 a[Cfg::A_CHUNKS];
+    u32x2 b[NB];
+    uint16_t s[NB], z[NB];
+  };
 
-  auto gload = [&](int step) {
+  auto gload = [&](int step, Regs &r) {
     const int k0 = step * BK;
 #pragma unroll
-    for (int c = 0; c < Cfg::A_CHUNKS; ++c)
-      a_reg[c] = a_src[c] ? *reinterpret_cast<const u32x4 *>(a_src[c] + k0) : u32x4{0u, 0u, 0u, 0u};
+    for (int c = 0; c < Cfg::A_CHUNKS; ++c) r.a[c] = *reinterpret_cast<const u32x4 *>(a_src[c] + k0);
 #pragma unroll
     for (int c = 0; c < NB; ++c) {
       if constexpr (WBITS == 4) {
         const int kb = step >> 1, h = step & 1;
-        b_reg[c] = *reinterpret_cast<const u32x2 *>(b_src[c] + static_cast<size_t>(kb) * 1024 + h * 8);
+        r.b[c] = *reinterpret_cast<const u32x2 *>(b_src[c] + static_cast<size_t>(kb) * 1024 + h * 8);
         const size_t gi = b_sidx[c] + (k0 / p.group);
-        s_reg[c] = bits_to_f32<ACT>(Sbase[gi]);
-        z_reg[c] = bits_to_f32<ACT>(Zbase[gi]);
+        r.s[c] = Sbase[gi];
+        r.z[c] = Zbase[gi];
       } else {
-        b_reg[c] = *reinterpret_cast<const u32x2 *>(b_src[c] + static_cast<size_t>(step) * 1024);
+        r.b[c] = *reinterpret_cast<const u32x2 *>(b_src[c] + static_cast<size_t>(step) * 1024);
       }
     }
   };
 
-  auto lstore = [&](int stage) {
+  auto lstore = [&](int stage, const Regs &r) {
     char *As = lds + stage * Cfg::STAGE;
     char *Bs = As + BM * 128;
 #pragma unroll
-    for (int c = 0; c < Cfg::A_CHUNKS; ++c) *reinterpret_cast<u32x4 *>(As + a_lds[c]) = a_reg[c];
+    for (int c = 0; c < Cfg::A_CHUNKS; ++c) {
+      const uint32_t k = a_keep[c];
+      *reinterpret_cast<u32x4 *>(As + a_lds[c]) = u32x4{r.a[c].x & k, r.a[c].y & k, r.a[c].z & k, r.a[c].w & k};
+    }
 #pragma unroll
     for (int c = 0; c < NB; ++c) {
       if constexpr (WBITS == 4) {
-        const float s = s_reg[c], z8 = z_reg[c] - 8.0f * s;
-        *reinterpret_cast<u32x4 *>(Bs + b_lds0[c]) = dequant_word_w4<ACT>(b_reg[c].x, s, z8);
-        *reinterpret_cast<u32x4 *>(Bs + b_lds1[c]) = dequant_word_w4<ACT>(b_reg[c].y, s, z8);
+        const float s = bits_to_f32<ACT>(r.s[c]);
+        const float z8 = bits_to_f32<ACT>(r.z[c]) - 8.0f * s;
+        *reinterpret_cast<u32x4 *>(Bs + b_lds0[c]) = dequant_word_w4<ACT>(r.b[c].x, s, z8);
+        *reinterpret_cast<u32x4 *>(Bs + b_lds1[c]) = dequant_word_w4<ACT>(r.b[c].y, s, z8);
       } else {
         *reinterpret_cast<u32x4 *>(Bs + b_lds0[c]) =
-            (ACT == kFP16) ? w8_run_to_f16(b_reg[c].x, b_reg[c].y) : w8_run_to_bf16(b_reg[c].x, b_reg[c].y);
+            (ACT == kFP16) ? w8_run_to_f16(r.b[c].x, r.b[c].y) : w8_run_to_bf16(r.b[c].x, r.b[c].y);
       }
     }
   };
@@ -231,13 +246,8 @@ __device__ __forceinline__ void tile_gemm(const TileProblem &p, int tile_m, int 
   }
   const int khalf = lane >> 5;
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int step = 0; step < nsteps; ++step) {
-    const int cur = step & 1;
-    if (step + 1 < nsteps) gload(step + 1);
-    const char *As = lds + cur * Cfg::STAGE;
+  auto compute = [&](int stage) {
+    const char *As = lds + stage * Cfg::STAGE;
     const char *Bs = As + BM * 128;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
@@ -252,9 +262,54 @@ __device__ __forceinline__ void tile_gemm(const TileProblem &p, int tile_m, int 
 #pragma unroll
         for (int jn = 0; jn < TN; ++jn) acc[i][jn] = mfma32x32x16<ACT>(af[i], bf[jn], acc[i][jn]);
     }
-    if (step + 1 < nsteps) lstore(cur ^ 1);
+  };
+
+  // One pipeline step: issue loads for step + 2 into `nxt2`, run the matrix
+  // cores on LDS stage step % 2, then stage step + 1 (held in `nxt1`).  Both
+  // are unconditional -- near the end they re-read the last step and store
+  // into the idle LDS buffer, which is never read again -- because a load
+  // inside a branch makes the wait-count insertion drain every outstanding
+  // load before the store, which would cancel the prefetch.
+  // Scheduling barriers keep that order: the compiler would otherwise hoist
+  // the LDS stores (and the waits on their loads) above the matrix-core work
+  // and sink the new loads below it.
+  auto body = [&](int step, Regs &nxt1, Regs &nxt2) {
+    gload(min(step + 2, nsteps - 1), nxt2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(step & 1);
+    if constexpr (Cfg::INTERLEAVE == 0) __builtin_amdgcn_sched_barrier(0);
+    lstore((step + 1) & 1, nxt1);
+    if constexpr (Cfg::INTERLEAVE > 0) {
+      // Spread the next stage's dequant (VALU) and LDS writes between this
+      // stage's matrix-core instructions, so each wave keeps the MFMA pipe
+      // busy while it converts weights.
+      constexpr int NMF = TM * TN * (BK / 16);
+#pragma unroll
+      for (int i = 0; i < NMF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                 // DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, Cfg::INTERLEAVE, 0);   // VALU
+        if (i % 2 == 1) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0); // DS write
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
+  };
+
+  Regs r0, r1;
+  gload(0, r0);
+  gload(min(1, nsteps - 1), r1);
+  lstore(0, r0);
+  __syncthreads();
+  // Unrolled by two so the register sets are named statically: at an even
+  // step r1 holds step + 1 and r0 receives step + 2; at an odd step the roles
+  // swap.
+  int step = 0;
+  for (; step + 1 < nsteps; step += 2) {
+    body(step, r1, r0);
+    body(step + 1, r0, r1);
   }
+  if (step < nsteps) body(step, r1, r0);
 
   // ---- epilogue -----------------------------------------------------------
   // 32x32 accumulator: value v of lane -> row 8*(v/4) + 4*(lane/32) + v%4,
