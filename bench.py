@@ -113,6 +113,28 @@ def gpu_lead(torch, ms=20.0):
         pass
 
 
+def kernel_only(args, torch, qg, si):
+    """Only the N=131072 M=1 GEMV, `--steps` times, then a plain copy kernel over
+    512 MiB three times (torch's elementwise negation: reads 512 MiB, writes
+    512 MiB, in full cache lines): the workload for rocprofv3 counter runs, the
+    copy of known size calibrating FETCH_SIZE / WRITE_SIZE."""
+    dev = "cuda"
+    n = 131072
+    w = Weights(torch, qg, si, n, DECODE_K, DECODE_G, "cfg1", copies_for(w4_bytes(1, n, DECODE_K, DECODE_G)))
+    A = torch.from_numpy(si.activations(1, DECODE_K, si.seed_of("cfg1", "a", 1, DECODE_K))
+                         .view("int16")).view(torch.bfloat16).to(dev)
+    C = torch.empty((1, n), dtype=torch.bfloat16, device=dev)
+    for i in range(args.steps):
+        B, S, Z = w[i]
+        qg.gemm_w4a16(A, B, S, Z, None, DECODE_G, out=C)
+    src = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log(f"kernel-only: {args.steps} GEMVs (M=1, N={n}) and 3 copies of 512 MiB")
+
+
 def run(args):
     import torch
 
@@ -126,6 +148,9 @@ def run(args):
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
     log(f"device: {props.name} ({props.gcnArchName}), CUs {props.multi_processor_count}")
+    if args.kernel_only:
+        kernel_only(args, torch, qg, si)
+        return
 
     # ---- decode workload ------------------------------------------------------
     t0 = time.time()
@@ -203,7 +228,7 @@ def run(args):
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic,
-                "kernel": "k_decode_w4 (M=1, N=131072, K=2048, g=64)",
+                "kernel": "k_decode_w4_stream (M=1, N=131072, K=2048, g=64)",
                 "bytes_per_launch": lm_bytes, "mean_launch_us": round(lm_ms * 1e3, 2)}
 
     # ---- full decode sweep (M = 1, 2, 4, 8) -----------------------------------
@@ -285,6 +310,19 @@ def run(args):
         del w1, w2, ws
         torch.cuda.empty_cache()
 
+    # ---- ceiling: a plain device-to-device copy (read + write) ----------------------
+    ceil = None
+    if not args.quick:
+        nbytes = 1 << 30
+        bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(i) for i in range(3)]
+        reps = 10
+        ms = timed(lambda i: bufs[(i + 1) % 3].copy_(bufs[i % 3]), reps) / reps
+        ceil = {"copy_GBps": round(2 * nbytes / (ms * 1e-3) / 1e9, 1),
+                "note": "torch device copy of 1 GiB, read + write bytes"}
+        del bufs
+        torch.cuda.empty_cache()
+        log(f"ceiling: {ceil}")
+
     # ---- CPU oracle baseline -----------------------------------------------------
     cpu = None
     if not args.no_cpu:
@@ -334,6 +372,7 @@ def run(args):
         "sweep": sweep,
         "prefill": prefill,
         "moe": moe,
+        "ceiling": ceil,
     }
     print(json.dumps(result), flush=True)
 
@@ -347,7 +386,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-moe", action="store_true")
-    ap.add_argument("--quick", action="store_true", help="skip the M sweep")
+    ap.add_argument("--quick", action="store_true", help="skip the M sweep and the copy ceiling")
+    ap.add_argument("--kernel-only", action="store_true",
+                    help="run only the N=131072 GEMV (--steps times) and a calibration copy; "
+                         "for profiler counter runs; prints no result line")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

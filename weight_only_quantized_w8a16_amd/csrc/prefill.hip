@@ -83,7 +83,7 @@ hipError_t dispatch(const GemmArgs &a, hipStream_t s) {
     if (c == "S") return run<CfgS, ACT, WBITS>(a, s);
   }
   if (n256 && a.M > 128 && tiles(256, 256) >= 400) return run<CfgX, ACT, WBITS>(a, s);
-  if (n128 && a.M > 128 && tiles(256, 128) >= 256) return run<CfgL, ACT, WBITS>(a, s);
+  if (n128 && a.M > 128 && tiles(256, 128) >= 200) return run<CfgL, ACT, WBITS>(a, s);
   if (n128 && a.M > 64 && tiles(128, 128) >= 256) return run<CfgM, ACT, WBITS>(a, s);
   return run<CfgS, ACT, WBITS>(a, s);
 }
