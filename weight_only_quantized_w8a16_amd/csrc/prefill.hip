@@ -12,6 +12,7 @@
 #include <string>
 
 #include "qg_launch.hpp"
+#include "tile_big.hpp"
 #include "tile_gemm.hpp"
 
 namespace qg {
@@ -31,6 +32,17 @@ __global__ __launch_bounds__(Cfg::NTHR) void k_prefill(TileProblem p, int tiles_
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int id = xcd_linear_id();
   tile_gemm<Cfg, ACT, WBITS, kDense>(p, id / tiles_n, id % tiles_n, lds);
+}
+
+template <int ACT, int WBITS>
+__global__ __launch_bounds__(BigCfg::NTHR) void k_prefill_big(TileProblem p, int tiles_n) {
+  __shared__ __attribute__((aligned(16))) char a0[BigCfg::STAGE];
+  __shared__ __attribute__((aligned(16))) char a1[BigCfg::STAGE];
+  __shared__ __attribute__((aligned(16))) char b0[BigCfg::STAGE];
+  __shared__ __attribute__((aligned(16))) char b1[BigCfg::STAGE];
+  const BigLds L{{a0, a1}, {b0, b1}};
+  const int id = xcd_linear_id();
+  tile_gemm_big<ACT, WBITS>(p, id / tiles_n, id % tiles_n, L);
 }
 
 namespace {
@@ -67,10 +79,33 @@ hipError_t run(const GemmArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int ACT, int WBITS>
+hipError_t run_big(const GemmArgs &a, hipStream_t s) {
+  TileProblem p{};
+  p.A = a.A;
+  p.B = static_cast<const uint8_t *>(a.B);
+  p.S = a.S;
+  p.Z = a.Z;
+  p.bias = a.bias;
+  p.C = a.C;
+  p.M = a.M;
+  p.N = a.N;
+  p.K = a.K;
+  p.group = a.group > 0 ? a.group : a.K;
+  p.bias_dt = a.bias_dt;
+  // The kernel keeps 32-bit element / byte offsets.
+  const uint64_t lim = uint64_t(1) << 31;
+  if (uint64_t(a.M) * a.K >= lim || uint64_t(a.N) * a.K * WBITS / 8 >= lim) return run<CfgX, ACT, WBITS>(a, s);
+  const int tm = (a.M + BigCfg::BM - 1) / BigCfg::BM, tn = a.N / BigCfg::BN;
+  hipLaunchKernelGGL((k_prefill_big<ACT, WBITS>), dim3(tm * tn), dim3(BigCfg::NTHR), 0, s, p, tn);
+  return hipGetLastError();
+}
+
 // Tile choice, from on-device sweeps at K = 2048: the biggest tile (fewest
 // LDS bytes per matrix-core instruction) once there are enough tiles to give
 // every CU about two; smaller tiles when the problem would leave CUs idle.
-// QGEMM_PREFILL_TILE=X|L|M|S forces one (tests and tuning).
+// QGEMM_PREFILL_TILE=X|B|L|M|S forces one (tests and tuning); B is the
+// 4-wave 256 x 256 kernel with direct-to-LDS activation loads.
 template <int ACT, int WBITS>
 hipError_t dispatch(const GemmArgs &a, hipStream_t s) {
   auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * (a.N / bn); };
@@ -78,6 +113,7 @@ hipError_t dispatch(const GemmArgs &a, hipStream_t s) {
   if (const char *o = std::getenv("QGEMM_PREFILL_TILE")) {
     const std::string c(o);
     if (c == "X" && n256) return run<CfgX, ACT, WBITS>(a, s);
+    if (c == "B" && n256) return run_big<ACT, WBITS>(a, s);
     if (c == "L" && n128) return run<CfgL, ACT, WBITS>(a, s);
     if (c == "M" && n128) return run<CfgM, ACT, WBITS>(a, s);
     if (c == "S") return run<CfgS, ACT, WBITS>(a, s);
