@@ -34,20 +34,23 @@ __global__ __launch_bounds__(Cfg::NTHR) void k_prefill(TileProblem p, int tiles_
   tile_gemm<Cfg, ACT, WBITS, kDense>(p, id / tiles_n, id % tiles_n, lds);
 }
 
-template <int ACT, int WBITS>
-__global__ __launch_bounds__(BigCfg::NTHR) void k_prefill_big(TileProblem p, int tiles_n) {
-  __shared__ __attribute__((aligned(16))) char a0[BigCfg::STAGE];
-  __shared__ __attribute__((aligned(16))) char a1[BigCfg::STAGE];
-  __shared__ __attribute__((aligned(16))) char b0[BigCfg::STAGE];
-  __shared__ __attribute__((aligned(16))) char b1[BigCfg::STAGE];
-  const BigLds L{{a0, a1}, {b0, b1}};
+template <class Cfg, int ACT, int WBITS>
+__global__ __launch_bounds__(Cfg::NTHR) void k_prefill_dma(TileProblem p, int tiles_n) {
+  __shared__ __attribute__((aligned(16))) char a0[Cfg::STAGE];
+  __shared__ __attribute__((aligned(16))) char a1[Cfg::STAGE];
+  __shared__ __attribute__((aligned(16))) char b0[Cfg::STAGE];
+  __shared__ __attribute__((aligned(16))) char b1[Cfg::STAGE];
+  __shared__ __attribute__((aligned(16))) char sc[2 * Cfg::SC_WIN];
+  const DmaLds L{{a0, a1}, {b0, b1}, sc};
   const int id = xcd_linear_id();
-  tile_gemm_big<ACT, WBITS>(p, id / tiles_n, id % tiles_n, L);
+  tile_gemm_dma<Cfg, ACT, WBITS>(p, id / tiles_n, id % tiles_n, L);
 }
 
 namespace {
 
 using CfgX = TileCfg<256, 256, 2, 4>;   // 8 waves, 128x64 per wave
+using CfgD4 = DmaCfg<2, 2>;             // 4 waves, 128x128 per wave, A direct to LDS
+using CfgD8 = DmaCfg<2, 4>;             // 8 waves, 128x64 per wave, A direct to LDS
 using CfgL = TileCfg<256, 128, 4, 2>;   // 8 waves, 64x64 per wave
 using CfgM = TileCfg<128, 128, 2, 2>;   // 4 waves, 64x64 per wave
 using CfgS = TileCfg<64, 64, 2, 2>;     // 4 waves, 32x32 per wave
@@ -79,8 +82,15 @@ hipError_t run(const GemmArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int ACT, int WBITS>
-hipError_t run_big(const GemmArgs &a, hipStream_t s) {
+template <class Cfg, int ACT, int WBITS>
+hipError_t run_dma(const GemmArgs &a, hipStream_t s) {
+  // The kernel keeps 32-bit element / byte offsets.
+  const uint64_t lim = uint64_t(1) << 31;
+  if (uint64_t(a.M) * a.K >= lim || uint64_t(a.N) * a.K * WBITS / 8 >= lim) return run<CfgX, ACT, WBITS>(a, s);
+  // int4 scales/zeros arrive as 4-byte pairs of groups.
+  if (WBITS == 4 && (((a.K / a.group) & 1) != 0 || (reinterpret_cast<uintptr_t>(a.S) & 3) != 0 ||
+                     (reinterpret_cast<uintptr_t>(a.Z) & 3) != 0))
+    return run<CfgX, ACT, WBITS>(a, s);
   TileProblem p{};
   p.A = a.A;
   p.B = static_cast<const uint8_t *>(a.B);
@@ -93,19 +103,16 @@ hipError_t run_big(const GemmArgs &a, hipStream_t s) {
   p.K = a.K;
   p.group = a.group > 0 ? a.group : a.K;
   p.bias_dt = a.bias_dt;
-  // The kernel keeps 32-bit element / byte offsets.
-  const uint64_t lim = uint64_t(1) << 31;
-  if (uint64_t(a.M) * a.K >= lim || uint64_t(a.N) * a.K * WBITS / 8 >= lim) return run<CfgX, ACT, WBITS>(a, s);
-  const int tm = (a.M + BigCfg::BM - 1) / BigCfg::BM, tn = a.N / BigCfg::BN;
-  hipLaunchKernelGGL((k_prefill_big<ACT, WBITS>), dim3(tm * tn), dim3(BigCfg::NTHR), 0, s, p, tn);
+  const int tm = (a.M + Cfg::BM - 1) / Cfg::BM, tn = a.N / Cfg::BN;
+  hipLaunchKernelGGL((k_prefill_dma<Cfg, ACT, WBITS>), dim3(tm * tn), dim3(Cfg::NTHR), 0, s, p, tn);
   return hipGetLastError();
 }
 
-// Tile choice, from on-device sweeps at K = 2048: the biggest tile (fewest
-// LDS bytes per matrix-core instruction) once there are enough tiles to give
-// every CU about two; smaller tiles when the problem would leave CUs idle.
-// QGEMM_PREFILL_TILE=X|B|L|M|S forces one (tests and tuning); B is the
-// 4-wave 256 x 256 kernel with direct-to-LDS activation loads.
+// Tile choice, from on-device sweeps at K = 2048 and 3584: the 256 x 256
+// direct-load tile once there are enough tiles to keep most CUs busy;
+// smaller tiles when the problem would leave CUs idle.
+// QGEMM_PREFILL_TILE=X|D4|D8|L|M|S forces one (tests and tuning); D4 / D8
+// are the 256 x 256 tiles with direct-to-LDS activation loads.
 template <int ACT, int WBITS>
 hipError_t dispatch(const GemmArgs &a, hipStream_t s) {
   auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * (a.N / bn); };
@@ -113,12 +120,13 @@ hipError_t dispatch(const GemmArgs &a, hipStream_t s) {
   if (const char *o = std::getenv("QGEMM_PREFILL_TILE")) {
     const std::string c(o);
     if (c == "X" && n256) return run<CfgX, ACT, WBITS>(a, s);
-    if (c == "B" && n256) return run_big<ACT, WBITS>(a, s);
+    if (c == "D4" && n256) return run_dma<CfgD4, ACT, WBITS>(a, s);
+    if (c == "D8" && n256) return run_dma<CfgD8, ACT, WBITS>(a, s);
     if (c == "L" && n128) return run<CfgL, ACT, WBITS>(a, s);
     if (c == "M" && n128) return run<CfgM, ACT, WBITS>(a, s);
     if (c == "S") return run<CfgS, ACT, WBITS>(a, s);
   }
-  if (n256 && a.M > 128 && tiles(256, 256) >= 400) return run<CfgX, ACT, WBITS>(a, s);
+  if (n256 && a.M > 128 && tiles(256, 256) >= 160) return run_dma<CfgD8, ACT, WBITS>(a, s);
   if (n128 && a.M > 128 && tiles(256, 128) >= 200) return run<CfgL, ACT, WBITS>(a, s);
   if (n128 && a.M > 64 && tiles(128, 128) >= 256) return run<CfgM, ACT, WBITS>(a, s);
   return run<CfgS, ACT, WBITS>(a, s);

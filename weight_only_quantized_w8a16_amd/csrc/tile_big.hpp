@@ -1,29 +1,34 @@
-// tile_big.hpp -- the large-tile prefill GEMM for gfx950: a 256 x 256 tile of
-// C = A . W^T per workgroup, four waves of 128 x 128, one wave per SIMD.
+// tile_big.hpp -- the 256 x 256 prefill GEMM tile for gfx950 with the
+// activations loaded straight into LDS: C = A . W^T for one 256 x 256 output
+// tile per workgroup, WM x WN waves, each wave a (256 / WM) x (256 / WN)
+// block of 32 x 32 accumulators.
 //
-// With one wave per SIMD nothing else hides latency, so the kernel pipelines
-// explicitly:
-//  - A goes from global memory straight into LDS (global_load_lds_dwordx4)
-//    one 64-k step ahead of use, into one of two LDS stages;
-//  - the packed weight codes (and their scales) are loaded into registers two
-//    steps ahead, dequantized by all 256 threads and written into one of two
-//    LDS stages while the matrix cores work on the current stage;
-//  - operand fragments are double-buffered in registers across the four
-//    16-k sub-steps of a step, so the LDS reads of sub-step s + 1 are in
-//    flight during the sixteen v_mfma_f32_32x32x16 of sub-step s.
-// The 128 x 128 wave tile halves the LDS bytes read per matrix-core
-// instruction relative to 64 x 64 tiles (LDS bandwidth limits this part).
+// Per 64-k step:
+//  - A goes from global memory into LDS with global_load_lds_dwordx4, one
+//    step ahead of use, into one of two LDS stages (no trip through VGPRs,
+//    so no registers, address arithmetic or LDS store instructions for it);
+//  - the packed weight codes (and their scales and zeros) are loaded into
+//    registers two steps ahead, dequantized by every thread and written into
+//    one of two LDS stages while the matrix cores work on the current stage;
+//  - the int4 scales and zeros come through LDS as well: a window holds 8
+//    groups of all 256 channels (16 bytes of each row of the scale and zero
+//    matrices, read with 4-byte direct loads, 1/4 of a window per step), so
+//    each row's scales cost one cache-line visit per 8 groups instead of a
+//    16-line gather per group;
+//  - every wave then waits for its own direct loads and meets the others at
+//    one barrier.
 //
-// LDS rows hold 64 k (128 bytes) plus a 16-byte pad: with a 144-byte stride
-// the 16 rows served together by one 16-byte-per-lane access land on 16
-// distinct bank groups, and every sub-step / stage offset is a compile-time
-// immediate of the LDS instruction (an XOR placement would need a register
-// per (stage, sub-step, fragment)).  The stages are separate __shared__
-// objects addressed only by constants, so alias analysis can tell the
-// direct-to-LDS writes into one stage from the reads of the other.
+// LDS placement: a stage holds 256 rows of 64 k (128 bytes), the 16-byte
+// chunk c of row r at chunk c ^ ((r / 2) % 8).  A 16-lane group reading one
+// chunk of 16 consecutive rows then touches 16 distinct 16-byte bank groups
+// of the 256-byte bank space.  A direct load writes 64 consecutive 16-byte
+// slots, so the swizzle is applied on the source side: slot (r, c') is
+// loaded from the row's chunk c' ^ ((r / 2) % 8).
 //
 // Rows of A past the problem's end are read from the last valid row (a
 // direct-to-LDS load cannot be masked); their output rows are never stored.
+// All loads go through buffer resources with 32-bit offsets: the host routes
+// problems with M * K or the code bytes at or above 2^31 elsewhere.
 #pragma once
 
 #include <type_traits>
@@ -32,63 +37,86 @@
 
 namespace qg {
 
-struct BigCfg {
-  static constexpr int BM = 256, BN = 256, BK = 64, NTHR = 256;
-  static constexpr int RS = 144;                      // LDS row stride (bytes)
-  static constexpr int STAGE = 256 * RS;              // 36864 bytes
-  static constexpr int TM = 4, TN = 4;                // 32x32 subtiles per wave
-  static constexpr int A_DMA = 9;                     // 1 KiB direct loads per wave per step
+template <int WM_, int WN_>
+struct DmaCfg {
+  static constexpr int WM = WM_, WN = WN_;
+  static constexpr int BM = 256, BN = 256, BK = 64;
+  static constexpr int NTHR = 64 * WM * WN;
+  static constexpr int WTM = BM / WM, WTN = BN / WN;   // wave tile
+  static constexpr int TM = WTM / 32, TN = WTN / 32;   // 32x32 accumulators per wave
+  static constexpr int STAGE = 256 * 128;              // bytes per LDS stage (A or W)
+  static constexpr int A_DMA = BM * 8 / NTHR;          // direct loads per thread per step
+  static constexpr int NB4 = BN * 4 / NTHR;            // int4: 8-byte code runs per thread
+  static constexpr int NB8 = BN * 8 / NTHR;            // int8: 8-byte code runs per thread
+  static constexpr int SC_WIN = 8192;                   // bytes per scale/zero window
+  static constexpr int SC_DMA = 512 / NTHR;             // 4-byte window loads per thread per step
+  static_assert(A_DMA >= 1 && NB4 >= 1 && SC_DMA >= 1, "thread count");
 };
 
-struct BigLds {
+struct DmaLds {
   char *a[2];
   char *b[2];
+  char *sc;   // two scale/zero windows of DmaCfg::SC_WIN bytes
 };
 
-template <int ACT, int WBITS>
-__device__ __forceinline__ void tile_gemm_big(const TileProblem &p, int tile_m, int tile_n,
-                                              const BigLds &L) {
-  using Cfg = BigCfg;
-  constexpr int BK = Cfg::BK, RS = Cfg::RS;
-  constexpr int TM = Cfg::TM, TN = Cfg::TN;
+__device__ __forceinline__ int dswz(int row, int chunk) {
+  return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
+}
+
+template <class Cfg, int ACT, int WBITS>
+__device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, int tile_n,
+                                              const DmaLds &L) {
+  constexpr int BK = Cfg::BK, TM = Cfg::TM, TN = Cfg::TN, NTHR = Cfg::NTHR;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
   const int K = p.K;
   const int nsteps = K / BK;
   const int row_lo = tile_m * Cfg::BM;
   const int row_last = min(p.M, row_lo + Cfg::BM) - 1;
   const int n0 = tile_n * Cfg::BN;
 
-  // ---- A: 9 direct loads per wave per step, 64 x 16 bytes each, filling
-  // the stage linearly: 16-byte slot q holds row q / 9, chunk q % 9 (chunk 8
-  // is the pad, loaded from the row's first chunk and never read).
-  // 32-bit element offsets keep the address registers few; the host sends
-  // problems whose offsets would not fit to the generic tile kernel.
-  uint32_t a_off32[Cfg::A_DMA];
+  // Buffer resources: 32-bit per-lane offsets, the step's offset in an SGPR.
+  // (A flat/global direct-to-LDS load would also be taken by the wait-count
+  // pass as a pending LDS access, and every later wait would become a full
+  // drain.)
+  constexpr int kRsrcFlags = 0x00020000;
+  const uint32_t a_bytes = static_cast<uint32_t>(static_cast<uint64_t>(p.M) * K * 2);
+  const uint32_t b_bytes = static_cast<uint32_t>(static_cast<uint64_t>(p.N) * K * WBITS / 8);
+  const auto rA = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(p.A), 0, static_cast<int>(a_bytes), kRsrcFlags);
+  const auto rB = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(p.B), 0, static_cast<int>(b_bytes), kRsrcFlags);
+  [[maybe_unused]] const uint32_t s_bytes =
+      (WBITS == 4) ? static_cast<uint32_t>(static_cast<uint64_t>(p.N) * (K / p.group) * 2) : 0u;
+  [[maybe_unused]] const auto rS =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(p.S), 0, static_cast<int>(s_bytes), kRsrcFlags);
+  [[maybe_unused]] const auto rZ =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(p.Z), 0, static_cast<int>(s_bytes), kRsrcFlags);
+
+  // ---- A: slot q = (wave * A_DMA + i) * 64 + lane of a stage is row q / 8,
+  // placed chunk q % 8; it holds the row's chunk (q % 8) ^ ((row / 2) % 8).
+  uint32_t a_voff[Cfg::A_DMA];   // bytes
 #pragma unroll
   for (int i = 0; i < Cfg::A_DMA; ++i) {
     const int q = (wave * Cfg::A_DMA + i) * 64 + lane;
-    const int r = q / 9, ch = q % 9;
+    const int r = q >> 3, c = (q & 7) ^ ((r >> 1) & 7);
     const int grow = min(row_lo + r, row_last);
-    a_off32[i] = static_cast<uint32_t>(grow) * static_cast<uint32_t>(K) + (ch == 8 ? 0 : ch * 8);
+    a_voff[i] = (static_cast<uint32_t>(grow) * static_cast<uint32_t>(K) + c * 8) * 2u;
   }
   auto a_issue = [&](int step, char *stage) {
     char *dst = stage + wave * Cfg::A_DMA * 1024;
 #pragma unroll
     for (int i = 0; i < Cfg::A_DMA; ++i)
-      __builtin_amdgcn_global_load_lds(p.A + a_off32[i] + step * BK,
-                                       (__attribute__((address_space(3))) void *)(dst + i * 1024),
-                                       16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rA, (__attribute__((address_space(3))) void *)(dst + i * 1024), 16, a_voff[i], step * BK * 2, 0, 0);
   };
 
-  // ---- W: packed codes (and scales) per thread.
-  constexpr int NB = (WBITS == 4) ? 4 : 8;   // 8-byte runs per thread per step
+  // ---- W: packed codes per thread.
+  constexpr int NB = (WBITS == 4) ? Cfg::NB4 : Cfg::NB8;
   uint32_t b_src[NB];        // byte offsets into the tiled codes
   int b_lds0[NB], b_lds1[NB];
-  uint32_t b_sidx[NB];       // scale row offsets
+  int b_sc[NB];              // scale-window offsets of the runs' rows
 #pragma unroll
   for (int c = 0; c < NB; ++c) {
-    const int idx = tid + c * Cfg::NTHR;
+    const int idx = tid + c * NTHR;
     int l, bi, t = 0;
     if constexpr (WBITS == 4) { l = idx & 63; bi = idx >> 6; }
     else { t = idx & 1; l = (idx >> 1) & 63; bi = idx >> 7; }
@@ -97,40 +125,84 @@ __device__ __forceinline__ void tile_gemm_big(const TileProblem &p, int tile_m, 
     const int wrow = n0 + lrow;
     if constexpr (WBITS == 4) {
       b_src[c] = static_cast<uint32_t>(wrow >> 4) * static_cast<uint32_t>(K >> 7) * 1024u + l * 16;
-      b_lds0[c] = lrow * RS + j * 16;           // word 2h   -> k-chunk j
-      b_lds1[c] = lrow * RS + (4 + j) * 16;     // word 2h+1 -> k-chunk 4 + j
-      b_sidx[c] = static_cast<uint32_t>(wrow) * static_cast<uint32_t>(K / p.group);
+      b_lds0[c] = dswz(lrow, j);          // word 2h   -> k-chunk j
+      b_lds1[c] = dswz(lrow, 4 + j);      // word 2h+1 -> k-chunk 4 + j
+      b_sc[c] = lrow * 16;
     } else {
       b_src[c] = static_cast<uint32_t>(wrow >> 4) * static_cast<uint32_t>(K >> 6) * 1024u + l * 16 + t * 8;
-      b_lds0[c] = lrow * RS + (4 * t + j) * 16;
+      b_lds0[c] = dswz(lrow, 4 * t + j);
       b_lds1[c] = 0;
-      b_sidx[c] = 0;
+      b_sc[c] = 0;
     }
   }
   struct Regs {
     u32x2 b[NB];
-    uint16_t s[NB], z[NB];
   };
   auto b_issue = [&](int step, Regs &r) {
 #pragma unroll
     for (int c = 0; c < NB; ++c) {
       if constexpr (WBITS == 4) {
         const int kb = step >> 1, h = step & 1;
-        r.b[c] = *reinterpret_cast<const u32x2 *>(p.B + b_src[c] + static_cast<uint32_t>(kb) * 1024u + h * 8);
-        const uint32_t gi = b_sidx[c] + (step * BK) / p.group;
-        r.s[c] = p.S[gi];
-        r.z[c] = p.Z[gi];
+        r.b[c] = __builtin_amdgcn_raw_buffer_load_b64(rB, b_src[c], kb * 1024 + h * 8, 0);
       } else {
-        r.b[c] = *reinterpret_cast<const u32x2 *>(p.B + b_src[c] + static_cast<uint32_t>(step) * 1024u);
+        r.b[c] = __builtin_amdgcn_raw_buffer_load_b64(rB, b_src[c], step * 1024, 0);
       }
     }
   };
-  auto b_store = [&](char *Bs, const Regs &r) {
+
+  // ---- int4 scale/zero windows.  Window w holds groups 8w .. 8w + 7 of the
+  // tile's 256 rows: byte (part * 256 + row) * 16 + 2 * (group % 8), part 0
+  // the scales, 1 the zeros; windows alternate between two buffers.  Step u
+  // uses group u / spg (spg = group_size / 64 steps per group).  A direct
+  // load writes 4 bytes per lane (two groups), so a window is four parts of
+  // 2 KiB; part t, slot = wave * SC_DMA + i covers rows
+  // 128 (t % 2) + 16 slot + lane / 4, groups 2 (lane % 4) + {0, 1}, of part
+  // t / 2.  At the top of step s, before any new direct load, each thread
+  // reads the scales of step s + 1 (dequantized in step s) from LDS; then
+  // part (s + 1) % 4 of window (s + 1) / (8 spg) + 1 is issued (every part
+  // at least twice per window, the repeats rewriting equal bytes).  A window
+  // is complete one step before its first use, and its buffer was last read
+  // one step before its first part lands.  Windows past the last group read
+  // other rows or (past the end of the matrices) zeros; they are never used.
+  [[maybe_unused]] const int kg = K / p.group;
+  [[maybe_unused]] const int spg_lg = (p.group == 128) ? 1 : 0;
+  uint32_t sc_voff[Cfg::SC_DMA];
+#pragma unroll
+  for (int i = 0; i < Cfg::SC_DMA; ++i) {
+    const int slot = wave * Cfg::SC_DMA + i;
+    sc_voff[i] = (static_cast<uint32_t>(n0 + slot * 16 + (lane >> 2)) * static_cast<uint32_t>(kg) + (lane & 3) * 2) * 2u;
+  }
+  auto sc_issue = [&](int t, int w) {
+    if constexpr (WBITS == 4) {
+      const int soff = (t & 1) * 128 * kg * 2 + w * 16;
+      char *dst = L.sc + (w & 1) * Cfg::SC_WIN + (t * 8 + wave * Cfg::SC_DMA) * 256;
+#pragma unroll
+      for (int i = 0; i < Cfg::SC_DMA; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(t >= 2 ? rZ : rS,
+                                                 (__attribute__((address_space(3))) void *)(dst + i * 256), 4,
+                                                 sc_voff[i], soff, 0, 0);
+    }
+  };
+  struct ScaleRegs {
+    uint16_t s[NB], z[NB];
+  };
+  auto sc_read = [&](int u, ScaleRegs &v) {
+    if constexpr (WBITS == 4) {
+      const int gi = u >> spg_lg;
+      const char *win = L.sc + ((gi >> 3) & 1) * Cfg::SC_WIN + (gi & 7) * 2;
+#pragma unroll
+      for (int c = 0; c < NB; ++c) {
+        v.s[c] = *reinterpret_cast<const uint16_t *>(win + b_sc[c]);
+        v.z[c] = *reinterpret_cast<const uint16_t *>(win + 4096 + b_sc[c]);
+      }
+    }
+  };
+  auto b_store = [&](char *Bs, const Regs &r, const ScaleRegs &v) {
 #pragma unroll
     for (int c = 0; c < NB; ++c) {
       if constexpr (WBITS == 4) {
-        const float s = bits_to_f32<ACT>(r.s[c]);
-        const float z8 = bits_to_f32<ACT>(r.z[c]) - 8.0f * s;
+        const float s = bits_to_f32<ACT>(v.s[c]);
+        const float z8 = bits_to_f32<ACT>(v.z[c]) - 8.0f * s;
         *reinterpret_cast<u32x4 *>(Bs + b_lds0[c]) = dequant_word_w4<ACT>(r.b[c].x, s, z8);
         *reinterpret_cast<u32x4 *>(Bs + b_lds1[c]) = dequant_word_w4<ACT>(r.b[c].y, s, z8);
       } else {
@@ -140,21 +212,26 @@ __device__ __forceinline__ void tile_gemm_big(const TileProblem &p, int tile_m, 
     }
   };
 
-  // ---- fragments: lane reads row (wave tile row + lane % 32), k-chunk
-  // 2 * ks + lane / 32, i.e. a fixed per-lane base plus an immediate.
+  // ---- fragments: lane reads row (wave tile row + 32 i + lane % 32), chunk
+  // 2 ks + lane / 32, placed at that ^ ((lane / 2) % 8) (the wave tile and
+  // 32 i leave (row / 2) % 8 unchanged).  One address per ks; i and the stage
+  // are immediates.
   const int khalf = lane >> 5;
-  const int a_base = (wm * 128 + (lane & 31)) * RS + khalf * 16;
-  const int b_base = (wn * 128 + (lane & 31)) * RS + khalf * 16;
+  const int g = khalf ^ ((lane >> 1) & 7);
+  int a_addr[4], b_addr[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    a_addr[ks] = (wm * Cfg::WTM + (lane & 31)) * 128 + (((2 * ks) ^ g) << 4);
+    b_addr[ks] = (wn * Cfg::WTN + (lane & 31)) * 128 + (((2 * ks) ^ g) << 4);
+  }
   struct Frags {
     u32x4 a[TM], b[TN];
   };
   auto fread = [&](const char *As, const char *Bs, int ks, Frags &f) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
-      f.a[i] = *reinterpret_cast<const u32x4 *>(As + a_base + 32 * i * RS + 32 * ks);
+    for (int i = 0; i < TM; ++i) f.a[i] = *reinterpret_cast<const u32x4 *>(As + a_addr[ks] + 4096 * i);
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
-      f.b[j] = *reinterpret_cast<const u32x4 *>(Bs + b_base + 32 * j * RS + 32 * ks);
+    for (int j = 0; j < TN; ++j) f.b[j] = *reinterpret_cast<const u32x4 *>(Bs + b_addr[ks] + 4096 * j);
   };
 
   f32x16 acc[TM][TN];
@@ -172,34 +249,56 @@ __device__ __forceinline__ void tile_gemm_big(const TileProblem &p, int tile_m, 
       for (int j = 0; j < TN; ++j) acc[i][j] = mfma32x32x16<ACT>(f.a[i], f.b[j], acc[i][j]);
   };
 
-  // VMEM instructions this wave issues per step after its A loads of that
-  // step: the W loads (codes, scales, zeros) of the step two ahead.  The
-  // waits and barriers are written out rather than taken from
-  // __syncthreads(), whose workgroup fence would also wait for those W loads
-  // (the fence counts the direct-to-LDS loads as pending LDS writes).
-  constexpr int VMEM_B = (WBITS == 4) ? 3 * NB : NB;
+  // VMEM instructions a thread issues per step after its direct loads: the
+  // W code loads of the step two ahead.  The wait before each barrier leaves
+  // exactly those in flight.  It is a compiler builtin (not inline asm), so
+  // the wait-count pass knows what it covers and adds no waits of its own
+  // for the LDS data read after the barrier.
+  constexpr int VMEM_B = NB;
+  static_assert(VMEM_B < 16, "vmcnt field");
+  constexpr int WAIT = VMEM_B | (7 << 4);                    // vmcnt(VMEM_B) lgkmcnt(0)
+  constexpr int WAIT_ALL_BUT_2B = (2 * VMEM_B < 16 ? 2 * VMEM_B : 15) | (7 << 4);
+  auto barrier = [&] {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
 
-  // ---- prologue: A step 0 and W steps 0, 1 in flight; W step 0 staged.
-  // The empty asm statements with a memory clobber pin the issue order (A
-  // loads before W loads), which the explicit vmcnt waits count on.
+  // ---- prologue: scale window 0 and part 0 of window 1, A of step 0, W
+  // codes of steps 0 and 1; once the direct loads have landed everywhere,
+  // dequantize step 0.  The empty asm statements with a memory clobber keep
+  // the direct loads ahead of the code loads, which the waits count on.
   Regs r0, r1;
+  ScaleRegs sv;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) sc_issue(t, 0);
+  sc_issue(0, 1);
   a_issue(0, L.a[0]);
   asm volatile("" ::: "memory");
   b_issue(0, r0);
   b_issue(min(1, nsteps - 1), r1);
-  b_store(L.b[0], r0);
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(VMEM_B) : "memory");
+  __builtin_amdgcn_s_waitcnt(WAIT_ALL_BUT_2B);
+  barrier();
+  sc_read(0, sv);
+  b_store(L.b[0], r0, sv);
+  __builtin_amdgcn_s_waitcnt(WAIT);
+  barrier();
 
-  // ---- one step s (stage I = s % 2): issue A of step s + 1 into A stage
-  // 1 - I and the W codes of step s + 2 into `nxt2`; compute on stage I while
-  // dequantizing step s + 1 (held in `nxt1`) into W stage 1 - I; wait for this
-  // wave's A loads; meet the other waves.  Near the end the issued step is
-  // clamped to the last one (the loads are then unused, or rewrite equal
-  // bytes into the idle stage).
+  // ---- step s on stage I = s % 2: read the scales of step s + 1; issue the
+  // next scale-window part, A of step s + 1 into A stage 1 - I and W of step
+  // s + 2 into `nxt2`; run the matrix cores on stage I while dequantizing
+  // step s + 1 (`nxt1`) into W stage 1 - I.  Stage 1 - I was last read in
+  // step s - 1, before the barrier that ended it.  Near the end the issued
+  // step is clamped to the last one (the loads are then unused, or rewrite
+  // equal bytes into the idle stage).
   auto body = [&](auto Ic, int step, Regs &nxt1, Regs &nxt2) {
     constexpr int I = decltype(Ic)::value;
     char *As = L.a[I];
     char *Bs = L.b[I];
+    ScaleRegs v;
+    sc_read(step + 1, v);
+    asm volatile("" ::: "memory");
+    sc_issue((step + 1) & 3, ((step + 1) >> (3 + spg_lg)) + 1);
     a_issue(min(step + 1, nsteps - 1), L.a[1 - I]);
     asm volatile("" ::: "memory");
     b_issue(min(step + 2, nsteps - 1), nxt2);
@@ -208,14 +307,26 @@ __device__ __forceinline__ void tile_gemm_big(const TileProblem &p, int tile_m, 
     fread(As, Bs, 0, f0);
     fread(As, Bs, 1, f1);
     mma(f0);
-    b_store(L.b[1 - I], nxt1);
+    b_store(L.b[1 - I], nxt1, v);
     fread(As, Bs, 2, f0);
     mma(f1);
     fread(As, Bs, 3, f1);
     mma(f0);
     mma(f1);
+    // Keep the fragment reads one sub-step ahead of the matrix cores (the
+    // scheduler would otherwise sink each sub-step's reads down to their
+    // first use and expose the LDS latency four times per step).
+    constexpr int NR = TM + TN, NM = TM * TN;
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * NR, 0);   // reads, sub-steps 0, 1
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);       // MFMA, sub-step 0
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);       // reads, sub-step 2
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);       // MFMA, sub-step 1
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);       // reads, sub-step 3
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);       // MFMA, sub-step 2
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);       // MFMA, sub-step 3
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(VMEM_B) : "memory");
+    __builtin_amdgcn_s_waitcnt(WAIT);
+    barrier();
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
@@ -227,11 +338,12 @@ __device__ __forceinline__ void tile_gemm_big(const TileProblem &p, int tile_m, 
   }
   if (step < nsteps) body(I0{}, step, r1, r0);
 
-  // ---- epilogue
+  // ---- epilogue: 32x32 accumulator value v of a lane is row
+  // 8 (v / 4) + 4 (lane / 32) + v % 4, column lane % 32.
   const int col_in = lane & 31;
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
-    const int col = n0 + wn * 128 + 32 * j + col_in;
+    const int col = n0 + wn * Cfg::WTN + 32 * j + col_in;
     float cs = 1.0f, cb = 0.0f;
     if constexpr (WBITS == 8) cs = bits_to_f32<ACT>(p.S[col]);
     if (p.bias) cb = bits_to_f32_dyn(p.bias[col], p.bias_dt);
@@ -239,7 +351,7 @@ __device__ __forceinline__ void tile_gemm_big(const TileProblem &p, int tile_m, 
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int r = row_lo + wm * 128 + 32 * i + 8 * (v >> 2) + 4 * khalf + (v & 3);
+        const int r = row_lo + wm * Cfg::WTM + 32 * i + 8 * (v >> 2) + 4 * khalf + (v & 3);
         if (r <= row_last) {
           float val = acc[i][j][v];
           if constexpr (WBITS == 8) val *= cs;

@@ -50,12 +50,12 @@ struct TileProblem {
   int w_rows;                // rows of one expert's weight matrix
 };
 
-// INTERLEAVE: 0 = run the stage's matrix-core work, then dequantize the next
-// stage; > 0 = interleave them, with up to that many VALU instructions after
-// each MFMA.
-template <int BM_, int BN_, int WM_, int WN_, int INTERLEAVE_ = 0>
+// PHASE: which waves dequantize the next stage before (rather than after)
+// their matrix-core work of a step -- 0: none; 1: waves 4..7; 2: odd waves.
+// SWZ: LDS chunk placement -- 0: chunk ^ (row % 8); 1: chunk ^ ((row / 2) % 8).
+template <int BM_, int BN_, int WM_, int WN_, int PHASE_ = 0, int SWZ_ = 0>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, INTERLEAVE = INTERLEAVE_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, PHASE = PHASE_, SWZ = SWZ_;
   static constexpr int BK = 64;
   static constexpr int NTHR = 64 * WM * WN;
   static constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
@@ -68,14 +68,23 @@ struct TileCfg {
   static_assert(A_CHUNKS >= 1 && B_SLOTS >= 1, "tile too small for the thread count");
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+template <int SWZ = 0>
+__device__ __forceinline__ int swz(int row, int chunk) {
+  if constexpr (SWZ == 0) return row * 128 + ((chunk ^ (row & 7)) << 4);
+  else return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
+}
 
 // Dequantize one tiled int4 word (codes k0..k0+7, code e at its tiled nibble
 // slot) with scale s and z8 = z - 8 s into 8 packed 16-bit values.
 template <int ACT>
 __device__ __forceinline__ u32x4 dequant_word_w4(uint32_t w, float s, float z8) {
-  const uint32_t m0 = w & 0x0F0F0F0Fu;          // nibble slots 0,2,4,6 -> codes 0,4,1,5
-  const uint32_t m1 = (w >> 4) & 0x0F0F0F0Fu;   // nibble slots 1,3,5,7 -> codes 2,6,3,7
+  uint32_t m0 = w & 0x0F0F0F0Fu;          // nibble slots 0,2,4,6 -> codes 0,4,1,5
+  uint32_t m1 = (w >> 4) & 0x0F0F0F0Fu;   // nibble slots 1,3,5,7 -> codes 2,6,3,7
+  // Hide the masks' known zero bits from the optimizer: it would otherwise
+  // turn each byte extraction into a 4-bit field extract plus a byte-0
+  // convert instead of one v_cvt_f32_ubyteN.
+  asm("" : "+v"(m0));
+  asm("" : "+v"(m1));
   float q0 = static_cast<float>(m0 & 0xFFu), q4 = static_cast<float>((m0 >> 8) & 0xFFu);
   float q1 = static_cast<float>((m0 >> 16) & 0xFFu), q5 = static_cast<float>(m0 >> 24);
   float q2 = static_cast<float>(m1 & 0xFFu), q6 = static_cast<float>((m1 >> 8) & 0xFFu);
@@ -129,7 +138,7 @@ __device__ __forceinline__ void tile_gemm(const TileProblem &p, int tile_m, int 
     const int r = idx >> 3, ch = idx & 7;
     const int grow = row_lo + r;
     const bool live = grow < row_hi;
-    a_lds[c] = swz(r, ch);
+    a_lds[c] = swz<Cfg::SWZ>(r, ch);
     a_keep[c] = live ? 0xFFFFFFFFu : 0u;
     const int srow = live ? grow : row_lo;
     size_t arow;
@@ -161,12 +170,12 @@ __device__ __forceinline__ void tile_gemm(const TileProblem &p, int tile_m, int 
       wrow = n0 + lrow;
     if constexpr (WBITS == 4) {
       b_src[c] = Bbase + (static_cast<size_t>(wrow >> 4) * (K >> 7)) * 1024 + l * 16;
-      b_lds0[c] = swz(lrow, j);        // word 2h   -> k-chunk j      (of the 64-k step)
-      b_lds1[c] = swz(lrow, 4 + j);    // word 2h+1 -> k-chunk 4 + j
+      b_lds0[c] = swz<Cfg::SWZ>(lrow, j);        // word 2h   -> k-chunk j      (of the 64-k step)
+      b_lds1[c] = swz<Cfg::SWZ>(lrow, 4 + j);    // word 2h+1 -> k-chunk 4 + j
       b_sidx[c] = static_cast<size_t>(wrow) * (K / p.group);
     } else {
       b_src[c] = Bbase + (static_cast<size_t>(wrow >> 4) * (K >> 6)) * 1024 + l * 16 + t * 8;
-      b_lds0[c] = swz(lrow, 4 * t + j);
+      b_lds0[c] = swz<Cfg::SWZ>(lrow, 4 * t + j);
       b_lds1[c] = 0;
       b_sidx[c] = 0;
     }
@@ -254,9 +263,9 @@ __device__ __forceinline__ void tile_gemm(const TileProblem &p, int tile_m, int 
       const int chunk = 2 * ks + khalf;
       u32x4 af[TM], bf[TN];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const u32x4 *>(As + swz(a_row[i], chunk));
+      for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const u32x4 *>(As + swz<Cfg::SWZ>(a_row[i], chunk));
 #pragma unroll
-      for (int jn = 0; jn < TN; ++jn) bf[jn] = *reinterpret_cast<const u32x4 *>(Bs + swz(b_row[jn], chunk));
+      for (int jn = 0; jn < TN; ++jn) bf[jn] = *reinterpret_cast<const u32x4 *>(Bs + swz<Cfg::SWZ>(b_row[jn], chunk));
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -273,24 +282,19 @@ __device__ __forceinline__ void tile_gemm(const TileProblem &p, int tile_m, int 
   // Scheduling barriers keep that order: the compiler would otherwise hoist
   // the LDS stores (and the waits on their loads) above the matrix-core work
   // and sink the new loads below it.
+  [[maybe_unused]] const int swave = __builtin_amdgcn_readfirstlane(wave);
+  [[maybe_unused]] const bool late = (Cfg::PHASE == 1) ? ((swave >> 2) & 1) : (swave & 1);
   auto body = [&](int step, Regs &nxt1, Regs &nxt2) {
     gload(min(step + 2, nsteps - 1), nxt2);
     __builtin_amdgcn_sched_barrier(0);
-    compute(step & 1);
-    if constexpr (Cfg::INTERLEAVE == 0) __builtin_amdgcn_sched_barrier(0);
-    lstore((step + 1) & 1, nxt1);
-    if constexpr (Cfg::INTERLEAVE > 0) {
-      // Spread the next stage's dequant (VALU) and LDS writes between this
-      // stage's matrix-core instructions, so each wave keeps the MFMA pipe
-      // busy while it converts weights.
-      constexpr int NMF = TM * TN * (BK / 16);
-#pragma unroll
-      for (int i = 0; i < NMF; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                 // DS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, Cfg::INTERLEAVE, 0);   // VALU
-        if (i % 2 == 1) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0); // DS write
-      }
+    if (Cfg::PHASE != 0 && late) {
+      lstore((step + 1) & 1, nxt1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(step & 1);
+    } else {
+      compute(step & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      lstore((step + 1) & 1, nxt1);
     }
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
