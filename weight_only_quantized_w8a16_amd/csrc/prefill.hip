@@ -49,7 +49,6 @@ __global__ __launch_bounds__(Cfg::NTHR) void k_prefill_dma(TileProblem p, int ti
 namespace {
 
 using CfgX = TileCfg<256, 256, 2, 4>;   // 8 waves, 128x64 per wave
-using CfgD4 = DmaCfg<2, 2>;             // 4 waves, 128x128 per wave, A direct to LDS
 using CfgD8 = DmaCfg<2, 4>;             // 8 waves, 128x64 per wave, A direct to LDS
 using CfgL = TileCfg<256, 128, 4, 2>;   // 8 waves, 64x64 per wave
 using CfgM = TileCfg<128, 128, 2, 2>;   // 4 waves, 64x64 per wave
@@ -111,8 +110,8 @@ hipError_t run_dma(const GemmArgs &a, hipStream_t s) {
 // Tile choice, from on-device sweeps at K = 2048 and 3584: the 256 x 256
 // direct-load tile once there are enough tiles to keep most CUs busy;
 // smaller tiles when the problem would leave CUs idle.
-// QGEMM_PREFILL_TILE=X|D4|D8|L|M|S forces one (tests and tuning); D4 / D8
-// are the 256 x 256 tiles with direct-to-LDS activation loads.
+// QGEMM_PREFILL_TILE=X|D8|L|M|S forces one (tests and tuning); D8 is the
+// 256 x 256 tile with direct-to-LDS activation loads.
 template <int ACT, int WBITS>
 hipError_t dispatch(const GemmArgs &a, hipStream_t s) {
   auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * (a.N / bn); };
@@ -120,7 +119,6 @@ hipError_t dispatch(const GemmArgs &a, hipStream_t s) {
   if (const char *o = std::getenv("QGEMM_PREFILL_TILE")) {
     const std::string c(o);
     if (c == "X" && n256) return run<CfgX, ACT, WBITS>(a, s);
-    if (c == "D4" && n256) return run_dma<CfgD4, ACT, WBITS>(a, s);
     if (c == "D8" && n256) return run_dma<CfgD8, ACT, WBITS>(a, s);
     if (c == "L" && n128) return run<CfgL, ACT, WBITS>(a, s);
     if (c == "M" && n128) return run<CfgM, ACT, WBITS>(a, s);

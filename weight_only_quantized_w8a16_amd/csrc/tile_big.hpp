@@ -242,11 +242,15 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
+  // The weights are the row operand and the activations the column
+  // operand, so acc[i][j] holds C^T: a lane keeps one row of C (activation
+  // row 32 i + lane % 32) and 16 of its columns, four consecutive ones per
+  // group of four values -- which the epilogue stores as 8-byte pieces.
   auto mma = [&](const Frags &f) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = mfma32x32x16<ACT>(f.a[i], f.b[j], acc[i][j]);
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma32x32x16<ACT>(f.b[j], f.a[i], acc[i][j]);
   };
 
   // VMEM instructions a thread issues per step after its direct loads: the
@@ -338,27 +342,48 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
   }
   if (step < nsteps) body(I0{}, step, r1, r0);
 
-  // ---- epilogue: 32x32 accumulator value v of a lane is row
-  // 8 (v / 4) + 4 (lane / 32) + v % 4, column lane % 32.
-  const int col_in = lane & 31;
+  // ---- epilogue: value v of acc[i][j] is C[row][col], row = wave tile row
+  // + 32 i + lane % 32, col = wave tile column + 32 j + 8 (v / 4) +
+  // 4 (lane / 32) + v % 4.  Per i, each wave stages its 32 x 64 block in LDS
+  // (8-byte pieces, 144-byte rows) and stores it as 16-byte row pieces, so
+  // every store instruction writes whole 128-byte lines.  The W stages are
+  // free: the last step ended with a barrier after every wave's last read.
+  static_assert(Cfg::WTN == 64 && Cfg::NTHR == 512, "epilogue staging assumes 8 waves of 128 x 64");
+  char *stg = ((wave >> 2) ? L.b[1] : L.b[0]) + (wave & 3) * (32 * 144);
+  const int row_in = lane & 31;
+  float add[TN][4][4];    // bias (and int8 scale) per column of this lane
+  float mul[TN][4][4];
+  asm volatile("" ::: "memory");   // keep these loads out of the main loop's live range
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int col = n0 + wn * Cfg::WTN + 32 * j + col_in;
-    float cs = 1.0f, cb = 0.0f;
-    if constexpr (WBITS == 8) cs = bits_to_f32<ACT>(p.S[col]);
-    if (p.bias) cb = bits_to_f32_dyn(p.bias[col], p.bias_dt);
+  for (int j = 0; j < TN; ++j)
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = row_lo + wm * Cfg::WTM + 32 * i + 8 * (v >> 2) + 4 * khalf + (v & 3);
-        if (r <= row_last) {
-          float val = acc[i][j][v];
-          if constexpr (WBITS == 8) val *= cs;
-          val += cb;
-          p.C[static_cast<size_t>(r) * p.N + col] = f32_to_bits<ACT>(val);
-        }
+      for (int e = 0; e < 4; ++e) {
+        const int col = n0 + wn * Cfg::WTN + 32 * j + 8 * q + 4 * khalf + e;
+        mul[j][q][e] = (WBITS == 8) ? bits_to_f32<ACT>(p.S[col]) : 1.0f;
+        add[j][q][e] = p.bias ? bits_to_f32_dyn(p.bias[col], p.bias_dt) : 0.0f;
       }
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * q + e] * mul[j][q][e] + add[j][q][e];
+        *reinterpret_cast<u32x2 *>(stg + row_in * 144 + (32 * j + 8 * q + 4 * khalf) * 2) =
+            u32x2{pack2<ACT>(v[0], v[1]), pack2<ACT>(v[2], v[3])};
+      }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int rr = 8 * t + (lane >> 3), ch = lane & 7;
+      const u32x4 val = *reinterpret_cast<const u32x4 *>(stg + rr * 144 + ch * 16);
+      const int r = row_lo + wm * Cfg::WTM + 32 * i + rr;
+      if (r <= row_last)
+        *reinterpret_cast<u32x4 *>(p.C + static_cast<size_t>(r) * p.N + n0 + wn * Cfg::WTN + ch * 8) = val;
+    }
   }
 }
 
