@@ -39,16 +39,36 @@ def check(p, tokens=None, tol=TOL[BF16]):
     return out
 
 
+@pytest.fixture(params=["default", "S"])
+def moe_tile(request, monkeypatch):
+    """Run a test on the default grouped-GEMM tile and on the 128 x 128 one."""
+    if request.param == "S":
+        monkeypatch.setenv("QGEMM_MOE_TILE", "S")
+    else:
+        monkeypatch.delenv("QGEMM_MOE_TILE", raising=False)
+    return request.param
+
+
 @pytest.mark.parametrize("T,H,I,E,k,g", [
     (4, 128, 128, 4, 2, 64), (33, 256, 256, 16, 4, 64), (1, 256, 128, 8, 8, 128),
     (64, 256, 384, 8, 1, 64), (200, 128, 128, 64, 6, 64), (130, 384, 256, 4, 2, 128),
+    (512, 256, 256, 4, 2, 64), (300, 512, 640, 8, 3, 128),
 ])
-def test_moe_small_full(T, H, I, E, k, g):
+def test_moe_small_full(T, H, I, E, k, g, moe_tile):
     p = si.moe_problem(T, H, I, E, k, g, tag="moe-small")
     check(p)
 
 
-def test_moe_fp16():
+def test_moe_expert_tiles_exactly_full(moe_tile):
+    # 256 tokens all routed to experts 5 and 2: two experts of exactly 256 rows.
+    p = si.moe_problem(256, 256, 256, 8, 2, 64, tag="moe-full-tiles")
+    p.logits[:] = 0.0
+    p.logits[:, 5] = 3.0
+    p.logits[:, 2] = 2.0
+    check(p)
+
+
+def test_moe_fp16(moe_tile):
     p = si.moe_problem(48, 256, 256, 8, 2, 64, tag="moe-f16", dtype=FP16)
     check(p, tol=TOL[FP16] * 3)
 
@@ -72,7 +92,7 @@ def test_moe_forced_routes_and_empty_experts():
     check(p)
 
 
-def test_moe_full_size_sampled_tokens():
+def test_moe_full_size_sampled_tokens(moe_tile):
     # 2048 tokens, hidden 2048, inter 1408, 64 experts, top-6, g=64
     p = si.moe_problem(2048, 2048, 1408, 64, 6, 64, tag="cfg4")
     toks = np.unique(np.concatenate([[0, 1, 2047], np.random.default_rng(4).integers(0, 2048, 21)]))

@@ -14,8 +14,14 @@
 //            permutation, gate and up columns in one tile, silu(gate) * up
 //            in the epilogue;
 //   fc2      grouped tile GEMM over the activation rows;
+// The grouped GEMMs use the 256 x 256 direct-load tile (tile_big.hpp) with
+// 256-row expert tiles where the shapes allow it, else the 128 x 128 tile
+// kernel with 128-row expert tiles.
 //   combine  out[t] = sum_j w[t, j] * y[row(t, j)], fp32 in rank order.
+#include <cstdlib>
+
 #include "qg_launch.hpp"
+#include "tile_big.hpp"
 #include "tile_gemm.hpp"
 
 namespace qg {
@@ -23,7 +29,8 @@ namespace qg {
 namespace {
 
 using CfgMoe = TileCfg<128, 128, 2, 2>;
-constexpr int kMoeBM = CfgMoe::BM;
+using CfgMoeDma = DmaCfg<2, 4>;
+constexpr int kMoeBM = CfgMoe::BM;   // smallest expert tile (sizes the tile list)
 
 size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
@@ -95,7 +102,7 @@ __global__ __launch_bounds__(256) void k_moe_route(const float *__restrict__ log
 
 // Single workgroup: counts, offsets, tile list, permutation.
 __global__ __launch_bounds__(1024) void k_moe_plan(const int32_t *__restrict__ ids, int R, int E,
-                                                   int topk, MoeTile *__restrict__ tiles,
+                                                   int topk, int bm, MoeTile *__restrict__ tiles,
                                                    int32_t *__restrict__ ntiles,
                                                    int32_t *__restrict__ row_src,
                                                    int32_t *__restrict__ dest) {
@@ -109,11 +116,11 @@ __global__ __launch_bounds__(1024) void k_moe_plan(const int32_t *__restrict__ i
     int nt = 0;
     for (int e = 0; e < E; ++e) {
       off[e + 1] = off[e] + cnt[e];
-      for (int r0 = off[e]; r0 < off[e + 1]; r0 += kMoeBM) {
+      for (int r0 = off[e]; r0 < off[e + 1]; r0 += bm) {
         MoeTile tl;
         tl.expert = e;
         tl.row0 = r0;
-        tl.row1 = min(r0 + kMoeBM, off[e + 1]);
+        tl.row1 = min(r0 + bm, off[e + 1]);
         tl.pad = 0;
         tiles[nt++] = tl;
       }
@@ -135,6 +142,19 @@ __global__ __launch_bounds__(CfgMoe::NTHR) void k_moe_gemm(TileProblem p, int ti
   const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
   if (tm >= *p.ntiles) return;
   tile_gemm<CfgMoe, ACT, 4, MODE>(p, tm, tn, lds);
+}
+
+template <int ACT, int MODE>
+__global__ __launch_bounds__(CfgMoeDma::NTHR) void k_moe_dma(TileProblem p, int tiles_n) {
+  __shared__ __attribute__((aligned(16))) char a0[CfgMoeDma::STAGE];
+  __shared__ __attribute__((aligned(16))) char a1[CfgMoeDma::STAGE];
+  __shared__ __attribute__((aligned(16))) char b0[CfgMoeDma::STAGE];
+  __shared__ __attribute__((aligned(16))) char b1[CfgMoeDma::STAGE];
+  __shared__ __attribute__((aligned(16))) char sc[2 * CfgMoeDma::SC_WIN];
+  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+  if (tm >= *p.ntiles) return;
+  const DmaLds L{{a0, a1}, {b0, b1}, sc};
+  tile_gemm_dma<CfgMoeDma, ACT, 4, MODE>(p, tm, tn, L);
 }
 
 // out[t, h..h+7] = sum_j w[t, j] * y[dest[t, j], h..h+7]
@@ -186,11 +206,24 @@ hipError_t run_moe(const MoeArgs &a, hipStream_t s) {
   int32_t *ntiles = reinterpret_cast<int32_t *>(ws + L.ntiles);
   uint16_t *act = reinterpret_cast<uint16_t *>(ws + L.act);
   uint16_t *y = reinterpret_cast<uint16_t *>(ws + L.y);
-  const int max_tiles = (R + kMoeBM - 1) / kMoeBM + a.E;
+  // The direct-load tile needs whole 256-column output tiles for fc2, an
+  // even number of groups per row (scale/zero pairs), 4-byte aligned scales
+  // and zeros, and 32-bit offsets.
+  const uintptr_t sz_or = reinterpret_cast<uintptr_t>(a.s1) | reinterpret_cast<uintptr_t>(a.z1) |
+                          reinterpret_cast<uintptr_t>(a.s2) | reinterpret_cast<uintptr_t>(a.z2);
+  const uint64_t lim = uint64_t(1) << 31;
+  const bool dma = a.H % CfgMoeDma::BN == 0 && (a.H / a.group) % 2 == 0 && (a.I / a.group) % 2 == 0 &&
+                   (sz_or & 3) == 0 && uint64_t(a.T) * a.H < lim && uint64_t(R) * a.I < lim &&
+                   uint64_t(2 * a.I) * a.H / 2 < lim;
+  // QGEMM_MOE_TILE=S forces the 128 x 128 path (tests and tuning).
+  const char *force = std::getenv("QGEMM_MOE_TILE");
+  const bool use_dma = dma && !(force && force[0] == 'S');
+  const int bm = use_dma ? CfgMoeDma::BM : kMoeBM;
+  const int max_tiles = (R + bm - 1) / bm + a.E;
 
   hipLaunchKernelGGL(k_moe_route, dim3((a.T + 3) / 4), dim3(256), 0, s, a.logits, a.T, a.E,
                      a.topk, ids, wts);
-  hipLaunchKernelGGL(k_moe_plan, dim3(1), dim3(1024), 0, s, ids, R, a.E, a.topk, tiles, ntiles,
+  hipLaunchKernelGGL(k_moe_plan, dim3(1), dim3(1024), 0, s, ids, R, a.E, a.topk, bm, tiles, ntiles,
                      row_src, dest);
 
   static bool attr = false;
@@ -216,9 +249,16 @@ hipError_t run_moe(const MoeArgs &a, hipStream_t s) {
   p1.b_expert_stride = static_cast<size_t>(2 * a.I) * (a.H / 2);
   p1.s_expert_stride = static_cast<size_t>(2 * a.I) * (a.H / a.group);
   p1.w_rows = 2 * a.I;
-  const int tn1 = a.I / (CfgMoe::BN / 2);
-  hipLaunchKernelGGL((k_moe_gemm<ACT, kMoeFc1>), dim3(max_tiles * tn1), dim3(CfgMoe::NTHR),
-                     CfgMoe::LDS, s, p1, tn1);
+  p1.a_rows = a.T;
+  if (use_dma) {
+    const int tn1 = a.I / (CfgMoeDma::BN / 2);
+    hipLaunchKernelGGL((k_moe_dma<ACT, kMoeFc1>), dim3(max_tiles * tn1), dim3(CfgMoeDma::NTHR), 0, s,
+                       p1, tn1);
+  } else {
+    const int tn1 = a.I / (CfgMoe::BN / 2);
+    hipLaunchKernelGGL((k_moe_gemm<ACT, kMoeFc1>), dim3(max_tiles * tn1), dim3(CfgMoe::NTHR),
+                       CfgMoe::LDS, s, p1, tn1);
+  }
 
   TileProblem p2{};
   p2.A = act;
@@ -235,9 +275,16 @@ hipError_t run_moe(const MoeArgs &a, hipStream_t s) {
   p2.b_expert_stride = static_cast<size_t>(a.H) * (a.I / 2);
   p2.s_expert_stride = static_cast<size_t>(a.H) * (a.I / a.group);
   p2.w_rows = a.H;
-  const int tn2 = a.H / CfgMoe::BN;
-  hipLaunchKernelGGL((k_moe_gemm<ACT, kMoeFc2>), dim3(max_tiles * tn2), dim3(CfgMoe::NTHR),
-                     CfgMoe::LDS, s, p2, tn2);
+  p2.a_rows = R;
+  if (use_dma) {
+    const int tn2 = a.H / CfgMoeDma::BN;
+    hipLaunchKernelGGL((k_moe_dma<ACT, kMoeFc2>), dim3(max_tiles * tn2), dim3(CfgMoeDma::NTHR), 0, s,
+                       p2, tn2);
+  } else {
+    const int tn2 = a.H / CfgMoe::BN;
+    hipLaunchKernelGGL((k_moe_gemm<ACT, kMoeFc2>), dim3(max_tiles * tn2), dim3(CfgMoe::NTHR),
+                       CfgMoe::LDS, s, p2, tn2);
+  }
 
   const long long items = static_cast<long long>(a.T) * (a.H / 8);
   hipLaunchKernelGGL((k_moe_combine<ACT>), dim3(static_cast<unsigned>((items + 255) / 256)),

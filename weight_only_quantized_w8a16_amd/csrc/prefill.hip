@@ -102,6 +102,7 @@ hipError_t run_dma(const GemmArgs &a, hipStream_t s) {
   p.K = a.K;
   p.group = a.group > 0 ? a.group : a.K;
   p.bias_dt = a.bias_dt;
+  p.a_rows = a.M;
   const int tm = (a.M + Cfg::BM - 1) / Cfg::BM, tn = a.N / Cfg::BN;
   hipLaunchKernelGGL((k_prefill_dma<Cfg, ACT, WBITS>), dim3(tm * tn), dim3(Cfg::NTHR), 0, s, p, tn);
   return hipGetLastError();

@@ -63,33 +63,61 @@ __device__ __forceinline__ int dswz(int row, int chunk) {
   return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
 
-template <class Cfg, int ACT, int WBITS>
+// MODE (tile_gemm.hpp): kDense; kMoeFc1 -- rows of one expert's tile, the
+// activation rows gathered through row_src, the 256 weight rows being 128
+// gate and the matching 128 up rows of the expert (wave column block wn
+// holds gate rows 32 wn .. 32 wn + 31 of the tile's 128 outputs, then the
+// same up rows), output silu(gate) * up; kMoeFc2 -- rows of one expert's
+// tile, contiguous.
+template <class Cfg, int ACT, int WBITS, int MODE = kDense>
 __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, int tile_n,
                                               const DmaLds &L) {
   constexpr int BK = Cfg::BK, TM = Cfg::TM, TN = Cfg::TN, NTHR = Cfg::NTHR;
+  static_assert(MODE == kDense || WBITS == 4, "MoE experts are int4");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
   const int K = p.K;
   const int nsteps = K / BK;
-  const int row_lo = tile_m * Cfg::BM;
-  const int row_last = min(p.M, row_lo + Cfg::BM) - 1;
-  const int n0 = tile_n * Cfg::BN;
+  int row_lo, row_last;
+  const uint8_t *Bb = p.B;
+  const uint16_t *Sb = p.S, *Zb = p.Z;
+  uint32_t b_bytes, s_bytes;     // buffer extents (one expert for MoE)
+  if constexpr (MODE == kDense) {
+    row_lo = tile_m * Cfg::BM;
+    row_last = min(p.M, row_lo + Cfg::BM) - 1;
+    b_bytes = static_cast<uint32_t>(static_cast<uint64_t>(p.N) * K * WBITS / 8);
+    s_bytes = (WBITS == 4) ? static_cast<uint32_t>(static_cast<uint64_t>(p.N) * (K / p.group) * 2) : 0u;
+  } else {
+    const MoeTile t = p.tiles[tile_m];
+    row_lo = t.row0;
+    row_last = t.row1 - 1;
+    Bb += static_cast<size_t>(t.expert) * p.b_expert_stride;
+    Sb += static_cast<size_t>(t.expert) * p.s_expert_stride;
+    Zb += static_cast<size_t>(t.expert) * p.s_expert_stride;
+    b_bytes = static_cast<uint32_t>(p.b_expert_stride);
+    s_bytes = static_cast<uint32_t>(p.s_expert_stride * 2);
+  }
+  const int n0 = (MODE == kMoeFc1) ? tile_n * (Cfg::BN / 2) : tile_n * Cfg::BN;
+  // Weight row of LDS row `lrow` (0..255).
+  auto wrow_of = [&](int lrow) {
+    if constexpr (MODE == kMoeFc1)
+      return (((lrow >> 5) & 1) ? p.N : 0) + n0 + 32 * (lrow >> 6) + (lrow & 31);
+    else
+      return n0 + lrow;
+  };
 
   // Buffer resources: 32-bit per-lane offsets, the step's offset in an SGPR.
   // (A flat/global direct-to-LDS load would also be taken by the wait-count
   // pass as a pending LDS access, and every later wait would become a full
   // drain.)
   constexpr int kRsrcFlags = 0x00020000;
-  const uint32_t a_bytes = static_cast<uint32_t>(static_cast<uint64_t>(p.M) * K * 2);
-  const uint32_t b_bytes = static_cast<uint32_t>(static_cast<uint64_t>(p.N) * K * WBITS / 8);
+  const uint32_t a_bytes = static_cast<uint32_t>(static_cast<uint64_t>(p.a_rows) * K * 2);
   const auto rA = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(p.A), 0, static_cast<int>(a_bytes), kRsrcFlags);
-  const auto rB = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(p.B), 0, static_cast<int>(b_bytes), kRsrcFlags);
-  [[maybe_unused]] const uint32_t s_bytes =
-      (WBITS == 4) ? static_cast<uint32_t>(static_cast<uint64_t>(p.N) * (K / p.group) * 2) : 0u;
+  const auto rB = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(Bb), 0, static_cast<int>(b_bytes), kRsrcFlags);
   [[maybe_unused]] const auto rS =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(p.S), 0, static_cast<int>(s_bytes), kRsrcFlags);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(Sb), 0, static_cast<int>(s_bytes), kRsrcFlags);
   [[maybe_unused]] const auto rZ =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(p.Z), 0, static_cast<int>(s_bytes), kRsrcFlags);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(Zb), 0, static_cast<int>(s_bytes), kRsrcFlags);
 
   // ---- A: slot q = (wave * A_DMA + i) * 64 + lane of a stage is row q / 8,
   // placed chunk q % 8; it holds the row's chunk (q % 8) ^ ((row / 2) % 8).
@@ -98,7 +126,8 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
   for (int i = 0; i < Cfg::A_DMA; ++i) {
     const int q = (wave * Cfg::A_DMA + i) * 64 + lane;
     const int r = q >> 3, c = (q & 7) ^ ((r >> 1) & 7);
-    const int grow = min(row_lo + r, row_last);
+    int grow = min(row_lo + r, row_last);
+    if constexpr (MODE == kMoeFc1) grow = p.row_src[grow];
     a_voff[i] = (static_cast<uint32_t>(grow) * static_cast<uint32_t>(K) + c * 8) * 2u;
   }
   auto a_issue = [&](int step, char *stage) {
@@ -122,7 +151,7 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
     else { t = idx & 1; l = (idx >> 1) & 63; bi = idx >> 7; }
     const int nl = l & 15, j = l >> 4;
     const int lrow = bi * 16 + nl;
-    const int wrow = n0 + lrow;
+    const int wrow = wrow_of(lrow);
     if constexpr (WBITS == 4) {
       b_src[c] = static_cast<uint32_t>(wrow >> 4) * static_cast<uint32_t>(K >> 7) * 1024u + l * 16;
       b_lds0[c] = dswz(lrow, j);          // word 2h   -> k-chunk j
@@ -170,11 +199,13 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
 #pragma unroll
   for (int i = 0; i < Cfg::SC_DMA; ++i) {
     const int slot = wave * Cfg::SC_DMA + i;
-    sc_voff[i] = (static_cast<uint32_t>(n0 + slot * 16 + (lane >> 2)) * static_cast<uint32_t>(kg) + (lane & 3) * 2) * 2u;
+    sc_voff[i] = (static_cast<uint32_t>(wrow_of(slot * 16 + (lane >> 2))) * static_cast<uint32_t>(kg) + (lane & 3) * 2) * 2u;
   }
+  // Rows 128 .. 255 of the tile are weight rows 128 (fc1: 64) further on.
+  constexpr int kHalfRows = (MODE == kMoeFc1) ? 64 : 128;
   auto sc_issue = [&](int t, int w) {
     if constexpr (WBITS == 4) {
-      const int soff = (t & 1) * 128 * kg * 2 + w * 16;
+      const int soff = (t & 1) * kHalfRows * kg * 2 + w * 16;
       char *dst = L.sc + (w & 1) * Cfg::SC_WIN + (t * 8 + wave * Cfg::SC_DMA) * 256;
 #pragma unroll
       for (int i = 0; i < Cfg::SC_DMA; ++i)
@@ -351,6 +382,34 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
   static_assert(Cfg::WTN == 64 && Cfg::NTHR == 512, "epilogue staging assumes 8 waves of 128 x 64");
   char *stg = ((wave >> 2) ? L.b[1] : L.b[0]) + (wave & 3) * (32 * 144);
   const int row_in = lane & 31;
+  if constexpr (MODE == kMoeFc1) {
+    // acc[i][0] is gate, acc[i][1] up, of output columns
+    // n0 + 32 wn + 8 (v / 4) + 4 (lane / 32) + v % 4; 32 x 32 blocks staged
+    // in 80-byte rows.
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float g = acc[i][0][4 * q + e], u = acc[i][1][4 * q + e];
+          v[e] = g / (1.0f + __expf(-g)) * u;
+        }
+        *reinterpret_cast<u32x2 *>(stg + row_in * 80 + (8 * q + 4 * khalf) * 2) =
+            u32x2{pack2<ACT>(v[0], v[1]), pack2<ACT>(v[2], v[3])};
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int rr = 16 * t + (lane >> 2), ch = lane & 3;
+        const u32x4 val = *reinterpret_cast<const u32x4 *>(stg + rr * 80 + ch * 16);
+        const int r = row_lo + wm * Cfg::WTM + 32 * i + rr;
+        if (r <= row_last)
+          *reinterpret_cast<u32x4 *>(p.C + static_cast<size_t>(r) * p.N + n0 + 32 * wn + ch * 8) = val;
+      }
+    }
+    return;
+  }
   float add[TN][4][4];    // bias (and int8 scale) per column of this lane
   float mul[TN][4][4];
   asm volatile("" ::: "memory");   // keep these loads out of the main loop's live range

@@ -48,6 +48,7 @@ struct TileProblem {
   size_t b_expert_stride;    // bytes of tiled codes per expert
   size_t s_expert_stride;    // scale/zero elements per expert
   int w_rows;                // rows of one expert's weight matrix
+  int a_rows;                // rows of A (fc1: tokens; else M)
 };
 
 // PHASE: which waves dequantize the next stage before (rather than after)
