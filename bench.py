@@ -66,16 +66,23 @@ DECODE_SOURCES = ["weight_only_quantized_w8a16_amd/csrc/decode.hip",
                   "weight_only_quantized_w8a16_amd/csrc/qg_common.hpp"]
 
 
-def load_traffic():
-    """HBM bytes per launch of the headline kernel from committed rocprofv3
-    counter runs, if they were taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", "traffic_decode_w4_m1_n131072.json")
+PREFILL_SOURCES = ["weight_only_quantized_w8a16_amd/csrc/prefill.hip",
+                   "weight_only_quantized_w8a16_amd/csrc/tile_big.hpp",
+                   "weight_only_quantized_w8a16_amd/csrc/tile_gemm.hpp",
+                   "weight_only_quantized_w8a16_amd/csrc/qg_common.hpp"]
+PREFILL_TRAFFIC_SHAPE = (512, 131072, 64)
+
+
+def load_traffic(name="traffic_decode_w4_m1_n131072.json", sources=None):
+    """HBM bytes per launch of a kernel from committed rocprofv3 counter
+    runs, if they were taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", name)
     try:
         with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_digest") != source_digest(DECODE_SOURCES):
+    if rec.get("source_digest") != source_digest(sources or DECODE_SOURCES):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -114,7 +121,8 @@ def gpu_lead(torch, ms=20.0):
 
 
 def kernel_only(args, torch, qg, si):
-    """Only the N=131072 M=1 GEMV, `--steps` times, then a plain copy kernel over
+    """Only the N=131072 M=1 GEMV, `--steps` times, the M=512 N=131072 g=64
+    prefill GEMM (fp16 bias) `--steps` times, then a plain copy kernel over
     512 MiB three times (torch's elementwise negation: reads 512 MiB, writes
     512 MiB, in full cache lines): the workload for rocprofv3 counter runs, the
     copy of known size calibrating FETCH_SIZE / WRITE_SIZE."""
@@ -127,12 +135,23 @@ def kernel_only(args, torch, qg, si):
     for i in range(args.steps):
         B, S, Z = w[i]
         qg.gemm_w4a16(A, B, S, Z, None, DECODE_G, out=C)
+    del w, C
+    pm, pn, pg = PREFILL_TRAFFIC_SHAPE
+    wp = Weights(torch, qg, si, pn, 2048, pg, "cfg3", 2, bias=True)
+    Ap = torch.from_numpy(si.activations(pm, 2048, si.seed_of("cfg3", "a", pm, 2048))
+                          .view("int16")).view(torch.bfloat16).to(dev)
+    Cp = torch.empty((pm, pn), dtype=torch.bfloat16, device=dev)
+    for i in range(args.steps):
+        B, S, Z = wp[i]
+        qg.gemm_w4a16(Ap, B, S, Z, wp.bias, pg, out=Cp)
+    del wp, Cp
     src = torch.ones(128 << 20, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     for _ in range(3):
         torch.neg(src, out=dst)
     torch.cuda.synchronize()
-    log(f"kernel-only: {args.steps} GEMVs (M=1, N={n}) and 3 copies of 512 MiB")
+    log(f"kernel-only: {args.steps} GEMVs (M=1, N={n}), {args.steps} prefill GEMMs "
+        f"(M={pm}, N={pn}, g={pg}) and 3 copies of 512 MiB")
 
 
 def run(args):
@@ -272,11 +291,16 @@ def run(args):
                                     "frac": round(flop / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 3)}
             del w, C
         tf = tot_flop / (tot_ms * 1e-3) / 1e12
+        pm, pn, pg = PREFILL_TRAFFIC_SHAPE
         prefill = {"metric": "prefill TFLOPS at M=512 (W4A16, K=2048, fp16 bias)",
                    "value": round(tf, 1), "unit": "TFLOP/s",
                    "roofline": {"bound": "mfma", "achieved": round(tf, 1),
                                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None},
+                                "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                                "traffic": load_traffic("traffic_prefill_w4_m512_n131072.json",
+                                                        PREFILL_SOURCES),
+                                "traffic_kernel": f"k_prefill_dma (M={pm}, N={pn}, K=2048, g={pg})",
+                                "bytes_per_launch": w4_bytes(pm, pn, 2048, pg, bias=True)},
                    "shapes": shapes}
         log(f"prefill: {prefill}")
         torch.cuda.empty_cache()

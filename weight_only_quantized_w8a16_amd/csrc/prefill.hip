@@ -27,11 +27,28 @@ __device__ __forceinline__ int xcd_linear_id() {
   return (xcd < rem) ? xcd * (per + 1) + loc : rem * (per + 1) + (xcd - rem) * per + loc;
 }
 
+// Tile of linear position `id` (after the XCD renumbering): groups of up to
+// four rows of tiles, walked column by column, so the weight tile of one
+// column is used by all row tiles of the group while it is still in L2
+// (consecutive positions share an XCD), and the group's activation rows (a
+// few MiB) stay resident.
+__device__ __forceinline__ void grouped_tile(int id, int tiles_m, int tiles_n, int &tm, int &tn) {
+  constexpr int G = 4;
+  const int per_group = G * tiles_n;
+  const int first_m = (id / per_group) * G;
+  const int gsz = min(G, tiles_m - first_m);
+  const int in = id - (id / per_group) * per_group;
+  tm = first_m + in % gsz;
+  tn = in / gsz;
+}
+
 template <class Cfg, int ACT, int WBITS>
 __global__ __launch_bounds__(Cfg::NTHR) void k_prefill(TileProblem p, int tiles_n) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int id = xcd_linear_id();
-  tile_gemm<Cfg, ACT, WBITS, kDense>(p, id / tiles_n, id % tiles_n, lds);
+  int tm, tn;
+  grouped_tile(id, gridDim.x / tiles_n, tiles_n, tm, tn);
+  tile_gemm<Cfg, ACT, WBITS, kDense>(p, tm, tn, lds);
 }
 
 template <class Cfg, int ACT, int WBITS>
@@ -43,7 +60,9 @@ __global__ __launch_bounds__(Cfg::NTHR) void k_prefill_dma(TileProblem p, int ti
   __shared__ __attribute__((aligned(16))) char sc[2 * Cfg::SC_WIN];
   const DmaLds L{{a0, a1}, {b0, b1}, sc};
   const int id = xcd_linear_id();
-  tile_gemm_dma<Cfg, ACT, WBITS>(p, id / tiles_n, id % tiles_n, L);
+  int tm, tn;
+  grouped_tile(id, gridDim.x / tiles_n, tiles_n, tm, tn);
+  tile_gemm_dma<Cfg, ACT, WBITS>(p, tm, tn, L);
 }
 
 namespace {
