@@ -146,10 +146,10 @@ __global__ __launch_bounds__(CfgMoe::NTHR) void k_moe_gemm(TileProblem p, int ti
 
 template <int ACT, int MODE>
 __global__ __launch_bounds__(CfgMoeDma::NTHR) void k_moe_dma(TileProblem p, int tiles_n) {
-  __shared__ __attribute__((aligned(16))) char a0[CfgMoeDma::STAGE];
-  __shared__ __attribute__((aligned(16))) char a1[CfgMoeDma::STAGE];
-  __shared__ __attribute__((aligned(16))) char b0[CfgMoeDma::STAGE];
-  __shared__ __attribute__((aligned(16))) char b1[CfgMoeDma::STAGE];
+  __shared__ __attribute__((aligned(16))) char a0[CfgMoeDma::STAGE_A];
+  __shared__ __attribute__((aligned(16))) char a1[CfgMoeDma::STAGE_A];
+  __shared__ __attribute__((aligned(16))) char b0[CfgMoeDma::STAGE_B];
+  __shared__ __attribute__((aligned(16))) char b1[CfgMoeDma::STAGE_B];
   __shared__ __attribute__((aligned(16))) char sc[2 * CfgMoeDma::SC_WIN];
   const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
   if (tm >= *p.ntiles) return;

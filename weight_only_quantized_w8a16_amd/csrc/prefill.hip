@@ -10,6 +10,7 @@
 // written back to memory.
 #include <cstdlib>
 #include <string>
+#include <type_traits>
 
 #include "qg_launch.hpp"
 #include "tile_big.hpp"
@@ -53,10 +54,10 @@ __global__ __launch_bounds__(Cfg::NTHR) void k_prefill(TileProblem p, int tiles_
 
 template <class Cfg, int ACT, int WBITS>
 __global__ __launch_bounds__(Cfg::NTHR) void k_prefill_dma(TileProblem p, int tiles_n) {
-  __shared__ __attribute__((aligned(16))) char a0[Cfg::STAGE];
-  __shared__ __attribute__((aligned(16))) char a1[Cfg::STAGE];
-  __shared__ __attribute__((aligned(16))) char b0[Cfg::STAGE];
-  __shared__ __attribute__((aligned(16))) char b1[Cfg::STAGE];
+  __shared__ __attribute__((aligned(16))) char a0[Cfg::STAGE_A];
+  __shared__ __attribute__((aligned(16))) char a1[Cfg::STAGE_A];
+  __shared__ __attribute__((aligned(16))) char b0[Cfg::STAGE_B];
+  __shared__ __attribute__((aligned(16))) char b1[Cfg::STAGE_B];
   __shared__ __attribute__((aligned(16))) char sc[2 * Cfg::SC_WIN];
   const DmaLds L{{a0, a1}, {b0, b1}, sc};
   const int id = xcd_linear_id();
@@ -69,6 +70,7 @@ namespace {
 
 using CfgX = TileCfg<256, 256, 2, 4>;   // 8 waves, 128x64 per wave
 using CfgD8 = DmaCfg<2, 4>;             // 8 waves, 128x64 per wave, A direct to LDS
+using CfgD8N = DmaCfg<4, 2, 128>;       // 256 x 128 tile, 8 waves of 64x64
 using CfgL = TileCfg<256, 128, 4, 2>;   // 8 waves, 64x64 per wave
 using CfgM = TileCfg<128, 128, 2, 2>;   // 4 waves, 64x64 per wave
 using CfgS = TileCfg<64, 64, 2, 2>;     // 4 waves, 32x32 per wave
@@ -104,11 +106,13 @@ template <class Cfg, int ACT, int WBITS>
 hipError_t run_dma(const GemmArgs &a, hipStream_t s) {
   // The kernel keeps 32-bit element / byte offsets.
   const uint64_t lim = uint64_t(1) << 31;
-  if (uint64_t(a.M) * a.K >= lim || uint64_t(a.N) * a.K * WBITS / 8 >= lim) return run<CfgX, ACT, WBITS>(a, s);
+  // Otherwise the generic tile kernel of the same width takes the problem.
+  using Fallback = std::conditional_t<Cfg::BN == 256, CfgX, CfgL>;
+  if (uint64_t(a.M) * a.K >= lim || uint64_t(a.N) * a.K * WBITS / 8 >= lim) return run<Fallback, ACT, WBITS>(a, s);
   // int4 scales/zeros arrive as 4-byte pairs of groups.
   if (WBITS == 4 && (((a.K / a.group) & 1) != 0 || (reinterpret_cast<uintptr_t>(a.S) & 3) != 0 ||
                      (reinterpret_cast<uintptr_t>(a.Z) & 3) != 0))
-    return run<CfgX, ACT, WBITS>(a, s);
+    return run<Fallback, ACT, WBITS>(a, s);
   TileProblem p{};
   p.A = a.A;
   p.B = static_cast<const uint8_t *>(a.B);
@@ -130,8 +134,9 @@ hipError_t run_dma(const GemmArgs &a, hipStream_t s) {
 // Tile choice, from on-device sweeps at K = 2048 and 3584: the 256 x 256
 // direct-load tile once there are enough tiles to keep most CUs busy;
 // smaller tiles when the problem would leave CUs idle.
-// QGEMM_PREFILL_TILE=X|D8|L|M|S forces one (tests and tuning); D8 is the
-// 256 x 256 tile with direct-to-LDS activation loads.
+// QGEMM_PREFILL_TILE=X|D8|D8N|L|M|S forces one (tests and tuning); D8 and
+// D8N are the 256 x 256 and 256 x 128 tiles with direct-to-LDS activation
+// loads.
 template <int ACT, int WBITS>
 hipError_t dispatch(const GemmArgs &a, hipStream_t s) {
   auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * (a.N / bn); };
@@ -140,11 +145,13 @@ hipError_t dispatch(const GemmArgs &a, hipStream_t s) {
     const std::string c(o);
     if (c == "X" && n256) return run<CfgX, ACT, WBITS>(a, s);
     if (c == "D8" && n256) return run_dma<CfgD8, ACT, WBITS>(a, s);
+    if (c == "D8N" && n128) return run_dma<CfgD8N, ACT, WBITS>(a, s);
     if (c == "L" && n128) return run<CfgL, ACT, WBITS>(a, s);
     if (c == "M" && n128) return run<CfgM, ACT, WBITS>(a, s);
     if (c == "S") return run<CfgS, ACT, WBITS>(a, s);
   }
   if (n256 && a.M > 128 && tiles(256, 256) >= 160) return run_dma<CfgD8, ACT, WBITS>(a, s);
+  if (n128 && a.M > 128 && tiles(256, 128) >= 128) return run_dma<CfgD8N, ACT, WBITS>(a, s);
   if (n128 && a.M > 128 && tiles(256, 128) >= 200) return run<CfgL, ACT, WBITS>(a, s);
   if (n128 && a.M > 64 && tiles(128, 128) >= 256) return run<CfgM, ACT, WBITS>(a, s);
   return run<CfgS, ACT, WBITS>(a, s);

@@ -1,6 +1,6 @@
-// tile_big.hpp -- the 256 x 256 prefill GEMM tile for gfx950 with the
-// activations loaded straight into LDS: C = A . W^T for one 256 x 256 output
-// tile per workgroup, WM x WN waves, each wave a (256 / WM) x (256 / WN)
+// tile_big.hpp -- the 256 x BN (BN = 256 or 128) prefill GEMM tile for gfx950
+// with the activations loaded straight into LDS: C = A . W^T for one output
+// tile per workgroup, WM x WN waves, each wave a (256 / WM) x (BN / WN)
 // block of 32 x 32 accumulators.
 //
 // Per 64-k step:
@@ -37,19 +37,22 @@
 
 namespace qg {
 
-template <int WM_, int WN_>
+template <int WM_, int WN_, int BN_ = 256>
 struct DmaCfg {
   static constexpr int WM = WM_, WN = WN_;
-  static constexpr int BM = 256, BN = 256, BK = 64;
+  static constexpr int BM = 256, BN = BN_, BK = 64;
   static constexpr int NTHR = 64 * WM * WN;
   static constexpr int WTM = BM / WM, WTN = BN / WN;   // wave tile
   static constexpr int TM = WTM / 32, TN = WTN / 32;   // 32x32 accumulators per wave
-  static constexpr int STAGE = 256 * 128;              // bytes per LDS stage (A or W)
+  static constexpr int STAGE_A = BM * 128;             // bytes per A stage
+  static constexpr int STAGE_B = BN * 128;             // bytes per W stage
   static constexpr int A_DMA = BM * 8 / NTHR;          // direct loads per thread per step
   static constexpr int NB4 = BN * 4 / NTHR;            // int4: 8-byte code runs per thread
   static constexpr int NB8 = BN * 8 / NTHR;            // int8: 8-byte code runs per thread
-  static constexpr int SC_WIN = 8192;                   // bytes per scale/zero window
-  static constexpr int SC_DMA = 512 / NTHR;             // 4-byte window loads per thread per step
+  static constexpr int SC_WIN = 2 * BN * 16;           // bytes per scale/zero window
+  static constexpr int SC_PARTS = BN / 64;             // 2 KiB parts per window
+  static constexpr int SC_DMA = 512 / NTHR;            // 4-byte window loads per thread per step
+  static_assert(BN == 128 || BN == 256, "tile width");
   static_assert(A_DMA >= 1 && NB4 >= 1 && SC_DMA >= 1, "thread count");
 };
 
@@ -74,6 +77,7 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
                                               const DmaLds &L) {
   constexpr int BK = Cfg::BK, TM = Cfg::TM, TN = Cfg::TN, NTHR = Cfg::NTHR;
   static_assert(MODE == kDense || WBITS == 4, "MoE experts are int4");
+  static_assert(MODE != kMoeFc1 || Cfg::BN == 256, "fc1 pairs 128 gate with 128 up rows");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
   const int K = p.K;
@@ -180,16 +184,17 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
   };
 
   // ---- int4 scale/zero windows.  Window w holds groups 8w .. 8w + 7 of the
-  // tile's 256 rows: byte (part * 256 + row) * 16 + 2 * (group % 8), part 0
-  // the scales, 1 the zeros; windows alternate between two buffers.  Step u
-  // uses group u / spg (spg = group_size / 64 steps per group).  A direct
-  // load writes 4 bytes per lane (two groups), so a window is four parts of
-  // 2 KiB; part t, slot = wave * SC_DMA + i covers rows
-  // 128 (t % 2) + 16 slot + lane / 4, groups 2 (lane % 4) + {0, 1}, of part
-  // t / 2.  At the top of step s, before any new direct load, each thread
-  // reads the scales of step s + 1 (dequantized in step s) from LDS; then
-  // part (s + 1) % 4 of window (s + 1) / (8 spg) + 1 is issued (every part
-  // at least twice per window, the repeats rewriting equal bytes).  A window
+  // tile's BN rows: byte (c * BN + row) * 16 + 2 * (group % 8), component c
+  // 0 the scales, 1 the zeros; windows alternate between two buffers.  Step
+  // u uses group u / spg (spg = group_size / 64 steps per group).  A direct
+  // load writes 4 bytes per lane (two groups), so a window is BN / 64 parts
+  // of 2 KiB; part t, slot = wave * SC_DMA + i covers rows
+  // 128 (t % (BN / 128)) + 16 slot + lane / 4, groups 2 (lane % 4) + {0, 1},
+  // of component t / (BN / 128).  At the top of step s, before any new
+  // direct load, each thread reads the scales of step s + 1 (dequantized in
+  // step s) from LDS; then part (s + 1) % (BN / 64) of window
+  // (s + 1) / (8 spg) + 1 is issued (every part at least twice per window,
+  // the repeats rewriting equal bytes).  A window
   // is complete one step before its first use, and its buffer was last read
   // one step before its first part lands.  Windows past the last group read
   // other rows or (past the end of the matrices) zeros; they are never used.
@@ -201,15 +206,16 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
     const int slot = wave * Cfg::SC_DMA + i;
     sc_voff[i] = (static_cast<uint32_t>(wrow_of(slot * 16 + (lane >> 2))) * static_cast<uint32_t>(kg) + (lane & 3) * 2) * 2u;
   }
-  // Rows 128 .. 255 of the tile are weight rows 128 (fc1: 64) further on.
+  // Rows 128 .. 255 of a 256-row tile are weight rows 128 (fc1: 64) further on.
   constexpr int kHalfRows = (MODE == kMoeFc1) ? 64 : 128;
+  constexpr int PPC = Cfg::BN / 128;   // parts per component
   auto sc_issue = [&](int t, int w) {
     if constexpr (WBITS == 4) {
-      const int soff = (t & 1) * kHalfRows * kg * 2 + w * 16;
+      const int soff = (t % PPC) * kHalfRows * kg * 2 + w * 16;
       char *dst = L.sc + (w & 1) * Cfg::SC_WIN + (t * 8 + wave * Cfg::SC_DMA) * 256;
 #pragma unroll
       for (int i = 0; i < Cfg::SC_DMA; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(t >= 2 ? rZ : rS,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(t >= PPC ? rZ : rS,
                                                  (__attribute__((address_space(3))) void *)(dst + i * 256), 4,
                                                  sc_voff[i], soff, 0, 0);
     }
@@ -224,7 +230,7 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
 #pragma unroll
       for (int c = 0; c < NB; ++c) {
         v.s[c] = *reinterpret_cast<const uint16_t *>(win + b_sc[c]);
-        v.z[c] = *reinterpret_cast<const uint16_t *>(win + 4096 + b_sc[c]);
+        v.z[c] = *reinterpret_cast<const uint16_t *>(win + Cfg::BN * 16 + b_sc[c]);
       }
     }
   };
@@ -306,7 +312,7 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
   Regs r0, r1;
   ScaleRegs sv;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) sc_issue(t, 0);
+  for (int t = 0; t < Cfg::SC_PARTS; ++t) sc_issue(t, 0);
   sc_issue(0, 1);
   a_issue(0, L.a[0]);
   asm volatile("" ::: "memory");
@@ -333,7 +339,7 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
     ScaleRegs v;
     sc_read(step + 1, v);
     asm volatile("" ::: "memory");
-    sc_issue((step + 1) & 3, ((step + 1) >> (3 + spg_lg)) + 1);
+    sc_issue((step + 1) % Cfg::SC_PARTS, ((step + 1) >> (3 + spg_lg)) + 1);
     a_issue(min(step + 1, nsteps - 1), L.a[1 - I]);
     asm volatile("" ::: "memory");
     b_issue(min(step + 2, nsteps - 1), nxt2);
@@ -377,10 +383,10 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
   // + 32 i + lane % 32, col = wave tile column + 32 j + 8 (v / 4) +
   // 4 (lane / 32) + v % 4.  Per i, each wave stages its 32 x 64 block in LDS
   // (8-byte pieces, 144-byte rows) and stores it as 16-byte row pieces, so
-  // every store instruction writes whole 128-byte lines.  The W stages are
+  // every store instruction writes whole 128-byte lines.  The A stages are
   // free: the last step ended with a barrier after every wave's last read.
-  static_assert(Cfg::WTN == 64 && Cfg::NTHR == 512, "epilogue staging assumes 8 waves of 128 x 64");
-  char *stg = ((wave >> 2) ? L.b[1] : L.b[0]) + (wave & 3) * (32 * 144);
+  static_assert(Cfg::WTN == 64 && Cfg::NTHR == 512, "epilogue staging assumes 8 waves, 64 columns each");
+  char *stg = ((wave >> 2) ? L.a[1] : L.a[0]) + (wave & 3) * (32 * 144);
   const int row_in = lane & 31;
   if constexpr (MODE == kMoeFc1) {
     // acc[i][0] is gate, acc[i][1] up, of output columns
