@@ -100,34 +100,62 @@ __global__ __launch_bounds__(256) void k_moe_route(const float *__restrict__ log
   }
 }
 
-// Single workgroup: counts, offsets, tile list, permutation.
+// Single workgroup: counts, offsets, tile list, permutation.  The exclusive
+// scans over experts (rows and tiles) run in one wave, the tile list is
+// written by one thread per expert, and rows take their slot within the
+// expert through LDS atomics (the order of rows inside an expert does not
+// change any output: every row is computed independently).
 __global__ __launch_bounds__(1024) void k_moe_plan(const int32_t *__restrict__ ids, int R, int E,
                                                    int topk, int bm, MoeTile *__restrict__ tiles,
                                                    int32_t *__restrict__ ntiles,
                                                    int32_t *__restrict__ row_src,
                                                    int32_t *__restrict__ dest) {
-  __shared__ int cnt[256], off[257], fill[256];
+  __shared__ int cnt[256], off[256], toff[256], fill[256];
   for (int e = threadIdx.x; e < 256; e += blockDim.x) { cnt[e] = 0; fill[e] = 0; }
   __syncthreads();
   for (int r = threadIdx.x; r < R; r += blockDim.x) atomicAdd(&cnt[ids[r]], 1);
   __syncthreads();
-  if (threadIdx.x == 0) {
-    off[0] = 0;
-    int nt = 0;
-    for (int e = 0; e < E; ++e) {
-      off[e + 1] = off[e] + cnt[e];
-      for (int r0 = off[e]; r0 < off[e + 1]; r0 += bm) {
-        MoeTile tl;
-        tl.expert = e;
-        tl.row0 = r0;
-        tl.row1 = min(r0 + bm, off[e + 1]);
-        tl.pad = 0;
-        tiles[nt++] = tl;
-      }
+  if (threadIdx.x < 64) {
+    // lane l scans experts 4l .. 4l + 3, then the lanes' totals
+    const int lane = threadIdx.x;
+    int c[4], t[4], rs = 0, ts = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * lane + i;
+      c[i] = e < E ? cnt[e] : 0;
+      t[i] = (c[i] + bm - 1) / bm;
+      rs += c[i];
+      ts += t[i];
     }
-    *ntiles = nt;
+    int ri = rs, ti = ts;   // inclusive scans over lanes
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int ru = __shfl_up(ri, d), tu = __shfl_up(ti, d);
+      if (lane >= d) { ri += ru; ti += tu; }
+    }
+    int ro = ri - rs, to = ti - ts;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * lane + i;
+      if (e < E) { off[e] = ro; toff[e] = to; }
+      ro += c[i];
+      to += t[i];
+    }
+    if (lane == 63) *ntiles = ti;
   }
   __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    const int r1 = off[e] + cnt[e];
+    int k = toff[e];
+    for (int r0 = off[e]; r0 < r1; r0 += bm) {
+      MoeTile tl;
+      tl.expert = e;
+      tl.row0 = r0;
+      tl.row1 = min(r0 + bm, r1);
+      tl.pad = 0;
+      tiles[k++] = tl;
+    }
+  }
   for (int r = threadIdx.x; r < R; r += blockDim.x) {
     const int e = ids[r];
     const int pos = off[e] + atomicAdd(&fill[e], 1);
