@@ -51,12 +51,9 @@ struct TileProblem {
   int a_rows;                // rows of A (fc1: tokens; else M)
 };
 
-// PHASE: which waves dequantize the next stage before (rather than after)
-// their matrix-core work of a step -- 0: none; 1: waves 4..7; 2: odd waves.
-// SWZ: LDS chunk placement -- 0: chunk ^ (row % 8); 1: chunk ^ ((row / 2) % 8).
-template <int BM_, int BN_, int WM_, int WN_, int PHASE_ = 0, int SWZ_ = 0>
+template <int BM_, int BN_, int WM_, int WN_>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, PHASE = PHASE_, SWZ = SWZ_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
   static constexpr int BK = 64;
   static constexpr int NTHR = 64 * WM * WN;
   static constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
@@ -69,11 +66,7 @@ struct TileCfg {
   static_assert(A_CHUNKS >= 1 && B_SLOTS >= 1, "tile too small for the thread count");
 };
 
-template <int SWZ = 0>
-__device__ __forceinline__ int swz(int row, int chunk) {
-  if constexpr (SWZ == 0) return row * 128 + ((chunk ^ (row & 7)) << 4);
-  else return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
-}
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
 
 // Dequantize one tiled int4 word (codes k0..k0+7, code e at its tiled nibble
 // slot) with scale s and z8 = z - 8 s into 8 packed 16-bit values.
@@ -139,7 +132,7 @@ __device__ __forceinline__ void tile_gemm(const TileProblem &p, int tile_m, int 
     const int r = idx >> 3, ch = idx & 7;
     const int grow = row_lo + r;
     const bool live = grow < row_hi;
-    a_lds[c] = swz<Cfg::SWZ>(r, ch);
+    a_lds[c] = swz(r, ch);
     a_keep[c] = live ? 0xFFFFFFFFu : 0u;
     const int srow = live ? grow : row_lo;
     size_t arow;
@@ -171,12 +164,12 @@ __device__ __forceinline__ void tile_gemm(const TileProblem &p, int tile_m, int 
       wrow = n0 + lrow;
     if constexpr (WBITS == 4) {
       b_src[c] = Bbase + (static_cast<size_t>(wrow >> 4) * (K >> 7)) * 1024 + l * 16;
-      b_lds0[c] = swz<Cfg::SWZ>(lrow, j);        // word 2h   -> k-chunk j      (of the 64-k step)
-      b_lds1[c] = swz<Cfg::SWZ>(lrow, 4 + j);    // word 2h+1 -> k-chunk 4 + j
+      b_lds0[c] = swz(lrow, j);        // word 2h   -> k-chunk j      (of the 64-k step)
+      b_lds1[c] = swz(lrow, 4 + j);    // word 2h+1 -> k-chunk 4 + j
       b_sidx[c] = static_cast<size_t>(wrow) * (K / p.group);
     } else {
       b_src[c] = Bbase + (static_cast<size_t>(wrow >> 4) * (K >> 6)) * 1024 + l * 16 + t * 8;
-      b_lds0[c] = swz<Cfg::SWZ>(lrow, 4 * t + j);
+      b_lds0[c] = swz(lrow, 4 * t + j);
       b_lds1[c] = 0;
       b_sidx[c] = 0;
     }
@@ -264,9 +257,9 @@ __device__ __forceinline__ void tile_gemm(const TileProblem &p, int tile_m, int 
       const int chunk = 2 * ks + khalf;
       u32x4 af[TM], bf[TN];
 #pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const u32x4 *>(As + swz<Cfg::SWZ>(a_row[i], chunk));
+      for (int i = 0; i < TM; ++i) af[i] = *reinterpret_cast<const u32x4 *>(As + swz(a_row[i], chunk));
 #pragma unroll
-      for (int jn = 0; jn < TN; ++jn) bf[jn] = *reinterpret_cast<const u32x4 *>(Bs + swz<Cfg::SWZ>(b_row[jn], chunk));
+      for (int jn = 0; jn < TN; ++jn) bf[jn] = *reinterpret_cast<const u32x4 *>(Bs + swz(b_row[jn], chunk));
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -283,20 +276,12 @@ __device__ __forceinline__ void tile_gemm(const TileProblem &p, int tile_m, int 
   // Scheduling barriers keep that order: the compiler would otherwise hoist
   // the LDS stores (and the waits on their loads) above the matrix-core work
   // and sink the new loads below it.
-  [[maybe_unused]] const int swave = __builtin_amdgcn_readfirstlane(wave);
-  [[maybe_unused]] const bool late = (Cfg::PHASE == 1) ? ((swave >> 2) & 1) : (swave & 1);
   auto body = [&](int step, Regs &nxt1, Regs &nxt2) {
     gload(min(step + 2, nsteps - 1), nxt2);
     __builtin_amdgcn_sched_barrier(0);
-    if (Cfg::PHASE != 0 && late) {
-      lstore((step + 1) & 1, nxt1);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(step & 1);
-    } else {
-      compute(step & 1);
-      __builtin_amdgcn_sched_barrier(0);
-      lstore((step + 1) & 1, nxt1);
-    }
+    compute(step & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    lstore((step + 1) & 1, nxt1);
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
   };
