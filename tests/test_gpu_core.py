@@ -186,7 +186,7 @@ def test_prefill_tiles_w8_integer_exact(tile, monkeypatch):
 
 @pytest.mark.parametrize("m,n,k", [(1, 256, 128), (300, 512, 640), (513, 768, 2048), (256, 256, 384)])
 @pytest.mark.parametrize("dtype", [BF16, FP16])
-@pytest.mark.parametrize("tile", ["D8", "D8N", "X"])
+@pytest.mark.parametrize("tile", ["D8", "D8N", "D64", "D128", "X"])
 @pytest.mark.parametrize("group", [64, 128])
 def test_prefill_dma_tile_integer_exact(tile, group, m, n, k, dtype, monkeypatch):
     p = si.w4_exact_problem(m, n, k, group, seed=m + k, dtype=dtype, bias_dtype=FP16)
@@ -196,7 +196,7 @@ def test_prefill_dma_tile_integer_exact(tile, group, m, n, k, dtype, monkeypatch
     assert np.array_equal(got, _exact_expected(Cref, dtype))
 
 
-@pytest.mark.parametrize("tile", ["D8", "D8N", "X"])
+@pytest.mark.parametrize("tile", ["D8", "D8N", "D64", "D128", "X"])
 def test_prefill_dma_tile_w8_integer_exact(tile, monkeypatch):
     p = si.w8_exact_problem(300, 512, 576, seed=4, dtype=FP16, bias_dtype=FP16)
     Cref = oracle.gemm_w8(p.A, p.codes, p.scale, -1, FP16, p.bias, FP16)

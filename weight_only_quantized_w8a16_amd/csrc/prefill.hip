@@ -71,6 +71,8 @@ namespace {
 using CfgX = TileCfg<256, 256, 2, 4>;   // 8 waves, 128x64 per wave
 using CfgD8 = DmaCfg<2, 4>;             // 8 waves, 128x64 per wave, A direct to LDS
 using CfgD8N = DmaCfg<4, 2, 128>;       // 256 x 128 tile, 8 waves of 64x64
+using CfgD64 = DmaCfg<2, 4, 256, 64>;   // 64 x 256 tile, 8 waves of 32x64
+using CfgD128 = DmaCfg<2, 4, 256, 128>; // 128 x 256 tile, 8 waves of 64x64
 using CfgL = TileCfg<256, 128, 4, 2>;   // 8 waves, 64x64 per wave
 using CfgM = TileCfg<128, 128, 2, 2>;   // 4 waves, 64x64 per wave
 using CfgS = TileCfg<64, 64, 2, 2>;     // 4 waves, 32x32 per wave
@@ -131,12 +133,13 @@ hipError_t run_dma(const GemmArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Tile choice, from on-device sweeps at K = 2048 and 3584: the 256 x 256
-// direct-load tile once there are enough tiles to keep most CUs busy;
-// smaller tiles when the problem would leave CUs idle.
-// QGEMM_PREFILL_TILE=X|D8|D8N|L|M|S forces one (tests and tuning); D8 and
-// D8N are the 256 x 256 and 256 x 128 tiles with direct-to-LDS activation
-// loads.
+// Tile choice, from on-device sweeps at K = 2048 and 3584 (M from 32 to
+// 4096): the direct-load tiles once there are enough of them to keep most
+// CUs busy, the generic tiles (down to 64 x 64) when the problem would leave
+// CUs idle.
+// QGEMM_PREFILL_TILE=X|D8|D8N|D64|D128|L|M|S forces one (tests and tuning);
+// D8, D8N, D64 and D128 are the 256 x 256, 256 x 128, 64 x 256 and
+// 128 x 256 tiles with direct-to-LDS activation loads.
 template <int ACT, int WBITS>
 hipError_t dispatch(const GemmArgs &a, hipStream_t s) {
   auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * (a.N / bn); };
@@ -146,12 +149,21 @@ hipError_t dispatch(const GemmArgs &a, hipStream_t s) {
     if (c == "X" && n256) return run<CfgX, ACT, WBITS>(a, s);
     if (c == "D8" && n256) return run_dma<CfgD8, ACT, WBITS>(a, s);
     if (c == "D8N" && n128) return run_dma<CfgD8N, ACT, WBITS>(a, s);
+    if (c == "D64" && n256) return run_dma<CfgD64, ACT, WBITS>(a, s);
+    if (c == "D128" && n256) return run_dma<CfgD128, ACT, WBITS>(a, s);
     if (c == "L" && n128) return run<CfgL, ACT, WBITS>(a, s);
     if (c == "M" && n128) return run<CfgM, ACT, WBITS>(a, s);
     if (c == "S") return run<CfgS, ACT, WBITS>(a, s);
   }
   if (n256 && a.M > 128 && tiles(256, 256) >= 160) return run_dma<CfgD8, ACT, WBITS>(a, s);
+  // Up to 192 rows the 64-row tile wastes fewer rows than a 256-row one.
+  if (n256 && a.M > 128 && a.M <= 192 && tiles(64, 256) >= 128) return run_dma<CfgD64, ACT, WBITS>(a, s);
   if (n128 && a.M > 128 && tiles(256, 128) >= 128) return run_dma<CfgD8N, ACT, WBITS>(a, s);
+  // Fewer rows: shorter direct-load tiles over the full 256-wide weight tile,
+  // once there are enough of them.
+  if (n256 && a.M <= 64 && tiles(64, 256) >= 256) return run_dma<CfgD64, ACT, WBITS>(a, s);
+  if (n256 && a.M > 64 && a.M <= 128 && tiles(128, 256) >= 256) return run_dma<CfgD128, ACT, WBITS>(a, s);
+  if (n256 && a.M > 128 && a.M <= 256 && tiles(64, 256) >= 128) return run_dma<CfgD64, ACT, WBITS>(a, s);
   if (n128 && a.M > 128 && tiles(256, 128) >= 200) return run<CfgL, ACT, WBITS>(a, s);
   if (n128 && a.M > 64 && tiles(128, 128) >= 256) return run<CfgM, ACT, WBITS>(a, s);
   return run<CfgS, ACT, WBITS>(a, s);

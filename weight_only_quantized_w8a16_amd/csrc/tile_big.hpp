@@ -37,10 +37,10 @@
 
 namespace qg {
 
-template <int WM_, int WN_, int BN_ = 256>
+template <int WM_, int WN_, int BN_ = 256, int BM_ = 256>
 struct DmaCfg {
   static constexpr int WM = WM_, WN = WN_;
-  static constexpr int BM = 256, BN = BN_, BK = 64;
+  static constexpr int BM = BM_, BN = BN_, BK = 64;
   static constexpr int NTHR = 64 * WM * WN;
   static constexpr int WTM = BM / WM, WTN = BN / WN;   // wave tile
   static constexpr int TM = WTM / 32, TN = WTN / 32;   // 32x32 accumulators per wave
@@ -53,6 +53,7 @@ struct DmaCfg {
   static constexpr int SC_PARTS = BN / 64;             // 2 KiB parts per window
   static constexpr int SC_DMA = 512 / NTHR;            // 4-byte window loads per thread per step
   static_assert(BN == 128 || BN == 256, "tile width");
+  static_assert(BM % 64 == 0 && WTM % 32 == 0, "tile height");
   static_assert(A_DMA >= 1 && NB4 >= 1 && SC_DMA >= 1, "thread count");
 };
 
@@ -383,10 +384,14 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
   // + 32 i + lane % 32, col = wave tile column + 32 j + 8 (v / 4) +
   // 4 (lane / 32) + v % 4.  Per i, each wave stages its 32 x 64 block in LDS
   // (8-byte pieces, 144-byte rows) and stores it as 16-byte row pieces, so
-  // every store instruction writes whole 128-byte lines.  The A stages are
-  // free: the last step ended with a barrier after every wave's last read.
+  // every store instruction writes whole 128-byte lines.  Four waves share
+  // one stage (A or W, whichever is large enough); all stages are free: the
+  // last step ended with a barrier after every wave's last read.
   static_assert(Cfg::WTN == 64 && Cfg::NTHR == 512, "epilogue staging assumes 8 waves, 64 columns each");
-  char *stg = ((wave >> 2) ? L.a[1] : L.a[0]) + (wave & 3) * (32 * 144);
+  constexpr bool kStageInA = Cfg::STAGE_A >= 4 * 32 * 144;
+  static_assert(kStageInA || Cfg::STAGE_B >= 4 * 32 * 144, "no LDS stage holds four 32 x 64 blocks");
+  char *stg = (kStageInA ? ((wave >> 2) ? L.a[1] : L.a[0]) : ((wave >> 2) ? L.b[1] : L.b[0])) +
+              (wave & 3) * (32 * 144);
   const int row_in = lane & 31;
   if constexpr (MODE == kMoeFc1) {
     // acc[i][0] is gate, acc[i][1] up, of output columns
