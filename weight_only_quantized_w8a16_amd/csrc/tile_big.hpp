@@ -1,29 +1,30 @@
-// tile_big.hpp -- the 256 x BN (BN = 256 or 128) prefill GEMM tile for gfx950
-// with the activations loaded straight into LDS: C = A . W^T for one output
-// tile per workgroup, WM x WN waves, each wave a (256 / WM) x (BN / WN)
-// block of 32 x 32 accumulators.
+// tile_big.hpp -- the direct-load prefill GEMM tile for gfx950: C = A . W^T
+// for one BM x BN output tile per workgroup (BM 64, 128 or 256; BN 128 or
+// 256), WM x WN waves, each wave a (BM / WM) x (BN / WN) block of 32 x 32
+// accumulators.
 //
 // Per 64-k step:
-//  - A goes from global memory into LDS with global_load_lds_dwordx4, one
-//    step ahead of use, into one of two LDS stages (no trip through VGPRs,
-//    so no registers, address arithmetic or LDS store instructions for it);
-//  - the packed weight codes (and their scales and zeros) are loaded into
-//    registers two steps ahead, dequantized by every thread and written into
-//    one of two LDS stages while the matrix cores work on the current stage;
+//  - A goes from global memory into LDS with buffer_load_dwordx4 ... lds,
+//    one step ahead of use, into one of two LDS stages (no trip through
+//    VGPRs, so no registers, address arithmetic or LDS store instructions
+//    for it);
+//  - the packed weight codes are loaded into registers two steps ahead,
+//    dequantized by every thread and written into one of two LDS stages
+//    while the matrix cores work on the current stage;
 //  - the int4 scales and zeros come through LDS as well: a window holds 8
-//    groups of all 256 channels (16 bytes of each row of the scale and zero
-//    matrices, read with 4-byte direct loads, 1/4 of a window per step), so
-//    each row's scales cost one cache-line visit per 8 groups instead of a
-//    16-line gather per group;
+//    groups of the tile's BN channels (16 bytes of each row of the scale and
+//    zero matrices, read with 4-byte direct loads, one 2 KiB part per step),
+//    so each row's scales cost one cache-line visit per 8 groups instead of
+//    a 16-line gather per group;
 //  - every wave then waits for its own direct loads and meets the others at
 //    one barrier.
 //
-// LDS placement: a stage holds 256 rows of 64 k (128 bytes), the 16-byte
-// chunk c of row r at chunk c ^ ((r / 2) % 8).  A 16-lane group reading one
-// chunk of 16 consecutive rows then touches 16 distinct 16-byte bank groups
-// of the 256-byte bank space.  A direct load writes 64 consecutive 16-byte
-// slots, so the swizzle is applied on the source side: slot (r, c') is
-// loaded from the row's chunk c' ^ ((r / 2) % 8).
+// LDS placement: a stage holds BM (A) or BN (W) rows of 64 k (128 bytes),
+// the 16-byte chunk c of row r at chunk c ^ ((r / 2) % 8).  A 16-lane group
+// reading one chunk of 16 consecutive rows then touches 16 distinct 16-byte
+// bank groups of the 256-byte bank space.  A direct load writes 64
+// consecutive 16-byte slots, so the swizzle is applied on the source side:
+// slot (r, c') is loaded from the row's chunk c' ^ ((r / 2) % 8).
 //
 // Rows of A past the problem's end are read from the last valid row (a
 // direct-to-LDS load cannot be masked); their output rows are never stored.
@@ -103,7 +104,7 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
     s_bytes = static_cast<uint32_t>(p.s_expert_stride * 2);
   }
   const int n0 = (MODE == kMoeFc1) ? tile_n * (Cfg::BN / 2) : tile_n * Cfg::BN;
-  // Weight row of LDS row `lrow` (0..255).
+  // Weight row of LDS row `lrow` (0 .. BN - 1).
   auto wrow_of = [&](int lrow) {
     if constexpr (MODE == kMoeFc1)
       return (((lrow >> 5) & 1) ? p.N : 0) + n0 + 32 * (lrow >> 6) + (lrow & 31);
@@ -195,10 +196,10 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
   // direct load, each thread reads the scales of step s + 1 (dequantized in
   // step s) from LDS; then part (s + 1) % (BN / 64) of window
   // (s + 1) / (8 spg) + 1 is issued (every part at least twice per window,
-  // the repeats rewriting equal bytes).  A window
-  // is complete one step before its first use, and its buffer was last read
-  // one step before its first part lands.  Windows past the last group read
-  // other rows or (past the end of the matrices) zeros; they are never used.
+  // the repeats rewriting equal bytes).  A window is complete one step
+  // before its first use, and its buffer was last read one step before its
+  // first part lands.  Windows past the last group read other rows or (past
+  // the end of the matrices) zeros; they are never used.
   [[maybe_unused]] const int kg = K / p.group;
   [[maybe_unused]] const int spg_lg = (p.group == 128) ? 1 : 0;
   uint32_t sc_voff[Cfg::SC_DMA];
