@@ -162,3 +162,25 @@ def test_unaligned_scale_rows_fall_back():
     r, c = sample_pairs(1, 65536, seed=3)
     ref = oracle.gemm_w4_at(p.A, p.packed, p.scale, p.zero, 64, r, c)
     assert rel_err(C[r, c], ref) <= TOL[BF16]
+
+
+# -- Tile-choice boundaries: M just below / above each rule of the prefill
+#    dispatch, at a width where the direct-load tiles are eligible.  Sampled
+#    outputs against the oracle (K small to keep the oracle quick).
+@pytest.mark.parametrize("m", [17, 64, 65, 128, 129, 192, 193, 256, 257])
+@pytest.mark.parametrize("bits", [4, 8])
+def test_prefill_dispatch_boundaries(m, bits):
+    n, k = 65536, 256
+    r, c = sample_pairs(m, n, seed=m + bits, grid_rows=4, grid_cols=64, rand=256)
+    if bits == 4:
+        p = si.w4_problem(m, n, k, 64, tag="dispatch", bias_dtype=FP16)
+        got = gpu_w4(p)[r, c]
+        ref = oracle.gemm_w4_at(p.A, p.packed, p.scale, p.zero, 64, r, c, BF16, p.bias, FP16)
+        tol = TOL[BF16]
+    else:
+        p = si.w8_problem(m, n, k, tag="dispatch", bias_dtype=FP16)
+        got = gpu_w8(p)[r, c]
+        ref = oracle.gemm_w8_at(p.A, p.codes, p.scale, r, c, -1, FP16, p.bias, FP16)
+        tol = TOL[FP16]
+    err = np.abs(got - ref).max() / np.abs(ref).max()
+    assert err <= tol, (m, bits, err)
