@@ -163,7 +163,7 @@ hipError_t dispatch(const GemmArgs &a, hipStream_t s) {
   // once there are enough of them.
   if (n256 && a.M <= 64 && tiles(64, 256) >= 256) return run_dma<CfgD64, ACT, WBITS>(a, s);
   if (n256 && a.M > 64 && a.M <= 128 && tiles(128, 256) >= 256) return run_dma<CfgD128, ACT, WBITS>(a, s);
-  if (n256 && a.M > 128 && a.M <= 256 && tiles(64, 256) >= 128) return run_dma<CfgD64, ACT, WBITS>(a, s);
+  if (n256 && a.M > 128 && tiles(64, 256) >= 128) return run_dma<CfgD64, ACT, WBITS>(a, s);
   if (n128 && a.M > 128 && tiles(256, 128) >= 200) return run<CfgL, ACT, WBITS>(a, s);
   if (n128 && a.M > 64 && tiles(128, 128) >= 256) return run<CfgM, ACT, WBITS>(a, s);
   return run<CfgS, ACT, WBITS>(a, s);
