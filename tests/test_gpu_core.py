@@ -25,7 +25,7 @@ def _no_forced_path(monkeypatch):
 
 # -- repack -------------------------------------------------------------------
 
-@pytest.mark.parametrize("n,k", [(16, 128), (48, 384), (128, 256), (2048, 2048)])
+@pytest.mark.parametrize("n,k", [(16, 128), (48, 384), (128, 256), (32, 640), (64, 896), (2048, 2048)])
 def test_repack_w4_matches_documented_layout_and_inverts(n, k):
     packed = np.random.default_rng(n + k).integers(0, 256, (n, k // 2), dtype=np.uint8)
     d = to_dev(packed)
@@ -47,8 +47,9 @@ def test_repack_w8_matches_documented_layout_and_inverts(n, k):
 
 @pytest.mark.parametrize("dtype", [BF16, FP16])
 @pytest.mark.parametrize("group", [64, 128])
-def test_dequant_w4_bit_exact(dtype, group):
-    n, k = 96, 512
+@pytest.mark.parametrize("k", [512, 640])
+def test_dequant_w4_bit_exact(dtype, group, k):
+    n = 96
     packed, s, z, _ = si.w4_weights(n, k, group, seed=11 + group, dtype=dtype)
     ref = oracle.dequant4(packed, s, z, group, dtype)
     tiled = qg.repack_w4(to_dev(packed))
@@ -115,7 +116,7 @@ def _exact_expected(Cref, dtype):
 
 @pytest.mark.parametrize("m,n,k,group", [
     (1, 16, 128, 64), (4, 128, 256, 64), (16, 48, 384, 128), (5, 2048, 2048, 64),
-    (33, 128, 256, 64), (100, 192, 512, 128), (256, 256, 1024, 64),
+    (33, 128, 256, 64), (100, 192, 512, 128), (256, 256, 1024, 64), (7, 256, 640, 64),
 ])
 @pytest.mark.parametrize("path", ["decode", "prefill"])
 @pytest.mark.parametrize("dtype", [BF16, FP16])
