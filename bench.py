@@ -202,15 +202,19 @@ def run(args):
     stream = torch.cuda.current_stream()
     K = args.steps
 
-    def timed(fn, reps, calls_per_rep=1):
+    def timed(fn, reps, calls_per_rep=1, warm=0):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         # the lead outlasts the host's enqueue time (generously 0.2 ms a call);
-        # the start event is taken when the wait ends, so it adds no time.
-        gpu_lead(torch, 2.0 + 0.2 * reps * calls_per_rep)
+        # `warm` untimed calls run right before the start event, so a
+        # compute-bound kernel is timed at its steady clock, not while the
+        # clocks ramp up after the wait.
+        gpu_lead(torch, 2.0 + 0.2 * (reps + warm) * calls_per_rep)
+        for i in range(warm):
+            fn(i)
         a.record(stream)
         for i in range(reps):
-            fn(i)
+            fn(warm + i)
         b.record(stream)
         torch.cuda.synchronize()
         return a.elapsed_time(b)
@@ -282,7 +286,7 @@ def run(args):
             def call(i, w=w, C=C, g=g):
                 B, S, Z = w[i]
                 qg.gemm_w4a16(A, B, S, Z, w.bias, g, out=C)
-            ms = timed(call, reps) / reps
+            ms = timed(call, reps, warm=reps) / reps
             flop = 2.0 * m * n * 2048
             tot_flop += flop
             tot_ms += ms
@@ -324,7 +328,7 @@ def run(args):
             qg.moe_grouped(x, lg, w1, s1, z1, w2, s2, z2, TK, G, workspace=ws)
         reps = max(5, K // 5)
         ms = timed(lambda i: qg.moe_grouped(x, lg, w1, s1, z1, w2, s2, z2, TK, G, workspace=ws),
-                   reps, 4) / reps
+                   reps, 4, warm=reps) / reps
         flop = 2.0 * T * TK * (2 * I * H + H * I)
         wbytes = E * (w4_bytes(0, 2 * I, H, G) + w4_bytes(0, H, I, G))
         moe = {"config": "T=2048 H=2048 I=1408 E=64 top-6 g=64", "us": round(ms * 1e3, 1),

