@@ -68,6 +68,22 @@ def test_moe_expert_tiles_exactly_full(moe_tile):
     check(p)
 
 
+def test_moe_expert_row_counts_cover_every_partial_tile(moe_tile):
+    # Top-1 routes with chosen expert sizes: every number of filled 32-row
+    # blocks in each half of a 256-row expert tile, exact multiples of 32 and
+    # their neighbours, experts longer than one tile, and an empty expert.
+    counts = [1, 31, 32, 33, 64, 96, 127, 128, 129, 160, 191, 192, 193, 224, 255, 256, 257,
+              300, 0]
+    E, T = len(counts), sum(counts)
+    p = si.moe_problem(T, 256, 128, E, 1, 64, tag="moe-counts")
+    owner = np.repeat(np.arange(E), counts)
+    np.random.default_rng(7).shuffle(owner)
+    p.logits[:] = 0.0
+    p.logits[np.arange(T), owner] = 4.0
+    assert np.array_equal(np.bincount(owner, minlength=E), counts)
+    check(p)
+
+
 def test_moe_fp16(moe_tile):
     p = si.moe_problem(48, 256, 256, 8, 2, 64, tag="moe-f16", dtype=FP16)
     check(p, tol=TOL[FP16] * 3)

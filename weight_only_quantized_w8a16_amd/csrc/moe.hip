@@ -104,16 +104,33 @@ __global__ __launch_bounds__(256) void k_moe_route(const float *__restrict__ log
 // scans over experts (rows and tiles) run in one wave, the tile list is
 // written by one thread per expert, and rows take their slot within the
 // expert through LDS atomics (the order of rows inside an expert does not
-// change any output: every row is computed independently).
+// change any output: every row is computed independently).  Each thread
+// loads its ids kPlanBatch at a time before using them, so the passes over
+// the ids wait for memory once per batch rather than once per row.
+constexpr int kPlanBatch = 16;
 __global__ __launch_bounds__(1024) void k_moe_plan(const int32_t *__restrict__ ids, int R, int E,
                                                    int topk, int bm, MoeTile *__restrict__ tiles,
                                                    int32_t *__restrict__ ntiles,
                                                    int32_t *__restrict__ row_src,
                                                    int32_t *__restrict__ dest) {
   __shared__ int cnt[256], off[256], toff[256], fill[256];
-  for (int e = threadIdx.x; e < 256; e += blockDim.x) { cnt[e] = 0; fill[e] = 0; }
+  const int nthr = blockDim.x;
+  for (int e = threadIdx.x; e < 256; e += nthr) { cnt[e] = 0; fill[e] = 0; }
   __syncthreads();
-  for (int r = threadIdx.x; r < R; r += blockDim.x) atomicAdd(&cnt[ids[r]], 1);
+  auto load_batch = [&](int base, int (&e)[kPlanBatch]) {
+#pragma unroll
+    for (int u = 0; u < kPlanBatch; ++u) {
+      const int r = base + u * nthr + static_cast<int>(threadIdx.x);
+      e[u] = r < R ? ids[r] : -1;
+    }
+  };
+  for (int base = 0; base < R; base += kPlanBatch * nthr) {
+    int e[kPlanBatch];
+    load_batch(base, e);
+#pragma unroll
+    for (int u = 0; u < kPlanBatch; ++u)
+      if (e[u] >= 0) atomicAdd(&cnt[e[u]], 1);
+  }
   __syncthreads();
   if (threadIdx.x < 64) {
     // lane l scans experts 4l .. 4l + 3, then the lanes' totals
@@ -156,11 +173,17 @@ __global__ __launch_bounds__(1024) void k_moe_plan(const int32_t *__restrict__ i
       tiles[k++] = tl;
     }
   }
-  for (int r = threadIdx.x; r < R; r += blockDim.x) {
-    const int e = ids[r];
-    const int pos = off[e] + atomicAdd(&fill[e], 1);
-    row_src[pos] = r / topk;
-    dest[r] = pos;
+  for (int base = 0; base < R; base += kPlanBatch * nthr) {
+    int e[kPlanBatch];
+    load_batch(base, e);
+#pragma unroll
+    for (int u = 0; u < kPlanBatch; ++u) {
+      if (e[u] < 0) continue;
+      const int r = base + u * nthr + static_cast<int>(threadIdx.x);
+      const int pos = off[e[u]] + atomicAdd(&fill[e[u]], 1);
+      row_src[pos] = r / topk;
+      dest[r] = pos;
+    }
   }
 }
 

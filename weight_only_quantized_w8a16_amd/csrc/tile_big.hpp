@@ -266,9 +266,10 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
   struct Frags {
     u32x4 a[TM], b[TN];
   };
-  auto fread = [&](const char *As, const char *Bs, int ks, Frags &f) {
+  auto fread = [&](auto NAc, const char *As, const char *Bs, int ks, Frags &f) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) f.a[i] = *reinterpret_cast<const u32x4 *>(As + a_addr[ks] + 4096 * i);
+    for (int i = 0; i < decltype(NAc)::value; ++i)
+      f.a[i] = *reinterpret_cast<const u32x4 *>(As + a_addr[ks] + 4096 * i);
 #pragma unroll
     for (int j = 0; j < TN; ++j) f.b[j] = *reinterpret_cast<const u32x4 *>(Bs + b_addr[ks] + 4096 * j);
   };
@@ -285,9 +286,9 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
   // operand, so acc[i][j] holds C^T: a lane keeps one row of C (activation
   // row 32 i + lane % 32) and 16 of its columns, four consecutive ones per
   // group of four values -- which the epilogue stores as 8-byte pieces.
-  auto mma = [&](const Frags &f) {
+  auto mma = [&](auto NAc, const Frags &f) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < decltype(NAc)::value; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = mfma32x32x16<ACT>(f.b[j], f.a[i], acc[i][j]);
   };
@@ -334,8 +335,9 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
   // step s - 1, before the barrier that ended it.  Near the end the issued
   // step is clamped to the last one (the loads are then unused, or rewrite
   // equal bytes into the idle stage).
-  auto body = [&](auto Ic, int step, Regs &nxt1, Regs &nxt2) {
+  auto body = [&](auto NAc, auto Ic, int step, Regs &nxt1, Regs &nxt2) {
     constexpr int I = decltype(Ic)::value;
+    constexpr int NA = decltype(NAc)::value;
     char *As = L.a[I];
     char *Bs = L.b[I];
     ScaleRegs v;
@@ -346,27 +348,31 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
     asm volatile("" ::: "memory");
     b_issue(min(step + 2, nsteps - 1), nxt2);
     __builtin_amdgcn_sched_barrier(0);
-    Frags f0, f1;
-    fread(As, Bs, 0, f0);
-    fread(As, Bs, 1, f1);
-    mma(f0);
-    b_store(L.b[1 - I], nxt1, v);
-    fread(As, Bs, 2, f0);
-    mma(f1);
-    fread(As, Bs, 3, f1);
-    mma(f0);
-    mma(f1);
-    // Keep the fragment reads one sub-step ahead of the matrix cores (the
-    // scheduler would otherwise sink each sub-step's reads down to their
-    // first use and expose the LDS latency four times per step).
-    constexpr int NR = TM + TN, NM = TM * TN;
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * NR, 0);   // reads, sub-steps 0, 1
-    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);       // MFMA, sub-step 0
-    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);       // reads, sub-step 2
-    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);       // MFMA, sub-step 1
-    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);       // reads, sub-step 3
-    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);       // MFMA, sub-step 2
-    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);       // MFMA, sub-step 3
+    if constexpr (NA > 0) {
+      Frags f0, f1;
+      fread(NAc, As, Bs, 0, f0);
+      fread(NAc, As, Bs, 1, f1);
+      mma(NAc, f0);
+      b_store(L.b[1 - I], nxt1, v);
+      fread(NAc, As, Bs, 2, f0);
+      mma(NAc, f1);
+      fread(NAc, As, Bs, 3, f1);
+      mma(NAc, f0);
+      mma(NAc, f1);
+      // Keep the fragment reads one sub-step ahead of the matrix cores (the
+      // scheduler would otherwise sink each sub-step's reads down to their
+      // first use and expose the LDS latency four times per step).
+      constexpr int NR = NA + TN, NM = NA * TN;
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * NR, 0);   // reads, sub-steps 0, 1
+      __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);       // MFMA, sub-step 0
+      __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);       // reads, sub-step 2
+      __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);       // MFMA, sub-step 1
+      __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);       // reads, sub-step 3
+      __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);       // MFMA, sub-step 2
+      __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);       // MFMA, sub-step 3
+    } else {
+      b_store(L.b[1 - I], nxt1, v);
+    }
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(WAIT);
     barrier();
@@ -374,12 +380,29 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
 
-  int step = 0;
-  for (; step + 2 <= nsteps; step += 2) {
-    body(I0{}, step, r1, r0);
-    body(I1{}, step + 1, r0, r1);
+  auto main_loop = [&](auto NAc) {
+    int step = 0;
+    for (; step + 2 <= nsteps; step += 2) {
+      body(NAc, I0{}, step, r1, r0);
+      body(NAc, I1{}, step + 1, r0, r1);
+    }
+    if (step < nsteps) body(NAc, I0{}, step, r1, r0);
+  };
+  if constexpr (MODE == kDense) {
+    main_loop(std::integral_constant<int, TM>{});
+  } else {
+    // An expert tile is mostly partly filled: a wave skips the fragment
+    // reads and matrix-core work of its 32-row blocks that hold no rows
+    // (it still loads and dequantizes its share and meets every barrier).
+    const int valid = row_last - row_lo + 1 - wm * Cfg::WTM;
+    const int na = __builtin_amdgcn_readfirstlane(valid <= 0 ? 0 : min(TM, (valid + 31) >> 5));
+    static_assert(TM == 4, "expert tiles: four 32-row blocks per wave");
+    if (na == 4) main_loop(std::integral_constant<int, 4>{});
+    else if (na == 3) main_loop(std::integral_constant<int, 3>{});
+    else if (na == 2) main_loop(std::integral_constant<int, 2>{});
+    else if (na == 1) main_loop(std::integral_constant<int, 1>{});
+    else main_loop(std::integral_constant<int, 0>{});
   }
-  if (step < nsteps) body(I0{}, step, r1, r0);
 
   // ---- epilogue: value v of acc[i][j] is C[row][col], row = wave tile row
   // + 32 i + lane % 32, col = wave tile column + 32 j + 8 (v / 4) +
@@ -401,6 +424,7 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
     // in 80-byte rows.
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
+      if (row_lo + wm * Cfg::WTM + 32 * i > row_last) break;   // block holds no rows
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         float v[4];
@@ -438,6 +462,7 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
       }
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
+    if (row_lo + wm * Cfg::WTM + 32 * i > row_last) break;   // block holds no rows
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
