@@ -22,7 +22,8 @@
  *   [cpuint4] vllm-omni cpu_int4.py: module docstring (checkpoint format
  *             weight_packed uint8 [N, K/2], byte j = w[2j] | w[2j+1] << 4,
  *             bf16 scale/zero [N, K/group], w = (q - 8) * scale + zero),
- *             pack_nibbles / unpack_nibbles, CPUInt4EmbeddingMethod.embedding
+ *             pack_nibbles / unpack_nibbles, quantize_groupwise (min/max
+ *             grid per group), CPUInt4EmbeddingMethod.embedding
  *             (dequantize in fp32, then cast), CPUInt4LinearMethod.apply
  *             (bias added after the GEMM).
  *
@@ -151,6 +152,49 @@ void qref_unpack4(const uint8_t *packed, int32_t *codes, int64_t n, int64_t k)
             uint8_t byte = packed[r * (k / 2) + c / 2];
             codes[r * k + c] = (c % 2 == 0) ? (byte & 0xF) : (byte >> 4);
         }
+}
+
+/* ---------------------------------------------------------------------- */
+/* Groupwise min/max 4-bit quantizer  [cpuint4] quantize_groupwise.  For    */
+/* each K-group of a row, with lo / hi its smallest / largest value:        */
+/*   scale = max(hi - lo, 1e-9) / 15,  zero = lo + 8 * scale,               */
+/*   q = round((w - lo) / scale), ties to even, clamped to [0, 15],         */
+/* so that (q - 8) * scale + zero gives lo at q = 0 and hi at q = 15 (the   */
+/* docstring's grid).  Every step in fp32, as the page's float tensors;     */
+/* codes packed as pack_nibbles.  rintf rounds to nearest even under the    */
+/* default floating-point environment, like torch's round.                  */
+/* ---------------------------------------------------------------------- */
+void qref_quantize4(const float *w, int64_t n, int64_t k, int64_t group, uint8_t *packed,
+                    float *scale, float *zero)
+{
+    int64_t ngroups = k / group;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r) {
+        for (int64_t g = 0; g < ngroups; ++g) {
+            const float *x = w + r * k + g * group;
+            float lo = x[0], hi = x[0];
+            for (int64_t i = 1; i < group; ++i) {
+                if (x[i] < lo) lo = x[i];
+                if (x[i] > hi) hi = x[i];
+            }
+            float range = hi - lo;
+            if (range < 1e-9f) range = 1e-9f;
+            float s = range / 15.0f;
+            float z = lo + 8.0f * s;
+            scale[r * ngroups + g] = s;
+            zero[r * ngroups + g] = z;
+            for (int64_t i = 0; i < group; ++i) {
+                float q = rintf((x[i] - lo) / s);
+                if (q < 0.0f) q = 0.0f;
+                if (q > 15.0f) q = 15.0f;
+                int64_t col = g * group + i;
+                uint8_t *byte = &packed[r * (k / 2) + col / 2];
+                uint8_t code = (uint8_t)q;
+                if (col % 2 == 0) *byte = (uint8_t)((*byte & 0xF0u) | code);
+                else *byte = (uint8_t)((*byte & 0x0Fu) | (code << 4));
+            }
+        }
+    }
 }
 
 /* ---------------------------------------------------------------------- */

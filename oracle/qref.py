@@ -23,7 +23,7 @@ import numpy as np
 
 __all__ = [
     "NONE", "BF16", "FP16", "build", "lib", "bf16_to_f32", "f16_to_f32", "f32_to_bf16",
-    "f32_to_f16", "pack4", "unpack4", "dequant4", "dequant8", "gemm_w4", "gemm_w8",
+    "f32_to_f16", "pack4", "unpack4", "quantize4", "dequant4", "dequant8", "gemm_w4", "gemm_w8",
     "gemm_w4_at", "gemm_w8_at", "moe_route", "moe", "threads",
 ]
 
@@ -64,6 +64,7 @@ _SIGS = {
     "qref_f32_to_f16": (ctypes.c_uint16, [ctypes.c_float]),
     "qref_pack4": (None, [_P, _P, _I, _I]),
     "qref_unpack4": (None, [_P, _P, _I, _I]),
+    "qref_quantize4": (None, [_P, _I, _I, _I, _P, _P, _P]),
     "qref_dequant4": (None, [_P, _P, _P, _I, _I, _I, _INT, _P]),
     "qref_dequant8": (None, [_P, _P, _I, _I, _I, _INT, _P]),
     "qref_gemm_w4": (None, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _INT, _INT, _P]),
@@ -155,6 +156,23 @@ def unpack4(packed):
     out = np.empty((n, half * 2), dtype=np.int32)
     lib().qref_unpack4(_ptr(p), _ptr(out), n, half * 2)
     return out
+
+
+# -- quantization ---------------------------------------------------------------
+
+def quantize4(w, group):
+    """Groupwise min/max 4-bit quantization of fp32 [N, K].
+
+    Returns (packed uint8 [N, K/2], scale fp32 [N, K/g], zero fp32 [N, K/g]).
+    """
+    x = _c(w, np.float32)
+    n, k = x.shape
+    assert k % group == 0 and k % 2 == 0
+    packed = np.zeros((n, k // 2), dtype=np.uint8)
+    scale = np.empty((n, k // group), dtype=np.float32)
+    zero = np.empty((n, k // group), dtype=np.float32)
+    lib().qref_quantize4(_ptr(x), n, k, group, _ptr(packed), _ptr(scale), _ptr(zero))
+    return packed, scale, zero
 
 
 # -- dequantization -----------------------------------------------------------

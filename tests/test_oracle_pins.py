@@ -140,6 +140,75 @@ def test_quantizer_extremes_identity(j):
     assert W[0, 0] == wmin and W[0, 1] == wmax
 
 
+# -- groupwise quantizer ([cpuint4] quantize_groupwise) --------------------------
+
+@pytest.mark.parametrize("group", [64, 128])
+def test_quantize4_grid_values_recover_their_codes(group):
+    # Values on a dyadic grid lo + q * step, each group holding q = 0 and
+    # q = 15: scale = (hi - lo) / 15 = step and zero = lo + 8 * step exactly,
+    # and every value maps back to its own q (low nibble = even k).
+    rng = np.random.default_rng(group)
+    n, k = 6, 4 * group
+    q = rng.integers(0, 16, (n, k))
+    q[:, ::group] = 0
+    q[:, 1::group] = 15
+    step = 2.0 ** -rng.integers(2, 7, (n, k // group))
+    lo = rng.integers(-32, 33, (n, k // group)) / 8.0
+    w = (np.repeat(lo, group, axis=1) + q * np.repeat(step, group, axis=1)).astype(np.float32)
+    packed, scale, zero = oracle.quantize4(w, group)
+    assert np.array_equal(oracle.unpack4(packed), q)
+    assert np.array_equal(packed[:, 0] & 0xF, q[:, 0]) and np.array_equal(packed[:, 0] >> 4, q[:, 1])
+    assert np.array_equal(scale, step.astype(np.float32))
+    assert np.array_equal(zero, (lo + 8 * step).astype(np.float32))
+
+
+def test_quantize4_ties_round_half_to_even():
+    # lo = 0, hi = 15: step 1, so (w - lo) / scale = w exactly; halves go to
+    # the even neighbour (torch's round), not up.
+    w = np.zeros((1, 64), dtype=np.float32)
+    w[0, 1] = 15.0
+    halves = [0.5, 1.5, 2.5, 3.5, 6.5, 7.5, 8.5, 13.5, 14.5]
+    w[0, 2:2 + len(halves)] = halves
+    packed, scale, zero = oracle.quantize4(w, 64)
+    codes = oracle.unpack4(packed)[0]
+    assert scale[0, 0] == 1.0 and zero[0, 0] == 8.0
+    assert codes[2:2 + len(halves)].tolist() == [0, 2, 2, 4, 6, 8, 8, 14, 14]
+
+
+def test_quantize4_constant_group():
+    # hi = lo: the range is clamped to 1e-9 before the division by 15; every
+    # code is 0 and the dequantized value is lo up to the zero's rounding.
+    w = np.full((2, 128), -0.75, dtype=np.float32)
+    packed, scale, zero = oracle.quantize4(w, 64)
+    assert (oracle.unpack4(packed) == 0).all()
+    assert (scale == np.float32(np.float32(1e-9) / np.float32(15.0))).all()
+    assert (zero == np.float32(np.float32(-0.75) + np.float32(8.0) * scale)).all()
+
+
+@pytest.mark.parametrize("group", [64, 128])
+def test_quantize4_error_within_half_a_step(group):
+    # Nearest point of the grid lo + q * scale: the reconstruction
+    # (q - 8) * scale + zero is within scale / 2 of w (plus fp32 rounding of
+    # the quotient, the zero and the difference), and each group's extremes
+    # get codes 0 and 15.
+    rng = np.random.default_rng(9 + group)
+    n, k = 64, 1024
+    w = (rng.standard_normal((n, k)) * rng.uniform(0.01, 2.0, (n, 1))).astype(np.float32)
+    packed, scale, zero = oracle.quantize4(w, group)
+    q = oracle.unpack4(packed)
+    s = np.repeat(scale.astype(np.float64), group, axis=1)
+    z = np.repeat(zero.astype(np.float64), group, axis=1)
+    rec = (q - 8) * s + z
+    wd = w.astype(np.float64)
+    slack = 2.0 ** -21 * (np.abs(wd) + np.abs(z) + 16 * s)
+    assert (np.abs(rec - wd) <= 0.5 * s + slack).all()
+    g = w.reshape(n, k // group, group)
+    qg_ = q.reshape(n, k // group, group)
+    rows, grp = np.indices(g.shape[:2])
+    assert (qg_[rows, grp, g.argmin(axis=2)] == 0).all()
+    assert (qg_[rows, grp, g.argmax(axis=2)] == 15).all()
+
+
 def test_group_indexing_closed_form():
     # constant code c and A = 1: C[n] = sum_g group * ((c - 8) * s[n, g] + z[n, g])
     rng = np.random.default_rng(5)
