@@ -12,6 +12,8 @@ Secondary sections on the same JSON line:
            fp16 bias: TFLOP/s against the dense bf16 matrix-core peak;
   moe      grouped W4A16 MoE, 2048 tokens, hidden 2048, inter 1408,
            64 experts, top-6;
+  quantize the load-side groupwise int4 quantizer on bf16 weights
+           [N, 2048], N in {13312, 131072}, group 64 (GB/s against HBM);
   roofline the decode kernel of the N=131072 GEMV: algorithmic bytes per
            launch / its mean launch time (HIP events on the launch stream);
   cpu_baseline  the CPU oracle on a bounded sample of the decode step.
@@ -340,6 +342,39 @@ def run(args):
         del w1, w2, ws
         torch.cuda.empty_cache()
 
+    # ---- load-side quantizer ------------------------------------------------------
+    quant = None
+    if not args.no_quant:
+        qk, qgp = 2048, 64
+        qshapes, best = {}, None
+        for n in (13312, 131072):
+            gen = torch.Generator(device=dev)
+            gen.manual_seed(n)
+            nbytes = n * qk * 2
+            copies = max(1, min(16, math.ceil(ROTATE_BYTES / nbytes)))
+            Ws = [(torch.randn(n, qk, generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+                  for _ in range(copies)]
+            for i in range(2):
+                qg.quantize_w4(Ws[i % copies], qgp)
+            reps = max(10, K // 5)
+            ms = timed(lambda i: qg.quantize_w4(Ws[i % copies], qgp), reps, warm=reps) / reps
+            b = nbytes + n * qk // 2 + 2 * 2 * n * (qk // qgp)
+            gbps = b / (ms * 1e-3) / 1e9
+            qshapes[f"N{n}"] = {"us": round(ms * 1e3, 1), "GBps": round(gbps, 1),
+                                "frac": round(gbps / HBM_PEAK_GBS, 3), "bytes": b}
+            best = (n, gbps, b, ms)
+            del Ws
+        n, gbps, b, ms = best
+        quant = {"metric": "int4 groupwise min/max quantizer: bf16 W [N, 2048] -> portable "
+                           "codes + bf16 scale/zero, group 64",
+                 "shapes": qshapes,
+                 "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBS,
+                              "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBS, 4),
+                              "traffic": None, "kernel": f"k_quantize_w4 (N={n}, K=2048, g=64)",
+                              "bytes_per_launch": b, "mean_launch_us": round(ms * 1e3, 2)}}
+        log(f"quantize: {quant}")
+        torch.cuda.empty_cache()
+
     # ---- ceiling: a plain device-to-device copy (read + write) ----------------------
     ceil = None
     if not args.quick:
@@ -402,6 +437,7 @@ def run(args):
         "sweep": sweep,
         "prefill": prefill,
         "moe": moe,
+        "quantize": quant,
         "ceiling": ceil,
     }
     print(json.dumps(result), flush=True)
@@ -416,6 +452,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-moe", action="store_true")
+    ap.add_argument("--no-quant", action="store_true")
     ap.add_argument("--quick", action="store_true", help="skip the M sweep and the copy ceiling")
     ap.add_argument("--kernel-only", action="store_true",
                     help="run only the N=131072 GEMV (--steps times) and a calibration copy; "

@@ -104,6 +104,30 @@ qg_status qrepack_w8(const int8_t *src_nk, int8_t *dst_tiled, int n, int k, void
 qg_status qunrepack_w8(const int8_t *src_tiled, int8_t *dst_nk, int n, int k, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Groupwise min/max 4-bit quantizer (vllm-omni cpu_int4.py,
+ * quantize_groupwise): fp weights W [n, k] -> portable int4 codes and one
+ * scale and zero per (row, K-group), chosen so that (q - 8) * scale + zero
+ * gives the group's smallest value at q = 0 and its largest at q = 15.
+ * For a group with smallest value lo and largest hi, all in fp32:
+ *     scale = max(hi - lo, 1e-9) / 15
+ *     zero  = lo + 8 * scale
+ *     q     = round((w - lo) / scale), ties to even, clamped to [0, 15]
+ * The division is the correctly rounded one, so the codes are bit-exact.
+ *   W       device [n, k] in w_dtype (QG_BF16, QG_FP16 or QG_FP32)
+ *   packed  device uint8 [n, k/2], the portable int4 layout above (pass it
+ *           to qrepack_w4 before the GEMMs)
+ *   scales, zeros  device [n, k/group] in sz_dtype: QG_FP32 (the values
+ *           above) or QG_BF16 / QG_FP16 (those values rounded to nearest
+ *           even, the form the GEMMs take; the codes still come from the
+ *           fp32 scale)
+ *   group_size: 64 or 128, k % group_size == 0.  n == 0 or k == 0: no-op.
+ *   Alignment: W and packed 16 bytes; scales and zeros 4 bytes for fp32,
+ *   else 2.  W must not overlap the outputs.
+ * ---------------------------------------------------------------------- */
+qg_status qquantize_w4(const void *W, uint8_t *packed, void *scales, void *zeros, int n, int k,
+                       int group_size, qg_dtype w_dtype, qg_dtype sz_dtype, void *stream);
+
+/* ------------------------------------------------------------------------
  * Dequantization hook (testing and fallback use): tiled codes -> W [n, k]
  * row-major in out_dtype (QG_FP32, or the activation dtype).  The fp32
  * value is (q - 8) * s + z (int4; the product is exact, the add rounds to

@@ -154,3 +154,23 @@ def test_layout_helpers_are_permutations():
     c = np.random.default_rng(1).integers(-128, 128, (16, 128)).astype(np.int8)
     t8 = tiled_w8_expected(c)
     assert sorted((t8.view(np.uint8) ^ 0x80).ravel().tolist()) == sorted(c.view(np.uint8).ravel().tolist())
+
+
+def q4(**kw):
+    a = dict(W=FAKE, p=FAKE, s=FAKE, z=FAKE, n=32, k=256, g=64, wdt=BF16, sdt=BF16)
+    a.update(kw)
+    return qg.lib().qquantize_w4(a["W"], a["p"], a["s"], a["z"], a["n"], a["k"], a["g"], a["wdt"],
+                                 a["sdt"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=-1), SHAPE), (dict(k=-128), SHAPE),
+    (dict(W=None), NULL), (dict(p=None), NULL), (dict(s=None), NULL), (dict(z=None), NULL),
+    (dict(wdt=0), DTYPE), (dict(wdt=7), DTYPE), (dict(sdt=0), DTYPE), (dict(sdt=9), DTYPE),
+    (dict(g=32), GROUP), (dict(g=-1), GROUP), (dict(k=192, g=128), GROUP), (dict(k=100), GROUP),
+    (dict(W=FAKE + 8), ALIGN), (dict(p=FAKE + 4), ALIGN), (dict(s=FAKE + 1), ALIGN),
+    (dict(sdt=FP32, z=FAKE + 2), ALIGN),
+    (dict(n=0), OK), (dict(k=0), OK), (dict(n=0, W=None), OK),
+])
+def test_quantize_validation(kw, status):
+    assert q4(**kw) == status

@@ -17,7 +17,7 @@ from ._abi import QG_BF16, QG_FP16, QG_FP32, QG_NONE, QGemmError, check, lib
 
 __all__ = [
     "QGemmError", "lib", "repack_w4", "unrepack_w4", "repack_w8", "unrepack_w8", "dequant_w4",
-    "dequant_w8", "gemm_w4a16", "gemm_w8a16", "moe_grouped", "moe_workspace_size",
+    "dequant_w8", "quantize_w4", "gemm_w4a16", "gemm_w8a16", "moe_grouped", "moe_workspace_size",
     "gemm_workspace_size", "dtype_code",
 ]
 
@@ -90,6 +90,27 @@ def unrepack_w8(tiled: torch.Tensor) -> torch.Tensor:
     out = torch.empty_like(tiled)
     check("qunrepack_w8", lib().qunrepack_w8(_ptr(tiled), _ptr(out), n, k, _stream(tiled)))
     return out
+
+
+# -- quantizer -----------------------------------------------------------------
+
+def quantize_w4(W: torch.Tensor, group_size: int = 64, sz_dtype: Optional[torch.dtype] = None):
+    """Groupwise min/max int4 quantization of W [n, k] (bf16, fp16 or fp32).
+
+    Returns (packed uint8 [n, k/2] in the portable layout, scales, zeros
+    [n, k/group] in sz_dtype, default W's dtype).
+    """
+    _dev(W, "W")
+    n, k = W.shape
+    sz_dtype = W.dtype if sz_dtype is None else sz_dtype
+    packed = torch.empty((n, k // 2), dtype=torch.uint8, device=W.device)
+    ng = k // group_size if group_size > 0 else 0
+    scales = torch.empty((n, ng), dtype=sz_dtype, device=W.device)
+    zeros = torch.empty((n, ng), dtype=sz_dtype, device=W.device)
+    check("qquantize_w4", lib().qquantize_w4(_ptr(W), _ptr(packed), _ptr(scales), _ptr(zeros), n, k,
+                                             group_size, dtype_code(W.dtype), dtype_code(sz_dtype),
+                                             _stream(W)))
+    return packed, scales, zeros
 
 
 # -- dequant hook ------------------------------------------------------------

@@ -129,6 +129,27 @@ qg_status qunrepack_w8(const int8_t *src, int8_t *dst, int n, int k, void *strea
 // ---------------------------------------------------------------------------
 // Dequant hook
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// Quantizer
+// ---------------------------------------------------------------------------
+qg_status qquantize_w4(const void *W, uint8_t *packed, void *scales, void *zeros, int n, int k,
+                       int group, qg_dtype w_dt, qg_dtype sz_dt, void *stream) {
+  if (n < 0 || k < 0) return QG_ERR_SHAPE;
+  if (n == 0 || k == 0) return QG_OK;
+  if (!W || !packed || !scales || !zeros) return QG_ERR_NULL;
+  if (!(act_ok(w_dt) || w_dt == QG_FP32) || !(act_ok(sz_dt) || sz_dt == QG_FP32))
+    return QG_ERR_DTYPE;
+  if (group != 64 && group != 128) return QG_ERR_GROUP;
+  if (k % group != 0) return QG_ERR_GROUP;
+  const size_t sz_align = sz_dt == QG_FP32 ? 4 : 2;
+  if (!aligned(W, 16) || !aligned(packed, 16) || !aligned(scales, sz_align) ||
+      !aligned(zeros, sz_align))
+    return QG_ERR_ALIGN;
+  return hip_status(qg::launch_quantize_w4(W, packed, scales, zeros, n, k, group,
+                                           static_cast<int>(w_dt), static_cast<int>(sz_dt),
+                                           as_stream(stream)));
+}
+
 qg_status qdequant_w4(const uint8_t *B, const void *scales, const void *zeros, void *W, int n,
                       int k, int group, qg_dtype act, qg_dtype out, void *stream) {
   if (n < 0 || k < 0) return QG_ERR_SHAPE;

@@ -15,6 +15,9 @@ hipError_t launch_unrepack_w4(const uint8_t *src, uint8_t *dst, int n, int k, hi
 hipError_t launch_repack_w8(const int8_t *src, int8_t *dst, int n, int k, hipStream_t s);
 hipError_t launch_unrepack_w8(const int8_t *src, int8_t *dst, int n, int k, hipStream_t s);
 
+hipError_t launch_quantize_w4(const void *W, uint8_t *packed, void *scale, void *zero, int n,
+                              int k, int group, int w_dt, int sz_dt, hipStream_t s);
+
 hipError_t launch_dequant_w4(const uint8_t *B, const uint16_t *S, const uint16_t *Z, void *W,
                              int n, int k, int group, int act, int out, hipStream_t s);
 hipError_t launch_dequant_w8(const int8_t *B, const uint16_t *S, void *W, int n, int k, int act,

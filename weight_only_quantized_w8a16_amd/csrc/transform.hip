@@ -68,6 +68,134 @@ static inline unsigned grid_for(long long items, int block) {
   return static_cast<unsigned>((items + block - 1) / block);
 }
 
+// ---------------------------------------------------------------------------
+// Groupwise min/max quantizer (vllm-omni cpu_int4.py, quantize_groupwise):
+// per K-group, scale = max(hi - lo, 1e-9) / 15, zero = lo + 8 scale,
+// q = round-half-even((w - lo) / scale) clamped to [0, 15], in fp32 (the
+// codes are those of the correctly rounded division; see below).  A run is
+// 8 consecutive values of a row -- one 32-bit word of the portable layout;
+// GROUP / 8 consecutive lanes hold a group's runs and exchange their
+// partial minimum and maximum.  Groups never straddle rows
+// (k % GROUP == 0), so the flat run index r is also the word index and
+// r / (GROUP / 8) the group index.
+// ---------------------------------------------------------------------------
+template <int WT>
+__device__ __forceinline__ void load8(const void *W, long long r, float (&x)[8]) {
+  if constexpr (WT == QG_FP32) {
+    const float4 *p = static_cast<const float4 *>(W) + 2 * r;
+    const float4 a = p[0], b = p[1];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  } else {
+    const uint4 v = static_cast<const uint4 *>(W)[r];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = bits_to_f32<WT>(static_cast<uint16_t>(w[i] & 0xFFFFu));
+      x[2 * i + 1] = bits_to_f32<WT>(static_cast<uint16_t>(w[i] >> 16));
+    }
+  }
+}
+
+template <int SZ>
+__device__ __forceinline__ void store_sz(void *dst, long long i, float v) {
+  if constexpr (SZ == QG_FP32) static_cast<float *>(dst)[i] = v;
+  else static_cast<uint16_t *>(dst)[i] = f32_to_bits<SZ>(v);
+}
+
+template <int WT, int SZ, int GROUP>
+__global__ __launch_bounds__(256) void k_quantize_w4(const void *__restrict__ W,
+                                                     uint32_t *__restrict__ packed,
+                                                     void *__restrict__ scale,
+                                                     void *__restrict__ zero, long long runs) {
+  constexpr int LPG = GROUP / 8;   // threads per group
+  const long long r = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (r >= runs) return;           // whole groups only: runs is a multiple of LPG
+  float x[8];
+  load8<WT>(W, r, x);
+  // Group extremes.  The NaN-propagating minimum / maximum take the values
+  // as they are (no quieting pass), and agree with < / > on the finite
+  // inputs the quantizer is defined for.
+  float lo = x[0], hi = x[0];
+#pragma unroll
+  for (int e = 1; e < 8; ++e) {
+    lo = __builtin_elementwise_minimum(lo, x[e]);
+    hi = __builtin_elementwise_maximum(hi, x[e]);
+  }
+#pragma unroll
+  for (int off = 1; off < LPG; off <<= 1) {
+    lo = __builtin_elementwise_minimum(lo, __shfl_xor(lo, off));
+    hi = __builtin_elementwise_maximum(hi, __shfl_xor(hi, off));
+  }
+  float range = hi - lo;
+  if (range < 1e-9f) range = 1e-9f;
+  const float s = range / 15.0f;   // correctly rounded: it is an output
+  const float z = lo + 8.0f * s;
+  // Each code is rint of the correctly rounded quotient d = fl((w - lo) / s).
+  // Here 0 <= w - lo <= range (rounding is monotone) and s is range / 15
+  // rounded, so d lies in [0, 15 (1 + 2^-23)].  Adding 1.5 * 2^23 rounds a
+  // value of that range to an integer, ties to even, which then sits in the
+  // low byte of the sum's bits.  With rcp the hardware reciprocal of s
+  // (error below 1 ulp), the product (w - lo) * rcp is within 4e-6 of d and
+  // is rounded by one fused multiply-add; unless it lies within 1e-5 of a
+  // half-integer (its distance to the chosen integer, from a second fused
+  // multiply-add, is then below 0.5 - 1e-5), it rounds to the same integer
+  // as d.  Otherwise the run's quotients are recomputed by division (rare:
+  // about one run in 6000).
+  constexpr float kRound = 12582912.0f;   // 1.5 * 2^23
+  const float rcp = __builtin_amdgcn_rcpf(s);
+  float a[8], t[8];
+  float worst = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = x[e] - lo;
+    t[e] = __builtin_fmaf(a[e], rcp, kRound);
+    worst = fmaxf(worst, fabsf(__builtin_fmaf(a[e], rcp, kRound - t[e])));
+  }
+  if (worst > 0.5f - 1e-5f) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[e] = a[e] / s + kRound;
+  }
+  // Low bytes hold the codes: pair them into nibbles, then gather the bytes.
+  uint32_t p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    p[i] = (__float_as_uint(t[2 * i + 1]) << 4) | __float_as_uint(t[2 * i]);
+  const uint32_t lo16 = __builtin_amdgcn_perm(p[1], p[0], 0x0C0C0400u);
+  const uint32_t hi16 = __builtin_amdgcn_perm(p[3], p[2], 0x0C0C0400u);
+  packed[r] = __builtin_amdgcn_perm(hi16, lo16, 0x05040100u);
+  if ((r & (LPG - 1)) == 0) {
+    store_sz<SZ>(scale, r / LPG, s);
+    store_sz<SZ>(zero, r / LPG, z);
+  }
+}
+
+hipError_t launch_quantize_w4(const void *W, uint8_t *packed, void *scale, void *zero, int n,
+                              int k, int group, int w_dt, int sz_dt, hipStream_t s) {
+  const long long runs = static_cast<long long>(n) * k / 8;
+  dim3 g(grid_for(runs, 256)), b(256);
+  uint32_t *P = reinterpret_cast<uint32_t *>(packed);
+#define QG_Q4(WT_, SZ_)                                                                          \
+  do {                                                                                           \
+    if (group == 64)                                                                             \
+      hipLaunchKernelGGL((k_quantize_w4<WT_, SZ_, 64>), g, b, 0, s, W, P, scale, zero, runs);  \
+    else                                                                                         \
+      hipLaunchKernelGGL((k_quantize_w4<WT_, SZ_, 128>), g, b, 0, s, W, P, scale, zero, runs); \
+  } while (0)
+#define QG_Q4_SZ(WT_)                                   \
+  do {                                                  \
+    if (sz_dt == QG_FP32) QG_Q4(WT_, QG_FP32);          \
+    else if (sz_dt == QG_BF16) QG_Q4(WT_, QG_BF16);     \
+    else QG_Q4(WT_, QG_FP16);                           \
+  } while (0)
+  if (w_dt == QG_FP32) QG_Q4_SZ(QG_FP32);
+  else if (w_dt == QG_BF16) QG_Q4_SZ(QG_BF16);
+  else QG_Q4_SZ(QG_FP16);
+#undef QG_Q4_SZ
+#undef QG_Q4
+  return hipGetLastError();
+}
+
 hipError_t launch_repack_w4(const uint8_t *src, uint8_t *dst, int n, int k, hipStream_t s) {
   long long words = static_cast<long long>(n) * k / 8;
   hipLaunchKernelGGL(k_repack_w4, dim3(grid_for(words, 256)), dim3(256), 0, s,
