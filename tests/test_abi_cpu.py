@@ -98,6 +98,14 @@ def test_repack_and_dequant_validation():
     assert L.qunrepack_w4(FAKE, None, 16, 128, None) == NULL
     assert L.qrepack_w8(FAKE, FAKE, 16, 96, None) == UNSUP
     assert L.qunrepack_w8(FAKE, FAKE, 16, 0, None) == OK
+    for f in (L.qrepack_w8_kn, L.qunrepack_w8_kn):
+        assert f(FAKE, FAKE, -16, 64, None) == SHAPE
+        assert f(FAKE, None, 16, 64, None) == NULL
+        assert f(FAKE, FAKE, 40, 64, None) == UNSUP
+        assert f(FAKE, FAKE, 16, 96, None) == UNSUP
+        assert f(FAKE, FAKE + 8, 16, 64, None) == ALIGN
+        assert f(FAKE, FAKE, 0, 64, None) == OK
+        assert f(FAKE, FAKE, 16, 64 * 65536, None) == UNSUP
     assert L.qdequant_w4(FAKE, FAKE, FAKE, FAKE, 16, 128, 32, BF16, FP32, None) == GROUP
     assert L.qdequant_w4(FAKE, FAKE, FAKE, FAKE, 16, 128, 64, BF16, FP16, None) == DTYPE
     assert L.qdequant_w4(FAKE, FAKE, None, FAKE, 16, 128, 64, BF16, FP32, None) == NULL

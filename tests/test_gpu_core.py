@@ -43,6 +43,19 @@ def test_repack_w8_matches_documented_layout_and_inverts(n, k):
     assert np.array_equal(qg.unrepack_w8(tiled).cpu().numpy(), codes)
 
 
+@pytest.mark.parametrize("n,k", [(16, 64), (48, 192), (80, 320), (208, 128), (3584, 3584)])
+def test_repack_w8_kn_matches_transposed_repack_and_inverts(n, k):
+    # K-major int8 [k, n] in: the same tiled bytes as repacking the [n, k]
+    # transpose, from the layout formula; the inverse returns [k, n].
+    codes = np.random.default_rng(n + 3 * k).integers(-128, 128, (n, k)).astype(np.int8)
+    codes[0, :2] = [-128, 127]
+    kn = to_dev(np.ascontiguousarray(codes.T))
+    tiled = qg.repack_w8_kn(kn)
+    assert tuple(tiled.shape) == (n, k)
+    assert np.array_equal(tiled.cpu().numpy(), tiled_w8_expected(codes))
+    assert np.array_equal(qg.unrepack_w8_kn(tiled).cpu().numpy(), codes.T)
+
+
 # -- dequant hook (bit-exact) ---------------------------------------------------
 
 @pytest.mark.parametrize("dtype", [BF16, FP16])

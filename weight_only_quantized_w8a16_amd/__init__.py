@@ -16,9 +16,9 @@ import torch
 from ._abi import QG_BF16, QG_FP16, QG_FP32, QG_NONE, QGemmError, check, lib
 
 __all__ = [
-    "QGemmError", "lib", "repack_w4", "unrepack_w4", "repack_w8", "unrepack_w8", "dequant_w4",
-    "dequant_w8", "quantize_w4", "gemm_w4a16", "gemm_w8a16", "moe_grouped", "moe_workspace_size",
-    "gemm_workspace_size", "dtype_code",
+    "QGemmError", "lib", "repack_w4", "unrepack_w4", "repack_w8", "unrepack_w8", "repack_w8_kn",
+    "unrepack_w8_kn", "quantize_w4", "dequant_w4", "dequant_w8", "gemm_w4a16", "gemm_w8a16",
+    "moe_grouped", "moe_workspace_size", "gemm_workspace_size", "dtype_code",
 ]
 
 _CODES = {torch.bfloat16: QG_BF16, torch.float16: QG_FP16, torch.float32: QG_FP32}
@@ -89,6 +89,24 @@ def unrepack_w8(tiled: torch.Tensor) -> torch.Tensor:
     n, k = tiled.shape
     out = torch.empty_like(tiled)
     check("qunrepack_w8", lib().qunrepack_w8(_ptr(tiled), _ptr(out), n, k, _stream(tiled)))
+    return out
+
+
+def repack_w8_kn(codes_kn: torch.Tensor) -> torch.Tensor:
+    """int8 [k, n] (K-major) -> tiled layout [n, k] (as repack_w8 of the transpose)."""
+    _dev(codes_kn, "codes_kn")
+    k, n = codes_kn.shape
+    out = torch.empty((n, k), dtype=codes_kn.dtype, device=codes_kn.device)
+    check("qrepack_w8_kn", lib().qrepack_w8_kn(_ptr(codes_kn), _ptr(out), n, k, _stream(codes_kn)))
+    return out
+
+
+def unrepack_w8_kn(tiled: torch.Tensor) -> torch.Tensor:
+    """Tiled int8 [n, k] -> int8 [k, n] (K-major)."""
+    _dev(tiled, "tiled")
+    n, k = tiled.shape
+    out = torch.empty((k, n), dtype=tiled.dtype, device=tiled.device)
+    check("qunrepack_w8_kn", lib().qunrepack_w8_kn(_ptr(tiled), _ptr(out), n, k, _stream(tiled)))
     return out
 
 

@@ -33,6 +33,8 @@ SIGNATURES = {
     "qunrepack_w4": (_ST, [_P, _P, _INT, _INT, _P]),
     "qrepack_w8": (_ST, [_P, _P, _INT, _INT, _P]),
     "qunrepack_w8": (_ST, [_P, _P, _INT, _INT, _P]),
+    "qrepack_w8_kn": (_ST, [_P, _P, _INT, _INT, _P]),
+    "qunrepack_w8_kn": (_ST, [_P, _P, _INT, _INT, _P]),
     "qquantize_w4": (_ST, [_P, _P, _P, _P, _INT, _INT, _INT, _INT, _INT, _P]),
     "qdequant_w4": (_ST, [_P, _P, _P, _P, _INT, _INT, _INT, _INT, _INT, _P]),
     "qdequant_w8": (_ST, [_P, _P, _P, _INT, _INT, _INT, _INT, _INT, _P]),

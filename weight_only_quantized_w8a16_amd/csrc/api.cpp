@@ -125,6 +125,18 @@ qg_status qunrepack_w8(const int8_t *src, int8_t *dst, int n, int k, void *strea
   if (st != QG_OK || n == 0 || k == 0) return st;
   return hip_status(qg::launch_unrepack_w8(src, dst, n, k, as_stream(stream)));
 }
+qg_status qrepack_w8_kn(const int8_t *src, int8_t *dst, int n, int k, void *stream) {
+  qg_status st = repack_checks(src, dst, n, k, 64);
+  if (st != QG_OK || n == 0 || k == 0) return st;
+  if (static_cast<long long>(k / 64) > 65535) return QG_ERR_UNSUPPORTED;
+  return hip_status(qg::launch_repack_w8_kn(src, dst, n, k, as_stream(stream)));
+}
+qg_status qunrepack_w8_kn(const int8_t *src, int8_t *dst, int n, int k, void *stream) {
+  qg_status st = repack_checks(src, dst, n, k, 64);
+  if (st != QG_OK || n == 0 || k == 0) return st;
+  if (static_cast<long long>(k / 64) > 65535) return QG_ERR_UNSUPPORTED;
+  return hip_status(qg::launch_unrepack_w8_kn(src, dst, n, k, as_stream(stream)));
+}
 
 // ---------------------------------------------------------------------------
 // Dequant hook

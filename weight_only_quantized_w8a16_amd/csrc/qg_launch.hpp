@@ -14,6 +14,8 @@ hipError_t launch_repack_w4(const uint8_t *src, uint8_t *dst, int n, int k, hipS
 hipError_t launch_unrepack_w4(const uint8_t *src, uint8_t *dst, int n, int k, hipStream_t s);
 hipError_t launch_repack_w8(const int8_t *src, int8_t *dst, int n, int k, hipStream_t s);
 hipError_t launch_unrepack_w8(const int8_t *src, int8_t *dst, int n, int k, hipStream_t s);
+hipError_t launch_repack_w8_kn(const int8_t *src, int8_t *dst, int n, int k, hipStream_t s);
+hipError_t launch_unrepack_w8_kn(const int8_t *src, int8_t *dst, int n, int k, hipStream_t s);
 
 hipError_t launch_quantize_w4(const void *W, uint8_t *packed, void *scale, void *zero, int n,
                               int k, int group, int w_dt, int sz_dt, hipStream_t s);
