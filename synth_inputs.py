@@ -140,17 +140,19 @@ def w4_exact_problem(m, n, k, group, seed, dtype=BF16, bias_dtype=NONE) -> W4Pro
     return W4Problem(m, n, k, group, dtype, A, packed, scale, zero, bias, bias_dtype)
 
 
-def w8_exact_problem(m, n, k, seed, dtype=FP16, bias_dtype=NONE) -> W8Problem:
-    """A in {-1, 0, 1}, per-channel scales 2^-4 .. 2^-6: |C| < 2^7, exact."""
+def w8_exact_problem(m, n, k, seed, dtype=FP16, bias_dtype=NONE, group=-1) -> W8Problem:
+    """A in {-1, 0, 1}, scales 2^-4 .. 2^-6 (per channel, or per K-group for
+    group 64 / 128): |C| < 2^15, every partial sum a multiple of 2^-6, exact."""
     g = _gen(seed)
     codes = torch.randint(-128, 128, (n, k), generator=g, dtype=torch.int8).numpy()
-    sexp = torch.randint(4, 7, (n,), generator=g)
+    sshape = (n,) if group in (-1, k) else (n, k // group)
+    sexp = torch.randint(4, 7, sshape, generator=g)
     scale = _bits(torch.pow(2.0, -sexp.float()), dtype)
     bias = None
     if bias_dtype != NONE:
         bias = _bits(torch.randint(-8, 9, (n,), generator=g).float() / 4.0, bias_dtype)
     A = _bits(torch.randint(-1, 2, (m, k), generator=g).float(), dtype)
-    return W8Problem(m, n, k, -1, dtype, A, codes, scale, bias, bias_dtype)
+    return W8Problem(m, n, k, group, dtype, A, codes, scale, bias, bias_dtype)
 
 
 # -- MoE ---------------------------------------------------------------------------

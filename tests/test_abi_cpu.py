@@ -78,7 +78,8 @@ def test_w4_validation(kw, status):
     (dict(m=-2), SHAPE), (dict(k=-64), SHAPE),
     (dict(A=None), NULL), (dict(s=None), NULL), (dict(bdt=BF16), NULL),
     (dict(act=FP32), DTYPE), (dict(bias=FAKE, bdt=0), DTYPE),
-    (dict(g=64), GROUP), (dict(g=128), GROUP),
+    (dict(g=32), GROUP), (dict(g=256, k=512), GROUP), (dict(g=128, k=192), GROUP),
+    (dict(g=0), GROUP),
     (dict(n=8), UNSUP), (dict(k=96, g=96), UNSUP),
     (dict(A=FAKE + 4), ALIGN), (dict(s=FAKE + 1), ALIGN),
     (dict(m=0), OK), (dict(g=256, m=0), OK),
@@ -109,7 +110,8 @@ def test_repack_and_dequant_validation():
     assert L.qdequant_w4(FAKE, FAKE, FAKE, FAKE, 16, 128, 32, BF16, FP32, None) == GROUP
     assert L.qdequant_w4(FAKE, FAKE, FAKE, FAKE, 16, 128, 64, BF16, FP16, None) == DTYPE
     assert L.qdequant_w4(FAKE, FAKE, None, FAKE, 16, 128, 64, BF16, FP32, None) == NULL
-    assert L.qdequant_w8(FAKE, FAKE, FAKE, 16, 128, 64, FP16, FP32, None) == GROUP
+    assert L.qdequant_w8(FAKE, FAKE, FAKE, 16, 128, 32, FP16, FP32, None) == GROUP
+    assert L.qdequant_w8(FAKE, FAKE, FAKE, 16, 192, 128, FP16, FP32, None) == GROUP
     assert L.qdequant_w8(FAKE, FAKE, FAKE, 16, 128, -1, FP16, BF16, None) == DTYPE
 
 

@@ -88,6 +88,21 @@ def test_dequant_w8_bit_exact(dtype):
     assert np.array_equal(to_bits(qg.dequant_w8(tiled, S, S.dtype)), conv(ref))
 
 
+@pytest.mark.parametrize("dtype", [FP16, BF16])
+@pytest.mark.parametrize("group", [64, 128])
+def test_dequant_w8_grouped_bit_exact(dtype, group):
+    n, k = 48, 640
+    codes, s, _ = si.w8_weights(n, k, group, seed=group + 1, dtype=dtype)
+    codes[0, :4] = [-128, 127, 0, -1]
+    ref = oracle.dequant8(codes, s, group, dtype)
+    tiled = qg.repack_w8(to_dev(codes))
+    S = to_dev(s, dtype)
+    W32 = qg.dequant_w8(tiled, S, torch.float32, group).cpu().numpy()
+    assert np.array_equal(W32.view(np.uint32), ref.view(np.uint32))
+    conv = oracle.f32_to_bf16 if dtype == BF16 else oracle.f32_to_f16
+    assert np.array_equal(to_bits(qg.dequant_w8(tiled, S, S.dtype, group)), conv(ref))
+
+
 # -- integer-exact GEMMs: bit-exact on every path --------------------------------
 
 def _run_w4(p, path=None):
@@ -113,7 +128,7 @@ def _run_w8(p, path=None):
     if path:
         os.environ["QGEMM_FORCE_PATH"] = path
     try:
-        C = qg.gemm_w8a16(A, tiled, S, bias, -1)
+        C = qg.gemm_w8a16(A, tiled, S, bias, p.group)
     finally:
         os.environ.pop("QGEMM_FORCE_PATH", None)
     torch.cuda.synchronize()
@@ -154,6 +169,60 @@ def test_w8_integer_exact(m, n, k, path, dtype):
     exp = _exact_expected(Cref, dtype)
     bad = np.argwhere(got != exp)
     assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:4].tolist()}"
+
+
+@pytest.mark.parametrize("m,n,k,group", [
+    (1, 16, 128, 64), (3, 64, 448, 64), (16, 3584, 3584, 128), (40, 128, 640, 128),
+    (130, 256, 512, 64), (300, 512, 640, 128),
+])
+@pytest.mark.parametrize("path", ["decode", "prefill"])
+@pytest.mark.parametrize("dtype", [FP16, BF16])
+def test_w8_grouped_integer_exact(m, n, k, group, path, dtype):
+    # int8 codes with one scale per (channel, K-group): dyadic scales keep
+    # q * s exact in 16 bits, so every path must match RNE(Cref) bitwise.
+    p = si.w8_exact_problem(m, n, k, seed=m + n + k + group, dtype=dtype, bias_dtype=FP16,
+                            group=group)
+    Cref = oracle.gemm_w8(p.A, p.codes, p.scale, group, dtype, p.bias, FP16)
+    got = to_bits(_run_w8(p, path))
+    exp = _exact_expected(Cref, dtype)
+    bad = np.argwhere(got != exp)
+    assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:4].tolist()}"
+
+
+@pytest.mark.parametrize("tile", ["D8", "D8N", "D64", "D128", "X", "L", "M", "S"])
+@pytest.mark.parametrize("group", [64, 128])
+def test_prefill_tiles_w8_grouped_integer_exact(tile, group, monkeypatch):
+    p = si.w8_exact_problem(300, 512, 1024, seed=group, dtype=BF16, bias_dtype=FP16, group=group)
+    Cref = oracle.gemm_w8(p.A, p.codes, p.scale, group, BF16, p.bias, FP16)
+    monkeypatch.setenv("QGEMM_PREFILL_TILE", tile)
+    got = to_bits(_run_w8(p, "prefill"))
+    assert np.array_equal(got, _exact_expected(Cref, BF16))
+
+
+def test_prefill_w8_grouped_odd_group_count_falls_back(monkeypatch):
+    # K / group = 3: the direct-load tile needs pairs of groups; the generic
+    # tile of the same width takes the problem.
+    p = si.w8_exact_problem(300, 512, 384, seed=21, dtype=FP16, bias_dtype=FP16, group=128)
+    Cref = oracle.gemm_w8(p.A, p.codes, p.scale, 128, FP16, p.bias, FP16)
+    monkeypatch.setenv("QGEMM_PREFILL_TILE", "D8")
+    got = to_bits(_run_w8(p, "prefill"))
+    assert np.array_equal(got, _exact_expected(Cref, FP16))
+
+
+@pytest.mark.parametrize("m", [1, 16, 1024])
+@pytest.mark.parametrize("group", [64, 128])
+def test_w8_grouped_random_tolerance(m, group):
+    # Qwen2-7B-sized layer, random codes and scales: outputs sampled across
+    # the matrix within the fp16 tolerance.
+    n = k = 3584
+    p = si.w8_problem(m, n, k, group=group, tag="w8g", dtype=FP16)
+    C = _run_w8(p).float().cpu().numpy()
+    rng = np.random.default_rng(m + group)
+    rows = rng.integers(0, m, 96)
+    cols = rng.integers(0, n, 96)
+    ref = oracle.gemm_w8_at(p.A, p.codes, p.scale, rows, cols, group, FP16)
+    err = np.abs(C[rows, cols] - ref).max() / np.abs(ref).max()
+    assert err <= TOL[FP16], err
 
 
 # -- the tiny W4A16 problem (M=4, K=256, N=128, g=64), full oracle ----------------

@@ -146,12 +146,12 @@ def dequant_w4(tiled: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor, g
 
 
 def dequant_w8(tiled: torch.Tensor, scales: torch.Tensor,
-               out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+               out_dtype: torch.dtype = torch.float32, group_size: int = -1) -> torch.Tensor:
     _dev(tiled, "tiled")
     _dev(scales, "scales")
     n, k = tiled.shape
     out = torch.empty((n, k), dtype=out_dtype, device=tiled.device)
-    check("qdequant_w8", lib().qdequant_w8(_ptr(tiled), _ptr(scales), _ptr(out), n, k, -1,
+    check("qdequant_w8", lib().qdequant_w8(_ptr(tiled), _ptr(scales), _ptr(out), n, k, group_size,
                                            dtype_code(scales.dtype), dtype_code(out_dtype),
                                            _stream(tiled)))
     return out

@@ -63,7 +63,8 @@ qg_status gemm_checks(const void *A, const void *B, const void *scales, const vo
     if (k % group != 0) return QG_ERR_GROUP;
     if (n % 16 != 0 || k % 128 != 0) return QG_ERR_UNSUPPORTED;
   } else {
-    if (group != -1 && group != k) return QG_ERR_GROUP;
+    if (group != -1 && group != k && group != 64 && group != 128) return QG_ERR_GROUP;
+    if (group > 0 && k % group != 0) return QG_ERR_GROUP;
     if (n % 16 != 0 || k % 64 != 0) return QG_ERR_UNSUPPORTED;
   }
   if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(scales, 2) ||
@@ -184,11 +185,13 @@ qg_status qdequant_w8(const int8_t *B, const void *scales, void *W, int n, int k
   if (n == 0 || k == 0) return QG_OK;
   if (!B || !scales || !W) return QG_ERR_NULL;
   if (!act_ok(act) || !(out == QG_FP32 || out == act)) return QG_ERR_DTYPE;
-  if (group != -1 && group != k) return QG_ERR_GROUP;
+  if (group != -1 && group != k && group != 64 && group != 128) return QG_ERR_GROUP;
+  if (group > 0 && k % group != 0) return QG_ERR_GROUP;
   if (n % 16 != 0 || k % 64 != 0) return QG_ERR_UNSUPPORTED;
   if (!aligned(B, 16) || !aligned(W, 16) || !aligned(scales, 2)) return QG_ERR_ALIGN;
-  return hip_status(qg::launch_dequant_w8(B, static_cast<const uint16_t *>(scales), W, n, k, act,
-                                          out, as_stream(stream)));
+  const int g = (group == -1 || group == k) ? 0 : group;
+  return hip_status(qg::launch_dequant_w8(B, static_cast<const uint16_t *>(scales), W, n, k, g,
+                                          act, out, as_stream(stream)));
 }
 
 // ---------------------------------------------------------------------------
@@ -224,9 +227,10 @@ qg_status qgemm_w8a16(const void *A, const int8_t *B, const void *scales, const 
   (void)workspace; (void)ws_bytes;
   qg_status st = gemm_checks(A, B, scales, nullptr, C, bias, m, n, k, group, act, bias_dt, 8);
   if (st != QG_OK || m == 0 || n == 0) return st;
+  const int g = (group == -1 || group == k) ? 0 : group;   // 0: one scale per channel
   qg::GemmArgs a{static_cast<const uint16_t *>(A), B, static_cast<const uint16_t *>(scales),
                  nullptr, static_cast<const uint16_t *>(bias), static_cast<uint16_t *>(C),
-                 m, n, k, 0, static_cast<int>(act), static_cast<int>(bias_dt)};
+                 m, n, k, g, static_cast<int>(act), static_cast<int>(bias_dt)};
   hipStream_t s = as_stream(stream);
   const ForcedPath f = forced_path();
   const bool prefill_ok = n % 64 == 0;

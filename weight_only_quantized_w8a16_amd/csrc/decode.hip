@@ -187,7 +187,11 @@ __global__ __launch_bounds__(decode_threads<BPW>()) void k_decode_w4(const uint1
   reduce_store<ACT, NT>(red, nwaves, bias, bias_dt, nullptr, C, M, N, nt0);
 }
 
-template <int ACT, int BPW, int NT>
+// GS: 0 = one scale per channel, applied to the finished sum; 64 or 128 =
+// one scale per (channel, K-group), applied to each 64-k block's partial
+// product (the lane's channel is its output column, so the scale is a
+// per-lane value).
+template <int ACT, int BPW, int NT, int GS>
 __global__ __launch_bounds__(decode_threads<BPW>()) void k_decode_w8(const uint16_t *__restrict__ A,
                                                    const u32x4 *__restrict__ Bt,
                                                    const uint16_t *__restrict__ S,
@@ -211,21 +215,39 @@ __global__ __launch_bounds__(decode_threads<BPW>()) void k_decode_w8(const uint1
 #pragma unroll
       for (int t = 0; t < 2; ++t) af[b][t] = load_afrag(A, M, K, nl, (kb0 + b) * 64 + 32 * t + 8 * j);
     u32x4 bw[NT][BPW];
+    [[maybe_unused]] uint16_t sb[NT][BPW];
 #pragma unroll
     for (int i = 0; i < NT; ++i)
 #pragma unroll
-      for (int b = 0; b < BPW; ++b)
+      for (int b = 0; b < BPW; ++b) {
         bw[i][b] = __builtin_nontemporal_load(&Bt[(static_cast<size_t>(nt0 + i) * nb + kb0 + b) * 64 + lane]);
+        if constexpr (GS > 0)
+          sb[i][b] = S[static_cast<size_t>((nt0 + i) * 16 + nl) * (K / GS) + (kb0 + b) * 64 / GS];
+      }
 #pragma unroll
     for (int i = 0; i < NT; ++i)
 #pragma unroll
-      for (int b = 0; b < BPW; ++b)
+      for (int b = 0; b < BPW; ++b) {
+        if constexpr (GS == 0) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          u32x4 op = (ACT == kFP16) ? w8_run_to_f16(bw[i][b][2 * t], bw[i][b][2 * t + 1])
-                                    : w8_run_to_bf16(bw[i][b][2 * t], bw[i][b][2 * t + 1]);
-          acc[i] = mfma16x16x32<ACT>(af[b][t], op, acc[i]);
+          for (int t = 0; t < 2; ++t) {
+            u32x4 op = (ACT == kFP16) ? w8_run_to_f16(bw[i][b][2 * t], bw[i][b][2 * t + 1])
+                                      : w8_run_to_bf16(bw[i][b][2 * t], bw[i][b][2 * t + 1]);
+            acc[i] = mfma16x16x32<ACT>(af[b][t], op, acc[i]);
+          }
+        } else {
+          f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            u32x4 op = (ACT == kFP16) ? w8_run_to_f16(bw[i][b][2 * t], bw[i][b][2 * t + 1])
+                                      : w8_run_to_bf16(bw[i][b][2 * t], bw[i][b][2 * t + 1]);
+            d = mfma16x16x32<ACT>(af[b][t], op, d);
+          }
+          const float sc = bits_to_f32<ACT>(sb[i][b]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][r] += sc * d[r];
         }
+      }
   }
   constexpr int PER = NT * 256;
 #pragma unroll
@@ -233,7 +255,7 @@ __global__ __launch_bounds__(decode_threads<BPW>()) void k_decode_w8(const uint1
 #pragma unroll
     for (int r = 0; r < 4; ++r) red[wave * PER + i * 256 + r * 64 + lane] = acc[i][r];
   __syncthreads();
-  reduce_store<ACT, NT>(red, nwaves, bias, bias_dt, S, C, M, N, nt0);
+  reduce_store<ACT, NT>(red, nwaves, bias, bias_dt, GS > 0 ? nullptr : S, C, M, N, nt0);
 }
 
 // ---------------------------------------------------------------------------
@@ -466,9 +488,15 @@ hipError_t launch_decode_w8(const GemmArgs &a, hipStream_t s) {
   dim3 grid(ntiles / p.nt), block(64 * p.waves);
   size_t lds = static_cast<size_t>(p.waves) * p.nt * 256 * sizeof(float);
   const u32x4 *B = static_cast<const u32x4 *>(a.B);
-#define QG_DEC8(ACT_, BPW_, NT_)                                                               \
-  hipLaunchKernelGGL((k_decode_w8<ACT_, BPW_, NT_>), grid, block, lds, s, a.A, B, a.S, a.bias, \
+#define QG_DEC8G(ACT_, BPW_, NT_, GS_)                                                             \
+  hipLaunchKernelGGL((k_decode_w8<ACT_, BPW_, NT_, GS_>), grid, block, lds, s, a.A, B, a.S, a.bias, \
                      a.bias_dt, a.C, a.M, a.N, a.K)
+#define QG_DEC8(ACT_, BPW_, NT_)                                \
+  do {                                                          \
+    if (a.group == 64) QG_DEC8G(ACT_, BPW_, NT_, 64);           \
+    else if (a.group == 128) QG_DEC8G(ACT_, BPW_, NT_, 128);    \
+    else QG_DEC8G(ACT_, BPW_, NT_, 0);                          \
+  } while (0)
 #define QG_DEC8_NT(ACT_, BPW_)                       \
   if (p.nt == 2) QG_DEC8(ACT_, BPW_, 2);             \
   else QG_DEC8(ACT_, BPW_, 1);
@@ -479,6 +507,7 @@ hipError_t launch_decode_w8(const GemmArgs &a, hipStream_t s) {
 #undef QG_DEC8_BPW
 #undef QG_DEC8_NT
 #undef QG_DEC8
+#undef QG_DEC8G
   return hipGetLastError();
 }
 

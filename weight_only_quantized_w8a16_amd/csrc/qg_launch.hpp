@@ -22,8 +22,8 @@ hipError_t launch_quantize_w4(const void *W, uint8_t *packed, void *scale, void 
 
 hipError_t launch_dequant_w4(const uint8_t *B, const uint16_t *S, const uint16_t *Z, void *W,
                              int n, int k, int group, int act, int out, hipStream_t s);
-hipError_t launch_dequant_w8(const int8_t *B, const uint16_t *S, void *W, int n, int k, int act,
-                             int out, hipStream_t s);
+hipError_t launch_dequant_w8(const int8_t *B, const uint16_t *S, void *W, int n, int k, int group,
+                             int act, int out, hipStream_t s);
 
 // Dense GEMM problem as the kernels see it.
 struct GemmArgs {
@@ -33,7 +33,7 @@ struct GemmArgs {
   const uint16_t *Z;      // zeros (w4) or null
   const uint16_t *bias;   // [N] or null
   uint16_t *C;            // [M, N]
-  int M, N, K, group;     // group: 64/128 (w4), 0 = per channel (w8)
+  int M, N, K, group;     // group: 64/128 (w4; w8 with group scales), 0 = per channel (w8)
   int act, bias_dt;
 };
 

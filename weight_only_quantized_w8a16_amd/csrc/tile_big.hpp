@@ -74,11 +74,16 @@ __device__ __forceinline__ int dswz(int row, int chunk) {
 // holds gate rows 32 wn .. 32 wn + 31 of the tile's 128 outputs, then the
 // same up rows), output silu(gate) * up; kMoeFc2 -- rows of one expert's
 // tile, contiguous.
-template <class Cfg, int ACT, int WBITS, int MODE = kDense>
+// GS8 (int8 only): one scale per (channel, K-group), brought through the
+// same LDS windows as the int4 scales (the zero half of each window holds a
+// second copy of the scales, unused) and applied while dequantizing.
+template <class Cfg, int ACT, int WBITS, int MODE = kDense, bool GS8 = false>
 __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, int tile_n,
                                               const DmaLds &L) {
   constexpr int BK = Cfg::BK, TM = Cfg::TM, TN = Cfg::TN, NTHR = Cfg::NTHR;
   static_assert(MODE == kDense || WBITS == 4, "MoE experts are int4");
+  static_assert(!GS8 || WBITS == 8, "group scales without zeros: int8");
+  constexpr bool kWin = WBITS == 4 || GS8;   // scales through the LDS windows
   static_assert(MODE != kMoeFc1 || Cfg::BN == 256, "fc1 pairs 128 gate with 128 up rows");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
@@ -86,13 +91,13 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
   const int nsteps = K / BK;
   int row_lo, row_last;
   const uint8_t *Bb = p.B;
-  const uint16_t *Sb = p.S, *Zb = p.Z;
+  const uint16_t *Sb = p.S, *Zb = GS8 ? p.S : p.Z;
   uint32_t b_bytes, s_bytes;     // buffer extents (one expert for MoE)
   if constexpr (MODE == kDense) {
     row_lo = tile_m * Cfg::BM;
     row_last = min(p.M, row_lo + Cfg::BM) - 1;
     b_bytes = static_cast<uint32_t>(static_cast<uint64_t>(p.N) * K * WBITS / 8);
-    s_bytes = (WBITS == 4) ? static_cast<uint32_t>(static_cast<uint64_t>(p.N) * (K / p.group) * 2) : 0u;
+    s_bytes = kWin ? static_cast<uint32_t>(static_cast<uint64_t>(p.N) * (K / p.group) * 2) : 0u;
   } else {
     const MoeTile t = p.tiles[tile_m];
     row_lo = t.row0;
@@ -167,7 +172,7 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
       b_src[c] = static_cast<uint32_t>(wrow >> 4) * static_cast<uint32_t>(K >> 6) * 1024u + l * 16 + t * 8;
       b_lds0[c] = dswz(lrow, 4 * t + j);
       b_lds1[c] = 0;
-      b_sc[c] = 0;
+      b_sc[c] = GS8 ? lrow * 16 : 0;
     }
   }
   struct Regs {
@@ -212,7 +217,7 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
   constexpr int kHalfRows = (MODE == kMoeFc1) ? 64 : 128;
   constexpr int PPC = Cfg::BN / 128;   // parts per component
   auto sc_issue = [&](int t, int w) {
-    if constexpr (WBITS == 4) {
+    if constexpr (kWin) {
       const int soff = (t % PPC) * kHalfRows * kg * 2 + w * 16;
       char *dst = L.sc + (w & 1) * Cfg::SC_WIN + (t * 8 + wave * Cfg::SC_DMA) * 256;
 #pragma unroll
@@ -226,7 +231,7 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
     uint16_t s[NB], z[NB];
   };
   auto sc_read = [&](int u, ScaleRegs &v) {
-    if constexpr (WBITS == 4) {
+    if constexpr (kWin) {
       const int gi = u >> spg_lg;
       const char *win = L.sc + ((gi >> 3) & 1) * Cfg::SC_WIN + (gi & 7) * 2;
 #pragma unroll
@@ -244,6 +249,9 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
         const float z8 = bits_to_f32<ACT>(v.z[c]) - 8.0f * s;
         *reinterpret_cast<u32x4 *>(Bs + b_lds0[c]) = dequant_word_w4<ACT>(r.b[c].x, s, z8);
         *reinterpret_cast<u32x4 *>(Bs + b_lds1[c]) = dequant_word_w4<ACT>(r.b[c].y, s, z8);
+      } else if constexpr (GS8) {
+        *reinterpret_cast<u32x4 *>(Bs + b_lds0[c]) =
+            dequant_run_w8<ACT>(r.b[c].x, r.b[c].y, bits_to_f32<ACT>(v.s[c]));
       } else {
         *reinterpret_cast<u32x4 *>(Bs + b_lds0[c]) =
             (ACT == kFP16) ? w8_run_to_f16(r.b[c].x, r.b[c].y) : w8_run_to_bf16(r.b[c].x, r.b[c].y);
@@ -457,7 +465,7 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int col = n0 + wn * Cfg::WTN + 32 * j + 8 * q + 4 * khalf + e;
-        mul[j][q][e] = (WBITS == 8) ? bits_to_f32<ACT>(p.S[col]) : 1.0f;
+        mul[j][q][e] = (WBITS == 8 && !GS8) ? bits_to_f32<ACT>(p.S[col]) : 1.0f;
         add[j][q][e] = p.bias ? bits_to_f32_dyn(p.bias[col], p.bias_dt) : 0.0f;
       }
 #pragma unroll

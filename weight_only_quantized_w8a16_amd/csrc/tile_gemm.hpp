@@ -17,7 +17,8 @@
 // Dequant in this kernel: int4 w = fma(q, s, z - 8 s) rounded to nearest even
 // (equal to the exact (q - 8) s + z whenever z - 8 s is exact in fp32, as it
 // is for the scale/zero ranges used); int8 per-channel stages the exact code q
-// and multiplies the finished fp32 sum by the channel's scale.
+// and multiplies the finished fp32 sum by the channel's scale; int8 with
+// group scales stages q * s rounded to nearest even.
 #pragma once
 
 #include "qg_common.hpp"
@@ -91,7 +92,31 @@ __device__ __forceinline__ u32x4 dequant_word_w4(uint32_t w, float s, float z8) 
   return r;
 }
 
-template <class Cfg, int ACT, int WBITS, int MODE>
+// int8 codes with one scale per (channel, K-group): 8 offset-binary bytes ->
+// 8 packed 16-bit values q * s, q = byte - 128.  (q - 128 folded into the
+// fma: byte * s and 128 * s are exact in fp32 and so is their difference,
+// which then rounds once, to nearest even, into the 16-bit type.)
+template <int ACT>
+__device__ __forceinline__ u32x4 dequant_run_w8(uint32_t lo, uint32_t hi, float s) {
+  const float m = -128.0f * s;
+  const uint32_t ws[2] = {lo, hi};
+  u32x4 r;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float f0 = __builtin_fmaf(static_cast<float>(ws[h] & 0xFFu), s, m);
+    const float f1 = __builtin_fmaf(static_cast<float>((ws[h] >> 8) & 0xFFu), s, m);
+    const float f2 = __builtin_fmaf(static_cast<float>((ws[h] >> 16) & 0xFFu), s, m);
+    const float f3 = __builtin_fmaf(static_cast<float>(ws[h] >> 24), s, m);
+    r[2 * h] = pack2<ACT>(f0, f1);
+    r[2 * h + 1] = pack2<ACT>(f2, f3);
+  }
+  return r;
+}
+
+// GS8 (int8 only): one scale per (channel, K-group of p.group), applied
+// while dequantizing into LDS; otherwise int8 scales are per channel and
+// multiply the finished sum.
+template <class Cfg, int ACT, int WBITS, int MODE, bool GS8 = false>
 __device__ __forceinline__ void tile_gemm(const TileProblem &p, int tile_m, int tile_n,
                                           char *lds) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, NTHR = Cfg::NTHR;
@@ -171,7 +196,7 @@ __device__ __forceinline__ void tile_gemm(const TileProblem &p, int tile_m, int 
       b_src[c] = Bbase + (static_cast<size_t>(wrow >> 4) * (K >> 6)) * 1024 + l * 16 + t * 8;
       b_lds0[c] = swz(lrow, 4 * t + j);
       b_lds1[c] = 0;
-      b_sidx[c] = 0;
+      b_sidx[c] = GS8 ? static_cast<size_t>(wrow) * (K / p.group) : 0;
     }
   }
 
@@ -198,6 +223,7 @@ __device__ __forceinline__ void tile_gemm(const TileProblem &p, int tile_m, int 
         r.z[c] = Zbase[gi];
       } else {
         r.b[c] = *reinterpret_cast<const u32x2 *>(b_src[c] + static_cast<size_t>(step) * 1024);
+        if constexpr (GS8) r.s[c] = Sbase[b_sidx[c] + k0 / p.group];
       }
     }
   };
@@ -217,6 +243,9 @@ __device__ __forceinline__ void tile_gemm(const TileProblem &p, int tile_m, int 
         const float z8 = bits_to_f32<ACT>(r.z[c]) - 8.0f * s;
         *reinterpret_cast<u32x4 *>(Bs + b_lds0[c]) = dequant_word_w4<ACT>(r.b[c].x, s, z8);
         *reinterpret_cast<u32x4 *>(Bs + b_lds1[c]) = dequant_word_w4<ACT>(r.b[c].y, s, z8);
+      } else if constexpr (GS8) {
+        *reinterpret_cast<u32x4 *>(Bs + b_lds0[c]) =
+            dequant_run_w8<ACT>(r.b[c].x, r.b[c].y, bits_to_f32<ACT>(r.s[c]));
       } else {
         *reinterpret_cast<u32x4 *>(Bs + b_lds0[c]) =
             (ACT == kFP16) ? w8_run_to_f16(r.b[c].x, r.b[c].y) : w8_run_to_bf16(r.b[c].x, r.b[c].y);
@@ -327,7 +356,7 @@ __device__ __forceinline__ void tile_gemm(const TileProblem &p, int tile_m, int 
     for (int jn = 0; jn < TN; ++jn) {
       const int col = n0 + wn * Cfg::WTN + 32 * jn + col_in;
       float cs = 1.0f, cb = 0.0f;
-      if constexpr (WBITS == 8) cs = bits_to_f32<ACT>(Sbase[col]);
+      if constexpr (WBITS == 8 && !GS8) cs = bits_to_f32<ACT>(Sbase[col]);
       if (MODE == kDense && p.bias) cb = bits_to_f32_dyn(p.bias[col], p.bias_dt);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
@@ -336,7 +365,7 @@ __device__ __forceinline__ void tile_gemm(const TileProblem &p, int tile_m, int 
           const int r = row_lo + wm * Cfg::WTM + 32 * i + 8 * (v >> 2) + 4 * khalf + (v & 3);
           if (r < row_hi) {
             float val = acc[i][jn][v];
-            if constexpr (WBITS == 8) val *= cs;
+            if constexpr (WBITS == 8 && !GS8) val *= cs;
             val += cb;
             p.C[static_cast<size_t>(r) * p.N + col] = f32_to_bits<ACT>(val);
           }

@@ -334,15 +334,16 @@ __global__ void k_dequant_w4(const uint8_t *__restrict__ B, const uint16_t *__re
   }
 }
 
+// group 0: one scale per channel; else one per (channel, K-group).
 template <int ACT, int OUT>
 __global__ void k_dequant_w8(const int8_t *__restrict__ B, const uint16_t *__restrict__ S,
-                             void *__restrict__ W, int n, int k, long long runs) {
+                             void *__restrict__ W, int n, int k, int group, long long runs) {
   long long r = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (r >= runs) return;
   int per_row = k >> 3;
   int row = static_cast<int>(r / per_row), k0 = static_cast<int>(r % per_row) * 8;
   uint2 run = *reinterpret_cast<const uint2 *>(B + w8_run_offset(row, k0, k));
-  float s = bits_to_f32<ACT>(S[row]);
+  float s = bits_to_f32<ACT>(group > 0 ? S[static_cast<size_t>(row) * (k / group) + k0 / group] : S[row]);
   float v[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -379,11 +380,11 @@ hipError_t launch_dequant_w4(const uint8_t *B, const uint16_t *S, const uint16_t
   return hipGetLastError();
 }
 
-hipError_t launch_dequant_w8(const int8_t *B, const uint16_t *S, void *W, int n, int k, int act,
-                             int out, hipStream_t s) {
+hipError_t launch_dequant_w8(const int8_t *B, const uint16_t *S, void *W, int n, int k, int group,
+                             int act, int out, hipStream_t s) {
   long long runs = static_cast<long long>(n) * k / 8;
   dim3 g(grid_for(runs, 256)), b(256);
-#define QG_DQ8(A_, O_) hipLaunchKernelGGL((k_dequant_w8<A_, O_>), g, b, 0, s, B, S, W, n, k, runs)
+#define QG_DQ8(A_, O_) hipLaunchKernelGGL((k_dequant_w8<A_, O_>), g, b, 0, s, B, S, W, n, k, group, runs)
   if (act == kBF16) {
     if (out == QG_FP32) QG_DQ8(kBF16, QG_FP32); else QG_DQ8(kBF16, kBF16);
   } else {
