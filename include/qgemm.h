@@ -170,8 +170,13 @@ qg_status qdequant_w8(const int8_t *B_tiled, const void *scales, void *W_out, in
  *           product instead); per channel the scale multiplies the fp32 sum.
  *   Tile multiples: n % 16 == 0; k % 128 == 0 (w4) or k % 64 == 0 (w8);
  *   m is any value >= 0.  Accumulation is fp32; C = RNE(acc + bias).
- *   workspace: device scratch of at least qgemm_workspace_size() bytes
- *   (may be NULL when that size is 0).  The current kernels need none.
+ *   workspace: optional device scratch, 256-byte aligned.  When it holds at
+ *   least qgemm_workspace_size() bytes (> 0 only for problems the prefill
+ *   path splits along K: today the 64 x 64 tile at m <= 128 with k >= 2048)
+ *   the K slices write fp32 partials [slices, m, n] there and one more
+ *   launch sums them in slice order, then scales, adds bias and rounds;
+ *   with less (or NULL) the same call runs unsplit.  Calls that share a
+ *   workspace must not overlap.
  * ---------------------------------------------------------------------- */
 size_t qgemm_workspace_size(int m, int n, int k, int group_size, int weight_bits);
 

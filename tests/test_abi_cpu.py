@@ -184,3 +184,15 @@ def q4(**kw):
 ])
 def test_quantize_validation(kw, status):
     assert q4(**kw) == status
+
+
+def test_workspace_query_and_alignment():
+    L = qg.lib()
+    # split-K partials: two fp32 [m, n] slices where the plan splits K
+    assert L.qgemm_workspace_size(128, 3072, 2048, 64, 4) == 2 * 128 * 3072 * 4
+    assert L.qgemm_workspace_size(128, 3584, 3584, -1, 8) == 2 * 128 * 3584 * 4
+    for args in [(512, 3072, 2048, 64, 4), (16, 3072, 2048, 64, 4), (128, 131072, 2048, 64, 4),
+                 (0, 3072, 2048, 64, 4), (128, 3072, 2048, 64, 5), (128, 3072, 2048, 96, 4)]:
+        assert L.qgemm_workspace_size(*args) == 0, args
+    # a workspace that is given must be 256-byte aligned (checked before any launch)
+    assert w4(m=128, n=3072, k=2048, ws=FAKE + 16, wsb=1 << 20) == ALIGN

@@ -1,0 +1,94 @@
+"""GPU parity of the split-K prefill path: K slices write fp32 partials to
+the caller's workspace and one reduction sums them in slice order.  On
+integer-exact inputs every summation order gives the same fp32 value, so
+every tile, slice count and weight format must match the oracle bitwise."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth_inputs as si
+import weight_only_quantized_w8a16_amd as qg
+from helpers import BF16, FP16, to_bits, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _prefill_only(monkeypatch):
+    monkeypatch.setenv("QGEMM_FORCE_PATH", "prefill")
+    monkeypatch.delenv("QGEMM_SPLITK", raising=False)
+    monkeypatch.delenv("QGEMM_PREFILL_TILE", raising=False)
+
+
+def expected(Cref, dtype):
+    conv = oracle.f32_to_bf16 if dtype == BF16 else oracle.f32_to_f16
+    return conv(Cref.astype(np.float32))
+
+
+def _bias(p):
+    return to_dev(p.bias, p.bias_dtype) if p.bias is not None else None
+
+
+def run_w4(p, workspace=None):
+    C = qg.gemm_w4a16(to_dev(p.A, p.dtype), qg.repack_w4(to_dev(p.packed)), to_dev(p.scale, p.dtype),
+                      to_dev(p.zero, p.dtype), _bias(p), p.group, workspace=workspace)
+    torch.cuda.synchronize()
+    return to_bits(C)
+
+
+def run_w8(p, workspace=None):
+    C = qg.gemm_w8a16(to_dev(p.A, p.dtype), qg.repack_w8(to_dev(p.codes)), to_dev(p.scale, p.dtype),
+                      _bias(p), p.group, workspace=workspace)
+    torch.cuda.synchronize()
+    return to_bits(C)
+
+
+@pytest.mark.parametrize("tile", ["D8", "D8N", "D64", "D128", "X", "L", "M", "S"])
+@pytest.mark.parametrize("slices", [2, 3, 4])
+@pytest.mark.parametrize("group", [64, 128])
+def test_split_w4_every_tile_exact(tile, slices, group, monkeypatch):
+    # K = 4096: 64 steps, so with 128-groups (16-step windows) 3 and 4
+    # slices still give more than one slice; M and N ragged against tiles.
+    p = si.w4_exact_problem(300, 768, 4096, group, seed=slices + group, dtype=BF16, bias_dtype=FP16)
+    Cref = oracle.gemm_w4(p.A, p.packed, p.scale, p.zero, group, BF16, p.bias, FP16)
+    monkeypatch.setenv("QGEMM_PREFILL_TILE", tile)
+    monkeypatch.setenv("QGEMM_SPLITK", str(slices))
+    assert np.array_equal(run_w4(p), expected(Cref, BF16))
+
+
+@pytest.mark.parametrize("tile", ["D8", "D8N", "D64", "D128", "X", "L", "M", "S"])
+@pytest.mark.parametrize("group", [-1, 128])
+def test_split_w8_every_tile_exact(tile, group, monkeypatch):
+    p = si.w8_exact_problem(200, 512, 3584, seed=7, dtype=FP16, bias_dtype=FP16, group=group)
+    Cref = oracle.gemm_w8(p.A, p.codes, p.scale, group, FP16, p.bias, FP16)
+    monkeypatch.setenv("QGEMM_PREFILL_TILE", tile)
+    monkeypatch.setenv("QGEMM_SPLITK", "3")
+    assert np.array_equal(run_w8(p), expected(Cref, FP16))
+
+
+def test_automatic_split_shape_and_small_workspace():
+    # M = 128, N = 3072, K = 2048: the plan splits K in two (the library asks
+    # for workspace); with too little workspace the call runs unsplit.  Both
+    # give the exact result.
+    m, n, k, g = 128, 3072, 2048, 64
+    assert qg.gemm_workspace_size(m, n, k, g, 4) == 2 * m * n * 4
+    p = si.w4_exact_problem(m, n, k, g, seed=5, dtype=BF16, bias_dtype=FP16)
+    exp = expected(oracle.gemm_w4(p.A, p.packed, p.scale, p.zero, g, BF16, p.bias, FP16), BF16)
+    assert np.array_equal(run_w4(p), exp)
+    small = torch.empty(1024, dtype=torch.uint8, device="cuda")
+    assert np.array_equal(run_w4(p, workspace=small), exp)
+
+
+def test_split_random_data_within_tolerance(monkeypatch):
+    # Random bf16 data: the split result stays within the bf16 tolerance of
+    # the oracle (only the fp32 summation order differs from unsplit).
+    p = si.w4_problem(96, 1024, 4096, 64, tag="split")
+    Cref = oracle.gemm_w4(p.A, p.packed, p.scale, p.zero, 64, BF16)
+    monkeypatch.setenv("QGEMM_SPLITK", "4")
+    got = run_w4(p)
+    C = torch.from_numpy(got.view(np.int16)).view(torch.bfloat16).float().numpy()
+    err = np.abs(C - Cref).max() / np.abs(Cref).max()
+    assert err <= 1e-2, err

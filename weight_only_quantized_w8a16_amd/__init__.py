@@ -163,9 +163,23 @@ def gemm_workspace_size(m: int, n: int, k: int, group_size: int, weight_bits: in
     return int(lib().qgemm_workspace_size(m, n, k, group_size, weight_bits))
 
 
+def _workspace(m: int, n: int, k: int, group_size: int, bits: int, device,
+               given: Optional[torch.Tensor]):
+    """(tensor, bytes) of workspace for a GEMM: the caller's, else a fresh
+    one when the library asks for any (split-K partials), else (None, 0)."""
+    if given is not None:
+        _dev(given, "workspace")
+        return given, given.numel() * given.element_size()
+    need = int(lib().qgemm_workspace_size(m, n, k, group_size, bits))
+    if need == 0:
+        return None, 0
+    return torch.empty(need, dtype=torch.uint8, device=device), need
+
+
 def gemm_w4a16(A: torch.Tensor, B_tiled: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
                bias: Optional[torch.Tensor] = None, group_size: int = 64,
-               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+               out: Optional[torch.Tensor] = None,
+               workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """C = A . dequant(B)^T (+ bias); A [..., k] bf16/fp16, B tiled int4."""
     _dev(A, "A")
     for t, nm in ((B_tiled, "B_tiled"), (scales, "scales"), (zeros, "zeros")):
@@ -178,16 +192,18 @@ def gemm_w4a16(A: torch.Tensor, B_tiled: torch.Tensor, scales: torch.Tensor, zer
     m, n = A2.shape[0], B_tiled.shape[0]
     C = out if out is not None else torch.empty((m, n), dtype=A.dtype, device=A.device)
     _dev(C, "out")
+    ws, ws_bytes = _workspace(m, n, k, group_size, 4, A.device, workspace)
     check("qgemm_w4a16", lib().qgemm_w4a16(
         _ptr(A2), _ptr(B_tiled), _ptr(scales), _ptr(zeros), _ptr(bias), _ptr(C), m, n, k,
         group_size, dtype_code(A.dtype), dtype_code(None if bias is None else bias.dtype),
-        None, 0, _stream(A)))
+        _ptr(ws), ws_bytes, _stream(A)))
     return C.reshape(*lead, n)
 
 
 def gemm_w8a16(A: torch.Tensor, B_tiled: torch.Tensor, scales: torch.Tensor,
                bias: Optional[torch.Tensor] = None, group_size: int = -1,
-               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+               out: Optional[torch.Tensor] = None,
+               workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """C = A . dequant(B)^T (+ bias); A [..., k] bf16/fp16, B tiled int8."""
     _dev(A, "A")
     _dev(B_tiled, "B_tiled")
@@ -200,10 +216,11 @@ def gemm_w8a16(A: torch.Tensor, B_tiled: torch.Tensor, scales: torch.Tensor,
     m, n = A2.shape[0], B_tiled.shape[0]
     C = out if out is not None else torch.empty((m, n), dtype=A.dtype, device=A.device)
     _dev(C, "out")
+    ws, ws_bytes = _workspace(m, n, k, group_size, 8, A.device, workspace)
     check("qgemm_w8a16", lib().qgemm_w8a16(
         _ptr(A2), _ptr(B_tiled), _ptr(scales), _ptr(bias), _ptr(C), m, n, k, group_size,
-        dtype_code(A.dtype), dtype_code(None if bias is None else bias.dtype), None, 0,
-        _stream(A)))
+        dtype_code(A.dtype), dtype_code(None if bias is None else bias.dtype), _ptr(ws),
+        ws_bytes, _stream(A)))
     return C.reshape(*lead, n)
 
 

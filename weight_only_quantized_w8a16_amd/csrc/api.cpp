@@ -197,47 +197,59 @@ qg_status qdequant_w8(const int8_t *B, const void *scales, void *W, int n, int k
 // ---------------------------------------------------------------------------
 // GEMM
 // ---------------------------------------------------------------------------
+// Whether a GEMM runs on the prefill path (else the decode kernels).
+static bool uses_prefill(int m, int n) {
+  const ForcedPath f = forced_path();
+  const bool prefill_ok = n % 64 == 0;
+  if (f == kForcePrefill && prefill_ok) return true;
+  return !(f == kForceDecode || m <= kDecodeMaxM || !prefill_ok);
+}
+
+// Workspace: the prefill path's split-K partials for problems it would
+// split; 0 for everything else (and for arguments a GEMM would reject).
 size_t qgemm_workspace_size(int m, int n, int k, int group_size, int weight_bits) {
-  (void)m; (void)n; (void)k; (void)group_size; (void)weight_bits;
-  return 0;
+  if (m <= 0 || n <= 0 || k <= 0 || (weight_bits != 4 && weight_bits != 8)) return 0;
+  if (!uses_prefill(m, n)) return 0;
+  qg::GemmArgs a{};
+  a.M = m;
+  a.N = n;
+  a.K = k;
+  if (weight_bits == 4) a.group = group_size;
+  else a.group = (group_size == -1 || group_size == k) ? 0 : group_size;
+  if (a.group < 0 || (a.group > 0 && k % a.group != 0)) return 0;
+  const size_t b = qg::prefill_workspace_bytes(a, weight_bits);
+  return b ? (b + 255) & ~static_cast<size_t>(255) : 0;
 }
 
 qg_status qgemm_w4a16(const void *A, const uint8_t *B, const void *scales, const void *zeros,
                       const void *bias, void *C, int m, int n, int k, int group, qg_dtype act,
                       qg_dtype bias_dt, void *workspace, size_t ws_bytes, void *stream) {
-  (void)workspace; (void)ws_bytes;
   qg_status st = gemm_checks(A, B, scales, zeros, C, bias, m, n, k, group, act, bias_dt, 4);
   if (st != QG_OK || m == 0 || n == 0) return st;
+  if (workspace && ws_bytes && !aligned(workspace, 256)) return QG_ERR_ALIGN;
   qg::GemmArgs a{static_cast<const uint16_t *>(A), B, static_cast<const uint16_t *>(scales),
                  static_cast<const uint16_t *>(zeros), static_cast<const uint16_t *>(bias),
                  static_cast<uint16_t *>(C), m, n, k, group, static_cast<int>(act),
-                 static_cast<int>(bias_dt)};
+                 static_cast<int>(bias_dt), workspace, workspace ? ws_bytes : 0};
   hipStream_t s = as_stream(stream);
-  const ForcedPath f = forced_path();
-  const bool prefill_ok = n % 64 == 0;
-  if (f == kForcePrefill && prefill_ok) return hip_status(qg::launch_prefill_w4(a, s));
-  if (f == kForceDecode || m <= kDecodeMaxM || !prefill_ok)
-    return hip_status(by_row_slabs(a, qg::launch_decode_w4, s));
-  return hip_status(qg::launch_prefill_w4(a, s));
+  if (uses_prefill(m, n)) return hip_status(qg::launch_prefill_w4(a, s));
+  return hip_status(by_row_slabs(a, qg::launch_decode_w4, s));
 }
 
 qg_status qgemm_w8a16(const void *A, const int8_t *B, const void *scales, const void *bias,
                       void *C, int m, int n, int k, int group, qg_dtype act, qg_dtype bias_dt,
                       void *workspace, size_t ws_bytes, void *stream) {
-  (void)workspace; (void)ws_bytes;
   qg_status st = gemm_checks(A, B, scales, nullptr, C, bias, m, n, k, group, act, bias_dt, 8);
   if (st != QG_OK || m == 0 || n == 0) return st;
+  if (workspace && ws_bytes && !aligned(workspace, 256)) return QG_ERR_ALIGN;
   const int g = (group == -1 || group == k) ? 0 : group;   // 0: one scale per channel
   qg::GemmArgs a{static_cast<const uint16_t *>(A), B, static_cast<const uint16_t *>(scales),
                  nullptr, static_cast<const uint16_t *>(bias), static_cast<uint16_t *>(C),
-                 m, n, k, g, static_cast<int>(act), static_cast<int>(bias_dt)};
+                 m, n, k, g, static_cast<int>(act), static_cast<int>(bias_dt), workspace,
+                 workspace ? ws_bytes : 0};
   hipStream_t s = as_stream(stream);
-  const ForcedPath f = forced_path();
-  const bool prefill_ok = n % 64 == 0;
-  if (f == kForcePrefill && prefill_ok) return hip_status(qg::launch_prefill_w8(a, s));
-  if (f == kForceDecode || m <= kDecodeMaxM || !prefill_ok)
-    return hip_status(by_row_slabs(a, qg::launch_decode_w8, s));
-  return hip_status(qg::launch_prefill_w8(a, s));
+  if (uses_prefill(m, n)) return hip_status(qg::launch_prefill_w8(a, s));
+  return hip_status(by_row_slabs(a, qg::launch_decode_w8, s));
 }
 
 // ---------------------------------------------------------------------------

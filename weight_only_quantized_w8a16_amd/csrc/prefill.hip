@@ -43,17 +43,65 @@ __device__ __forceinline__ void grouped_tile(int id, int tiles_m, int tiles_n, i
   tn = in / gsz;
 }
 
+// A split-K grid is nsplit copies of the tile grid, slice-major: position
+// id is tile id % T of K slice id / T (T tiles).
+template <bool SPLIT>
+__device__ __forceinline__ void split_tile(const TileProblem &p, int tiles_n, int &tm, int &tn,
+                                           int &slice) {
+  if constexpr (!SPLIT) {
+    slice = 0;
+    grouped_tile(xcd_linear_id(), gridDim.x / tiles_n, tiles_n, tm, tn);
+    return;
+  }
+  const int nsplit = (p.K / 64 + p.kseg - 1) / p.kseg;
+  const int per = gridDim.x / nsplit;
+  const int id = xcd_linear_id();
+  slice = id / per;
+  grouped_tile(id - slice * per, per / tiles_n, tiles_n, tm, tn);
+}
+
 // GS8: int8 codes with one scale per (channel, K-group).
 template <class Cfg, int ACT, int WBITS, bool GS8>
 __global__ __launch_bounds__(Cfg::NTHR) void k_prefill(TileProblem p, int tiles_n) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  const int id = xcd_linear_id();
-  int tm, tn;
-  grouped_tile(id, gridDim.x / tiles_n, tiles_n, tm, tn);
-  tile_gemm<Cfg, ACT, WBITS, kDense, GS8>(p, tm, tn, lds);
+  int tm, tn, slice = 0;
+  if (p.part) split_tile<true>(p, tiles_n, tm, tn, slice);
+  else split_tile<false>(p, tiles_n, tm, tn, slice);
+  tile_gemm<Cfg, ACT, WBITS, kDense, GS8>(p, tm, tn, lds, slice);
 }
 
-template <class Cfg, int ACT, int WBITS, bool GS8>
+// Split-K reduction: C = RNE(sum of the slices' fp32 partials, in slice
+// order (x the channel scale for per-channel int8) + bias), 4 outputs per
+// thread.
+template <int ACT>
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__ part, int nsplit,
+                                                       int M, int N,
+                                                       const uint16_t *__restrict__ colscale,
+                                                       const uint16_t *__restrict__ bias,
+                                                       int bias_dt, uint16_t *__restrict__ C) {
+  const long long q = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (q >= static_cast<long long>(M) * N / 4) return;
+  const size_t mn = static_cast<size_t>(M) * N;
+  f32x4 acc = *reinterpret_cast<const f32x4 *>(part + 4 * q);
+  for (int sl = 1; sl < nsplit; ++sl) acc += *reinterpret_cast<const f32x4 *>(part + sl * mn + 4 * q);
+  const int col = static_cast<int>((4 * q) % N);
+  uint32_t out[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float v[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      float x = acc[2 * h + e];
+      if (colscale) x *= bits_to_f32<ACT>(colscale[col + 2 * h + e]);
+      if (bias) x += bits_to_f32_dyn(bias[col + 2 * h + e], bias_dt);
+      v[e] = x;
+    }
+    out[h] = pack2<ACT>(v[0], v[1]);
+  }
+  *reinterpret_cast<uint2 *>(C + 4 * q) = make_uint2(out[0], out[1]);
+}
+
+template <class Cfg, int ACT, int WBITS, bool GS8, bool SPLIT>
 __global__ __launch_bounds__(Cfg::NTHR) void k_prefill_dma(TileProblem p, int tiles_n) {
   __shared__ __attribute__((aligned(16))) char a0[Cfg::STAGE_A];
   __shared__ __attribute__((aligned(16))) char a1[Cfg::STAGE_A];
@@ -61,10 +109,9 @@ __global__ __launch_bounds__(Cfg::NTHR) void k_prefill_dma(TileProblem p, int ti
   __shared__ __attribute__((aligned(16))) char b1[Cfg::STAGE_B];
   __shared__ __attribute__((aligned(16))) char sc[2 * Cfg::SC_WIN];
   const DmaLds L{{a0, a1}, {b0, b1}, sc};
-  const int id = xcd_linear_id();
-  int tm, tn;
-  grouped_tile(id, gridDim.x / tiles_n, tiles_n, tm, tn);
-  tile_gemm_dma<Cfg, ACT, WBITS, kDense, GS8>(p, tm, tn, L);
+  int tm, tn, slice;
+  split_tile<SPLIT>(p, tiles_n, tm, tn, slice);
+  tile_gemm_dma<Cfg, ACT, WBITS, kDense, GS8, SPLIT>(p, tm, tn, L, slice);
 }
 
 namespace {
@@ -78,46 +125,13 @@ using CfgL = TileCfg<256, 128, 4, 2>;   // 8 waves, 64x64 per wave
 using CfgM = TileCfg<128, 128, 2, 2>;   // 4 waves, 64x64 per wave
 using CfgS = TileCfg<64, 64, 2, 2>;     // 4 waves, 32x32 per wave
 
-template <class Cfg, int ACT, int WBITS, bool GS8>
-hipError_t run(const GemmArgs &a, hipStream_t s) {
-  TileProblem p{};
-  p.A = a.A;
-  p.B = static_cast<const uint8_t *>(a.B);
-  p.S = a.S;
-  p.Z = a.Z;
-  p.bias = a.bias;
-  p.C = a.C;
-  p.M = a.M;
-  p.N = a.N;
-  p.K = a.K;
-  p.group = a.group > 0 ? a.group : a.K;
-  p.bias_dt = a.bias_dt;
-  const int tm = (a.M + Cfg::BM - 1) / Cfg::BM, tn = a.N / Cfg::BN;
-  auto kern = k_prefill<Cfg, ACT, WBITS, GS8>;
-  static bool attr_set = false;   // benign race: idempotent
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  hipLaunchKernelGGL(kern, dim3(tm * tn), dim3(Cfg::NTHR), Cfg::LDS, s, p, tn);
-  return hipGetLastError();
-}
+// K slices of one launch: partials in `part` (nullptr: no split).
+struct Split {
+  float *part = nullptr;
+  int kseg = 0, nsplit = 1;
+};
 
-template <class Cfg, int ACT, int WBITS, bool GS8>
-hipError_t run_dma(const GemmArgs &a, hipStream_t s) {
-  // The kernel keeps 32-bit element / byte offsets.
-  const uint64_t lim = uint64_t(1) << 31;
-  // Otherwise the generic tile kernel of the same width takes the problem.
-  using Fallback = std::conditional_t<Cfg::BN == 256, CfgX, CfgL>;
-  if (uint64_t(a.M) * a.K >= lim || uint64_t(a.N) * a.K * WBITS / 8 >= lim)
-    return run<Fallback, ACT, WBITS, GS8>(a, s);
-  // Group scales (and int4 zeros) arrive as 4-byte pairs of groups.
-  if ((WBITS == 4 || GS8) &&
-      (((a.K / a.group) & 1) != 0 || (reinterpret_cast<uintptr_t>(a.S) & 3) != 0 ||
-       (WBITS == 4 && (reinterpret_cast<uintptr_t>(a.Z) & 3) != 0)))
-    return run<Fallback, ACT, WBITS, GS8>(a, s);
+TileProblem dense_problem(const GemmArgs &a, const Split &sp) {
   TileProblem p{};
   p.A = a.A;
   p.B = static_cast<const uint8_t *>(a.B);
@@ -131,48 +145,167 @@ hipError_t run_dma(const GemmArgs &a, hipStream_t s) {
   p.group = a.group > 0 ? a.group : a.K;
   p.bias_dt = a.bias_dt;
   p.a_rows = a.M;
-  const int tm = (a.M + Cfg::BM - 1) / Cfg::BM, tn = a.N / Cfg::BN;
-  hipLaunchKernelGGL((k_prefill_dma<Cfg, ACT, WBITS, GS8>), dim3(tm * tn), dim3(Cfg::NTHR), 0, s, p, tn);
+  p.part = sp.part;
+  p.kseg = sp.kseg;
+  return p;
+}
+
+template <int ACT, int WBITS, bool GS8>
+hipError_t reduce_split(const GemmArgs &a, const Split &sp, hipStream_t s) {
+  if (!sp.part) return hipGetLastError();
+  const long long q = static_cast<long long>(a.M) * a.N / 4;
+  hipLaunchKernelGGL(k_splitk_reduce<ACT>, dim3(static_cast<unsigned>((q + 255) / 256)), dim3(256), 0, s,
+                     sp.part, sp.nsplit, a.M, a.N, (WBITS == 8 && !GS8) ? a.S : nullptr, a.bias,
+                     a.bias_dt, a.C);
   return hipGetLastError();
 }
 
-// Tile choice, from on-device sweeps at K = 2048 and 3584 (M from 32 to
-// 4096): the direct-load tiles once there are enough of them to keep most
-// CUs busy, the generic tiles (down to 64 x 64) when the problem would leave
-// CUs idle.
-// QGEMM_PREFILL_TILE=X|D8|D8N|D64|D128|L|M|S forces one (tests and tuning);
-// D8, D8N, D64 and D128 are the 256 x 256, 256 x 128, 64 x 256 and
-// 128 x 256 tiles with direct-to-LDS activation loads.
-template <int ACT, int WBITS, bool GS8 = false>
-hipError_t dispatch(const GemmArgs &a, hipStream_t s) {
+template <class Cfg, int ACT, int WBITS, bool GS8>
+hipError_t run(const GemmArgs &a, hipStream_t s, const Split &sp = Split{}) {
+  const TileProblem p = dense_problem(a, sp);
+  const int tm = (a.M + Cfg::BM - 1) / Cfg::BM, tn = a.N / Cfg::BN;
+  auto kern = k_prefill<Cfg, ACT, WBITS, GS8>;
+  static bool attr_set = false;   // benign race: idempotent
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(tm * tn * sp.nsplit), dim3(Cfg::NTHR), Cfg::LDS, s, p, tn);
+  return reduce_split<ACT, WBITS, GS8>(a, sp, s);
+}
+
+// Whether the direct-load tiles take the problem (else the generic tile of
+// the same width does): 32-bit offsets, and group scales (int4 zeros too)
+// in 4-byte pairs of groups.
+template <int WBITS, bool GS8>
+bool dma_ok(const GemmArgs &a) {
+  const uint64_t lim = uint64_t(1) << 31;
+  if (uint64_t(a.M) * a.K >= lim || uint64_t(a.N) * a.K * WBITS / 8 >= lim) return false;
+  if ((WBITS == 4 || GS8) &&
+      (((a.K / a.group) & 1) != 0 || (reinterpret_cast<uintptr_t>(a.S) & 3) != 0 ||
+       (WBITS == 4 && (reinterpret_cast<uintptr_t>(a.Z) & 3) != 0)))
+    return false;
+  return true;
+}
+
+template <class Cfg, int ACT, int WBITS, bool GS8>
+hipError_t run_dma(const GemmArgs &a, hipStream_t s, const Split &sp = Split{}) {
+  using Fallback = std::conditional_t<Cfg::BN == 256, CfgX, CfgL>;
+  if (!dma_ok<WBITS, GS8>(a)) return run<Fallback, ACT, WBITS, GS8>(a, s, sp);
+  const TileProblem p = dense_problem(a, sp);
+  const int tm = (a.M + Cfg::BM - 1) / Cfg::BM, tn = a.N / Cfg::BN;
+  if (sp.part)
+    hipLaunchKernelGGL((k_prefill_dma<Cfg, ACT, WBITS, GS8, true>), dim3(tm * tn * sp.nsplit),
+                       dim3(Cfg::NTHR), 0, s, p, tn);
+  else
+    hipLaunchKernelGGL((k_prefill_dma<Cfg, ACT, WBITS, GS8, false>), dim3(tm * tn), dim3(Cfg::NTHR),
+                       0, s, p, tn);
+  return reduce_split<ACT, WBITS, GS8>(a, sp, s);
+}
+
+// Tile shapes.  Choice, from on-device sweeps at K = 2048 and 3584 (M from
+// 32 to 4096): the direct-load tiles once there are enough of them to keep
+// most CUs busy, the generic tiles (down to 64 x 64) when the problem would
+// leave CUs idle.  QGEMM_PREFILL_TILE=X|D8|D8N|D64|D128|L|M|S forces one
+// (tests and tuning); D8, D8N, D64 and D128 are the 256 x 256, 256 x 128,
+// 64 x 256 and 128 x 256 tiles with direct-to-LDS activation loads.
+enum Tile { kX, kD8, kD8N, kD64, kD128, kL, kM, kS };
+
+int choose_tile(const GemmArgs &a) {
   auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * (a.N / bn); };
   const bool n256 = a.N % 256 == 0, n128 = a.N % 128 == 0;
   if (const char *o = std::getenv("QGEMM_PREFILL_TILE")) {
     const std::string c(o);
-    if (c == "X" && n256) return run<CfgX, ACT, WBITS, GS8>(a, s);
-    if (c == "D8" && n256) return run_dma<CfgD8, ACT, WBITS, GS8>(a, s);
-    if (c == "D8N" && n128) return run_dma<CfgD8N, ACT, WBITS, GS8>(a, s);
-    if (c == "D64" && n256) return run_dma<CfgD64, ACT, WBITS, GS8>(a, s);
-    if (c == "D128" && n256) return run_dma<CfgD128, ACT, WBITS, GS8>(a, s);
-    if (c == "L" && n128) return run<CfgL, ACT, WBITS, GS8>(a, s);
-    if (c == "M" && n128) return run<CfgM, ACT, WBITS, GS8>(a, s);
-    if (c == "S") return run<CfgS, ACT, WBITS, GS8>(a, s);
+    if (c == "X" && n256) return kX;
+    if (c == "D8" && n256) return kD8;
+    if (c == "D8N" && n128) return kD8N;
+    if (c == "D64" && n256) return kD64;
+    if (c == "D128" && n256) return kD128;
+    if (c == "L" && n128) return kL;
+    if (c == "M" && n128) return kM;
+    if (c == "S") return kS;
   }
-  if (n256 && a.M > 128 && tiles(256, 256) >= 160) return run_dma<CfgD8, ACT, WBITS, GS8>(a, s);
+  if (n256 && a.M > 128 && tiles(256, 256) >= 160) return kD8;
   // Up to 192 rows the 64-row tile wastes fewer rows than a 256-row one.
-  if (n256 && a.M > 128 && a.M <= 192 && tiles(64, 256) >= 128) return run_dma<CfgD64, ACT, WBITS, GS8>(a, s);
-  if (n128 && a.M > 128 && tiles(256, 128) >= 128) return run_dma<CfgD8N, ACT, WBITS, GS8>(a, s);
+  if (n256 && a.M > 128 && a.M <= 192 && tiles(64, 256) >= 128) return kD64;
+  if (n128 && a.M > 128 && tiles(256, 128) >= 128) return kD8N;
   // Fewer rows: shorter direct-load tiles over the full 256-wide weight tile,
   // once there are enough of them.
-  if (n256 && a.M <= 64 && tiles(64, 256) >= 256) return run_dma<CfgD64, ACT, WBITS, GS8>(a, s);
-  if (n256 && a.M > 64 && a.M <= 128 && tiles(128, 256) >= 256) return run_dma<CfgD128, ACT, WBITS, GS8>(a, s);
-  if (n256 && a.M > 128 && tiles(64, 256) >= 128) return run_dma<CfgD64, ACT, WBITS, GS8>(a, s);
-  if (n128 && a.M > 128 && tiles(256, 128) >= 200) return run<CfgL, ACT, WBITS, GS8>(a, s);
-  if (n128 && a.M > 64 && tiles(128, 128) >= 256) return run<CfgM, ACT, WBITS, GS8>(a, s);
-  return run<CfgS, ACT, WBITS, GS8>(a, s);
+  if (n256 && a.M <= 64 && tiles(64, 256) >= 256) return kD64;
+  if (n256 && a.M > 64 && a.M <= 128 && tiles(128, 256) >= 256) return kD128;
+  if (n256 && a.M > 128 && tiles(64, 256) >= 128) return kD64;
+  if (n128 && a.M > 128 && tiles(256, 128) >= 200) return kL;
+  if (n128 && a.M > 64 && tiles(128, 128) >= 256) return kM;
+  return kS;
+}
+
+// Split-K plan: K slices written as fp32 partials to the caller's
+// workspace, then summed by one reduction launch.  Measured on MI355X, the
+// partials' traffic and the extra launch cost about what the shorter K loop
+// saves, except on the 64 x 64 tile at up to 128 rows with a long K loop
+// (few small tiles, each walking all of K): there two slices gain 15 %
+// (M = 128: N = 3072, K = 2048, int4 16.5 -> 13.9 us; N = 3584, K = 3584,
+// int8 20.4 -> 17.3 us), while at 256 rows and above, and on the larger
+// tiles, splitting was slower.  A slice is a whole number of scale windows
+// (8 groups) when the scales come through the direct-load tile's windows,
+// a multiple of 8 steps otherwise.  QGEMM_SPLITK=<n> asks for n slices (1:
+// none) on the tile chosen above (tests and tuning).
+struct Plan {
+  int tile;
+  Split split;
+  size_t bytes;   // workspace for the partials
+};
+
+Plan plan_prefill(const GemmArgs &a, int wbits, bool gs8) {
+  Plan pl{choose_tile(a), Split{}, 0};
+  const int nsteps = a.K / 64;
+  int want = (pl.tile == kS && a.M <= 128 && nsteps >= 32) ? 2 : 1;
+  if (const char *o = std::getenv("QGEMM_SPLITK")) want = std::atoi(o);
+  if (want <= 1) return pl;
+  const int g = a.group > 0 ? a.group : a.K;
+  const int unit = (wbits == 4 || gs8) ? 8 * (g / 64) : 8;
+  int kseg = (nsteps + want - 1) / want;
+  kseg = (kseg + unit - 1) / unit * unit;
+  const int nsplit = (nsteps + kseg - 1) / kseg;
+  if (nsplit < 2) return pl;
+  pl.split.kseg = kseg;
+  pl.split.nsplit = nsplit;
+  pl.bytes = static_cast<size_t>(nsplit) * a.M * a.N * sizeof(float);
+  return pl;
+}
+
+template <int ACT, int WBITS, bool GS8>
+hipError_t launch_tile(int tile, const GemmArgs &a, hipStream_t s, const Split &sp) {
+  switch (tile) {
+    case kX: return run<CfgX, ACT, WBITS, GS8>(a, s, sp);
+    case kD8: return run_dma<CfgD8, ACT, WBITS, GS8>(a, s, sp);
+    case kD8N: return run_dma<CfgD8N, ACT, WBITS, GS8>(a, s, sp);
+    case kD64: return run_dma<CfgD64, ACT, WBITS, GS8>(a, s, sp);
+    case kD128: return run_dma<CfgD128, ACT, WBITS, GS8>(a, s, sp);
+    case kL: return run<CfgL, ACT, WBITS, GS8>(a, s, sp);
+    case kM: return run<CfgM, ACT, WBITS, GS8>(a, s, sp);
+    default: return run<CfgS, ACT, WBITS, GS8>(a, s, sp);
+  }
+}
+
+template <int ACT, int WBITS, bool GS8 = false>
+hipError_t dispatch(const GemmArgs &a, hipStream_t s) {
+  Plan pl = plan_prefill(a, WBITS, GS8);
+  if (pl.split.nsplit > 1 && a.ws && a.ws_bytes >= pl.bytes)
+    pl.split.part = static_cast<float *>(a.ws);
+  else
+    pl.split = Split{};
+  return launch_tile<ACT, WBITS, GS8>(pl.tile, a, s, pl.split);
 }
 
 }  // namespace
+
+size_t prefill_workspace_bytes(const GemmArgs &a, int wbits) {
+  const Plan pl = plan_prefill(a, wbits, wbits == 8 && a.group > 0);
+  return pl.split.nsplit > 1 ? pl.bytes : 0;
+}
 
 hipError_t launch_prefill_w4(const GemmArgs &a, hipStream_t s) {
   return a.act == kBF16 ? dispatch<kBF16, 4>(a, s) : dispatch<kFP16, 4>(a, s);

@@ -35,6 +35,8 @@ struct GemmArgs {
   uint16_t *C;            // [M, N]
   int M, N, K, group;     // group: 64/128 (w4; w8 with group scales), 0 = per channel (w8)
   int act, bias_dt;
+  void *ws = nullptr;     // caller's workspace (split-K partials), may be null
+  size_t ws_bytes = 0;
 };
 
 // Decode path: M <= 16, weights streamed once.
@@ -42,6 +44,9 @@ hipError_t launch_decode_w4(const GemmArgs &a, hipStream_t s);
 hipError_t launch_decode_w8(const GemmArgs &a, hipStream_t s);
 // Prefill path: any M, matrix-core tiles with weights dequantized into LDS.
 hipError_t launch_prefill_w4(const GemmArgs &a, hipStream_t s);
+// Workspace bytes the prefill path would use for split-K on this problem (0:
+// none); with less workspace it runs unsplit.
+size_t prefill_workspace_bytes(const GemmArgs &a, int wbits);
 hipError_t launch_prefill_w8(const GemmArgs &a, hipStream_t s);
 
 // MoE pipeline.

@@ -77,9 +77,13 @@ __device__ __forceinline__ int dswz(int row, int chunk) {
 // GS8 (int8 only): one scale per (channel, K-group), brought through the
 // same LDS windows as the int4 scales (the zero half of each window holds a
 // second copy of the scales, unused) and applied while dequantizing.
-template <class Cfg, int ACT, int WBITS, int MODE = kDense, bool GS8 = false>
+// SPLIT: a dense split-K launch (TileProblem::part, kseg); `slice` is this
+// workgroup's K slice.  With scale windows kseg is a multiple of a window's
+// steps, so a slice starts on a window boundary.  Without SPLIT the kernel
+// runs all of K and the slice code is not compiled in.
+template <class Cfg, int ACT, int WBITS, int MODE = kDense, bool GS8 = false, bool SPLIT = false>
 __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, int tile_n,
-                                              const DmaLds &L) {
+                                              const DmaLds &L, int slice = 0) {
   constexpr int BK = Cfg::BK, TM = Cfg::TM, TN = Cfg::TN, NTHR = Cfg::NTHR;
   static_assert(MODE == kDense || WBITS == 4, "MoE experts are int4");
   static_assert(!GS8 || WBITS == 8, "group scales without zeros: int8");
@@ -88,7 +92,9 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
   const int K = p.K;
-  const int nsteps = K / BK;
+  static_assert(!SPLIT || MODE == kDense, "split-K: dense problems");
+  const int s0 = SPLIT ? slice * p.kseg : 0;                    // steps [s0, s1)
+  const int s1 = SPLIT ? min(K / BK, s0 + p.kseg) : K / BK;
   int row_lo, row_last;
   const uint8_t *Bb = p.B;
   const uint16_t *Sb = p.S, *Zb = GS8 ? p.S : p.Z;
@@ -322,16 +328,17 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
   // the direct loads ahead of the code loads, which the waits count on.
   Regs r0, r1;
   ScaleRegs sv;
+  const int w0 = s0 >> (3 + spg_lg);   // first scale window
 #pragma unroll
-  for (int t = 0; t < Cfg::SC_PARTS; ++t) sc_issue(t, 0);
-  sc_issue(0, 1);
-  a_issue(0, L.a[0]);
+  for (int t = 0; t < Cfg::SC_PARTS; ++t) sc_issue(t, w0);
+  sc_issue(0, w0 + 1);
+  a_issue(s0, L.a[0]);
   asm volatile("" ::: "memory");
-  b_issue(0, r0);
-  b_issue(min(1, nsteps - 1), r1);
+  b_issue(s0, r0);
+  b_issue(min(s0 + 1, s1 - 1), r1);
   __builtin_amdgcn_s_waitcnt(WAIT_ALL_BUT_2B);
   barrier();
-  sc_read(0, sv);
+  sc_read(s0, sv);
   b_store(L.b[0], r0, sv);
   __builtin_amdgcn_s_waitcnt(WAIT);
   barrier();
@@ -352,9 +359,9 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
     sc_read(step + 1, v);
     asm volatile("" ::: "memory");
     sc_issue((step + 1) % Cfg::SC_PARTS, ((step + 1) >> (3 + spg_lg)) + 1);
-    a_issue(min(step + 1, nsteps - 1), L.a[1 - I]);
+    a_issue(min(step + 1, s1 - 1), L.a[1 - I]);
     asm volatile("" ::: "memory");
-    b_issue(min(step + 2, nsteps - 1), nxt2);
+    b_issue(min(step + 2, s1 - 1), nxt2);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (NA > 0) {
       Frags f0, f1;
@@ -389,12 +396,12 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
   using I1 = std::integral_constant<int, 1>;
 
   auto main_loop = [&](auto NAc) {
-    int step = 0;
-    for (; step + 2 <= nsteps; step += 2) {
+    int step = s0;
+    for (; step + 2 <= s1; step += 2) {
       body(NAc, I0{}, step, r1, r0);
       body(NAc, I1{}, step + 1, r0, r1);
     }
-    if (step < nsteps) body(NAc, I0{}, step, r1, r0);
+    if (step < s1) body(NAc, I0{}, step, r1, r0);
   };
   if constexpr (MODE == kDense) {
     main_loop(std::integral_constant<int, TM>{});
@@ -420,6 +427,25 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
   // output is not read again by this kernel; measured 1-3 % faster).  Four waves share
   // one stage (A or W, whichever is large enough); all stages are free: the
   // last step ended with a barrier after every wave's last read.
+  if constexpr (SPLIT) {
+    {   // split-K slice: the raw fp32 partial sums, 4 columns per store
+      float *dst = p.part + static_cast<size_t>(slice) * p.M * p.N;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int r = row_lo + wm * Cfg::WTM + 32 * i + (lane & 31);
+        if (r > row_last) continue;
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int col = n0 + wn * Cfg::WTN + 32 * j + 8 * q + 4 * khalf;
+            *reinterpret_cast<f32x4 *>(dst + static_cast<size_t>(r) * p.N + col) =
+                f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          }
+      }
+      return;
+    }
+  }
   static_assert(Cfg::WTN == 64 && Cfg::NTHR == 512, "epilogue staging assumes 8 waves, 64 columns each");
   constexpr bool kStageInA = Cfg::STAGE_A >= 4 * 32 * 144;
   static_assert(kStageInA || Cfg::STAGE_B >= 4 * 32 * 144, "no LDS stage holds four 32 x 64 blocks");

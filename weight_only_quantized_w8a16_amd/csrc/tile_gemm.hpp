@@ -50,6 +50,11 @@ struct TileProblem {
   size_t s_expert_stride;    // scale/zero elements per expert
   int w_rows;                // rows of one expert's weight matrix
   int a_rows;                // rows of A (fc1: tokens; else M)
+  // Dense split-K: K slices of kseg 64-k steps; a slice writes its fp32
+  // partial tile to part + slice * M * N (no scale, bias or rounding) for a
+  // separate reduction.  part == nullptr: one slice, finished output.
+  float *part;
+  int kseg;
 };
 
 template <int BM_, int BN_, int WM_, int WN_>
@@ -118,13 +123,16 @@ __device__ __forceinline__ u32x4 dequant_run_w8(uint32_t lo, uint32_t hi, float 
 // multiply the finished sum.
 template <class Cfg, int ACT, int WBITS, int MODE, bool GS8 = false>
 __device__ __forceinline__ void tile_gemm(const TileProblem &p, int tile_m, int tile_n,
-                                          char *lds) {
+                                          char *lds, int slice = 0) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, NTHR = Cfg::NTHR;
   constexpr int TM = Cfg::TM, TN = Cfg::TN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
   const int K = p.K;
-  const int nsteps = K / BK;
+  // This workgroup's 64-k steps: [s0, s1) (all of K unless split).
+  const int s0 = p.part ? slice * p.kseg : 0;
+  const int s1 = p.part ? min(K / BK, s0 + p.kseg) : K / BK;
+  const int nsteps = s1 - s0;
 
   // ---- row sources for A -------------------------------------------------
   int row_lo, row_hi;         // valid global row range of this tile
@@ -305,8 +313,8 @@ __device__ __forceinline__ void tile_gemm(const TileProblem &p, int tile_m, int 
   // Scheduling barriers keep that order: the compiler would otherwise hoist
   // the LDS stores (and the waits on their loads) above the matrix-core work
   // and sink the new loads below it.
-  auto body = [&](int step, Regs &nxt1, Regs &nxt2) {
-    gload(min(step + 2, nsteps - 1), nxt2);
+  auto body = [&](int step, Regs &nxt1, Regs &nxt2) {   // step relative to s0
+    gload(s0 + min(step + 2, nsteps - 1), nxt2);
     __builtin_amdgcn_sched_barrier(0);
     compute(step & 1);
     __builtin_amdgcn_sched_barrier(0);
@@ -316,8 +324,8 @@ __device__ __forceinline__ void tile_gemm(const TileProblem &p, int tile_m, int 
   };
 
   Regs r0, r1;
-  gload(0, r0);
-  gload(min(1, nsteps - 1), r1);
+  gload(s0, r0);
+  gload(s0 + min(1, nsteps - 1), r1);
   lstore(0, r0);
   __syncthreads();
   // Unrolled by two so the register sets are named statically: at an even
@@ -334,6 +342,23 @@ __device__ __forceinline__ void tile_gemm(const TileProblem &p, int tile_m, int 
   // 32x32 accumulator: value v of lane -> row 8*(v/4) + 4*(lane/32) + v%4,
   // column lane % 32.
   const int col_in = lane & 31;
+  if constexpr (MODE == kDense) {
+    if (p.part) {   // split-K slice: the raw fp32 partial sums
+      float *dst = p.part + static_cast<size_t>(slice) * p.M * p.N;
+#pragma unroll
+      for (int jn = 0; jn < TN; ++jn) {
+        const int col = n0 + wn * Cfg::WTN + 32 * jn + col_in;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int r = row_lo + wm * Cfg::WTM + 32 * i + 8 * (v >> 2) + 4 * khalf + (v & 3);
+            if (r < row_hi) dst[static_cast<size_t>(r) * p.N + col] = acc[i][jn][v];
+          }
+      }
+      return;
+    }
+  }
   if constexpr (MODE == kMoeFc1) {
     constexpr int HALF = TN / 2;
 #pragma unroll
