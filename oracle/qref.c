@@ -203,16 +203,22 @@ void qref_quantize4(const float *w, int64_t n, int64_t k, int64_t group, uint8_t
 
 /* int4, groupwise: w = (q - 8) * scale[n, k/g] + zero[n, k/g]   [cpuint4]
  * docstring; groups along K [acext] 1.3.3.  Evaluated in fp32 as
- * CPUInt4EmbeddingMethod.embedding does: the product is exact, the add rounds. */
+ * CPUInt4EmbeddingMethod.embedding does: the product is exact, the add rounds.
+ * group -1 (or >= k): one scale and zero per output channel (the per-column
+ * mode of [acext] 1.3.2, which passes k as the group size).  zero == NULL:
+ * scale-only, w = (q - 8) * scale, i.e. a zero of 0 ([acext] 1.3.2 runs
+ * int4 with scales and no zero points; the unsigned code q stands for the
+ * signed value q - 8). */
 static void dequant4_row(const uint8_t *packed, const uint16_t *scale, const uint16_t *zero,
                          int64_t row, int64_t k, int64_t group, int dtype, float *w)
 {
-    int64_t ngroups = k / group;
+    int64_t ngroups = (group <= 0 || group >= k) ? 1 : k / group;
+    int64_t gsz = (ngroups == 1) ? k : group;
     for (int64_t c = 0; c < k; ++c) {
         uint8_t byte = packed[row * (k / 2) + c / 2];
         int q = (c % 2 == 0) ? (byte & 0xF) : (byte >> 4);
-        float s = act_to_f32(scale[row * ngroups + c / group], dtype);
-        float z = act_to_f32(zero[row * ngroups + c / group], dtype);
+        float s = act_to_f32(scale[row * ngroups + c / gsz], dtype);
+        float z = zero ? act_to_f32(zero[row * ngroups + c / gsz], dtype) : 0.0f;
         float prod = (float)(q - 8) * s;
         w[c] = prod + z;
     }

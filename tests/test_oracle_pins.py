@@ -221,6 +221,40 @@ def test_group_indexing_closed_form():
     assert np.array_equal(C[0], expect)
 
 
+@pytest.mark.parametrize("group", [-1, 1024])
+def test_per_column_closed_form(group):
+    # One scale and zero per channel (group -1, or k itself): with a constant
+    # code c and A = 1, C[n] = k * ((c - 8) * s[n] + z[n]), exact in double.
+    rng = np.random.default_rng(15)
+    n, k, c = 6, 1024, 3
+    s = (rng.integers(1, 64, (n,)) / 64.0).astype(np.float32)
+    z = (rng.integers(-32, 33, (n,)) / 64.0).astype(np.float32)
+    packed = oracle.pack4(np.full((n, k), c))
+    C = oracle.gemm_w4(bf16_bits(np.ones((1, k))), packed, bf16_bits(s), bf16_bits(z), group)
+    assert np.array_equal(C[0], k * ((c - 8) * s.astype(np.float64) + z))
+    W = oracle.dequant4(packed, bf16_bits(s), bf16_bits(z), group)
+    assert np.array_equal(W, np.repeat(((c - 8) * s + z)[:, None], k, axis=1).astype(np.float32))
+
+
+def test_scale_only_closed_forms():
+    # No zero points: w = (q - 8) * s.  Scale 1 turns every code into q - 8;
+    # a constant code c with A = 1 sums to sum_g g * (c - 8) * s[n, g].
+    q = np.random.default_rng(16).integers(0, 16, (8, 256))
+    W = oracle.dequant4(oracle.pack4(q), bf16_bits(np.ones((8, 4))), None, 64)
+    assert (W == q - 8).all()
+    rng = np.random.default_rng(17)
+    n, k, g, c = 5, 512, 128, 13
+    s = (rng.integers(1, 64, (n, k // g)) / 64.0).astype(np.float32)
+    C = oracle.gemm_w4(bf16_bits(np.ones((1, k))), oracle.pack4(np.full((n, k), c)), bf16_bits(s),
+                       None, g)
+    assert np.array_equal(C[0], (g * (c - 8) * s.astype(np.float64)).sum(axis=1))
+    # per-column and scale-only together
+    s1 = (rng.integers(1, 64, (n,)) / 64.0).astype(np.float32)
+    C1 = oracle.gemm_w4(bf16_bits(np.ones((1, k))), oracle.pack4(np.full((n, k), c)), bf16_bits(s1),
+                        None, -1)
+    assert np.array_equal(C1[0], k * (c - 8) * s1.astype(np.float64))
+
+
 def test_dequant_rounds_once_in_fp32():
     # (q - 8) * s is exact in fp32; only the add of the zero rounds, to nearest even.
     rng = np.random.default_rng(6)
