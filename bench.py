@@ -12,6 +12,10 @@ Secondary sections on the same JSON line:
            fp16 bias: TFLOP/s against the dense bf16 matrix-core peak;
   moe      grouped W4A16 MoE, 2048 tokens, hidden 2048, inter 1408,
            64 experts, top-6;
+  w8       W8A16 at K=3584, N in {3584, 18944}, M from 1 to 4096, per-channel
+           and group-128 scales;
+  w4_forms W4A16 N=13312, K=2048 at M in {1, 512} for each scale form
+           (groupwise with zeros, scale-only, per channel);
   quantize the load-side groupwise int4 quantizer on bf16 weights
            [N, 2048], N in {13312, 131072}, group 64 (GB/s against HBM);
   roofline the decode kernel of the N=131072 GEMV: algorithmic bytes per
@@ -342,6 +346,88 @@ def run(args):
         del w1, w2, ws
         torch.cuda.empty_cache()
 
+    # ---- W8A16 (int8 weights, fp16 activations), K = 3584 ----------------------------
+    w8 = None
+    if not args.no_w8:
+        k8 = 3584
+        w8shapes = {}
+        for group in (-1, 128):
+            for n in (3584, 18944):
+                codes, sc, _ = si.w8_weights(n, k8, group, si.seed_of("cfg2", "w", n, k8, group))
+                base = qg.repack_w8(torch.from_numpy(codes).to(dev))
+                S = torch.from_numpy(sc.view("int16")).view(torch.float16).to(dev)
+                wb = n * k8 + 2 * S.numel()
+                copies = copies_for(wb)
+                sets = [(base, S)] + [(base.clone(), S.clone()) for _ in range(copies - 1)]
+                ms_list = (1, 16, 128, 1024, 4096) if group == -1 else (1, 16, 1024)
+                for m in ms_list:
+                    A = torch.from_numpy(si.activations(m, k8, si.seed_of("cfg2", "a", m, k8),
+                                                        si.FP16).view("int16")).view(torch.float16).to(dev)
+                    C = torch.empty((m, n), dtype=torch.float16, device=dev)
+                    reps = max(10, K // 5)
+
+                    def call(i, A=A, C=C, sets=sets, group=group):
+                        B, S_ = sets[i % len(sets)]
+                        qg.gemm_w8a16(A, B, S_, None, group, out=C)
+                    for i in range(3):
+                        call(i)
+                    ms = timed(call, reps, warm=reps) / reps
+                    b = wb + 2 * m * k8 + 2 * m * n
+                    flop = 2.0 * m * n * k8
+                    w8shapes[f"g{group}_M{m}_N{n}"] = {
+                        "us": round(ms * 1e3, 2), "GBps": round(b / (ms * 1e-3) / 1e9, 1),
+                        "TFLOPS": round(flop / (ms * 1e-3) / 1e12, 1),
+                        "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 3),
+                        "frac_mfma": round(flop / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 3)}
+                    del A, C
+                del sets, base
+                torch.cuda.empty_cache()
+        w8 = {"config": "W8A16, K=3584, N in {3584, 18944}, fp16 A/C, int8 codes; per-channel "
+                        "scales (g-1) and group-128 scales (g128); GB/s against 8 TB/s for "
+                        "small M, TFLOP/s against the 2.5 PFLOP/s fp16 peak for large M",
+              "shapes": w8shapes}
+        log(f"w8: {w8}")
+
+    # ---- int4 scale forms: groupwise with zeros, scale-only, per channel ----------
+    forms = None
+    if not args.no_w8:
+        fk, fn = 2048, 13312
+        fshapes = {}
+        for label, group, zeros in (("g64_zeros", 64, True), ("g64_scale_only", 64, False),
+                                    ("per_channel_zeros", -1, True),
+                                    ("per_channel_scale_only", -1, False)):
+            packed, sc, ze, _ = si.w4_weights(fn, fk, group, si.seed_of("forms", "w", fn, fk, group))
+            base = qg.repack_w4(torch.from_numpy(packed).to(dev))
+            S = torch.from_numpy(sc.view("int16")).view(torch.bfloat16).to(dev)
+            Z = torch.from_numpy(ze.view("int16")).view(torch.bfloat16).to(dev) if zeros else None
+            wb = fn * fk // 2 + 2 * S.numel() * (2 if zeros else 1)
+            copies = copies_for(wb)
+            sets = [(base, S, Z)] + [(base.clone(), S.clone(), None if Z is None else Z.clone())
+                                     for _ in range(copies - 1)]
+            for m in (1, 512):
+                A = torch.from_numpy(si.activations(m, fk, si.seed_of("forms", "a", m, fk))
+                                     .view("int16")).view(torch.bfloat16).to(dev)
+                C = torch.empty((m, fn), dtype=torch.bfloat16, device=dev)
+                reps = max(10, K // 5)
+
+                def call(i, A=A, C=C, sets=sets, group=group):
+                    B, S_, Z_ = sets[i % len(sets)]
+                    qg.gemm_w4a16(A, B, S_, Z_, None, group, out=C)
+                for i in range(3):
+                    call(i)
+                ms = timed(call, reps, warm=reps) / reps
+                b = wb + 2 * m * fk + 2 * m * fn
+                fshapes[f"{label}_M{m}"] = {"us": round(ms * 1e3, 2),
+                                            "GBps": round(b / (ms * 1e-3) / 1e9, 1),
+                                            "TFLOPS": round(2.0 * m * fn * fk / (ms * 1e-3) / 1e12, 1)}
+                del A, C
+            del sets, base
+        forms = {"config": "W4A16 N=13312 K=2048 bf16, M in {1, 512}: groupwise g64 with zeros / "
+                           "scale-only, per-channel with zeros / scale-only",
+                 "shapes": fshapes}
+        log(f"w4 forms: {forms}")
+        torch.cuda.empty_cache()
+
     # ---- load-side quantizer ------------------------------------------------------
     quant = None
     if not args.no_quant:
@@ -437,6 +523,8 @@ def run(args):
         "sweep": sweep,
         "prefill": prefill,
         "moe": moe,
+        "w8": w8,
+        "w4_forms": forms,
         "quantize": quant,
         "ceiling": ceil,
     }
@@ -453,6 +541,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-moe", action="store_true")
     ap.add_argument("--no-quant", action="store_true")
+    ap.add_argument("--no-w8", action="store_true")
     ap.add_argument("--quick", action="store_true", help="skip the M sweep and the copy ceiling")
     ap.add_argument("--kernel-only", action="store_true",
                     help="run only the N=131072 GEMV (--steps times) and a calibration copy; "

@@ -6,6 +6,8 @@
  * from integer codes:
  *
  *   int4, groupwise:  W[n, k] = (q[n, k] - 8) * scale[n, k/g] + zero[n, k/g]
+ *         (per channel with g = k; scale-only when there are no zeros:
+ *         zero = 0, the scale-only forms of acext 1.3.2)
  *   int8, per channel: W[n, k] = q[n, k] * scale[n]
  *   int8, groupwise:   W[n, k] = q[n, k] * scale[n, k/g]   (no zero)
  *
@@ -144,9 +146,10 @@ qg_status qquantize_w4(const void *W, uint8_t *packed, void *scales, void *zeros
  * value is (q - 8) * s + z (int4; the product is exact, the add rounds to
  * nearest even) or q * s (int8, exact); the 16-bit output is that fp32 value
  * rounded to nearest even.  Bit-exact by contract.
- *   group_size: int4 64 or 128; int8 -1 (per channel), 64 or 128.
- *   scales/zeros: [n, k/group] (int4; int8 groupwise) or [n] (int8 per
- *   channel), act_dtype.
+ *   group_size: int4 64, 128 or -1 (= k, per channel); int8 -1 (per
+ *   channel), 64 or 128.
+ *   scales/zeros: [n, k/group] (groupwise) or [n] (per channel), act_dtype;
+ *   zeros NULL (int4): scale-only, a zero of 0.
  * ---------------------------------------------------------------------- */
 qg_status qdequant_w4(const uint8_t *B_tiled, const void *scales, const void *zeros, void *W_out,
                       int n, int k, int group_size, qg_dtype act_dtype, qg_dtype out_dtype,
@@ -160,10 +163,14 @@ qg_status qdequant_w8(const int8_t *B_tiled, const void *scales, void *W_out, in
  *   B_tiled device, the tiled layout above (qrepack_w4 / qrepack_w8 output)
  *   scales  device [n, k/group] (w4; w8 with group 64/128) or [n] (w8,
  *           group -1), act_dtype
- *   zeros   device [n, k/group], act_dtype (w4 only; required)
+ *   zeros   device [n, k/group], act_dtype (w4 only); NULL for scale-only
+ *           int4 weights, w = (q - 8) * scale (acext 1.3.2 runs int4 with
+ *           scales and no zero points)
  *   bias    device [n] in bias_dtype, or NULL with bias_dtype QG_NONE
  *   C       device [m, n], act_dtype; written, never read
- *   group_size: w4 64 or 128; w8 -1 (k is accepted as a synonym of -1),
+ *   group_size: w4 64, 128, or -1 (one scale (and zero) per channel, [n];
+ *           acext 1.3.2's per-column int4; k is accepted as a synonym);
+ *           w8 -1 (k is accepted as a synonym of -1),
  *           64 or 128 (one scale per K-group; k % group_size == 0).  With
  *           groups the GEMMs stage q * s rounded to the activation dtype
  *           for the matrix cores (decode scales each block's fp32 partial

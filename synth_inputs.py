@@ -87,8 +87,9 @@ def w4_weights(n, k, group, seed, dtype=BF16, scale_range=(0.005, 0.02), zero_st
                bias_dtype=NONE, bias_std=0.02):
     g = _gen(seed)
     packed = torch.randint(0, 256, (n, k // 2), generator=g, dtype=torch.uint8).numpy()
-    scale = _bits(_uniform(g, (n, k // group), *scale_range), dtype)
-    zero = _bits(_normal(g, (n, k // group), zero_std), dtype)
+    sshape = (n,) if group in (-1, k) else (n, k // group)   # -1: one per channel
+    scale = _bits(_uniform(g, sshape, *scale_range), dtype)
+    zero = _bits(_normal(g, sshape, zero_std), dtype)
     bias = _bits(_normal(g, (n,), bias_std), bias_dtype) if bias_dtype != NONE else None
     return packed, scale, zero, bias
 
@@ -127,12 +128,18 @@ def w8_problem(m, n, k, group=-1, tag="w8", dtype=FP16, bias_dtype=NONE, **kw) -
 # [-1, 1], bias multiples of 1/4: every partial sum is a multiple of 2^-2 well
 # below 2^24 in magnitude, so any fp32 summation order gives the exact value.
 
-def w4_exact_problem(m, n, k, group, seed, dtype=BF16, bias_dtype=NONE) -> W4Problem:
+def w4_exact_problem(m, n, k, group, seed, dtype=BF16, bias_dtype=NONE,
+                     zeros=True) -> W4Problem:
+    """group -1: one scale (and zero) per channel; zeros=False: no zeros
+    (scale-only weights), `zero` is None."""
     g = _gen(seed)
     packed = torch.randint(0, 256, (n, k // 2), generator=g, dtype=torch.uint8).numpy()
-    sexp = torch.randint(0, 3, (n, k // group), generator=g)
+    sshape = (n,) if group in (-1, k) else (n, k // group)
+    sexp = torch.randint(0, 3, sshape, generator=g)
     scale = _bits(torch.pow(2.0, -sexp.float()), dtype)
-    zero = _bits(torch.randint(-4, 5, (n, k // group), generator=g).float() / 4.0, dtype)
+    zero = _bits(torch.randint(-4, 5, sshape, generator=g).float() / 4.0, dtype)
+    if not zeros:
+        zero = None
     bias = None
     if bias_dtype != NONE:
         bias = _bits(torch.randint(-8, 9, (n,), generator=g).float() / 4.0, bias_dtype)

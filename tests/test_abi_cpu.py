@@ -60,11 +60,13 @@ def w8(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(m=-1), SHAPE), (dict(n=-16), SHAPE), (dict(k=0), SHAPE),
-    (dict(A=None), NULL), (dict(B=None), NULL), (dict(s=None), NULL), (dict(z=None), NULL),
+    (dict(A=None), NULL), (dict(B=None), NULL), (dict(s=None), NULL),
     (dict(C=None), NULL), (dict(bdt=FP16), NULL),
+    (dict(z=None, n=24), UNSUP),      # zeros are optional (scale-only int4)
     (dict(act=0), DTYPE), (dict(act=FP32), DTYPE), (dict(act=7), DTYPE),
     (dict(bias=FAKE, bdt=0), DTYPE), (dict(bias=FAKE, bdt=FP32), DTYPE),
-    (dict(g=32), GROUP), (dict(g=-1), GROUP), (dict(g=256), GROUP), (dict(k=192, g=128), GROUP),
+    (dict(g=32), GROUP), (dict(g=-2), GROUP), (dict(g=512), GROUP), (dict(k=192, g=128), GROUP),
+    (dict(g=-1, n=24), UNSUP), (dict(g=256, n=24), UNSUP),   # per channel: -1 or k
     (dict(n=24), UNSUP), (dict(k=192), UNSUP),
     (dict(A=FAKE + 8), ALIGN), (dict(B=FAKE + 4), ALIGN), (dict(C=FAKE + 2), ALIGN),
     (dict(s=FAKE + 1), ALIGN), (dict(z=FAKE + 1), ALIGN), (dict(bias=FAKE + 1, bdt=FP16), ALIGN),
@@ -109,7 +111,9 @@ def test_repack_and_dequant_validation():
         assert f(FAKE, FAKE, 16, 64 * 65536, None) == UNSUP
     assert L.qdequant_w4(FAKE, FAKE, FAKE, FAKE, 16, 128, 32, BF16, FP32, None) == GROUP
     assert L.qdequant_w4(FAKE, FAKE, FAKE, FAKE, 16, 128, 64, BF16, FP16, None) == DTYPE
-    assert L.qdequant_w4(FAKE, FAKE, None, FAKE, 16, 128, 64, BF16, FP32, None) == NULL
+    assert L.qdequant_w4(FAKE, None, FAKE, FAKE, 16, 128, 64, BF16, FP32, None) == NULL
+    assert L.qdequant_w4(FAKE, FAKE, None, FAKE, 24, 128, 64, BF16, FP32, None) == UNSUP   # no zeros: ok
+    assert L.qdequant_w4(FAKE, FAKE, FAKE, FAKE, 24, 128, -1, BF16, FP32, None) == UNSUP   # per channel
     assert L.qdequant_w8(FAKE, FAKE, FAKE, 16, 128, 32, FP16, FP32, None) == GROUP
     assert L.qdequant_w8(FAKE, FAKE, FAKE, 16, 192, 128, FP16, FP32, None) == GROUP
     assert L.qdequant_w8(FAKE, FAKE, FAKE, 16, 128, -1, FP16, BF16, None) == DTYPE

@@ -108,7 +108,8 @@ def test_dequant_w8_grouped_bit_exact(dtype, group):
 def _run_w4(p, path=None):
     A = to_dev(p.A, p.dtype)
     tiled = qg.repack_w4(to_dev(p.packed))
-    S, Z = to_dev(p.scale, p.dtype), to_dev(p.zero, p.dtype)
+    S = to_dev(p.scale, p.dtype)
+    Z = to_dev(p.zero, p.dtype) if p.zero is not None else None
     bias = to_dev(p.bias, p.bias_dtype) if p.bias is not None else None
     if path:
         os.environ["QGEMM_FORCE_PATH"] = path
@@ -223,6 +224,66 @@ def test_w8_grouped_random_tolerance(m, group):
     ref = oracle.gemm_w8_at(p.A, p.codes, p.scale, rows, cols, group, FP16)
     err = np.abs(C[rows, cols] - ref).max() / np.abs(ref).max()
     assert err <= TOL[FP16], err
+
+
+# -- int4 scale forms: per channel (group -1) and scale-only (no zeros) ----------
+
+FORMS = [(-1, True), (-1, False), (64, False), (128, False)]
+
+
+@pytest.mark.parametrize("group,zeros", FORMS)
+@pytest.mark.parametrize("dtype", [BF16, FP16])
+def test_dequant_w4_scale_forms_bit_exact(group, zeros, dtype):
+    n, k = 48, 640
+    p = si.w4_exact_problem(1, n, k, group, seed=3, dtype=dtype, zeros=zeros)
+    ref = oracle.dequant4(p.packed, p.scale, p.zero, group, dtype)
+    tiled = qg.repack_w4(to_dev(p.packed))
+    S = to_dev(p.scale, dtype)
+    Z = to_dev(p.zero, dtype) if zeros else None
+    W32 = qg.dequant_w4(tiled, S, Z, group, torch.float32).cpu().numpy()
+    assert np.array_equal(W32.view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 16, 128), (5, 256, 2048), (33, 128, 256), (300, 512, 640),
+                                   (16, 3584, 3584), (1, 65536, 256)])
+@pytest.mark.parametrize("group,zeros", FORMS)
+@pytest.mark.parametrize("path", ["decode", "prefill"])
+def test_w4_scale_forms_integer_exact(m, n, k, group, zeros, path):
+    if path == "prefill" and n > 8192:
+        pytest.skip("a decode-sized problem")
+    p = si.w4_exact_problem(m, n, k, group, seed=m + n + k, dtype=BF16, bias_dtype=FP16, zeros=zeros)
+    Cref = oracle.gemm_w4(p.A, p.packed, p.scale, p.zero, group, BF16, p.bias, FP16)
+    got = to_bits(_run_w4(p, path))
+    exp = _exact_expected(Cref, BF16)
+    bad = np.argwhere(got != exp)
+    assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:4].tolist()}"
+
+
+@pytest.mark.parametrize("tile", ["D8", "D8N", "D64", "D128", "X", "L", "M", "S"])
+@pytest.mark.parametrize("group,zeros", FORMS)
+def test_prefill_tiles_w4_scale_forms_exact(tile, group, zeros, monkeypatch):
+    # scale-only groups keep the direct-load tiles (their zero windows read an
+    # empty buffer, i.e. zeros); per-channel scales fall back to the generic tile
+    p = si.w4_exact_problem(300, 512, 1024, group, seed=29, dtype=FP16, bias_dtype=FP16, zeros=zeros)
+    Cref = oracle.gemm_w4(p.A, p.packed, p.scale, p.zero, group, FP16, p.bias, FP16)
+    monkeypatch.setenv("QGEMM_PREFILL_TILE", tile)
+    got = to_bits(_run_w4(p, "prefill"))
+    assert np.array_equal(got, _exact_expected(Cref, FP16))
+
+
+@pytest.mark.parametrize("group,zeros", FORMS)
+def test_w4_scale_forms_random_tolerance(group, zeros):
+    # random bf16 data on the decode and prefill paths, sampled outputs
+    for m in (1, 256):
+        p = si.w4_problem(m, 2048, 2048, group, tag="forms")
+        if not zeros:
+            p.zero = None
+        C = _run_w4(p).float().cpu().numpy()
+        rng = np.random.default_rng(m)
+        rows, cols = rng.integers(0, m, 64), rng.integers(0, 2048, 64)
+        ref = oracle.gemm_w4_at(p.A, p.packed, p.scale, p.zero, group, rows, cols, BF16)
+        err = np.abs(C[rows, cols] - ref).max() / np.abs(ref).max()
+        assert err <= TOL[BF16], (m, err)
 
 
 # -- the tiny W4A16 problem (M=4, K=256, N=128, g=64), full oracle ----------------

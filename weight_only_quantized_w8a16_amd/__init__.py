@@ -133,10 +133,12 @@ def quantize_w4(W: torch.Tensor, group_size: int = 64, sz_dtype: Optional[torch.
 
 # -- dequant hook ------------------------------------------------------------
 
-def dequant_w4(tiled: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor, group_size: int,
-               out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+def dequant_w4(tiled: torch.Tensor, scales: torch.Tensor, zeros: Optional[torch.Tensor],
+               group_size: int, out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """Tiled int4 -> W [n, k]; zeros None = scale-only, group_size -1 = per channel."""
     for t, nm in ((tiled, "tiled"), (scales, "scales"), (zeros, "zeros")):
-        _dev(t, nm)
+        if t is not None:
+            _dev(t, nm)
     n, half = tiled.shape
     out = torch.empty((n, 2 * half), dtype=out_dtype, device=tiled.device)
     check("qdequant_w4", lib().qdequant_w4(_ptr(tiled), _ptr(scales), _ptr(zeros), _ptr(out), n,
@@ -176,14 +178,19 @@ def _workspace(m: int, n: int, k: int, group_size: int, bits: int, device,
     return torch.empty(need, dtype=torch.uint8, device=device), need
 
 
-def gemm_w4a16(A: torch.Tensor, B_tiled: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
-               bias: Optional[torch.Tensor] = None, group_size: int = 64,
-               out: Optional[torch.Tensor] = None,
+def gemm_w4a16(A: torch.Tensor, B_tiled: torch.Tensor, scales: torch.Tensor,
+               zeros: Optional[torch.Tensor], bias: Optional[torch.Tensor] = None,
+               group_size: int = 64, out: Optional[torch.Tensor] = None,
                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """C = A . dequant(B)^T (+ bias); A [..., k] bf16/fp16, B tiled int4."""
+    """C = A . dequant(B)^T (+ bias); A [..., k] bf16/fp16, B tiled int4.
+
+    group_size 64 / 128 (scales [n, k/g]) or -1 (one per channel, [n]);
+    zeros None for scale-only weights, w = (q - 8) * s.
+    """
     _dev(A, "A")
     for t, nm in ((B_tiled, "B_tiled"), (scales, "scales"), (zeros, "zeros")):
-        _dev(t, nm)
+        if t is not None:
+            _dev(t, nm)
     if bias is not None:
         _dev(bias, "bias")
     lead = A.shape[:-1]

@@ -54,13 +54,13 @@ qg_status gemm_checks(const void *A, const void *B, const void *scales, const vo
                       qg_dtype act, qg_dtype bias_dt, int wbits) {
   if (m < 0 || n < 0 || k <= 0) return QG_ERR_SHAPE;
   if (m == 0 || n == 0) return QG_OK;   // nothing to compute; pointers unused
-  if (!A || !B || !scales || !C || (wbits == 4 && !zeros)) return QG_ERR_NULL;
+  if (!A || !B || !scales || !C) return QG_ERR_NULL;   // zeros are optional (int4)
   if (bias_dt != QG_NONE && !bias) return QG_ERR_NULL;
   if (!act_ok(act)) return QG_ERR_DTYPE;
   if (bias_dt == QG_NONE ? bias != nullptr : !act_ok(bias_dt)) return QG_ERR_DTYPE;
   if (wbits == 4) {
-    if (group != 64 && group != 128) return QG_ERR_GROUP;
-    if (k % group != 0) return QG_ERR_GROUP;
+    if (group != 64 && group != 128 && group != -1 && group != k) return QG_ERR_GROUP;
+    if (group > 0 && k % group != 0) return QG_ERR_GROUP;
     if (n % 16 != 0 || k % 128 != 0) return QG_ERR_UNSUPPORTED;
   } else {
     if (group != -1 && group != k && group != 64 && group != 128) return QG_ERR_GROUP;
@@ -167,16 +167,16 @@ qg_status qdequant_w4(const uint8_t *B, const void *scales, const void *zeros, v
                       int k, int group, qg_dtype act, qg_dtype out, void *stream) {
   if (n < 0 || k < 0) return QG_ERR_SHAPE;
   if (n == 0 || k == 0) return QG_OK;
-  if (!B || !scales || !zeros || !W) return QG_ERR_NULL;
+  if (!B || !scales || !W) return QG_ERR_NULL;   // zeros optional
   if (!act_ok(act) || !(out == QG_FP32 || out == act)) return QG_ERR_DTYPE;
-  if (group != 64 && group != 128) return QG_ERR_GROUP;
-  if (k % group != 0) return QG_ERR_GROUP;
+  if (group != 64 && group != 128 && group != -1 && group != k) return QG_ERR_GROUP;
+  if (group > 0 && k % group != 0) return QG_ERR_GROUP;
   if (n % 16 != 0 || k % 128 != 0) return QG_ERR_UNSUPPORTED;
-  if (!aligned(B, 16) || !aligned(W, 16) || !aligned(scales, 2) || !aligned(zeros, 2))
+  if (!aligned(B, 16) || !aligned(W, 16) || !aligned(scales, 2) || (zeros && !aligned(zeros, 2)))
     return QG_ERR_ALIGN;
   return hip_status(qg::launch_dequant_w4(B, static_cast<const uint16_t *>(scales),
-                                          static_cast<const uint16_t *>(zeros), W, n, k, group,
-                                          act, out, as_stream(stream)));
+                                          static_cast<const uint16_t *>(zeros), W, n, k,
+                                          group == -1 ? k : group, act, out, as_stream(stream)));
 }
 
 qg_status qdequant_w8(const int8_t *B, const void *scales, void *W, int n, int k, int group,
@@ -214,7 +214,7 @@ size_t qgemm_workspace_size(int m, int n, int k, int group_size, int weight_bits
   a.M = m;
   a.N = n;
   a.K = k;
-  if (weight_bits == 4) a.group = group_size;
+  if (weight_bits == 4) a.group = group_size == -1 ? k : group_size;
   else a.group = (group_size == -1 || group_size == k) ? 0 : group_size;
   if (a.group < 0 || (a.group > 0 && k % a.group != 0)) return 0;
   const size_t b = qg::prefill_workspace_bytes(a, weight_bits);
@@ -229,8 +229,9 @@ qg_status qgemm_w4a16(const void *A, const uint8_t *B, const void *scales, const
   if (workspace && ws_bytes && !aligned(workspace, 256)) return QG_ERR_ALIGN;
   qg::GemmArgs a{static_cast<const uint16_t *>(A), B, static_cast<const uint16_t *>(scales),
                  static_cast<const uint16_t *>(zeros), static_cast<const uint16_t *>(bias),
-                 static_cast<uint16_t *>(C), m, n, k, group, static_cast<int>(act),
-                 static_cast<int>(bias_dt), workspace, workspace ? ws_bytes : 0};
+                 static_cast<uint16_t *>(C), m, n, k, group == -1 ? k : group,
+                 static_cast<int>(act), static_cast<int>(bias_dt), workspace,
+                 workspace ? ws_bytes : 0};
   hipStream_t s = as_stream(stream);
   if (uses_prefill(m, n)) return hip_status(qg::launch_prefill_w4(a, s));
   return hip_status(by_row_slabs(a, qg::launch_decode_w4, s));

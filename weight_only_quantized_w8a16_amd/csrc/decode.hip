@@ -90,6 +90,16 @@ __device__ __forceinline__ Groups<NG> load_groups(const uint16_t *__restrict__ p
   return g;
 }
 
+// One 16-bit value in every group slot.
+template <int NG>
+__device__ __forceinline__ Groups<NG> splat_groups(uint16_t v) {
+  Groups<NG> g;
+  const uint32_t w = static_cast<uint32_t>(v) | (static_cast<uint32_t>(v) << 16);
+#pragma unroll
+  for (int i = 0; i < Groups<NG>::W; ++i) g.w[i] = w;
+  return g;
+}
+
 template <int ACT, int NG>
 __device__ __forceinline__ float group_value(const Groups<NG> &g, int i) {
   const uint32_t w = g.w[i >> 1];
@@ -103,13 +113,19 @@ __device__ __forceinline__ float group_value(const Groups<NG> &g, int i) {
 template <int BPW>
 constexpr int decode_threads() { return BPW == 1 ? 1024 : (BPW == 2 ? 512 : 256); }
 
-template <int ACT, int G, int BPW, int NT, bool VEC>
+// SPECIAL: the scale forms other than groupwise-with-zeros, decided at run
+// time -- one scale (and zero) per channel when group != G (group = K, run
+// with G = 128: every 128-k block then reads the channel's values), and no
+// zeros when Z is null (w = (q - 8) s).  The common form compiles without
+// these branches.
+template <int ACT, int G, int BPW, int NT, bool VEC, bool SPECIAL>
 __global__ __launch_bounds__(decode_threads<BPW>()) void k_decode_w4(const uint16_t *__restrict__ A,
                                                    const u32x4 *__restrict__ Bt,
                                                    const uint16_t *__restrict__ S,
                                                    const uint16_t *__restrict__ Z,
                                                    const uint16_t *__restrict__ bias, int bias_dt,
-                                                   uint16_t *__restrict__ C, int M, int N, int K) {
+                                                   uint16_t *__restrict__ C, int M, int N, int K,
+                                                   int group) {
   extern __shared__ float red[];
   constexpr int GPB = 128 / G;        // groups per 128-k block
   constexpr int TPG = 4 / GPB;        // 32-k MFMA steps per group
@@ -155,8 +171,18 @@ __global__ __launch_bounds__(decode_threads<BPW>()) void k_decode_w4(const uint1
       for (int b = 0; b < BPW; ++b)
         bw[i][b] = __builtin_nontemporal_load(&Bt[(static_cast<size_t>(nt) * nb + kb0 + b) * 64 + lane]);
       const size_t srow = static_cast<size_t>(nt * 16 + nl) * ngroups + kb0 * GPB;
-      sv[i] = load_groups<NG, VEC>(S + srow);
-      zv[i] = load_groups<NG, VEC>(Z + srow);
+      if constexpr (SPECIAL) {
+        if (group != G) {
+          sv[i] = splat_groups<NG>(S[nt * 16 + nl]);
+          zv[i] = Z ? splat_groups<NG>(Z[nt * 16 + nl]) : Groups<NG>{};
+        } else {
+          sv[i] = load_groups<NG, VEC>(S + srow);
+          zv[i] = Z ? load_groups<NG, VEC>(Z + srow) : Groups<NG>{};
+        }
+      } else {
+        sv[i] = load_groups<NG, VEC>(S + srow);
+        zv[i] = load_groups<NG, VEC>(Z + srow);
+      }
     }
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
@@ -435,9 +461,12 @@ hipError_t launch_stream_m(const GemmArgs &a, hipStream_t s) {
 
 hipError_t launch_decode_w4(const GemmArgs &a, hipStream_t s) {
   const int nb = a.K >> 7, ntiles = a.N >> 4;
+  // Per-channel scales (group = K) or no zeros: the run-time forms of the
+  // split-K kernel (group 128 for per-channel).
+  const bool special = a.Z == nullptr || (a.group != 64 && a.group != 128);
   // Streaming kernel: one or two rows, many tiles, K a multiple of 512,
   // scale rows 16-byte aligned, activations that fit in LDS.
-  const bool aligned16 =
+  const bool aligned16 = !special &&
       ((reinterpret_cast<uintptr_t>(a.S) | reinterpret_cast<uintptr_t>(a.Z)) & 15) == 0 &&
       ((a.K / a.group) % 8) == 0;
   const bool fits = static_cast<size_t>(a.M) * (2 * static_cast<size_t>(a.K) + 16) +
@@ -453,17 +482,20 @@ hipError_t launch_decode_w4(const GemmArgs &a, hipStream_t s) {
   const u32x4 *B = static_cast<const u32x4 *>(a.B);
   // Vector scale loads need the scale/zero bases aligned to a chunk's worth
   // of groups (the row offsets are multiples of it by construction).
-  const int ng = p.bpw * (128 / a.group);
+  const int ng = p.bpw * (a.group == 64 ? 2 : 1);
   const uintptr_t amask = static_cast<uintptr_t>(2 * ng - 1);
   const bool vec = ((reinterpret_cast<uintptr_t>(a.S) | reinterpret_cast<uintptr_t>(a.Z)) & amask) == 0;
-#define QG_DEC4(ACT_, G_, BPW_, NT_)                                                            \
-  do {                                                                                          \
-    if (vec)                                                                                    \
-      hipLaunchKernelGGL((k_decode_w4<ACT_, G_, BPW_, NT_, true>), grid, block, lds, s, a.A, B, \
-                         a.S, a.Z, a.bias, a.bias_dt, a.C, a.M, a.N, a.K);                      \
-    else                                                                                        \
-      hipLaunchKernelGGL((k_decode_w4<ACT_, G_, BPW_, NT_, false>), grid, block, lds, s, a.A,   \
-                         B, a.S, a.Z, a.bias, a.bias_dt, a.C, a.M, a.N, a.K);                   \
+#define QG_DEC4(ACT_, G_, BPW_, NT_)                                                                 \
+  do {                                                                                               \
+    if (special)                                                                                     \
+      hipLaunchKernelGGL((k_decode_w4<ACT_, G_, BPW_, NT_, false, true>), grid, block, lds, s, a.A,  \
+                         B, a.S, a.Z, a.bias, a.bias_dt, a.C, a.M, a.N, a.K, a.group);              \
+    else if (vec)                                                                                    \
+      hipLaunchKernelGGL((k_decode_w4<ACT_, G_, BPW_, NT_, true, false>), grid, block, lds, s, a.A,  \
+                         B, a.S, a.Z, a.bias, a.bias_dt, a.C, a.M, a.N, a.K, a.group);              \
+    else                                                                                             \
+      hipLaunchKernelGGL((k_decode_w4<ACT_, G_, BPW_, NT_, false, false>), grid, block, lds, s, a.A, \
+                         B, a.S, a.Z, a.bias, a.bias_dt, a.C, a.M, a.N, a.K, a.group);              \
   } while (0)
 #define QG_DEC4_NT(ACT_, G_, BPW_)                   \
   if (p.nt == 2) QG_DEC4(ACT_, G_, BPW_, 2);         \

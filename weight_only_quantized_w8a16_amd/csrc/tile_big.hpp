@@ -133,8 +133,9 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
   const auto rB = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(Bb), 0, static_cast<int>(b_bytes), kRsrcFlags);
   [[maybe_unused]] const auto rS =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(Sb), 0, static_cast<int>(s_bytes), kRsrcFlags);
-  [[maybe_unused]] const auto rZ =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(Zb), 0, static_cast<int>(s_bytes), kRsrcFlags);
+  // No zeros (scale-only int4): an empty resource, whose loads return 0.
+  [[maybe_unused]] const auto rZ = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(Zb), 0, Zb ? static_cast<int>(s_bytes) : 0, kRsrcFlags);
 
   // ---- A: slot q = (wave * A_DMA + i) * 64 + lane of a stage is row q / 8,
   // placed chunk q % 8; it holds the row's chunk (q % 8) ^ ((row / 2) % 8).

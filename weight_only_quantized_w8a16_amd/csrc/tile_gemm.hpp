@@ -228,7 +228,7 @@ __device__ __forceinline__ void tile_gemm(const TileProblem &p, int tile_m, int 
         r.b[c] = *reinterpret_cast<const u32x2 *>(b_src[c] + static_cast<size_t>(kb) * 1024 + h * 8);
         const size_t gi = b_sidx[c] + (k0 / p.group);
         r.s[c] = Sbase[gi];
-        r.z[c] = Zbase[gi];
+        r.z[c] = Zbase ? Zbase[gi] : uint16_t(0);   // no zeros: scale-only
       } else {
         r.b[c] = *reinterpret_cast<const u32x2 *>(b_src[c] + static_cast<size_t>(step) * 1024);
         if constexpr (GS8) r.s[c] = Sbase[b_sidx[c] + k0 / p.group];

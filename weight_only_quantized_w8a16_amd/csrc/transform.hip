@@ -314,7 +314,7 @@ __global__ void k_dequant_w4(const uint8_t *__restrict__ B, const uint16_t *__re
   uint32_t word = *reinterpret_cast<const uint32_t *>(B + w4_word_offset(row, k0, k));
   size_t gi = static_cast<size_t>(row) * (k / group) + k0 / group;
   float s = bits_to_f32<ACT>(S[gi]);
-  float z = bits_to_f32<ACT>(Z[gi]);
+  float z = Z ? bits_to_f32<ACT>(Z[gi]) : 0.0f;   // no zeros: scale-only
   float v[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e)
