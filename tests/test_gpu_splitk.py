@@ -48,7 +48,7 @@ def run_w8(p, workspace=None):
 
 @pytest.mark.parametrize("tile", ["D8", "D8N", "D64", "D128", "X", "L", "M", "S"])
 @pytest.mark.parametrize("slices", [2, 3, 4])
-@pytest.mark.parametrize("group", [64, 128])
+@pytest.mark.parametrize("group", [64, 128, -1])
 def test_split_w4_every_tile_exact(tile, slices, group, monkeypatch):
     # K = 4096: 64 steps, so with 128-groups (16-step windows) 3 and 4
     # slices still give more than one slice; M and N ragged against tiles.

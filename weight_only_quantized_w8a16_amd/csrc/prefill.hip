@@ -101,7 +101,7 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float *__restrict__
   *reinterpret_cast<uint2 *>(C + 4 * q) = make_uint2(out[0], out[1]);
 }
 
-template <class Cfg, int ACT, int WBITS, bool GS8, bool SPLIT>
+template <class Cfg, int ACT, int WBITS, bool GS8, bool SPLIT, bool PC>
 __global__ __launch_bounds__(Cfg::NTHR) void k_prefill_dma(TileProblem p, int tiles_n) {
   __shared__ __attribute__((aligned(16))) char a0[Cfg::STAGE_A];
   __shared__ __attribute__((aligned(16))) char a1[Cfg::STAGE_A];
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(Cfg::NTHR) void k_prefill_dma(TileProblem p, int ti
   const DmaLds L{{a0, a1}, {b0, b1}, sc};
   int tm, tn, slice;
   split_tile<SPLIT>(p, tiles_n, tm, tn, slice);
-  tile_gemm_dma<Cfg, ACT, WBITS, kDense, GS8, SPLIT>(p, tm, tn, L, slice);
+  tile_gemm_dma<Cfg, ACT, WBITS, kDense, GS8, SPLIT, PC>(p, tm, tn, L, slice);
 }
 
 namespace {
@@ -179,29 +179,29 @@ hipError_t run(const GemmArgs &a, hipStream_t s, const Split &sp = Split{}) {
 // Whether the direct-load tiles take the problem (else the generic tile of
 // the same width does): 32-bit offsets, and group scales (int4 zeros too)
 // in 4-byte pairs of groups.
-template <int WBITS, bool GS8>
+template <int WBITS, bool GS8, bool PC>
 bool dma_ok(const GemmArgs &a) {
   const uint64_t lim = uint64_t(1) << 31;
   if (uint64_t(a.M) * a.K >= lim || uint64_t(a.N) * a.K * WBITS / 8 >= lim) return false;
-  if ((WBITS == 4 || GS8) &&
+  if (((WBITS == 4 && !PC) || GS8) &&
       (((a.K / a.group) & 1) != 0 || (reinterpret_cast<uintptr_t>(a.S) & 3) != 0 ||
        (WBITS == 4 && (reinterpret_cast<uintptr_t>(a.Z) & 3) != 0)))
     return false;
   return true;
 }
 
-template <class Cfg, int ACT, int WBITS, bool GS8>
+template <class Cfg, int ACT, int WBITS, bool GS8, bool PC = false>
 hipError_t run_dma(const GemmArgs &a, hipStream_t s, const Split &sp = Split{}) {
   using Fallback = std::conditional_t<Cfg::BN == 256, CfgX, CfgL>;
-  if (!dma_ok<WBITS, GS8>(a)) return run<Fallback, ACT, WBITS, GS8>(a, s, sp);
+  if (!dma_ok<WBITS, GS8, PC>(a)) return run<Fallback, ACT, WBITS, GS8>(a, s, sp);
   const TileProblem p = dense_problem(a, sp);
   const int tm = (a.M + Cfg::BM - 1) / Cfg::BM, tn = a.N / Cfg::BN;
   if (sp.part)
-    hipLaunchKernelGGL((k_prefill_dma<Cfg, ACT, WBITS, GS8, true>), dim3(tm * tn * sp.nsplit),
+    hipLaunchKernelGGL((k_prefill_dma<Cfg, ACT, WBITS, GS8, true, PC>), dim3(tm * tn * sp.nsplit),
                        dim3(Cfg::NTHR), 0, s, p, tn);
   else
-    hipLaunchKernelGGL((k_prefill_dma<Cfg, ACT, WBITS, GS8, false>), dim3(tm * tn), dim3(Cfg::NTHR),
-                       0, s, p, tn);
+    hipLaunchKernelGGL((k_prefill_dma<Cfg, ACT, WBITS, GS8, false, PC>), dim3(tm * tn),
+                       dim3(Cfg::NTHR), 0, s, p, tn);
   return reduce_split<ACT, WBITS, GS8>(a, sp, s);
 }
 
@@ -265,7 +265,8 @@ Plan plan_prefill(const GemmArgs &a, int wbits, bool gs8) {
   if (const char *o = std::getenv("QGEMM_SPLITK")) want = std::atoi(o);
   if (want <= 1) return pl;
   const int g = a.group > 0 ? a.group : a.K;
-  const int unit = (wbits == 4 || gs8) ? 8 * (g / 64) : 8;
+  const bool windows = (wbits == 4 && g != a.K) || gs8;   // scales through LDS windows
+  const int unit = windows ? 8 * (g / 64) : 8;
   int kseg = (nsteps + want - 1) / want;
   kseg = (kseg + unit - 1) / unit * unit;
   const int nsplit = (nsteps + kseg - 1) / kseg;
@@ -276,28 +277,28 @@ Plan plan_prefill(const GemmArgs &a, int wbits, bool gs8) {
   return pl;
 }
 
-template <int ACT, int WBITS, bool GS8>
+template <int ACT, int WBITS, bool GS8, bool PC>
 hipError_t launch_tile(int tile, const GemmArgs &a, hipStream_t s, const Split &sp) {
   switch (tile) {
     case kX: return run<CfgX, ACT, WBITS, GS8>(a, s, sp);
-    case kD8: return run_dma<CfgD8, ACT, WBITS, GS8>(a, s, sp);
-    case kD8N: return run_dma<CfgD8N, ACT, WBITS, GS8>(a, s, sp);
-    case kD64: return run_dma<CfgD64, ACT, WBITS, GS8>(a, s, sp);
-    case kD128: return run_dma<CfgD128, ACT, WBITS, GS8>(a, s, sp);
+    case kD8: return run_dma<CfgD8, ACT, WBITS, GS8, PC>(a, s, sp);
+    case kD8N: return run_dma<CfgD8N, ACT, WBITS, GS8, PC>(a, s, sp);
+    case kD64: return run_dma<CfgD64, ACT, WBITS, GS8, PC>(a, s, sp);
+    case kD128: return run_dma<CfgD128, ACT, WBITS, GS8, PC>(a, s, sp);
     case kL: return run<CfgL, ACT, WBITS, GS8>(a, s, sp);
     case kM: return run<CfgM, ACT, WBITS, GS8>(a, s, sp);
     default: return run<CfgS, ACT, WBITS, GS8>(a, s, sp);
   }
 }
 
-template <int ACT, int WBITS, bool GS8 = false>
+template <int ACT, int WBITS, bool GS8 = false, bool PC = false>
 hipError_t dispatch(const GemmArgs &a, hipStream_t s) {
   Plan pl = plan_prefill(a, WBITS, GS8);
   if (pl.split.nsplit > 1 && a.ws && a.ws_bytes >= pl.bytes)
     pl.split.part = static_cast<float *>(a.ws);
   else
     pl.split = Split{};
-  return launch_tile<ACT, WBITS, GS8>(pl.tile, a, s, pl.split);
+  return launch_tile<ACT, WBITS, GS8, PC>(pl.tile, a, s, pl.split);
 }
 
 }  // namespace
@@ -308,6 +309,8 @@ size_t prefill_workspace_bytes(const GemmArgs &a, int wbits) {
 }
 
 hipError_t launch_prefill_w4(const GemmArgs &a, hipStream_t s) {
+  if (a.group == a.K)   // one scale and zero per channel
+    return a.act == kBF16 ? dispatch<kBF16, 4, false, true>(a, s) : dispatch<kFP16, 4, false, true>(a, s);
   return a.act == kBF16 ? dispatch<kBF16, 4>(a, s) : dispatch<kFP16, 4>(a, s);
 }
 hipError_t launch_prefill_w8(const GemmArgs &a, hipStream_t s) {

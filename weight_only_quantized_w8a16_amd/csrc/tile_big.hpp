@@ -81,13 +81,17 @@ __device__ __forceinline__ int dswz(int row, int chunk) {
 // workgroup's K slice.  With scale windows kseg is a multiple of a window's
 // steps, so a slice starts on a window boundary.  Without SPLIT the kernel
 // runs all of K and the slice code is not compiled in.
-template <class Cfg, int ACT, int WBITS, int MODE = kDense, bool GS8 = false, bool SPLIT = false>
+// PC (int4 only): one scale and zero per channel (group = K), read once per
+// run into registers instead of through the LDS windows.
+template <class Cfg, int ACT, int WBITS, int MODE = kDense, bool GS8 = false, bool SPLIT = false,
+          bool PC = false>
 __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, int tile_n,
                                               const DmaLds &L, int slice = 0) {
   constexpr int BK = Cfg::BK, TM = Cfg::TM, TN = Cfg::TN, NTHR = Cfg::NTHR;
   static_assert(MODE == kDense || WBITS == 4, "MoE experts are int4");
   static_assert(!GS8 || WBITS == 8, "group scales without zeros: int8");
-  constexpr bool kWin = WBITS == 4 || GS8;   // scales through the LDS windows
+  static_assert(!PC || (WBITS == 4 && MODE == kDense), "per-channel int4: dense");
+  constexpr bool kWin = (WBITS == 4 && !PC) || GS8;   // scales through the LDS windows
   static_assert(MODE != kMoeFc1 || Cfg::BN == 256, "fc1 pairs 128 gate with 128 up rows");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
@@ -161,6 +165,7 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
   uint32_t b_src[NB];        // byte offsets into the tiled codes
   int b_lds0[NB], b_lds1[NB];
   int b_sc[NB];              // scale-window offsets of the runs' rows
+  [[maybe_unused]] int b_wrow[NB];   // weight rows of the runs (per-channel scales)
 #pragma unroll
   for (int c = 0; c < NB; ++c) {
     const int idx = tid + c * NTHR;
@@ -170,6 +175,7 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
     const int nl = l & 15, j = l >> 4;
     const int lrow = bi * 16 + nl;
     const int wrow = wrow_of(lrow);
+    b_wrow[c] = wrow;
     if constexpr (WBITS == 4) {
       b_src[c] = static_cast<uint32_t>(wrow >> 4) * static_cast<uint32_t>(K >> 7) * 1024u + l * 16;
       b_lds0[c] = dswz(lrow, j);          // word 2h   -> k-chunk j
@@ -237,7 +243,16 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
   struct ScaleRegs {
     uint16_t s[NB], z[NB];
   };
+  [[maybe_unused]] ScaleRegs pcv;   // per-channel: fixed for the whole K loop
+  if constexpr (PC) {
+#pragma unroll
+    for (int c = 0; c < NB; ++c) {
+      pcv.s[c] = p.S[b_wrow[c]];
+      pcv.z[c] = p.Z ? p.Z[b_wrow[c]] : uint16_t(0);
+    }
+  }
   auto sc_read = [&](int u, ScaleRegs &v) {
+    if constexpr (PC) v = pcv;
     if constexpr (kWin) {
       const int gi = u >> spg_lg;
       const char *win = L.sc + ((gi >> 3) & 1) * Cfg::SC_WIN + (gi & 7) * 2;
