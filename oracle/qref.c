@@ -343,6 +343,30 @@ void qref_gemm_w8_at(const uint16_t *A, const int8_t *codes, const uint16_t *sca
 }
 
 /* ---------------------------------------------------------------------- */
+/* W8A8: int8 activations times int8 weights  [acext] 1.2.2 w8a8 GEMM and   */
+/* 1.3.4 SmoothQuant: C[m, n] = (sum_k A[m, k] B[n, k]) * alpha_row * alpha_col */
+/* with alpha_row one value (per tensor) or one per row m (per token) and    */
+/* alpha_col one value or one per output channel n; both fp32.  The integer */
+/* sum is exact (int64); the scaling is done in double.                      */
+/* ---------------------------------------------------------------------- */
+void qref_gemm_w8a8(const int8_t *A, const int8_t *B, const float *alpha_row, int per_token,
+                    const float *alpha_col, int per_channel, int64_t m, int64_t n, int64_t k,
+                    int64_t *acc_out, double *C)
+{
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t col = 0; col < n; ++col) {
+        for (int64_t row = 0; row < m; ++row) {
+            int64_t acc = 0;
+            for (int64_t c = 0; c < k; ++c) acc += (int64_t)A[row * k + c] * (int64_t)B[col * k + c];
+            double ar = (double)alpha_row[per_token ? row : 0];
+            double ac = (double)alpha_col[per_channel ? col : 0];
+            if (acc_out) acc_out[row * n + col] = acc;
+            C[row * n + col] = (double)acc * ar * ac;
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------- */
 /* MoE  [acext] 1.2.3 runMoe: fp32 gating logits, top-k experts per row,   */
 /* normalised expert scales, fc1 with a gated activation, fc2, and a        */
 /* weighted combine into the final output.                                  */

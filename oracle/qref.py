@@ -24,7 +24,7 @@ import numpy as np
 __all__ = [
     "NONE", "BF16", "FP16", "build", "lib", "bf16_to_f32", "f16_to_f32", "f32_to_bf16",
     "f32_to_f16", "pack4", "unpack4", "quantize4", "dequant4", "dequant8", "gemm_w4", "gemm_w8",
-    "gemm_w4_at", "gemm_w8_at", "moe_route", "moe", "threads",
+    "gemm_w4_at", "gemm_w8_at", "gemm_w8a8", "moe_route", "moe", "threads",
 ]
 
 NONE, BF16, FP16 = 0, 1, 2
@@ -71,6 +71,7 @@ _SIGS = {
     "qref_gemm_w8": (None, [_P, _P, _P, _P, _I, _I, _I, _I, _INT, _INT, _P]),
     "qref_gemm_w4_at": (None, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _INT, _INT, _P, _P, _I, _P]),
     "qref_gemm_w8_at": (None, [_P, _P, _P, _P, _I, _I, _I, _I, _INT, _INT, _P, _P, _I, _P]),
+    "qref_gemm_w8a8": (None, [_P, _P, _P, _INT, _P, _INT, _I, _I, _I, _P, _P]),
     "qref_moe_route": (None, [_P, _I, _I, _I, _P, _P]),
     "qref_moe": (None, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _INT,
                         _P, _I, _P, _P, _P]),
@@ -264,6 +265,29 @@ def gemm_w8_at(A, codes, scale, rows, cols, group=-1, dtype=FP16, bias=None, bia
                           dtype, bias_dtype if bb is not None else NONE, _ptr(r), _ptr(c), r.size,
                           _ptr(out))
     return out
+
+
+# -- W8A8 ---------------------------------------------------------------------
+
+def gemm_w8a8(A, B, alpha_row, alpha_col):
+    """int8 A [M, K] x int8 B [N, K]: (exact int64 sums [M, N], double C [M, N]).
+
+    alpha_row has M entries (per token) or 1 (per tensor); alpha_col N or 1.
+    """
+    a = _c(A, np.int8)
+    b = _c(B, np.int8)
+    m, k = a.shape
+    n = b.shape[0]
+    assert b.shape[1] == k
+    ar = _c(np.atleast_1d(alpha_row), np.float32)
+    ac = _c(np.atleast_1d(alpha_col), np.float32)
+    per_token, per_channel = int(ar.size == m and m > 1), int(ac.size == n and n > 1)
+    assert ar.size in (1, m) and ac.size in (1, n)
+    acc = np.empty((m, n), dtype=np.int64)
+    out = np.empty((m, n), dtype=np.float64)
+    lib().qref_gemm_w8a8(_ptr(a), _ptr(b), _ptr(ar), per_token, _ptr(ac), per_channel, m, n, k,
+                         _ptr(acc), _ptr(out))
+    return acc, out
 
 
 # -- MoE ----------------------------------------------------------------------

@@ -300,6 +300,45 @@ def test_w8_gemm_vs_numpy_matmul(m, n, k):
     assert np.array_equal(W, p.codes.astype(np.float64) * s[:, None])
 
 
+# -- W8A8 ([acext] 1.2.2, 1.3.4) ----------------------------------------------------
+
+def test_w8a8_worked_example():
+    # Row [1, -2, 3] against weight rows [4, 5, -6] and [127, -128, 1]: the
+    # integer sums are 4 - 10 - 18 = -24 and 127 + 256 + 3 = 386; with the
+    # per-tensor activation scale 2 and per-channel scales [0.5, 0.25]:
+    # C = [-24, 193].
+    acc, C = oracle.gemm_w8a8(np.array([[1, -2, 3]], np.int8),
+                              np.array([[4, 5, -6], [127, -128, 1]], np.int8), [2.0], [0.5, 0.25])
+    assert acc.tolist() == [[-24, 386]] and C.tolist() == [[-24.0, 193.0]]
+
+
+@pytest.mark.parametrize("per_token,per_channel", [(0, 0), (0, 1), (1, 0), (1, 1)])
+def test_w8a8_vs_numpy_integer_matmul(per_token, per_channel):
+    # The four QuantMode variants: the exact int64 product from numpy, times
+    # the row and column scales (one value each when per tensor).
+    rng = np.random.default_rng(per_token * 2 + per_channel)
+    m, n, k = 7, 24, 320
+    A = rng.integers(-128, 128, (m, k)).astype(np.int8)
+    B = rng.integers(-128, 128, (n, k)).astype(np.int8)
+    ar = rng.uniform(0.001, 0.1, m if per_token else 1).astype(np.float32)
+    ac = rng.uniform(0.001, 0.1, n if per_channel else 1).astype(np.float32)
+    acc, C = oracle.gemm_w8a8(A, B, ar, ac)
+    ref_acc = A.astype(np.int64) @ B.astype(np.int64).T
+    assert np.array_equal(acc, ref_acc)
+    scale = np.outer(np.broadcast_to(ar.astype(np.float64), (m,)),
+                     np.broadcast_to(ac.astype(np.float64), (n,)))
+    np.testing.assert_allclose(C, ref_acc * scale, rtol=1e-15)
+
+
+def test_w8a8_extremes():
+    # -128 * -128 over k = 4096 is 2^26, beyond int32's fp32-exact range but
+    # exact in the int64 sum.
+    k = 4096
+    acc, C = oracle.gemm_w8a8(np.full((1, k), -128, np.int8), np.full((2, k), -128, np.int8),
+                              [1.0], [1.0])
+    assert (acc == 16384 * k).all() and (C == 16384.0 * k).all()
+
+
 def test_w4_exact_inputs_are_exact():
     p = si.w4_exact_problem(3, 32, 256, 64, seed=7, bias_dtype=FP16)
     C = oracle.gemm_w4(p.A, p.packed, p.scale, p.zero, 64, BF16, p.bias, FP16)
