@@ -16,6 +16,8 @@ Secondary sections on the same JSON line:
            and group-128 scales;
   w4_forms W4A16 N=13312, K=2048 at M in {1, 512} for each scale form
            (groupwise with zeros, scale-only, per channel);
+  w8a8     int8 x int8 GEMM at K=3584, N in {3584, 18944}, M from 1 to 4096,
+           per-token x per-channel scales (TOP/s against the int8 peak);
   quantize the load-side groupwise int4 quantizer on bf16 weights
            [N, 2048], N in {13312, 131072}, group 64 (GB/s against HBM);
   roofline the decode kernel of the N=131072 GEMV: algorithmic bytes per
@@ -42,6 +44,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores, TFLOP/s
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 matrix cores, TOP/s
 ROTATE_BYTES = 1 << 30
 
 DECODE_K, DECODE_G = 2048, 64
@@ -428,6 +431,50 @@ def run(args):
         log(f"w4 forms: {forms}")
         torch.cuda.empty_cache()
 
+    # ---- W8A8 (int8 x int8, per-token x per-channel scales), K = 3584 ------------------
+    w8a8 = None
+    if not args.no_w8a8:
+        ka = 3584
+        ashapes = {}
+        for n in (3584, 18944):
+            p0 = si.w8a8_problem(1, n, ka, True, True, tag="w8a8-bench")
+            base = torch.from_numpy(p0.B).to(dev)
+            col = torch.from_numpy(p0.alpha_col).to(dev)
+            wb = n * ka + 4 * n
+            copies = copies_for(wb)
+            sets = [(base, col)] + [(base.clone(), col.clone()) for _ in range(copies - 1)]
+            for m in (1, 16, 128, 1024, 4096):
+                pa = si.w8a8_problem(m, n, ka, True, True, tag="w8a8-bench")
+                A = torch.from_numpy(pa.A).to(dev)
+                row = torch.from_numpy(pa.alpha_row).to(dev)
+                C = torch.empty((m, n), dtype=torch.float16, device=dev)
+                need = qg.w8a8_workspace_size(m, n, ka)
+                ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+                reps = max(10, K // 5)
+
+                def call(i, A=A, C=C, sets=sets, row=row, ws=ws):
+                    B, col_ = sets[i % len(sets)]
+                    qg.gemm_w8a8(A, B, row, col_, out=C, workspace=ws)
+                for i in range(3):
+                    call(i)
+                ms = timed(call, reps, warm=reps) / reps
+                b = wb + m * ka + 4 * m + 2 * m * n
+                ops = 2.0 * m * n * ka
+                ashapes[f"M{m}_N{n}"] = {
+                    "us": round(ms * 1e3, 2), "GBps": round(b / (ms * 1e-3) / 1e9, 1),
+                    "TOPS": round(ops / (ms * 1e-3) / 1e12, 1),
+                    "frac_hbm": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 3),
+                    "frac_mfma_i8": round(ops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 3),
+                    "split_k_ws_bytes": need}
+                del A, C, ws
+            del sets, base
+            torch.cuda.empty_cache()
+        w8a8 = {"config": "W8A8 int8 x int8, K=3584, N in {3584, 18944}, per-token x "
+                          "per-channel fp32 scales, fp16 C; GB/s against 8 TB/s for small M, "
+                          "TOP/s against the 5.0 POP/s dense int8 peak for large M",
+                "shapes": ashapes}
+        log(f"w8a8: {w8a8}")
+
     # ---- load-side quantizer ------------------------------------------------------
     quant = None
     if not args.no_quant:
@@ -525,6 +572,7 @@ def run(args):
         "moe": moe,
         "w8": w8,
         "w4_forms": forms,
+        "w8a8": w8a8,
         "quantize": quant,
         "ceiling": ceil,
     }
@@ -542,6 +590,7 @@ def main():
     ap.add_argument("--no-moe", action="store_true")
     ap.add_argument("--no-quant", action="store_true")
     ap.add_argument("--no-w8", action="store_true")
+    ap.add_argument("--no-w8a8", action="store_true")
     ap.add_argument("--quick", action="store_true", help="skip the M sweep and the copy ceiling")
     ap.add_argument("--kernel-only", action="store_true",
                     help="run only the N=131072 GEMV (--steps times) and a calibration copy; "

@@ -37,7 +37,7 @@
  *    tokens == 0) is a successful no-op that reads no pointer; k must be
  *    positive (repack and dequant also accept k == 0).  The first failed
  *    check decides the status, in the order: sizes, NULL pointers, dtypes,
- *    group size, tile multiples, alignment, workspace.
+ *    group size (or W8A8 quant mode), tile multiples, alignment, workspace.
  *  - Functions are reentrant; calls on different streams may overlap unless
  *    they share a workspace.
  */
@@ -60,7 +60,8 @@ typedef enum {
     QG_ERR_ALIGN = 5,       /* a device pointer is not 16-byte aligned */
     QG_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required */
     QG_ERR_UNSUPPORTED = 7, /* valid, but outside the tile multiples listed per call */
-    QG_ERR_HIP = 8          /* the HIP runtime rejected a launch */
+    QG_ERR_HIP = 8,         /* the HIP runtime rejected a launch */
+    QG_ERR_MODE = 9         /* W8A8 quant mode outside the four variants */
 } qg_status;
 
 typedef enum { QG_NONE = 0, QG_BF16 = 1, QG_FP16 = 2, QG_FP32 = 3 } qg_dtype;
@@ -196,6 +197,46 @@ qg_status qgemm_w8a16(const void *A, const int8_t *B_tiled, const void *scales, 
                       void *C, int m, int n, int k, int group_size, qg_dtype act_dtype,
                       qg_dtype bias_dtype, void *workspace, size_t workspace_bytes,
                       void *stream);
+
+/* ------------------------------------------------------------------------
+ * W8A8: int8 activations times int8 weights with fp32 row and column scales
+ * (acext User Guide (v1.7), 1.2.2 w8a8 GEMM: A, B, quant mode, alphaCol,
+ * alphaRow, C, m, n, k, workspace, stream, the output type a parameter;
+ * 1.3.4 SmoothQuant: both operands stay integer, four variants).
+ *   C[m, n] = RNE_out( float(sum_k A[m, k] * B[n, k]) * alpha_row[r] * alpha_col[c] )
+ * with the integer sum exact (int32), r = m for per-token activations (else
+ * 0) and c = n for per-channel weights (else 0); the two fp32 products are
+ * taken left to right.
+ *   A          device int8 [m, k] row-major (activation codes)
+ *   B          device int8 [n, k] row-major (weight codes, one row per output
+ *              channel; no repack: the rows are already in the order the
+ *              int8 matrix instruction reads)
+ *   quant_mode QG_W8A8_PER_TENSOR (0), or an OR of QG_W8A8_PER_CHANNEL (1:
+ *              alpha_col holds n values) and QG_W8A8_PER_TOKEN (2: alpha_row
+ *              holds m values); the four values are the page's
+ *              A_PerTensor_W_PerTensor, A_PerTensor_W_PerChannel,
+ *              A_PerToken_W_PerTensor and A_PerToken_W_PerChannel
+ *   alpha_col  device fp32 [n] (per channel) or [1]
+ *   alpha_row  device fp32 [m] (per token) or [1]
+ *   C          device [m, n] in out_dtype (QG_BF16, QG_FP16 or QG_FP32);
+ *              written, never read
+ *   Tile multiples: n % 16 == 0, k % 128 == 0, k <= 130944 (so that
+ *   2^14 * k < 2^31: the int32 sum cannot overflow), m * k and n * k below
+ *   2^31.  Alignment: A, B, C 16 bytes, alpha_* 4 bytes.
+ *   workspace: optional, 256-byte aligned.  With at least
+ *   qgemm_w8a8_workspace_size() bytes (> 0 when the output has too few tiles
+ *   to fill the GPU, e.g. decode-sized m) K slices write int32 partials
+ *   [slices, m, n] there and one more launch adds them (exactly) and scales;
+ *   with less (or NULL) the same call runs unsplit.  Calls that share a
+ *   workspace must not overlap.
+ * ---------------------------------------------------------------------- */
+enum { QG_W8A8_PER_TENSOR = 0, QG_W8A8_PER_CHANNEL = 1, QG_W8A8_PER_TOKEN = 2 };
+
+size_t qgemm_w8a8_workspace_size(int m, int n, int k);
+
+qg_status qgemm_w8a8(const int8_t *A, const int8_t *B, int quant_mode, const float *alpha_col,
+                     const float *alpha_row, void *C, int m, int n, int k, qg_dtype out_dtype,
+                     void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * Top-k MoE with SiLU-gated int4 experts  (acext User Guide (v1.7), 1.2.3

@@ -123,6 +123,44 @@ def w8_problem(m, n, k, group=-1, tag="w8", dtype=FP16, bias_dtype=NONE, **kw) -
     return W8Problem(m, n, k, group, dtype, A, codes, scale, bias, bias_dtype)
 
 
+# -- W8A8: int8 activation and weight codes, fp32 row / column scales ----------
+
+@dataclass
+class W8A8Problem:
+    m: int
+    n: int
+    k: int
+    A: np.ndarray           # int8 [m, k]
+    B: np.ndarray           # int8 [n, k]
+    alpha_row: np.ndarray   # fp32 [m] (per token) or [1]
+    alpha_col: np.ndarray   # fp32 [n] (per channel) or [1]
+
+
+def _codes8(g, shape, lo, hi):
+    return torch.randint(lo, hi + 1, shape, generator=g, dtype=torch.int32).to(torch.int8).numpy()
+
+
+def w8a8_problem(m, n, k, per_token, per_channel, tag="w8a8", code_range=(-127, 127),
+                 row_range=(0.005, 0.05), col_range=(0.001, 0.01), scales=None) -> W8A8Problem:
+    """Symmetric int8 codes uniform in code_range for both operands; scales
+    uniform in the given ranges, or drawn from the list `scales` (e.g. powers
+    of two) when given."""
+    gw = _gen(seed_of(tag, "w", n, k, per_channel, code_range))
+    B = _codes8(gw, (n, k), *code_range)
+    nc = n if per_channel else 1
+    ga = _gen(seed_of(tag, "a", m, k, per_token, code_range))
+    A = _codes8(ga, (m, k), *code_range)
+    nr = m if per_token else 1
+    if scales is None:
+        col = _uniform(gw, (nc,), *col_range).numpy()
+        row = _uniform(ga, (nr,), *row_range).numpy()
+    else:
+        sv = torch.tensor(scales, dtype=torch.float32)
+        col = sv[torch.randint(0, len(scales), (nc,), generator=gw)].numpy()
+        row = sv[torch.randint(0, len(scales), (nr,), generator=ga)].numpy()
+    return W8A8Problem(m, n, k, A, B, row.astype(np.float32), col.astype(np.float32))
+
+
 # -- inputs whose exact product is representable -------------------------------
 # Activations in {-2..2}, scales in {1, 1/2, 1/4}, zeros multiples of 1/4 in
 # [-1, 1], bias multiples of 1/4: every partial sum is a multiple of 2^-2 well

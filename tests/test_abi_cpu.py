@@ -38,8 +38,8 @@ def test_library_exports_every_declared_symbol():
 def test_version_and_strerror():
     L = qg.lib()
     assert L.qg_version() >= 10000
-    for s in range(9):
-        assert L.qg_strerror(s)
+    for s in range(10):
+        assert L.qg_strerror(s) != b"unknown status"
     assert L.qg_strerror(99) == b"unknown status"
 
 
@@ -200,3 +200,45 @@ def test_workspace_query_and_alignment():
         assert L.qgemm_workspace_size(*args) == 0, args
     # a workspace that is given must be 256-byte aligned (checked before any launch)
     assert w4(m=128, n=3072, k=2048, ws=FAKE + 16, wsb=1 << 20) == ALIGN
+
+
+# -- W8A8 -----------------------------------------------------------------------
+
+MODE = 9
+
+
+def w8a8(**kw):
+    a = dict(A=FAKE, B=FAKE, mode=3, ac=FAKE, ar=FAKE, C=FAKE, m=4, n=128, k=256, out=FP16,
+             ws=None, wsb=0)
+    a.update(kw)
+    return qg.lib().qgemm_w8a8(a["A"], a["B"], a["mode"], a["ac"], a["ar"], a["C"], a["m"], a["n"],
+                               a["k"], a["out"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(m=-1), SHAPE), (dict(n=-16), SHAPE), (dict(k=0), SHAPE),
+    (dict(A=None), NULL), (dict(B=None), NULL), (dict(ac=None), NULL), (dict(ar=None), NULL),
+    (dict(C=None), NULL),
+    (dict(out=0), DTYPE), (dict(out=7), DTYPE),
+    (dict(mode=4), MODE), (dict(mode=-1), MODE),
+    (dict(n=24), UNSUP), (dict(k=192), UNSUP), (dict(k=131136), UNSUP),
+    (dict(m=1 << 14, k=131072), UNSUP),
+    (dict(A=FAKE + 8), ALIGN), (dict(B=FAKE + 4), ALIGN), (dict(C=FAKE + 2), ALIGN),
+    (dict(ac=FAKE + 2), ALIGN), (dict(ar=FAKE + 1), ALIGN), (dict(ws=FAKE + 16, wsb=64), ALIGN),
+    (dict(m=0), OK), (dict(n=0), OK), (dict(m=0, A=None), OK),
+])
+def test_w8a8_validation(kw, status):
+    assert w8a8(**kw) == status
+
+
+def test_w8a8_modes_and_workspace_query():
+    # The four modes are 0..3 (weights per channel = 1, activations per
+    # token = 2); a decode-sized problem asks for split-K partials, a large one
+    # for none, invalid sizes for none.
+    L = qg.lib()
+    assert (_abi.QG_W8A8_PER_TENSOR, _abi.QG_W8A8_PER_CHANNEL, _abi.QG_W8A8_PER_TOKEN) == (0, 1, 2)
+    assert L.qgemm_w8a8_workspace_size(1, 3584, 3584) > 0
+    assert L.qgemm_w8a8_workspace_size(1, 3584, 3584) % 256 == 0
+    assert L.qgemm_w8a8_workspace_size(4096, 18944, 3584) == 0
+    assert L.qgemm_w8a8_workspace_size(0, 3584, 3584) == 0
+    assert L.qgemm_w8a8_workspace_size(1, 3584, 3500) == 0

@@ -13,12 +13,14 @@ from typing import Optional
 
 import torch
 
-from ._abi import QG_BF16, QG_FP16, QG_FP32, QG_NONE, QGemmError, check, lib
+from ._abi import (QG_BF16, QG_FP16, QG_FP32, QG_NONE, QG_W8A8_PER_CHANNEL, QG_W8A8_PER_TOKEN,
+                   QGemmError, check, lib)
 
 __all__ = [
     "QGemmError", "lib", "repack_w4", "unrepack_w4", "repack_w8", "unrepack_w8", "repack_w8_kn",
     "unrepack_w8_kn", "quantize_w4", "dequant_w4", "dequant_w8", "gemm_w4a16", "gemm_w8a16",
-    "moe_grouped", "moe_workspace_size", "gemm_workspace_size", "dtype_code",
+    "moe_grouped", "moe_workspace_size", "gemm_workspace_size", "dtype_code", "gemm_w8a8",
+    "w8a8_workspace_size",
 ]
 
 _CODES = {torch.bfloat16: QG_BF16, torch.float16: QG_FP16, torch.float32: QG_FP32}
@@ -228,6 +230,46 @@ def gemm_w8a16(A: torch.Tensor, B_tiled: torch.Tensor, scales: torch.Tensor,
         _ptr(A2), _ptr(B_tiled), _ptr(scales), _ptr(bias), _ptr(C), m, n, k, group_size,
         dtype_code(A.dtype), dtype_code(None if bias is None else bias.dtype), _ptr(ws),
         ws_bytes, _stream(A)))
+    return C.reshape(*lead, n)
+
+
+# -- W8A8 ----------------------------------------------------------------------
+
+def w8a8_workspace_size(m: int, n: int, k: int) -> int:
+    return int(lib().qgemm_w8a8_workspace_size(m, n, k))
+
+
+def gemm_w8a8(A: torch.Tensor, B: torch.Tensor, alpha_row: torch.Tensor,
+              alpha_col: torch.Tensor, out_dtype: torch.dtype = torch.float16,
+              out: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C = (A_int8 . B_int8^T) * alpha_row * alpha_col; A [..., k] int8,
+    B [n, k] int8, alpha_row fp32 [m] (per token) or [1], alpha_col fp32 [n]
+    (per channel) or [1]; the quant mode follows the scale lengths."""
+    _dev(A, "A")
+    _dev(B, "B")
+    _dev(alpha_row, "alpha_row")
+    _dev(alpha_col, "alpha_col")
+    lead = A.shape[:-1]
+    k = A.shape[-1]
+    A2 = A.reshape(-1, k)
+    m, n = A2.shape[0], B.shape[0]
+    if alpha_row.numel() not in (1, m) or alpha_col.numel() not in (1, n):
+        raise QGemmError("qgemm_w8a8", 2, "alpha_row must hold 1 or m values, alpha_col 1 or n")
+    mode = ((QG_W8A8_PER_TOKEN if alpha_row.numel() == m and m > 1 else 0)
+            | (QG_W8A8_PER_CHANNEL if alpha_col.numel() == n and n > 1 else 0))
+    C = out if out is not None else torch.empty((m, n), dtype=out_dtype, device=A.device)
+    _dev(C, "out")
+    if tuple(C.shape) != (m, n):
+        raise QGemmError("qgemm_w8a8", 2, f"out must be [{m}, {n}]")
+    need = w8a8_workspace_size(m, n, k)
+    ws = workspace
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=A.device)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    check("qgemm_w8a8", lib().qgemm_w8a8(
+        _ptr(A2), _ptr(B), mode, _ptr(alpha_col), _ptr(alpha_row), _ptr(C), m, n, k,
+        dtype_code(C.dtype), _ptr(ws), ws_bytes, _stream(A)))
     return C.reshape(*lead, n)
 
 

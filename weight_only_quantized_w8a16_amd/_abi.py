@@ -17,8 +17,10 @@ QG_OK = 0
 STATUS_NAMES = {
     0: "QG_OK", 1: "QG_ERR_NULL", 2: "QG_ERR_SHAPE", 3: "QG_ERR_GROUP", 4: "QG_ERR_DTYPE",
     5: "QG_ERR_ALIGN", 6: "QG_ERR_WORKSPACE", 7: "QG_ERR_UNSUPPORTED", 8: "QG_ERR_HIP",
+    9: "QG_ERR_MODE",
 }
 QG_NONE, QG_BF16, QG_FP16, QG_FP32 = 0, 1, 2, 3
+QG_W8A8_PER_TENSOR, QG_W8A8_PER_CHANNEL, QG_W8A8_PER_TOKEN = 0, 1, 2
 
 _P = ctypes.c_void_p
 _INT = ctypes.c_int
@@ -41,6 +43,8 @@ SIGNATURES = {
     "qgemm_workspace_size": (_SZ, [_INT, _INT, _INT, _INT, _INT]),
     "qgemm_w4a16": (_ST, [_P, _P, _P, _P, _P, _P, _INT, _INT, _INT, _INT, _INT, _INT, _P, _SZ, _P]),
     "qgemm_w8a16": (_ST, [_P, _P, _P, _P, _P, _INT, _INT, _INT, _INT, _INT, _INT, _P, _SZ, _P]),
+    "qgemm_w8a8_workspace_size": (_SZ, [_INT, _INT, _INT]),
+    "qgemm_w8a8": (_ST, [_P, _P, _INT, _P, _P, _P, _INT, _INT, _INT, _INT, _P, _SZ, _P]),
     "qmoe_workspace_size": (_SZ, [_INT, _INT, _INT, _INT, _INT]),
     "qmoe_grouped": (_ST, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _INT, _INT, _INT, _INT, _INT, _INT,
                            _INT, _P, _P, _P, _SZ, _P]),

@@ -88,6 +88,7 @@ const char *qg_strerror(qg_status s) {
     case QG_ERR_WORKSPACE: return "workspace missing or too small";
     case QG_ERR_UNSUPPORTED: return "sizes outside the supported tile multiples";
     case QG_ERR_HIP: return "HIP runtime error at launch";
+    case QG_ERR_MODE: return "W8A8 quant mode is not one of the four variants";
   }
   return "unknown status";
 }
@@ -251,6 +252,41 @@ qg_status qgemm_w8a16(const void *A, const int8_t *B, const void *scales, const 
   hipStream_t s = as_stream(stream);
   if (uses_prefill(m, n)) return hip_status(qg::launch_prefill_w8(a, s));
   return hip_status(by_row_slabs(a, qg::launch_decode_w8, s));
+}
+
+// ---------------------------------------------------------------------------
+// W8A8
+// ---------------------------------------------------------------------------
+// Largest k whose int32 sum cannot overflow (2^14 k < 2^31), rounded down to
+// the 128-k step.
+constexpr int kW8A8MaxK = 130944;
+
+size_t qgemm_w8a8_workspace_size(int m, int n, int k) {
+  if (m <= 0 || n <= 0 || k <= 0 || k % 128 != 0 || k > kW8A8MaxK) return 0;
+  const size_t b = qg::w8a8_workspace_bytes(m, n, k);
+  return b ? (b + 255) & ~static_cast<size_t>(255) : 0;
+}
+
+qg_status qgemm_w8a8(const int8_t *A, const int8_t *B, int mode, const float *alpha_col,
+                     const float *alpha_row, void *C, int m, int n, int k, qg_dtype out,
+                     void *workspace, size_t ws_bytes, void *stream) {
+  if (m < 0 || n < 0 || k <= 0) return QG_ERR_SHAPE;
+  if (m == 0 || n == 0) return QG_OK;   // nothing to compute; pointers unused
+  if (!A || !B || !alpha_col || !alpha_row || !C) return QG_ERR_NULL;
+  if (!(act_ok(out) || out == QG_FP32)) return QG_ERR_DTYPE;
+  if (mode < 0 || mode > (QG_W8A8_PER_CHANNEL | QG_W8A8_PER_TOKEN)) return QG_ERR_MODE;
+  const uint64_t lim = uint64_t(1) << 31;
+  if (n % 16 != 0 || k % 128 != 0 || k > kW8A8MaxK || uint64_t(m) * k >= lim ||
+      uint64_t(n) * k >= lim)
+    return QG_ERR_UNSUPPORTED;
+  if (!aligned(A, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(alpha_col, 4) ||
+      !aligned(alpha_row, 4))
+    return QG_ERR_ALIGN;
+  if (workspace && ws_bytes && !aligned(workspace, 256)) return QG_ERR_ALIGN;
+  qg::W8A8Args a{A, B, alpha_row, alpha_col, C, m, n, k,
+                 (mode & QG_W8A8_PER_TOKEN) ? 1 : 0, (mode & QG_W8A8_PER_CHANNEL) ? 1 : 0,
+                 static_cast<int>(out), workspace, workspace ? ws_bytes : 0};
+  return hip_status(qg::launch_w8a8(a, as_stream(stream)));
 }
 
 // ---------------------------------------------------------------------------

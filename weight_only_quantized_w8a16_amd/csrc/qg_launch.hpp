@@ -67,3 +67,25 @@ size_t moe_workspace_bytes(int T, int H, int I, int E, int topk);
 hipError_t launch_moe(const MoeArgs &a, hipStream_t s);
 
 }  // namespace qg
+
+namespace qg {
+
+// W8A8 (int8 activations x int8 weights, fp32 row/column scales).
+struct W8A8Args {
+  const int8_t *A;          // [M, K]
+  const int8_t *B;          // [N, K]
+  const float *alpha_row;   // [M] if per_token else [1]
+  const float *alpha_col;   // [N] if per_channel else [1]
+  void *C;                  // [M, N] in `out`
+  int M, N, K;
+  int per_token, per_channel;
+  int out;                  // QG_BF16, QG_FP16 or QG_FP32
+  void *ws;                 // split-K partials, may be null
+  size_t ws_bytes;
+};
+// Workspace bytes the W8A8 kernels would use (split-K), 0 if none; with
+// less they run unsplit.
+size_t w8a8_workspace_bytes(int m, int n, int k);
+hipError_t launch_w8a8(const W8A8Args &a, hipStream_t s);
+
+}  // namespace qg

@@ -1,0 +1,402 @@
+// w8a8.hip -- int8 x int8 GEMM with tensor, token and channel scales (W8A8,
+// SmoothQuant) on gfx950:
+//
+//   C[m, n] = RNE_out( float(sum_k A[m, k] * B[n, k]) * alpha_row[m] * alpha_col[n] )
+//
+// alpha_row is one value (per tensor) or one per activation row (per token),
+// alpha_col one value or one per output channel.  Sources: "acext User Guide
+// (v1.7)", 1.2.2 w8a8 GEMM (the runner's arguments: A, B, quant mode, column
+// and row scales, C, m, n, k, workspace, stream; the output type is the
+// template parameter) and 1.3.4 SmoothQuant (both operands stay integer; four
+// variants: activations per tensor or per token, weights per tensor or per
+// channel).
+//
+// Both operands are K-contiguous int8 rows, which is the operand order of the
+// int8 matrix instruction, so nothing is repacked: a workgroup moves 128-k
+// slabs of its BM activation rows and BN weight rows from global memory
+// straight into LDS (buffer_load ... lds, 16 bytes per lane, no VGPRs), one
+// step ahead of use in two stages, and runs v_mfma_i32_32x32x32_i8 on them.
+// The int32 accumulators are exact (|sum| <= 2^14 k < 2^31 for the k the
+// host accepts); the scales are applied once, in fp32, in the epilogue.
+//
+// LDS placement (as in the weight-only tiles): a stage row is 128 bytes, its
+// 16-byte chunk c stored at chunk c ^ ((row / 2) % 8), so the 16 rows a lane
+// group reads at one chunk land in 16 distinct bank groups.  A direct load
+// writes 64 consecutive 16-byte slots, so the swizzle is applied on the
+// source side.  Rows past the end of A or B are read from the last valid row
+// (a direct load cannot be masked); their outputs are never stored.
+#include <algorithm>
+#include <cstdlib>
+#include <type_traits>
+
+#include "qg_common.hpp"
+#include "qg_launch.hpp"
+
+namespace qg {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+
+struct W8A8Problem {
+  const int8_t *A;       // [M, K]
+  const int8_t *B;       // [N, K]
+  const float *arow;     // [M] (per token) or [1]
+  const float *acol;     // [N] (per channel) or [1]
+  void *C;               // [M, N], out dtype
+  int32_t *part;         // split-K: int32 partial sums [nsplit, M, N]; else null
+  int M, N, K;
+  int per_token, per_channel;
+  int kseg;              // 128-k steps per K slice (split-K)
+};
+
+template <int BM_, int BN_, int WM_, int WN_>
+struct W8Cfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int NTHR = 64 * WM * WN;
+  static constexpr int WTM = BM / WM, WTN = BN / WN;   // wave tile
+  static constexpr int TM = WTM / 32, TN = WTN / 32;   // 32x32 accumulators per wave
+  static constexpr int A_DMA = BM * 8 / NTHR;          // 16-byte direct loads per thread per step
+  static constexpr int B_DMA = BN * 8 / NTHR;
+  static_assert(NTHR == 512, "eight waves");
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0 && A_DMA >= 1 && B_DMA >= 1, "tile shape");
+};
+
+// Output element conversion.
+template <int OUT>
+__device__ __forceinline__ void store4(void *C, size_t off, const float (&v)[4]) {
+  if constexpr (OUT == QG_FP32) {
+    *reinterpret_cast<f32x4 *>(static_cast<float *>(C) + off) = f32x4{v[0], v[1], v[2], v[3]};
+  } else {
+    *reinterpret_cast<u32x2 *>(static_cast<uint16_t *>(C) + off) =
+        u32x2{pack2<OUT>(v[0], v[1]), pack2<OUT>(v[2], v[3])};
+  }
+}
+
+// Workgroup b runs on XCD b % 8.  Each XCD takes a contiguous run of the
+// tile order, so neighbouring tiles share an L2.
+__device__ __forceinline__ int w8a8_linear_id() {
+  const int bid = blockIdx.x, nblk = gridDim.x;
+  const int xcd = bid & 7, loc = bid >> 3;
+  const int per = nblk >> 3, rem = nblk & 7;
+  return (xcd < rem) ? xcd * (per + 1) + loc : rem * (per + 1) + (xcd - rem) * per + loc;
+}
+
+// Tile order: bands of four row tiles walked column by column, so one weight
+// tile serves the band's row tiles while it is in L2.
+__device__ __forceinline__ void w8a8_tile(int id, int tiles_m, int tiles_n, int &tm, int &tn) {
+  constexpr int G = 4;
+  const int band = id / (G * tiles_n);
+  const int first = band * G, gsz = min(G, tiles_m - first);
+  const int in = id - band * G * tiles_n;
+  tm = first + in % gsz;
+  tn = in / gsz;
+}
+
+template <class Cfg, int OUT, bool SPLIT>
+__device__ __forceinline__ void w8a8_tile_gemm(const W8A8Problem &p, int tiles_m, int tiles_n,
+                                               char (*a_st)[Cfg::BM * 128], char (*b_st)[Cfg::BN * 128]) {
+  constexpr int TM = Cfg::TM, TN = Cfg::TN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
+  const int K = p.K, nsteps = K / 128;
+
+  const int id = w8a8_linear_id();
+  const int per = tiles_m * tiles_n;
+  const int slice = SPLIT ? id / per : 0;
+  int tm, tn;
+  w8a8_tile(id - slice * per, tiles_m, tiles_n, tm, tn);
+  const int s0 = SPLIT ? slice * p.kseg : 0;
+  const int s1 = SPLIT ? min(nsteps, s0 + p.kseg) : nsteps;
+  const int row_lo = tm * Cfg::BM, row_last = min(p.M, row_lo + Cfg::BM) - 1;
+  const int col_lo = tn * Cfg::BN, col_last = min(p.N, col_lo + Cfg::BN) - 1;
+
+  constexpr int kRsrcFlags = 0x00020000;
+  const auto rA = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(p.A), 0,
+                                                    static_cast<int>(static_cast<uint32_t>(p.M) * static_cast<uint32_t>(K)), kRsrcFlags);
+  const auto rB = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(p.B), 0,
+                                                    static_cast<int>(static_cast<uint32_t>(p.N) * static_cast<uint32_t>(K)), kRsrcFlags);
+
+  // Slot q = (wave * X_DMA + i) * 64 + lane of a stage is row q / 8, placed
+  // chunk q % 8, holding the row's chunk (q % 8) ^ ((row / 2) % 8).
+  uint32_t a_voff[Cfg::A_DMA], b_voff[Cfg::B_DMA];
+#pragma unroll
+  for (int i = 0; i < Cfg::A_DMA; ++i) {
+    const int q = (wave * Cfg::A_DMA + i) * 64 + lane;
+    const int r = q >> 3, c = (q & 7) ^ ((r >> 1) & 7);
+    a_voff[i] = static_cast<uint32_t>(min(row_lo + r, row_last)) * static_cast<uint32_t>(K) + c * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < Cfg::B_DMA; ++i) {
+    const int q = (wave * Cfg::B_DMA + i) * 64 + lane;
+    const int r = q >> 3, c = (q & 7) ^ ((r >> 1) & 7);
+    b_voff[i] = static_cast<uint32_t>(min(col_lo + r, col_last)) * static_cast<uint32_t>(K) + c * 16;
+  }
+  auto issue = [&](int step, int st) {
+    char *da = a_st[st] + wave * Cfg::A_DMA * 1024;
+    char *db = b_st[st] + wave * Cfg::B_DMA * 1024;
+#pragma unroll
+    for (int i = 0; i < Cfg::A_DMA; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rA, (__attribute__((address_space(3))) void *)(da + i * 1024), 16, a_voff[i], step * 128, 0, 0);
+#pragma unroll
+    for (int i = 0; i < Cfg::B_DMA; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rB, (__attribute__((address_space(3))) void *)(db + i * 1024), 16, b_voff[i], step * 128, 0, 0);
+  };
+
+  // Fragments: sub-step ks covers k bytes 32 ks .. 32 ks + 31; lane reads
+  // row (wave tile row + 32 i + lane % 32), chunk 2 ks + lane / 32, placed at
+  // that ^ ((lane / 2) % 8) (32 i and the wave tile leave (row / 2) % 8
+  // unchanged).  The two operands read the same k bytes per lane, so the
+  // instruction's k order within a fragment does not matter.
+  const int khalf = lane >> 5;
+  const int g = khalf ^ ((lane >> 1) & 7);
+  int a_addr[4], b_addr[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    a_addr[ks] = (wm * Cfg::WTM + (lane & 31)) * 128 + (((2 * ks) ^ g) << 4);
+    b_addr[ks] = (wn * Cfg::WTN + (lane & 31)) * 128 + (((2 * ks) ^ g) << 4);
+  }
+  struct Frags {
+    i32x4 a[TM], b[TN];
+  };
+  auto fread = [&](const char *As, const char *Bs, int ks, Frags &f) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) f.a[i] = *reinterpret_cast<const i32x4 *>(As + a_addr[ks] + 4096 * i);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) f.b[j] = *reinterpret_cast<const i32x4 *>(Bs + b_addr[ks] + 4096 * j);
+  };
+
+  // Weights as the row operand, activations as the column operand: acc[i][j]
+  // holds C^T, a lane one row of C (32 i + lane % 32) and 16 of its columns,
+  // four consecutive ones per group of four values.
+  i32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
+  auto mma = [&](const Frags &f) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+  };
+  auto barrier = [] {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  constexpr int WAIT_ALL = 7 << 4;   // vmcnt(0) lgkmcnt(0)
+
+  // Step s on stage I: issue step s + 1 into the other stage (last read in
+  // step s - 1, before the barrier that ended it), run the four sub-steps,
+  // wait for this wave's loads, meet the other waves.
+  auto body = [&](auto Ic, int step) {
+    constexpr int I = decltype(Ic)::value;
+    if (step + 1 < s1) issue(step + 1, 1 - I);
+    __builtin_amdgcn_sched_barrier(0);
+    const char *As = a_st[I], *Bs = b_st[I];
+    Frags f0, f1;
+    fread(As, Bs, 0, f0);
+    fread(As, Bs, 1, f1);
+    mma(f0);
+    fread(As, Bs, 2, f0);
+    mma(f1);
+    fread(As, Bs, 3, f1);
+    mma(f0);
+    mma(f1);
+    // Fragment reads one sub-step ahead of the matrix instructions.
+    constexpr int NR = TM + TN, NM = TM * TN;
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * NR, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(WAIT_ALL);
+    barrier();
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+
+  issue(s0, 0);
+  __builtin_amdgcn_s_waitcnt(WAIT_ALL);
+  barrier();
+  int step = s0;
+  for (; step + 2 <= s1; step += 2) {
+    body(I0{}, step);
+    body(I1{}, step + 1);
+  }
+  if (step < s1) body(I0{}, step);
+
+  // Epilogue: value v of acc[i][j] is C[row][col], row = wave tile row +
+  // 32 i + lane % 32, col = wave tile column + 32 j + 8 (v / 4) +
+  // 4 (lane / 32) + v % 4.  The column scales of this lane's 16 columns are
+  // read once (clamped to the last column; columns past it are not stored).
+  [[maybe_unused]] float cs[TN][4][4];
+  if constexpr (!SPLIT) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int col = min(col_lo + wn * Cfg::WTN + 32 * j + 8 * q + 4 * khalf + e, col_last);
+          cs[j][q][e] = p.acol[p.per_channel ? col : 0];
+        }
+  }
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int r = row_lo + wm * Cfg::WTM + 32 * i + (lane & 31);
+    if (r > row_last) continue;
+    if constexpr (SPLIT) {
+      int32_t *dst = p.part + static_cast<size_t>(slice) * p.M * p.N + static_cast<size_t>(r) * p.N;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = col_lo + wn * Cfg::WTN + 32 * j + 8 * q + 4 * khalf;
+          if (col <= col_last)
+            *reinterpret_cast<i32x4 *>(dst + col) =
+                i32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        }
+    } else {
+      const float ar = p.arow[p.per_token ? r : 0];
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = col_lo + wn * Cfg::WTN + 32 * j + 8 * q + 4 * khalf;
+          if (col > col_last) continue;
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = static_cast<float>(acc[i][j][4 * q + e]) * ar * cs[j][q][e];
+          store4<OUT>(p.C, static_cast<size_t>(r) * p.N + col, v);
+        }
+    }
+  }
+}
+
+template <class Cfg, int OUT, bool SPLIT>
+__global__ __launch_bounds__(Cfg::NTHR) void k_w8a8(W8A8Problem p, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(16))) char a_st[2][Cfg::BM * 128];
+  __shared__ __attribute__((aligned(16))) char b_st[2][Cfg::BN * 128];
+  w8a8_tile_gemm<Cfg, OUT, SPLIT>(p, tiles_m, tiles_n, a_st, b_st);
+}
+
+// Split-K: C = RNE_out(float(sum of the slices' int32 partials) * scales);
+// the integer sum is exact, so the slice order does not matter.
+template <int OUT>
+__global__ __launch_bounds__(256) void k_w8a8_reduce(W8A8Problem p, int nsplit) {
+  const long long q = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const size_t mn = static_cast<size_t>(p.M) * p.N;
+  if (q >= static_cast<long long>(mn / 4)) return;
+  i32x4 s = *reinterpret_cast<const i32x4 *>(p.part + 4 * q);
+  for (int sl = 1; sl < nsplit; ++sl) s += *reinterpret_cast<const i32x4 *>(p.part + sl * mn + 4 * q);
+  const int r = static_cast<int>((4 * q) / p.N), col = static_cast<int>((4 * q) % p.N);
+  const float ar = p.arow[p.per_token ? r : 0];
+  float v[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = static_cast<float>(s[e]) * ar * p.acol[p.per_channel ? col + e : 0];
+  store4<OUT>(p.C, 4 * q, v);
+}
+
+namespace {
+
+using T256x256 = W8Cfg<256, 256, 2, 4>;   // waves of 128 x 64
+using T256x128 = W8Cfg<256, 128, 4, 2>;   // waves of 64 x 64
+using T128x128 = W8Cfg<128, 128, 2, 4>;   // waves of 64 x 32
+using T64x128 = W8Cfg<64, 128, 2, 4>;     // waves of 32 x 32
+enum { kT256, kT256N, kT128, kT64 };
+
+struct W8A8Plan {
+  int tile;
+  int kseg, nsplit;
+  size_t bytes;   // int32 partials of a split plan
+};
+
+int tiles_of(int M, int N, int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); }
+
+// Tile by problem size: the largest tile that still gives most CUs work,
+// then K slices when even the smallest tile leaves the chip mostly idle
+// (decode-sized M), each slice at least two steps.
+W8A8Plan plan_w8a8(int M, int N, int K) {
+  W8A8Plan pl{kT64, 0, 1, 0};
+  if (M > 128 && tiles_of(M, N, 256, 256) >= 192) pl.tile = kT256;
+  else if (M > 128 && tiles_of(M, N, 256, 128) >= 192) pl.tile = kT256N;
+  else if (M > 64 && tiles_of(M, N, 128, 128) >= 128) pl.tile = kT128;
+  else pl.tile = kT64;
+  const int bm = pl.tile == kT64 ? 64 : pl.tile == kT128 ? 128 : 256;
+  const int bn = pl.tile == kT256 ? 256 : 128;
+  const int tiles = tiles_of(M, N, bm, bn), nsteps = K / 128;
+  if (tiles < 128 && nsteps >= 4) {
+    int want = (512 + tiles - 1) / tiles;
+    want = std::min(want, std::min(nsteps / 2, 16));
+    if (want >= 2) {
+      const int kseg = (nsteps + want - 1) / want;
+      pl.kseg = kseg;
+      pl.nsplit = (nsteps + kseg - 1) / kseg;
+      pl.bytes = static_cast<size_t>(pl.nsplit) * M * N * sizeof(int32_t);
+    }
+  }
+  return pl;
+}
+
+template <class Cfg, int OUT>
+hipError_t run_w8a8(W8A8Problem p, const W8A8Plan &pl, hipStream_t s) {
+  const int tm = (p.M + Cfg::BM - 1) / Cfg::BM, tn = (p.N + Cfg::BN - 1) / Cfg::BN;
+  if (p.part) {
+    hipLaunchKernelGGL((k_w8a8<Cfg, OUT, true>), dim3(tm * tn * pl.nsplit), dim3(Cfg::NTHR), 0, s, p, tm, tn);
+    const long long q = static_cast<long long>(p.M) * p.N / 4;
+    hipLaunchKernelGGL(k_w8a8_reduce<OUT>, dim3(static_cast<unsigned>((q + 255) / 256)), dim3(256), 0, s,
+                       p, pl.nsplit);
+  } else {
+    hipLaunchKernelGGL((k_w8a8<Cfg, OUT, false>), dim3(tm * tn), dim3(Cfg::NTHR), 0, s, p, tm, tn);
+  }
+  return hipGetLastError();
+}
+
+template <int OUT>
+hipError_t dispatch_w8a8(W8A8Problem p, const W8A8Plan &pl, hipStream_t s) {
+  switch (pl.tile) {
+    case kT256: return run_w8a8<T256x256, OUT>(p, pl, s);
+    case kT256N: return run_w8a8<T256x128, OUT>(p, pl, s);
+    case kT128: return run_w8a8<T128x128, OUT>(p, pl, s);
+    default: return run_w8a8<T64x128, OUT>(p, pl, s);
+  }
+}
+
+}  // namespace
+
+size_t w8a8_workspace_bytes(int m, int n, int k) {
+  const W8A8Plan pl = plan_w8a8(m, n, k);
+  return pl.nsplit > 1 ? pl.bytes : 0;
+}
+
+hipError_t launch_w8a8(const W8A8Args &a, hipStream_t s) {
+  W8A8Plan pl = plan_w8a8(a.M, a.N, a.K);
+  W8A8Problem p{a.A, a.B, a.alpha_row, a.alpha_col, a.C, nullptr, a.M, a.N, a.K, a.per_token,
+                a.per_channel, 0};
+  if (pl.nsplit > 1 && a.ws && a.ws_bytes >= pl.bytes) {
+    p.part = static_cast<int32_t *>(a.ws);
+    p.kseg = pl.kseg;
+  } else {
+    pl.nsplit = 1;
+  }
+  if (const char *o = std::getenv("QGEMM_W8A8_TILE")) {   // tests and tuning
+    const int t = std::atoi(o);
+    if (t >= kT256 && t <= kT64) pl.tile = t;
+  }
+  switch (a.out) {
+    case QG_FP32: return dispatch_w8a8<QG_FP32>(p, pl, s);
+    case QG_FP16: return dispatch_w8a8<QG_FP16>(p, pl, s);
+    default: return dispatch_w8a8<QG_BF16>(p, pl, s);
+  }
+}
+
+}  // namespace qg
