@@ -233,12 +233,13 @@ def test_w8a8_validation(kw, status):
 
 def test_w8a8_modes_and_workspace_query():
     # The four modes are 0..3 (weights per channel = 1, activations per
-    # token = 2); a decode-sized problem asks for split-K partials, a large one
-    # for none, invalid sizes for none.
+    # token = 2); a problem with few tiles asks for split-K partials, decode
+    # (m <= 16) and large problems for none, invalid sizes for none.
     L = qg.lib()
     assert (_abi.QG_W8A8_PER_TENSOR, _abi.QG_W8A8_PER_CHANNEL, _abi.QG_W8A8_PER_TOKEN) == (0, 1, 2)
-    assert L.qgemm_w8a8_workspace_size(1, 3584, 3584) > 0
-    assert L.qgemm_w8a8_workspace_size(1, 3584, 3584) % 256 == 0
+    assert L.qgemm_w8a8_workspace_size(64, 3584, 3584) > 0
+    assert L.qgemm_w8a8_workspace_size(64, 3584, 3584) % 256 == 0
+    assert L.qgemm_w8a8_workspace_size(1, 3584, 3584) == 0     # streaming decode kernel
     assert L.qgemm_w8a8_workspace_size(4096, 18944, 3584) == 0
     assert L.qgemm_w8a8_workspace_size(0, 3584, 3584) == 0
     assert L.qgemm_w8a8_workspace_size(1, 3584, 3500) == 0

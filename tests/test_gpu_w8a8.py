@@ -59,10 +59,30 @@ def test_w8a8_integer_sums_bit_exact(monkeypatch, tile, m, n, k):
     assert np.array_equal(C, acc.astype(np.float64))
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 3584, 3584), (16, 3584, 1024), (3, 1040, 2048)])
-def test_w8a8_split_k_equals_unsplit_bitwise(m, n, k):
-    # Decode-sized problems are split along K into int32 partials; integer
-    # sums are exact in any order, so split and unsplit agree bit for bit.
+@pytest.mark.parametrize("m,n,k", [(1, 16, 128), (1, 528, 384), (5, 144, 1024), (16, 8192, 896), (1, 8192, 768),
+                                   (9, 3584, 3584), (16, 18944, 1024)])
+def test_w8a8_decode_kernel_bit_exact(m, n, k):
+    # m <= 16 runs the streaming decode kernel (one or two 16-channel tiles
+    # per workgroup, waves over 128-k chunks); unit and power-of-two scales
+    # keep the fp32 output exact.
+    p = si.w8a8_problem(m, n, k, False, False, scales=[1.0])
+    acc, _ = ref(p)
+    if np.abs(acc).max() < 2 ** 24:
+        assert np.array_equal(run(p), acc.astype(np.float64))
+    for pt, pc in ((0, 1), (1, 0), (1, 1)):
+        p = si.w8a8_problem(m, n, k, bool(pt), bool(pc), scales=[0.25, 0.5, 1.0, 2.0],
+                            code_range=(-64, 64))
+        _, Cref = ref(p)
+        if np.abs(Cref).max() < 2 ** 24 / 8:
+            assert np.array_equal(run(p), Cref)
+
+
+@pytest.mark.parametrize("m,n,k", [(64, 3584, 3584), (32, 3584, 1024), (40, 1040, 2048)])
+def test_w8a8_split_k_equals_unsplit_bitwise(monkeypatch, m, n, k):
+    # Problems with few 64 x 128 tiles are split along K into int32 partials;
+    # integer sums are exact in any order, so split and unsplit agree bit for
+    # bit.
+    monkeypatch.setenv("QGEMM_W8A8_TILE", "3")
     assert qg.w8a8_workspace_size(m, n, k) > 0
     p = si.w8a8_problem(m, n, k, True, True)
     assert np.array_equal(run(p, "fp32", True), run(p, "fp32", False))

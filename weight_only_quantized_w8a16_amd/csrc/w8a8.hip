@@ -306,6 +306,71 @@ __global__ __launch_bounds__(256) void k_w8a8_reduce(W8A8Problem p, int nsplit) 
   store4<OUT>(p.C, 4 * q, v);
 }
 
+// ---------------------------------------------------------------------------
+// Decode-sized problems (m <= 16): the weights are streamed once, so the
+// kernel is bound by HBM, not by the matrix cores.  A workgroup owns NT tiles
+// of 16 output channels over all of K; its waves take KC-byte chunks of K in
+// turn.  Within a chunk, lane (nl = lane % 16, j = lane / 16) loads the
+// 16-byte pieces at k = 64 t + 16 j (t < KC / 64) of weight row nl -- so one
+// load instruction reads 64 contiguous bytes of each of 16 rows -- and the
+// same pieces of activation row nl (zero for rows >= m), and feeds piece t of
+// both to the t-th v_mfma_i32_16x16x64_i8, the weights as the row operand.
+// Both operands use the same k bytes per lane, so the k order inside a
+// fragment does not matter.  The waves' int32 sums meet in LDS (exact), then
+// one pass scales and stores.
+// ---------------------------------------------------------------------------
+template <int OUT, int NT, int KC>
+__global__ __launch_bounds__(512) void k_w8a8_decode(W8A8Problem p) {
+  extern __shared__ int red[];   // [waves][NT][256]
+  constexpr int NP = KC / 64;    // pieces per lane per chunk
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  const int nl = lane & 15, j = lane >> 4;
+  const int K = p.K, nchunks = K / KC;
+  const int nt0 = blockIdx.x * NT;
+  const bool live = nl < p.M;
+  const int8_t *arow = p.A + static_cast<size_t>(live ? nl : 0) * K + 16 * j;
+  i32x4 acc[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) acc[i] = i32x4{0, 0, 0, 0};
+  for (int c = wave; c < nchunks; c += nwaves) {
+    const int k0 = c * KC;
+    i32x4 w[NT][NP];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const i32x4 *src = reinterpret_cast<const i32x4 *>(
+          p.B + static_cast<size_t>((nt0 + i) * 16 + nl) * K + k0 + 16 * j);
+#pragma unroll
+      for (int t = 0; t < NP; ++t) w[i][t] = src[4 * t];
+    }
+    i32x4 a[NP];
+#pragma unroll
+    for (int t = 0; t < NP; ++t)
+      a[t] = live ? *reinterpret_cast<const i32x4 *>(arow + k0 + 64 * t) : i32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int t = 0; t < NP; ++t) acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w[i][t], a[t], acc[i], 0, 0, 0);
+  }
+  // acc[i][r] of lane l is the sum for activation row l % 16 and channel
+  // 16 (nt0 + i) + 4 (l / 16) + r.
+#pragma unroll
+  for (int i = 0; i < NT; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[(wave * NT + i) * 256 + r * 64 + lane] = acc[i][r];
+  __syncthreads();
+  for (int e = threadIdx.x; e < NT * 256; e += blockDim.x) {
+    const int i = e >> 8, r = (e >> 6) & 3, l = e & 63;
+    const int m = l & 15;
+    if (m >= p.M) continue;
+    int sum = 0;
+    for (int w = 0; w < nwaves; ++w) sum += red[w * NT * 256 + e];
+    const int n = (nt0 + i) * 16 + 4 * (l >> 4) + r;
+    const float v = static_cast<float>(sum) * p.arow[p.per_token ? m : 0] * p.acol[p.per_channel ? n : 0];
+    if constexpr (OUT == QG_FP32) static_cast<float *>(p.C)[static_cast<size_t>(m) * p.N + n] = v;
+    else static_cast<uint16_t *>(p.C)[static_cast<size_t>(m) * p.N + n] = f32_to_bits<OUT>(v);
+  }
+}
+
 namespace {
 
 using T256x256 = W8Cfg<256, 256, 2, 4>;   // waves of 128 x 64
@@ -323,8 +388,11 @@ struct W8A8Plan {
 int tiles_of(int M, int N, int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); }
 
 // Tile by problem size: the largest tile that still gives most CUs work,
-// then K slices when even the smallest tile leaves the chip mostly idle
-// (decode-sized M), each slice at least two steps.
+// then K slices when even the smallest tile leaves the chip mostly idle,
+// enough for about one workgroup per CU, each slice at least two steps
+// (measured at K = 3584, m = 128, n = 3584: 56 tiles, 4-5 slices 15 us,
+// unsplit 28 us, 8-10 slices 18-21 us).  QGEMM_W8A8_SPLIT=<n> asks for n
+// slices (tests and tuning).
 W8A8Plan plan_w8a8(int M, int N, int K) {
   W8A8Plan pl{kT64, 0, 1, 0};
   if (M > 128 && tiles_of(M, N, 256, 256) >= 192) pl.tile = kT256;
@@ -334,9 +402,10 @@ W8A8Plan plan_w8a8(int M, int N, int K) {
   const int bm = pl.tile == kT64 ? 64 : pl.tile == kT128 ? 128 : 256;
   const int bn = pl.tile == kT256 ? 256 : 128;
   const int tiles = tiles_of(M, N, bm, bn), nsteps = K / 128;
-  if (tiles < 128 && nsteps >= 4) {
-    int want = (512 + tiles - 1) / tiles;
-    want = std::min(want, std::min(nsteps / 2, 16));
+  int want = 1;
+  if (tiles < 128 && nsteps >= 4) want = std::min((256 + tiles - 1) / tiles, std::min(nsteps / 2, 16));
+  if (const char *o = std::getenv("QGEMM_W8A8_SPLIT")) want = std::min(std::atoi(o), nsteps);   // tuning
+  {
     if (want >= 2) {
       const int kseg = (nsteps + want - 1) / want;
       pl.kseg = kseg;
@@ -373,15 +442,47 @@ hipError_t dispatch_w8a8(W8A8Problem p, const W8A8Plan &pl, hipStream_t s) {
 
 }  // namespace
 
+// Decode kernel for m <= 16 unless a tile is forced (tests and tuning).
+bool w8a8_use_decode(int m) {
+  if (std::getenv("QGEMM_W8A8_TILE")) return false;
+  return m <= 16;
+}
+
 size_t w8a8_workspace_bytes(int m, int n, int k) {
+  if (w8a8_use_decode(m)) return 0;
   const W8A8Plan pl = plan_w8a8(m, n, k);
   return pl.nsplit > 1 ? pl.bytes : 0;
+}
+
+// Two tiles per workgroup and 256-k chunks once there are many channel tiles
+// (more bytes in flight per wave); measured on MI355X at K = 3584: N = 18944,
+// m = 1: 23 -> 16 us against one tile and 128-k chunks read as 32 contiguous
+// bytes per lane (half-line loads), N = 3584 unchanged within noise.
+template <int OUT>
+hipError_t launch_w8a8_decode(const W8A8Problem &p, hipStream_t s) {
+  const int ntiles = p.N >> 4;
+  const bool wide = ntiles >= 512 && ntiles % 2 == 0 && p.K % 256 == 0;
+  const int nchunks = wide ? p.K >> 8 : p.K >> 7;
+  const int waves = nchunks < 8 ? nchunks : 8;
+  const size_t lds = static_cast<size_t>(waves) * (wide ? 2 : 1) * 256 * sizeof(int);
+  if (wide)
+    hipLaunchKernelGGL((k_w8a8_decode<OUT, 2, 256>), dim3(ntiles / 2), dim3(64 * waves), lds, s, p);
+  else
+    hipLaunchKernelGGL((k_w8a8_decode<OUT, 1, 128>), dim3(ntiles), dim3(64 * waves), lds, s, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_w8a8(const W8A8Args &a, hipStream_t s) {
   W8A8Plan pl = plan_w8a8(a.M, a.N, a.K);
   W8A8Problem p{a.A, a.B, a.alpha_row, a.alpha_col, a.C, nullptr, a.M, a.N, a.K, a.per_token,
                 a.per_channel, 0};
+  if (w8a8_use_decode(a.M)) {
+    switch (a.out) {
+      case QG_FP32: return launch_w8a8_decode<QG_FP32>(p, s);
+      case QG_FP16: return launch_w8a8_decode<QG_FP16>(p, s);
+      default: return launch_w8a8_decode<QG_BF16>(p, s);
+    }
+  }
   if (pl.nsplit > 1 && a.ws && a.ws_bytes >= pl.bytes) {
     p.part = static_cast<int32_t *>(a.ws);
     p.kseg = pl.kseg;
