@@ -252,6 +252,42 @@ void qref_dequant8(const int8_t *codes, const uint16_t *scale, int64_t n, int64_
 }
 
 /* ---------------------------------------------------------------------- */
+/* Embedding lookup  [cpuint4] CPUInt4EmbeddingMethod.embedding: gather the */
+/* rows of the quantized vocab table named by the token ids, dequantize     */
+/* them in fp32 with the same rule as the linear layers (the table is the   */
+/* tied output head), and hand them on in the activation dtype.  Here the   */
+/* fp32 rows are written; rounding to the 16-bit dtype is qref_f32_to_*.    */
+/* Ids outside [0, vocab) have no row in the page's definition; this oracle */
+/* gives them a row of zeros.                                               */
+/* ---------------------------------------------------------------------- */
+void qref_embed4(const int32_t *ids, int64_t tokens, const uint8_t *packed, const uint16_t *scale,
+                 const uint16_t *zero, int64_t vocab, int64_t hidden, int64_t group, int dtype,
+                 float *out)
+{
+    for (int64_t t = 0; t < tokens; ++t) {
+        float *o = out + t * hidden;
+        if (ids[t] < 0 || ids[t] >= vocab) {
+            for (int64_t c = 0; c < hidden; ++c) o[c] = 0.0f;
+            continue;
+        }
+        dequant4_row(packed, scale, zero, ids[t], hidden, group, dtype, o);
+    }
+}
+
+void qref_embed8(const int32_t *ids, int64_t tokens, const int8_t *codes, const uint16_t *scale,
+                 int64_t vocab, int64_t hidden, int64_t group, int dtype, float *out)
+{
+    for (int64_t t = 0; t < tokens; ++t) {
+        float *o = out + t * hidden;
+        if (ids[t] < 0 || ids[t] >= vocab) {
+            for (int64_t c = 0; c < hidden; ++c) o[c] = 0.0f;
+            continue;
+        }
+        dequant8_row(codes, scale, ids[t], hidden, group, dtype, o);
+    }
+}
+
+/* ---------------------------------------------------------------------- */
 /* GEMM  C[m, n] = sum_k A[m, k] * W[n, k] (+ bias[n])   [acext] 1.2.1,    */
 /* bias after the product [cpuint4] CPUInt4LinearMethod.apply.  Double      */
 /* accumulation, result left unrounded in double.                           */

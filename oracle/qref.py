@@ -24,7 +24,7 @@ import numpy as np
 __all__ = [
     "NONE", "BF16", "FP16", "build", "lib", "bf16_to_f32", "f16_to_f32", "f32_to_bf16",
     "f32_to_f16", "pack4", "unpack4", "quantize4", "dequant4", "dequant8", "gemm_w4", "gemm_w8",
-    "gemm_w4_at", "gemm_w8_at", "gemm_w8a8", "moe_route", "moe", "threads",
+    "gemm_w4_at", "gemm_w8_at", "gemm_w8a8", "moe_route", "moe", "threads", "embed4", "embed8",
 ]
 
 NONE, BF16, FP16 = 0, 1, 2
@@ -71,6 +71,8 @@ _SIGS = {
     "qref_gemm_w8": (None, [_P, _P, _P, _P, _I, _I, _I, _I, _INT, _INT, _P]),
     "qref_gemm_w4_at": (None, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _INT, _INT, _P, _P, _I, _P]),
     "qref_gemm_w8_at": (None, [_P, _P, _P, _P, _I, _I, _I, _I, _INT, _INT, _P, _P, _I, _P]),
+    "qref_embed4": (None, [_P, _I, _P, _P, _P, _I, _I, _I, _INT, _P]),
+    "qref_embed8": (None, [_P, _I, _P, _P, _I, _I, _I, _INT, _P]),
     "qref_gemm_w8a8": (None, [_P, _P, _P, _INT, _P, _INT, _I, _I, _I, _P, _P]),
     "qref_moe_route": (None, [_P, _I, _I, _I, _P, _P]),
     "qref_moe": (None, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _INT,
@@ -197,6 +199,31 @@ def dequant8(codes, scale, group=-1, dtype=FP16):
     s = _c(scale, np.uint16)
     out = np.empty((n, k), dtype=np.float32)
     lib().qref_dequant8(_ptr(q), _ptr(s), n, k, group, dtype, _ptr(out))
+    return out
+
+
+def embed4(ids, packed, scale, zero, group, dtype=BF16):
+    """fp32 [T, hidden]: row ids[t] of the int4 table (portable [vocab,
+    hidden/2] codes), dequantized; rows of zeros for ids outside the table."""
+    i = _c(np.asarray(ids).reshape(-1), np.int32)
+    p = _c(packed, np.uint8)
+    vocab, half = p.shape
+    hidden = half * 2
+    out = np.empty((i.size, hidden), dtype=np.float32)
+    lib().qref_embed4(_ptr(i), i.size, _ptr(p), _ptr(_c(scale, np.uint16)), _ptr(_c(zero, np.uint16)),
+                      vocab, hidden, group, dtype, _ptr(out))
+    return out
+
+
+def embed8(ids, codes, scale, group=-1, dtype=FP16):
+    """fp32 [T, hidden]: row ids[t] of the int8 table [vocab, hidden],
+    dequantized; rows of zeros for ids outside the table."""
+    i = _c(np.asarray(ids).reshape(-1), np.int32)
+    q = _c(codes, np.int8)
+    vocab, hidden = q.shape
+    out = np.empty((i.size, hidden), dtype=np.float32)
+    lib().qref_embed8(_ptr(i), i.size, _ptr(q), _ptr(_c(scale, np.uint16)), vocab, hidden, group,
+                      dtype, _ptr(out))
     return out
 
 

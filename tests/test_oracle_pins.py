@@ -108,6 +108,29 @@ def test_e1_dequant_and_gemm(golden_dir):
     assert W16.tolist() == e["W"]
 
 
+def test_e1_embedding_rows(golden_dir):
+    # [cpuint4] CPUInt4EmbeddingMethod.embedding: a token's row of the
+    # quantized table, dequantized.  With E1's table the rows are E1's W;
+    # ids outside the table give zeros (this oracle's reading).
+    e = load(golden_dir, "e1_w4_groupwise.json")
+    packed = np.array(e["packed"], dtype=np.uint8)
+    s, z = bf16_bits(e["scale"]), bf16_bits(e["zero"])
+    out = oracle.embed4([1, 0, 1, -1, 2], packed, s, z, e["group"], BF16)
+    W, zero_row = e["W"], [0.0] * e["k"]
+    assert out.tolist() == [W[1], W[0], W[1], zero_row, zero_row]
+    # scale-only (no zeros) rows: (q - 8) * s by hand from E1's codes
+    q, sc = np.array(e["codes"]), np.array(e["scale"])
+    hand = (q - 8) * np.repeat(sc, e["group"], axis=1)
+    assert oracle.embed4([0, 1], packed, s, None, e["group"], BF16).tolist() == hand.tolist()
+
+
+def test_e2_embedding_rows(golden_dir):
+    e = load(golden_dir, "e2_w8_perchannel.json")
+    codes = np.array(e["codes"], dtype=np.int8)
+    out = oracle.embed8([1, 1, 0, 5], codes, f16_bits(e["scale"]), -1, FP16)
+    assert out.tolist() == [e["W"][1], e["W"][1], e["W"][0], [0.0] * codes.shape[1]]
+
+
 def test_e2_w8_dequant_and_gemm(golden_dir):
     e = load(golden_dir, "e2_w8_perchannel.json")
     codes = np.array(e["codes"], dtype=np.int8)
