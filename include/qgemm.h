@@ -61,7 +61,7 @@ typedef enum {
     QG_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required */
     QG_ERR_UNSUPPORTED = 7, /* valid, but outside the tile multiples listed per call */
     QG_ERR_HIP = 8,         /* the HIP runtime rejected a launch */
-    QG_ERR_MODE = 9         /* W8A8 quant mode outside the four variants */
+    QG_ERR_MODE = 9         /* a mode argument (W8A8 quant mode, table layout) outside its values */
 } qg_status;
 
 typedef enum { QG_NONE = 0, QG_BF16 = 1, QG_FP16 = 2, QG_FP32 = 3 } qg_dtype;
@@ -237,6 +237,35 @@ size_t qgemm_w8a8_workspace_size(int m, int n, int k);
 qg_status qgemm_w8a8(const int8_t *A, const int8_t *B, int quant_mode, const float *alpha_col,
                      const float *alpha_row, void *C, int m, int n, int k, qg_dtype out_dtype,
                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Quantized embedding lookup (vllm-omni cpu_int4.py, CPUInt4EmbeddingMethod:
+ * with tied embeddings the vocab table is the quantized output head; a lookup
+ * gathers the token's row, dequantizes it in fp32 with the linear layers'
+ * rule and casts it to the activation dtype).
+ *   out[t, :] = RNE_out( dequant(table)[ids[t], :] ),  a row of zeros when
+ *   ids[t] is outside [0, vocab)
+ * with the fp32 values of qdequant_w4 / qdequant_w8 (bit-exact by contract).
+ *   ids     device int32 [tokens]
+ *   table   device codes of the [vocab, hidden] table in `layout`:
+ *           QG_LAYOUT_TILED (1), the qrepack_w4 / qrepack_w8 output that
+ *           qgemm_w4a16 / qgemm_w8a16 read as the lm_head weight (one copy
+ *           serves both), or QG_LAYOUT_PORTABLE (0), the portable layout
+ *   scales, zeros  as for the GEMM of the same table (zeros optional, int4)
+ *   out     device [tokens, hidden] in out_dtype (QG_FP32 or act_dtype)
+ *   group_size: int4 64, 128, -1 (= hidden); int8 -1 (= hidden), 64, 128.
+ *   Requires vocab >= 1, hidden % 8 == 0, and for the tiled layout the
+ *   repack's multiples (vocab % 16, hidden % 128 for int4 or % 64 for int8).
+ *   Alignment: ids 4 bytes, table and out 16, scales and zeros 2.
+ * ---------------------------------------------------------------------- */
+enum { QG_LAYOUT_PORTABLE = 0, QG_LAYOUT_TILED = 1 };
+
+qg_status qembed_w4(const int32_t *ids, int tokens, const uint8_t *table, int layout,
+                    const void *scales, const void *zeros, void *out, int vocab, int hidden,
+                    int group_size, qg_dtype act_dtype, qg_dtype out_dtype, void *stream);
+qg_status qembed_w8(const int32_t *ids, int tokens, const int8_t *table, int layout,
+                    const void *scales, void *out, int vocab, int hidden, int group_size,
+                    qg_dtype act_dtype, qg_dtype out_dtype, void *stream);
 
 /* ------------------------------------------------------------------------
  * Top-k MoE with SiLU-gated int4 experts  (acext User Guide (v1.7), 1.2.3

@@ -243,3 +243,53 @@ def test_w8a8_modes_and_workspace_query():
     assert L.qgemm_w8a8_workspace_size(4096, 18944, 3584) == 0
     assert L.qgemm_w8a8_workspace_size(0, 3584, 3584) == 0
     assert L.qgemm_w8a8_workspace_size(1, 3584, 3500) == 0
+
+
+# -- embedding lookup ---------------------------------------------------------------
+
+def emb4(**kw):
+    a = dict(ids=FAKE, T=8, tab=FAKE, layout=1, s=FAKE, z=FAKE, out=FAKE, vocab=256, hidden=256,
+             g=64, act=BF16, odt=BF16)
+    a.update(kw)
+    return qg.lib().qembed_w4(a["ids"], a["T"], a["tab"], a["layout"], a["s"], a["z"], a["out"],
+                              a["vocab"], a["hidden"], a["g"], a["act"], a["odt"], None)
+
+
+def emb8(**kw):
+    a = dict(ids=FAKE, T=8, tab=FAKE, layout=1, s=FAKE, out=FAKE, vocab=256, hidden=256, g=-1,
+             act=FP16, odt=FP32)
+    a.update(kw)
+    return qg.lib().qembed_w8(a["ids"], a["T"], a["tab"], a["layout"], a["s"], a["out"], a["vocab"],
+                              a["hidden"], a["g"], a["act"], a["odt"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), SHAPE), (dict(vocab=0), SHAPE), (dict(hidden=0), SHAPE),
+    (dict(ids=None), NULL), (dict(tab=None), NULL), (dict(s=None), NULL), (dict(out=None), NULL),
+    (dict(act=FP32), DTYPE), (dict(odt=FP16), DTYPE), (dict(odt=0), DTYPE),
+    (dict(layout=2), 9), (dict(layout=-1), 9),
+    (dict(g=32), GROUP), (dict(hidden=320, g=128), GROUP),
+    (dict(vocab=24), UNSUP), (dict(hidden=192, g=64), UNSUP), (dict(layout=0, hidden=36, g=-1), UNSUP),
+    (dict(ids=FAKE + 2), ALIGN), (dict(tab=FAKE + 8), ALIGN), (dict(out=FAKE + 4), ALIGN),
+    (dict(s=FAKE + 1), ALIGN), (dict(z=FAKE + 1), ALIGN),
+    (dict(T=0), OK), (dict(T=0, ids=None), OK),
+])
+def test_embed_w4_validation(kw, status):
+    assert emb4(**kw) == status
+
+
+def test_embed_w4_zeros_optional_and_portable_multiples():
+    # zeros may be NULL (scale-only); the portable layout needs only
+    # hidden % 8 and no vocab multiple -- both stop at the (later) alignment
+    # check when the out pointer is misaligned, proving they passed the rest.
+    assert emb4(z=None, out=FAKE + 4) == ALIGN
+    assert emb4(layout=0, vocab=7, hidden=136, g=-1, out=FAKE + 4) == ALIGN
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-3), SHAPE), (dict(s=None), NULL), (dict(act=0), DTYPE), (dict(layout=5), 9),
+    (dict(g=96), GROUP), (dict(vocab=24), UNSUP), (dict(hidden=96, g=-1), UNSUP),
+    (dict(tab=FAKE + 4), ALIGN), (dict(T=0), OK),
+])
+def test_embed_w8_validation(kw, status):
+    assert emb8(**kw) == status

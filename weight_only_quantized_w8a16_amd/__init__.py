@@ -13,14 +13,14 @@ from typing import Optional
 
 import torch
 
-from ._abi import (QG_BF16, QG_FP16, QG_FP32, QG_NONE, QG_W8A8_PER_CHANNEL, QG_W8A8_PER_TOKEN,
-                   QGemmError, check, lib)
+from ._abi import (QG_BF16, QG_FP16, QG_FP32, QG_LAYOUT_PORTABLE, QG_LAYOUT_TILED, QG_NONE,
+                   QG_W8A8_PER_CHANNEL, QG_W8A8_PER_TOKEN, QGemmError, check, lib)
 
 __all__ = [
     "QGemmError", "lib", "repack_w4", "unrepack_w4", "repack_w8", "unrepack_w8", "repack_w8_kn",
     "unrepack_w8_kn", "quantize_w4", "dequant_w4", "dequant_w8", "gemm_w4a16", "gemm_w8a16",
     "moe_grouped", "moe_workspace_size", "gemm_workspace_size", "dtype_code", "gemm_w8a8",
-    "w8a8_workspace_size",
+    "w8a8_workspace_size", "embed_w4", "embed_w8",
 ]
 
 _CODES = {torch.bfloat16: QG_BF16, torch.float16: QG_FP16, torch.float32: QG_FP32}
@@ -271,6 +271,49 @@ def gemm_w8a8(A: torch.Tensor, B: torch.Tensor, alpha_row: torch.Tensor,
         _ptr(A2), _ptr(B), mode, _ptr(alpha_col), _ptr(alpha_row), _ptr(C), m, n, k,
         dtype_code(C.dtype), _ptr(ws), ws_bytes, _stream(A)))
     return C.reshape(*lead, n)
+
+
+# -- embedding lookup ----------------------------------------------------------
+
+def _embed_out(ids, hidden, act_dtype, out_dtype, device):
+    return torch.empty((*ids.shape, hidden), dtype=out_dtype or act_dtype, device=device)
+
+
+def embed_w4(ids: torch.Tensor, table: torch.Tensor, scales: torch.Tensor,
+             zeros: Optional[torch.Tensor], group_size: int, tiled: bool = True,
+             out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
+    """Rows ids of the int4 table, dequantized: [*ids.shape, hidden].  The
+    table is the tiled [vocab, hidden/2] GEMM weight (tiled=True) or the
+    portable one; scales (and zeros) set the activation dtype."""
+    for t, name in ((ids, "ids"), (table, "table"), (scales, "scales")):
+        _dev(t, name)
+    if zeros is not None:
+        _dev(zeros, "zeros")
+    if ids.dtype != torch.int32:
+        raise QGemmError("qembed_w4", 4, "ids must be int32")
+    vocab, hidden = table.shape[0], table.shape[1] * 2
+    out = _embed_out(ids, hidden, scales.dtype, out_dtype, table.device)
+    check("qembed_w4", lib().qembed_w4(
+        _ptr(ids), ids.numel(), _ptr(table), QG_LAYOUT_TILED if tiled else QG_LAYOUT_PORTABLE,
+        _ptr(scales), _ptr(zeros), _ptr(out), vocab, hidden, group_size, dtype_code(scales.dtype),
+        dtype_code(out.dtype), _stream(table)))
+    return out
+
+
+def embed_w8(ids: torch.Tensor, table: torch.Tensor, scales: torch.Tensor, group_size: int = -1,
+             tiled: bool = True, out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
+    """Rows ids of the int8 table [vocab, hidden], dequantized."""
+    for t, name in ((ids, "ids"), (table, "table"), (scales, "scales")):
+        _dev(t, name)
+    if ids.dtype != torch.int32:
+        raise QGemmError("qembed_w8", 4, "ids must be int32")
+    vocab, hidden = table.shape
+    out = _embed_out(ids, hidden, scales.dtype, out_dtype, table.device)
+    check("qembed_w8", lib().qembed_w8(
+        _ptr(ids), ids.numel(), _ptr(table), QG_LAYOUT_TILED if tiled else QG_LAYOUT_PORTABLE,
+        _ptr(scales), _ptr(out), vocab, hidden, group_size, dtype_code(scales.dtype),
+        dtype_code(out.dtype), _stream(table)))
+    return out
 
 
 # -- MoE -----------------------------------------------------------------------

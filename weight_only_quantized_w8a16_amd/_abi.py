@@ -21,6 +21,7 @@ STATUS_NAMES = {
 }
 QG_NONE, QG_BF16, QG_FP16, QG_FP32 = 0, 1, 2, 3
 QG_W8A8_PER_TENSOR, QG_W8A8_PER_CHANNEL, QG_W8A8_PER_TOKEN = 0, 1, 2
+QG_LAYOUT_PORTABLE, QG_LAYOUT_TILED = 0, 1
 
 _P = ctypes.c_void_p
 _INT = ctypes.c_int
@@ -45,6 +46,8 @@ SIGNATURES = {
     "qgemm_w8a16": (_ST, [_P, _P, _P, _P, _P, _INT, _INT, _INT, _INT, _INT, _INT, _P, _SZ, _P]),
     "qgemm_w8a8_workspace_size": (_SZ, [_INT, _INT, _INT]),
     "qgemm_w8a8": (_ST, [_P, _P, _INT, _P, _P, _P, _INT, _INT, _INT, _INT, _P, _SZ, _P]),
+    "qembed_w4": (_ST, [_P, _INT, _P, _INT, _P, _P, _P, _INT, _INT, _INT, _INT, _INT, _P]),
+    "qembed_w8": (_ST, [_P, _INT, _P, _INT, _P, _P, _INT, _INT, _INT, _INT, _INT, _P]),
     "qmoe_workspace_size": (_SZ, [_INT, _INT, _INT, _INT, _INT]),
     "qmoe_grouped": (_ST, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _INT, _INT, _INT, _INT, _INT, _INT,
                            _INT, _P, _P, _P, _SZ, _P]),

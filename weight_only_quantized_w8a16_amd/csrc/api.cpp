@@ -88,7 +88,7 @@ const char *qg_strerror(qg_status s) {
     case QG_ERR_WORKSPACE: return "workspace missing or too small";
     case QG_ERR_UNSUPPORTED: return "sizes outside the supported tile multiples";
     case QG_ERR_HIP: return "HIP runtime error at launch";
-    case QG_ERR_MODE: return "W8A8 quant mode is not one of the four variants";
+    case QG_ERR_MODE: return "mode argument (W8A8 quant mode, table layout) outside its values";
   }
   return "unknown status";
 }
@@ -287,6 +287,47 @@ qg_status qgemm_w8a8(const int8_t *A, const int8_t *B, int mode, const float *al
                  (mode & QG_W8A8_PER_TOKEN) ? 1 : 0, (mode & QG_W8A8_PER_CHANNEL) ? 1 : 0,
                  static_cast<int>(out), workspace, workspace ? ws_bytes : 0};
   return hip_status(qg::launch_w8a8(a, as_stream(stream)));
+}
+
+// ---------------------------------------------------------------------------
+// Embedding lookup
+// ---------------------------------------------------------------------------
+static qg_status embed(const int32_t *ids, int tokens, const void *table, int layout,
+                       const void *scales, const void *zeros, void *out, int vocab, int hidden,
+                       int group, qg_dtype act, qg_dtype out_dt, int bits, void *stream) {
+  if (tokens < 0 || vocab <= 0 || hidden <= 0) return QG_ERR_SHAPE;
+  if (tokens == 0) return QG_OK;   // nothing to look up; pointers unused
+  if (!ids || !table || !scales || !out) return QG_ERR_NULL;   // zeros optional (int4)
+  if (!act_ok(act) || !(out_dt == QG_FP32 || out_dt == act)) return QG_ERR_DTYPE;
+  if (layout != QG_LAYOUT_PORTABLE && layout != QG_LAYOUT_TILED) return QG_ERR_MODE;
+  if (group != 64 && group != 128 && group != -1 && group != hidden) return QG_ERR_GROUP;
+  if (group > 0 && hidden % group != 0) return QG_ERR_GROUP;
+  if (hidden % 8 != 0) return QG_ERR_UNSUPPORTED;
+  if (layout == QG_LAYOUT_TILED && (vocab % 16 != 0 || hidden % (bits == 4 ? 128 : 64) != 0))
+    return QG_ERR_UNSUPPORTED;
+  if (!aligned(ids, 4) || !aligned(table, 16) || !aligned(out, 16) || !aligned(scales, 2) ||
+      (zeros && !aligned(zeros, 2)))
+    return QG_ERR_ALIGN;
+  int g = group == -1 ? hidden : group;
+  if (bits == 8 && g == hidden) g = 0;   // one scale per row
+  qg::EmbedArgs a{ids, tokens, table, layout == QG_LAYOUT_TILED ? 1 : 0, bits,
+                  static_cast<const uint16_t *>(scales), static_cast<const uint16_t *>(zeros), out,
+                  vocab, hidden, g, static_cast<int>(act), static_cast<int>(out_dt)};
+  return hip_status(qg::launch_embed(a, as_stream(stream)));
+}
+
+qg_status qembed_w4(const int32_t *ids, int tokens, const uint8_t *table, int layout,
+                    const void *scales, const void *zeros, void *out, int vocab, int hidden,
+                    int group, qg_dtype act, qg_dtype out_dt, void *stream) {
+  return embed(ids, tokens, table, layout, scales, zeros, out, vocab, hidden, group, act, out_dt, 4,
+               stream);
+}
+
+qg_status qembed_w8(const int32_t *ids, int tokens, const int8_t *table, int layout,
+                    const void *scales, void *out, int vocab, int hidden, int group, qg_dtype act,
+                    qg_dtype out_dt, void *stream) {
+  return embed(ids, tokens, table, layout, scales, nullptr, out, vocab, hidden, group, act, out_dt, 8,
+               stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -89,3 +89,22 @@ size_t w8a8_workspace_bytes(int m, int n, int k);
 hipError_t launch_w8a8(const W8A8Args &a, hipStream_t s);
 
 }  // namespace qg
+
+namespace qg {
+
+// Quantized embedding lookup.
+struct EmbedArgs {
+  const int32_t *ids;       // [tokens]
+  int tokens;
+  const void *B;            // table codes, tiled or portable
+  int tiled;                // 1: the GEMM's tiled layout; 0: portable
+  int bits;                 // 4 or 8
+  const uint16_t *S, *Z;    // scales, zeros (int4, may be null)
+  void *out;                // [tokens, hidden] in out_dt
+  int vocab, hidden;
+  int group;                // int4: 64, 128 or hidden; int8: 0 (per row), 64 or 128
+  int act, out_dt;
+};
+hipError_t launch_embed(const EmbedArgs &a, hipStream_t s);
+
+}  // namespace qg
