@@ -18,6 +18,7 @@ Secondary sections on the same JSON line:
            (groupwise with zeros, scale-only, per channel);
   w8a8     int8 x int8 GEMM at K=3584, N in {3584, 18944}, M from 1 to 4096,
            per-token x per-channel scales (TOP/s against the int8 peak);
+  embed    int4 embedding lookups from the tied 131072 x 2048 table;
   quantize the load-side groupwise int4 quantizer on bf16 weights
            [N, 2048], N in {13312, 131072}, group 64 (GB/s against HBM);
   roofline the decode kernel of the N=131072 GEMV: algorithmic bytes per
@@ -475,6 +476,31 @@ def run(args):
                 "shapes": ashapes}
         log(f"w8a8: {w8a8}")
 
+    # ---- embedding lookup from the tied vocab table ------------------------------------
+    emb = None
+    if not args.no_w8a8:
+        vocab, hid, eg = 131072, 2048, 64
+        packed, sc, ze, _ = si.w4_weights(vocab, hid, eg, si.seed_of("cfg1", "w", vocab, hid, eg))
+        table = qg.repack_w4(torch.from_numpy(packed).to(dev))
+        S = torch.from_numpy(sc.view("int16")).view(torch.bfloat16).to(dev)
+        Z = torch.from_numpy(ze.view("int16")).view(torch.bfloat16).to(dev)
+        eshapes = {}
+        for T in (1, 64, 2048):
+            gen = torch.Generator().manual_seed(T)
+            ids = [torch.randint(0, vocab, (T,), generator=gen, dtype=torch.int32).to(dev)
+                   for _ in range(8)]
+            reps = max(10, K // 5)
+            for i in range(3):
+                qg.embed_w4(ids[i % 8], table, S, Z, eg)
+            ms = timed(lambda i: qg.embed_w4(ids[i % 8], table, S, Z, eg), reps, warm=reps) / reps
+            b = T * (hid // 2 + 4 * (hid // eg) + 4 + 2 * hid)
+            eshapes[f"T{T}"] = {"us": round(ms * 1e3, 2), "GBps": round(b / (ms * 1e-3) / 1e9, 1),
+                                "bytes": b}
+        emb = {"config": "int4 embedding lookup from the tied 131072 x 2048 table (tiled, g64, "
+                         "bf16 out), T random token ids", "shapes": eshapes}
+        del table, S, Z
+        log(f"embed: {emb}")
+
     # ---- load-side quantizer ------------------------------------------------------
     quant = None
     if not args.no_quant:
@@ -573,6 +599,7 @@ def run(args):
         "w8": w8,
         "w4_forms": forms,
         "w8a8": w8a8,
+        "embed": emb,
         "quantize": quant,
         "ceiling": ceil,
     }

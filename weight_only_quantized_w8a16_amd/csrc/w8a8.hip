@@ -395,8 +395,13 @@ int tiles_of(int M, int N, int bm, int bn) { return ((M + bm - 1) / bm) * ((N + 
 // slices (tests and tuning).
 W8A8Plan plan_w8a8(int M, int N, int K) {
   W8A8Plan pl{kT64, 0, 1, 0};
-  if (M > 128 && tiles_of(M, N, 256, 256) >= 192) pl.tile = kT256;
-  else if (M > 128 && tiles_of(M, N, 256, 128) >= 192) pl.tile = kT256N;
+  // The 256 x 256 tile when its tiles fill the CUs in one round or in many
+  // (a second, partly filled round of large tiles costs more than smaller
+  // tiles: K = 3584, m = 1024, n = 18944, 296 tiles: 132 us, 128 x 128: 108).
+  const int t256 = tiles_of(M, N, 256, 256);
+  // The 256 x 128 tile was never the fastest in those sweeps (m 128 to 4096);
+  // it stays available through QGEMM_W8A8_TILE.
+  if (M > 128 && t256 >= 192 && (t256 <= 256 || t256 >= 768)) pl.tile = kT256;
   else if (M > 64 && tiles_of(M, N, 128, 128) >= 128) pl.tile = kT128;
   else pl.tile = kT64;
   const int bm = pl.tile == kT64 ? 64 : pl.tile == kT128 ? 128 : 256;
