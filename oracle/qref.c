@@ -408,48 +408,82 @@ void qref_gemm_w8a8(const int8_t *A, const int8_t *B, const float *alpha_row, in
 /* weighted combine into the final output.                                  */
 /* ---------------------------------------------------------------------- */
 
-/* Top-k selection over raw logits, descending, ties to the lower index;
- * weights = softmax restricted to the selected logits (in double). */
-void qref_moe_route(const float *logits, int64_t tokens, int64_t experts, int64_t topk,
-                    int32_t *ids, double *weights)
+/* Routing  [acext] 1.2.3 runMoe: fp32 gating logits, an optional second
+ * set of logits "with bias" used to choose the experts, rows marked
+ * finished, and the expert-scale normalization mode.
+ * Selection: the topk largest selection logits (the biased set when given,
+ * else the gating logits), descending, ties to the lower index.
+ * Weights, from the unbiased gating logits l:
+ *   renormalize: exp(l_e) / sum over the selected experts of exp(l)
+ *   none:        exp(l_e) / sum over all experts of exp(l)  (the softmax
+ *                probability, not renormalized)
+ * both in double, shifted by the largest l of the sum for range.  A finished
+ * row takes no expert: ids -1, weights 0. */
+void qref_moe_route_ex(const float *logits, const float *sel_logits, const uint8_t *finished,
+                       int64_t tokens, int64_t experts, int64_t topk, int renormalize,
+                       int32_t *ids, double *weights)
 {
     for (int64_t t = 0; t < tokens; ++t) {
         const float *l = logits + t * experts;
+        const float *sl = sel_logits ? sel_logits + t * experts : l;
+        if (finished && finished[t]) {
+            for (int64_t j = 0; j < topk; ++j) { ids[t * topk + j] = -1; weights[t * topk + j] = 0.0; }
+            continue;
+        }
         for (int64_t j = 0; j < topk; ++j) {
             int64_t best = -1;
             for (int64_t e = 0; e < experts; ++e) {
                 int taken = 0;
                 for (int64_t p = 0; p < j; ++p) if (ids[t * topk + p] == (int32_t)e) taken = 1;
                 if (taken) continue;
-                if (best < 0 || l[e] > l[best]) best = e;   /* strict: ties keep lower index */
+                if (best < 0 || sl[e] > sl[best]) best = e;   /* strict: ties keep lower index */
             }
             ids[t * topk + j] = (int32_t)best;
         }
-        double lmax = (double)l[ids[t * topk]];
-        double denom = 0.0;
-        for (int64_t j = 0; j < topk; ++j) denom += exp((double)l[ids[t * topk + j]] - lmax);
+        double lmax = -INFINITY, denom = 0.0;
+        if (renormalize) {
+            for (int64_t j = 0; j < topk; ++j)
+                if ((double)l[ids[t * topk + j]] > lmax) lmax = (double)l[ids[t * topk + j]];
+            for (int64_t j = 0; j < topk; ++j) denom += exp((double)l[ids[t * topk + j]] - lmax);
+        } else {
+            for (int64_t e = 0; e < experts; ++e) if ((double)l[e] > lmax) lmax = (double)l[e];
+            for (int64_t e = 0; e < experts; ++e) denom += exp((double)l[e] - lmax);
+        }
         for (int64_t j = 0; j < topk; ++j)
             weights[t * topk + j] = exp((double)l[ids[t * topk + j]] - lmax) / denom;
     }
 }
 
+/* Top-k selection over raw logits, descending, ties to the lower index;
+ * weights = softmax restricted to the selected logits (in double). */
+void qref_moe_route(const float *logits, int64_t tokens, int64_t experts, int64_t topk,
+                    int32_t *ids, double *weights)
+{
+    qref_moe_route_ex(logits, NULL, NULL, tokens, experts, topk, 1, ids, weights);
+}
+
 static double silu(double x) { return x / (1.0 + exp(-x)); }
 
 /* out[t, :] = sum_j w[t, j] * fc2_e( silu(gate) * up ),  e = ids[t, j],
- * gate/up = rows [0, I) / [I, 2I) of fc1_e applied to x[t].  Weights of
- * expert e: w1 packed [E][2I][H/2], s1/z1 [E][2I][H/g], w2 packed [E][H][I/2],
- * s2/z2 [E][H][I/g].  Only the tokens listed in `sel` (count ntok) are
- * computed; out is [ntok, H] in double.  Expert-major so that each expert's
- * weights are dequantized once. */
-void qref_moe(const uint16_t *x, const float *logits, const uint8_t *w1, const uint16_t *s1,
-              const uint16_t *z1, const uint8_t *w2, const uint16_t *s2, const uint16_t *z2,
-              int64_t tokens, int64_t hidden, int64_t inter, int64_t experts, int64_t topk,
-              int64_t group, int dtype, const int64_t *sel, int64_t ntok, int32_t *ids_out,
-              double *weights_out, double *out)
+ * gate/up = rows [0, I) / [I, 2I) of fc1_e applied to x[t] (plus the fc1
+ * bias b1[e] when given), fc2_e(a) = W2_e a (plus the fc2 bias b2[e]).
+ * Weights of expert e: w1 packed [E][2I][H/2], s1/z1 [E][2I][H/g], w2 packed
+ * [E][H][I/2], s2/z2 [E][H][I/g]; biases b1 [E][2I] and b2 [E][H] in the
+ * activation dtype ([acext] 1.2.3 runMoe's fc1/fc2 expert biases).  Routing
+ * as qref_moe_route_ex; finished rows get an output of zeros.  Only the
+ * tokens listed in `sel` (count ntok) are computed; out is [ntok, H] in
+ * double.  Expert-major so that each expert's weights are dequantized once. */
+void qref_moe_ex(const uint16_t *x, const float *logits, const float *sel_logits,
+                 const uint8_t *finished, const uint8_t *w1, const uint16_t *s1,
+                 const uint16_t *z1, const uint16_t *b1, const uint8_t *w2, const uint16_t *s2,
+                 const uint16_t *z2, const uint16_t *b2, int64_t tokens, int64_t hidden,
+                 int64_t inter, int64_t experts, int64_t topk, int64_t group, int renormalize,
+                 int dtype, const int64_t *sel, int64_t ntok, int32_t *ids_out,
+                 double *weights_out, double *out)
 {
     int32_t *ids = (int32_t *)malloc(sizeof(int32_t) * (size_t)(tokens * topk));
     double *wts = (double *)malloc(sizeof(double) * (size_t)(tokens * topk));
-    qref_moe_route(logits, tokens, experts, topk, ids, wts);
+    qref_moe_route_ex(logits, sel_logits, finished, tokens, experts, topk, renormalize, ids, wts);
     if (ids_out) memcpy(ids_out, ids, sizeof(int32_t) * (size_t)(tokens * topk));
     if (weights_out) memcpy(weights_out, wts, sizeof(double) * (size_t)(tokens * topk));
     memset(out, 0, sizeof(double) * (size_t)(ntok * hidden));
@@ -483,6 +517,7 @@ void qref_moe(const uint16_t *x, const float *logits, const uint8_t *w1, const u
                         double acc = 0.0;
                         for (int64_t c = 0; c < hidden; ++c)
                             acc += act_to_double(x[t * hidden + c], dtype) * (double)W1[r * hidden + c];
+                        if (b1) acc += act_to_double(b1[e * two_i + r], dtype);
                         h[r] = acc;
                     }
                     for (int64_t r = 0; r < inter; ++r) a[r] = silu(h[r]) * h[inter + r];
@@ -490,6 +525,7 @@ void qref_moe(const uint16_t *x, const float *logits, const uint8_t *w1, const u
                     for (int64_t r = 0; r < hidden; ++r) {
                         double acc = 0.0;
                         for (int64_t c = 0; c < inter; ++c) acc += a[c] * (double)W2[r * inter + c];
+                        if (b2) acc += act_to_double(b2[e * hidden + r], dtype);
                         out[i * hidden + r] += wj * acc;
                     }
                 }
@@ -498,4 +534,14 @@ void qref_moe(const uint16_t *x, const float *logits, const uint8_t *w1, const u
         }
     }
     free(W1); free(W2); free(ids); free(wts);
+}
+
+void qref_moe(const uint16_t *x, const float *logits, const uint8_t *w1, const uint16_t *s1,
+              const uint16_t *z1, const uint8_t *w2, const uint16_t *s2, const uint16_t *z2,
+              int64_t tokens, int64_t hidden, int64_t inter, int64_t experts, int64_t topk,
+              int64_t group, int dtype, const int64_t *sel, int64_t ntok, int32_t *ids_out,
+              double *weights_out, double *out)
+{
+    qref_moe_ex(x, logits, NULL, NULL, w1, s1, z1, NULL, w2, s2, z2, NULL, tokens, hidden, inter,
+                experts, topk, group, 1, dtype, sel, ntok, ids_out, weights_out, out);
 }

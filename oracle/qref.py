@@ -75,6 +75,9 @@ _SIGS = {
     "qref_embed8": (None, [_P, _I, _P, _P, _I, _I, _I, _INT, _P]),
     "qref_gemm_w8a8": (None, [_P, _P, _P, _INT, _P, _INT, _I, _I, _I, _P, _P]),
     "qref_moe_route": (None, [_P, _I, _I, _I, _P, _P]),
+    "qref_moe_route_ex": (None, [_P, _P, _P, _I, _I, _I, _INT, _P, _P]),
+    "qref_moe_ex": (None, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
+                           _INT, _INT, _P, _I, _P, _P, _P]),
     "qref_moe": (None, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _INT,
                         _P, _I, _P, _P, _P]),
 }
@@ -319,22 +322,29 @@ def gemm_w8a8(A, B, alpha_row, alpha_col):
 
 # -- MoE ----------------------------------------------------------------------
 
-def moe_route(logits, topk):
-    """Top-k expert ids (int32 [T, k], descending logit, ties to lower id)
-    and their renormalised softmax weights (double [T, k])."""
+def moe_route(logits, topk, sel_logits=None, finished=None, renormalize=True):
+    """Top-k expert ids (int32 [T, k], descending selection logit, ties to the
+    lower id) and their weights (double [T, k]): softmax of the gating logits
+    over the selected experts (renormalize) or over all of them.  sel_logits:
+    the biased logits that choose the experts (default: the gating logits);
+    finished rows: ids -1, weights 0."""
     lg = _c(logits, np.float32)
     t, e = lg.shape
     ids = np.empty((t, topk), dtype=np.int32)
     w = np.empty((t, topk), dtype=np.float64)
-    lib().qref_moe_route(_ptr(lg), t, e, topk, _ptr(ids), _ptr(w))
+    lib().qref_moe_route_ex(_ptr(lg), _ptr(_c(sel_logits, np.float32)), _ptr(_c(finished, np.uint8)),
+                            t, e, topk, int(bool(renormalize)), _ptr(ids), _ptr(w))
     return ids, w
 
 
-def moe(x, logits, w1, s1, z1, w2, s2, z2, topk, group, dtype=BF16, tokens=None):
+def moe(x, logits, w1, s1, z1, w2, s2, z2, topk, group, dtype=BF16, tokens=None, b1=None, b2=None,
+        sel_logits=None, finished=None, renormalize=True):
     """Top-k MoE with SiLU-gated experts, in double.
 
     x [T, H] (16-bit bits), logits fp32 [T, E], w1 [E, 2I, H/2] u8,
-    s1/z1 [E, 2I, H/g], w2 [E, H, I/2] u8, s2/z2 [E, H, I/g].
+    s1/z1 [E, 2I, H/g], w2 [E, H, I/2] u8, s2/z2 [E, H, I/g]; optional fc1 /
+    fc2 biases b1 [E, 2I], b2 [E, H] (16-bit bits), selection logits,
+    finished rows (zero output) and the normalization mode (see moe_route).
     ``tokens`` selects which rows of the output to compute (default: all).
     Returns (out [len(tokens), H] double, ids [T, k] int32, weights [T, k]).
     """
@@ -351,7 +361,10 @@ def moe(x, logits, w1, s1, z1, w2, s2, z2, topk, group, dtype=BF16, tokens=None)
     out = np.empty((sel.size, h), dtype=np.float64)
     ids = np.empty((t, topk), dtype=np.int32)
     wts = np.empty((t, topk), dtype=np.float64)
-    lib().qref_moe(_ptr(xx), _ptr(lg), _ptr(W1), _ptr(_c(s1, np.uint16)), _ptr(_c(z1, np.uint16)),
-                   _ptr(W2), _ptr(_c(s2, np.uint16)), _ptr(_c(z2, np.uint16)), t, h, inter, e, topk,
-                   group, dtype, _ptr(sel), sel.size, _ptr(ids), _ptr(wts), _ptr(out))
+    lib().qref_moe_ex(_ptr(xx), _ptr(lg), _ptr(_c(sel_logits, np.float32)),
+                      _ptr(_c(finished, np.uint8)), _ptr(W1), _ptr(_c(s1, np.uint16)),
+                      _ptr(_c(z1, np.uint16)), _ptr(_c(b1, np.uint16)), _ptr(W2),
+                      _ptr(_c(s2, np.uint16)), _ptr(_c(z2, np.uint16)), _ptr(_c(b2, np.uint16)),
+                      t, h, inter, e, topk, group, int(bool(renormalize)), dtype, _ptr(sel), sel.size,
+                      _ptr(ids), _ptr(wts), _ptr(out))
     return out, ids, wts

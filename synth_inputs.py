@@ -238,3 +238,18 @@ def moe_problem(tokens, hidden, inter, experts, topk, group=64, tag="moe", dtype
     logits = _normal(ga, (tokens, experts), logit_std).numpy()
     return MoEProblem(tokens, hidden, inter, experts, topk, group, dtype, x, logits,
                       w1, s1, z1, w2, s2, z2)
+
+
+def moe_extras(p: MoEProblem, tag="moe-extras", bias_std=0.02, gate_bias_std=0.5,
+               finished_frac=0.1):
+    """Inputs of the MoE's optional parts: fc1 / fc2 expert biases (activation
+    dtype, N(0, bias_std)), selection logits = gating logits + a per-expert
+    bias drawn N(0, gate_bias_std) (the 'gating output with bias' input), and
+    a finished-row mask with about finished_frac of the rows set."""
+    g = _gen(seed_of(tag, p.tokens, p.hidden, p.inter, p.experts))
+    b1 = _bits(_normal(g, (p.experts, 2 * p.inter), bias_std), p.dtype)
+    b2 = _bits(_normal(g, (p.experts, p.hidden), bias_std), p.dtype)
+    gbias = _normal(g, (1, p.experts), gate_bias_std)
+    sel = (torch.from_numpy(p.logits) + gbias).numpy().astype(np.float32)
+    finished = (torch.rand((p.tokens,), generator=g) < finished_frac).to(torch.uint8).numpy()
+    return b1, b2, sel, finished

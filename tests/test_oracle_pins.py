@@ -447,3 +447,68 @@ def test_moe_token_subset_matches_full():
     full, _, _ = oracle.moe(p.x, p.logits, p.w1, p.s1, p.z1, p.w2, p.s2, p.z2, 3, 64)
     part, _, _ = oracle.moe(p.x, p.logits, p.w1, p.s1, p.z1, p.w2, p.s2, p.z2, 3, 64, tokens=[4, 1])
     np.testing.assert_array_equal(part, full[[4, 1]])
+
+
+# -- MoE extras: selection logits with bias, normalization mode, finished rows,
+# fc1 / fc2 expert biases ([acext] 1.2.3 runMoe) ---------------------------------
+
+def test_moe_route_selection_bias_hand_worked():
+    # Gating logits l = [0, 1, 2, 3]; the biased selection logits
+    # [5, 1, 2, 0] choose experts 0 and 2; the weights come from l:
+    # exp(0) / (exp(0) + exp(2)) and exp(2) / (exp(0) + exp(2)).
+    l = np.array([[0.0, 1.0, 2.0, 3.0]], np.float32)
+    sl = np.array([[5.0, 1.0, 2.0, 0.0]], np.float32)
+    ids, w = oracle.moe_route(l, 2, sel_logits=sl)
+    assert ids.tolist() == [[0, 2]]
+    e2 = np.exp(2.0)
+    np.testing.assert_allclose(w[0], [1 / (1 + e2), e2 / (1 + e2)], rtol=1e-15)
+    ids, w = oracle.moe_route(l, 2)                    # without the bias: 3, 2
+    assert ids.tolist() == [[3, 2]]
+
+
+def test_moe_route_no_renormalization_is_softmax_probability():
+    # Logits log(1..4): the softmax over all four is [0.1, 0.2, 0.3, 0.4];
+    # without renormalization the top-2 keep their probabilities 0.4, 0.3.
+    l = np.log(np.array([[1.0, 2.0, 3.0, 4.0]])).astype(np.float32)
+    ids, w = oracle.moe_route(l, 2, renormalize=False)
+    assert ids.tolist() == [[3, 2]]
+    np.testing.assert_allclose(w[0], [0.4, 0.3], rtol=1e-6)
+    _, w1 = oracle.moe_route(l, 1, renormalize=True)
+    assert w1.tolist() == [[1.0]]
+
+
+def test_moe_finished_rows_take_no_expert():
+    p = si.moe_problem(5, 64, 64, 4, 2, group=64, tag="pin-moe5")
+    fin = np.array([0, 1, 0, 0, 1], np.uint8)
+    out, ids, w = oracle.moe(p.x, p.logits, p.w1, p.s1, p.z1, p.w2, p.s2, p.z2, 2, 64, finished=fin)
+    assert (ids[fin == 1] == -1).all() and (w[fin == 1] == 0).all()
+    assert (out[fin == 1] == 0).all()
+    full, ids0, _ = oracle.moe(p.x, p.logits, p.w1, p.s1, p.z1, p.w2, p.s2, p.z2, 2, 64)
+    np.testing.assert_array_equal(out[fin == 0], full[fin == 0])
+    np.testing.assert_array_equal(ids[fin == 0], ids0[fin == 0])
+
+
+def _dense_swiglu_bias(xf, W1, b1, W2, b2, inter):
+    h = xf @ W1.T + b1
+    gate, up = h[:, :inter], h[:, inter:]
+    a = gate / (1.0 + np.exp(-gate)) * up
+    return a @ W2.T + b2
+
+
+@pytest.mark.parametrize("renormalize", [True, False])
+def test_moe_identical_experts_with_biases_equal_dense_ffn(renormalize):
+    # Every expert the same (weights and biases): with renormalized weights
+    # the output is the dense biased SwiGLU FFN; without, that FFN times the
+    # sum of the selected probabilities.
+    p = si.moe_problem(6, 64, 64, 4, 2, group=64, tag="pin-moe6")
+    b1, b2, _, _ = si.moe_extras(p)
+    for arr in (p.w1, p.s1, p.z1, p.w2, p.s2, p.z2, b1, b2):
+        arr[1:] = arr[0]
+    out, _, w = oracle.moe(p.x, p.logits, p.w1, p.s1, p.z1, p.w2, p.s2, p.z2, 2, 64, b1=b1, b2=b2,
+                           renormalize=renormalize)
+    W1 = oracle.dequant4(p.w1[0], p.s1[0], p.z1[0], 64).astype(np.float64)
+    W2 = oracle.dequant4(p.w2[0], p.s2[0], p.z2[0], 64).astype(np.float64)
+    ref = _dense_swiglu_bias(_conv(p.x, BF16), W1, _conv(b1[0], BF16), W2, _conv(b2[0], BF16), 64)
+    np.testing.assert_allclose(out, ref * w.sum(axis=1, keepdims=True), rtol=1e-10, atol=1e-10)
+    if renormalize:
+        np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=1e-15)
