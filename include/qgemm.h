@@ -300,6 +300,35 @@ qg_status qmoe_grouped(const void *x, const float *logits, const uint8_t *w1_til
                        float *topk_w_out, void *workspace, size_t workspace_bytes,
                        void *stream);
 
+/* The same MoE with the optional inputs of runMoe (acext User Guide (v1.7),
+ * 1.2.3: gating_output_with_bias, fc1/fc2 expert biases, finished,
+ * normalization_mode):
+ *   sel_logits  optional device fp32 [tokens, experts]: the biased logits
+ *               that choose the experts (NULL: the gating logits).  The
+ *               weights always come from `logits`.
+ *   finished    optional device uint8 [tokens] (bool): a nonzero row takes
+ *               no expert (topk ids -1, weights 0) and its output row is 0.
+ *   b1          optional device [experts, 2*inter], act_dtype: fc1 biases,
+ *               added to gate and up before the activation.
+ *   b2          optional device [experts, hidden], act_dtype: fc2 biases,
+ *               added to each expert's output (in fp32, in the combine).
+ *   norm_mode   QG_MOE_RENORMALIZE (1): softmax over the selected logits (as
+ *               qmoe_grouped); QG_MOE_NORM_NONE (0): the full softmax
+ *               probability of each selected expert, not renormalized.
+ * The page's active_rows (the count of unfinished rows) follows from
+ * `finished` and is not an argument.  Other arguments and requirements as
+ * qmoe_grouped (the same workspace size); alignment: sel_logits 4 bytes,
+ * b1 and b2 16 bytes. */
+enum { QG_MOE_NORM_NONE = 0, QG_MOE_RENORMALIZE = 1 };
+
+qg_status qmoe_grouped_ex(const void *x, const float *logits, const float *sel_logits,
+                          const uint8_t *finished, const uint8_t *w1_tiled, const void *s1,
+                          const void *z1, const void *b1, const uint8_t *w2_tiled, const void *s2,
+                          const void *z2, const void *b2, void *out, int tokens, int hidden,
+                          int inter, int experts, int topk, int group_size, int norm_mode,
+                          qg_dtype act_dtype, int32_t *topk_ids_out, float *topk_w_out,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -293,3 +293,26 @@ def test_embed_w4_zeros_optional_and_portable_multiples():
 ])
 def test_embed_w8_validation(kw, status):
     assert emb8(**kw) == status
+
+
+# -- MoE with the optional parts ------------------------------------------------------
+
+def moe_ex(**kw):
+    a = dict(x=FAKE, lg=FAKE, sel=None, fin=None, w1=FAKE, s1=FAKE, z1=FAKE, b1=None, w2=FAKE,
+             s2=FAKE, z2=FAKE, b2=None, out=FAKE, T=8, H=128, I=128, E=4, k=2, g=64, norm=1,
+             act=BF16, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return qg.lib().qmoe_grouped_ex(a["x"], a["lg"], a["sel"], a["fin"], a["w1"], a["s1"], a["z1"],
+                                    a["b1"], a["w2"], a["s2"], a["z2"], a["b2"], a["out"], a["T"],
+                                    a["H"], a["I"], a["E"], a["k"], a["g"], a["norm"], a["act"],
+                                    None, None, a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), SHAPE), (dict(k=5), SHAPE), (dict(x=None), NULL), (dict(act=FP32), DTYPE),
+    (dict(norm=2), 9), (dict(norm=-1), 9), (dict(g=32), GROUP), (dict(H=192, g=64), UNSUP),
+    (dict(sel=FAKE + 2), ALIGN), (dict(b1=FAKE + 8), ALIGN), (dict(b2=FAKE + 2), ALIGN),
+    (dict(ws=None), WORKSPACE), (dict(wsb=16), WORKSPACE), (dict(T=0), OK),
+])
+def test_moe_ex_validation(kw, status):
+    assert moe_ex(**kw) == status

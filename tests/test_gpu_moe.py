@@ -113,3 +113,70 @@ def test_moe_full_size_sampled_tokens(moe_tile):
     p = si.moe_problem(2048, 2048, 1408, 64, 6, 64, tag="cfg4")
     toks = np.unique(np.concatenate([[0, 1, 2047], np.random.default_rng(4).integers(0, 2048, 21)]))
     check(p, tokens=toks)
+
+
+# -- optional parts of runMoe: biased selection logits, finished rows, fc1 / fc2
+# expert biases, normalization mode -------------------------------------------------
+
+def run_moe_ex(p, b1, b2, sel, fin, renormalize):
+    dev = "cuda"
+    x = to_dev(p.x, p.dtype)
+    lg = torch.from_numpy(p.logits).to(dev)
+    w1 = torch.stack([qg.repack_w4(to_dev(p.w1[e])) for e in range(p.experts)])
+    w2 = torch.stack([qg.repack_w4(to_dev(p.w2[e])) for e in range(p.experts)])
+    s1, z1, s2, z2 = (to_dev(a, p.dtype) for a in (p.s1, p.z1, p.s2, p.z2))
+    kw = dict(renormalize=renormalize)
+    if b1 is not None:
+        kw["b1"] = to_dev(b1, p.dtype)
+    if b2 is not None:
+        kw["b2"] = to_dev(b2, p.dtype)
+    if sel is not None:
+        kw["sel_logits"] = torch.from_numpy(sel).to(dev)
+    if fin is not None:
+        kw["finished"] = torch.from_numpy(fin.astype(bool)).to(dev)
+    out, ids, w = qg.moe_grouped(x, lg, w1, s1, z1, w2, s2, z2, p.topk, p.group,
+                                 return_routing=True, **kw)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy()
+
+
+@pytest.mark.parametrize("parts", ["biases", "selection", "finished", "no_renorm", "all"])
+@pytest.mark.parametrize("T,H,I,E,k,g", [(37, 256, 256, 8, 2, 64), (300, 512, 384, 16, 4, 128)])
+def test_moe_optional_parts(parts, T, H, I, E, k, g, moe_tile):
+    p = si.moe_problem(T, H, I, E, k, g, tag="moe-extras")
+    b1, b2, sel, fin = si.moe_extras(p)
+    use = dict(b1=b1 if parts in ("biases", "all") else None,
+               b2=b2 if parts in ("biases", "all") else None,
+               sel=sel if parts in ("selection", "all") else None,
+               fin=fin if parts in ("finished", "all") else None,
+               renormalize=parts not in ("no_renorm", "all"))
+    out, ids, w = run_moe_ex(p, **use)
+    ref, rids, rw = oracle.moe(p.x, p.logits, p.w1, p.s1, p.z1, p.w2, p.s2, p.z2, p.topk, p.group,
+                               p.dtype, b1=use["b1"], b2=use["b2"], sel_logits=use["sel"],
+                               finished=use["fin"], renormalize=use["renormalize"])
+    assert np.array_equal(ids, rids)
+    np.testing.assert_allclose(w, rw, rtol=2e-6, atol=1e-7)
+    assert rel_err(out, ref) <= TOL[BF16]
+    if use["fin"] is not None:
+        assert fin.any() and (out[fin == 1] == 0).all() and (ids[fin == 1] == -1).all()
+
+
+def test_moe_all_rows_finished():
+    p = si.moe_problem(16, 128, 128, 4, 2, 64, tag="moe-allfin")
+    out, ids, w = run_moe_ex(p, None, None, None, np.ones(16, np.uint8), True)
+    assert (out == 0).all() and (ids == -1).all() and (w == 0).all()
+
+
+def test_moe_optional_parts_full_size_sampled():
+    # The 2048-token, 64-expert workload with every optional part on.
+    p = si.moe_problem(2048, 2048, 1408, 64, 6, 64, tag="cfg4")
+    b1, b2, sel, fin = si.moe_extras(p)
+    out, ids, w = run_moe_ex(p, b1, b2, sel, fin, False)
+    toks = np.unique(np.concatenate([[0, 2047], np.flatnonzero(fin)[:3],
+                                     np.random.default_rng(9).integers(0, 2048, 16)]))
+    ref, rids, rw = oracle.moe(p.x, p.logits, p.w1, p.s1, p.z1, p.w2, p.s2, p.z2, 6, 64, BF16,
+                               tokens=toks, b1=b1, b2=b2, sel_logits=sel, finished=fin,
+                               renormalize=False)
+    assert np.array_equal(ids, rids)
+    np.testing.assert_allclose(w, rw, rtol=2e-6, atol=1e-7)
+    assert rel_err(out[toks], ref) <= TOL[BF16]

@@ -13,8 +13,9 @@ from typing import Optional
 
 import torch
 
-from ._abi import (QG_BF16, QG_FP16, QG_FP32, QG_LAYOUT_PORTABLE, QG_LAYOUT_TILED, QG_NONE,
-                   QG_W8A8_PER_CHANNEL, QG_W8A8_PER_TOKEN, QGemmError, check, lib)
+from ._abi import (QG_BF16, QG_FP16, QG_FP32, QG_LAYOUT_PORTABLE, QG_LAYOUT_TILED,
+                   QG_MOE_NORM_NONE, QG_MOE_RENORMALIZE, QG_NONE, QG_W8A8_PER_CHANNEL,
+                   QG_W8A8_PER_TOKEN, QGemmError, check, lib)
 
 __all__ = [
     "QGemmError", "lib", "repack_w4", "unrepack_w4", "repack_w8", "unrepack_w8", "repack_w8_kn",
@@ -325,16 +326,26 @@ def moe_workspace_size(tokens: int, hidden: int, inter: int, experts: int, topk:
 def moe_grouped(x: torch.Tensor, logits: torch.Tensor, w1_tiled: torch.Tensor, s1: torch.Tensor,
                 z1: torch.Tensor, w2_tiled: torch.Tensor, s2: torch.Tensor, z2: torch.Tensor,
                 topk: int, group_size: int = 64, return_routing: bool = False,
-                workspace: Optional[torch.Tensor] = None):
+                workspace: Optional[torch.Tensor] = None, b1: Optional[torch.Tensor] = None,
+                b2: Optional[torch.Tensor] = None, sel_logits: Optional[torch.Tensor] = None,
+                finished: Optional[torch.Tensor] = None, renormalize: bool = True):
     """Top-k MoE with SiLU-gated int4 experts.
 
     x [T, H]; logits fp32 [T, E]; w1_tiled [E, 2I, H/2] (tiled per expert);
-    s1/z1 [E, 2I, H/g]; w2_tiled [E, H, I/2]; s2/z2 [E, H, I/g].
-    Returns out [T, H] (and (ids int32 [T, k], weights fp32 [T, k])).
+    s1/z1 [E, 2I, H/g]; w2_tiled [E, H, I/2]; s2/z2 [E, H, I/g].  Optional:
+    fc1 / fc2 expert biases b1 [E, 2I], b2 [E, H] (x's dtype), biased
+    selection logits fp32 [T, E], a finished mask (bool/uint8 [T]) and the
+    normalization mode.  Returns out [T, H] (and (ids int32 [T, k], weights
+    fp32 [T, k])).
     """
     for t, nm in ((x, "x"), (logits, "logits"), (w1_tiled, "w1_tiled"), (s1, "s1"), (z1, "z1"),
                   (w2_tiled, "w2_tiled"), (s2, "s2"), (z2, "z2")):
         _dev(t, nm)
+    for t, nm in ((b1, "b1"), (b2, "b2"), (sel_logits, "sel_logits"), (finished, "finished")):
+        if t is not None:
+            _dev(t, nm)
+    if finished is not None and finished.dtype == torch.bool:
+        finished = finished.view(torch.uint8)
     T, H = x.shape
     E = logits.shape[1]
     inter = w1_tiled.shape[1] // 2
@@ -345,10 +356,18 @@ def moe_grouped(x: torch.Tensor, logits: torch.Tensor, w1_tiled: torch.Tensor, s
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     _dev(workspace, "workspace")
-    check("qmoe_grouped", lib().qmoe_grouped(
-        _ptr(x), _ptr(logits), _ptr(w1_tiled), _ptr(s1), _ptr(z1), _ptr(w2_tiled), _ptr(s2),
-        _ptr(z2), _ptr(out), T, H, inter, E, topk, group_size, dtype_code(x.dtype), _ptr(ids),
-        _ptr(wts), _ptr(workspace), workspace.numel(), _stream(x)))
+    if b1 is None and b2 is None and sel_logits is None and finished is None and renormalize:
+        check("qmoe_grouped", lib().qmoe_grouped(
+            _ptr(x), _ptr(logits), _ptr(w1_tiled), _ptr(s1), _ptr(z1), _ptr(w2_tiled), _ptr(s2),
+            _ptr(z2), _ptr(out), T, H, inter, E, topk, group_size, dtype_code(x.dtype), _ptr(ids),
+            _ptr(wts), _ptr(workspace), workspace.numel(), _stream(x)))
+    else:
+        check("qmoe_grouped_ex", lib().qmoe_grouped_ex(
+            _ptr(x), _ptr(logits), _ptr(sel_logits), _ptr(finished), _ptr(w1_tiled), _ptr(s1),
+            _ptr(z1), _ptr(b1), _ptr(w2_tiled), _ptr(s2), _ptr(z2), _ptr(b2), _ptr(out), T, H,
+            inter, E, topk, group_size, QG_MOE_RENORMALIZE if renormalize else QG_MOE_NORM_NONE,
+            dtype_code(x.dtype), _ptr(ids), _ptr(wts), _ptr(workspace), workspace.numel(),
+            _stream(x)))
     if return_routing:
         return out, ids, wts
     return out

@@ -22,6 +22,7 @@ STATUS_NAMES = {
 QG_NONE, QG_BF16, QG_FP16, QG_FP32 = 0, 1, 2, 3
 QG_W8A8_PER_TENSOR, QG_W8A8_PER_CHANNEL, QG_W8A8_PER_TOKEN = 0, 1, 2
 QG_LAYOUT_PORTABLE, QG_LAYOUT_TILED = 0, 1
+QG_MOE_NORM_NONE, QG_MOE_RENORMALIZE = 0, 1
 
 _P = ctypes.c_void_p
 _INT = ctypes.c_int
@@ -51,6 +52,8 @@ SIGNATURES = {
     "qmoe_workspace_size": (_SZ, [_INT, _INT, _INT, _INT, _INT]),
     "qmoe_grouped": (_ST, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _INT, _INT, _INT, _INT, _INT, _INT,
                            _INT, _P, _P, _P, _SZ, _P]),
+    "qmoe_grouped_ex": (_ST, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _INT, _INT, _INT,
+                              _INT, _INT, _INT, _INT, _INT, _P, _P, _P, _SZ, _P]),
 }
 
 _lock = threading.Lock()

@@ -338,23 +338,28 @@ size_t qmoe_workspace_size(int tokens, int hidden, int inter, int experts, int t
   return qg::moe_workspace_bytes(tokens, hidden, inter, experts, topk);
 }
 
-qg_status qmoe_grouped(const void *x, const float *logits, const uint8_t *w1, const void *s1,
-                       const void *z1, const uint8_t *w2, const void *s2, const void *z2,
-                       void *out, int tokens, int hidden, int inter, int experts, int topk,
-                       int group, qg_dtype act, int32_t *ids_out, float *w_out, void *workspace,
-                       size_t ws_bytes, void *stream) {
+static qg_status moe_call(const void *x, const float *logits, const float *sel_logits,
+                          const uint8_t *finished, const uint8_t *w1, const void *s1,
+                          const void *z1, const void *b1, const uint8_t *w2, const void *s2,
+                          const void *z2, const void *b2, void *out, int tokens, int hidden,
+                          int inter, int experts, int topk, int group, int norm, qg_dtype act,
+                          int32_t *ids_out, float *w_out, void *workspace, size_t ws_bytes,
+                          void *stream) {
   if (tokens < 0 || hidden <= 0 || inter <= 0 || experts <= 0 || topk <= 0 || topk > experts)
     return QG_ERR_SHAPE;
   if (tokens == 0) return QG_OK;        // nothing to compute; pointers unused
   if (!x || !logits || !w1 || !s1 || !z1 || !w2 || !s2 || !z2 || !out) return QG_ERR_NULL;
   if (!act_ok(act)) return QG_ERR_DTYPE;
+  if (norm != QG_MOE_NORM_NONE && norm != QG_MOE_RENORMALIZE) return QG_ERR_MODE;
   if (group != 64 && group != 128) return QG_ERR_GROUP;
   if (hidden % group != 0 || inter % group != 0) return QG_ERR_GROUP;
   if (hidden % 128 != 0 || inter % 128 != 0 || experts > 256 || topk > 64)
     return QG_ERR_UNSUPPORTED;
   if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w2, 16) || !aligned(out, 16) ||
       !aligned(logits, 4) || !aligned(s1, 2) || !aligned(z1, 2) || !aligned(s2, 2) ||
-      !aligned(z2, 2) || (ids_out && !aligned(ids_out, 4)) || (w_out && !aligned(w_out, 4)))
+      !aligned(z2, 2) || (ids_out && !aligned(ids_out, 4)) || (w_out && !aligned(w_out, 4)) ||
+      (sel_logits && !aligned(sel_logits, 4)) || (b1 && !aligned(b1, 16)) ||
+      (b2 && !aligned(b2, 16)))
     return QG_ERR_ALIGN;
   const size_t need = qg::moe_workspace_bytes(tokens, hidden, inter, experts, topk);
   if (!workspace || ws_bytes < need) return QG_ERR_WORKSPACE;
@@ -364,7 +369,34 @@ qg_status qmoe_grouped(const void *x, const float *logits, const uint8_t *w1, co
                 static_cast<const uint16_t *>(s2), static_cast<const uint16_t *>(z2),
                 static_cast<uint16_t *>(out), tokens, hidden, inter, experts, topk, group,
                 static_cast<int>(act), ids_out, w_out, workspace};
+  a.sel_logits = sel_logits;
+  a.finished = finished;
+  a.b1 = static_cast<const uint16_t *>(b1);
+  a.b2 = static_cast<const uint16_t *>(b2);
+  a.renorm = norm == QG_MOE_RENORMALIZE ? 1 : 0;
   return hip_status(qg::launch_moe(a, as_stream(stream)));
+}
+
+qg_status qmoe_grouped(const void *x, const float *logits, const uint8_t *w1, const void *s1,
+                       const void *z1, const uint8_t *w2, const void *s2, const void *z2,
+                       void *out, int tokens, int hidden, int inter, int experts, int topk,
+                       int group, qg_dtype act, int32_t *ids_out, float *w_out, void *workspace,
+                       size_t ws_bytes, void *stream) {
+  return moe_call(x, logits, nullptr, nullptr, w1, s1, z1, nullptr, w2, s2, z2, nullptr, out,
+                  tokens, hidden, inter, experts, topk, group, QG_MOE_RENORMALIZE, act, ids_out,
+                  w_out, workspace, ws_bytes, stream);
+}
+
+qg_status qmoe_grouped_ex(const void *x, const float *logits, const float *sel_logits,
+                          const uint8_t *finished, const uint8_t *w1, const void *s1,
+                          const void *z1, const void *b1, const uint8_t *w2, const void *s2,
+                          const void *z2, const void *b2, void *out, int tokens, int hidden,
+                          int inter, int experts, int topk, int group, int norm, qg_dtype act,
+                          int32_t *ids_out, float *w_out, void *workspace, size_t ws_bytes,
+                          void *stream) {
+  return moe_call(x, logits, sel_logits, finished, w1, s1, z1, b1, w2, s2, z2, b2, out, tokens,
+                  hidden, inter, experts, topk, group, norm, act, ids_out, w_out, workspace,
+                  ws_bytes, stream);
 }
 
 }  // extern "C"

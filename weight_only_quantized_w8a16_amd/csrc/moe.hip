@@ -17,7 +17,12 @@
 // The grouped GEMMs use the 256 x 256 direct-load tile (tile_big.hpp) with
 // 256-row expert tiles where the shapes allow it, else the 128 x 128 tile
 // kernel with 128-row expert tiles.
-//   combine  out[t] = sum_j w[t, j] * y[row(t, j)], fp32 in rank order.
+//   combine  out[t] = sum_j w[t, j] * (y[row(t, j)] + b2[e]), fp32 in rank
+//            order.
+// Optional parts of runMoe: biased selection logits (route), finished rows
+// (route gives them no expert; plan and combine skip their slots), the fc1
+// expert biases (fc1 epilogue, before the activation) and the fc2 ones
+// (combine), and the normalization mode (route).
 #include <cstdlib>
 
 #include "qg_launch.hpp"
@@ -61,20 +66,34 @@ size_t moe_workspace_bytes(int T, int H, int I, int E, int topk) {
   return moe_layout(T, H, I, E, topk).total;
 }
 
-// One wave per token; up to 256 experts (4 logits per lane).
-__global__ __launch_bounds__(256) void k_moe_route(const float *__restrict__ logits, int T, int E,
-                                                   int topk, int32_t *__restrict__ ids,
+// One wave per token; up to 256 experts (4 logits per lane).  The experts
+// are chosen by `sel` (the biased logits when given, else the gating logits)
+// and weighted from the gating logits: softmax over the chosen experts
+// (renormalize) or over all of them.  A finished row takes no expert.
+__global__ __launch_bounds__(256) void k_moe_route(const float *__restrict__ logits,
+                                                   const float *__restrict__ sel_logits,
+                                                   const uint8_t *__restrict__ finished, int T, int E,
+                                                   int topk, int renorm, int32_t *__restrict__ ids,
                                                    float *__restrict__ wts) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  float v[4];
+  if (finished && finished[t]) {
+    if (lane < topk) {
+      ids[static_cast<size_t>(t) * topk + lane] = -1;
+      wts[static_cast<size_t>(t) * topk + lane] = 0.0f;
+    }
+    return;
+  }
+  const float *sl = sel_logits ? sel_logits : logits;
+  float v[4], u[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;
-    v[i] = e < E ? logits[static_cast<size_t>(t) * E + e] : -__builtin_inff();
+    v[i] = e < E ? sl[static_cast<size_t>(t) * E + e] : -__builtin_inff();
+    u[i] = e < E ? logits[static_cast<size_t>(t) * E + e] : -__builtin_inff();
   }
-  float lmax = 0.f, denom = 0.f, my_l = 0.f;
+  float my_l = -__builtin_inff();
   int my_id = 0;
   for (int j = 0; j < topk; ++j) {
     // lane-local best (strict > keeps the lower expert id on ties)
@@ -89,14 +108,29 @@ __global__ __launch_bounds__(256) void k_moe_route(const float *__restrict__ log
       const int oi = __shfl_xor(bi, off);
       if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
     }
-    if ((bi & 63) == lane) v[bi >> 6] = -__builtin_inff();
-    if (j == 0) lmax = bv;
-    denom += expf(bv - lmax);
-    if (lane == j) { my_l = bv; my_id = bi; }
+    // the chosen expert's gating logit, from the lane that holds it
+    const int slot = bi >> 6;
+    const float mine = slot == 0 ? u[0] : slot == 1 ? u[1] : slot == 2 ? u[2] : u[3];
+    const float ul = __shfl(mine, bi & 63);
+    if ((bi & 63) == lane) v[slot] = -__builtin_inff();
+    if (lane == j) { my_l = ul; my_id = bi; }
   }
+  // max and sum over the chosen experts (lanes < topk) or over all experts
+  float m = renorm ? my_l : fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3]));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  float d = 0.0f;
+  if (renorm) {
+    d = lane < topk ? expf(my_l - m) : 0.0f;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d += (lane + 64 * i < E) ? expf(u[i] - m) : 0.0f;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) d += __shfl_xor(d, off);
   if (lane < topk) {
     ids[static_cast<size_t>(t) * topk + lane] = my_id;
-    wts[static_cast<size_t>(t) * topk + lane] = expf(my_l - lmax) / denom;
+    wts[static_cast<size_t>(t) * topk + lane] = expf(my_l - m) / d;
   }
 }
 
@@ -178,8 +212,12 @@ __global__ __launch_bounds__(1024) void k_moe_plan(const int32_t *__restrict__ i
     load_batch(base, e);
 #pragma unroll
     for (int u = 0; u < kPlanBatch; ++u) {
-      if (e[u] < 0) continue;
       const int r = base + u * nthr + static_cast<int>(threadIdx.x);
+      if (r >= R) continue;
+      if (e[u] < 0) {   // a finished row's slot: no expert row
+        dest[r] = -1;
+        continue;
+      }
       const int pos = off[e[u]] + atomicAdd(&fill[e[u]], 1);
       row_src[pos] = r / topk;
       dest[r] = pos;
@@ -208,11 +246,14 @@ __global__ __launch_bounds__(CfgMoeDma::NTHR) void k_moe_dma(TileProblem p, int 
   tile_gemm_dma<CfgMoeDma, ACT, 4, MODE>(p, tm, tn, L);
 }
 
-// out[t, h..h+7] = sum_j w[t, j] * y[dest[t, j], h..h+7]
+// out[t, h..h+7] = sum_j w[t, j] * (y[dest[t, j], h..h+7] + b2[e, h..h+7]),
+// e = ids[t, j]; slots without an expert row (finished rows) add nothing.
 template <int ACT>
 __global__ __launch_bounds__(256) void k_moe_combine(const uint16_t *__restrict__ y,
                                                      const float *__restrict__ wts,
                                                      const int32_t *__restrict__ dest,
+                                                     const int32_t *__restrict__ ids,
+                                                     const uint16_t *__restrict__ b2,
                                                      uint16_t *__restrict__ out, int T, int H,
                                                      int topk) {
   const long long idx = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -223,11 +264,16 @@ __global__ __launch_bounds__(256) void k_moe_combine(const uint16_t *__restrict_
   for (int j = 0; j < topk; ++j) {
     const float w = wts[static_cast<size_t>(t) * topk + j];
     const int row = dest[static_cast<size_t>(t) * topk + j];
+    if (row < 0) continue;
     const u32x4 v = *reinterpret_cast<const u32x4 *>(y + static_cast<size_t>(row) * H + h0);
+    u32x4 b = {0u, 0u, 0u, 0u};
+    if (b2) b = *reinterpret_cast<const u32x4 *>(b2 + static_cast<size_t>(ids[static_cast<size_t>(t) * topk + j]) * H + h0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      acc[2 * i] += w * bits_to_f32<ACT>(static_cast<uint16_t>(v[i] & 0xFFFFu));
-      acc[2 * i + 1] += w * bits_to_f32<ACT>(static_cast<uint16_t>(v[i] >> 16));
+      acc[2 * i] += w * (bits_to_f32<ACT>(static_cast<uint16_t>(v[i] & 0xFFFFu)) +
+                         bits_to_f32<ACT>(static_cast<uint16_t>(b[i] & 0xFFFFu)));
+      acc[2 * i + 1] += w * (bits_to_f32<ACT>(static_cast<uint16_t>(v[i] >> 16)) +
+                             bits_to_f32<ACT>(static_cast<uint16_t>(b[i] >> 16)));
     }
   }
   u32x4 o;
@@ -272,8 +318,8 @@ hipError_t run_moe(const MoeArgs &a, hipStream_t s) {
   const int bm = use_dma ? CfgMoeDma::BM : kMoeBM;
   const int max_tiles = (R + bm - 1) / bm + a.E;
 
-  hipLaunchKernelGGL(k_moe_route, dim3((a.T + 3) / 4), dim3(256), 0, s, a.logits, a.T, a.E,
-                     a.topk, ids, wts);
+  hipLaunchKernelGGL(k_moe_route, dim3((a.T + 3) / 4), dim3(256), 0, s, a.logits, a.sel_logits,
+                     a.finished, a.T, a.E, a.topk, a.renorm, ids, wts);
   hipLaunchKernelGGL(k_moe_plan, dim3(1), dim3(1024), 0, s, ids, R, a.E, a.topk, bm, tiles, ntiles,
                      row_src, dest);
 
@@ -290,6 +336,7 @@ hipError_t run_moe(const MoeArgs &a, hipStream_t s) {
   p1.S = a.s1;
   p1.Z = a.z1;
   p1.C = act;
+  p1.bias = a.b1;   // [E, 2I] or null, added before the activation
   p1.M = R;
   p1.N = a.I;
   p1.K = a.H;
@@ -339,7 +386,7 @@ hipError_t run_moe(const MoeArgs &a, hipStream_t s) {
 
   const long long items = static_cast<long long>(a.T) * (a.H / 8);
   hipLaunchKernelGGL((k_moe_combine<ACT>), dim3(static_cast<unsigned>((items + 255) / 256)),
-                     dim3(256), 0, s, y, wts, dest, a.out, a.T, a.H, a.topk);
+                     dim3(256), 0, s, y, wts, dest, ids, a.b2, a.out, a.T, a.H, a.topk);
   return hipGetLastError();
 }
 

@@ -62,6 +62,12 @@ struct MoeArgs {
   int32_t *ids_out;
   float *w_out;
   void *ws;
+  // optional parts of runMoe (null / 1 for the plain call)
+  const float *sel_logits = nullptr;    // [T, E] biased logits that choose the experts
+  const uint8_t *finished = nullptr;    // [T], nonzero: no expert, zero output
+  const uint16_t *b1 = nullptr;         // [E, 2I] fc1 biases
+  const uint16_t *b2 = nullptr;         // [E, H] fc2 biases
+  int renorm = 1;                       // 1: renormalize over the chosen experts
 };
 size_t moe_workspace_bytes(int T, int H, int I, int E, int topk);
 hipError_t launch_moe(const MoeArgs &a, hipStream_t s);

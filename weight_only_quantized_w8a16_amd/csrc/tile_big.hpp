@@ -100,6 +100,7 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
   const int s0 = SPLIT ? slice * p.kseg : 0;                    // steps [s0, s1)
   const int s1 = SPLIT ? min(K / BK, s0 + p.kseg) : K / BK;
   int row_lo, row_last;
+  [[maybe_unused]] int expert = 0;
   const uint8_t *Bb = p.B;
   const uint16_t *Sb = p.S, *Zb = GS8 ? p.S : p.Z;
   uint32_t b_bytes, s_bytes;     // buffer extents (one expert for MoE)
@@ -110,6 +111,7 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
     s_bytes = kWin ? static_cast<uint32_t>(static_cast<uint64_t>(p.N) * (K / p.group) * 2) : 0u;
   } else {
     const MoeTile t = p.tiles[tile_m];
+    expert = t.expert;
     row_lo = t.row0;
     row_last = t.row1 - 1;
     Bb += static_cast<size_t>(t.expert) * p.b_expert_stride;
@@ -471,7 +473,18 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
   if constexpr (MODE == kMoeFc1) {
     // acc[i][0] is gate, acc[i][1] up, of output columns
     // n0 + 32 wn + 8 (v / 4) + 4 (lane / 32) + v % 4; 32 x 32 blocks staged
-    // in 80-byte rows.
+    // in 80-byte rows.  The expert's fc1 biases (gate row col, up row N + col)
+    // are added before the activation.
+    float bg[4][4], bu[4][4];
+    const uint16_t *b1 = p.bias ? p.bias + static_cast<size_t>(expert) * p.w_rows : nullptr;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int col = n0 + 32 * wn + 8 * q + 4 * khalf + e;
+        bg[q][e] = b1 ? bits_to_f32<ACT>(b1[col]) : 0.0f;
+        bu[q][e] = b1 ? bits_to_f32<ACT>(b1[p.N + col]) : 0.0f;
+      }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       if (row_lo + wm * Cfg::WTM + 32 * i > row_last) break;   // block holds no rows
@@ -480,7 +493,7 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float g = acc[i][0][4 * q + e], u = acc[i][1][4 * q + e];
+          const float g = acc[i][0][4 * q + e] + bg[q][e], u = acc[i][1][4 * q + e] + bu[q][e];
           v[e] = g / (1.0f + __expf(-g)) * u;
         }
         *reinterpret_cast<u32x2 *>(stg + row_in * 80 + (8 * q + 4 * khalf) * 2) =

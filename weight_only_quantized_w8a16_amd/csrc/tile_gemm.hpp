@@ -37,7 +37,7 @@ struct TileProblem {
   const uint16_t *A;         // dense: [M, K]; fc1: x [T, K] gathered; fc2: act [R, K]
   const uint8_t *B;          // tiled codes (expert 0 for MoE)
   const uint16_t *S, *Z;     // scales / zeros (expert 0 for MoE)
-  const uint16_t *bias;      // dense only, [N] or null
+  const uint16_t *bias;      // dense: [N] or null; fc1: expert biases [E, 2N] or null
   uint16_t *C;               // dense: [M, N]; fc1: act [R, N]; fc2: y [R, N]
   int M, N, K;               // N = output columns (fc1: inter)
   int group;                 // 64 / 128 (w4); 0 (w8 per channel)
@@ -138,6 +138,7 @@ __device__ __forceinline__ void tile_gemm(const TileProblem &p, int tile_m, int 
   int row_lo, row_hi;         // valid global row range of this tile
   const uint8_t *Bbase = p.B;
   const uint16_t *Sbase = p.S, *Zbase = p.Z;
+  [[maybe_unused]] const uint16_t *b1base = nullptr;   // fc1: this expert's [2 N] bias
   if constexpr (MODE == kDense) {
     row_lo = tile_m * BM;
     row_hi = min(p.M, row_lo + BM);
@@ -148,6 +149,7 @@ __device__ __forceinline__ void tile_gemm(const TileProblem &p, int tile_m, int 
     Bbase += static_cast<size_t>(t.expert) * p.b_expert_stride;
     Sbase += static_cast<size_t>(t.expert) * p.s_expert_stride;
     if (Zbase) Zbase += static_cast<size_t>(t.expert) * p.s_expert_stride;
+    if (MODE == kMoeFc1 && p.bias) b1base = p.bias + static_cast<size_t>(t.expert) * p.w_rows;
   }
   const int n0 = (MODE == kMoeFc1) ? tile_n * (BN / 2) : tile_n * BN;
 
@@ -366,11 +368,14 @@ __device__ __forceinline__ void tile_gemm(const TileProblem &p, int tile_m, int 
 #pragma unroll
       for (int jn = 0; jn < HALF; ++jn) {
         const int col = n0 + wn * (Cfg::WTN / 2) + 32 * jn + col_in;
+        // fc1 biases of the gate and up rows (before the activation)
+        const float bg = b1base ? bits_to_f32<ACT>(b1base[col]) : 0.0f;
+        const float bu = b1base ? bits_to_f32<ACT>(b1base[p.N + col]) : 0.0f;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int r = row_lo + wm * Cfg::WTM + 32 * i + 8 * (v >> 2) + 4 * khalf + (v & 3);
           if (r < row_hi) {
-            const float g = acc[i][jn][v], u = acc[i][jn + HALF][v];
+            const float g = acc[i][jn][v] + bg, u = acc[i][jn + HALF][v] + bu;
             const float a = g / (1.0f + __expf(-g)) * u;
             p.C[static_cast<size_t>(r) * p.N + col] = f32_to_bits<ACT>(a);
           }
