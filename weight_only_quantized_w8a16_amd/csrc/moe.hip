@@ -225,11 +225,30 @@ __global__ __launch_bounds__(1024) void k_moe_plan(const int32_t *__restrict__ i
   }
 }
 
+// The grid is sized for the most expert tiles routing can produce; the plan
+// writes how many there are.  Workgroups past ntiles * tiles_n exit; the
+// others (the first ones dispatched, so spread evenly over the XCDs, which
+// take workgroup b on XCD b % 8) are renumbered so that each XCD walks a
+// contiguous run of (row tile, column tile) pairs: all column tiles of an
+// expert row tile then share one XCD's L2 for the tile's activation rows,
+// instead of every XCD fetching them (with 8 or 11 column tiles and plain
+// order each column tile sat on its own XCD).
+__device__ __forceinline__ bool moe_tile_of(const TileProblem &p, int tiles_n, int &tm, int &tn) {
+  const int real = *p.ntiles * tiles_n;
+  const int b = blockIdx.x;
+  if (b >= real) return false;
+  const int xcd = b & 7, loc = b >> 3, per = real >> 3, rem = real & 7;
+  const int id = (xcd < rem) ? xcd * (per + 1) + loc : rem * (per + 1) + (xcd - rem) * per + loc;
+  tm = id / tiles_n;
+  tn = id - tm * tiles_n;
+  return true;
+}
+
 template <int ACT, int MODE>
 __global__ __launch_bounds__(CfgMoe::NTHR) void k_moe_gemm(TileProblem p, int tiles_n) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
-  if (tm >= *p.ntiles) return;
+  int tm, tn;
+  if (!moe_tile_of(p, tiles_n, tm, tn)) return;
   tile_gemm<CfgMoe, ACT, 4, MODE>(p, tm, tn, lds);
 }
 
@@ -240,8 +259,8 @@ __global__ __launch_bounds__(CfgMoeDma::NTHR) void k_moe_dma(TileProblem p, int 
   __shared__ __attribute__((aligned(16))) char b0[CfgMoeDma::STAGE_B];
   __shared__ __attribute__((aligned(16))) char b1[CfgMoeDma::STAGE_B];
   __shared__ __attribute__((aligned(16))) char sc[2 * CfgMoeDma::SC_WIN];
-  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
-  if (tm >= *p.ntiles) return;
+  int tm, tn;
+  if (!moe_tile_of(p, tiles_n, tm, tn)) return;
   const DmaLds L{{a0, a1}, {b0, b1}, sc};
   tile_gemm_dma<CfgMoeDma, ACT, 4, MODE>(p, tm, tn, L);
 }
