@@ -37,7 +37,8 @@
  *    tokens == 0) is a successful no-op that reads no pointer; k must be
  *    positive (repack and dequant also accept k == 0).  The first failed
  *    check decides the status, in the order: sizes, NULL pointers, dtypes,
- *    group size (or W8A8 quant mode), tile multiples, alignment, workspace.
+ *    mode arguments (W8A8 quant mode, table layout, MoE normalization), group
+ *    size, tile multiples, alignment, workspace.
  *  - Functions are reentrant; calls on different streams may overlap unless
  *    they share a workspace.
  */
