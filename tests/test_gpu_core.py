@@ -35,6 +35,25 @@ def test_repack_w4_matches_documented_layout_and_inverts(n, k):
     assert np.array_equal(back.cpu().numpy(), packed)
 
 
+@pytest.mark.parametrize("bits", [4, 8])
+def test_repack_by_row_chunks_equals_whole(bits):
+    # The tiled layouts are tile-major over 16-row channel tiles, so repacking
+    # a weight in row chunks (multiples of 16, as a loader streaming a large
+    # table would) and concatenating gives the bytes of the whole repack.
+    n, k = 1040, 1024
+    rng = np.random.default_rng(bits)
+    if bits == 4:
+        src = rng.integers(0, 256, (n, k // 2), dtype=np.uint8)
+        rep = qg.repack_w4
+    else:
+        src = rng.integers(-128, 128, (n, k)).astype(np.int8)
+        rep = qg.repack_w8
+    whole = rep(to_dev(src)).cpu().numpy()
+    cuts = [0, 16, 400, 656, 1040]
+    parts = [rep(to_dev(np.ascontiguousarray(src[a:b]))).cpu().numpy() for a, b in zip(cuts, cuts[1:])]
+    assert np.array_equal(np.concatenate(parts), whole)
+
+
 @pytest.mark.parametrize("n,k", [(16, 64), (32, 192), (3584, 3584)])
 def test_repack_w8_matches_documented_layout_and_inverts(n, k):
     codes = np.random.default_rng(n * k).integers(-128, 128, (n, k)).astype(np.int8)
