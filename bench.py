@@ -544,6 +544,37 @@ def run(args):
         ceil = {"copy_GBps": round(2 * nbytes / (ms * 1e-3) / 1e9, 1),
                 "note": "torch device copy of 1 GiB, read + write bytes"}
         del bufs
+        # Streaming-read probe over the decode step's byte counts (rotating
+        # over 1 GiB of distinct bytes so nothing is served from the
+        # Infinity Cache), and an empty launch: the read floor of each GEMV.
+        big = torch.empty(ROTATE_BYTES + (256 << 20), dtype=torch.uint8, device=dev)
+        outp = torch.empty(int(qg.lib().qg_read_probe_blocks(1 << 30)), dtype=torch.int32, device=dev)
+        probe, floor_us = {}, 0.0
+        for n in [0] + DECODE_N:
+            b = w4_bytes(1, n, DECODE_K, DECODE_G) // 16 * 16 if n else 0
+            slots = max(1, ROTATE_BYTES // max(b, 1)) if b else 1
+            reps = max(20, K // 2)
+
+            def call(i, b=b, slots=slots):
+                off = (i % slots) * b
+                qg.read_probe(big[off:off + b] if b else None, b, outp)
+            for i in range(3):
+                call(i)
+            us = timed(call, reps, warm=reps) / reps * 1e3
+            key = f"N{n}" if n else "empty_launch"
+            probe[key] = {"us": round(us, 2), "bytes": b,
+                          "GBps": round(b / (us * 1e-6) / 1e9, 1) if b else None}
+            if n:
+                floor_us += us
+        ceil["read_probe"] = probe
+        ceil["read_floor_step_us"] = round(floor_us, 2)
+        ceil["read_floor_step_GBps"] = round(step_bytes / (floor_us * 1e-6) / 1e9, 1)
+        ceil["decode_step_vs_read_floor"] = round(floor_us / (ms_per_step * 1e3), 3)
+        # the headline kernel against a plain read of the same bytes
+        pr = probe[f"N{DECODE_N[-1]}"]["GBps"]
+        roofline["read_probe_GBps"] = pr
+        roofline["frac_of_read_probe"] = round(roofline["achieved"] / pr, 3)
+        del big, outp
         torch.cuda.empty_cache()
         log(f"ceiling: {ceil}")
 

@@ -330,6 +330,18 @@ qg_status qmoe_grouped_ex(const void *x, const float *logits, const float *sel_l
                           qg_dtype act_dtype, int32_t *topk_ids_out, float *topk_w_out,
                           void *workspace, size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Measurement probe (no part of the method): the ceiling the HBM-bound
+ * kernels are compared with.  Reads `bytes` (a multiple of 16) of `buf` once
+ * with 16-byte streaming loads, the grid sweeping one contiguous window, and
+ * writes one 32-bit XOR of what it read per workgroup to `out` (device, at
+ * least qg_read_probe_blocks(bytes) entries).  bytes == 0 launches one
+ * workgroup that reads nothing: the cost of a launch.  buf 16-byte aligned
+ * (may be NULL when bytes == 0), out 4-byte aligned.
+ * ---------------------------------------------------------------------- */
+size_t qg_read_probe_blocks(size_t bytes);
+qg_status qg_read_probe(const void *buf, size_t bytes, uint32_t *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -316,3 +316,14 @@ def moe_ex(**kw):
 ])
 def test_moe_ex_validation(kw, status):
     assert moe_ex(**kw) == status
+
+
+def test_read_probe_validation_and_blocks():
+    L = qg.lib()
+    assert L.qg_read_probe(FAKE, 24, FAKE, None) == SHAPE
+    assert L.qg_read_probe(None, 16, FAKE, None) == NULL
+    assert L.qg_read_probe(FAKE, 16, None, None) == NULL
+    assert L.qg_read_probe(FAKE + 8, 16, FAKE, None) == ALIGN
+    assert L.qg_read_probe(FAKE, 16, FAKE + 2, None) == ALIGN
+    assert L.qg_read_probe_blocks(0) == 1
+    assert 1 <= L.qg_read_probe_blocks(1 << 30) <= 4096

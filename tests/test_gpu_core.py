@@ -377,3 +377,19 @@ def test_prefill_dma_tile_odd_group_count_falls_back(tile, monkeypatch):
     monkeypatch.setenv("QGEMM_PREFILL_TILE", tile)
     got = to_bits(_run_w4(p, "prefill"))
     assert np.array_equal(got, _exact_expected(Cref, BF16))
+
+
+@pytest.mark.parametrize("nbytes", [0, 16, 4096 + 48, 10 * (1 << 20) + 160])
+def test_read_probe_reads_every_byte_once(nbytes):
+    # The streaming-read probe XOR-folds what it reads; the XOR of its
+    # per-workgroup words equals the XOR of every 32-bit word of the range.
+    rng = np.random.default_rng(nbytes)
+    host = rng.integers(0, 2 ** 32, (nbytes + 64) // 4, dtype=np.uint32)
+    buf = to_dev(host)
+    blocks = int(qg.lib().qg_read_probe_blocks(nbytes))
+    out = torch.zeros(blocks, dtype=torch.int32, device="cuda")
+    qg.read_probe(buf if nbytes else None, nbytes, out)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
+    want = np.bitwise_xor.reduce(host[: nbytes // 4]) if nbytes else np.uint32(0)
+    assert got == want

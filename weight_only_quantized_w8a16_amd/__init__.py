@@ -21,7 +21,7 @@ __all__ = [
     "QGemmError", "lib", "repack_w4", "unrepack_w4", "repack_w8", "unrepack_w8", "repack_w8_kn",
     "unrepack_w8_kn", "quantize_w4", "dequant_w4", "dequant_w8", "gemm_w4a16", "gemm_w8a16",
     "moe_grouped", "moe_workspace_size", "gemm_workspace_size", "dtype_code", "gemm_w8a8",
-    "w8a8_workspace_size", "embed_w4", "embed_w8",
+    "w8a8_workspace_size", "embed_w4", "embed_w8", "read_probe",
 ]
 
 _CODES = {torch.bfloat16: QG_BF16, torch.float16: QG_FP16, torch.float32: QG_FP32}
@@ -314,6 +314,23 @@ def embed_w8(ids: torch.Tensor, table: torch.Tensor, scales: torch.Tensor, group
         _ptr(ids), ids.numel(), _ptr(table), QG_LAYOUT_TILED if tiled else QG_LAYOUT_PORTABLE,
         _ptr(scales), _ptr(out), vocab, hidden, group_size, dtype_code(scales.dtype),
         dtype_code(out.dtype), _stream(table)))
+    return out
+
+
+# -- measurement probe -----------------------------------------------------------
+
+def read_probe(buf: Optional[torch.Tensor], nbytes: int, out: torch.Tensor) -> torch.Tensor:
+    """Stream-read the first nbytes of buf once (the HBM read ceiling); out
+    (uint32/int32, >= qg_read_probe_blocks(nbytes) entries) gets one XOR word
+    per workgroup.  nbytes == 0: one empty workgroup (the launch cost)."""
+    _dev(out, "out")
+    if buf is not None:
+        _dev(buf, "buf")
+        if nbytes > buf.numel() * buf.element_size():
+            raise QGemmError("qg_read_probe", 2, "nbytes exceeds the buffer")
+    if out.numel() < int(lib().qg_read_probe_blocks(nbytes)):
+        raise QGemmError("qg_read_probe", 2, "out is too small")
+    check("qg_read_probe", lib().qg_read_probe(_ptr(buf), nbytes, _ptr(out), _stream(out)))
     return out
 
 

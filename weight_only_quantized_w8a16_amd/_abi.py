@@ -49,6 +49,8 @@ SIGNATURES = {
     "qgemm_w8a8": (_ST, [_P, _P, _INT, _P, _P, _P, _INT, _INT, _INT, _INT, _P, _SZ, _P]),
     "qembed_w4": (_ST, [_P, _INT, _P, _INT, _P, _P, _P, _INT, _INT, _INT, _INT, _INT, _P]),
     "qembed_w8": (_ST, [_P, _INT, _P, _INT, _P, _P, _INT, _INT, _INT, _INT, _INT, _P]),
+    "qg_read_probe_blocks": (_SZ, [_SZ]),
+    "qg_read_probe": (_ST, [_P, _SZ, _P, _P]),
     "qmoe_workspace_size": (_SZ, [_INT, _INT, _INT, _INT, _INT]),
     "qmoe_grouped": (_ST, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _INT, _INT, _INT, _INT, _INT, _INT,
                            _INT, _P, _P, _P, _SZ, _P]),

@@ -399,4 +399,16 @@ qg_status qmoe_grouped_ex(const void *x, const float *logits, const float *sel_l
                   ws_bytes, stream);
 }
 
+// ---------------------------------------------------------------------------
+// Measurement probe
+// ---------------------------------------------------------------------------
+size_t qg_read_probe_blocks(size_t bytes) { return qg::read_probe_blocks(bytes); }
+
+qg_status qg_read_probe(const void *buf, size_t bytes, uint32_t *out, void *stream) {
+  if (bytes % 16 != 0) return QG_ERR_SHAPE;
+  if (!out || (bytes && !buf)) return QG_ERR_NULL;
+  if ((buf && !aligned(buf, 16)) || !aligned(out, 4)) return QG_ERR_ALIGN;
+  return hip_status(qg::launch_read_probe(buf, bytes, out, as_stream(stream)));
+}
+
 }  // extern "C"

@@ -1,0 +1,64 @@
+// probe.hip -- a plain streaming read, the ceiling the HBM-bound kernels are
+// measured against.  Each thread reads 16-byte pieces with streaming
+// (nontemporal) loads; in iteration i workgroup b reads piece
+// (i * gridDim + b) * blockDim + thread, so at every moment the grid sweeps one
+// contiguous window of the buffer.  The pieces are XOR-folded and each
+// workgroup writes one 32-bit word, so the loads cannot be dropped.
+#include "qg_common.hpp"
+#include "qg_launch.hpp"
+
+namespace qg {
+
+namespace {
+// Measured on MI355X (151 MB / 15.4 MB / 2.4 MB, rotated over 1 GiB): 256
+// threads, up to 4096 workgroups, two pieces in flight per thread read
+// fastest at the small sizes and within 1 % of the best at 151 MB, against
+// 512 x 1024 x 4, 256 x 2048 x 4, 256 x 1024 x 8, 1024 x 256 x 8 and
+// 256 x 512 x 16.
+constexpr int kProbeThreads = 256;
+constexpr unsigned kProbeMaxBlocks = 4096;
+constexpr int kDepth = 2;
+}  // namespace
+
+__global__ __launch_bounds__(kProbeThreads) void k_read_probe(const u32x4 *__restrict__ buf,
+                                                              unsigned long long pieces,
+                                                              uint32_t *__restrict__ out) {
+  __shared__ uint32_t part[kProbeThreads / 64];
+  const unsigned long long stride = static_cast<unsigned long long>(gridDim.x) * blockDim.x;
+  unsigned long long q = static_cast<unsigned long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  // kDepth pieces in flight per thread per iteration.
+  for (; q + (kDepth - 1) * stride < pieces; q += kDepth * stride) {
+    u32x4 v[kDepth];
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i) v[i] = __builtin_nontemporal_load(buf + q + i * stride);
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i) acc ^= v[i];
+  }
+  for (; q < pieces; q += stride) acc ^= __builtin_nontemporal_load(buf + q);
+  uint32_t x = acc.x ^ acc.y ^ acc.z ^ acc.w;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x ^= __shfl_xor(x, off);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = 0;
+    for (int w = 0; w < kProbeThreads / 64; ++w) r ^= part[w];
+    out[blockIdx.x] = r;
+  }
+}
+
+size_t read_probe_blocks(size_t bytes) {
+  const unsigned long long pieces = bytes / 16;
+  const unsigned long long want = (pieces + 1ull * kDepth * kProbeThreads - 1) / (1ull * kDepth * kProbeThreads);
+  return want < 1 ? 1 : (want > kProbeMaxBlocks ? kProbeMaxBlocks : static_cast<size_t>(want));
+}
+
+hipError_t launch_read_probe(const void *buf, size_t bytes, uint32_t *out, hipStream_t s) {
+  const unsigned blocks = static_cast<unsigned>(read_probe_blocks(bytes));
+  hipLaunchKernelGGL(k_read_probe, dim3(blocks), dim3(kProbeThreads), 0, s,
+                     static_cast<const u32x4 *>(buf), static_cast<unsigned long long>(bytes / 16), out);
+  return hipGetLastError();
+}
+
+}  // namespace qg

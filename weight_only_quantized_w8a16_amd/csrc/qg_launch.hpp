@@ -114,3 +114,11 @@ struct EmbedArgs {
 hipError_t launch_embed(const EmbedArgs &a, hipStream_t s);
 
 }  // namespace qg
+
+namespace qg {
+
+// Streaming-read probe (measurement).
+size_t read_probe_blocks(size_t bytes);
+hipError_t launch_read_probe(const void *buf, size_t bytes, uint32_t *out, hipStream_t s);
+
+}  // namespace qg
