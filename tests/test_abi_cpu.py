@@ -196,6 +196,7 @@ def test_workspace_query_and_alignment():
     assert L.qgemm_workspace_size(128, 3072, 2048, 64, 4) == 2 * 128 * 3072 * 4
     assert L.qgemm_workspace_size(128, 3584, 3584, -1, 8) == 2 * 128 * 3584 * 4
     for args in [(512, 3072, 2048, 64, 4), (16, 3072, 2048, 64, 4), (128, 131072, 2048, 64, 4),
+                 (128, 18944, 3584, -1, 8),
                  (0, 3072, 2048, 64, 4), (128, 3072, 2048, 64, 5), (128, 3072, 2048, 96, 4)]:
         assert L.qgemm_workspace_size(*args) == 0, args
     # a workspace that is given must be 256-byte aligned (checked before any launch)

@@ -247,8 +247,9 @@ int choose_tile(const GemmArgs &a) {
 // saves, except on the 64 x 64 tile at up to 128 rows with a long K loop
 // (few small tiles, each walking all of K): there two slices gain 15 %
 // (M = 128: N = 3072, K = 2048, int4 16.5 -> 13.9 us; N = 3584, K = 3584,
-// int8 20.4 -> 17.3 us), while at 256 rows and above, and on the larger
-// tiles, splitting was slower.  A slice is a whole number of scale windows
+// int8 20.4 -> 17.3 us), while at 256 rows and above, on the larger tiles,
+// and once the 64 x 64 tiles alone number 256 or more (M = 128, N = 18944,
+// K = 3584, int8: 45 us unsplit, 51 us in two slices), splitting was slower.  A slice is a whole number of scale windows
 // (8 groups) when the scales come through the direct-load tile's windows,
 // a multiple of 8 steps otherwise.  QGEMM_SPLITK=<n> asks for n slices (1:
 // none) on the tile chosen above (tests and tuning).
@@ -261,7 +262,8 @@ struct Plan {
 Plan plan_prefill(const GemmArgs &a, int wbits, bool gs8) {
   Plan pl{choose_tile(a), Split{}, 0};
   const int nsteps = a.K / 64;
-  int want = (pl.tile == kS && a.M <= 128 && nsteps >= 32) ? 2 : 1;
+  const int tiles_s = ((a.M + 63) / 64) * (a.N / 64);
+  int want = (pl.tile == kS && a.M <= 128 && nsteps >= 32 && tiles_s < 256) ? 2 : 1;
   if (const char *o = std::getenv("QGEMM_SPLITK")) want = std::atoi(o);
   if (want <= 1) return pl;
   const int g = a.group > 0 ? a.group : a.K;
