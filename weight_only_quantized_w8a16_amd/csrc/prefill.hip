@@ -248,8 +248,10 @@ int choose_tile(const GemmArgs &a) {
 // (few small tiles, each walking all of K): there two slices gain 15 %
 // (M = 128: N = 3072, K = 2048, int4 16.5 -> 13.9 us; N = 3584, K = 3584,
 // int8 20.4 -> 17.3 us), while at 256 rows and above, on the larger tiles,
-// and once the 64 x 64 tiles alone number 256 or more (M = 128, N = 18944,
-// K = 3584, int8: 45 us unsplit, 51 us in two slices), splitting was slower.  A slice is a whole number of scale windows
+// and once the 64 x 64 tiles alone number 256 or more (M = 128, K = 3584,
+// int8, N = 18944: 45 us unsplit, 51 us in two slices; K = 2048, int4,
+// N = 13312: 29.5 / 38.8 us, N = 8192: 23.9 / 25.3 us, while N = 4096, 128
+// tiles, gains: 23.1 / 18.6 us), splitting was slower.  A slice is a whole number of scale windows
 // (8 groups) when the scales come through the direct-load tile's windows,
 // a multiple of 8 steps otherwise.  QGEMM_SPLITK=<n> asks for n slices (1:
 // none) on the tile chosen above (tests and tuning).
