@@ -601,6 +601,27 @@ def run(args):
                "kind": "oracle",
                "sample": f"{passes} full passes of the M=1 decode step "
                          f"(N={DECODE_N}, K=2048, g=64) in {t_cpu:.1f}s, fp64 accumulation"}
+        # The same oracle on one thread (a child process with OMP_NUM_THREADS=1,
+        # about three seconds of the two smallest GEMVs of the step).
+        import subprocess
+        code = ("import sys, time; sys.path.insert(0, %r); import oracle, synth_inputs as si\n"
+                "A = si.activations(1, 2048, si.seed_of('cfg1', 'a', 1, 2048))\n"
+                "ps = [si.w4_weights(n, 2048, 64, si.seed_of('cfg1', 'w', n, 2048, 64))[:3] "
+                "for n in (2048, 3072)]\n"
+                "b = sum(n * 1024 + 4 * n * 32 + 4096 + 2 * n for n in (2048, 3072))\n"
+                "oracle.gemm_w4(A, *ps[0], 64); t0 = time.perf_counter(); k = 0\n"
+                "while time.perf_counter() - t0 < 3.0:\n"
+                "    [oracle.gemm_w4(A, *p, 64) for p in ps]; k += 1\n"
+                "print(k * b / (time.perf_counter() - t0) / 1e9)\n") % ROOT
+        try:
+            env = dict(os.environ, OMP_NUM_THREADS="1")
+            outp = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True,
+                                  text=True, timeout=120)
+            cpu["single_thread"] = {"value": round(float(outp.stdout.strip().splitlines()[-1]), 3),
+                                    "unit": "GB/s", "cores": 1,
+                                    "sample": "M=1 GEMVs N in {2048, 3072}, K=2048, g=64, ~3 s"}
+        except Exception as exc:   # report, do not fail the benchmark over it
+            cpu["single_thread"] = {"error": str(exc)[:200]}
         log(f"cpu baseline: {cpu}")
 
     result = {
