@@ -92,3 +92,16 @@ def test_split_random_data_within_tolerance(monkeypatch):
     C = torch.from_numpy(got.view(np.int16)).view(torch.bfloat16).float().numpy()
     err = np.abs(C - Cref).max() / np.abs(Cref).max()
     assert err <= 1e-2, err
+
+
+@pytest.mark.parametrize("n,split", [(4032, True), (8128, True), (8192, False), (13312, False)])
+def test_split_threshold_by_tile_count(n, split):
+    # M = 128 on the 64 x 64 tile splits K only while those tiles number
+    # fewer than 256 (2 x 127 = 254 splits, 2 x 128 = 256 does not); both
+    # sides give the exact result.
+    m, k, g = 128, 2048, 64
+    ws = qg.gemm_workspace_size(m, n, k, g, 4)
+    assert (ws > 0) == split, (n, ws)
+    p = si.w4_exact_problem(m, n, k, g, seed=n, dtype=BF16, bias_dtype=FP16)
+    exp = expected(oracle.gemm_w4(p.A, p.packed, p.scale, p.zero, g, BF16, p.bias, FP16), BF16)
+    assert np.array_equal(run_w4(p), exp)
