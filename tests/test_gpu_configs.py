@@ -136,6 +136,8 @@ def test_repeated_calls_are_deterministic():
 @pytest.mark.parametrize("m,n,k,g,bias", [
     (1, 65536, 2048, 64, False), (2, 65536, 2048, 128, True), (1, 65536, 512, 64, True),
     (2, 65536, 4096, 64, False), (1, 65536, 1152, 128, False), (3, 65536, 2048, 64, True),
+    (4, 65536, 2048, 64, False), (5, 65536, 2048, 128, True), (8, 65536, 2048, 64, True),
+    (8, 65536, 4096, 64, False), (6, 131072, 2048, 64, False),
 ])
 def test_large_n_decode(m, n, k, g, bias):
     p = si.w4_problem(m, n, k, g, tag="stream", bias_dtype=FP16 if bias else si.NONE)

@@ -393,3 +393,20 @@ def test_read_probe_reads_every_byte_once(nbytes):
     got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
     want = np.bitwise_xor.reduce(host[: nbytes // 4]) if nbytes else np.uint32(0)
     assert got == want
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 7, 8])
+@pytest.mark.parametrize("group,dtype", [(64, BF16), (128, FP16)])
+def test_large_n_decode_integer_exact(m, group, dtype):
+    # Many channel tiles (N = 65536): one or two rows run the streaming decode
+    # kernel, more rows the split-K one; on integer-exact inputs every output
+    # is RNE of the exact sum.
+    n, k = 65536, 2048
+    p = si.w4_exact_problem(m, n, k, group, seed=m * 7 + group, dtype=dtype, bias_dtype=FP16)
+    C = to_bits(_run_w4(p))
+    rows = np.arange(m)
+    cols = np.unique(np.concatenate([[0, 15, 16, n - 1], np.random.default_rng(m).integers(0, n, 300)]))
+    r, c = np.meshgrid(rows, cols, indexing="ij")
+    ref = oracle.gemm_w4_at(p.A, p.packed, p.scale, p.zero, group, r.ravel(), c.ravel(), dtype,
+                            p.bias, FP16)
+    assert np.array_equal(C[r.ravel(), c.ravel()], _exact_expected(ref, dtype))
