@@ -296,8 +296,12 @@ __global__ __launch_bounds__(decode_threads<BPW>()) void k_decode_w8(const uint1
 // R: accumulator rows per lane that can hold a live output (lane rows are
 // m = 4 * (lane / 16) + r): M = 1 needs r = 0 only, M = 2 r < 2.  Only the
 // live rows get the per-group scale update, which is most of the VALU work.
+// Register budget for five resident waves per SIMD (five workgroups per CU):
+// measured on MI355X at M = 1, N = 131072, K = 2048, 27.2-27.5 us against
+// 27.5-27.6 with four and 27.9-28.3 with the compiler's default budget (three
+// waves); six (28.9) and eight (31.6, with spills) were slower.
 template <int ACT, int G, int SEG, int R>
-__global__ __launch_bounds__(256) void k_decode_w4_stream(const uint16_t *__restrict__ A,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void k_decode_w4_stream(const uint16_t *__restrict__ A,
                                                           const u32x4 *__restrict__ Bt,
                                                           const uint16_t *__restrict__ S,
                                                           const uint16_t *__restrict__ Z,
@@ -444,9 +448,9 @@ hipError_t launch_stream(const GemmArgs &a, hipStream_t s) {
   const int ntiles = a.N >> 4;
   const size_t lds = static_cast<size_t>(a.M) * (2 * a.K + 16) + static_cast<size_t>(a.K / G) * 64;
   auto kern = k_decode_w4_stream<ACT, G, SEG, R>;
-  // One resident pass: 4 workgroups of 4 waves per CU on 256 CUs.
+  // One resident pass: 5 workgroups of 4 waves per CU on 256 CUs.
   int grid = (ntiles + 3) / 4;
-  if (grid > 1024) grid = 1024;
+  if (grid > 1280) grid = 1280;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, s, a.A, static_cast<const u32x4 *>(a.B),
                      a.S, a.Z, a.bias, a.bias_dt, a.C, a.M, a.N, a.K);
   return hipGetLastError();
