@@ -303,12 +303,6 @@ __global__ __launch_bounds__(256) void k_moe_combine(const uint16_t *__restrict_
 
 namespace {
 
-template <class K>
-hipError_t set_lds(K kern, int bytes) {
-  return hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-}
-
 template <int ACT>
 hipError_t run_moe(const MoeArgs &a, hipStream_t s) {
   const MoeLayout L = moe_layout(a.T, a.H, a.I, a.E, a.topk);
@@ -342,13 +336,11 @@ hipError_t run_moe(const MoeArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(k_moe_plan, dim3(1), dim3(1024), 0, s, ids, R, a.E, a.topk, bm, tiles, ntiles,
                      row_src, dest);
 
-  static bool attr = false;
-  if (!attr) {
-    hipError_t e = set_lds(k_moe_gemm<ACT, kMoeFc1>, CfgMoe::LDS);
-    if (e == hipSuccess) e = set_lds(k_moe_gemm<ACT, kMoeFc2>, CfgMoe::LDS);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
+  static std::atomic<uint64_t> attr_fc1{0}, attr_fc2{0};
+  if (hipError_t e = set_lds_limit_once(k_moe_gemm<ACT, kMoeFc1>, CfgMoe::LDS, attr_fc1); e != hipSuccess)
+    return e;
+  if (hipError_t e = set_lds_limit_once(k_moe_gemm<ACT, kMoeFc2>, CfgMoe::LDS, attr_fc2); e != hipSuccess)
+    return e;
   TileProblem p1{};
   p1.A = a.x;
   p1.B = a.w1;

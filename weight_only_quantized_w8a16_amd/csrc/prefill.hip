@@ -165,13 +165,8 @@ hipError_t run(const GemmArgs &a, hipStream_t s, const Split &sp = Split{}) {
   const TileProblem p = dense_problem(a, sp);
   const int tm = (a.M + Cfg::BM - 1) / Cfg::BM, tn = a.N / Cfg::BN;
   auto kern = k_prefill<Cfg, ACT, WBITS, GS8>;
-  static bool attr_set = false;   // benign race: idempotent
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::LDS);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> attr_done{0};
+  if (hipError_t e = set_lds_limit_once(kern, Cfg::LDS, attr_done); e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(tm * tn * sp.nsplit), dim3(Cfg::NTHR), Cfg::LDS, s, p, tn);
   return reduce_split<ACT, WBITS, GS8>(a, sp, s);
 }

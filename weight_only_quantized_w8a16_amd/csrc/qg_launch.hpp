@@ -8,7 +8,26 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace qg {
+
+// Raises a kernel's dynamic-LDS limit to `bytes` once per device (the
+// attribute belongs to the current device's copy of the kernel): `done`
+// holds one bit per device id, set after a successful call.  Concurrent
+// first calls may both set it, which is harmless.
+template <class Kern>
+hipError_t set_lds_limit_once(Kern kern, int bytes, std::atomic<uint64_t> &done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t(1) << dev) : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
 
 hipError_t launch_repack_w4(const uint8_t *src, uint8_t *dst, int n, int k, hipStream_t s);
 hipError_t launch_unrepack_w4(const uint8_t *src, uint8_t *dst, int n, int k, hipStream_t s);
