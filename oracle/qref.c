@@ -7,8 +7,10 @@
  * check and the benchmark's CPU-baseline leg may load it.  It shares no code,
  * header, table or helper with the HIP library; neither includes the other.
  *
- * Every floating-point reduction accumulates in double.  Nothing is blocked,
- * fused or reordered beyond the definitions cited at each function.
+ * Every floating-point reduction accumulates in double, except the two
+ * qref_gemm_*_f32acc functions, which carry the same sums in fp32 (the
+ * timed CPU baseline).  Nothing is blocked, fused or reordered beyond the
+ * definitions cited at each function.
  *
  * Sources (the three web pages this work is built from):
  *   [acext]   "acext User Guide (v1.7)": 1.2.1 fpAintB GEMM (argument set of
@@ -43,6 +45,7 @@
  *   patterns (uint16_t).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -50,6 +53,22 @@
 #define QREF_NONE 0
 #define QREF_BF16 1
 #define QREF_FP16 2
+
+/* Threads: the OpenMP loops below run on omp_get_max_threads() threads
+ * unless qref_set_threads() picked a count; qref_team_size() reports the
+ * size of the team a parallel region actually gets (what a timing used). */
+int qref_threads(void) { return omp_get_max_threads(); }
+void qref_set_threads(int n) { if (n > 0) omp_set_num_threads(n); }
+int qref_team_size(void)
+{
+    int t = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        t = omp_get_num_threads();
+    }
+    return t;
+}
 
 /* ---------------------------------------------------------------------- */
 /* 16-bit float <-> fp32, from the IEEE-754 / bfloat16 bit definitions.     */
@@ -335,6 +354,60 @@ void qref_gemm_w8(const uint16_t *A, const int8_t *codes, const uint16_t *scale,
             dequant8_row(codes, scale, col, k, group, dtype, w);
             double b = bias_value(bias, col, bias_dtype);
             for (int64_t row = 0; row < m; ++row) C[row * n + col] = dot_row(A, row, k, dtype, w) + b;
+        }
+        free(w);
+    }
+}
+
+/* The same GEMMs with the sum carried in fp32 instead of double: each
+ * product A[m, k] * W[n, k] rounds to fp32, then each add rounds (no fused
+ * multiply-add: the library is built with contraction off), in k order, and
+ * the bias is added last in fp32.  This is the plain fp32-accumulating CPU
+ * GEMM whose speed the benchmark reports beside the GPU's; its results are
+ * checked against the double-accumulating definition above (they agree to
+ * fp32 rounding of a K-term sum). */
+static float dot_row_f32(const uint16_t *A, int64_t m, int64_t k, int dtype, const float *w)
+{
+    float acc = 0.0f;
+    for (int64_t c = 0; c < k; ++c) acc += act_to_f32(A[m * k + c], dtype) * w[c];
+    return acc;
+}
+
+static float bias_value_f32(const uint16_t *bias, int64_t col, int bias_dtype)
+{
+    if (!bias || bias_dtype == QREF_NONE) return 0.0f;
+    return act_to_f32(bias[col], bias_dtype);
+}
+
+void qref_gemm_w4_f32acc(const uint16_t *A, const uint8_t *packed, const uint16_t *scale,
+                         const uint16_t *zero, const uint16_t *bias, int64_t m, int64_t n,
+                         int64_t k, int64_t group, int dtype, int bias_dtype, float *C)
+{
+#pragma omp parallel
+    {
+        float *w = (float *)malloc(sizeof(float) * (size_t)k);
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t col = 0; col < n; ++col) {
+            dequant4_row(packed, scale, zero, col, k, group, dtype, w);
+            float b = bias_value_f32(bias, col, bias_dtype);
+            for (int64_t row = 0; row < m; ++row) C[row * n + col] = dot_row_f32(A, row, k, dtype, w) + b;
+        }
+        free(w);
+    }
+}
+
+void qref_gemm_w8_f32acc(const uint16_t *A, const int8_t *codes, const uint16_t *scale,
+                         const uint16_t *bias, int64_t m, int64_t n, int64_t k, int64_t group,
+                         int dtype, int bias_dtype, float *C)
+{
+#pragma omp parallel
+    {
+        float *w = (float *)malloc(sizeof(float) * (size_t)k);
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t col = 0; col < n; ++col) {
+            dequant8_row(codes, scale, col, k, group, dtype, w);
+            float b = bias_value_f32(bias, col, bias_dtype);
+            for (int64_t row = 0; row < m; ++row) C[row * n + col] = dot_row_f32(A, row, k, dtype, w) + b;
         }
         free(w);
     }

@@ -25,6 +25,7 @@ __all__ = [
     "NONE", "BF16", "FP16", "build", "lib", "bf16_to_f32", "f16_to_f32", "f32_to_bf16",
     "f32_to_f16", "pack4", "unpack4", "quantize4", "dequant4", "dequant8", "gemm_w4", "gemm_w8",
     "gemm_w4_at", "gemm_w8_at", "gemm_w8a8", "moe_route", "moe", "threads", "embed4", "embed8",
+    "gemm_w4_f32acc", "gemm_w8_f32acc", "set_threads", "team_size",
 ]
 
 NONE, BF16, FP16 = 0, 1, 2
@@ -69,6 +70,11 @@ _SIGS = {
     "qref_dequant8": (None, [_P, _P, _I, _I, _I, _INT, _P]),
     "qref_gemm_w4": (None, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _INT, _INT, _P]),
     "qref_gemm_w8": (None, [_P, _P, _P, _P, _I, _I, _I, _I, _INT, _INT, _P]),
+    "qref_gemm_w4_f32acc": (None, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _INT, _INT, _P]),
+    "qref_gemm_w8_f32acc": (None, [_P, _P, _P, _P, _I, _I, _I, _I, _INT, _INT, _P]),
+    "qref_threads": (_INT, []),
+    "qref_set_threads": (None, [_INT]),
+    "qref_team_size": (_INT, []),
     "qref_gemm_w4_at": (None, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _INT, _INT, _P, _P, _I, _P]),
     "qref_gemm_w8_at": (None, [_P, _P, _P, _P, _I, _I, _I, _I, _INT, _INT, _P, _P, _I, _P]),
     "qref_embed4": (None, [_P, _I, _P, _P, _P, _I, _I, _I, _INT, _P]),
@@ -101,11 +107,19 @@ def lib():
 
 
 def threads() -> int:
-    """OpenMP threads the oracle will use (OMP_NUM_THREADS, else all cores)."""
-    env = os.environ.get("OMP_NUM_THREADS")
-    if env and env.strip().isdigit():
-        return int(env)
-    return os.cpu_count() or 1
+    """OpenMP threads the oracle's parallel loops will ask for
+    (omp_get_max_threads() inside the library)."""
+    return int(lib().qref_threads())
+
+
+def set_threads(n: int) -> None:
+    """Ask for n threads in the oracle's parallel loops from now on."""
+    lib().qref_set_threads(int(n))
+
+
+def team_size() -> int:
+    """Threads a parallel region of the oracle actually runs on."""
+    return int(lib().qref_team_size())
 
 
 def _ptr(a):
@@ -258,6 +272,35 @@ def gemm_w8(A, codes, scale, group=-1, dtype=FP16, bias=None, bias_dtype=NONE):
     bb = _c(bias, np.uint16)
     lib().qref_gemm_w8(_ptr(a), _ptr(q), _ptr(_c(scale, np.uint16)), _ptr(bb), m, n, k, group,
                        dtype, bias_dtype if bb is not None else NONE, _ptr(out))
+    return out
+
+
+def gemm_w4_f32acc(A, packed, scale, zero, group, dtype=BF16, bias=None, bias_dtype=NONE):
+    """The w4 GEMM with fp32 accumulation (the timed CPU baseline), float32 [M, N]."""
+    a = _c(A, np.uint16)
+    p = _c(packed, np.uint8)
+    m, k = a.shape
+    n = p.shape[0]
+    assert p.shape[1] * 2 == k
+    out = np.empty((m, n), dtype=np.float32)
+    bb = _c(bias, np.uint16)
+    lib().qref_gemm_w4_f32acc(_ptr(a), _ptr(p), _ptr(_c(scale, np.uint16)),
+                              _ptr(_c(zero, np.uint16)), _ptr(bb), m, n, k, group, dtype,
+                              bias_dtype if bb is not None else NONE, _ptr(out))
+    return out
+
+
+def gemm_w8_f32acc(A, codes, scale, group=-1, dtype=FP16, bias=None, bias_dtype=NONE):
+    """The w8 GEMM with fp32 accumulation, float32 [M, N]."""
+    a = _c(A, np.uint16)
+    q = _c(codes, np.int8)
+    m, k = a.shape
+    n = q.shape[0]
+    assert q.shape[1] == k
+    out = np.empty((m, n), dtype=np.float32)
+    bb = _c(bias, np.uint16)
+    lib().qref_gemm_w8_f32acc(_ptr(a), _ptr(q), _ptr(_c(scale, np.uint16)), _ptr(bb), m, n, k,
+                              group, dtype, bias_dtype if bb is not None else NONE, _ptr(out))
     return out
 
 

@@ -512,3 +512,108 @@ def test_moe_identical_experts_with_biases_equal_dense_ffn(renormalize):
     np.testing.assert_allclose(out, ref * w.sum(axis=1, keepdims=True), rtol=1e-10, atol=1e-10)
     if renormalize:
         np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=1e-15)
+
+
+# -- int8 with group scales (scale [n, k/g]) ------------------------------------------
+
+@pytest.mark.parametrize("dtype", [FP16, BF16])
+def test_e3_w8_groupwise_dequant_and_gemm(golden_dir, dtype):
+    # Two K-groups with distinct scales per row: the [n, k/g] scale layout
+    # gives E3's W and C; reading the scales as [k/g, n] would give the
+    # fixture's W_if_scales_transposed instead.
+    e = load(golden_dir, "e3_w8_groupwise.json")
+    codes = np.array(e["codes"], dtype=np.int8)
+    bits = f16_bits if dtype == FP16 else bf16_bits
+    s = bits(e["scale"])
+    W = oracle.dequant8(codes, s, e["group"], dtype)
+    assert W.tolist() == e["W"] and W.tolist() != e["W_if_scales_transposed"]
+    A = bits(e["A"])
+    assert oracle.gemm_w8(A, codes, s, e["group"], dtype).tolist() == e["C"]
+    Cb = oracle.gemm_w8(A, codes, s, e["group"], dtype, bits(e["bias"]), dtype)
+    assert Cb.tolist() == e["C_bias"]
+    at = oracle.gemm_w8_at(A, codes, s, [0, 0], [1, 0], e["group"], dtype, bits(e["bias"]), dtype)
+    assert at.tolist() == [e["C_bias"][0][1], e["C_bias"][0][0]]
+
+
+@pytest.mark.parametrize("g", [64, 128])
+def test_w8_group_closed_form(g):
+    # constant code c and A = 1: C[n] = sum_groups g * c * s[n, group]
+    rng = np.random.default_rng(31 + g)
+    n, k, c = 6, 1024, -37
+    s = (rng.integers(1, 64, (n, k // g)) / 1024.0).astype(np.float32)
+    codes = np.full((n, k), c, np.int8)
+    C = oracle.gemm_w8(f16_bits(np.ones((1, k))), codes, f16_bits(s), g, FP16)
+    assert np.array_equal(C[0], (g * c * s.astype(np.float64)).sum(axis=1))
+    W = oracle.dequant8(codes, f16_bits(s), g, FP16)
+    assert np.array_equal(W, c * np.repeat(s, g, axis=1))
+
+
+@pytest.mark.parametrize("g", [-1, 64, 128])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_w8_gemm_at_vs_numpy(g, with_bias):
+    # The sampled evaluation (used at full workload sizes) against numpy's
+    # fp64 matmul of the dequantized weight, at chosen (row, col) pairs
+    # including the corners.
+    m, n, k = 6, 48, 384
+    p = si.w8_problem(m, n, k, g, tag="pin-at", bias_dtype=FP16 if with_bias else 0)
+    W = oracle.dequant8(p.codes, p.scale, g, FP16).astype(np.float64)
+    ref = oracle.f16_to_f32(p.A).astype(np.float64) @ W.T
+    if with_bias:
+        ref = ref + oracle.f16_to_f32(p.bias)
+    rows = np.array([0, m - 1, 3, 0, m - 1, 2])
+    cols = np.array([0, n - 1, 17, n - 1, 0, 40])
+    at = oracle.gemm_w8_at(p.A, p.codes, p.scale, rows, cols, g, FP16,
+                           p.bias if with_bias else None, FP16 if with_bias else 0)
+    np.testing.assert_allclose(at, ref[rows, cols], rtol=1e-12, atol=1e-12)
+
+
+# -- fp32-accumulating variant (the timed CPU baseline) ------------------------------
+
+@pytest.mark.parametrize("m,n,k,g,bias", [(4, 128, 256, 64, False), (1, 2048, 2048, 64, False),
+                                          (3, 256, 2048, 128, True)])
+def test_w4_f32acc_agrees_with_double(m, n, k, g, bias):
+    # Same sums carried in fp32: they must agree with the double definition
+    # to within 1e-4 of the largest output (fp32 rounding of a K-term sum).
+    p = si.w4_problem(m, n, k, g, tag="f32acc", bias_dtype=FP16 if bias else 0)
+    kw = dict(bias=p.bias, bias_dtype=FP16) if bias else {}
+    ref = oracle.gemm_w4(p.A, p.packed, p.scale, p.zero, g, BF16, **kw)
+    got = oracle.gemm_w4_f32acc(p.A, p.packed, p.scale, p.zero, g, BF16, **kw)
+    assert got.dtype == np.float32
+    assert np.abs(got - ref).max() <= 1e-4 * np.abs(ref).max()
+    assert not np.array_equal(got.astype(np.float64), ref)   # really a different sum
+
+
+@pytest.mark.parametrize("g", [-1, 128])
+def test_w8_f32acc_agrees_with_double(g):
+    p = si.w8_problem(2, 512, 3584, g, tag="f32acc8")
+    ref = oracle.gemm_w8(p.A, p.codes, p.scale, g, FP16)
+    got = oracle.gemm_w8_f32acc(p.A, p.codes, p.scale, g, FP16)
+    assert np.abs(got - ref).max() <= 1e-4 * np.abs(ref).max()
+
+
+def test_f32acc_exact_inputs_equal_double():
+    # Integer/dyadic inputs: every partial sum is exact in fp32, so the two
+    # accumulations give identical results.
+    p = si.w4_exact_problem(3, 64, 512, 64, seed=11, bias_dtype=FP16)
+    ref = oracle.gemm_w4(p.A, p.packed, p.scale, p.zero, 64, BF16, p.bias, FP16)
+    got = oracle.gemm_w4_f32acc(p.A, p.packed, p.scale, p.zero, 64, BF16, p.bias, FP16)
+    assert np.array_equal(got.astype(np.float64), ref)
+
+
+# -- routing with -inf selection logits ------------------------------------------------
+
+def test_route_neg_inf_selection_logits_give_distinct_ids():
+    # Selection logits [-inf, 2, -inf, 1, -inf] with top-4: experts 1 and 3
+    # first, then the untaken -inf experts in index order, 0 then 2 (ties to
+    # the lower index); an expert is never chosen twice.  Weights come from
+    # the gating logits l = [0, 1, 2, 3, 4] over the chosen set {1, 3, 0, 2}.
+    ninf = -np.inf
+    sl = np.array([[ninf, 2.0, ninf, 1.0, ninf]], np.float32)
+    l = np.array([[0.0, 1.0, 2.0, 3.0, 4.0]], np.float32)
+    ids, w = oracle.moe_route(l, 4, sel_logits=sl)
+    assert ids.tolist() == [[1, 3, 0, 2]]
+    e = np.exp(np.array([1.0, 3.0, 0.0, 2.0]))
+    np.testing.assert_allclose(w[0], e / e.sum(), rtol=1e-15)
+    # all selection logits -inf: index order
+    ids, _ = oracle.moe_route(l, 5, sel_logits=np.full((1, 5), ninf, np.float32))
+    assert ids.tolist() == [[0, 1, 2, 3, 4]]
