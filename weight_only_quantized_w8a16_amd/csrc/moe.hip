@@ -23,8 +23,6 @@
 // (route gives them no expert; plan and combine skip their slots), the fc1
 // expert biases (fc1 epilogue, before the activation) and the fc2 ones
 // (combine), and the normalization mode (route).
-#include <cstdlib>
-
 #include "qg_launch.hpp"
 #include "tile_big.hpp"
 #include "tile_gemm.hpp"
@@ -87,32 +85,37 @@ __global__ __launch_bounds__(256) void k_moe_route(const float *__restrict__ log
   }
   const float *sl = sel_logits ? sel_logits : logits;
   float v[4], u[4];
+  bool cand[4];   // expert lane + 64 i exists and is not chosen yet
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;
-    v[i] = e < E ? sl[static_cast<size_t>(t) * E + e] : -__builtin_inff();
-    u[i] = e < E ? logits[static_cast<size_t>(t) * E + e] : -__builtin_inff();
+    cand[i] = e < E;
+    v[i] = cand[i] ? sl[static_cast<size_t>(t) * E + e] : 0.0f;
+    u[i] = cand[i] ? logits[static_cast<size_t>(t) * E + e] : -__builtin_inff();
   }
   float my_l = -__builtin_inff();
   int my_id = 0;
   for (int j = 0; j < topk; ++j) {
-    // lane-local best (strict > keeps the lower expert id on ties)
-    float bv = v[0];
-    int bi = lane;
+    // Lane-local best candidate (strict > keeps the lower expert id on
+    // ties), then the wave's best by (value, lower id).  A chosen expert
+    // leaves the candidate set, so it cannot win again even when every
+    // remaining value is -inf; bi < 0 marks a lane with no candidate.
+    float bv = 0.0f;
+    int bi = -1;
 #pragma unroll
-    for (int i = 1; i < 4; ++i)
-      if (v[i] > bv) { bv = v[i]; bi = lane + 64 * i; }
+    for (int i = 0; i < 4; ++i)
+      if (cand[i] && (bi < 0 || v[i] > bv)) { bv = v[i]; bi = lane + 64 * i; }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
       const float ov = __shfl_xor(bv, off);
       const int oi = __shfl_xor(bi, off);
-      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+      if (oi >= 0 && (bi < 0 || ov > bv || (ov == bv && oi < bi))) { bv = ov; bi = oi; }
     }
     // the chosen expert's gating logit, from the lane that holds it
     const int slot = bi >> 6;
     const float mine = slot == 0 ? u[0] : slot == 1 ? u[1] : slot == 2 ? u[2] : u[3];
     const float ul = __shfl(mine, bi & 63);
-    if ((bi & 63) == lane) v[slot] = -__builtin_inff();
+    if ((bi & 63) == lane) cand[slot] = false;
     if (lane == j) { my_l = ul; my_id = bi; }
   }
   // max and sum over the chosen experts (lanes < topk) or over all experts
@@ -325,9 +328,9 @@ hipError_t run_moe(const MoeArgs &a, hipStream_t s) {
   const bool dma = a.H % CfgMoeDma::BN == 0 && (a.H / a.group) % 2 == 0 && (a.I / a.group) % 2 == 0 &&
                    (sz_or & 3) == 0 && uint64_t(a.T) * a.H < lim && uint64_t(R) * a.I < lim &&
                    uint64_t(2 * a.I) * a.H / 2 < lim;
-  // QGEMM_MOE_TILE=S forces the 128 x 128 path (tests and tuning).
-  const char *force = std::getenv("QGEMM_MOE_TILE");
-  const bool use_dma = dma && !(force && force[0] == 'S');
+  // The dispatch override's moe_tile=S forces the 128 x 128 path (tests and
+  // tuning).
+  const bool use_dma = dma && !dispatch_override().moe_small_tile;
   const int bm = use_dma ? CfgMoeDma::BM : kMoeBM;
   const int max_tiles = (R + bm - 1) / bm + a.E;
 
