@@ -67,11 +67,38 @@ typedef enum {
 
 typedef enum { QG_NONE = 0, QG_BF16 = 1, QG_FP16 = 2, QG_FP32 = 3 } qg_dtype;
 
-/* Human-readable name of a status code (static storage, never NULL). */
+/* Human-readable name of a status code (static storage, never NULL).  The
+ * pages give the GEMM runners no error channel ("acext User Guide (v1.7)",
+ * 1.2.1: the runners return void); the explicit status follows the rule of
+ * vllm-omni cpu_int4.py (supports_direct_dequant and the shape checks of
+ * _create_int4_weights): refuse what is not supported, never misread it.
+ * This function only names the codes. */
 const char *qg_strerror(qg_status status);
 
-/* Library version as 10000*major + 100*minor + patch. */
+/* Library version as 10000*major + 100*minor + patch.  No passage of the
+ * pages applies (bookkeeping). */
 int qg_version(void);
+
+/* Dispatch override, for tests and tuning only (no passage of the pages
+ * applies; no part of the method): forces choices the library otherwise
+ * makes from a problem's sizes, for every later call in the process.
+ * spec is a comma-separated list of key=value pairs:
+ *   path=auto|decode|prefill        the GEMM path (else by m: decode for
+ *                                   m <= 16)
+ *   prefill_tile=auto|X|D8|D8N|D64|D128|L|M|S   the prefill tile
+ *   splitk=<n>                      prefill K slices (1: none), n >= 1
+ *   moe_tile=auto|S                 S: the MoE on the 128 x 128 tile
+ *   w8a8_tile=auto|T256|T256N|T128|T64   the W8A8 tile (also for m <= 16)
+ *   w8a8_split=<n>                  W8A8 K slices, n >= 1
+ * Keys not given take their automatic choice; NULL or "" restores every
+ * automatic choice.  A forced choice that does not fit a problem (a
+ * 256-wide tile for n % 256 != 0, the prefill path for n % 64 != 0) is
+ * ignored for that problem.  The environment variable QGEMM_OVERRIDE, read
+ * once when the library first dispatches, gives the initial spec (unless
+ * this function was called before).  Returns QG_ERR_MODE, changing nothing,
+ * for an unknown key or value.  Set it between calls: calls running on other
+ * threads may see either setting. */
+qg_status qg_set_override(const char *spec);
 
 /* ------------------------------------------------------------------------
  * Load-side repack (once per weight).  The portable layouts are
@@ -144,7 +171,10 @@ qg_status qquantize_w4(const void *W, uint8_t *packed, void *scales, void *zeros
 
 /* ------------------------------------------------------------------------
  * Dequantization hook (testing and fallback use): tiled codes -> W [n, k]
- * row-major in out_dtype (QG_FP32, or the activation dtype).  The fp32
+ * row-major in out_dtype (QG_FP32, or the activation dtype).  The rule is
+ * vllm-omni cpu_int4.py's (module docstring: w = (q - 8) * scale + zero;
+ * CPUInt4EmbeddingMethod.embedding: dequantize in fp32, then cast) and the
+ * int8 rule of "acext User Guide (v1.7)" 1.3.1 (w = q * scale per channel).  The fp32
  * value is (q - 8) * s + z (int4; the product is exact, the add rounds to
  * nearest even) or q * s (int8, exact); the 16-bit output is that fp32 value
  * rounded to nearest even.  Bit-exact by contract.

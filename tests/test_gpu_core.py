@@ -3,7 +3,6 @@ path, and the tiny W4A16 problem against the oracle.
 
 Every comparison runs the library through its C ABI (the binding passes raw
 pointers) and compares with the CPU oracle on identical seeded bytes."""
-import os
 
 import numpy as np
 import pytest
@@ -16,11 +15,6 @@ from helpers import (BF16, FP16, TOL, rel_err, tiled_w4_expected, tiled_w8_expec
                      to_dev)
 
 pytestmark = pytest.mark.gpu
-
-
-@pytest.fixture(autouse=True)
-def _no_forced_path(monkeypatch):
-    monkeypatch.delenv("QGEMM_FORCE_PATH", raising=False)
 
 
 # -- repack -------------------------------------------------------------------
@@ -131,11 +125,11 @@ def _run_w4(p, path=None):
     Z = to_dev(p.zero, p.dtype) if p.zero is not None else None
     bias = to_dev(p.bias, p.bias_dtype) if p.bias is not None else None
     if path:
-        os.environ["QGEMM_FORCE_PATH"] = path
+        qg.set_override(path=path)
     try:
         C = qg.gemm_w4a16(A, tiled, S, Z, bias, p.group)
     finally:
-        os.environ.pop("QGEMM_FORCE_PATH", None)
+        qg.set_override(path=None)
     torch.cuda.synchronize()
     return C
 
@@ -146,11 +140,11 @@ def _run_w8(p, path=None):
     S = to_dev(p.scale, p.dtype)
     bias = to_dev(p.bias, p.bias_dtype) if p.bias is not None else None
     if path:
-        os.environ["QGEMM_FORCE_PATH"] = path
+        qg.set_override(path=path)
     try:
         C = qg.gemm_w8a16(A, tiled, S, bias, p.group)
     finally:
-        os.environ.pop("QGEMM_FORCE_PATH", None)
+        qg.set_override(path=None)
     torch.cuda.synchronize()
     return C
 
@@ -211,20 +205,20 @@ def test_w8_grouped_integer_exact(m, n, k, group, path, dtype):
 
 @pytest.mark.parametrize("tile", ["D8", "D8N", "D64", "D128", "X", "L", "M", "S"])
 @pytest.mark.parametrize("group", [64, 128])
-def test_prefill_tiles_w8_grouped_integer_exact(tile, group, monkeypatch):
+def test_prefill_tiles_w8_grouped_integer_exact(tile, group):
     p = si.w8_exact_problem(300, 512, 1024, seed=group, dtype=BF16, bias_dtype=FP16, group=group)
     Cref = oracle.gemm_w8(p.A, p.codes, p.scale, group, BF16, p.bias, FP16)
-    monkeypatch.setenv("QGEMM_PREFILL_TILE", tile)
+    qg.set_override(prefill_tile=tile)
     got = to_bits(_run_w8(p, "prefill"))
     assert np.array_equal(got, _exact_expected(Cref, BF16))
 
 
-def test_prefill_w8_grouped_odd_group_count_falls_back(monkeypatch):
+def test_prefill_w8_grouped_odd_group_count_falls_back():
     # K / group = 3: the direct-load tile needs pairs of groups; the generic
     # tile of the same width takes the problem.
     p = si.w8_exact_problem(300, 512, 384, seed=21, dtype=FP16, bias_dtype=FP16, group=128)
     Cref = oracle.gemm_w8(p.A, p.codes, p.scale, 128, FP16, p.bias, FP16)
-    monkeypatch.setenv("QGEMM_PREFILL_TILE", "D8")
+    qg.set_override(prefill_tile="D8")
     got = to_bits(_run_w8(p, "prefill"))
     assert np.array_equal(got, _exact_expected(Cref, FP16))
 
@@ -280,12 +274,12 @@ def test_w4_scale_forms_integer_exact(m, n, k, group, zeros, path):
 
 @pytest.mark.parametrize("tile", ["D8", "D8N", "D64", "D128", "X", "L", "M", "S"])
 @pytest.mark.parametrize("group,zeros", FORMS)
-def test_prefill_tiles_w4_scale_forms_exact(tile, group, zeros, monkeypatch):
+def test_prefill_tiles_w4_scale_forms_exact(tile, group, zeros):
     # scale-only groups keep the direct-load tiles (their zero windows read an
     # empty buffer, i.e. zeros); per-channel scales fall back to the generic tile
     p = si.w4_exact_problem(300, 512, 1024, group, seed=29, dtype=FP16, bias_dtype=FP16, zeros=zeros)
     Cref = oracle.gemm_w4(p.A, p.packed, p.scale, p.zero, group, FP16, p.bias, FP16)
-    monkeypatch.setenv("QGEMM_PREFILL_TILE", tile)
+    qg.set_override(prefill_tile=tile)
     got = to_bits(_run_w4(p, "prefill"))
     assert np.array_equal(got, _exact_expected(Cref, FP16))
 
@@ -329,20 +323,20 @@ def test_empty_m_is_noop():
 
 @pytest.mark.parametrize("tile", ["X", "L", "M", "S"])
 @pytest.mark.parametrize("m", [1, 77, 300])
-def test_prefill_tiles_integer_exact(tile, m, monkeypatch):
+def test_prefill_tiles_integer_exact(tile, m):
     n, k, group = 512, 640, 128
     p = si.w4_exact_problem(m, n, k, group, seed=m + 3, dtype=BF16, bias_dtype=FP16)
     Cref = oracle.gemm_w4(p.A, p.packed, p.scale, p.zero, group, BF16, p.bias, FP16)
-    monkeypatch.setenv("QGEMM_PREFILL_TILE", tile)
+    qg.set_override(prefill_tile=tile)
     got = to_bits(_run_w4(p, "prefill"))
     assert np.array_equal(got, _exact_expected(Cref, BF16))
 
 
 @pytest.mark.parametrize("tile", ["X", "L", "M", "S"])
-def test_prefill_tiles_w8_integer_exact(tile, monkeypatch):
+def test_prefill_tiles_w8_integer_exact(tile):
     p = si.w8_exact_problem(200, 256, 576, seed=9, dtype=FP16, bias_dtype=FP16)
     Cref = oracle.gemm_w8(p.A, p.codes, p.scale, -1, FP16, p.bias, FP16)
-    monkeypatch.setenv("QGEMM_PREFILL_TILE", tile)
+    qg.set_override(prefill_tile=tile)
     got = to_bits(_run_w8(p, "prefill"))
     assert np.array_equal(got, _exact_expected(Cref, FP16))
 
@@ -351,30 +345,30 @@ def test_prefill_tiles_w8_integer_exact(tile, monkeypatch):
 @pytest.mark.parametrize("dtype", [BF16, FP16])
 @pytest.mark.parametrize("tile", ["D8", "D8N", "D64", "D128", "X"])
 @pytest.mark.parametrize("group", [64, 128])
-def test_prefill_dma_tile_integer_exact(tile, group, m, n, k, dtype, monkeypatch):
+def test_prefill_dma_tile_integer_exact(tile, group, m, n, k, dtype):
     p = si.w4_exact_problem(m, n, k, group, seed=m + k, dtype=dtype, bias_dtype=FP16)
     Cref = oracle.gemm_w4(p.A, p.packed, p.scale, p.zero, group, dtype, p.bias, FP16)
-    monkeypatch.setenv("QGEMM_PREFILL_TILE", tile)
+    qg.set_override(prefill_tile=tile)
     got = to_bits(_run_w4(p, "prefill"))
     assert np.array_equal(got, _exact_expected(Cref, dtype))
 
 
 @pytest.mark.parametrize("tile", ["D8", "D8N", "D64", "D128", "X"])
-def test_prefill_dma_tile_w8_integer_exact(tile, monkeypatch):
+def test_prefill_dma_tile_w8_integer_exact(tile):
     p = si.w8_exact_problem(300, 512, 576, seed=4, dtype=FP16, bias_dtype=FP16)
     Cref = oracle.gemm_w8(p.A, p.codes, p.scale, -1, FP16, p.bias, FP16)
-    monkeypatch.setenv("QGEMM_PREFILL_TILE", tile)
+    qg.set_override(prefill_tile=tile)
     got = to_bits(_run_w8(p, "prefill"))
     assert np.array_equal(got, _exact_expected(Cref, FP16))
 
 
 @pytest.mark.parametrize("tile", ["D8", "D8N"])
-def test_prefill_dma_tile_odd_group_count_falls_back(tile, monkeypatch):
+def test_prefill_dma_tile_odd_group_count_falls_back(tile):
     # K / group = 3: the scale windows need pairs of groups, so the generic
     # kernel of the same tile width takes the problem; results stay exact.
     p = si.w4_exact_problem(300, 512, 384, 128, seed=11, dtype=BF16, bias_dtype=FP16)
     Cref = oracle.gemm_w4(p.A, p.packed, p.scale, p.zero, 128, BF16, p.bias, FP16)
-    monkeypatch.setenv("QGEMM_PREFILL_TILE", tile)
+    qg.set_override(prefill_tile=tile)
     got = to_bits(_run_w4(p, "prefill"))
     assert np.array_equal(got, _exact_expected(Cref, BF16))
 

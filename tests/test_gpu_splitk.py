@@ -17,10 +17,8 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.fixture(autouse=True)
-def _prefill_only(monkeypatch):
-    monkeypatch.setenv("QGEMM_FORCE_PATH", "prefill")
-    monkeypatch.delenv("QGEMM_SPLITK", raising=False)
-    monkeypatch.delenv("QGEMM_PREFILL_TILE", raising=False)
+def _prefill_only():
+    qg.set_override(path="prefill")
 
 
 def expected(Cref, dtype):
@@ -49,23 +47,23 @@ def run_w8(p, workspace=None):
 @pytest.mark.parametrize("tile", ["D8", "D8N", "D64", "D128", "X", "L", "M", "S"])
 @pytest.mark.parametrize("slices", [2, 3, 4])
 @pytest.mark.parametrize("group", [64, 128, -1])
-def test_split_w4_every_tile_exact(tile, slices, group, monkeypatch):
+def test_split_w4_every_tile_exact(tile, slices, group):
     # K = 4096: 64 steps, so with 128-groups (16-step windows) 3 and 4
     # slices still give more than one slice; M and N ragged against tiles.
     p = si.w4_exact_problem(300, 768, 4096, group, seed=slices + group, dtype=BF16, bias_dtype=FP16)
     Cref = oracle.gemm_w4(p.A, p.packed, p.scale, p.zero, group, BF16, p.bias, FP16)
-    monkeypatch.setenv("QGEMM_PREFILL_TILE", tile)
-    monkeypatch.setenv("QGEMM_SPLITK", str(slices))
+    qg.set_override(prefill_tile=tile)
+    qg.set_override(splitk=slices)
     assert np.array_equal(run_w4(p), expected(Cref, BF16))
 
 
 @pytest.mark.parametrize("tile", ["D8", "D8N", "D64", "D128", "X", "L", "M", "S"])
 @pytest.mark.parametrize("group", [-1, 128])
-def test_split_w8_every_tile_exact(tile, group, monkeypatch):
+def test_split_w8_every_tile_exact(tile, group):
     p = si.w8_exact_problem(200, 512, 3584, seed=7, dtype=FP16, bias_dtype=FP16, group=group)
     Cref = oracle.gemm_w8(p.A, p.codes, p.scale, group, FP16, p.bias, FP16)
-    monkeypatch.setenv("QGEMM_PREFILL_TILE", tile)
-    monkeypatch.setenv("QGEMM_SPLITK", "3")
+    qg.set_override(prefill_tile=tile)
+    qg.set_override(splitk=3)
     assert np.array_equal(run_w8(p), expected(Cref, FP16))
 
 
@@ -82,12 +80,12 @@ def test_automatic_split_shape_and_small_workspace():
     assert np.array_equal(run_w4(p, workspace=small), exp)
 
 
-def test_split_random_data_within_tolerance(monkeypatch):
+def test_split_random_data_within_tolerance():
     # Random bf16 data: the split result stays within the bf16 tolerance of
     # the oracle (only the fp32 summation order differs from unsplit).
     p = si.w4_problem(96, 1024, 4096, 64, tag="split")
     Cref = oracle.gemm_w4(p.A, p.packed, p.scale, p.zero, 64, BF16)
-    monkeypatch.setenv("QGEMM_SPLITK", "4")
+    qg.set_override(splitk=4)
     got = run_w4(p)
     C = torch.from_numpy(got.view(np.int16)).view(torch.bfloat16).float().numpy()
     err = np.abs(C - Cref).max() / np.abs(Cref).max()

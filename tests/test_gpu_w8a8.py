@@ -17,14 +17,9 @@ from helpers import rel_err
 
 pytestmark = pytest.mark.gpu
 
-TILES = ["0", "1", "2", "3"]          # 256x256, 256x128, 128x128, 64x128
+TILES = ["T256", "T256N", "T128", "T64"]
 OUT = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}
 TOL = {"fp16": 3e-3, "bf16": 1e-2}
-
-
-@pytest.fixture(autouse=True)
-def _auto_tile(monkeypatch):
-    monkeypatch.delenv("QGEMM_W8A8_TILE", raising=False)
 
 
 def run(p, out="fp32", workspace=True):
@@ -49,9 +44,9 @@ def ref(p):
 @pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("m,n,k", [(1, 128, 128), (5, 144, 256), (70, 272, 384), (200, 400, 512),
                                    (300, 528, 1024)])
-def test_w8a8_integer_sums_bit_exact(monkeypatch, tile, m, n, k):
+def test_w8a8_integer_sums_bit_exact(tile, m, n, k):
     # Several tiles in each direction, ragged M and N tails (n % 128 != 0).
-    monkeypatch.setenv("QGEMM_W8A8_TILE", tile)
+    qg.set_override(w8a8_tile=tile)
     p = si.w8a8_problem(m, n, k, False, False, scales=[1.0])
     acc, _ = ref(p)
     assert np.abs(acc).max() < 2 ** 24
@@ -78,11 +73,11 @@ def test_w8a8_decode_kernel_bit_exact(m, n, k):
 
 
 @pytest.mark.parametrize("m,n,k", [(64, 3584, 3584), (32, 3584, 1024), (40, 1040, 2048)])
-def test_w8a8_split_k_equals_unsplit_bitwise(monkeypatch, m, n, k):
+def test_w8a8_split_k_equals_unsplit_bitwise(m, n, k):
     # Problems with few 64 x 128 tiles are split along K into int32 partials;
     # integer sums are exact in any order, so split and unsplit agree bit for
     # bit.
-    monkeypatch.setenv("QGEMM_W8A8_TILE", "3")
+    qg.set_override(w8a8_tile="T64")
     assert qg.w8a8_workspace_size(m, n, k) > 0
     p = si.w8a8_problem(m, n, k, True, True)
     assert np.array_equal(run(p, "fp32", True), run(p, "fp32", False))
@@ -92,10 +87,10 @@ def test_w8a8_split_k_equals_unsplit_bitwise(monkeypatch, m, n, k):
 
 
 @pytest.mark.parametrize("per_token,per_channel", [(0, 0), (0, 1), (1, 0), (1, 1)])
-@pytest.mark.parametrize("tile", ["0", "3"])
-def test_w8a8_power_of_two_scales_bit_exact(monkeypatch, per_token, per_channel, tile):
+@pytest.mark.parametrize("tile", ["T256", "T64"])
+def test_w8a8_power_of_two_scales_bit_exact(per_token, per_channel, tile):
     # Power-of-two scales keep every product exact: C == sum * row * col.
-    monkeypatch.setenv("QGEMM_W8A8_TILE", tile)
+    qg.set_override(w8a8_tile=tile)
     p = si.w8a8_problem(260, 400, 512, bool(per_token), bool(per_channel),
                         scales=[0.25, 0.5, 1.0, 2.0, 0.125])
     _, Cref = ref(p)

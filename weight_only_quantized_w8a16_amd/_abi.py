@@ -33,6 +33,7 @@ _ST = ctypes.c_int
 SIGNATURES = {
     "qg_strerror": (ctypes.c_char_p, [_ST]),
     "qg_version": (_INT, []),
+    "qg_set_override": (_ST, [ctypes.c_char_p]),
     "qrepack_w4": (_ST, [_P, _P, _INT, _INT, _P]),
     "qunrepack_w4": (_ST, [_P, _P, _INT, _INT, _P]),
     "qrepack_w8": (_ST, [_P, _P, _INT, _INT, _P]),

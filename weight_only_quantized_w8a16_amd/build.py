@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libqgemm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 DEVICE_SOURCES = ["transform.hip", "decode.hip", "prefill.hip", "moe.hip", "w8a8.hip", "embed.hip", "probe.hip"]
-HOST_SOURCES = ["api.cpp"]
+HOST_SOURCES = ["api.cpp", "override.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function"]
 # Packed fp32 VALU ops disabled: plain float code must not be turned into
 # v_pk_{add,mul,fma}_f32.

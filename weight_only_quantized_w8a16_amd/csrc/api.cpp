@@ -3,9 +3,6 @@
 // argument has been checked; on error nothing is enqueued.
 #include <hip/hip_runtime.h>
 
-#include <cstdlib>
-#include <cstring>
-
 #include "../../include/qgemm.h"
 #include "qg_launch.hpp"
 
@@ -17,18 +14,6 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 bool act_ok(qg_dtype d) { return d == QG_BF16 || d == QG_FP16; }
 hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
 qg_status hip_status(hipError_t e) { return e == hipSuccess ? QG_OK : QG_ERR_HIP; }
-
-// QGEMM_FORCE_PATH=decode|prefill overrides the choice by m, so that tests
-// can run both paths on the same inputs.  Read at every call (a getenv is
-// negligible next to a launch).
-enum ForcedPath { kAuto, kForceDecode, kForcePrefill };
-ForcedPath forced_path() {
-  const char *v = std::getenv("QGEMM_FORCE_PATH");
-  if (!v) return kAuto;
-  if (std::strcmp(v, "decode") == 0) return kForceDecode;
-  if (std::strcmp(v, "prefill") == 0) return kForcePrefill;
-  return kAuto;
-}
 
 constexpr int kDecodeMaxM = 16;
 
@@ -141,9 +126,6 @@ qg_status qunrepack_w8_kn(const int8_t *src, int8_t *dst, int n, int k, void *st
 }
 
 // ---------------------------------------------------------------------------
-// Dequant hook
-// ---------------------------------------------------------------------------
-// ---------------------------------------------------------------------------
 // Quantizer
 // ---------------------------------------------------------------------------
 qg_status qquantize_w4(const void *W, uint8_t *packed, void *scales, void *zeros, int n, int k,
@@ -164,6 +146,9 @@ qg_status qquantize_w4(const void *W, uint8_t *packed, void *scales, void *zeros
                                            as_stream(stream)));
 }
 
+// ---------------------------------------------------------------------------
+// Dequant hook
+// ---------------------------------------------------------------------------
 qg_status qdequant_w4(const uint8_t *B, const void *scales, const void *zeros, void *W, int n,
                       int k, int group, qg_dtype act, qg_dtype out, void *stream) {
   if (n < 0 || k < 0) return QG_ERR_SHAPE;
@@ -199,11 +184,13 @@ qg_status qdequant_w8(const int8_t *B, const void *scales, void *W, int n, int k
 // GEMM
 // ---------------------------------------------------------------------------
 // Whether a GEMM runs on the prefill path (else the decode kernels).
+// The dispatch override (qg_set_override) can force either path, so that
+// tests can run both on the same inputs.
 static bool uses_prefill(int m, int n) {
-  const ForcedPath f = forced_path();
+  const int f = qg::dispatch_override().path;
   const bool prefill_ok = n % 64 == 0;
-  if (f == kForcePrefill && prefill_ok) return true;
-  return !(f == kForceDecode || m <= kDecodeMaxM || !prefill_ok);
+  if (f == qg::kPathPrefill && prefill_ok) return true;
+  return !(f == qg::kPathDecode || m <= kDecodeMaxM || !prefill_ok);
 }
 
 // Workspace: the prefill path's split-K partials for problems it would

@@ -8,8 +8,6 @@
 // multi-row batches; "[Misc][Kernel]: Add GPTQAllSpark Quantization": the
 // large-M regime), with the dequantized weight kept on chip instead of
 // written back to memory.
-#include <cstdlib>
-#include <string>
 #include <type_traits>
 
 #include "qg_launch.hpp"
@@ -172,12 +170,13 @@ hipError_t run(const GemmArgs &a, hipStream_t s, const Split &sp = Split{}) {
 }
 
 // Whether the direct-load tiles take the problem (else the generic tile of
-// the same width does): 32-bit offsets, and group scales (int4 zeros too)
-// in 4-byte pairs of groups.
+// the same width does): activation and code bytes below 2 GiB (the buffer
+// resources take 31-bit extents and 32-bit offsets), and group scales (int4
+// zeros too) in 4-byte pairs of groups.
 template <int WBITS, bool GS8, bool PC>
 bool dma_ok(const GemmArgs &a) {
   const uint64_t lim = uint64_t(1) << 31;
-  if (uint64_t(a.M) * a.K >= lim || uint64_t(a.N) * a.K * WBITS / 8 >= lim) return false;
+  if (uint64_t(a.M) * a.K * 2 >= lim || uint64_t(a.N) * a.K * WBITS / 8 >= lim) return false;
   if (((WBITS == 4 && !PC) || GS8) &&
       (((a.K / a.group) & 1) != 0 || (reinterpret_cast<uintptr_t>(a.S) & 3) != 0 ||
        (WBITS == 4 && (reinterpret_cast<uintptr_t>(a.Z) & 3) != 0)))
@@ -203,24 +202,23 @@ hipError_t run_dma(const GemmArgs &a, hipStream_t s, const Split &sp = Split{}) 
 // Tile shapes.  Choice, from on-device sweeps at K = 2048 and 3584 (M from
 // 32 to 4096): the direct-load tiles once there are enough of them to keep
 // most CUs busy, the generic tiles (down to 64 x 64) when the problem would
-// leave CUs idle.  QGEMM_PREFILL_TILE=X|D8|D8N|D64|D128|L|M|S forces one
-// (tests and tuning); D8, D8N, D64 and D128 are the 256 x 256, 256 x 128,
-// 64 x 256 and 128 x 256 tiles with direct-to-LDS activation loads.
-enum Tile { kX, kD8, kD8N, kD64, kD128, kL, kM, kS };
+// leave CUs idle.  The dispatch override's prefill_tile forces one (tests
+// and tuning); D8, D8N, D64 and D128 are the 256 x 256, 256 x 128, 64 x 256
+// and 128 x 256 tiles with direct-to-LDS activation loads.
 
 int choose_tile(const GemmArgs &a) {
   auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * (a.N / bn); };
   const bool n256 = a.N % 256 == 0, n128 = a.N % 128 == 0;
-  if (const char *o = std::getenv("QGEMM_PREFILL_TILE")) {
-    const std::string c(o);
-    if (c == "X" && n256) return kX;
-    if (c == "D8" && n256) return kD8;
-    if (c == "D8N" && n128) return kD8N;
-    if (c == "D64" && n256) return kD64;
-    if (c == "D128" && n256) return kD128;
-    if (c == "L" && n128) return kL;
-    if (c == "M" && n128) return kM;
-    if (c == "S") return kS;
+  switch (dispatch_override().prefill_tile) {
+    case kX: if (n256) return kX; break;
+    case kD8: if (n256) return kD8; break;
+    case kD8N: if (n128) return kD8N; break;
+    case kD64: if (n256) return kD64; break;
+    case kD128: if (n256) return kD128; break;
+    case kL: if (n128) return kL; break;
+    case kM: if (n128) return kM; break;
+    case kS: return kS;
+    default: break;
   }
   if (n256 && a.M > 128 && tiles(256, 256) >= 160) return kD8;
   // Up to 192 rows the 64-row tile wastes fewer rows than a 256-row one.
@@ -248,8 +246,8 @@ int choose_tile(const GemmArgs &a) {
 // N = 13312: 29.5 / 38.8 us, N = 8192: 23.9 / 25.3 us, while N = 4096, 128
 // tiles, gains: 23.1 / 18.6 us), splitting was slower.  A slice is a whole number of scale windows
 // (8 groups) when the scales come through the direct-load tile's windows,
-// a multiple of 8 steps otherwise.  QGEMM_SPLITK=<n> asks for n slices (1:
-// none) on the tile chosen above (tests and tuning).
+// a multiple of 8 steps otherwise.  The dispatch override's splitk asks for
+// n slices (1: none) on the tile chosen above (tests and tuning).
 struct Plan {
   int tile;
   Split split;
@@ -261,7 +259,7 @@ Plan plan_prefill(const GemmArgs &a, int wbits, bool gs8) {
   const int nsteps = a.K / 64;
   const int tiles_s = ((a.M + 63) / 64) * (a.N / 64);
   int want = (pl.tile == kS && a.M <= 128 && nsteps >= 32 && tiles_s < 256) ? 2 : 1;
-  if (const char *o = std::getenv("QGEMM_SPLITK")) want = std::atoi(o);
+  if (const int o = dispatch_override().splitk; o > 0) want = o;
   if (want <= 1) return pl;
   const int g = a.group > 0 ? a.group : a.K;
   const bool windows = (wbits == 4 && g != a.K) || gs8;   // scales through LDS windows

@@ -29,6 +29,24 @@ hipError_t set_lds_limit_once(Kern kern, int bytes, std::atomic<uint64_t> &done)
   return e;
 }
 
+// Dispatch override (qg_set_override): forced choices, or the automatic
+// ones (kPathAuto, -1, 0, false).  A forced tile or path that does not fit a
+// problem is ignored for that problem.
+enum { kPathAuto = 0, kPathDecode = 1, kPathPrefill = 2 };
+// Prefill tiles (prefill.hip), in the order qg_set_override names them.
+enum PrefillTile { kX, kD8, kD8N, kD64, kD128, kL, kM, kS };
+// W8A8 tiles (w8a8.hip), in the order qg_set_override names them.
+enum W8A8Tile { kT256, kT256N, kT128, kT64 };
+struct Override {
+  int path = kPathAuto;
+  int prefill_tile = -1;       // PrefillTile, or -1
+  int splitk = 0;              // prefill K slices (1: none), or 0
+  bool moe_small_tile = false; // MoE grouped GEMMs on the 128 x 128 tile
+  int w8a8_tile = -1;          // W8A8Tile, or -1
+  int w8a8_split = 0;          // W8A8 K slices, or 0
+};
+Override dispatch_override();
+
 hipError_t launch_repack_w4(const uint8_t *src, uint8_t *dst, int n, int k, hipStream_t s);
 hipError_t launch_unrepack_w4(const uint8_t *src, uint8_t *dst, int n, int k, hipStream_t s);
 hipError_t launch_repack_w8(const int8_t *src, int8_t *dst, int n, int k, hipStream_t s);

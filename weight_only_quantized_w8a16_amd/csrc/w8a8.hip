@@ -26,7 +26,6 @@
 // source side.  Rows past the end of A or B are read from the last valid row
 // (a direct load cannot be masked); their outputs are never stored.
 #include <algorithm>
-#include <cstdlib>
 #include <type_traits>
 
 #include "qg_common.hpp"
@@ -377,7 +376,6 @@ using T256x256 = W8Cfg<256, 256, 2, 4>;   // waves of 128 x 64
 using T256x128 = W8Cfg<256, 128, 4, 2>;   // waves of 64 x 64
 using T128x128 = W8Cfg<128, 128, 2, 4>;   // waves of 64 x 32
 using T64x128 = W8Cfg<64, 128, 2, 4>;     // waves of 32 x 32
-enum { kT256, kT256N, kT128, kT64 };
 
 struct W8A8Plan {
   int tile;
@@ -391,8 +389,8 @@ int tiles_of(int M, int N, int bm, int bn) { return ((M + bm - 1) / bm) * ((N + 
 // then K slices when even the smallest tile leaves the chip mostly idle,
 // enough for about one workgroup per CU, each slice at least two steps
 // (measured at K = 3584, m = 128, n = 3584: 56 tiles, 4-5 slices 15 us,
-// unsplit 28 us, 8-10 slices 18-21 us).  QGEMM_W8A8_SPLIT=<n> asks for n
-// slices (tests and tuning).
+// unsplit 28 us, 8-10 slices 18-21 us).  The dispatch override's w8a8_split
+// asks for n slices (tests and tuning).
 W8A8Plan plan_w8a8(int M, int N, int K) {
   W8A8Plan pl{kT64, 0, 1, 0};
   // The 256 x 256 tile when its tiles fill the CUs in one round or in many
@@ -400,7 +398,7 @@ W8A8Plan plan_w8a8(int M, int N, int K) {
   // tiles: K = 3584, m = 1024, n = 18944, 296 tiles: 132 us, 128 x 128: 108).
   const int t256 = tiles_of(M, N, 256, 256);
   // The 256 x 128 tile was never the fastest in those sweeps (m 128 to 4096);
-  // it stays available through QGEMM_W8A8_TILE.
+  // it stays available through the dispatch override.
   if (M > 128 && t256 >= 192 && (t256 <= 256 || t256 >= 768)) pl.tile = kT256;
   else if (M > 64 && tiles_of(M, N, 128, 128) >= 128) pl.tile = kT128;
   else pl.tile = kT64;
@@ -409,7 +407,7 @@ W8A8Plan plan_w8a8(int M, int N, int K) {
   const int tiles = tiles_of(M, N, bm, bn), nsteps = K / 128;
   int want = 1;
   if (tiles < 128 && nsteps >= 4) want = std::min((256 + tiles - 1) / tiles, std::min(nsteps / 2, 16));
-  if (const char *o = std::getenv("QGEMM_W8A8_SPLIT")) want = std::min(std::atoi(o), nsteps);   // tuning
+  if (const int o = dispatch_override().w8a8_split; o > 0) want = std::min(o, nsteps);   // tuning
   {
     if (want >= 2) {
       const int kseg = (nsteps + want - 1) / want;
@@ -449,7 +447,7 @@ hipError_t dispatch_w8a8(W8A8Problem p, const W8A8Plan &pl, hipStream_t s) {
 
 // Decode kernel for m <= 16 unless a tile is forced (tests and tuning).
 bool w8a8_use_decode(int m) {
-  if (std::getenv("QGEMM_W8A8_TILE")) return false;
+  if (dispatch_override().w8a8_tile >= 0) return false;
   return m <= 16;
 }
 
@@ -494,10 +492,7 @@ hipError_t launch_w8a8(const W8A8Args &a, hipStream_t s) {
   } else {
     pl.nsplit = 1;
   }
-  if (const char *o = std::getenv("QGEMM_W8A8_TILE")) {   // tests and tuning
-    const int t = std::atoi(o);
-    if (t >= kT256 && t <= kT64) pl.tile = t;
-  }
+  if (const int t = dispatch_override().w8a8_tile; t >= 0) pl.tile = t;   // tests and tuning
   switch (a.out) {
     case QG_FP32: return dispatch_w8a8<QG_FP32>(p, pl, s);
     case QG_FP16: return dispatch_w8a8<QG_FP16>(p, pl, s);
