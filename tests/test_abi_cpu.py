@@ -328,3 +328,145 @@ def test_read_probe_validation_and_blocks():
     assert L.qg_read_probe(FAKE, 16, FAKE + 2, None) == ALIGN
     assert L.qg_read_probe_blocks(0) == 1
     assert 1 <= L.qg_read_probe_blocks(1 << 30) <= 4096
+
+
+# -- the torch binding refuses wrong shapes and dtypes before any pointer is
+# passed (host tensors suffice: the checks run before the device checks) -----
+
+import torch  # noqa: E402
+
+BF, F16 = torch.bfloat16, torch.float16
+
+
+def _t(shape, dtype):
+    return torch.zeros(shape, dtype=dtype)
+
+
+def _status(fn, *a, **kw):
+    with pytest.raises(qg.QGemmError) as e:
+        fn(*a, **kw)
+    return e.value.status
+
+
+def _w4_args(m=4, n=128, k=256, g=64, dt=BF):
+    return dict(A=_t((m, k), dt), B_tiled=_t((n, k // 2), torch.uint8),
+                scales=_t((n, k // g), dt), zeros=_t((n, k // g), dt))
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(A=_t((4, 256), torch.float32)), DTYPE),
+    (dict(B_tiled=_t((128, 128), torch.int8)), DTYPE),
+    (dict(B_tiled=_t((128, 64), torch.uint8)), SHAPE),            # k / 2 wrong
+    (dict(scales=_t((128, 4), torch.float32)), DTYPE),           # fp32 scales, bf16 A
+    (dict(scales=_t((128, 4), F16)), DTYPE),
+    (dict(scales=_t((4, 128), BF)), SHAPE),                       # transposed
+    (dict(scales=_t((128, 2), BF)), SHAPE),
+    (dict(zeros=_t((128, 4), F16)), DTYPE),
+    (dict(zeros=_t((128, 8), BF)), SHAPE),
+    (dict(bias=_t((127,), F16)), SHAPE),
+    (dict(bias=_t((128,), torch.float32)), DTYPE),
+    (dict(out=_t((4, 127), BF)), SHAPE),
+    (dict(out=_t((4, 128), F16)), DTYPE),
+])
+def test_binding_w4_rejects_bad_operands(change, status):
+    a = _w4_args()
+    a.update(change)
+    assert _status(qg.gemm_w4a16, group_size=64, **a) == status
+
+
+def test_binding_w4_per_channel_scale_shape():
+    a = _w4_args(g=256)
+    a["scales"], a["zeros"] = _t((128, 2), BF), _t((128,), BF)
+    assert _status(qg.gemm_w4a16, group_size=-1, **a) == SHAPE
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(B_tiled=_t((128, 256), torch.uint8)), DTYPE),
+    (dict(B_tiled=_t((128, 128), torch.int8)), SHAPE),
+    (dict(scales=_t((128,), BF)), DTYPE),
+    (dict(scales=_t((64,), F16)), SHAPE),
+    (dict(scales=_t((128, 2), F16)), SHAPE),                      # group -1 needs [n]
+    (dict(out=_t((4, 64), F16)), SHAPE),
+])
+def test_binding_w8_rejects_bad_operands(change, status):
+    a = dict(A=_t((4, 256), F16), B_tiled=_t((128, 256), torch.int8), scales=_t((128,), F16))
+    a.update(change)
+    assert _status(qg.gemm_w8a16, group_size=-1, **a) == status
+
+
+def test_binding_w8_group_scale_shape():
+    a = dict(A=_t((4, 256), F16), B_tiled=_t((128, 256), torch.int8), scales=_t((2, 128), F16))
+    assert _status(qg.gemm_w8a16, group_size=128, **a) == SHAPE
+
+
+def _moe_args(T=8, H=128, I=128, E=4, g=64, dt=BF):
+    return dict(x=_t((T, H), dt), logits=_t((T, E), torch.float32),
+                w1_tiled=_t((E, 2 * I, H // 2), torch.uint8), s1=_t((E, 2 * I, H // g), dt),
+                z1=_t((E, 2 * I, H // g), dt), w2_tiled=_t((E, H, I // 2), torch.uint8),
+                s2=_t((E, H, I // g), dt), z2=_t((E, H, I // g), dt))
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(logits=_t((8, 4), BF)), DTYPE),
+    (dict(logits=_t((7, 4), torch.float32)), SHAPE),
+    (dict(w1_tiled=_t((4, 256, 32), torch.uint8)), SHAPE),
+    (dict(w1_tiled=_t((3, 256, 64), torch.uint8)), SHAPE),
+    (dict(w2_tiled=_t((4, 128, 32), torch.uint8)), SHAPE),
+    (dict(s1=_t((4, 256, 2), torch.float32)), DTYPE),
+    (dict(s1=_t((4, 2, 256), BF)), SHAPE),
+    (dict(z2=_t((4, 128, 3), BF)), SHAPE),
+    (dict(b1=_t((4, 128), BF)), SHAPE),
+    (dict(b2=_t((4, 128), F16)), SHAPE),
+    (dict(sel_logits=_t((8, 5), torch.float32)), SHAPE),
+    (dict(finished=_t((7,), torch.bool)), SHAPE),
+    (dict(topk=5), SHAPE),
+])
+def test_binding_moe_rejects_bad_operands(change, status):
+    a = _moe_args()
+    a["topk"] = 2
+    a.update(change)
+    assert _status(qg.moe_grouped, **a) == status
+
+
+@pytest.mark.parametrize("call,status", [
+    (lambda: qg.dequant_w4(_t((16, 64), torch.uint8), _t((16, 2), torch.float32), None, 64), DTYPE),
+    (lambda: qg.dequant_w4(_t((16, 64), torch.uint8), _t((2, 16), BF), None, 64), SHAPE),
+    (lambda: qg.dequant_w4(_t((16, 64), torch.uint8), _t((16, 2), BF), _t((16, 2), F16), 64), DTYPE),
+    (lambda: qg.dequant_w4(_t((16, 64), torch.uint8), _t((16, 2), BF), None, 64, F16), DTYPE),
+    (lambda: qg.dequant_w8(_t((16, 128), torch.int8), _t((16, 2), F16), torch.float32, -1), SHAPE),
+    (lambda: qg.dequant_w8(_t((16, 128), torch.uint8), _t((16,), F16)), DTYPE),
+    (lambda: qg.embed_w4(_t((3,), torch.int64), _t((16, 64), torch.uint8), _t((16, 2), BF), None, 64), DTYPE),
+    (lambda: qg.embed_w4(_t((3,), torch.int32), _t((16, 64), torch.uint8), _t((16, 4), BF), None, 64), SHAPE),
+    (lambda: qg.embed_w8(_t((3,), torch.int32), _t((16, 128), torch.int8), _t((8,), F16)), SHAPE),
+    (lambda: qg.repack_w4(_t((16, 64), torch.int8)), DTYPE),
+    (lambda: qg.repack_w8(_t((16, 64), torch.uint8)), DTYPE),
+    (lambda: qg.quantize_w4(_t((16, 128), torch.int32)), DTYPE),
+    (lambda: qg.gemm_w8a8(_t((4, 128), torch.int8), _t((16, 64), torch.int8), _t((1,), torch.float32),
+                          _t((1,), torch.float32)), SHAPE),
+    (lambda: qg.gemm_w8a8(_t((4, 128), torch.int8), _t((16, 128), torch.int8), _t((1,), F16),
+                          _t((1,), torch.float32)), DTYPE),
+])
+def test_binding_other_calls_reject_bad_operands(call, status):
+    assert _status(call) == status
+
+
+def test_binding_device_check_follows_shape_checks():
+    # Right shapes and dtypes on the host: the device check is what refuses.
+    assert _status(qg.gemm_w4a16, group_size=64, **_w4_args()) == NULL
+
+
+def test_override_spec_validation():
+    L = qg.lib()
+    assert L.qg_set_override(b"path=decode,prefill_tile=D8,splitk=2,moe_tile=S,"
+                             b"w8a8_tile=T64,w8a8_split=3") == OK
+    for bad in (b"path=fast", b"tile=D8", b"splitk=0", b"prefill_tile=Q", b"w8a8_tile=7",
+                b"moe_tile=L", b"splitk", b"splitk=2x"):
+        assert L.qg_set_override(bad) == 9, bad
+    assert L.qg_set_override(None) == OK and L.qg_set_override(b"") == OK
+    qg.set_override(path="prefill")
+    qg.set_override(splitk=3)
+    assert qg._override == {"path": "prefill", "splitk": 3}
+    qg.set_override(path=None)
+    assert qg._override == {"splitk": 3}
+    qg.clear_override()
+    assert qg._override == {}

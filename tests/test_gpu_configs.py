@@ -10,7 +10,7 @@ import torch
 import oracle
 import synth_inputs as si
 import weight_only_quantized_w8a16_amd as qg
-from helpers import BF16, FP16, TOL, rel_err, to_dev
+from helpers import BF16, FP16, TOL, TORCH_DT, rel_err, to_bits, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -27,11 +27,20 @@ def sample_pairs(m, n, seed, grid_rows=6, grid_cols=192, rand=512):
     return r, c
 
 
+def _nan_out(m, n, dtype):
+    """An output buffer filled with NaN: a finite result everywhere proves
+    the kernels wrote every element (the sampled checks below cannot)."""
+    return torch.full((m, n), float("nan"), dtype=TORCH_DT[dtype], device="cuda")
+
+
 def gpu_w4(p):
     A = to_dev(p.A, p.dtype)
     tiled = qg.repack_w4(to_dev(p.packed))
     bias = to_dev(p.bias, p.bias_dtype) if p.bias is not None else None
-    C = qg.gemm_w4a16(A, tiled, to_dev(p.scale, p.dtype), to_dev(p.zero, p.dtype), bias, p.group)
+    Z = to_dev(p.zero, p.dtype) if p.zero is not None else None
+    C = qg.gemm_w4a16(A, tiled, to_dev(p.scale, p.dtype), Z, bias, p.group,
+                      out=_nan_out(p.m, p.n, p.dtype))
+    assert bool(torch.isfinite(C).all()), "an output element was never written"
     return C.float().cpu().numpy()
 
 
@@ -39,7 +48,9 @@ def gpu_w8(p):
     A = to_dev(p.A, p.dtype)
     tiled = qg.repack_w8(to_dev(p.codes))
     bias = to_dev(p.bias, p.bias_dtype) if p.bias is not None else None
-    C = qg.gemm_w8a16(A, tiled, to_dev(p.scale, p.dtype), bias, -1)
+    C = qg.gemm_w8a16(A, tiled, to_dev(p.scale, p.dtype), bias, p.group,
+                      out=_nan_out(p.m, p.n, p.dtype))
+    assert bool(torch.isfinite(C).all()), "an output element was never written"
     return C.float().cpu().numpy()
 
 
@@ -87,6 +98,31 @@ def test_prefill(m, n, g):
         ref = oracle.gemm_w4_at(p.A, p.packed, p.scale, p.zero, g, r, c, BF16, p.bias, FP16)
         err = rel_err(C[r, c], ref)
     assert err <= TOL[BF16], (m, n, g, err)
+
+
+def test_prefill_integer_exact_at_the_metric_shape():
+    # M = 512, N = 131072, K = 2048, g = 64 with an fp16 bias, on the tile
+    # and grouped per-XCD tile order the benchmark times: dyadic inputs make
+    # every partial sum exact in fp32, so all 67M outputs must equal the
+    # round-to-nearest-even of the exact product bit for bit.  The exact
+    # product is the oracle's dequantized weight times A in fp64 (exact for
+    # these inputs), a library matmul as the brute-force step.
+    m, n, k, g = 512, 131072, 2048, 64
+    p = si.w4_exact_problem(m, n, k, g, seed=512, dtype=BF16, bias_dtype=FP16)
+    A = to_dev(p.A, BF16)
+    tiled = qg.repack_w4(to_dev(p.packed))
+    C = qg.gemm_w4a16(A, tiled, to_dev(p.scale, BF16), to_dev(p.zero, BF16),
+                      to_dev(p.bias, FP16), g, out=_nan_out(m, n, BF16))
+    got = to_bits(C)
+    W = oracle.dequant4(p.packed, p.scale, p.zero, g, BF16).astype(np.float64)
+    Cref = oracle.bf16_to_f32(p.A).astype(np.float64) @ W.T + oracle.f16_to_f32(p.bias)
+    del W
+    assert np.array_equal(Cref.astype(np.float32).astype(np.float64), Cref)
+    r, c = sample_pairs(m, n, seed=5)
+    at = oracle.gemm_w4_at(p.A, p.packed, p.scale, p.zero, g, r, c, BF16, p.bias, FP16)
+    assert np.array_equal(at, Cref[r, c])           # the sum agrees with the oracle's own
+    exp = torch.from_numpy(Cref.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy()
+    assert np.array_equal(got.view(np.int16), exp)
 
 
 # -- ragged and edge shapes ------------------------------------------------------------

@@ -91,3 +91,24 @@ def test_w4_activations_past_2gib():
            rows, cols, BF16, "prefill")
     del tiled, C
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("m", [32767, 32769])
+def test_w4_activations_at_the_2gib_boundary(m):
+    # M * K * 2 bytes of activations just below 2^31 (the 256 x 128
+    # direct-load tile, 32-bit buffer offsets up to the last row) and just
+    # above (the generic tile of the same width).
+    n, g = 256, 64
+    p = si.w4_problem(m, n, K, g, tag="edge-a")
+    assert (p.A.nbytes < 2 ** 31) == (m == 32767)
+    tiled = qg.repack_w4(to_dev(p.packed))
+    C = qg.gemm_w4a16(to_dev(p.A, BF16), tiled, to_dev(p.scale, BF16), to_dev(p.zero, BF16),
+                      None, g)
+    torch.cuda.synchronize()
+    rows, cols = _pairs(m, n, 4)
+    rows = np.concatenate([rows, [m - 1, m - 2, 32766]])
+    cols = np.concatenate([cols, [255, 0, 131]])
+    _check(C, oracle.gemm_w4_at(p.A, p.packed, p.scale, p.zero, g, rows, cols, BF16),
+           rows, cols, BF16, f"m={m}")
+    del tiled, C
+    torch.cuda.empty_cache()

@@ -21,7 +21,7 @@ __all__ = [
     "QGemmError", "lib", "repack_w4", "unrepack_w4", "repack_w8", "unrepack_w8", "repack_w8_kn",
     "unrepack_w8_kn", "quantize_w4", "dequant_w4", "dequant_w8", "gemm_w4a16", "gemm_w8a16",
     "moe_grouped", "moe_workspace_size", "gemm_workspace_size", "dtype_code", "gemm_w8a8",
-    "w8a8_workspace_size", "embed_w4", "embed_w8", "read_probe",
+    "w8a8_workspace_size", "embed_w4", "embed_w8", "read_probe", "set_override", "clear_override",
 ]
 
 _CODES = {torch.bfloat16: QG_BF16, torch.float16: QG_FP16, torch.float32: QG_FP32}
@@ -59,10 +59,82 @@ def _stream(t: torch.Tensor):
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
+# -- operand checks: shapes and dtypes, before any pointer reaches the library --
+# The C ABI takes raw pointers and sizes, so a tensor of the wrong shape or
+# dtype would be read past its end or misread; these raise instead.
+
+_SHAPE, _DTYPE = 2, 4
+_ACT = (torch.bfloat16, torch.float16)
+
+
+def _need(cond: bool, func: str, status: int, msg: str) -> None:
+    if not cond:
+        raise QGemmError(func, status, msg)
+
+
+def _shape(t) -> tuple:
+    return tuple(t.shape)
+
+
+def _check_groups(func: str, name: str, t: torch.Tensor, dtype, rows: int, k: int, group: int,
+                  lead: tuple = ()) -> None:
+    """scales / zeros: `dtype`, shape lead + [rows, k / group] (groupwise) or
+    lead + [rows] (group -1 or k: one per row; a trailing 1 is accepted)."""
+    _need(t.dtype == dtype, func, _DTYPE, f"{name} must be {dtype} (got {t.dtype})")
+    if group in (-1, k):
+        ok = _shape(t) in (lead + (rows,), lead + (rows, 1))
+        want = f"{list(lead + (rows,))}"
+    elif group > 0 and k % group == 0:
+        ok = _shape(t) == lead + (rows, k // group)
+        want = f"{list(lead + (rows, k // group))}"
+    else:
+        return   # the library rejects the group size itself
+    _need(ok, func, _SHAPE, f"{name} must be {want} (got {list(t.shape)})")
+
+
+def _check_out(func: str, out: torch.Tensor, dtype, m: int, n: int) -> None:
+    _need(out.dtype == dtype, func, _DTYPE, f"out must be {dtype} (got {out.dtype})")
+    _need(out.dim() >= 1 and out.shape[-1] == n and out.numel() == m * n, func, _SHAPE,
+          f"out must hold [{m}, {n}] (got {list(out.shape)})")
+
+
+def _check_bias(func: str, bias: Optional[torch.Tensor], n: int) -> None:
+    if bias is None:
+        return
+    _need(bias.dtype in _ACT, func, _DTYPE, f"bias must be bf16 or fp16 (got {bias.dtype})")
+    _need(_shape(bias) == (n,), func, _SHAPE, f"bias must be [{n}] (got {list(bias.shape)})")
+
+
+# -- dispatch override (tests and tuning) -------------------------------------
+
+_override: dict = {}
+
+
+def set_override(**choices) -> None:
+    """Force dispatch choices for later calls (qg_set_override): path,
+    prefill_tile, splitk, moe_tile, w8a8_tile, w8a8_split.  Merges with the
+    choices set before; a value of None returns that key to automatic."""
+    for key, val in choices.items():
+        if val is None:
+            _override.pop(key, None)
+        else:
+            _override[key] = val
+    spec = ",".join(f"{k}={v}" for k, v in _override.items())
+    check("qg_set_override", lib().qg_set_override(spec.encode()))
+
+
+def clear_override() -> None:
+    """Every dispatch choice automatic again."""
+    _override.clear()
+    check("qg_set_override", lib().qg_set_override(None))
+
+
 # -- load-side repack -------------------------------------------------------
 
 def repack_w4(packed: torch.Tensor) -> torch.Tensor:
     """Portable int4 [n, k/2] uint8 -> tiled layout (same shape and bytes)."""
+    _need(packed.dtype == torch.uint8 and packed.dim() == 2, "qrepack_w4", _DTYPE,
+          "packed must be a 2-D uint8 tensor [n, k/2]")
     _dev(packed, "packed")
     n, half = packed.shape
     out = torch.empty_like(packed)
@@ -71,6 +143,8 @@ def repack_w4(packed: torch.Tensor) -> torch.Tensor:
 
 
 def unrepack_w4(tiled: torch.Tensor) -> torch.Tensor:
+    _need(tiled.dtype == torch.uint8 and tiled.dim() == 2, "qunrepack_w4", _DTYPE,
+          "tiled must be a 2-D uint8 tensor [n, k/2]")
     _dev(tiled, "tiled")
     n, half = tiled.shape
     out = torch.empty_like(tiled)
@@ -80,6 +154,8 @@ def unrepack_w4(tiled: torch.Tensor) -> torch.Tensor:
 
 def repack_w8(codes: torch.Tensor) -> torch.Tensor:
     """Portable int8 [n, k] -> tiled layout (same shape, offset-binary bytes)."""
+    _need(codes.dtype == torch.int8 and codes.dim() == 2, "qrepack_w8", _DTYPE,
+          "codes must be a 2-D int8 tensor [n, k]")
     _dev(codes, "codes")
     n, k = codes.shape
     out = torch.empty_like(codes)
@@ -88,6 +164,8 @@ def repack_w8(codes: torch.Tensor) -> torch.Tensor:
 
 
 def unrepack_w8(tiled: torch.Tensor) -> torch.Tensor:
+    _need(tiled.dtype == torch.int8 and tiled.dim() == 2, "qunrepack_w8", _DTYPE,
+          "tiled must be a 2-D int8 tensor [n, k]")
     _dev(tiled, "tiled")
     n, k = tiled.shape
     out = torch.empty_like(tiled)
@@ -97,6 +175,8 @@ def unrepack_w8(tiled: torch.Tensor) -> torch.Tensor:
 
 def repack_w8_kn(codes_kn: torch.Tensor) -> torch.Tensor:
     """int8 [k, n] (K-major) -> tiled layout [n, k] (as repack_w8 of the transpose)."""
+    _need(codes_kn.dtype == torch.int8 and codes_kn.dim() == 2, "qrepack_w8_kn", _DTYPE,
+          "codes_kn must be a 2-D int8 tensor [k, n]")
     _dev(codes_kn, "codes_kn")
     k, n = codes_kn.shape
     out = torch.empty((n, k), dtype=codes_kn.dtype, device=codes_kn.device)
@@ -106,6 +186,8 @@ def repack_w8_kn(codes_kn: torch.Tensor) -> torch.Tensor:
 
 def unrepack_w8_kn(tiled: torch.Tensor) -> torch.Tensor:
     """Tiled int8 [n, k] -> int8 [k, n] (K-major)."""
+    _need(tiled.dtype == torch.int8 and tiled.dim() == 2, "qunrepack_w8_kn", _DTYPE,
+          "tiled must be a 2-D int8 tensor [n, k]")
     _dev(tiled, "tiled")
     n, k = tiled.shape
     out = torch.empty((k, n), dtype=tiled.dtype, device=tiled.device)
@@ -121,9 +203,13 @@ def quantize_w4(W: torch.Tensor, group_size: int = 64, sz_dtype: Optional[torch.
     Returns (packed uint8 [n, k/2] in the portable layout, scales, zeros
     [n, k/group] in sz_dtype, default W's dtype).
     """
+    _need(W.dtype in _ACT + (torch.float32,) and W.dim() == 2, "qquantize_w4", _DTYPE,
+          "W must be a 2-D bf16, fp16 or fp32 tensor [n, k]")
+    sz_dtype = W.dtype if sz_dtype is None else sz_dtype
+    _need(sz_dtype in _ACT + (torch.float32,), "qquantize_w4", _DTYPE,
+          "sz_dtype must be bf16, fp16 or fp32")
     _dev(W, "W")
     n, k = W.shape
-    sz_dtype = W.dtype if sz_dtype is None else sz_dtype
     packed = torch.empty((n, k // 2), dtype=torch.uint8, device=W.device)
     ng = k // group_size if group_size > 0 else 0
     scales = torch.empty((n, ng), dtype=sz_dtype, device=W.device)
@@ -139,6 +225,15 @@ def quantize_w4(W: torch.Tensor, group_size: int = 64, sz_dtype: Optional[torch.
 def dequant_w4(tiled: torch.Tensor, scales: torch.Tensor, zeros: Optional[torch.Tensor],
                group_size: int, out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
     """Tiled int4 -> W [n, k]; zeros None = scale-only, group_size -1 = per channel."""
+    f = "qdequant_w4"
+    _need(tiled.dtype == torch.uint8 and tiled.dim() == 2, f, _DTYPE,
+          "tiled must be a 2-D uint8 tensor [n, k/2]")
+    _need(scales.dtype in _ACT, f, _DTYPE, "scales must be bf16 or fp16")
+    _check_groups(f, "scales", scales, scales.dtype, tiled.shape[0], 2 * tiled.shape[1], group_size)
+    if zeros is not None:
+        _check_groups(f, "zeros", zeros, scales.dtype, tiled.shape[0], 2 * tiled.shape[1], group_size)
+    _need(out_dtype in (torch.float32, scales.dtype), f, _DTYPE,
+          "out_dtype must be fp32 or the scales' dtype")
     for t, nm in ((tiled, "tiled"), (scales, "scales"), (zeros, "zeros")):
         if t is not None:
             _dev(t, nm)
@@ -152,6 +247,13 @@ def dequant_w4(tiled: torch.Tensor, scales: torch.Tensor, zeros: Optional[torch.
 
 def dequant_w8(tiled: torch.Tensor, scales: torch.Tensor,
                out_dtype: torch.dtype = torch.float32, group_size: int = -1) -> torch.Tensor:
+    f = "qdequant_w8"
+    _need(tiled.dtype == torch.int8 and tiled.dim() == 2, f, _DTYPE,
+          "tiled must be a 2-D int8 tensor [n, k]")
+    _need(scales.dtype in _ACT, f, _DTYPE, "scales must be bf16 or fp16")
+    _check_groups(f, "scales", scales, scales.dtype, tiled.shape[0], tiled.shape[1], group_size)
+    _need(out_dtype in (torch.float32, scales.dtype), f, _DTYPE,
+          "out_dtype must be fp32 or the scales' dtype")
     _dev(tiled, "tiled")
     _dev(scales, "scales")
     n, k = tiled.shape
@@ -190,6 +292,21 @@ def gemm_w4a16(A: torch.Tensor, B_tiled: torch.Tensor, scales: torch.Tensor,
     group_size 64 / 128 (scales [n, k/g]) or -1 (one per channel, [n]);
     zeros None for scale-only weights, w = (q - 8) * s.
     """
+    f = "qgemm_w4a16"
+    _need(A.dtype in _ACT and A.dim() >= 1, f, _DTYPE, f"A must be bf16 or fp16 (got {A.dtype})")
+    k = A.shape[-1]
+    m = A.numel() // k if k else 0
+    _need(B_tiled.dtype == torch.uint8 and B_tiled.dim() == 2, f, _DTYPE,
+          "B_tiled must be a 2-D uint8 tensor [n, k/2]")
+    _need(2 * B_tiled.shape[1] == k, f, _SHAPE,
+          f"B_tiled must be [n, {k // 2}] for k = {k} (got {list(B_tiled.shape)})")
+    n = B_tiled.shape[0]
+    _check_groups(f, "scales", scales, A.dtype, n, k, group_size)
+    if zeros is not None:
+        _check_groups(f, "zeros", zeros, A.dtype, n, k, group_size)
+    _check_bias(f, bias, n)
+    if out is not None:
+        _check_out(f, out, A.dtype, m, n)
     _dev(A, "A")
     for t, nm in ((B_tiled, "B_tiled"), (scales, "scales"), (zeros, "zeros")):
         if t is not None:
@@ -197,9 +314,7 @@ def gemm_w4a16(A: torch.Tensor, B_tiled: torch.Tensor, scales: torch.Tensor,
     if bias is not None:
         _dev(bias, "bias")
     lead = A.shape[:-1]
-    k = A.shape[-1]
     A2 = A.reshape(-1, k)
-    m, n = A2.shape[0], B_tiled.shape[0]
     C = out if out is not None else torch.empty((m, n), dtype=A.dtype, device=A.device)
     _dev(C, "out")
     ws, ws_bytes = _workspace(m, n, k, group_size, 4, A.device, workspace)
@@ -215,15 +330,26 @@ def gemm_w8a16(A: torch.Tensor, B_tiled: torch.Tensor, scales: torch.Tensor,
                out: Optional[torch.Tensor] = None,
                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """C = A . dequant(B)^T (+ bias); A [..., k] bf16/fp16, B tiled int8."""
+    f = "qgemm_w8a16"
+    _need(A.dtype in _ACT and A.dim() >= 1, f, _DTYPE, f"A must be bf16 or fp16 (got {A.dtype})")
+    k = A.shape[-1]
+    m = A.numel() // k if k else 0
+    _need(B_tiled.dtype == torch.int8 and B_tiled.dim() == 2, f, _DTYPE,
+          "B_tiled must be a 2-D int8 tensor [n, k]")
+    _need(B_tiled.shape[1] == k, f, _SHAPE,
+          f"B_tiled must be [n, {k}] (got {list(B_tiled.shape)})")
+    n = B_tiled.shape[0]
+    _check_groups(f, "scales", scales, A.dtype, n, k, group_size)
+    _check_bias(f, bias, n)
+    if out is not None:
+        _check_out(f, out, A.dtype, m, n)
     _dev(A, "A")
     _dev(B_tiled, "B_tiled")
     _dev(scales, "scales")
     if bias is not None:
         _dev(bias, "bias")
     lead = A.shape[:-1]
-    k = A.shape[-1]
     A2 = A.reshape(-1, k)
-    m, n = A2.shape[0], B_tiled.shape[0]
     C = out if out is not None else torch.empty((m, n), dtype=A.dtype, device=A.device)
     _dev(C, "out")
     ws, ws_bytes = _workspace(m, n, k, group_size, 8, A.device, workspace)
@@ -247,12 +373,18 @@ def gemm_w8a8(A: torch.Tensor, B: torch.Tensor, alpha_row: torch.Tensor,
     """C = (A_int8 . B_int8^T) * alpha_row * alpha_col; A [..., k] int8,
     B [n, k] int8, alpha_row fp32 [m] (per token) or [1], alpha_col fp32 [n]
     (per channel) or [1]; the quant mode follows the scale lengths."""
+    f = "qgemm_w8a8"
+    _need(A.dtype == torch.int8 and A.dim() >= 1, f, _DTYPE, "A must be int8")
+    _need(B.dtype == torch.int8 and B.dim() == 2, f, _DTYPE, "B must be a 2-D int8 tensor [n, k]")
+    _need(alpha_row.dtype == torch.float32 and alpha_col.dtype == torch.float32, f, _DTYPE,
+          "alpha_row and alpha_col must be fp32")
+    k = A.shape[-1]
+    _need(B.shape[1] == k, f, _SHAPE, f"B must be [n, {k}] (got {list(B.shape)})")
     _dev(A, "A")
     _dev(B, "B")
     _dev(alpha_row, "alpha_row")
     _dev(alpha_col, "alpha_col")
     lead = A.shape[:-1]
-    k = A.shape[-1]
     A2 = A.reshape(-1, k)
     m, n = A2.shape[0], B.shape[0]
     if alpha_row.numel() not in (1, m) or alpha_col.numel() not in (1, n):
@@ -286,12 +418,18 @@ def embed_w4(ids: torch.Tensor, table: torch.Tensor, scales: torch.Tensor,
     """Rows ids of the int4 table, dequantized: [*ids.shape, hidden].  The
     table is the tiled [vocab, hidden/2] GEMM weight (tiled=True) or the
     portable one; scales (and zeros) set the activation dtype."""
+    f = "qembed_w4"
+    _need(ids.dtype == torch.int32, f, _DTYPE, "ids must be int32")
+    _need(table.dtype == torch.uint8 and table.dim() == 2, f, _DTYPE,
+          "table must be a 2-D uint8 tensor [vocab, hidden/2]")
+    _need(scales.dtype in _ACT, f, _DTYPE, "scales must be bf16 or fp16")
+    _check_groups(f, "scales", scales, scales.dtype, table.shape[0], 2 * table.shape[1], group_size)
+    if zeros is not None:
+        _check_groups(f, "zeros", zeros, scales.dtype, table.shape[0], 2 * table.shape[1], group_size)
     for t, name in ((ids, "ids"), (table, "table"), (scales, "scales")):
         _dev(t, name)
     if zeros is not None:
         _dev(zeros, "zeros")
-    if ids.dtype != torch.int32:
-        raise QGemmError("qembed_w4", 4, "ids must be int32")
     vocab, hidden = table.shape[0], table.shape[1] * 2
     out = _embed_out(ids, hidden, scales.dtype, out_dtype, table.device)
     check("qembed_w4", lib().qembed_w4(
@@ -304,10 +442,14 @@ def embed_w4(ids: torch.Tensor, table: torch.Tensor, scales: torch.Tensor,
 def embed_w8(ids: torch.Tensor, table: torch.Tensor, scales: torch.Tensor, group_size: int = -1,
              tiled: bool = True, out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
     """Rows ids of the int8 table [vocab, hidden], dequantized."""
+    f = "qembed_w8"
+    _need(ids.dtype == torch.int32, f, _DTYPE, "ids must be int32")
+    _need(table.dtype == torch.int8 and table.dim() == 2, f, _DTYPE,
+          "table must be a 2-D int8 tensor [vocab, hidden]")
+    _need(scales.dtype in _ACT, f, _DTYPE, "scales must be bf16 or fp16")
+    _check_groups(f, "scales", scales, scales.dtype, table.shape[0], table.shape[1], group_size)
     for t, name in ((ids, "ids"), (table, "table"), (scales, "scales")):
         _dev(t, name)
-    if ids.dtype != torch.int32:
-        raise QGemmError("qembed_w8", 4, "ids must be int32")
     vocab, hidden = table.shape
     out = _embed_out(ids, hidden, scales.dtype, out_dtype, table.device)
     check("qembed_w8", lib().qembed_w8(
@@ -345,16 +487,54 @@ def moe_grouped(x: torch.Tensor, logits: torch.Tensor, w1_tiled: torch.Tensor, s
                 topk: int, group_size: int = 64, return_routing: bool = False,
                 workspace: Optional[torch.Tensor] = None, b1: Optional[torch.Tensor] = None,
                 b2: Optional[torch.Tensor] = None, sel_logits: Optional[torch.Tensor] = None,
-                finished: Optional[torch.Tensor] = None, renormalize: bool = True):
+                finished: Optional[torch.Tensor] = None, renormalize: bool = True,
+                out: Optional[torch.Tensor] = None):
     """Top-k MoE with SiLU-gated int4 experts.
 
     x [T, H]; logits fp32 [T, E]; w1_tiled [E, 2I, H/2] (tiled per expert);
     s1/z1 [E, 2I, H/g]; w2_tiled [E, H, I/2]; s2/z2 [E, H, I/g].  Optional:
     fc1 / fc2 expert biases b1 [E, 2I], b2 [E, H] (x's dtype), biased
     selection logits fp32 [T, E], a finished mask (bool/uint8 [T]) and the
-    normalization mode.  Returns out [T, H] (and (ids int32 [T, k], weights
-    fp32 [T, k])).
+    normalization mode.  Returns out [T, H] (into `out` when given) (and
+    (ids int32 [T, k], weights fp32 [T, k])).
     """
+    f = "qmoe_grouped"
+    _need(x.dtype in _ACT and x.dim() == 2, f, _DTYPE, "x must be a 2-D bf16 or fp16 tensor [T, H]")
+    T, H = x.shape
+    _need(logits.dtype == torch.float32 and logits.dim() == 2, f, _DTYPE,
+          "logits must be a 2-D fp32 tensor [T, E]")
+    _need(logits.shape[0] == T, f, _SHAPE, f"logits must be [{T}, E] (got {list(logits.shape)})")
+    E = logits.shape[1]
+    _need(w1_tiled.dtype == torch.uint8 and w2_tiled.dtype == torch.uint8, f, _DTYPE,
+          "w1_tiled and w2_tiled must be uint8")
+    _need(w1_tiled.dim() == 3 and w1_tiled.shape[1] % 2 == 0, f, _SHAPE,
+          "w1_tiled must be [E, 2I, H/2]")
+    I2 = w1_tiled.shape[1]
+    _need(_shape(w1_tiled) == (E, I2, H // 2), f, _SHAPE,
+          f"w1_tiled must be [{E}, 2I, {H // 2}] (got {list(w1_tiled.shape)})")
+    _need(_shape(w2_tiled) == (E, H, I2 // 4), f, _SHAPE,
+          f"w2_tiled must be [{E}, {H}, {I2 // 4}] (got {list(w2_tiled.shape)})")
+    for t, nm in ((s1, "s1"), (z1, "z1")):
+        _check_groups(f, nm, t, x.dtype, I2, H, group_size, lead=(E,))
+    for t, nm in ((s2, "s2"), (z2, "z2")):
+        _check_groups(f, nm, t, x.dtype, H, I2 // 2, group_size, lead=(E,))
+    if b1 is not None:
+        _need(b1.dtype == x.dtype and _shape(b1) == (E, I2), f, _SHAPE,
+              f"b1 must be [{E}, {I2}] in x's dtype")
+    if b2 is not None:
+        _need(b2.dtype == x.dtype and _shape(b2) == (E, H), f, _SHAPE,
+              f"b2 must be [{E}, {H}] in x's dtype")
+    if sel_logits is not None:
+        _need(sel_logits.dtype == torch.float32 and _shape(sel_logits) == (T, E), f, _SHAPE,
+              f"sel_logits must be fp32 [{T}, {E}]")
+    if finished is not None:
+        _need(finished.dtype in (torch.bool, torch.uint8) and _shape(finished) == (T,), f, _SHAPE,
+              f"finished must be bool or uint8 [{T}]")
+    _need(isinstance(topk, int) and 1 <= topk <= E, f, _SHAPE, f"topk must be in [1, {E}]")
+    if out is not None:
+        _need(out.dtype == x.dtype and _shape(out) == (T, H), f, _SHAPE,
+              f"out must be [{T}, {H}] in x's dtype")
+        _dev(out, "out")
     for t, nm in ((x, "x"), (logits, "logits"), (w1_tiled, "w1_tiled"), (s1, "s1"), (z1, "z1"),
                   (w2_tiled, "w2_tiled"), (s2, "s2"), (z2, "z2")):
         _dev(t, nm)
@@ -363,10 +543,9 @@ def moe_grouped(x: torch.Tensor, logits: torch.Tensor, w1_tiled: torch.Tensor, s
             _dev(t, nm)
     if finished is not None and finished.dtype == torch.bool:
         finished = finished.view(torch.uint8)
-    T, H = x.shape
-    E = logits.shape[1]
-    inter = w1_tiled.shape[1] // 2
-    out = torch.empty_like(x)
+    inter = I2 // 2
+    if out is None:
+        out = torch.empty_like(x)
     ids = torch.empty((T, topk), dtype=torch.int32, device=x.device) if return_routing else None
     wts = torch.empty((T, topk), dtype=torch.float32, device=x.device) if return_routing else None
     need = moe_workspace_size(T, H, inter, E, topk)
