@@ -257,13 +257,13 @@ def test_dequant_w4_scale_forms_bit_exact(group, zeros, dtype):
     assert np.array_equal(W32.view(np.uint32), ref.view(np.uint32))
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 16, 128), (5, 256, 2048), (33, 128, 256), (300, 512, 640),
-                                   (16, 3584, 3584), (1, 65536, 256)])
+# (1, 65536, 256) is a decode-sized problem: the decode path only.
+@pytest.mark.parametrize("m,n,k,path", [
+    (m, n, k, path) for (m, n, k) in [(1, 16, 128), (5, 256, 2048), (33, 128, 256), (300, 512, 640),
+                                      (16, 3584, 3584), (1, 65536, 256)]
+    for path in ("decode", "prefill") if not (path == "prefill" and n > 8192)])
 @pytest.mark.parametrize("group,zeros", FORMS)
-@pytest.mark.parametrize("path", ["decode", "prefill"])
-def test_w4_scale_forms_integer_exact(m, n, k, group, zeros, path):
-    if path == "prefill" and n > 8192:
-        pytest.skip("a decode-sized problem")
+def test_w4_scale_forms_integer_exact(m, n, k, path, group, zeros):
     p = si.w4_exact_problem(m, n, k, group, seed=m + n + k, dtype=BF16, bias_dtype=FP16, zeros=zeros)
     Cref = oracle.gemm_w4(p.A, p.packed, p.scale, p.zero, group, BF16, p.bias, FP16)
     got = to_bits(_run_w4(p, path))
