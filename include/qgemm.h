@@ -331,6 +331,25 @@ qg_status qmoe_grouped(const void *x, const float *logits, const uint8_t *w1_til
                        float *topk_w_out, void *workspace, size_t workspace_bytes,
                        void *stream);
 
+/* Allocation-free variant of qmoe_grouped, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same computation, arguments and
+ * results, with no workspace argument.  Its workspace is a 64 MiB device
+ * array inside the library (one per GPU the library runs on, held until the
+ * process ends; its address is looked up once per device on the first call
+ * there); the call allocates nothing.  A problem whose qmoe_workspace_size()
+ * exceeds 64 MiB (2^26 bytes; e.g. more than about 1600 tokens at hidden
+ * 2048, inter 1408, 64 experts, top-6) returns QG_ERR_WORKSPACE before any
+ * launch.  Every call on one GPU shares that array: calls that overlap on
+ * one GPU (other streams, other threads) race and must be serialized by the
+ * caller.  Nothing in the array needs clearing between calls. */
+qg_status qmoe_grouped_noalloc(const void *x, const float *logits, const uint8_t *w1_tiled,
+                               const void *s1, const void *z1, const uint8_t *w2_tiled,
+                               const void *s2, const void *z2, void *out, int tokens, int hidden,
+                               int inter, int experts, int topk, int group_size,
+                               qg_dtype act_dtype, int32_t *topk_ids_out, float *topk_w_out,
+                               void *stream);
+
 /* The same MoE with the optional inputs of runMoe (acext User Guide (v1.7),
  * 1.2.3: gating_output_with_bias, fc1/fc2 expert biases, finished,
  * normalization_mode):

@@ -470,3 +470,15 @@ def test_override_spec_validation():
     assert qg._override == {"splitk": 3}
     qg.clear_override()
     assert qg._override == {}
+
+
+def test_moe_noalloc_rejects_problems_beyond_the_scratch():
+    # 2048 tokens at hidden 2048, inter 1408, 64 experts, top-6 need ~81 MiB
+    # of workspace (> the 64 MiB device scratch): refused on the host, before
+    # any pointer is touched.
+    L = qg.lib()
+    assert L.qmoe_workspace_size(2048, 2048, 1408, 64, 6) > (64 << 20)
+    args = [FAKE] * 9
+    assert L.qmoe_grouped_noalloc(*args, 2048, 2048, 1408, 64, 6, 64, BF16, None, None, None) == WORKSPACE
+    assert L.qmoe_grouped_noalloc(*args, 0, 2048, 1408, 64, 6, 64, BF16, None, None, None) == OK
+    assert L.qmoe_grouped_noalloc(*args, 64, 2048, 1408, 64, 7, 32, BF16, None, None, None) == GROUP

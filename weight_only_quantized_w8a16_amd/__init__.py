@@ -22,6 +22,7 @@ __all__ = [
     "unrepack_w8_kn", "quantize_w4", "dequant_w4", "dequant_w8", "gemm_w4a16", "gemm_w8a16",
     "moe_grouped", "moe_workspace_size", "gemm_workspace_size", "dtype_code", "gemm_w8a8",
     "w8a8_workspace_size", "embed_w4", "embed_w8", "read_probe", "set_override", "clear_override",
+    "moe_grouped_noalloc",
 ]
 
 _CODES = {torch.bfloat16: QG_BF16, torch.float16: QG_FP16, torch.float32: QG_FP32}
@@ -566,4 +567,45 @@ def moe_grouped(x: torch.Tensor, logits: torch.Tensor, w1_tiled: torch.Tensor, s
             _stream(x)))
     if return_routing:
         return out, ids, wts
+    return out
+
+
+def moe_grouped_noalloc(x: torch.Tensor, logits: torch.Tensor, w1_tiled: torch.Tensor,
+                        s1: torch.Tensor, z1: torch.Tensor, w2_tiled: torch.Tensor,
+                        s2: torch.Tensor, z2: torch.Tensor, topk: int, group_size: int,
+                        out: torch.Tensor, ids: Optional[torch.Tensor] = None,
+                        wts: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """moe_grouped into caller-given `out` (and optional `ids` int32 [T, k],
+    `wts` fp32 [T, k]) on the library's device scratch: no workspace, no
+    allocation (qmoe_grouped_noalloc; at most 64 MiB of workspace needed)."""
+    f = "qmoe_grouped_noalloc"
+    _need(x.dtype in _ACT and x.dim() == 2, f, _DTYPE, "x must be a 2-D bf16 or fp16 tensor [T, H]")
+    T, H = x.shape
+    _need(logits.dtype == torch.float32 and logits.dim() == 2 and logits.shape[0] == T, f, _SHAPE,
+          f"logits must be fp32 [{T}, E]")
+    E = logits.shape[1]
+    _need(w1_tiled.dtype == torch.uint8 and w1_tiled.dim() == 3, f, _DTYPE, "w1_tiled must be uint8 [E, 2I, H/2]")
+    I2 = w1_tiled.shape[1]
+    _need(_shape(w1_tiled) == (E, I2, H // 2) and I2 % 2 == 0, f, _SHAPE, "w1_tiled must be [E, 2I, H/2]")
+    _need(w2_tiled.dtype == torch.uint8 and _shape(w2_tiled) == (E, H, I2 // 4), f, _SHAPE,
+          "w2_tiled must be uint8 [E, H, I/2]")
+    for t, nm in ((s1, "s1"), (z1, "z1")):
+        _check_groups(f, nm, t, x.dtype, I2, H, group_size, lead=(E,))
+    for t, nm in ((s2, "s2"), (z2, "z2")):
+        _check_groups(f, nm, t, x.dtype, H, I2 // 2, group_size, lead=(E,))
+    _need(out.dtype == x.dtype and _shape(out) == (T, H), f, _SHAPE, f"out must be [{T}, {H}]")
+    if ids is not None:
+        _need(ids.dtype == torch.int32 and _shape(ids) == (T, topk), f, _SHAPE, f"ids must be int32 [{T}, {topk}]")
+    if wts is not None:
+        _need(wts.dtype == torch.float32 and _shape(wts) == (T, topk), f, _SHAPE,
+              f"wts must be fp32 [{T}, {topk}]")
+    for t, nm in ((x, "x"), (logits, "logits"), (w1_tiled, "w1_tiled"), (s1, "s1"), (z1, "z1"),
+                  (w2_tiled, "w2_tiled"), (s2, "s2"), (z2, "z2"), (out, "out"), (ids, "ids"),
+                  (wts, "wts")):
+        if t is not None:
+            _dev(t, nm)
+    check(f, lib().qmoe_grouped_noalloc(
+        _ptr(x), _ptr(logits), _ptr(w1_tiled), _ptr(s1), _ptr(z1), _ptr(w2_tiled), _ptr(s2),
+        _ptr(z2), _ptr(out), T, H, I2 // 2, E, topk, group_size, dtype_code(x.dtype), _ptr(ids),
+        _ptr(wts), _stream(x)))
     return out

@@ -55,6 +55,8 @@ SIGNATURES = {
     "qmoe_workspace_size": (_SZ, [_INT, _INT, _INT, _INT, _INT]),
     "qmoe_grouped": (_ST, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _INT, _INT, _INT, _INT, _INT, _INT,
                            _INT, _P, _P, _P, _SZ, _P]),
+    "qmoe_grouped_noalloc": (_ST, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _INT, _INT, _INT, _INT, _INT,
+                                   _INT, _INT, _P, _P, _P]),
     "qmoe_grouped_ex": (_ST, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _INT, _INT, _INT,
                               _INT, _INT, _INT, _INT, _INT, _P, _P, _P, _SZ, _P]),
 }

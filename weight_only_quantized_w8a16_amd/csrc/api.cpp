@@ -331,7 +331,7 @@ static qg_status moe_call(const void *x, const float *logits, const float *sel_l
                           const void *z2, const void *b2, void *out, int tokens, int hidden,
                           int inter, int experts, int topk, int group, int norm, qg_dtype act,
                           int32_t *ids_out, float *w_out, void *workspace, size_t ws_bytes,
-                          void *stream) {
+                          void *stream, bool noalloc = false) {
   if (tokens < 0 || hidden <= 0 || inter <= 0 || experts <= 0 || topk <= 0 || topk > experts)
     return QG_ERR_SHAPE;
   if (tokens == 0) return QG_OK;        // nothing to compute; pointers unused
@@ -349,8 +349,12 @@ static qg_status moe_call(const void *x, const float *logits, const float *sel_l
       (b2 && !aligned(b2, 16)))
     return QG_ERR_ALIGN;
   const size_t need = qg::moe_workspace_bytes(tokens, hidden, inter, experts, topk);
-  if (!workspace || ws_bytes < need) return QG_ERR_WORKSPACE;
-  if (!aligned(workspace, 256)) return QG_ERR_ALIGN;
+  if (noalloc) {
+    if (need > qg::kMoeScratchBytes) return QG_ERR_WORKSPACE;
+  } else {
+    if (!workspace || ws_bytes < need) return QG_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return QG_ERR_ALIGN;
+  }
   qg::MoeArgs a{static_cast<const uint16_t *>(x), logits, w1,
                 static_cast<const uint16_t *>(s1), static_cast<const uint16_t *>(z1), w2,
                 static_cast<const uint16_t *>(s2), static_cast<const uint16_t *>(z2),
@@ -361,6 +365,7 @@ static qg_status moe_call(const void *x, const float *logits, const float *sel_l
   a.b1 = static_cast<const uint16_t *>(b1);
   a.b2 = static_cast<const uint16_t *>(b2);
   a.renorm = norm == QG_MOE_RENORMALIZE ? 1 : 0;
+  if (noalloc) return hip_status(qg::launch_moe_noalloc(a, as_stream(stream)));
   return hip_status(qg::launch_moe(a, as_stream(stream)));
 }
 
@@ -372,6 +377,16 @@ qg_status qmoe_grouped(const void *x, const float *logits, const uint8_t *w1, co
   return moe_call(x, logits, nullptr, nullptr, w1, s1, z1, nullptr, w2, s2, z2, nullptr, out,
                   tokens, hidden, inter, experts, topk, group, QG_MOE_RENORMALIZE, act, ids_out,
                   w_out, workspace, ws_bytes, stream);
+}
+
+qg_status qmoe_grouped_noalloc(const void *x, const float *logits, const uint8_t *w1,
+                               const void *s1, const void *z1, const uint8_t *w2, const void *s2,
+                               const void *z2, void *out, int tokens, int hidden, int inter,
+                               int experts, int topk, int group, qg_dtype act, int32_t *ids_out,
+                               float *w_out, void *stream) {
+  return moe_call(x, logits, nullptr, nullptr, w1, s1, z1, nullptr, w2, s2, z2, nullptr, out,
+                  tokens, hidden, inter, experts, topk, group, QG_MOE_RENORMALIZE, act, ids_out,
+                  w_out, nullptr, 0, stream, true);
 }
 
 qg_status qmoe_grouped_ex(const void *x, const float *logits, const float *sel_logits,

@@ -23,11 +23,47 @@
 // (route gives them no expert; plan and combine skip their slots), the fc1
 // expert biases (fc1 epilogue, before the activation) and the fc2 ones
 // (combine), and the normalization mode (route).
+#include <mutex>
+
 #include "qg_launch.hpp"
 #include "tile_big.hpp"
 #include "tile_gemm.hpp"
 
 namespace qg {
+
+// Device scratch of the allocation-free MoE entry point
+// (qmoe_grouped_noalloc): the workspace of one call, held by every device the
+// library runs on until the process ends.  Host code never passes `scratch`
+// itself (on the host that name is a stand-in, not a device address): it
+// passes the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) char scratch[kMoeScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Address of the current device's copy of `scratch`, looked up once per
+// device (with that device current) and kept.
+hipError_t scratch_address(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
 
 namespace {
 
@@ -408,6 +444,16 @@ hipError_t run_moe(const MoeArgs &a, hipStream_t s) {
 
 hipError_t launch_moe(const MoeArgs &a, hipStream_t s) {
   return a.act == kBF16 ? run_moe<kBF16>(a, s) : run_moe<kFP16>(a, s);
+}
+
+// The same launches with the device scratch as the workspace.  Every stage
+// writes what a later stage reads (routing maps, tile count and list, fc1
+// and fc2 rows) before reading it, so nothing needs clearing between calls.
+hipError_t launch_moe_noalloc(MoeArgs a, hipStream_t s) {
+  void *ws = nullptr;
+  if (hipError_t e = scratch_address(&ws); e != hipSuccess) return e;
+  a.ws = ws;
+  return launch_moe(a, s);
 }
 
 }  // namespace qg

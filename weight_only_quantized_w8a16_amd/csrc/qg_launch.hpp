@@ -108,6 +108,10 @@ struct MoeArgs {
 };
 size_t moe_workspace_bytes(int T, int H, int I, int E, int topk);
 hipError_t launch_moe(const MoeArgs &a, hipStream_t s);
+// Allocation-free MoE: the workspace is the library's device scratch of
+// kMoeScratchBytes (moe.hip); callers check the problem fits first.
+constexpr size_t kMoeScratchBytes = size_t(64) << 20;
+hipError_t launch_moe_noalloc(MoeArgs a, hipStream_t s);
 
 }  // namespace qg
 
