@@ -299,7 +299,12 @@ __global__ __launch_bounds__(decode_threads<BPW>()) void k_decode_w8(const uint1
 // Register budget for five resident waves per SIMD (five workgroups per CU):
 // measured on MI355X at M = 1, N = 131072, K = 2048, 27.2-27.5 us against
 // 27.5-27.6 with four and 27.9-28.3 with the compiler's default budget (three
-// waves); six (28.9) and eight (31.6, with spills) were slower.
+// waves); six (28.9) and eight (31.6, with spills) were slower.  The first
+// item's loads are issued before the activation staging, whose group sums
+// are computed by all threads (a serial 64-value loop per group had every
+// workgroup wait about 4k cycles before its first weight load): 2.5 % faster
+// at M = 1, N = 131072 (27.6 against 28.3 us, same box); loading the next
+// item before the current item's math (two items live) measured 5 % slower.
 template <int ACT, int G, int SEG, int R>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void k_decode_w4_stream(const uint16_t *__restrict__ A,
                                                           const u32x4 *__restrict__ Bt,
@@ -320,26 +325,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void k
   const int Mr = M < 16 ? M : 16;
   float *sS = reinterpret_cast<float *>(lds + Mr * arow);   // [ngroups][16]
 
-  // Activation rows -> LDS (16-byte chunks), then S[g][m] = sum of a group.
-  for (int c = threadIdx.x; c < Mr * (K >> 3); c += blockDim.x) {
-    const int m = c / (K >> 3), k8 = c % (K >> 3);
-    *reinterpret_cast<u32x4 *>(lds + m * arow + k8 * 16) =
-        *reinterpret_cast<const u32x4 *>(A + static_cast<size_t>(m) * K + k8 * 8);
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < ngroups * 16; e += blockDim.x) {
-    const int g = e >> 4, m = e & 15;
-    float acc = 0.f;
-    if (m < Mr) {
-      const uint16_t *row = reinterpret_cast<const uint16_t *>(lds + m * arow) + g * G;
-      for (int i = 0; i < G; ++i) acc += bits_to_f32<ACT>(row[i]);
-    }
-    sS[e] = acc;
-  }
-  __syncthreads();
-
-  const bool active = nl < Mr;           // this lane's activation row exists
-  const char *arow_p = lds + (active ? nl : 0) * arow + 16 * j;
   const int total_waves = gridDim.x * (blockDim.x >> 6);
   const int nseg = nb / SEG;
   static_assert(R == 1 || R == 2, "streaming decode serves M <= 2");
@@ -374,11 +359,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void k
     }
   };
 
-  for (int tile = blockIdx.x * (blockDim.x >> 6) + wave; tile < ntiles; tile += total_waves) {
+  // The first item's loads go out before the activations are staged, so
+  // every wave has weights in flight from its first instructions on.
+  int tile = blockIdx.x * (blockDim.x >> 6) + wave;
+  Item cur;
+  if (tile < ntiles) fetch(tile, 0, cur);
+
+  // Activation rows -> LDS (16-byte chunks); S[g][m] = sum of group g of row
+  // m, summed from the same chunks: each thread adds its 8 values and the
+  // G / 8 consecutive lanes of a group combine by shuffles (a group never
+  // straddles rows, and every pass runs on all threads, so the lanes a
+  // shuffle reads are always active).  Rows m >= M read as zeros.
+  constexpr int LPG = G / 8;             // lanes per group
+  for (int e = threadIdx.x; e < ngroups * 16; e += blockDim.x)
+    if ((e & 15) >= Mr) sS[e] = 0.f;
+  for (int base = 0; base < Mr * (K >> 3); base += blockDim.x) {
+    const int c = base + static_cast<int>(threadIdx.x);
+    const bool ok = c < Mr * (K >> 3);
+    const int m = ok ? c / (K >> 3) : 0, k8 = ok ? c % (K >> 3) : 0;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (ok) {
+      v = *reinterpret_cast<const u32x4 *>(A + static_cast<size_t>(m) * K + k8 * 8);
+      *reinterpret_cast<u32x4 *>(lds + m * arow + k8 * 16) = v;
+    }
+    float part = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      part += bits_to_f32<ACT>(static_cast<uint16_t>(v[q] & 0xFFFFu));
+      part += bits_to_f32<ACT>(static_cast<uint16_t>(v[q] >> 16));
+    }
+#pragma unroll
+    for (int off = 1; off < LPG; off <<= 1) part += __shfl_xor(part, off);
+    if (ok && (k8 % LPG) == 0) sS[(k8 / LPG) * 16 + m] = part;
+  }
+  __syncthreads();
+
+  const bool active = nl < Mr;           // this lane's activation row exists
+  const char *arow_p = lds + (active ? nl : 0) * arow + 16 * j;
+
+  // One item is live at a time: after an item's math, the loads of the next
+  // one (the next segment of this tile, else the first of the wave's next
+  // tile) are issued.
+  for (; tile < ntiles; tile += total_waves) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int seg = 0; seg < nseg; ++seg) {
-      Item cur;
-      fetch(tile, seg, cur);
       const int kb0 = seg * SEG;
 #pragma unroll
       for (int b = 0; b < SEG; ++b)
@@ -405,6 +429,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void k
             acc[1] += sc * d[1] + zc * sg[1];
           }
         }
+      if (seg + 1 < nseg) fetch(tile, seg + 1, cur);
+      else if (tile + total_waves < ntiles) fetch(tile + total_waves, 0, cur);
     }
     const int n = tile * 16 + nl;
 #pragma unroll
