@@ -9,7 +9,8 @@ is one GEMV per shape; `value` = algorithmic bytes of a step / step time.
 Secondary sections on the same JSON line:
   sweep    every (M, N) of the decode workload, M in {1, 2, 4, 8};
   prefill  W4A16 M=512, K=2048, N in {3072, 13312, 131072}, g in {64, 128},
-           fp16 bias: TFLOP/s against the dense bf16 matrix-core peak;
+           fp16 bias: TFLOP/s against the dense bf16 matrix-core peak (the
+           aggregate over the M=512 shapes); the same shapes at M=2048 beside it;
   moe      grouped W4A16 MoE, 2048 tokens, hidden 2048, inter 1408,
            64 experts, top-6;
   w8       W8A16 at K=3584, N in {3584, 18944}, M from 1 to 4096, per-channel
@@ -23,7 +24,13 @@ Secondary sections on the same JSON line:
            [N, 2048], N in {13312, 131072}, group 64 (GB/s against HBM);
   roofline the decode kernel of the N=131072 GEMV: algorithmic bytes per
            launch / its mean launch time (HIP events on the launch stream);
-  cpu_baseline  the CPU oracle on a bounded sample of the decode step.
+  cpu_baseline  the CPU oracle (its fp32-accumulating GEMM) on bounded
+           samples: whole decode steps on every host thread (`value`), one
+           thread, and one prefill, W8A16 and MoE shape each, with the host's
+           CPU model, sockets and the thread count the oracle actually ran.
+
+`python bench.py --trace-summary <kernel_trace.csv>` prints per-dispatch
+statistics (median, p10, p90) of a rocprofv3 kernel trace of this script.
 
 Inputs are seeded synthetic data generated on the host and copied to HBM
 before timing.  Memory-bound shapes rotate over enough identical weight
@@ -52,6 +59,7 @@ DECODE_K, DECODE_G = 2048, 64
 DECODE_N = [2048, 3072, 13312, 131072]
 SWEEP = [(m, n) for m in (1, 2, 4, 8) for n in (2048, 3072, 13312)] + [(1, 131072)]
 PREFILL = [(512, n, g) for g in (64, 128) for n in (3072, 13312, 131072)]
+PREFILL_2048 = [(2048, n, g) for g in (64, 128) for n in (3072, 13312, 131072)]
 
 
 def log(*a):
@@ -162,6 +170,145 @@ def kernel_only(args, torch, qg, si):
     torch.cuda.synchronize()
     log(f"kernel-only: {args.steps} GEMVs (M=1, N={n}), {args.steps} prefill GEMMs "
         f"(M={pm}, N={pn}, g={pg}) and 3 copies of 512 MiB")
+
+
+def trace_summary(path, top=60):
+    """Per-dispatch statistics from a rocprofv3 kernel trace (CSV from
+    `rocprofv3 --kernel-trace --output-format csv`): for each library kernel
+    and launch shape (grid and workgroup size) the dispatch count and the
+    median, 10th and 90th percentile, mean, min and max duration in us, as a
+    markdown table, sorted by total time."""
+    import csv
+    import statistics
+    groups = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            name = row["Kernel_Name"]
+            if not name.lstrip("void ").startswith("qg::"):
+                continue
+            key = (name, int(row["Grid_Size_X"]), int(row["Workgroup_Size_X"]))
+            us = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
+            groups.setdefault(key, []).append(us)
+
+    def pct(xs, q):
+        xs = sorted(xs)
+        i = q * (len(xs) - 1)
+        lo = int(math.floor(i))
+        hi = min(lo + 1, len(xs) - 1)
+        return xs[lo] + (xs[hi] - xs[lo]) * (i - lo)
+    rows = sorted(groups.items(), key=lambda kv: -sum(kv[1]))[:top]
+    out = ["| dispatches | median us | p10 us | p90 us | mean us | min us | max us | grid threads | wg | kernel |",
+           "|---:|---:|---:|---:|---:|---:|---:|---:|---:|---|"]
+    for (name, grid, wg), xs in rows:
+        short = name if len(name) <= 110 else name[:107] + "..."
+        out.append(f"| {len(xs)} | {statistics.median(xs):.2f} | {pct(xs, 0.1):.2f} | {pct(xs, 0.9):.2f} | "
+                   f"{statistics.fmean(xs):.2f} | {min(xs):.2f} | {max(xs):.2f} | {grid} | {wg} | `{short}` |")
+    return "\n".join(out)
+
+
+def host_cpu():
+    """Model name, sockets and logical CPUs of this host (from /proc/cpuinfo)
+    and the CPUs this process may run on."""
+    model, sockets, logical = "unknown", set(), 0
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                k, _, v = line.partition(":")
+                k, v = k.strip(), v.strip()
+                if k == "model name" and model == "unknown":
+                    model = v
+                elif k == "physical id":
+                    sockets.add(v)
+                elif k == "processor":
+                    logical += 1
+    except OSError:
+        pass
+    return {"model": model, "sockets": max(1, len(sockets)), "logical_cpus": logical,
+            "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def cpu_baseline(args, si, step_bytes):
+    """The oracle (oracle/qref.c, as written) on bounded samples of the
+    workloads, on this host's cores.  The timed GEMMs are the oracle's
+    fp32-accumulating variant; the thread count is set inside the oracle
+    library (omp_set_num_threads) and `cores` is the team size a parallel
+    region of it actually got."""
+    import oracle
+    oracle.lib()
+    host = host_cpu()
+    nthr = host["affinity_cpus"]
+    oracle.set_threads(nthr)
+    team = oracle.team_size()
+
+    def rate(fn, min_s):
+        fn()
+        n, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            n += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_s:
+                return n, dt
+
+    # headline: whole M=1 decode steps (every N), GB/s of algorithmic bytes
+    probs = []
+    for n in DECODE_N:
+        packed, sc, ze, _ = si.w4_weights(n, DECODE_K, DECODE_G,
+                                          si.seed_of("cfg1", "w", n, DECODE_K, DECODE_G))
+        probs.append((packed, sc, ze))
+    A1 = si.activations(1, DECODE_K, si.seed_of("cfg1", "a", 1, DECODE_K))
+    def step():
+        for (packed, sc, ze) in probs:
+            oracle.gemm_w4_f32acc(A1, packed, sc, ze, DECODE_G)
+    passes, dt = rate(step, args.cpu_seconds)
+    cpu = {"value": round(passes * step_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": team,
+           "kind": "oracle",
+           "sample": f"{passes} full M=1 decode steps (N={DECODE_N}, K=2048, g=64) in {dt:.1f} s, "
+                     f"fp32-accumulating oracle GEMM, {team} OpenMP threads",
+           "host": host}
+
+    # one thread: the two smallest decode GEMVs, and the tiny config
+    oracle.set_threads(1)
+    team1 = oracle.team_size()
+    small = [(2048, probs[0]), (3072, probs[1])]
+    b_small = sum(w4_bytes(1, n, DECODE_K, DECODE_G) for n, _ in small)
+    passes1, dt1 = rate(lambda: [oracle.gemm_w4_f32acc(A1, *pp, DECODE_G) for _, pp in small], 3.0)
+    p0 = si.w4_problem(4, 128, 256, 64, tag="cfg0")
+    n0, dt0 = rate(lambda: oracle.gemm_w4_f32acc(p0.A, p0.packed, p0.scale, p0.zero, 64), 0.5)
+    cpu["single_thread"] = {"value": round(passes1 * b_small / dt1 / 1e9, 4), "unit": "GB/s",
+                            "cores": team1,
+                            "sample": f"M=1 GEMVs N in {{2048, 3072}}, K=2048, g=64, {dt1:.1f} s"}
+    cpu["tiny_single_thread"] = {"value": round(n0 * 2 * 4 * 128 * 256 / dt0 / 1e9, 4),
+                                 "unit": "GFLOP/s", "cores": team1,
+                                 "sample": "W4A16 M=4, K=256, N=128, g=64 (the tiny config)"}
+    oracle.set_threads(nthr)
+
+    # beside the GPU's other sections, on all threads
+    p3 = si.w4_problem(512, 3072, 2048, 64, tag="cfg3", bias_dtype=si.FP16)
+    n3, dt3 = rate(lambda: oracle.gemm_w4_f32acc(p3.A, p3.packed, p3.scale, p3.zero, 64, si.BF16,
+                                            p3.bias, si.FP16), 1.0)
+    p2 = si.w8_problem(128, 3584, 3584, -1, tag="cfg2")
+    n2, dt2 = rate(lambda: oracle.gemm_w8_f32acc(p2.A, p2.codes, p2.scale, -1, si.FP16), 1.0)
+    pm = si.moe_problem(2048, 2048, 1408, 64, 6, 64, tag="cfg4")
+    import numpy as np
+    toks = np.arange(16)
+    t0 = time.perf_counter()
+    oracle.moe(pm.x, pm.logits, pm.w1, pm.s1, pm.z1, pm.w2, pm.s2, pm.z2, 6, 64, tokens=toks)
+    dtm = time.perf_counter() - t0
+    moe_flop = 2.0 * len(toks) * 6 * (2 * 1408 * 2048 + 2048 * 1408)
+    cpu["configs"] = {
+        "prefill_M512_N3072_g64": {"value": round(n3 * 2.0 * 512 * 3072 * 2048 / dt3 / 1e9, 2),
+                                   "unit": "GFLOP/s", "cores": team,
+                                   "sample": f"{n3} GEMMs in {dt3:.1f} s, fp32 accumulation"},
+        "w8a16_M128_N3584_K3584": {"value": round(n2 * 2.0 * 128 * 3584 * 3584 / dt2 / 1e9, 2),
+                                   "unit": "GFLOP/s", "cores": team,
+                                   "sample": f"{n2} GEMMs in {dt2:.1f} s, fp32 accumulation"},
+        "moe_T2048_16_tokens": {"value": round(moe_flop / dtm / 1e9, 2), "unit": "GFLOP/s",
+                                "cores": team,
+                                "sample": f"16 of the 2048 tokens (routing of all) in {dtm:.1f} s, "
+                                          "fp64 oracle, expert weights dequantized once"},
+    }
+    return cpu
 
 
 def run(args):
@@ -283,32 +430,36 @@ def run(args):
     # ---- prefill M=512 ------------------------------------------------------------
     prefill = None
     if not args.no_prefill:
-        A = torch.from_numpy(si.activations(512, 2048, si.seed_of("cfg3", "a", 512, 2048))
-                             .view("int16")).view(torch.bfloat16).to(dev)
+        acts_p = {m: torch.from_numpy(si.activations(m, 2048, si.seed_of("cfg3", "a", m, 2048))
+                                      .view("int16")).view(torch.bfloat16).to(dev) for m in (512, 2048)}
         shapes = {}
         tot_flop, tot_ms = 0.0, 0.0
-        for (m, n, g) in PREFILL:
+        for (m, n, g) in PREFILL + ([] if args.quick else PREFILL_2048):
+            A = acts_p[m]
             w = Weights(torch, qg, si, n, 2048, g, "cfg3", 2, bias=True)
             C = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
             for i in range(3):
                 B, S, Z = w[i]
                 qg.gemm_w4a16(A, B, S, Z, w.bias, g, out=C)
-            reps = max(10, K // 2)
+            reps = max(10, K // 2) if m == 512 else max(5, K // 10)
 
-            def call(i, w=w, C=C, g=g):
+            def call(i, w=w, C=C, g=g, A=A):
                 B, S, Z = w[i]
                 qg.gemm_w4a16(A, B, S, Z, w.bias, g, out=C)
             ms = timed(call, reps, warm=reps) / reps
             flop = 2.0 * m * n * 2048
-            tot_flop += flop
-            tot_ms += ms
-            shapes[f"N{n}_g{g}"] = {"us": round(ms * 1e3, 1),
-                                    "TFLOPS": round(flop / (ms * 1e-3) / 1e12, 1),
-                                    "frac": round(flop / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 3)}
+            if m == 512:
+                tot_flop += flop
+                tot_ms += ms
+            key = f"N{n}_g{g}" if m == 512 else f"M{m}_N{n}_g{g}"
+            shapes[key] = {"us": round(ms * 1e3, 1),
+                           "TFLOPS": round(flop / (ms * 1e-3) / 1e12, 1),
+                           "frac": round(flop / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 3)}
             del w, C
         tf = tot_flop / (tot_ms * 1e-3) / 1e12
         pm, pn, pg = PREFILL_TRAFFIC_SHAPE
-        prefill = {"metric": "prefill TFLOPS at M=512 (W4A16, K=2048, fp16 bias)",
+        prefill = {"metric": "prefill TFLOPS at M=512 (W4A16, K=2048, fp16 bias); M=2048 shapes "
+                             "reported beside it",
                    "value": round(tf, 1), "unit": "TFLOP/s",
                    "roofline": {"bound": "mfma", "achieved": round(tf, 1),
                                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -581,47 +732,7 @@ def run(args):
     # ---- CPU oracle baseline -----------------------------------------------------
     cpu = None
     if not args.no_cpu:
-        import oracle
-        oracle.lib()
-        probs = []
-        for n in DECODE_N:
-            packed, s, z, _ = si.w4_weights(n, DECODE_K, DECODE_G,
-                                            si.seed_of("cfg1", "w", n, DECODE_K, DECODE_G))
-            probs.append((n, packed, s, z))
-        A1 = si.activations(1, DECODE_K, si.seed_of("cfg1", "a", 1, DECODE_K))
-        passes, t_cpu = 0, 0.0
-        while t_cpu < args.cpu_seconds or passes == 0:
-            c0 = time.perf_counter()
-            for (n, packed, s, z) in probs:
-                oracle.gemm_w4(A1, packed, s, z, DECODE_G)
-            t_cpu += time.perf_counter() - c0
-            passes += 1
-        cpu_val = passes * step_bytes / t_cpu / 1e9
-        cpu = {"value": round(cpu_val, 2), "unit": "GB/s", "cores": oracle.threads(),
-               "kind": "oracle",
-               "sample": f"{passes} full passes of the M=1 decode step "
-                         f"(N={DECODE_N}, K=2048, g=64) in {t_cpu:.1f}s, fp64 accumulation"}
-        # The same oracle on one thread (a child process with OMP_NUM_THREADS=1,
-        # about three seconds of the two smallest GEMVs of the step).
-        import subprocess
-        code = ("import sys, time; sys.path.insert(0, %r); import oracle, synth_inputs as si\n"
-                "A = si.activations(1, 2048, si.seed_of('cfg1', 'a', 1, 2048))\n"
-                "ps = [si.w4_weights(n, 2048, 64, si.seed_of('cfg1', 'w', n, 2048, 64))[:3] "
-                "for n in (2048, 3072)]\n"
-                "b = sum(n * 1024 + 4 * n * 32 + 4096 + 2 * n for n in (2048, 3072))\n"
-                "oracle.gemm_w4(A, *ps[0], 64); t0 = time.perf_counter(); k = 0\n"
-                "while time.perf_counter() - t0 < 3.0:\n"
-                "    [oracle.gemm_w4(A, *p, 64) for p in ps]; k += 1\n"
-                "print(k * b / (time.perf_counter() - t0) / 1e9)\n") % ROOT
-        try:
-            env = dict(os.environ, OMP_NUM_THREADS="1")
-            outp = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True,
-                                  text=True, timeout=120)
-            cpu["single_thread"] = {"value": round(float(outp.stdout.strip().splitlines()[-1]), 3),
-                                    "unit": "GB/s", "cores": 1,
-                                    "sample": "M=1 GEMVs N in {2048, 3072}, K=2048, g=64, ~3 s"}
-        except Exception as exc:   # report, do not fail the benchmark over it
-            cpu["single_thread"] = {"error": str(exc)[:200]}
+        cpu = cpu_baseline(args, si, step_bytes)
         log(f"cpu baseline: {cpu}")
 
     result = {
@@ -674,7 +785,12 @@ def main():
     ap.add_argument("--kernel-only", action="store_true",
                     help="run only the N=131072 GEMV (--steps times) and a calibration copy; "
                          "for profiler counter runs; prints no result line")
+    ap.add_argument("--trace-summary", metavar="CSV",
+                    help="print per-dispatch statistics of a rocprofv3 kernel trace and exit")
     args = ap.parse_args()
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only; there is no multi-GPU path to run "

@@ -2,7 +2,8 @@
 // measured against.  Each thread reads 16-byte pieces with streaming
 // (nontemporal) loads; in iteration i workgroup b reads piece
 // (i * gridDim + b) * blockDim + thread, so at every moment the grid sweeps one
-// contiguous window of the buffer.  The pieces are XOR-folded and each
+// contiguous window of the buffer (with the one-pass grid below: two windows,
+// the grid's first and second halves of the buffer).  The pieces are XOR-folded and each
 // workgroup writes one 32-bit word, so the loads cannot be dropped.
 #include "qg_common.hpp"
 #include "qg_launch.hpp"
@@ -10,13 +11,18 @@
 namespace qg {
 
 namespace {
-// Measured on MI355X (151 MB / 15.4 MB / 2.4 MB, rotated over 1 GiB): 256
-// threads, up to 4096 workgroups, two pieces in flight per thread read
-// fastest at the small sizes and within 1 % of the best at 151 MB, against
-// 512 x 1024 x 4, 256 x 2048 x 4, 256 x 1024 x 8, 1024 x 256 x 8 and
-// 256 x 512 x 16.
-constexpr int kProbeThreads = 256;
-constexpr unsigned kProbeMaxBlocks = 4096;
+// One pass: enough workgroups that every thread reads exactly kDepth pieces
+// (no loop), so the dispatcher keeps replacing finished workgroups with new
+// ones and the grid sweeps the buffer front to back.  Measured on MI355X
+// (HIP events over back-to-back launches, buffers rotated over 1 GiB) among
+// grid-stride, workgroup-chunk and wave-chunk orders with 256 to 1024
+// threads, 1 to 8 pieces in flight, 1024 to 8192 or one-pass grids, plain
+// and nontemporal loads: 512 threads x 2 pieces, one pass, nontemporal read
+// 151 MB in 22.9 us (6.6 TB/s) and 15.4 MB in 4.5 us, the fastest at both
+// sizes; grids capped at 4096 workgroups looping over the buffer read 151 MB
+// in 24-26 us, and plain loads were 10-20 % slower than nontemporal ones.
+constexpr int kProbeThreads = 512;
+constexpr unsigned long long kProbeMaxBlocks = 1ull << 22;
 constexpr int kDepth = 2;
 }  // namespace
 
