@@ -138,38 +138,124 @@ def gpu_lead(torch, ms=20.0):
         pass
 
 
+KERNEL_LEGS = ("decode", "prefill", "copy", "decode_small", "w8", "w8a8", "moe")
+
+
 def kernel_only(args, torch, qg, si):
-    """Only the N=131072 M=1 GEMV, `--steps` times, the M=512 N=131072 g=64
-    prefill GEMM (fp16 bias) `--steps` times, then a plain copy kernel over
-    512 MiB three times (torch's elementwise negation: reads 512 MiB, writes
-    512 MiB, in full cache lines): the workload for rocprofv3 counter runs, the
-    copy of known size calibrating FETCH_SIZE / WRITE_SIZE."""
+    """Only the chosen legs, each `--steps` times, for rocprofv3 counter runs:
+    decode -- the N=131072 M=1 GEMV; prefill -- the M=512 N=131072 g=64 GEMM
+    (fp16 bias); copy -- a plain copy kernel over 512 MiB three times (torch's
+    elementwise negation: reads 512 MiB, writes 512 MiB, in full cache lines),
+    calibrating FETCH_SIZE / WRITE_SIZE; decode_small -- the M=1 GEMVs at
+    N=2048, 3072, 13312; w8 -- W8A16 K=3584 N=18944 at M=1 and M=4096; w8a8 --
+    W8A8 K=3584 N=18944 at M=1 and M=4096; moe -- the 2048-token MoE."""
     dev = "cuda"
-    n = 131072
-    w = Weights(torch, qg, si, n, DECODE_K, DECODE_G, "cfg1", copies_for(w4_bytes(1, n, DECODE_K, DECODE_G)))
-    A = torch.from_numpy(si.activations(1, DECODE_K, si.seed_of("cfg1", "a", 1, DECODE_K))
-                         .view("int16")).view(torch.bfloat16).to(dev)
-    C = torch.empty((1, n), dtype=torch.bfloat16, device=dev)
-    for i in range(args.steps):
-        B, S, Z = w[i]
-        qg.gemm_w4a16(A, B, S, Z, None, DECODE_G, out=C)
-    del w, C
-    pm, pn, pg = PREFILL_TRAFFIC_SHAPE
-    wp = Weights(torch, qg, si, pn, 2048, pg, "cfg3", 2, bias=True)
-    Ap = torch.from_numpy(si.activations(pm, 2048, si.seed_of("cfg3", "a", pm, 2048))
-                          .view("int16")).view(torch.bfloat16).to(dev)
-    Cp = torch.empty((pm, pn), dtype=torch.bfloat16, device=dev)
-    for i in range(args.steps):
-        B, S, Z = wp[i]
-        qg.gemm_w4a16(Ap, B, S, Z, wp.bias, pg, out=Cp)
-    del wp, Cp
-    src = torch.ones(128 << 20, dtype=torch.float32, device=dev)
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        torch.neg(src, out=dst)
+    legs = args.kernel_only.split(",")
+    bad = [x for x in legs if x not in KERNEL_LEGS]
+    if bad:
+        raise SystemExit(f"unknown --kernel-only legs {bad}; choose from {KERNEL_LEGS}")
+
+    def act(m, k, tag, dt=torch.bfloat16, code=None):
+        bits = si.activations(m, k, si.seed_of(tag, "a", m, k), code if code else si.BF16)
+        return torch.from_numpy(bits.view("int16")).view(dt).to(dev)
+    if "decode" in legs:
+        n = 131072
+        w = Weights(torch, qg, si, n, DECODE_K, DECODE_G, "cfg1",
+                    copies_for(w4_bytes(1, n, DECODE_K, DECODE_G)))
+        A = act(1, DECODE_K, "cfg1")
+        C = torch.empty((1, n), dtype=torch.bfloat16, device=dev)
+        for i in range(args.steps):
+            B, S, Z = w[i]
+            qg.gemm_w4a16(A, B, S, Z, None, DECODE_G, out=C)
+        del w, C
+    if "prefill" in legs:
+        pm, pn, pg = PREFILL_TRAFFIC_SHAPE
+        wp = Weights(torch, qg, si, pn, 2048, pg, "cfg3", 2, bias=True)
+        Ap = act(pm, 2048, "cfg3")
+        Cp = torch.empty((pm, pn), dtype=torch.bfloat16, device=dev)
+        for i in range(args.steps):
+            B, S, Z = wp[i]
+            qg.gemm_w4a16(Ap, B, S, Z, wp.bias, pg, out=Cp)
+        del wp, Cp
+    if "decode_small" in legs:
+        A = act(1, DECODE_K, "cfg1")
+        for n in DECODE_N[:3]:
+            w = Weights(torch, qg, si, n, DECODE_K, DECODE_G, "cfg1",
+                        copies_for(w4_bytes(1, n, DECODE_K, DECODE_G)))
+            C = torch.empty((1, n), dtype=torch.bfloat16, device=dev)
+            for i in range(args.steps):
+                B, S, Z = w[i]
+                qg.gemm_w4a16(A, B, S, Z, None, DECODE_G, out=C)
+            del w, C
+    if "w8" in legs:
+        k8, n = 3584, 18944
+        codes, sc, _ = si.w8_weights(n, k8, -1, si.seed_of("cfg2", "w", n, k8, -1))
+        B = qg.repack_w8(torch.from_numpy(codes).to(dev))
+        S = torch.from_numpy(sc.view("int16")).view(torch.float16).to(dev)
+        sets = [(B, S)] + [(B.clone(), S.clone()) for _ in range(copies_for(n * k8) - 1)]
+        for m in (1, 4096):
+            A = act(m, k8, "cfg2", torch.float16, si.FP16)
+            C = torch.empty((m, n), dtype=torch.float16, device=dev)
+            for i in range(args.steps):
+                B_, S_ = sets[i % len(sets)]
+                qg.gemm_w8a16(A, B_, S_, None, -1, out=C)
+        del sets, B
+    if "w8a8" in legs:
+        ka, n = 3584, 18944
+        for m in (1, 4096):
+            pa = si.w8a8_problem(m, n, ka, True, True, tag="w8a8-bench")
+            A, B = torch.from_numpy(pa.A).to(dev), torch.from_numpy(pa.B).to(dev)
+            row, col = torch.from_numpy(pa.alpha_row).to(dev), torch.from_numpy(pa.alpha_col).to(dev)
+            C = torch.empty((m, n), dtype=torch.float16, device=dev)
+            need = qg.w8a8_workspace_size(m, n, ka)
+            ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+            for i in range(args.steps):
+                qg.gemm_w8a8(A, B, row, col, out=C, workspace=ws)
+    if "moe" in legs:
+        T, H, I, E, TK, G = 2048, 2048, 1408, 64, 6, 64
+        p = si.moe_problem(T, H, I, E, TK, G, tag="cfg4")
+
+        def up16(a):
+            return torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)
+        w1 = torch.stack([qg.repack_w4(torch.from_numpy(p.w1[e]).to(dev)) for e in range(E)])
+        w2 = torch.stack([qg.repack_w4(torch.from_numpy(p.w2[e]).to(dev)) for e in range(E)])
+        s1, z1, s2, z2 = (up16(a) for a in (p.s1, p.z1, p.s2, p.z2))
+        x, lg = up16(p.x), torch.from_numpy(p.logits).to(dev)
+        ws = torch.empty(qg.moe_workspace_size(T, H, I, E, TK), dtype=torch.uint8, device=dev)
+        for i in range(args.steps):
+            qg.moe_grouped(x, lg, w1, s1, z1, w2, s2, z2, TK, G, workspace=ws)
+    if "copy" in legs:
+        src = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
     torch.cuda.synchronize()
-    log(f"kernel-only: {args.steps} GEMVs (M=1, N={n}), {args.steps} prefill GEMMs "
-        f"(M={pm}, N={pn}, g={pg}) and 3 copies of 512 MiB")
+    log(f"kernel-only: legs {legs}, {args.steps} calls each")
+
+
+def counter_summary(path):
+    """Per-kernel means of every counter in a rocprofv3 counter collection
+    (`rocprofv3 --pmc ... --output-format csv`, run_counter_collection.csv),
+    for the library's kernels and the calibration copy, as a markdown table."""
+    import csv
+    vals = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            name = row["Kernel_Name"]
+            if "qg::" not in name and "neg_kernel" not in name and "AUnaryFunctor" not in name:
+                continue
+            key = (name, int(row.get("Grid_Size", row.get("Grid_Size_X", 0)) or 0))
+            d = vals.setdefault(key, {})
+            d.setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+    counters = sorted({c for d in vals.values() for c in d})
+    out = ["| kernel | grid threads | dispatches | " + " | ".join(counters) + " |",
+           "|---|---:|---:|" + "---:|" * len(counters)]
+    for (name, grid), d in sorted(vals.items()):
+        n = max(len(v) for v in d.values())
+        cells = [f"{sum(d[c]) / len(d[c]):,.0f}" if c in d else "" for c in counters]
+        short = name if len(name) <= 100 else name[:97] + "..."
+        out.append(f"| `{short}` | {grid} | {n} | " + " | ".join(cells) + " |")
+    return "\n".join(out)
 
 
 def trace_summary(path, top=60):
@@ -782,14 +868,20 @@ def main():
     ap.add_argument("--no-w8", action="store_true")
     ap.add_argument("--no-w8a8", action="store_true")
     ap.add_argument("--quick", action="store_true", help="skip the M sweep and the copy ceiling")
-    ap.add_argument("--kernel-only", action="store_true",
-                    help="run only the N=131072 GEMV (--steps times) and a calibration copy; "
-                         "for profiler counter runs; prints no result line")
+    ap.add_argument("--kernel-only", metavar="LEGS", nargs="?", const="decode,prefill,copy",
+                    help="run only the comma-separated legs (" + ",".join(KERNEL_LEGS) + "; "
+                         "default decode,prefill,copy), --steps calls each, for profiler "
+                         "counter runs; prints no result line")
+    ap.add_argument("--counter-summary", metavar="CSV",
+                    help="print per-kernel counter means of a rocprofv3 counter collection and exit")
     ap.add_argument("--trace-summary", metavar="CSV",
                     help="print per-dispatch statistics of a rocprofv3 kernel trace and exit")
     args = ap.parse_args()
     if args.trace_summary:
         print(trace_summary(args.trace_summary))
+        return
+    if args.counter_summary:
+        print(counter_summary(args.counter_summary))
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
