@@ -283,16 +283,18 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
     }
   };
 
-  // ---- fragments: lane reads row (wave tile row + 32 i + lane % 32), chunk
-  // 2 ks + lane / 32, placed at that ^ ((lane / 2) % 8) (the wave tile and
-  // 32 i leave (row / 2) % 8 unchanged).  One address per ks; i and the stage
-  // are immediates.
+  // ---- fragments: the tile's 32-row blocks are dealt out to the WM wave rows
+  // in turn (block b to wave row b % WM, as its block b / WM), so a partly
+  // filled expert tile gives every wave row about the same number of filled
+  // blocks.  Lane reads row 32 (i WM + wm) + lane % 32, chunk 2 ks + lane / 32,
+  // placed at that ^ ((lane / 2) % 8) (the block offset leaves (row / 2) % 8
+  // unchanged).  One address per ks; i and the stage are immediates.
   const int khalf = lane >> 5;
   const int g = khalf ^ ((lane >> 1) & 7);
   int a_addr[4], b_addr[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    a_addr[ks] = (wm * Cfg::WTM + (lane & 31)) * 128 + (((2 * ks) ^ g) << 4);
+    a_addr[ks] = (wm * 32 + (lane & 31)) * 128 + (((2 * ks) ^ g) << 4);
     b_addr[ks] = (wn * Cfg::WTN + (lane & 31)) * 128 + (((2 * ks) ^ g) << 4);
   }
   struct Frags {
@@ -301,7 +303,7 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
   auto fread = [&](auto NAc, const char *As, const char *Bs, int ks, Frags &f) {
 #pragma unroll
     for (int i = 0; i < decltype(NAc)::value; ++i)
-      f.a[i] = *reinterpret_cast<const u32x4 *>(As + a_addr[ks] + 4096 * i);
+      f.a[i] = *reinterpret_cast<const u32x4 *>(As + a_addr[ks] + Cfg::WM * 4096 * i);
 #pragma unroll
     for (int j = 0; j < TN; ++j) f.b[j] = *reinterpret_cast<const u32x4 *>(Bs + b_addr[ks] + 4096 * j);
   };
@@ -427,8 +429,11 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
     // An expert tile is mostly partly filled: a wave skips the fragment
     // reads and matrix-core work of its 32-row blocks that hold no rows
     // (it still loads and dequantizes its share and meets every barrier).
-    const int valid = row_last - row_lo + 1 - wm * Cfg::WTM;
-    const int na = __builtin_amdgcn_readfirstlane(valid <= 0 ? 0 : min(TM, (valid + 31) >> 5));
+    // With the blocks dealt out in turn, a 192-row expert gives both wave
+    // rows three blocks (in contiguous halves: four and two).
+    const int blocks = (row_last - row_lo + 32) >> 5;      // 32-row blocks holding rows
+    const int mine = blocks > wm ? (blocks - wm + Cfg::WM - 1) / Cfg::WM : 0;
+    const int na = __builtin_amdgcn_readfirstlane(min(TM, mine));
     static_assert(TM == 4, "expert tiles: four 32-row blocks per wave");
     if (na == 4) main_loop(std::integral_constant<int, 4>{});
     else if (na == 3) main_loop(std::integral_constant<int, 3>{});
@@ -437,8 +442,8 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
     else main_loop(std::integral_constant<int, 0>{});
   }
 
-  // ---- epilogue: value v of acc[i][j] is C[row][col], row = wave tile row
-  // + 32 i + lane % 32, col = wave tile column + 32 j + 8 (v / 4) +
+  // ---- epilogue: value v of acc[i][j] is C[row][col], row = 32 (i WM + wm)
+  // + lane % 32, col = wave tile column + 32 j + 8 (v / 4) +
   // 4 (lane / 32) + v % 4.  Per i, each wave stages its 32 x 64 block in LDS
   // (8-byte pieces, 144-byte rows) and stores it as 16-byte row pieces, so
   // every store instruction writes whole 128-byte lines (nontemporal: the
@@ -450,7 +455,7 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
       float *dst = p.part + static_cast<size_t>(slice) * p.M * p.N;
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
-        const int r = row_lo + wm * Cfg::WTM + 32 * i + (lane & 31);
+        const int r = row_lo + 32 * (i * Cfg::WM + wm) + (lane & 31);
         if (r > row_last) continue;
 #pragma unroll
         for (int j = 0; j < TN; ++j)
@@ -487,7 +492,7 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
       }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      if (row_lo + wm * Cfg::WTM + 32 * i > row_last) break;   // block holds no rows
+      if (row_lo + 32 * (i * Cfg::WM + wm) > row_last) break;   // block holds no rows
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         float v[4];
@@ -503,7 +508,7 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
       for (int t = 0; t < 2; ++t) {
         const int rr = 16 * t + (lane >> 2), ch = lane & 3;
         const u32x4 val = *reinterpret_cast<const u32x4 *>(stg + rr * 80 + ch * 16);
-        const int r = row_lo + wm * Cfg::WTM + 32 * i + rr;
+        const int r = row_lo + 32 * (i * Cfg::WM + wm) + rr;
         if (r <= row_last)
           __builtin_nontemporal_store(val, reinterpret_cast<u32x4 *>(p.C + static_cast<size_t>(r) * p.N + n0 + 32 * wn + ch * 8));
       }
@@ -525,7 +530,7 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
       }
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
-    if (row_lo + wm * Cfg::WTM + 32 * i > row_last) break;   // block holds no rows
+    if (row_lo + 32 * (i * Cfg::WM + wm) > row_last) break;   // block holds no rows
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -540,7 +545,7 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
     for (int t = 0; t < 4; ++t) {
       const int rr = 8 * t + (lane >> 3), ch = lane & 7;
       const u32x4 val = *reinterpret_cast<const u32x4 *>(stg + rr * 144 + ch * 16);
-      const int r = row_lo + wm * Cfg::WTM + 32 * i + rr;
+      const int r = row_lo + 32 * (i * Cfg::WM + wm) + rr;
       if (r <= row_last)
         __builtin_nontemporal_store(val, reinterpret_cast<u32x4 *>(p.C + static_cast<size_t>(r) * p.N + n0 + wn * Cfg::WTN + ch * 8));
     }
