@@ -804,6 +804,27 @@ def run(args):
             if n:
                 floor_us += us
         ceil["read_probe"] = probe
+        # The vendor library's plain dense GEMM on the prefill and W8A16 shapes
+        # (torch.mm -> hipBLASLt; no dequantization, 16-bit weights, so four or
+        # two times the weight bytes): what a tuned dense GEMM of these shapes
+        # reaches on this chip.
+        dense = {}
+        for (m, n, k, dt) in ((512, 131072, 2048, torch.bfloat16), (2048, 131072, 2048, torch.bfloat16),
+                              (512, 13312, 2048, torch.bfloat16), (4096, 18944, 3584, torch.float16)):
+            gen = torch.Generator(device=dev)
+            gen.manual_seed(m + n)
+            Ad = torch.randn(m, k, generator=gen, device=dev).to(dt)
+            Wt = torch.randn(k, n, generator=gen, device=dev).to(dt)   # [K, N], contiguous
+            Cd = torch.empty(m, n, dtype=dt, device=dev)
+            for _ in range(3):
+                torch.mm(Ad, Wt, out=Cd)
+            reps = 10 if m * n < 1e9 else 5
+            ms = timed(lambda i: torch.mm(Ad, Wt, out=Cd), reps, warm=reps) / reps
+            tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+            dense[f"M{m}_N{n}_K{k}_{'bf16' if dt == torch.bfloat16 else 'fp16'}"] = {
+                "us": round(ms * 1e3, 1), "TFLOPS": round(tf, 1), "frac": round(tf / BF16_PEAK_TFLOPS, 3)}
+            del Ad, Wt, Cd
+        ceil["dense_gemm_torch_mm"] = dense
         ceil["read_floor_step_us"] = round(floor_us, 2)
         ceil["read_floor_step_GBps"] = round(step_bytes / (floor_us * 1e-6) / 1e9, 1)
         ceil["decode_step_vs_read_floor"] = round(floor_us / (ms_per_step * 1e3), 3)

@@ -14,11 +14,19 @@
 // touches spread over the banks (measured on gfx950: unswizzled rows run
 // about 3x slower; this placement and chunk ^ ((row / 2) % 8) are within 1%).
 //
-// Dequant in this kernel: int4 w = fma(q, s, z - 8 s) rounded to nearest even
-// (equal to the exact (q - 8) s + z whenever z - 8 s is exact in fp32, as it
-// is for the scale/zero ranges used); int8 per-channel stages the exact code q
-// and multiplies the finished fp32 sum by the channel's scale; int8 with
-// group scales stages q * s rounded to nearest even.
+// Dequant in this kernel: int4 w = fma(q, s, z - 8 s) rounded to nearest even.
+// The fused multiply-add is exact before its one rounding, so this equals the
+// once-rounded (q - 8) s + z whenever z - 8 s is exact in fp32.  It is when
+// z = 0, and when |8 s| and |z| are within a factor 2^13 (fp16: 11
+// significant bits each) or 2^16 (bf16: 8) of each other, so that their
+// difference fits fp32's 24 bits; the dyadic test inputs always are.  A zero
+// much smaller than 8 s (e.g. |z| < 2^-10 |s| in fp16) makes z - 8 s round,
+// and the staged weight can then differ from the once-rounded value by one
+// unit in the last place of the 16-bit type: within the GEMM tolerance, and
+// not the bit-exact dequant contract, which qdequant_w4 implements directly.
+// int8 per-channel stages the exact code q and multiplies the finished fp32
+// sum by the channel's scale; int8 with group scales stages q * s rounded to
+// nearest even.
 #pragma once
 
 #include "qg_common.hpp"
