@@ -202,6 +202,42 @@ def test_unaligned_scale_rows_fall_back():
     assert rel_err(C[r, c], ref) <= TOL[BF16]
 
 
+# -- The direct-load prefill tiles bring the tile's bias and int8 channel
+#    scales into LDS with 4-byte direct loads; a pointer that is only 2-byte
+#    aligned keeps the per-element global loads.  Both paths give the same bits,
+#    and both match the oracle.  M = 512, N = 4096 runs the 256 x 256 tile.
+def _shifted(t):
+    buf = torch.empty(t.numel() + 1, dtype=t.dtype, device="cuda")
+    view = buf[1:].view(t.shape)                     # 2-byte aligned
+    view.copy_(t)
+    assert view.data_ptr() % 4 != 0
+    return view
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_prefill_epilogue_constants_unaligned(bits):
+    m, n, k = 512, 4096, 512
+    r, c = sample_pairs(m, n, seed=bits + 11)
+    if bits == 4:
+        p = si.w4_problem(m, n, k, 64, tag="epi-unal", bias_dtype=FP16)
+        A, tiled = to_dev(p.A, BF16), qg.repack_w4(to_dev(p.packed))
+        S, Z, b = to_dev(p.scale, BF16), to_dev(p.zero, BF16), to_dev(p.bias, FP16)
+        C0 = qg.gemm_w4a16(A, tiled, S, Z, b, 64)
+        C1 = qg.gemm_w4a16(A, tiled, S, Z, _shifted(b), 64)
+        ref = oracle.gemm_w4_at(p.A, p.packed, p.scale, p.zero, 64, r, c, BF16, p.bias, FP16)
+        tol = TOL[BF16]
+    else:
+        p = si.w8_problem(m, n, k, tag="epi-unal", bias_dtype=FP16)
+        A, tiled = to_dev(p.A, FP16), qg.repack_w8(to_dev(p.codes))
+        S, b = to_dev(p.scale, FP16), to_dev(p.bias, FP16)
+        C0 = qg.gemm_w8a16(A, tiled, S, b, -1)
+        C1 = qg.gemm_w8a16(A, tiled, _shifted(S), _shifted(b), -1)
+        ref = oracle.gemm_w8_at(p.A, p.codes, p.scale, r, c, -1, FP16, p.bias, FP16)
+        tol = TOL[FP16]
+    assert np.array_equal(to_bits(C0), to_bits(C1))
+    assert rel_err(C0.float().cpu().numpy()[r, c], ref) <= tol
+
+
 # -- Tile-choice boundaries: M just below / above each rule of the prefill
 #    dispatch, at a width where the direct-load tiles are eligible.  Sampled
 #    outputs against the oracle (K small to keep the oracle quick).

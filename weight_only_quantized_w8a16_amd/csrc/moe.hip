@@ -300,7 +300,7 @@ __global__ __launch_bounds__(CfgMoeDma::NTHR) void k_moe_dma(TileProblem p, int 
   __shared__ __attribute__((aligned(16))) char sc[2 * CfgMoeDma::SC_WIN];
   int tm, tn;
   if (!moe_tile_of(p, tiles_n, tm, tn)) return;
-  const DmaLds L{{a0, a1}, {b0, b1}, sc};
+  const DmaLds L{{a0, a1}, {b0, b1}, sc, nullptr};   // no dense epilogue constants
   tile_gemm_dma<CfgMoeDma, ACT, 4, MODE>(p, tm, tn, L);
 }
 

@@ -106,7 +106,8 @@ __global__ __launch_bounds__(Cfg::NTHR) void k_prefill_dma(TileProblem p, int ti
   __shared__ __attribute__((aligned(16))) char b0[Cfg::STAGE_B];
   __shared__ __attribute__((aligned(16))) char b1[Cfg::STAGE_B];
   __shared__ __attribute__((aligned(16))) char sc[2 * Cfg::SC_WIN];
-  const DmaLds L{{a0, a1}, {b0, b1}, sc};
+  __shared__ __attribute__((aligned(16))) char ep[2 * Cfg::BN * 2];
+  const DmaLds L{{a0, a1}, {b0, b1}, sc, ep};
   int tm, tn, slice;
   split_tile<SPLIT>(p, tiles_n, tm, tn, slice);
   tile_gemm_dma<Cfg, ACT, WBITS, kDense, GS8, SPLIT, PC>(p, tm, tn, L, slice);

@@ -62,6 +62,7 @@ struct DmaLds {
   char *a[2];
   char *b[2];
   char *sc;   // two scale/zero windows of DmaCfg::SC_WIN bytes
+  char *ep;   // dense tiles: the tile's bias, then its int8 channel scales (2 x BN x 2 bytes)
 };
 
 __device__ __forceinline__ int dswz(int row, int chunk) {
@@ -142,6 +143,34 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
   // No zeros (scale-only int4): an empty resource, whose loads return 0.
   [[maybe_unused]] const auto rZ = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t *>(Zb), 0, Zb ? static_cast<int>(s_bytes) : 0, kRsrcFlags);
+
+  // ---- epilogue constants: the tile's BN bias values and (per-channel int8)
+  // BN channel scales, 16-bit each, come into L.ep by 4-byte direct loads in
+  // the prologue (waves 0 .. BN / 128 - 1 the bias, the next ones the
+  // scales, 256 bytes a wave), so the epilogue reads them from LDS instead of
+  // waiting on 32 two-byte global loads per lane (measured at M = 512,
+  // N = 131072: 4.2k of the tile's 112k cycles).  A pointer that is not
+  // 4-byte aligned keeps the global loads.
+  constexpr bool kEpi = MODE == kDense && !SPLIT;
+  constexpr bool kColScale = WBITS == 8 && !GS8;
+  constexpr int kEpWaves = Cfg::BN / 128;
+  [[maybe_unused]] const bool bias_lds =
+      kEpi && p.bias && (reinterpret_cast<uintptr_t>(p.bias) & 3) == 0;
+  [[maybe_unused]] const bool cs_lds = kEpi && kColScale && (reinterpret_cast<uintptr_t>(p.S) & 3) == 0;
+  auto ep_issue = [&] {
+    if constexpr (kEpi) {
+      const bool scale_wave = wave >= kEpWaves;
+      const int part = scale_wave ? wave - kEpWaves : wave;
+      if (wave < 2 * kEpWaves && (scale_wave ? cs_lds : bias_lds)) {
+        const auto r = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(scale_wave ? p.S : p.bias), 0,
+            static_cast<int>(static_cast<uint32_t>(p.N) * 2u), kRsrcFlags);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (__attribute__((address_space(3))) void *)(L.ep + wave * 256), 4, lane * 4,
+            (n0 + part * 128) * 2, 0, 0);
+      }
+    }
+  };
 
   // ---- A: slot q = (wave * A_DMA + i) * 64 + lane of a stage is row q / 8,
   // placed chunk q % 8; it holds the row's chunk (q % 8) ^ ((row / 2) % 8).
@@ -352,6 +381,7 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
 #pragma unroll
   for (int t = 0; t < Cfg::SC_PARTS; ++t) sc_issue(t, w0);
   sc_issue(0, w0 + 1);
+  ep_issue();
   a_issue(s0, L.a[0]);
   asm volatile("" ::: "memory");
   b_issue(s0, r0);
@@ -518,16 +548,45 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
   float add[TN][4][4];    // bias (and int8 scale) per column of this lane
   float mul[TN][4][4];
   asm volatile("" ::: "memory");   // keep these loads out of the main loop's live range
+  // Column c of this lane's 4-column run (j, q): wn WTN + 32 j + 8 q + 4 (lane / 32) + e.
+  // One uniform choice per array, so each side is straight-line code.
+  auto lcol = [&](int j, int q) { return wn * Cfg::WTN + 32 * j + 8 * q + 4 * khalf; };
+  auto from_lds = [&](const char *base, int dt, float (&v)[TN][4][4]) {
 #pragma unroll
-  for (int j = 0; j < TN; ++j)
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+      for (int q = 0; q < 4; ++q) {
+        const u32x2 w = *reinterpret_cast<const u32x2 *>(base + lcol(j, q) * 2);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int col = n0 + wn * Cfg::WTN + 32 * j + 8 * q + 4 * khalf + e;
-        mul[j][q][e] = (WBITS == 8 && !GS8) ? bits_to_f32<ACT>(p.S[col]) : 1.0f;
-        add[j][q][e] = p.bias ? bits_to_f32_dyn(p.bias[col], p.bias_dt) : 0.0f;
+        for (int e = 0; e < 4; ++e)
+          v[j][q][e] = bits_to_f32_dyn(static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1))), dt);
       }
+  };
+  auto from_global = [&](const uint16_t *src, int dt, float (&v)[TN][4][4]) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[j][q][e] = bits_to_f32_dyn(src[n0 + lcol(j, q) + e], dt);
+  };
+  auto fill = [&](float x, float (&v)[TN][4][4]) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[j][q][e] = x;
+  };
+  if (bias_lds) from_lds(L.ep, p.bias_dt, add);
+  else if (p.bias) from_global(p.bias, p.bias_dt, add);
+  else fill(0.0f, add);
+  if constexpr (kColScale) {
+    if (cs_lds) from_lds(L.ep + kEpWaves * 256, ACT, mul);
+    else from_global(p.S, ACT, mul);
+  } else {
+    fill(1.0f, mul);
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     if (row_lo + 32 * (i * Cfg::WM + wm) > row_last) break;   // block holds no rows
