@@ -883,6 +883,18 @@ def run(args):
             if n:
                 floor_us += us
         ceil["read_probe"] = probe
+        # LDS read bandwidth per CU (qg_lds_probe: one workgroup per CU, a
+        # conflict-free 16-byte read loop timed by the shader clock): what the
+        # prefill tiles' fragment reads draw on.
+        lds = {}
+        for waves in (4, 8, 16):
+            cyc = torch.zeros(props.multi_processor_count, dtype=torch.int64, device=dev)
+            iters = 4096
+            for _ in range(3):
+                qg.lds_probe(waves, iters, cyc)
+            torch.cuda.synchronize()
+            lds[f"waves{waves}"] = round(iters * waves * 1024 / float(cyc.double().median()), 1)
+        ceil["lds_read_bytes_per_clock_per_cu"] = lds
         # The vendor library's plain dense GEMM on the prefill and W8A16 shapes
         # (torch.mm -> hipBLASLt; no dequantization, 16-bit weights, so four or
         # two times the weight bytes): what a tuned dense GEMM of these shapes

@@ -391,6 +391,16 @@ qg_status qmoe_grouped_ex(const void *x, const float *logits, const float *sel_l
 size_t qg_read_probe_blocks(size_t bytes);
 qg_status qg_read_probe(const void *buf, size_t bytes, uint32_t *out, void *stream);
 
+/* LDS read probe (a measurement; no part of the method): `blocks`
+ * workgroups of 64 * waves threads (waves 4, 8 or 16), each holding 96 KiB
+ * of LDS so that no two share a CU, read their LDS with conflict-free 16-byte
+ * loads, `iters` per thread, and write the shader-clock cycles of that loop
+ * to cycles[b] (device, `blocks` entries, 8-byte aligned).  LDS bytes per
+ * clock per CU = iters * waves * 64 * 16 / cycles[b].  Errors: QG_ERR_SHAPE
+ * (blocks outside 1..65536, iters outside 8..2^20 or not a multiple of 8),
+ * QG_ERR_MODE (waves), QG_ERR_NULL, QG_ERR_ALIGN. */
+qg_status qg_lds_probe(int waves, int iters, int blocks, unsigned long long *cycles, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

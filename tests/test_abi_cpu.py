@@ -330,6 +330,17 @@ def test_read_probe_validation_and_blocks():
     assert L.qg_read_probe_blocks(1 << 30) == (1 << 30) // (16 * 512 * 2)   # one pass: 512 threads x 2 pieces
 
 
+def test_lds_probe_validation():
+    L = qg.lib()
+    assert L.qg_lds_probe(8, 4096, 0, FAKE, None) == SHAPE
+    assert L.qg_lds_probe(8, 4096, 65537, FAKE, None) == SHAPE
+    assert L.qg_lds_probe(8, 4, 256, FAKE, None) == SHAPE
+    assert L.qg_lds_probe(8, 4100, 256, FAKE, None) == SHAPE
+    assert L.qg_lds_probe(6, 4096, 256, FAKE, None) == MODE
+    assert L.qg_lds_probe(8, 4096, 256, None, None) == NULL
+    assert L.qg_lds_probe(8, 4096, 256, FAKE + 4, None) == ALIGN
+
+
 # -- the torch binding refuses wrong shapes and dtypes before any pointer is
 # passed (host tensors suffice: the checks run before the device checks) -----
 

@@ -389,6 +389,21 @@ def test_read_probe_reads_every_byte_once(nbytes):
     assert got == want
 
 
+@pytest.mark.parametrize("waves", [4, 8, 16])
+def test_lds_probe_counts_cycles(waves):
+    # One workgroup per CU reading its LDS: every workgroup reports a loop of
+    # at least one clock per 256 bytes (the widest an LDS could serve) and
+    # well under a second's worth of cycles.
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 1024
+    cyc = torch.zeros(cus, dtype=torch.int64, device="cuda")
+    qg.lds_probe(waves, iters, cyc)
+    torch.cuda.synchronize()
+    c = cyc.cpu().numpy()
+    floor = iters * waves * 1024 / 256
+    assert (c >= floor).all() and (c < 2e9).all(), (c.min(), c.max(), floor)
+
+
 @pytest.mark.parametrize("m", [1, 2, 3, 4, 7, 8])
 @pytest.mark.parametrize("group,dtype", [(64, BF16), (128, FP16)])
 def test_large_n_decode_integer_exact(m, group, dtype):

@@ -21,7 +21,7 @@ __all__ = [
     "QGemmError", "lib", "repack_w4", "unrepack_w4", "repack_w8", "unrepack_w8", "repack_w8_kn",
     "unrepack_w8_kn", "quantize_w4", "dequant_w4", "dequant_w8", "gemm_w4a16", "gemm_w8a16",
     "moe_grouped", "moe_workspace_size", "gemm_workspace_size", "dtype_code", "gemm_w8a8",
-    "w8a8_workspace_size", "embed_w4", "embed_w8", "read_probe", "set_override", "clear_override",
+    "w8a8_workspace_size", "embed_w4", "embed_w8", "read_probe", "lds_probe", "set_override", "clear_override",
     "moe_grouped_noalloc",
 ]
 
@@ -475,6 +475,17 @@ def read_probe(buf: Optional[torch.Tensor], nbytes: int, out: torch.Tensor) -> t
         raise QGemmError("qg_read_probe", 2, "out is too small")
     check("qg_read_probe", lib().qg_read_probe(_ptr(buf), nbytes, _ptr(out), _stream(out)))
     return out
+
+
+def lds_probe(waves: int, iters: int, cycles: torch.Tensor) -> torch.Tensor:
+    """LDS read loop of cycles.numel() workgroups of 64 * waves threads, one
+    per CU (qg_lds_probe); cycles (int64, device) gets each workgroup's
+    shader-clock cycles.  Bytes per clock per CU = iters * waves * 1024 / cycles."""
+    _dev(cycles, "cycles")
+    if cycles.dtype != torch.int64:
+        raise QGemmError("qg_lds_probe", 4, "cycles must be int64")
+    check("qg_lds_probe", lib().qg_lds_probe(waves, iters, cycles.numel(), _ptr(cycles), _stream(cycles)))
+    return cycles
 
 
 # -- MoE -----------------------------------------------------------------------

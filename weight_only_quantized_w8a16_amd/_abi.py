@@ -52,6 +52,7 @@ SIGNATURES = {
     "qembed_w8": (_ST, [_P, _INT, _P, _INT, _P, _P, _INT, _INT, _INT, _INT, _INT, _P]),
     "qg_read_probe_blocks": (_SZ, [_SZ]),
     "qg_read_probe": (_ST, [_P, _SZ, _P, _P]),
+    "qg_lds_probe": (_ST, [ctypes.c_int, ctypes.c_int, ctypes.c_int, _P, _P]),
     "qmoe_workspace_size": (_SZ, [_INT, _INT, _INT, _INT, _INT]),
     "qmoe_grouped": (_ST, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _INT, _INT, _INT, _INT, _INT, _INT,
                            _INT, _P, _P, _P, _SZ, _P]),

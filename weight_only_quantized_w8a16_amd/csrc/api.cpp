@@ -413,4 +413,12 @@ qg_status qg_read_probe(const void *buf, size_t bytes, uint32_t *out, void *stre
   return hip_status(qg::launch_read_probe(buf, bytes, out, as_stream(stream)));
 }
 
+qg_status qg_lds_probe(int waves, int iters, int blocks, unsigned long long *cycles, void *stream) {
+  if (blocks < 1 || blocks > 65536 || iters < 8 || iters > (1 << 20) || iters % 8 != 0) return QG_ERR_SHAPE;
+  if (waves != 4 && waves != 8 && waves != 16) return QG_ERR_MODE;
+  if (!cycles) return QG_ERR_NULL;
+  if (!aligned(cycles, 8)) return QG_ERR_ALIGN;
+  return hip_status(qg::launch_lds_probe(waves, iters, blocks, cycles, as_stream(stream)));
+}
+
 }  // extern "C"

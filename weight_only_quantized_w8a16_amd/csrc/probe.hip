@@ -1,5 +1,6 @@
-// probe.hip -- a plain streaming read, the ceiling the HBM-bound kernels are
-// measured against.  Each thread reads 16-byte pieces with streaming
+// probe.hip -- measurement probes, no part of the method: a plain streaming
+// read, the ceiling the HBM-bound kernels are measured against, and an LDS
+// read loop, the LDS bandwidth the prefill tiles draw on.  The read probe:  Each thread reads 16-byte pieces with streaming
 // (nontemporal) loads; in iteration i workgroup b reads piece
 // (i * gridDim + b) * blockDim + thread, so at every moment the grid sweeps one
 // contiguous window of the buffer (with the one-pass grid below: two windows,
@@ -52,6 +53,43 @@ __global__ __launch_bounds__(kProbeThreads) void k_read_probe(const u32x4 *__res
     for (int w = 0; w < kProbeThreads / 64; ++w) r ^= part[w];
     out[blockIdx.x] = r;
   }
+}
+
+// LDS read probe: each workgroup holds 96 KiB of LDS (one workgroup per CU:
+// the CU's 160 KiB hold no second), fills its first 64 KiB, then every
+// thread reads 16-byte pieces from it `iters` times -- wave w's read j takes
+// the 1 KiB row (7 w + j) % 64, lane l its piece l, so a 16-lane group reads
+// 256 consecutive bytes and no two lanes of a group share a bank -- and
+// thread 0 writes the shader-clock cycles of the read loop (s_memtime,
+// between two barriers).  The pieces are XOR-folded; a fold equal to a fixed
+// constant would be written in place of the cycles, so the reads cannot be
+// dropped.
+template <int NT>
+__global__ __launch_bounds__(NT) void k_lds_probe(unsigned long long *__restrict__ cycles, int iters) {
+  __shared__ __attribute__((aligned(16))) char lds[96 * 1024];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int i = tid; i < 4096; i += NT)
+    reinterpret_cast<u32x4 *>(lds)[i] = u32x4{uint32_t(i), uint32_t(3 * i), uint32_t(5 * i), uint32_t(7 * i)};
+  __syncthreads();
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  const unsigned long long t0 = __builtin_readcyclecounter();
+#pragma unroll 8
+  for (int j = 0; j < iters; ++j)
+    acc ^= *reinterpret_cast<const u32x4 *>(lds + ((wave * 7 + j) & 63) * 1024 + lane * 16);
+  __syncthreads();
+  const unsigned long long t1 = __builtin_readcyclecounter();
+  if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9e3779b9u) cycles[blockIdx.x] = 0;
+  __syncthreads();
+  if (tid == 0) cycles[blockIdx.x] = t1 - t0;
+}
+
+hipError_t launch_lds_probe(int waves, int iters, int blocks, unsigned long long *cycles, hipStream_t s) {
+  switch (waves) {
+    case 4: hipLaunchKernelGGL(k_lds_probe<256>, dim3(blocks), dim3(256), 0, s, cycles, iters); break;
+    case 8: hipLaunchKernelGGL(k_lds_probe<512>, dim3(blocks), dim3(512), 0, s, cycles, iters); break;
+    default: hipLaunchKernelGGL(k_lds_probe<1024>, dim3(blocks), dim3(1024), 0, s, cycles, iters); break;
+  }
+  return hipGetLastError();
 }
 
 size_t read_probe_blocks(size_t bytes) {

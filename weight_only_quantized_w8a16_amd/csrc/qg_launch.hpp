@@ -161,5 +161,6 @@ namespace qg {
 // Streaming-read probe (measurement).
 size_t read_probe_blocks(size_t bytes);
 hipError_t launch_read_probe(const void *buf, size_t bytes, uint32_t *out, hipStream_t s);
+hipError_t launch_lds_probe(int waves, int iters, int blocks, unsigned long long *cycles, hipStream_t s);
 
 }  // namespace qg
