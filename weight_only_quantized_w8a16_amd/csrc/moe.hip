@@ -173,7 +173,8 @@ __global__ __launch_bounds__(256) void k_moe_route(const float *__restrict__ log
   }
 }
 
-// Single workgroup: counts, offsets, tile list, permutation.  The exclusive
+// Single workgroup: counts, offsets, tile list, permutation (the row -> token
+// map assembled in LDS and stored in order when it fits).  The exclusive
 // scans over experts (rows and tiles) run in one wave, the tile list is
 // written by one thread per expert, and rows take their slot within the
 // expert through LDS atomics (the order of rows inside an expert does not
@@ -181,12 +182,15 @@ __global__ __launch_bounds__(256) void k_moe_route(const float *__restrict__ log
 // loads its ids kPlanBatch at a time before using them, so the passes over
 // the ids wait for memory once per batch rather than once per row.
 constexpr int kPlanBatch = 16;
+constexpr int kPlanLdsRows = 16384;   // row -> token map built in LDS up to this many rows
 __global__ __launch_bounds__(1024) void k_moe_plan(const int32_t *__restrict__ ids, int R, int E,
                                                    int topk, int bm, MoeTile *__restrict__ tiles,
                                                    int32_t *__restrict__ ntiles,
                                                    int32_t *__restrict__ row_src,
                                                    int32_t *__restrict__ dest) {
   __shared__ int cnt[256], off[256], toff[256], fill[256];
+  __shared__ int src_lds[kPlanLdsRows];
+  const bool in_lds = R <= kPlanLdsRows;
   const int nthr = blockDim.x;
   for (int e = threadIdx.x; e < 256; e += nthr) { cnt[e] = 0; fill[e] = 0; }
   __syncthreads();
@@ -249,6 +253,13 @@ __global__ __launch_bounds__(1024) void k_moe_plan(const int32_t *__restrict__ i
   for (int base = 0; base < R; base += kPlanBatch * nthr) {
     int e[kPlanBatch];
     load_batch(base, e);
+    // All of the batch's slot claims first (independent LDS atomics, in
+    // flight together), then the stores: claiming and storing row by row
+    // made each thread wait out one atomic's latency per row (9.8k of the
+    // kernel's 18k cycles at 12288 rows).
+    int pos[kPlanBatch];
+#pragma unroll
+    for (int u = 0; u < kPlanBatch; ++u) pos[u] = e[u] >= 0 ? atomicAdd(&fill[e[u]], 1) : -1;
 #pragma unroll
     for (int u = 0; u < kPlanBatch; ++u) {
       const int r = base + u * nthr + static_cast<int>(threadIdx.x);
@@ -257,10 +268,18 @@ __global__ __launch_bounds__(1024) void k_moe_plan(const int32_t *__restrict__ i
         dest[r] = -1;
         continue;
       }
-      const int pos = off[e[u]] + atomicAdd(&fill[e[u]], 1);
-      row_src[pos] = r / topk;
-      dest[r] = pos;
+      const int q = off[e[u]] + pos[u];
+      if (in_lds) src_lds[q] = r / topk;
+      else row_src[q] = r / topk;
+      dest[r] = q;
     }
+  }
+  // Written out in order: scattered 4-byte stores from one workgroup (a
+  // cache line per lane) cost more than the LDS round trip.
+  if (in_lds) {
+    __syncthreads();
+    const int rows = off[E - 1] + cnt[E - 1];
+    for (int i = threadIdx.x; i < rows; i += nthr) row_src[i] = src_lds[i];
   }
 }
 
@@ -306,6 +325,8 @@ __global__ __launch_bounds__(CfgMoeDma::NTHR) void k_moe_dma(TileProblem p, int 
 
 // out[t, h..h+7] = sum_j w[t, j] * (y[dest[t, j], h..h+7] + b2[e, h..h+7]),
 // e = ids[t, j]; slots without an expert row (finished rows) add nothing.
+// y is read once and out written once: streaming (nontemporal) accesses
+// (measured 2.7 us faster on the 2048-token MoE than plain ones).
 template <int ACT>
 __global__ __launch_bounds__(256) void k_moe_combine(const uint16_t *__restrict__ y,
                                                      const float *__restrict__ wts,
@@ -323,7 +344,7 @@ __global__ __launch_bounds__(256) void k_moe_combine(const uint16_t *__restrict_
     const float w = wts[static_cast<size_t>(t) * topk + j];
     const int row = dest[static_cast<size_t>(t) * topk + j];
     if (row < 0) continue;
-    const u32x4 v = *reinterpret_cast<const u32x4 *>(y + static_cast<size_t>(row) * H + h0);
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(y + static_cast<size_t>(row) * H + h0));
     u32x4 b = {0u, 0u, 0u, 0u};
     if (b2) b = *reinterpret_cast<const u32x4 *>(b2 + static_cast<size_t>(ids[static_cast<size_t>(t) * topk + j]) * H + h0);
 #pragma unroll
@@ -337,7 +358,7 @@ __global__ __launch_bounds__(256) void k_moe_combine(const uint16_t *__restrict_
   u32x4 o;
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = pack2<ACT>(acc[2 * i], acc[2 * i + 1]);
-  *reinterpret_cast<u32x4 *>(out + static_cast<size_t>(t) * H + h0) = o;
+  __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(out + static_cast<size_t>(t) * H + h0));
 }
 
 namespace {
