@@ -200,12 +200,33 @@ hipError_t run_dma(const GemmArgs &a, hipStream_t s, const Split &sp = Split{}) 
   return reduce_split<ACT, WBITS, GS8>(a, sp, s);
 }
 
+// Compute units of the current device (cached per device; 256 if unknown).
+int device_cus() {
+  static std::atomic<int> cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int c = cus[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+    cus[dev].store(c, std::memory_order_relaxed);
+  }
+  return c;
+}
+
 // Tile shapes.  Choice, from on-device sweeps at K = 2048 and 3584 (M from
 // 32 to 4096): the direct-load tiles once there are enough of them to keep
 // most CUs busy, the generic tiles (down to 64 x 64) when the problem would
-// leave CUs idle.  The dispatch override's prefill_tile forces one (tests
-// and tuning); D8, D8N, D64 and D128 are the 256 x 256, 256 x 128, 64 x 256
-// and 128 x 256 tiles with direct-to-LDS activation loads.
+// leave CUs idle.  Every direct-load tile holds a CU alone (its LDS allows no
+// second workgroup), so a launch takes ceil(tiles / CUs) rounds of one tile's
+// time: above 192 rows, once the 256 x 256 tiles fill half the CUs, the
+// choice between them and the 256 x 128 tiles (twice as many, each measured
+// at 0.62 of a 256 x 256 tile's time) is the one with fewer round-weighted
+// tile times -- e.g. W8A16 M = 512, N = 18944 (148 tiles of 256 x 256: one
+// round): 79.6 us against 102.8 on 256 x 128; M = 1024 (296 tiles: two rounds
+// against three of 256 x 128): 171.4 against 159.9 us on 256 x 128.  The
+// dispatch override's prefill_tile forces one (tests and tuning); D8, D8N,
+// D64 and D128 are the 256 x 256, 256 x 128, 64 x 256 and 128 x 256 tiles
+// with direct-to-LDS activation loads.
 
 int choose_tile(const GemmArgs &a) {
   auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * (a.N / bn); };
@@ -221,6 +242,14 @@ int choose_tile(const GemmArgs &a) {
     case kS: return kS;
     default: break;
   }
+  if (n256 && a.M > 192) {
+    const int cus = device_cus();
+    const long t8 = tiles(256, 256);
+    if (2 * t8 > cus) {
+      const long rounds8 = (t8 + cus - 1) / cus, rounds8n = (2 * t8 + cus - 1) / cus;
+      return rounds8n * 62 < rounds8 * 100 ? kD8N : kD8;
+    }
+  }
   if (n256 && a.M > 128 && tiles(256, 256) >= 160) return kD8;
   // Up to 192 rows the 64-row tile wastes fewer rows than a 256-row one.
   if (n256 && a.M > 128 && a.M <= 192 && tiles(64, 256) >= 128) return kD64;
@@ -229,6 +258,9 @@ int choose_tile(const GemmArgs &a) {
   // once there are enough of them.
   if (n256 && a.M <= 64 && tiles(64, 256) >= 256) return kD64;
   if (n256 && a.M > 64 && a.M <= 128 && tiles(128, 256) >= 256) return kD128;
+  // 65 - 128 rows with at least half a round of 64 x 256 tiles (W8A16 M = 128,
+  // N = 18944: 36.5 us against 41.2 on the 64 x 64 tile)
+  if (n256 && a.M > 64 && a.M <= 128 && 2 * tiles(64, 256) >= device_cus()) return kD64;
   if (n256 && a.M > 128 && tiles(64, 256) >= 128) return kD64;
   if (n128 && a.M > 128 && tiles(256, 128) >= 200) return kL;
   if (n128 && a.M > 64 && tiles(128, 128) >= 256) return kM;
