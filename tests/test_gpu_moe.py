@@ -57,6 +57,16 @@ def test_moe_small_full(T, H, I, E, k, g, moe_tile):
     check(p)
 
 
+def test_moe_more_rows_than_the_plan_stages_in_lds(moe_tile):
+    # 3000 tokens x top-6 = 18000 expert rows: past the 16384 rows whose
+    # row -> token map the plan assembles in LDS, so the plan scatters it to
+    # memory directly (checked on a sample of tokens, routing in full).
+    p = si.moe_problem(3000, 256, 256, 8, 6, 64, tag="moe-many-rows")
+    assert p.tokens * p.topk > 16384
+    toks = np.unique(np.concatenate([[0, 1, 2999], np.random.default_rng(7).integers(0, 3000, 256)]))
+    check(p, tokens=toks)
+
+
 def test_moe_expert_tiles_exactly_full(moe_tile):
     # 256 tokens all routed to experts 5 and 2: two experts of exactly 256 rows.
     p = si.moe_problem(256, 256, 256, 8, 2, 64, tag="moe-full-tiles")
