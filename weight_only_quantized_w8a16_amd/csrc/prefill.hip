@@ -258,9 +258,6 @@ int choose_tile(const GemmArgs &a) {
   // once there are enough of them.
   if (n256 && a.M <= 64 && tiles(64, 256) >= 256) return kD64;
   if (n256 && a.M > 64 && a.M <= 128 && tiles(128, 256) >= 256) return kD128;
-  // 65 - 128 rows with at least half a round of 64 x 256 tiles (W8A16 M = 128,
-  // N = 18944: 36.5 us against 41.2 on the 64 x 64 tile)
-  if (n256 && a.M > 64 && a.M <= 128 && 2 * tiles(64, 256) >= device_cus()) return kD64;
   if (n256 && a.M > 128 && tiles(64, 256) >= 128) return kD64;
   if (n128 && a.M > 128 && tiles(256, 128) >= 200) return kL;
   if (n128 && a.M > 64 && tiles(128, 128) >= 256) return kM;
