@@ -6,10 +6,12 @@
 //
 // Stages, one launch each:
 //   route    one wave per token: top-k of the fp32 logits (ties to the lower
-//            expert id) and the softmax over the selected logits;
-//   plan     one workgroup: per-expert row counts, offsets, the list of
-//            (expert, row range) tiles for the grouped GEMMs, and the
-//            permutation token <-> expert-sorted row;
+//            expert id) and the softmax over the selected logits; per
+//            workgroup of 16 tokens also its rows' count per expert and each
+//            row's place among them;
+//   plan     per-expert row offsets from those counts, the list of (expert,
+//            row range) tiles for the grouped GEMMs, and the permutation
+//            token <-> expert-sorted row;
 //   fc1      grouped tile GEMM, activation rows gathered through the
 //            permutation, gate and up columns in one tile, silu(gate) * up
 //            in the epilogue;
@@ -23,6 +25,7 @@
 // (route gives them no expert; plan and combine skip their slots), the fc1
 // expert biases (fc1 epilogue, before the activation) and the fc2 ones
 // (combine), and the normalization mode (route).
+#include <climits>
 #include <mutex>
 
 #include "qg_launch.hpp"
@@ -73,19 +76,28 @@ constexpr int kMoeBM = CfgMoe::BM;   // smallest expert tile (sizes the tile lis
 
 size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// Routing: tokens per workgroup (one wave each).
+constexpr int kRouteTokens = 16;
+// Plan: at most this many workgroups (each reads every routing workgroup's
+// counts).
+constexpr int kPlanBlocks = 128;
+
 struct MoeLayout {
-  size_t ids, wts, row_src, dest, tiles, ntiles, act, y, total;
+  size_t ids, wts, row_src, dest, lpos, hist, tiles, ntiles, act, y, total;
 };
 
 MoeLayout moe_layout(int T, int H, int I, int E, int topk) {
   const size_t R = static_cast<size_t>(T) * topk;
   const size_t max_tiles = (R + kMoeBM - 1) / kMoeBM + E;
+  const size_t nw = (static_cast<size_t>(T) + kRouteTokens - 1) / kRouteTokens;
   MoeLayout l{};
   size_t o = 0;
   l.ids = o;     o = align_up(o + R * 4);
   l.wts = o;     o = align_up(o + R * 4);
   l.row_src = o; o = align_up(o + R * 4);
   l.dest = o;    o = align_up(o + R * 4);
+  l.lpos = o;    o = align_up(o + R * 4);
+  l.hist = o;    o = align_up(o + nw * E * 4);
   l.tiles = o;   o = align_up(o + max_tiles * sizeof(MoeTile));
   l.ntiles = o;  o = align_up(o + 4);
   l.act = o;     o = align_up(o + R * I * 2);
@@ -100,186 +112,258 @@ size_t moe_workspace_bytes(int T, int H, int I, int E, int topk) {
   return moe_layout(T, H, I, E, topk).total;
 }
 
-// One wave per token; up to 256 experts (4 logits per lane).  The experts
-// are chosen by `sel` (the biased logits when given, else the gating logits)
-// and weighted from the gating logits: softmax over the chosen experts
-// (renormalize) or over all of them.  A finished row takes no expert.
-__global__ __launch_bounds__(256) void k_moe_route(const float *__restrict__ logits,
-                                                   const float *__restrict__ sel_logits,
-                                                   const uint8_t *__restrict__ finished, int T, int E,
-                                                   int topk, int renorm, int32_t *__restrict__ ids,
-                                                   float *__restrict__ wts) {
+// Order-preserving integer key of a float: a > b as floats (with -0 == +0)
+// exactly when key(a) > key(b) as signed integers; NaNs sort above +inf
+// (positive sign) or below -inf (negative), so every value has a place and
+// equal keys mean equal values.
+__device__ __forceinline__ int order_key(float x) {
+  int b = __float_as_int(x);
+  if ((b & 0x7FFFFFFF) == 0) b = 0;
+  return b ^ ((b >> 31) & 0x7FFFFFFF);
+}
+
+// Largest value of x over the wave, by DPP steps inside each 16-lane row
+// (quad swaps, then the half-row and row mirrors) and the four row results.
+__device__ __forceinline__ int wave_max_i32(int x) {
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false));    // quad_perm [1,0,3,2]
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false));    // quad_perm [2,3,0,1]
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false));   // row_half_mirror
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false));   // row_mirror
+  return max(max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+             max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
+}
+
+// One wave per token, kRouteTokens tokens per workgroup; up to 256 experts,
+// expert lane + 64 i in slot i of a lane.  The experts are chosen by `sel`
+// (the biased logits when given, else the gating logits): k times the
+// largest remaining value (as an order key: the wave's largest key, then
+// the lowest expert id holding it), so ties go to the lower expert id.
+// Lane j keeps the j-th choice.  Weights come from the gating logits:
+// softmax over the chosen experts (renormalize) or over all of them.  A
+// finished row takes no expert.
+// For the plan, the workgroup also counts its rows per expert (hist, one
+// row of E counts per workgroup) and gives each routed row its place among
+// the workgroup's rows of that expert (lpos).  Places are taken with LDS
+// atomics, in no fixed order: every expert row is computed on its own, so
+// the order of rows within an expert changes no output.
+__global__ __launch_bounds__(64 * kRouteTokens) void k_moe_route(
+    const float *__restrict__ logits, const float *__restrict__ sel_logits,
+    const uint8_t *__restrict__ finished, int T, int E, int topk, int renorm,
+    int32_t *__restrict__ ids, float *__restrict__ wts, int32_t *__restrict__ lpos,
+    int32_t *__restrict__ hist) {
+  __shared__ int h[256];
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  if (finished && finished[t]) {
-    if (lane < topk) {
-      ids[static_cast<size_t>(t) * topk + lane] = -1;
-      wts[static_cast<size_t>(t) * topk + lane] = 0.0f;
-    }
-    return;
-  }
-  const float *sl = sel_logits ? sel_logits : logits;
-  float v[4], u[4];
-  bool cand[4];   // expert lane + 64 i exists and is not chosen yet
+  const int t = blockIdx.x * kRouteTokens + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // This token's logits (loads issued before the counts are cleared).
+  const int tc = min(t, T - 1);
+  const float *sl = (sel_logits ? sel_logits : logits) + static_cast<size_t>(tc) * E;
+  const float *lt = logits + static_cast<size_t>(tc) * E;
+  int key[4];
+  float u[4];     // gating logits (-inf past E)
+  bool cand[4];   // expert exists and is not chosen yet
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;
     cand[i] = e < E;
-    v[i] = cand[i] ? sl[static_cast<size_t>(t) * E + e] : 0.0f;
-    u[i] = cand[i] ? logits[static_cast<size_t>(t) * E + e] : -__builtin_inff();
+    key[i] = order_key(cand[i] ? sl[e] : 0.0f);
+    u[i] = cand[i] ? lt[e] : -__builtin_inff();
   }
-  float my_l = -__builtin_inff();
-  int my_id = 0;
-  for (int j = 0; j < topk; ++j) {
-    // Lane-local best candidate (strict > keeps the lower expert id on
-    // ties), then the wave's best by (value, lower id).  A chosen expert
-    // leaves the candidate set, so it cannot win again even when every
-    // remaining value is -inf; bi < 0 marks a lane with no candidate.
-    float bv = 0.0f;
-    int bi = -1;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) h[e] = 0;
+  __syncthreads();
+  int my_id = -1;   // lanes < topk: the expert of this choice
+  if (t < T) {
+    if (finished && finished[t]) {
+      if (lane < topk) {
+        ids[static_cast<size_t>(t) * topk + lane] = -1;
+        wts[static_cast<size_t>(t) * topk + lane] = 0.0f;
+      }
+    } else {
+      const int nslot = (E + 63) >> 6;   // slots in use (wave-uniform)
+      float my_l = 0.0f, m = -__builtin_inff();
+      for (int j = 0; j < topk; ++j) {
+        int best = INT_MIN;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (cand[i] && (bi < 0 || v[i] > bv)) { bv = v[i]; bi = lane + 64 * i; }
+        for (int i = 0; i < 4; ++i)
+          if (cand[i]) best = max(best, key[i]);
+        const int M = wave_max_i32(best);
+        // the lowest expert id among the candidates holding key M: slot by
+        // slot, the lowest lane (one exists: M is a candidate's key, or every
+        // candidate's key is INT_MIN)
+        int w = 0;
+        float uw = 0.0f;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (oi >= 0 && (bi < 0 || ov > bv || (ov == bv && oi < bi))) { bv = ov; bi = oi; }
+        for (int i = 0; i < 4; ++i) {
+          if (i >= nslot) break;
+          const unsigned long long hit = __ballot(cand[i] && key[i] == M);
+          if (hit) {
+            const int src = __builtin_ctzll(hit);
+            w = 64 * i + src;
+            uw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(u[i]), src));
+            if (lane == src) cand[i] = false;
+            break;
+          }
+        }
+        if (lane == j) { my_id = w; my_l = uw; }
+        m = fmaxf(m, uw);
+      }
+      // Softmax over the chosen experts (max m from the choices, the sum
+      // gathered in choice order) or over all of them.
+      float d = 0.0f, ex = 0.0f;
+      if (renorm) {
+        ex = lane < topk ? expf(my_l - m) : 0.0f;
+        for (int j = 0; j < topk; ++j)
+          d += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j));
+      } else {
+        m = fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3]));
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) d += (lane + 64 * i < E) ? expf(u[i] - m) : 0.0f;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) d += __shfl_xor(d, off);
+        ex = lane < topk ? expf(my_l - m) : 0.0f;
+      }
+      if (lane < topk) {
+        ids[static_cast<size_t>(t) * topk + lane] = my_id;
+        wts[static_cast<size_t>(t) * topk + lane] = ex / d;
+      }
     }
-    // the chosen expert's gating logit, from the lane that holds it
-    const int slot = bi >> 6;
-    const float mine = slot == 0 ? u[0] : slot == 1 ? u[1] : slot == 2 ? u[2] : u[3];
-    const float ul = __shfl(mine, bi & 63);
-    if ((bi & 63) == lane) cand[slot] = false;
-    if (lane == j) { my_l = ul; my_id = bi; }
   }
-  // max and sum over the chosen experts (lanes < topk) or over all experts
-  float m = renorm ? my_l : fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3]));
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  float d = 0.0f;
-  if (renorm) {
-    d = lane < topk ? expf(my_l - m) : 0.0f;
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) d += (lane + 64 * i < E) ? expf(u[i] - m) : 0.0f;
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) d += __shfl_xor(d, off);
-  if (lane < topk) {
-    ids[static_cast<size_t>(t) * topk + lane] = my_id;
-    wts[static_cast<size_t>(t) * topk + lane] = expf(my_l - m) / d;
-  }
+  if (my_id >= 0) lpos[static_cast<size_t>(t) * topk + lane] = atomicAdd(&h[my_id], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[static_cast<size_t>(blockIdx.x) * E + e] = h[e];
 }
 
-// Single workgroup: counts, offsets, tile list, permutation (the row -> token
-// map assembled in LDS and stored in order when it fits).  The exclusive
-// scans over experts (rows and tiles) run in one wave, the tile list is
-// written by one thread per expert, and rows take their slot within the
-// expert through LDS atomics (the order of rows inside an expert does not
-// change any output: every row is computed independently).  Each thread
-// loads its ids kPlanBatch at a time before using them, so the passes over
-// the ids wait for memory once per batch rather than once per row.
-constexpr int kPlanBatch = 16;
-constexpr int kPlanLdsRows = 16384;   // row -> token map built in LDS up to this many rows
-__global__ __launch_bounds__(1024) void k_moe_plan(const int32_t *__restrict__ ids, int R, int E,
-                                                   int topk, int bm, MoeTile *__restrict__ tiles,
-                                                   int32_t *__restrict__ ntiles,
-                                                   int32_t *__restrict__ row_src,
-                                                   int32_t *__restrict__ dest) {
-  __shared__ int cnt[256], off[256], toff[256], fill[256];
-  __shared__ int src_lds[kPlanLdsRows];
-  const bool in_lds = R <= kPlanLdsRows;
-  const int nthr = blockDim.x;
-  for (int e = threadIdx.x; e < 256; e += nthr) { cnt[e] = 0; fill[e] = 0; }
+// Inclusive prefix sum over the wave's lanes by DPP: sums of four lanes
+// inside each 16-lane row (row shifts by 1, 2, 3), of eight and sixteen
+// (shifts by 4 and 8 on the upper banks), then the row totals carried into
+// the rows above (row broadcasts of lanes 15 and 31).  Lanes shifted in
+// from outside a row read 0.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  int t = x;
+  t += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);   // row_shr:1
+  t += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);   // row_shr:2
+  t += __builtin_amdgcn_update_dpp(0, x, 0x113, 0xF, 0xF, true);   // row_shr:3
+  t += __builtin_amdgcn_update_dpp(0, t, 0x114, 0xF, 0xE, true);   // row_shr:4, lanes 4..15
+  t += __builtin_amdgcn_update_dpp(0, t, 0x118, 0xF, 0xC, true);   // row_shr:8, lanes 8..15
+  t += __builtin_amdgcn_update_dpp(0, t, 0x142, 0xA, 0xF, true);   // row_bcast:15, rows 1, 3
+  t += __builtin_amdgcn_update_dpp(0, t, 0x143, 0xC, 0xF, true);   // row_bcast:31, rows 2, 3
+  return t;
+}
+
+// Plan: workgroup b handles routing workgroups [b per, (b + 1) per).  Every
+// workgroup sums the routing counts per expert over all routing workgroups
+// (tot) and over those before its own (pre), scans tot over the experts into
+// row and tile offsets, and places its rows: routed row r of expert e goes to
+// off[e] + pre[e] + lpos[r].  Workgroup 0 also writes the tile list and its
+// length.  The counts (E per routing workgroup) are read once per workgroup.
+constexpr int kPlanThreads = 256;
+__global__ __launch_bounds__(kPlanThreads) void k_moe_plan(
+    const int32_t *__restrict__ ids, const int32_t *__restrict__ lpos,
+    const int32_t *__restrict__ hist, int R, int E, int topk, int nw, int per, int bm,
+    MoeTile *__restrict__ tiles, int32_t *__restrict__ ntiles, int32_t *__restrict__ row_src,
+    int32_t *__restrict__ dest) {
+  __shared__ int tot[256], pre[256], off[256], toff[256];
+  const int w0 = blockIdx.x * per, w1 = min(nw, w0 + per);
+  const int rows_per = kRouteTokens * topk;
+  // The first routing workgroup's rows (up to 4 per thread), loaded ahead.
+  int e_pre[4], l_pre[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int r = w0 * rows_per + k * kPlanThreads + static_cast<int>(threadIdx.x);
+    const bool ok = k * kPlanThreads + static_cast<int>(threadIdx.x) < rows_per && r < R;
+    e_pre[k] = ok ? ids[r] : -2;
+    l_pre[k] = ok ? lpos[r] : 0;
+  }
+  for (int e = threadIdx.x; e < E; e += kPlanThreads) { tot[e] = 0; pre[e] = 0; }
   __syncthreads();
-  auto load_batch = [&](int base, int (&e)[kPlanBatch]) {
+  {
+    // Thread (g, e) sums column e over routing workgroups g, g + G, ...
+    // (G = 256 / E column groups), 32 loads in flight at a time.
+    const int G = kPlanThreads / E;
+    const int g = static_cast<int>(threadIdx.x) / E, e = static_cast<int>(threadIdx.x) - g * E;
+    if (g < G) {
+      constexpr int kBatch = 32;
+      int st = 0, sp = 0;
+      for (int w = g; w < nw; w += kBatch * G) {
+        int v[kBatch];
 #pragma unroll
-    for (int u = 0; u < kPlanBatch; ++u) {
-      const int r = base + u * nthr + static_cast<int>(threadIdx.x);
-      e[u] = r < R ? ids[r] : -1;
+        for (int u = 0; u < kBatch; ++u) {
+          const int wu = w + u * G;
+          v[u] = wu < nw ? hist[static_cast<size_t>(wu) * E + e] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          st += v[u];
+          sp += (w + u * G < w0) ? v[u] : 0;
+        }
+      }
+      atomicAdd(&tot[e], st);
+      atomicAdd(&pre[e], sp);
     }
-  };
-  for (int base = 0; base < R; base += kPlanBatch * nthr) {
-    int e[kPlanBatch];
-    load_batch(base, e);
-#pragma unroll
-    for (int u = 0; u < kPlanBatch; ++u)
-      if (e[u] >= 0) atomicAdd(&cnt[e[u]], 1);
   }
   __syncthreads();
   if (threadIdx.x < 64) {
     // lane l scans experts 4l .. 4l + 3, then the lanes' totals
     const int lane = threadIdx.x;
-    int c[4], t[4], rs = 0, ts = 0;
+    int c[4], tl[4], rs = 0, ts = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = 4 * lane + i;
-      c[i] = e < E ? cnt[e] : 0;
-      t[i] = (c[i] + bm - 1) / bm;
+      c[i] = e < E ? tot[e] : 0;
+      tl[i] = (c[i] + bm - 1) / bm;
       rs += c[i];
-      ts += t[i];
+      ts += tl[i];
     }
-    int ri = rs, ti = ts;   // inclusive scans over lanes
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int ru = __shfl_up(ri, d), tu = __shfl_up(ti, d);
-      if (lane >= d) { ri += ru; ti += tu; }
-    }
+    const int ri = wave_incl_scan(rs), ti = wave_incl_scan(ts);
     int ro = ri - rs, to = ti - ts;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = 4 * lane + i;
       if (e < E) { off[e] = ro; toff[e] = to; }
       ro += c[i];
-      to += t[i];
+      to += tl[i];
     }
-    if (lane == 63) *ntiles = ti;
+    if (lane == 63 && blockIdx.x == 0) *ntiles = ti;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    const int r1 = off[e] + cnt[e];
-    int k = toff[e];
-    for (int r0 = off[e]; r0 < r1; r0 += bm) {
-      MoeTile tl;
-      tl.expert = e;
-      tl.row0 = r0;
-      tl.row1 = min(r0 + bm, r1);
-      tl.pad = 0;
-      tiles[k++] = tl;
-    }
-  }
-  for (int base = 0; base < R; base += kPlanBatch * nthr) {
-    int e[kPlanBatch];
-    load_batch(base, e);
-    // All of the batch's slot claims first (independent LDS atomics, in
-    // flight together), then the stores: claiming and storing row by row
-    // made each thread wait out one atomic's latency per row (9.8k of the
-    // kernel's 18k cycles at 12288 rows).
-    int pos[kPlanBatch];
-#pragma unroll
-    for (int u = 0; u < kPlanBatch; ++u) pos[u] = e[u] >= 0 ? atomicAdd(&fill[e[u]], 1) : -1;
-#pragma unroll
-    for (int u = 0; u < kPlanBatch; ++u) {
-      const int r = base + u * nthr + static_cast<int>(threadIdx.x);
-      if (r >= R) continue;
-      if (e[u] < 0) {   // a finished row's slot: no expert row
-        dest[r] = -1;
-        continue;
+  if (blockIdx.x == 0) {
+    for (int e = threadIdx.x; e < E; e += kPlanThreads) {
+      const int r1 = off[e] + tot[e];
+      int k = toff[e];
+      for (int r0 = off[e]; r0 < r1; r0 += bm) {
+        MoeTile tl;
+        tl.expert = e;
+        tl.row0 = r0;
+        tl.row1 = min(r0 + bm, r1);
+        tl.pad = 0;
+        tiles[k++] = tl;
       }
-      const int q = off[e[u]] + pos[u];
-      if (in_lds) src_lds[q] = r / topk;
-      else row_src[q] = r / topk;
-      dest[r] = q;
     }
   }
-  // Written out in order: scattered 4-byte stores from one workgroup (a
-  // cache line per lane) cost more than the LDS round trip.
-  if (in_lds) {
-    __syncthreads();
-    const int rows = off[E - 1] + cnt[E - 1];
-    for (int i = threadIdx.x; i < rows; i += nthr) row_src[i] = src_lds[i];
+  auto place = [&](int r, int e, int lp) {
+    if (e < 0) {   // a finished row's slot: no expert row
+      dest[r] = -1;
+      return;
+    }
+    const int q = off[e] + pre[e] + lp;
+    dest[r] = q;
+    row_src[q] = r / topk;
+  };
+  for (int w = w0; w < w1; ++w) {
+    const int r0 = w * rows_per, r1 = min(R, r0 + rows_per);
+    if (w == w0) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (e_pre[k] != -2) place(w0 * rows_per + k * kPlanThreads + static_cast<int>(threadIdx.x), e_pre[k], l_pre[k]);
+    } else {
+      for (int r = r0 + static_cast<int>(threadIdx.x); r < r1; r += kPlanThreads) place(r, ids[r], lpos[r]);
+    }
+    if (w + 1 < w1) {
+      __syncthreads();
+      for (int e = threadIdx.x; e < E; e += kPlanThreads) pre[e] += hist[static_cast<size_t>(w) * E + e];
+      __syncthreads();
+    }
   }
 }
 
@@ -391,10 +475,15 @@ hipError_t run_moe(const MoeArgs &a, hipStream_t s) {
   const int bm = use_dma ? CfgMoeDma::BM : kMoeBM;
   const int max_tiles = (R + bm - 1) / bm + a.E;
 
-  hipLaunchKernelGGL(k_moe_route, dim3((a.T + 3) / 4), dim3(256), 0, s, a.logits, a.sel_logits,
-                     a.finished, a.T, a.E, a.topk, a.renorm, ids, wts);
-  hipLaunchKernelGGL(k_moe_plan, dim3(1), dim3(1024), 0, s, ids, R, a.E, a.topk, bm, tiles, ntiles,
-                     row_src, dest);
+  int32_t *lpos = reinterpret_cast<int32_t *>(ws + L.lpos);
+  int32_t *hist = reinterpret_cast<int32_t *>(ws + L.hist);
+  const int nw = (a.T + kRouteTokens - 1) / kRouteTokens;
+  const int nplan = nw < kPlanBlocks ? nw : kPlanBlocks;
+  const int per = (nw + nplan - 1) / nplan;
+  hipLaunchKernelGGL(k_moe_route, dim3(nw), dim3(64 * kRouteTokens), 0, s, a.logits, a.sel_logits,
+                     a.finished, a.T, a.E, a.topk, a.renorm, ids, wts, lpos, hist);
+  hipLaunchKernelGGL(k_moe_plan, dim3((nw + per - 1) / per), dim3(kPlanThreads), 0, s, ids, lpos,
+                     hist, R, a.E, a.topk, nw, per, bm, tiles, ntiles, row_src, dest);
 
   static std::atomic<uint64_t> attr_fc1{0}, attr_fc2{0};
   if (hipError_t e = set_lds_limit_once(k_moe_gemm<ACT, kMoeFc1>, CfgMoe::LDS, attr_fc1); e != hipSuccess)
