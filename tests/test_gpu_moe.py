@@ -2,6 +2,8 @@
 
 Routing ids must equal the oracle's exactly (same fp32 comparisons, ties to
 the lower expert); weights and outputs within tolerance."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -149,6 +151,37 @@ def test_moe_route_neg_inf_selection_logits():
     ref, rids, rw = oracle.moe(p.x, p.logits, p.w1, p.s1, p.z1, p.w2, p.s2, p.z2, k, 64, BF16,
                                sel_logits=sel)
     assert all(len(set(r)) == k for r in ids.tolist())
+    assert np.array_equal(ids, rids)
+    np.testing.assert_allclose(w, rw, rtol=2e-6, atol=1e-7)
+    assert rel_err(out, ref) <= TOL[BF16]
+
+
+@pytest.mark.parametrize("E,k", [(65, 6), (96, 8), (128, 6), (200, 16), (256, 64), (64, 64)])
+def test_moe_route_many_experts(E, k):
+    # Routing over 65 .. 256 experts (a lane holds up to four, the last slot
+    # partly filled) and top-k up to 64 (every expert of 64): ids equal the
+    # oracle's, weights and outputs within tolerance.
+    p = si.moe_problem(40, 128, 128, E, k, 64, tag="moe-wide")
+    out, ids, w = run_moe_ex(p, None, None, None, None, True)
+    ref, rids, rw = oracle.moe(p.x, p.logits, p.w1, p.s1, p.z1, p.w2, p.s2, p.z2, k, 64, BF16)
+    assert all(len(set(r)) == k for r in ids.tolist())
+    assert np.array_equal(ids, rids)
+    np.testing.assert_allclose(w, rw, rtol=2e-6, atol=1e-7)
+    assert rel_err(out, ref) <= TOL[BF16]
+
+
+@pytest.mark.parametrize("E", [64, 200])
+def test_moe_route_ties_go_to_the_lower_expert(E):
+    # Logits on a coarse grid (many exact ties, -0.0 beside 0.0): every
+    # choice takes the lowest expert id among equal values, as the oracle's
+    # strict-greater scan does, also across a lane's four slots.
+    T, k = 64, 6
+    p = si.moe_problem(T, 128, 128, E, k, 64, tag="moe-ties")
+    lg = np.round(p.logits * 2.0).astype(np.float32) / 2.0
+    lg[lg == 0.0] = np.where(np.arange((lg == 0.0).sum()) % 2 == 0, 0.0, -0.0).astype(np.float32)
+    p = dataclasses.replace(p, logits=lg)
+    out, ids, w = run_moe_ex(p, None, None, None, None, True)
+    ref, rids, rw = oracle.moe(p.x, p.logits, p.w1, p.s1, p.z1, p.w2, p.s2, p.z2, k, 64, BF16)
     assert np.array_equal(ids, rids)
     np.testing.assert_allclose(w, rw, rtol=2e-6, atol=1e-7)
     assert rel_err(out, ref) <= TOL[BF16]
