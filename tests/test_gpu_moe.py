@@ -59,12 +59,14 @@ def test_moe_small_full(T, H, I, E, k, g, moe_tile):
     check(p)
 
 
-def test_moe_more_rows_than_the_plan_stages_in_lds(moe_tile):
-    # 3000 tokens x top-6 = 18000 expert rows: past the 16384 rows whose
-    # row -> token map the plan assembles in LDS, so the plan scatters it to
-    # memory directly (checked on a sample of tokens, routing in full).
+def test_moe_more_routing_workgroups_than_plan_workgroups(moe_tile):
+    # 3000 tokens x top-6 = 18000 expert rows from 188 routing workgroups of
+    # 16 tokens: more than the plan's 128 workgroups, so each plan workgroup
+    # places the rows of two routing workgroups (the second from counts
+    # carried over from the first; checked on a sample of tokens, routing in
+    # full).
     p = si.moe_problem(3000, 256, 256, 8, 6, 64, tag="moe-many-rows")
-    assert p.tokens * p.topk > 16384
+    assert -(-p.tokens // 16) > 128
     toks = np.unique(np.concatenate([[0, 1, 2999], np.random.default_rng(7).integers(0, 3000, 256)]))
     check(p, tokens=toks)
 
