@@ -122,7 +122,13 @@ using CfgD64 = DmaCfg<2, 4, 256, 64>;   // 64 x 256 tile, 8 waves of 32x64
 using CfgD128 = DmaCfg<2, 4, 256, 128>; // 128 x 256 tile, 8 waves of 64x64
 using CfgL = TileCfg<256, 128, 4, 2>;   // 8 waves, 64x64 per wave
 using CfgM = TileCfg<128, 128, 2, 2>;   // 4 waves, 64x64 per wave
-using CfgS = TileCfg<64, 64, 2, 2>;     // 4 waves, 32x32 per wave
+// The 64 x 64 tile runs as two K groups of 4 waves (each 32 x 32 per wave,
+// half of the K steps, accumulators added through LDS at the end): twice
+// the waves for the shapes that leave CUs idle.  Measured against one group:
+// M = 512, N = 3072, K = 2048 26.9 -> 25.6 us; M = 128 (two K slices)
+// 18.2 -> 15.1 us, M = 64 17.2 -> 14.0 us; W8A16 M = 128, N = 3584 20.4 ->
+// 19.4 us; four groups were slower (one workgroup per CU).
+using CfgS = TileCfg<64, 64, 2, 2, 2>;
 
 // K slices of one launch: partials in `part` (nullptr: no split).
 struct Split {

@@ -65,19 +65,26 @@ struct TileProblem {
   int kseg;
 };
 
-template <int BM_, int BN_, int WM_, int WN_>
+// KG > 1: the workgroup runs KG groups of WM x WN waves on the same tile,
+// group g on the g-th of KG consecutive parts of the K steps, each with its
+// own LDS stages; at the end the groups' accumulators are added through LDS
+// (group 0 first, then 1, ...) and group 0 writes the tile.  Twice the waves
+// on half the steps each, for problems with too few tiles to fill the CUs.
+template <int BM_, int BN_, int WM_, int WN_, int KG_ = 1>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, KG = KG_;
   static constexpr int BK = 64;
-  static constexpr int NTHR = 64 * WM * WN;
+  static constexpr int NTG = 64 * WM * WN;             // threads of one K group
+  static constexpr int NTHR = NTG * KG;
   static constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
   static constexpr int TM = WTM / 32, TN = WTN / 32;  // 32x32 subtiles per wave
-  static constexpr int A_CHUNKS = BM * 8 / NTHR;      // 16-byte A chunks per thread per step
-  static constexpr int B_SLOTS = BN * 4 / NTHR;       // 8-byte code runs per thread (w4)
-  static constexpr int B_RUNS8 = BN * 8 / NTHR;       // 8-byte code runs per thread (w8)
+  static constexpr int A_CHUNKS = BM * 8 / NTG;       // 16-byte A chunks per thread per step
+  static constexpr int B_SLOTS = BN * 4 / NTG;        // 8-byte code runs per thread (w4)
+  static constexpr int B_RUNS8 = BN * 8 / NTG;        // 8-byte code runs per thread (w8)
   static constexpr int STAGE = (BM + BN) * 128;       // bytes per LDS stage
-  static constexpr int LDS = 2 * STAGE;
+  static constexpr int LDS = KG * 2 * STAGE;
   static_assert(A_CHUNKS >= 1 && B_SLOTS >= 1, "tile too small for the thread count");
+  static_assert((KG - 1) * WM * WN * TM * TN * 16 * 64 * 4 <= LDS, "K-group partials fit the LDS");
 };
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
@@ -132,15 +139,26 @@ __device__ __forceinline__ u32x4 dequant_run_w8(uint32_t lo, uint32_t hi, float 
 template <class Cfg, int ACT, int WBITS, int MODE, bool GS8 = false>
 __device__ __forceinline__ void tile_gemm(const TileProblem &p, int tile_m, int tile_n,
                                           char *lds, int slice = 0) {
-  constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, NTHR = Cfg::NTHR;
+  constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, NTHR = Cfg::NTG;   // threads per K group
   constexpr int TM = Cfg::TM, TN = Cfg::TN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int GW = Cfg::WM * Cfg::WN;   // waves per K group
+  const int lane = threadIdx.x & 63;
+  const int kg = Cfg::KG > 1 ? static_cast<int>(threadIdx.x >> 6) / GW : 0;   // K group
+  const int wave = (threadIdx.x >> 6) - kg * GW, tid = threadIdx.x - kg * NTHR;
   const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
   const int K = p.K;
-  // This workgroup's 64-k steps: [s0, s1) (all of K unless split).
-  const int s0 = p.part ? slice * p.kseg : 0;
-  const int s1 = p.part ? min(K / BK, s0 + p.kseg) : K / BK;
-  const int nsteps = s1 - s0;
+  // This workgroup's 64-k steps: [sa, sb) (all of K unless split), and this K
+  // group's part of them: [s0, s0 + nmine).  Every group runs `nsteps` loop
+  // steps (the barriers are the workgroup's), the last group possibly a few
+  // without matrix-core work when the steps do not divide evenly; those load
+  // and stage a real step into the idle LDS stage.
+  const int sa = p.part ? slice * p.kseg : 0;
+  const int sb = p.part ? min(K / BK, sa + p.kseg) : K / BK;
+  const int nsteps = (sb - sa + Cfg::KG - 1) / Cfg::KG;
+  const int s0 = min(sa + kg * nsteps, sb - 1);
+  const int nmine = max(0, min(nsteps, sb - sa - kg * nsteps));
+  const int slast = s0 + max(nmine, 1) - 1;   // last real step of this group (a valid step)
+  lds += kg * 2 * Cfg::STAGE;
 
   // ---- row sources for A -------------------------------------------------
   int row_lo, row_hi;         // valid global row range of this tile
@@ -324,9 +342,9 @@ __device__ __forceinline__ void tile_gemm(const TileProblem &p, int tile_m, int 
   // the LDS stores (and the waits on their loads) above the matrix-core work
   // and sink the new loads below it.
   auto body = [&](int step, Regs &nxt1, Regs &nxt2) {   // step relative to s0
-    gload(s0 + min(step + 2, nsteps - 1), nxt2);
+    gload(min(s0 + step + 2, slast), nxt2);
     __builtin_amdgcn_sched_barrier(0);
-    compute(step & 1);
+    if (Cfg::KG == 1 || step < nmine) compute(step & 1);
     __builtin_amdgcn_sched_barrier(0);
     lstore((step + 1) & 1, nxt1);
     __builtin_amdgcn_sched_barrier(0);
@@ -335,7 +353,7 @@ __device__ __forceinline__ void tile_gemm(const TileProblem &p, int tile_m, int 
 
   Regs r0, r1;
   gload(s0, r0);
-  gload(s0 + min(1, nsteps - 1), r1);
+  gload(min(s0 + 1, slast), r1);
   lstore(0, r0);
   __syncthreads();
   // Unrolled by two so the register sets are named statically: at an even
@@ -347,6 +365,34 @@ __device__ __forceinline__ void tile_gemm(const TileProblem &p, int tile_m, int 
     body(step + 1, r0, r1);
   }
   if (step < nsteps) body(step, r1, r0);
+
+  if constexpr (Cfg::KG > 1) {
+    // Add the K groups' accumulators: groups 1 .. KG - 1 leave theirs in LDS
+    // (every stage is free: the last step ended with a barrier), group 0
+    // adds them in group order and goes on to the epilogue.
+    constexpr int PERW = TM * TN * 16 * 64;   // floats per wave
+    float *red = reinterpret_cast<float *>(lds - kg * 2 * Cfg::STAGE);
+    if (kg > 0) {
+      float *dst = red + ((kg - 1) * GW + wave) * PERW;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int jn = 0; jn < TN; ++jn)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) dst[((i * TN + jn) * 16 + v) * 64 + lane] = acc[i][jn][v];
+    }
+    __syncthreads();
+    if (kg > 0) return;
+    for (int g = 1; g < Cfg::KG; ++g) {
+      const float *src = red + ((g - 1) * GW + wave) * PERW;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int jn = 0; jn < TN; ++jn)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[i][jn][v] += src[((i * TN + jn) * 16 + v) * 64 + lane];
+    }
+  }
 
   // ---- epilogue -----------------------------------------------------------
   // 32x32 accumulator: value v of lane -> row 8*(v/4) + 4*(lane/32) + v%4,
