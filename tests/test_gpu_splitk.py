@@ -103,3 +103,28 @@ def test_split_threshold_by_tile_count(n, split):
     p = si.w4_exact_problem(m, n, k, g, seed=n, dtype=BF16, bias_dtype=FP16)
     exp = expected(oracle.gemm_w4(p.A, p.packed, p.scale, p.zero, g, BF16, p.bias, FP16), BF16)
     assert np.array_equal(run_w4(p), exp)
+
+
+# -- the 64 x 64 tile's two K groups on uneven step counts ------------------------
+
+@pytest.mark.parametrize("k,slices", [(64, 1), (192, 1), (576, 1), (576, 2), (576, 3), (1088, 2)])
+def test_k_groups_uneven_steps_w8_exact(k, slices):
+    # The 64 x 64 tile splits each slice's 64-k steps between two K groups of
+    # waves: K = 64 leaves the second group no step, 192 and 576 (3 and 9
+    # steps) give it one fewer than the first; with 8-step slices 576 splits
+    # 8 + 1 and 1088 (17 steps) 16 + 1, so a one-step slice again leaves the
+    # second group idle.  Integer-exact inputs: bitwise equal to the oracle.
+    p = si.w8_exact_problem(40, 192, k, seed=k + slices, dtype=FP16, bias_dtype=FP16)
+    Cref = oracle.gemm_w8(p.A, p.codes, p.scale, -1, FP16, p.bias, FP16)
+    qg.set_override(prefill_tile="S")
+    qg.set_override(splitk=slices)
+    assert np.array_equal(run_w8(p), expected(Cref, FP16))
+
+
+@pytest.mark.parametrize("k", [128, 384])
+def test_k_groups_w4_short_k_exact(k):
+    # W4 with 2 and 6 steps: one and three steps per K group.
+    p = si.w4_exact_problem(70, 128, k, 64, seed=k, dtype=BF16, bias_dtype=FP16)
+    Cref = oracle.gemm_w4(p.A, p.packed, p.scale, p.zero, 64, BF16, p.bias, FP16)
+    qg.set_override(prefill_tile="S")
+    assert np.array_equal(run_w4(p), expected(Cref, BF16))
