@@ -313,7 +313,9 @@ qg_status qembed_w8(const int32_t *ids, int tokens, const int8_t *table, int lay
  *   topk_ids_out  optional device int32 [tokens, topk] (NULL to skip)
  *   topk_w_out    optional device fp32 [tokens, topk] (NULL to skip)
  * Routing: the topk largest logits per row, in descending order, ties to
- * the lower expert id; weights = softmax over the selected logits only.
+ * the lower expert id (-0.0 equals 0.0; a NaN ranks above +inf, or below
+ * -inf when its sign bit is set); weights = softmax over the selected
+ * logits only.
  * out[t] = sum_j w[t, j] * fc2_e(silu(gate) * up), e = ids[t, j],
  * silu(x) = x / (1 + exp(-x)); the activation is rounded to act_dtype before
  * fc2, the combine sums in fp32 in rank order.
