@@ -323,7 +323,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void k
   const int nb = K >> 7, ngroups = K / G, ntiles = N >> 4;
   const int arow = 2 * K + 16;           // padded LDS row (bytes)
   const int Mr = M < 16 ? M : 16;
-  float *sS = reinterpret_cast<float *>(lds + Mr * arow);   // [ngroups][16]
+  // LDS: rows 0 .. Mr - 1 of A, then a row of zeros (read by the lanes of
+  // the padding rows m >= M, so every fragment read is unconditional), then
+  // the group sums.
+  float *sS = reinterpret_cast<float *>(lds + (Mr + 1) * arow);   // [ngroups][16]
 
   const int total_waves = gridDim.x * (blockDim.x >> 6);
   const int nseg = nb / SEG;
@@ -373,6 +376,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void k
   constexpr int LPG = G / 8;             // lanes per group
   for (int e = threadIdx.x; e < ngroups * 16; e += blockDim.x)
     if ((e & 15) >= Mr) sS[e] = 0.f;
+  for (int c = threadIdx.x; c < (K >> 3); c += blockDim.x)
+    *reinterpret_cast<u32x4 *>(lds + Mr * arow + c * 16) = u32x4{0u, 0u, 0u, 0u};
   for (int base = 0; base < Mr * (K >> 3); base += blockDim.x) {
     const int c = base + static_cast<int>(threadIdx.x);
     const bool ok = c < Mr * (K >> 3);
@@ -394,8 +399,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void k
   }
   __syncthreads();
 
-  const bool active = nl < Mr;           // this lane's activation row exists
-  const char *arow_p = lds + (active ? nl : 0) * arow + 16 * j;
+  const char *arow_p = lds + (nl < Mr ? nl : Mr) * arow + 16 * j;   // padding rows: the zero row
+  const W4Consts wc = w4_consts<ACT>();
 
   // One item is live at a time: after an item's math, the loads of the next
   // one (the next segment of this tile, else the first of the wave's next
@@ -413,9 +418,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void k
           for (int tt = 0; tt < TPG; ++tt) {
             const int t = h * TPG + tt;
             const int k = (kb0 + b) * 128 + 32 * t;          // + 8 j via arow_p
-            u32x4 af = {0u, 0u, 0u, 0u};
-            if (active) af = *reinterpret_cast<const u32x4 *>(arow_p + 2 * k);
-            d = mfma16x16x32<ACT>(af, w4_word_to_operand<ACT>(cur.bw[b][t]), d);
+            const u32x4 af = *reinterpret_cast<const u32x4 *>(arow_p + 2 * k);
+            d = mfma16x16x32<ACT>(af, w4_word_to_operand<ACT>(cur.bw[b][t], wc), d);
           }
           const int gl = b * GPB + h, g = kb0 * GPB + gl;
           const uint32_t swd = cur.sw[gl >> 1], zwd = cur.zw[gl >> 1];
@@ -472,7 +476,7 @@ template <int ACT, int G, int R>
 hipError_t launch_stream(const GemmArgs &a, hipStream_t s) {
   constexpr int SEG = 4;
   const int ntiles = a.N >> 4;
-  const size_t lds = static_cast<size_t>(a.M) * (2 * a.K + 16) + static_cast<size_t>(a.K / G) * 64;
+  const size_t lds = static_cast<size_t>(a.M + 1) * (2 * a.K + 16) + static_cast<size_t>(a.K / G) * 64;
   auto kern = k_decode_w4_stream<ACT, G, SEG, R>;
   // One resident pass: 5 workgroups of 4 waves per CU on 256 CUs.
   int grid = (ntiles + 3) / 4;
@@ -499,7 +503,7 @@ hipError_t launch_decode_w4(const GemmArgs &a, hipStream_t s) {
   const bool aligned16 = !special &&
       ((reinterpret_cast<uintptr_t>(a.S) | reinterpret_cast<uintptr_t>(a.Z)) & 15) == 0 &&
       ((a.K / a.group) % 8) == 0;
-  const bool fits = static_cast<size_t>(a.M) * (2 * static_cast<size_t>(a.K) + 16) +
+  const bool fits = static_cast<size_t>(a.M + 1) * (2 * static_cast<size_t>(a.K) + 16) +
                         static_cast<size_t>(a.K / a.group) * 64 <= 64 * 1024;
   if (a.M <= 2 && ntiles >= 4096 && aligned16 && fits && nb % 4 == 0) {
     if (a.act == kBF16)
