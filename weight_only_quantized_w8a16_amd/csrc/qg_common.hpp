@@ -149,6 +149,14 @@ __device__ __forceinline__ u32x4 w4_word_to_operand(uint32_t w, W4Consts c) {
   r.w = ((w >> 12) & c.mask) | c.magic;
   return r;
 }
+// silu(g) * u = g / (1 + exp(-g)) * u with the hardware reciprocal (about
+// one ulp of fp32) instead of an IEEE-rounded division, whose scaling and
+// fix-up steps cost about ten instructions per value; the result is rounded
+// to the 16-bit activation type right after.  exp(-g) overflowing to +inf
+// gives 0 * g, the limit.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
 // Offset that w4_word_to_operand adds to each code.
 template <int DT>
 constexpr float w4_operand_offset() { return DT == kFP16 ? 1024.0f : 128.0f; }

@@ -529,7 +529,7 @@ __device__ __forceinline__ void tile_gemm_dma(const TileProblem &p, int tile_m, 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float g = acc[i][0][4 * q + e] + bg[q][e], u = acc[i][1][4 * q + e] + bu[q][e];
-          v[e] = g / (1.0f + __expf(-g)) * u;
+          v[e] = silu_mul(g, u);
         }
         *reinterpret_cast<u32x2 *>(stg + row_in * 80 + (8 * q + 4 * khalf) * 2) =
             u32x2{pack2<ACT>(v[0], v[1]), pack2<ACT>(v[2], v[3])};

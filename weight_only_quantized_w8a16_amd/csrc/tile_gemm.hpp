@@ -430,7 +430,7 @@ __device__ __forceinline__ void tile_gemm(const TileProblem &p, int tile_m, int 
           const int r = row_lo + wm * Cfg::WTM + 32 * i + 8 * (v >> 2) + 4 * khalf + (v & 3);
           if (r < row_hi) {
             const float g = acc[i][jn][v] + bg, u = acc[i][jn + HALF][v] + bu;
-            const float a = g / (1.0f + __expf(-g)) * u;
+            const float a = silu_mul(g, u);
             p.C[static_cast<size_t>(r) * p.N + col] = f32_to_bits<ACT>(a);
           }
         }
