@@ -173,7 +173,9 @@ def test_w4_integer_exact(m, n, k, group, path, dtype):
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 16, 64), (3, 64, 448), (16, 3584, 3584), (40, 128, 192),
-                                   (130, 256, 512)])
+                                   (130, 256, 512),
+                                   # decode with up to 16 waves over K: 28, 17 and 12 chunks
+                                   (1, 3584, 3584), (4, 48, 1088), (2, 32, 1536)])
 @pytest.mark.parametrize("path", ["decode", "prefill"])
 @pytest.mark.parametrize("dtype", [FP16, BF16])
 def test_w8_integer_exact(m, n, k, path, dtype):
@@ -188,6 +190,7 @@ def test_w8_integer_exact(m, n, k, path, dtype):
 @pytest.mark.parametrize("m,n,k,group", [
     (1, 16, 128, 64), (3, 64, 448, 64), (16, 3584, 3584, 128), (40, 128, 640, 128),
     (130, 256, 512, 64), (300, 512, 640, 128),
+    (1, 3584, 3584, 128), (4, 48, 1088, 64), (2, 32, 1536, 128),
 ])
 @pytest.mark.parametrize("path", ["decode", "prefill"])
 @pytest.mark.parametrize("dtype", [FP16, BF16])

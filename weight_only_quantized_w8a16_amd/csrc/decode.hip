@@ -109,7 +109,8 @@ __device__ __forceinline__ float group_value(const Groups<NG> &g, int i) {
 }  // namespace
 
 // Launch bounds follow the plan: BPW 1 runs up to 16 waves, BPW 2 up to 8,
-// BPW 4 up to 4, so the register budget grows with the chunk size.
+// BPW 4 up to 4, so the register budget grows with the chunk size (the int8
+// kernel with one tile per workgroup runs up to 16 waves at any BPW).
 template <int BPW>
 constexpr int decode_threads() { return BPW == 1 ? 1024 : (BPW == 2 ? 512 : 256); }
 
@@ -216,9 +217,10 @@ __global__ __launch_bounds__(decode_threads<BPW>()) void k_decode_w4(const uint1
 // GS: 0 = one scale per channel, applied to the finished sum; 64 or 128 =
 // one scale per (channel, K-group), applied to each 64-k block's partial
 // product (the lane's channel is its output column, so the scale is a
-// per-lane value).
-template <int ACT, int BPW, int NT, int GS>
-__global__ __launch_bounds__(decode_threads<BPW>()) void k_decode_w8(const uint16_t *__restrict__ A,
+// per-lane value).  EARLY (up to 4 rows): every load of a chunk is issued
+// before its first wait.
+template <int ACT, int BPW, int NT, int GS, bool EARLY>
+__global__ __launch_bounds__(NT == 1 ? 1024 : decode_threads<BPW>()) void k_decode_w8(const uint16_t *__restrict__ A,
                                                    const u32x4 *__restrict__ Bt,
                                                    const uint16_t *__restrict__ S,
                                                    const uint16_t *__restrict__ bias, int bias_dt,
@@ -250,6 +252,13 @@ __global__ __launch_bounds__(decode_threads<BPW>()) void k_decode_w8(const uint1
         if constexpr (GS > 0)
           sb[i][b] = S[static_cast<size_t>((nt0 + i) * 16 + nl) * (K / GS) + (kb0 + b) * 64 / GS];
       }
+    // With EARLY all of the chunk's loads go out before its first wait; the
+    // scheduler would otherwise split them over two or three round trips.
+    // Measured on MI355X at K = 3584, N = 18944: M = 1 13.9 -> 13.4 us per
+    // channel, 15.2 -> 14.4 us with group 128; at M = 16 with group 128 it
+    // cost 4.6 % (20.8 -> 21.7 us), so the many-row forms keep the
+    // scheduler's order.
+    if constexpr (EARLY) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NT; ++i)
 #pragma unroll
@@ -551,12 +560,27 @@ hipError_t launch_decode_w4(const GemmArgs &a, hipStream_t s) {
 hipError_t launch_decode_w8(const GemmArgs &a, hipStream_t s) {
   const int nb = a.K >> 6, ntiles = a.N >> 4;
   DecodePlan p = plan_decode(nb, ntiles);
+  // One tile per workgroup (a few hundred tiles or fewer) and up to 4 rows:
+  // up to 16 waves share K, so each wave runs half as many chunks, each one
+  // a memory round trip.  Measured on MI355X at K = 3584, N = 3584: M = 1
+  // 5.38 -> 4.80 us (group 128: 5.41 -> 5.04), M = 4 5.46 -> 4.98; at M = 16
+  // and with two tiles per workgroup (N = 18944) no gain or a loss.
+  if (p.nt == 1 && a.M <= 4) {
+    const int nch = nb / p.bpw;
+    p.waves = nch < 16 ? nch : 16;
+  }
   dim3 grid(ntiles / p.nt), block(64 * p.waves);
   size_t lds = static_cast<size_t>(p.waves) * p.nt * 256 * sizeof(float);
   const u32x4 *B = static_cast<const u32x4 *>(a.B);
-#define QG_DEC8G(ACT_, BPW_, NT_, GS_)                                                             \
-  hipLaunchKernelGGL((k_decode_w8<ACT_, BPW_, NT_, GS_>), grid, block, lds, s, a.A, B, a.S, a.bias, \
-                     a.bias_dt, a.C, a.M, a.N, a.K)
+#define QG_DEC8G(ACT_, BPW_, NT_, GS_)                                                                  \
+  do {                                                                                                  \
+    if (a.M <= 4)                                                                                       \
+      hipLaunchKernelGGL((k_decode_w8<ACT_, BPW_, NT_, GS_, true>), grid, block, lds, s, a.A, B, a.S,  \
+                         a.bias, a.bias_dt, a.C, a.M, a.N, a.K);                                       \
+    else                                                                                                \
+      hipLaunchKernelGGL((k_decode_w8<ACT_, BPW_, NT_, GS_, false>), grid, block, lds, s, a.A, B, a.S, \
+                         a.bias, a.bias_dt, a.C, a.M, a.N, a.K);                                       \
+  } while (0)
 #define QG_DEC8(ACT_, BPW_, NT_)                                \
   do {                                                          \
     if (a.group == 64) QG_DEC8G(ACT_, BPW_, NT_, 64);           \
