@@ -319,7 +319,7 @@ __global__ __launch_bounds__(256) void k_w8a8_reduce(W8A8Problem p, int nsplit) 
 // one pass scales and stores.
 // ---------------------------------------------------------------------------
 template <int OUT, int NT, int KC>
-__global__ __launch_bounds__(512) void k_w8a8_decode(W8A8Problem p) {
+__global__ __launch_bounds__(NT == 1 ? 1024 : 512) void k_w8a8_decode(W8A8Problem p) {
   extern __shared__ int red[];   // [waves][NT][256]
   constexpr int NP = KC / 64;    // pieces per lane per chunk
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
@@ -460,13 +460,17 @@ size_t w8a8_workspace_bytes(int m, int n, int k) {
 // Two tiles per workgroup and 256-k chunks once there are many channel tiles
 // (more bytes in flight per wave); measured on MI355X at K = 3584: N = 18944,
 // m = 1: 23 -> 16 us against one tile and 128-k chunks read as 32 contiguous
-// bytes per lane (half-line loads), N = 3584 unchanged within noise.
+// bytes per lane (half-line loads), N = 3584 unchanged within noise.  With
+// one tile per workgroup up to 16 waves share K (half the chunks per wave,
+// each a memory round trip): N = 3584, m = 1 5.9 -> 4.9 us, m = 16
+// 6.3 -> 6.2 us; the two-tile form stays at 8 (16 measured 9-11 % slower).
 template <int OUT>
 hipError_t launch_w8a8_decode(const W8A8Problem &p, hipStream_t s) {
   const int ntiles = p.N >> 4;
   const bool wide = ntiles >= 512 && ntiles % 2 == 0 && p.K % 256 == 0;
   const int nchunks = wide ? p.K >> 8 : p.K >> 7;
-  const int waves = nchunks < 8 ? nchunks : 8;
+  const int maxw = wide ? 8 : 16;
+  const int waves = nchunks < maxw ? nchunks : maxw;
   const size_t lds = static_cast<size_t>(waves) * (wide ? 2 : 1) * 256 * sizeof(int);
   if (wide)
     hipLaunchKernelGGL((k_w8a8_decode<OUT, 2, 256>), dim3(ntiles / 2), dim3(64 * waves), lds, s, p);
