@@ -85,7 +85,9 @@ int qg_version(void);
  * spec is a comma-separated list of key=value pairs:
  *   path=auto|decode|prefill        the GEMM path (else by m: decode for
  *                                   m <= 16)
- *   prefill_tile=auto|X|D8|D8N|D64|D128|L|M|S   the prefill tile
+ *   prefill_tile=auto|X|D8|D8N|D64|D128|L|M|S|P256|P128|P64   the prefill
+ *                                   tile (P: dequantize-then-dense, which
+ *                                   needs n * k * 2 bytes of workspace)
  *   splitk=<n>                      prefill K slices (1: none), n >= 1
  *   moe_tile=auto|S                 S: the MoE on the 128 x 128 tile
  *   w8a8_tile=auto|T256|T256N|T128|T64   the W8A8 tile (also for m <= 16)
@@ -211,11 +213,15 @@ qg_status qdequant_w8(const int8_t *B_tiled, const void *scales, void *W_out, in
  *   m is any value >= 0.  Accumulation is fp32; C = RNE(acc + bias).
  *   workspace: optional device scratch, 256-byte aligned.  When it holds at
  *   least qgemm_workspace_size() bytes (> 0 only for problems the prefill
- *   path splits along K: today the 64 x 64 tile at m <= 128 with k >= 2048)
- *   the K slices write fp32 partials [slices, m, n] there and one more
- *   launch sums them in slice order, then scales, adds bias and rounds;
- *   with less (or NULL) the same call runs unsplit.  Calls that share a
- *   workspace must not overlap.
+ *   path splits along K -- today the 64 x 64 tile at m <= 128 with k >= 2048
+ *   -- or runs dequantize-then-dense) the K slices write fp32 partials
+ *   [slices, m, n] there and one more launch sums them in slice order, then
+ *   scales, adds bias and rounds; or the whole weight is dequantized there
+ *   (n x k values in the activation type, vllm-omni cpu_int4.py: the int4
+ *   linear's dequantize-then-dense path for batches of at least
+ *   dequant_threshold rows) and one dense tile runs on it, bit-equal to the
+ *   unsplit fused tiles.  With less (or NULL) the same call runs unsplit on
+ *   the fused tiles.  Calls that share a workspace must not overlap.
  * ---------------------------------------------------------------------- */
 size_t qgemm_workspace_size(int m, int n, int k, int group_size, int weight_bits);
 

@@ -206,7 +206,7 @@ def test_w8_grouped_integer_exact(m, n, k, group, path, dtype):
     assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:4].tolist()}"
 
 
-@pytest.mark.parametrize("tile", ["D8", "D8N", "D64", "D128", "X", "L", "M", "S"])
+@pytest.mark.parametrize("tile", ["D8", "D8N", "D64", "D128", "X", "L", "M", "S", "P256", "P128", "P64"])
 @pytest.mark.parametrize("group", [64, 128])
 def test_prefill_tiles_w8_grouped_integer_exact(tile, group):
     p = si.w8_exact_problem(300, 512, 1024, seed=group, dtype=BF16, bias_dtype=FP16, group=group)
@@ -275,7 +275,7 @@ def test_w4_scale_forms_integer_exact(m, n, k, path, group, zeros):
     assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:4].tolist()}"
 
 
-@pytest.mark.parametrize("tile", ["D8", "D8N", "D64", "D128", "X", "L", "M", "S"])
+@pytest.mark.parametrize("tile", ["D8", "D8N", "D64", "D128", "X", "L", "M", "S", "P256", "P128", "P64"])
 @pytest.mark.parametrize("group,zeros", FORMS)
 def test_prefill_tiles_w4_scale_forms_exact(tile, group, zeros):
     # scale-only groups keep the direct-load tiles (their zero windows read an
@@ -324,7 +324,7 @@ def test_empty_m_is_noop():
 
 # -- every prefill tile configuration, forced, on ragged M: bit-exact --------------
 
-@pytest.mark.parametrize("tile", ["X", "L", "M", "S"])
+@pytest.mark.parametrize("tile", ["X", "L", "M", "S", "P256", "P128", "P64"])
 @pytest.mark.parametrize("m", [1, 77, 300])
 def test_prefill_tiles_integer_exact(tile, m):
     n, k, group = 512, 640, 128
@@ -335,7 +335,7 @@ def test_prefill_tiles_integer_exact(tile, m):
     assert np.array_equal(got, _exact_expected(Cref, BF16))
 
 
-@pytest.mark.parametrize("tile", ["X", "L", "M", "S"])
+@pytest.mark.parametrize("tile", ["X", "L", "M", "S", "P256", "P128", "P64"])
 def test_prefill_tiles_w8_integer_exact(tile):
     p = si.w8_exact_problem(200, 256, 576, seed=9, dtype=FP16, bias_dtype=FP16)
     Cref = oracle.gemm_w8(p.A, p.codes, p.scale, -1, FP16, p.bias, FP16)
@@ -346,7 +346,7 @@ def test_prefill_tiles_w8_integer_exact(tile):
 
 @pytest.mark.parametrize("m,n,k", [(1, 256, 128), (300, 512, 640), (513, 768, 2048), (256, 256, 384)])
 @pytest.mark.parametrize("dtype", [BF16, FP16])
-@pytest.mark.parametrize("tile", ["D8", "D8N", "D64", "D128", "X"])
+@pytest.mark.parametrize("tile", ["D8", "D8N", "D64", "D128", "X", "P256", "P128", "P64"])
 @pytest.mark.parametrize("group", [64, 128])
 def test_prefill_dma_tile_integer_exact(tile, group, m, n, k, dtype):
     p = si.w4_exact_problem(m, n, k, group, seed=m + k, dtype=dtype, bias_dtype=FP16)
@@ -356,7 +356,7 @@ def test_prefill_dma_tile_integer_exact(tile, group, m, n, k, dtype):
     assert np.array_equal(got, _exact_expected(Cref, dtype))
 
 
-@pytest.mark.parametrize("tile", ["D8", "D8N", "D64", "D128", "X"])
+@pytest.mark.parametrize("tile", ["D8", "D8N", "D64", "D128", "X", "P256", "P128", "P64"])
 def test_prefill_dma_tile_w8_integer_exact(tile):
     p = si.w8_exact_problem(300, 512, 576, seed=4, dtype=FP16, bias_dtype=FP16)
     Cref = oracle.gemm_w8(p.A, p.codes, p.scale, -1, FP16, p.bias, FP16)
@@ -374,6 +374,84 @@ def test_prefill_dma_tile_odd_group_count_falls_back(tile):
     qg.set_override(prefill_tile=tile)
     got = to_bits(_run_w4(p, "prefill"))
     assert np.array_equal(got, _exact_expected(Cref, BF16))
+
+
+# -- dequantize-then-dense path ----------------------------------------------------
+
+DENSE_TILES = ["P256", "P128", "P64"]
+
+
+@pytest.mark.parametrize("tile", DENSE_TILES)
+@pytest.mark.parametrize("group,zeros", [(64, True), (128, True)] + FORMS)
+@pytest.mark.parametrize("dtype", [BF16, FP16])
+def test_dense_path_equals_fused_tile_bitwise_w4(tile, group, zeros, dtype):
+    # Random data: the dense tile accumulates the values the fused tile
+    # dequantizes into LDS in the same order (unsplit, one K group), so the
+    # two paths agree in every bit, ragged M included.
+    p = si.w4_problem(300, 512, 1024, group, tag="dense", dtype=dtype, bias_dtype=FP16)
+    if not zeros:
+        p.zero = None
+    qg.set_override(prefill_tile="D8")
+    fused = _run_w4(p, "prefill")
+    qg.set_override(prefill_tile=tile)
+    dense = _run_w4(p, "prefill")
+    assert torch.equal(fused.view(torch.int16), dense.view(torch.int16))
+
+
+@pytest.mark.parametrize("tile", DENSE_TILES)
+@pytest.mark.parametrize("group", [-1, 64, 128])
+@pytest.mark.parametrize("k", [1152, 1024])
+def test_dense_path_equals_fused_tile_bitwise_w8(tile, group, k):
+    # k % 256 == 0: the int8 dequant stages four code blocks in LDS; else one
+    # block per wave
+    p = si.w8_problem(130, 768, k, group=group, tag="dense8", dtype=FP16, bias_dtype=BF16)
+    qg.set_override(prefill_tile="D8")
+    fused = _run_w8(p, "prefill")
+    qg.set_override(prefill_tile=tile)
+    dense = _run_w8(p, "prefill")
+    assert torch.equal(fused.view(torch.int16), dense.view(torch.int16))
+
+
+@pytest.mark.parametrize("m,n,k,group,tile", [(512, 3072, 2048, 64, "P64"), (1024, 3072, 2048, 128, "P128")])
+def test_dense_path_taken_by_size_equals_forced_tile(m, n, k, group, tile):
+    # 512 .. 1024 rows over a few hundred 256-wide column tiles: the automatic
+    # choice is the dequantize-then-dense path (the binding allocates its
+    # workspace), bit-equal to the forced dense tile; sampled outputs within
+    # the bf16 tolerance of the oracle.
+    p = si.w4_problem(m, n, k, group, tag="dense-auto", bias_dtype=BF16)
+    auto = _run_w4(p, "prefill")
+    qg.set_override(prefill_tile=tile)
+    forced = _run_w4(p, "prefill")
+    assert torch.equal(auto.view(torch.int16), forced.view(torch.int16))
+    C = auto.float().cpu().numpy()
+    rng = np.random.default_rng(m + n)
+    rows, cols = rng.integers(0, m, 128), rng.integers(0, n, 128)
+    ref = oracle.gemm_w4_at(p.A, p.packed, p.scale, p.zero, group, rows, cols, BF16, p.bias, BF16)
+    assert np.abs(C[rows, cols] - ref).max() / np.abs(ref).max() <= TOL[BF16]
+
+
+@pytest.mark.parametrize("tile", DENSE_TILES)
+def test_dense_path_workspace_size_and_fallback(tile):
+    # The dense path asks for n * k 16-bit values of workspace; with less the
+    # call runs the fused tiles, bit-equal to the automatic choice.
+    m, n, k, group = 200, 256, 640, 64
+    p = si.w4_problem(m, n, k, group, tag="dense-ws")
+    A = to_dev(p.A, p.dtype)
+    tiled = qg.repack_w4(to_dev(p.packed))
+    S, Z = to_dev(p.scale, p.dtype), to_dev(p.zero, p.dtype)
+    qg.set_override(path="prefill")
+    auto = qg.gemm_w4a16(A, tiled, S, Z, None, group)
+    qg.set_override(prefill_tile=tile)
+    need = int(qg.lib().qgemm_workspace_size(m, n, k, group, 4))
+    assert need == n * k * 2
+    small = torch.empty(need - 256, dtype=torch.uint8, device="cuda")
+    fallback = qg.gemm_w4a16(A, tiled, S, Z, None, group, workspace=small)
+    full = torch.empty(need, dtype=torch.uint8, device="cuda")
+    dense = qg.gemm_w4a16(A, tiled, S, Z, None, group, workspace=full)
+    torch.cuda.synchronize()
+    assert torch.equal(auto.view(torch.int16), fallback.view(torch.int16))
+    ref = oracle.gemm_w4(p.A, p.packed, p.scale, p.zero, group, BF16)
+    assert rel_err(dense.float().cpu().numpy(), ref) <= TOL[BF16]
 
 
 @pytest.mark.parametrize("nbytes", [0, 16, 4096 + 48, 10 * (1 << 20) + 160])

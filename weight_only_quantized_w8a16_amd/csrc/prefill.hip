@@ -12,6 +12,7 @@
 
 #include "qg_launch.hpp"
 #include "tile_big.hpp"
+#include "tile_dense.hpp"
 #include "tile_gemm.hpp"
 
 namespace qg {
@@ -113,6 +114,123 @@ __global__ __launch_bounds__(Cfg::NTHR) void k_prefill_dma(TileProblem p, int ti
   tile_gemm_dma<Cfg, ACT, WBITS, kDense, GS8, SPLIT, PC>(p, tm, tn, L, slice);
 }
 
+// Dequantize-then-dense path, first half: W [N, K] 16-bit row-major into the
+// caller's workspace, holding the values the fused tiles put into LDS --
+// int4: fma(q, s, z - 8 s) rounded once to the activation type (z = 0
+// without zeros; group = K for one scale and zero per channel); int8: the
+// codes exactly (the channel scale is applied to the sum), or q * s rounded
+// (group scales).
+//
+// int4: one thread per 8 consecutive k of a row (one tiled 4-byte word), in
+// row-major order, so a wave writes one contiguous KiB.  Walking the tiled
+// codes in order instead (a wave reading one 1 KiB block of 16 rows and
+// writing 16 row pieces, with or without an LDS transpose for the writes)
+// measured faster alone (N = 3072, K = 2048: 5.7 against 7.2 us) but slower
+// ahead of the dense tile (GEMM + dequant, M = 512: 26.7 against 22.1 us).
+template <int ACT>
+__global__ __launch_bounds__(256) void k_predequant_w4(const uint8_t *__restrict__ B,
+                                                       const uint16_t *__restrict__ S,
+                                                       const uint16_t *__restrict__ Z,
+                                                       uint16_t *__restrict__ W, int K, int group,
+                                                       long long runs) {
+  const long long r = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (r >= runs) return;
+  const int per_row = K >> 3;
+  const int row = static_cast<int>(r / per_row), k0 = static_cast<int>(r % per_row) * 8;
+  const uint32_t word = *reinterpret_cast<const uint32_t *>(B + w4_word_offset(row, k0, K));
+  const size_t gi = static_cast<size_t>(row) * (K / group) + k0 / group;
+  const float sc = bits_to_f32<ACT>(S[gi]);
+  const float z8 = (Z ? bits_to_f32<ACT>(Z[gi]) : 0.0f) - 8.0f * sc;
+  *reinterpret_cast<u32x4 *>(W + static_cast<size_t>(row) * K + k0) = dequant_word_w4<ACT>(word, sc, z8);
+}
+
+// int8: a tiled 1 KiB block holds 16 rows x 64 k; lane l of a block holds
+// row l % 16 and the 8-k chunks j and 4 + j (j = l / 16), two 8-byte runs.
+// A wave converts one block, read as one contiguous KiB (row-major order,
+// one run per thread, measured 17.1 against 9.4 us at N = K = 3584).
+template <int ACT, bool GS8>
+__device__ __forceinline__ void predequant_w8_piece(u32x4 w, const uint16_t *__restrict__ S, int row,
+                                                    int kb0, int K, int group, u32x4 (&out)[2]) {
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {   // k 32 r + 8 j
+    if constexpr (GS8)
+      out[r] = dequant_run_w8<ACT>(w[2 * r], w[2 * r + 1],
+                                   bits_to_f32<ACT>(S[static_cast<size_t>(row) * (K / group) + (kb0 + 32 * r) / group]));
+    else
+      out[r] = (ACT == kFP16) ? w8_run_to_f16(w[2 * r], w[2 * r + 1]) : w8_run_to_bf16(w[2 * r], w[2 * r + 1]);
+  }
+}
+
+// Four consecutive blocks of one 16-row band per workgroup (K a multiple of
+// 256): the values are staged in LDS and each row's 256 values leave as
+// contiguous 16-byte pieces.
+template <int ACT, bool GS8>
+__global__ __launch_bounds__(256) void k_predequant_w8(const u32x4 *__restrict__ B,
+                                                       const uint16_t *__restrict__ S,
+                                                       uint16_t *__restrict__ W, int K, int group) {
+  constexpr int KB = 64;
+  constexpr int PITCH = 4 * KB * 2 + 16;       // LDS row bytes (padded)
+  constexpr int PPR = 4 * KB / 8;              // 16-byte pieces per row
+  __shared__ __attribute__((aligned(16))) char tile[16 * PITCH];
+  const int tid = threadIdx.x, wave = tid >> 6, l = tid & 63, nl = l & 15, j = l >> 4;
+  const int nkb = K / KB;
+  const long long blk0 = static_cast<long long>(blockIdx.x) * 4;   // first block
+  const int band = static_cast<int>(blk0 / nkb), kb0 = static_cast<int>(blk0 % nkb) * KB;
+  u32x4 out[2];
+  predequant_w8_piece<ACT, GS8>(__builtin_nontemporal_load(B + blk0 * 64 + tid), S, band * 16 + nl,
+                                kb0 + wave * KB, K, group, out);
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+    *reinterpret_cast<u32x4 *>(tile + nl * PITCH + (wave * KB + 32 * e + 8 * j) * 2) = out[e];
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < 16 * PPR / 256; ++it) {
+    const int q = it * 256 + tid, r = q / PPR, c = q % PPR;
+    *reinterpret_cast<u32x4 *>(W + static_cast<size_t>(band * 16 + r) * K + kb0 + c * 8) =
+        *reinterpret_cast<const u32x4 *>(tile + r * PITCH + c * 16);
+  }
+}
+
+// int8, any K (a multiple of 64): one block per wave, each lane's values
+// written where they belong.
+template <int ACT, bool GS8>
+__global__ __launch_bounds__(256) void k_predequant_w8_any(const u32x4 *__restrict__ B,
+                                                           const uint16_t *__restrict__ S,
+                                                           uint16_t *__restrict__ W, int K, int group,
+                                                           long long pieces) {
+  const long long t = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (t >= pieces) return;
+  const int nkb = K / 64;
+  const long long blk = t >> 6;
+  const int l = static_cast<int>(t & 63), nl = l & 15, j = l >> 4;
+  const int row = static_cast<int>(blk / nkb) * 16 + nl, kb0 = static_cast<int>(blk % nkb) * 64;
+  u32x4 out[2];
+  predequant_w8_piece<ACT, GS8>(__builtin_nontemporal_load(B + t), S, row, kb0, K, group, out);
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+    *reinterpret_cast<u32x4 *>(W + static_cast<size_t>(row) * K + kb0 + 32 * e + 8 * j) = out[e];
+}
+
+// Second half: the dense tile over the dequantized weights, tiles in the
+// fused tiles' XCD-grouped order.
+template <class Cfg, int ACT>
+__global__ __launch_bounds__(Cfg::NTHR) void k_dense(DenseProblem p, int tiles_n) {
+  constexpr int NA = Cfg::NS > 2 ? Cfg::STAGE_A : 16, NB = Cfg::NS > 2 ? Cfg::STAGE_B : 16;
+  constexpr int NA3 = Cfg::NS > 3 ? Cfg::STAGE_A : 16, NB3 = Cfg::NS > 3 ? Cfg::STAGE_B : 16;
+  __shared__ __attribute__((aligned(16))) char a0[Cfg::STAGE_A];
+  __shared__ __attribute__((aligned(16))) char a1[Cfg::STAGE_A];
+  __shared__ __attribute__((aligned(16))) char a2[NA];
+  __shared__ __attribute__((aligned(16))) char a3[NA3];
+  __shared__ __attribute__((aligned(16))) char b0[Cfg::STAGE_B];
+  __shared__ __attribute__((aligned(16))) char b1[Cfg::STAGE_B];
+  __shared__ __attribute__((aligned(16))) char b2[NB];
+  __shared__ __attribute__((aligned(16))) char b3[NB3];
+  const DenseLds L{{a0, a1, a2, a3}, {b0, b1, b2, b3}};
+  int tm, tn;
+  grouped_tile(xcd_linear_id(), gridDim.x / tiles_n, tiles_n, tm, tn);
+  dense_tile_gemm<Cfg, ACT>(p, tm, tn, L);
+}
+
 namespace {
 
 using CfgX = TileCfg<256, 256, 2, 4>;   // 8 waves, 128x64 per wave
@@ -129,6 +247,10 @@ using CfgM = TileCfg<128, 128, 2, 2>;   // 4 waves, 64x64 per wave
 // 18.2 -> 15.1 us, M = 64 17.2 -> 14.0 us; W8A16 M = 128, N = 3584 20.4 ->
 // 19.4 us; four groups were slower (one workgroup per CU).
 using CfgS = TileCfg<64, 64, 2, 2, 2>;
+// Dense tiles of the dequantize-then-dense path.
+using CfgP256 = DenseCfg<256, 256, 2, 4, 2>;   // 8 waves of 128 x 64, 2 stages
+using CfgP128 = DenseCfg<128, 128, 2, 4, 4>;   // 8 waves of 64 x 32, 4 stages
+using CfgP64 = DenseCfg<64, 128, 2, 4, 4>;     // 8 waves of 32 x 32, 4 stages
 
 // K slices of one launch: partials in `part` (nullptr: no split).
 struct Split {
@@ -234,7 +356,8 @@ int device_cus() {
 // D64 and D128 are the 256 x 256, 256 x 128, 64 x 256 and 128 x 256 tiles
 // with direct-to-LDS activation loads.
 
-int choose_tile(const GemmArgs &a) {
+// The fused tiles' choice (the forced fused tile, else by size).
+int choose_fused_tile(const GemmArgs &a) {
   auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * (a.N / bn); };
   const bool n256 = a.N % 256 == 0, n128 = a.N % 128 == 0;
   switch (dispatch_override().prefill_tile) {
@@ -270,6 +393,42 @@ int choose_tile(const GemmArgs &a) {
   return kS;
 }
 
+// Dequantize-then-dense: the whole weight dequantized once into the
+// caller's workspace (N K 16-bit values), then a dense tile; the operands
+// must fit its 32-bit buffer offsets.  Taken when forced, and by size where
+// the fused tiles would re-dequantize every weight for many row tiles while
+// leaving most CUs idle: 512 to 1024 rows, at least 3072 columns, fewer
+// 256 x 256 tiles than a quarter of the CUs.  Measured on MI355X (dequant + dense
+// tile against the fused choice): W4A16 K = 2048, N = 3072: M = 512
+// 28.4 -> 21.5 us (64 x 128 tile), M = 1024 31.0 -> 27.1 us (128 x 128);
+// W8A16 K = N = 3584, M = 1024: per channel 45.5 -> 43.9 us, group 128
+// 56.0 -> 42.6 us.  Slower at M = 256 (20.5 -> 20.7 us), M = 2048
+// (36.1 -> 45.4 us) and for N = 13312 or 18944 (M = 512, N = 13312, 104
+// tiles: 37.6 -> 65.7 us).
+int choose_dense_tile(const GemmArgs &a) {
+  const uint64_t lim = uint64_t(1) << 31;
+  if (uint64_t(a.M) * a.K * 2 >= lim || uint64_t(a.N) * a.K * 2 >= lim) return -1;
+  switch (dispatch_override().prefill_tile) {
+    case kP256: return a.N % 256 == 0 ? kP256 : -1;
+    case kP128: return a.N % 128 == 0 ? kP128 : -1;
+    case kP64: return a.N % 128 == 0 ? kP64 : -1;
+    case -1: break;
+    default: return -1;   // a fused tile is forced
+  }
+  const long t8 = static_cast<long>((a.M + 255) / 256) * (a.N / 256);
+  if (a.M >= 512 && a.M <= 1024 && a.N >= 3072 && a.N % 128 == 0 && 4 * t8 < device_cus())
+    return a.M <= 512 ? kP64 : kP128;
+  return -1;
+}
+
+int choose_tile(const GemmArgs &a) {
+  const int d = choose_dense_tile(a);
+  return d >= 0 ? d : choose_fused_tile(a);
+}
+
+bool is_dense(int tile) { return tile == kP256 || tile == kP128 || tile == kP64; }
+size_t dense_bytes(const GemmArgs &a) { return static_cast<size_t>(a.N) * a.K * 2; }
+
 // Split-K plan: K slices written as fp32 partials to the caller's
 // workspace, then summed by one reduction launch.  Measured on MI355X, the
 // partials' traffic and the extra launch cost about what the shorter K loop
@@ -292,6 +451,10 @@ struct Plan {
 
 Plan plan_prefill(const GemmArgs &a, int wbits, bool gs8) {
   Plan pl{choose_tile(a), Split{}, 0};
+  if (is_dense(pl.tile)) {
+    pl.bytes = dense_bytes(a);
+    return pl;
+  }
   const int nsteps = a.K / 64;
   const int tiles_s = ((a.M + 63) / 64) * (a.N / 64);
   int want = (pl.tile == kS && a.M <= 128 && nsteps >= 32 && tiles_s < 256) ? 2 : 1;
@@ -324,9 +487,52 @@ hipError_t launch_tile(int tile, const GemmArgs &a, hipStream_t s, const Split &
   }
 }
 
+template <class Cfg, int ACT>
+hipError_t launch_dense(const DenseProblem &p, hipStream_t s) {
+  const int tm = (p.M + Cfg::BM - 1) / Cfg::BM, tn = p.N / Cfg::BN;
+  hipLaunchKernelGGL((k_dense<Cfg, ACT>), dim3(tm * tn), dim3(Cfg::NTHR), 0, s, p, tn);
+  return hipGetLastError();
+}
+
+template <int ACT, int WBITS, bool GS8>
+hipError_t run_dense(int tile, const GemmArgs &a, hipStream_t s) {
+  uint16_t *W = static_cast<uint16_t *>(a.ws);
+  const int grp = a.group > 0 ? a.group : a.K;
+  if constexpr (WBITS == 4) {
+    const long long runs = static_cast<long long>(a.N) * a.K / 8;
+    hipLaunchKernelGGL(k_predequant_w4<ACT>, dim3(static_cast<unsigned>((runs + 255) / 256)), dim3(256), 0, s,
+                       static_cast<const uint8_t *>(a.B), a.S, a.Z, W, a.K, grp, runs);
+  } else {
+    const long long pieces = static_cast<long long>(a.N) * a.K / 16;   // 16-byte code pieces
+    const unsigned grid = static_cast<unsigned>((pieces + 255) / 256);
+    const auto *Bv = static_cast<const u32x4 *>(a.B);
+    if (a.K % 256 == 0)
+      hipLaunchKernelGGL((k_predequant_w8<ACT, GS8>), dim3(grid), dim3(256), 0, s, Bv, a.S, W, a.K, grp);
+    else
+      hipLaunchKernelGGL((k_predequant_w8_any<ACT, GS8>), dim3(grid), dim3(256), 0, s, Bv, a.S, W, a.K, grp,
+                         pieces);
+  }
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  const DenseProblem p{a.A, W, (WBITS == 8 && !GS8) ? a.S : nullptr, a.bias, a.bias_dt,
+                       a.C, a.M, a.N, a.K};
+  switch (tile) {
+    case kP256: return launch_dense<CfgP256, ACT>(p, s);
+    case kP128: return launch_dense<CfgP128, ACT>(p, s);
+    default: return launch_dense<CfgP64, ACT>(p, s);
+  }
+}
+
 template <int ACT, int WBITS, bool GS8 = false, bool PC = false>
 hipError_t dispatch(const GemmArgs &a, hipStream_t s) {
   Plan pl = plan_prefill(a, WBITS, GS8);
+  if (is_dense(pl.tile)) {
+    if (a.ws && a.ws_bytes >= pl.bytes) return run_dense<ACT, WBITS, GS8>(pl.tile, a, s);
+    // Too little workspace: the fused tiles, as if no dense tile were chosen.
+    GemmArgs b = a;
+    b.ws = nullptr;
+    b.ws_bytes = 0;
+    return launch_tile<ACT, WBITS, GS8, PC>(choose_fused_tile(a), b, s, Split{});
+  }
   if (pl.split.nsplit > 1 && a.ws && a.ws_bytes >= pl.bytes)
     pl.split.part = static_cast<float *>(a.ws);
   else
@@ -338,7 +544,7 @@ hipError_t dispatch(const GemmArgs &a, hipStream_t s) {
 
 size_t prefill_workspace_bytes(const GemmArgs &a, int wbits) {
   const Plan pl = plan_prefill(a, wbits, wbits == 8 && a.group > 0);
-  return pl.split.nsplit > 1 ? pl.bytes : 0;
+  return (pl.split.nsplit > 1 || is_dense(pl.tile)) ? pl.bytes : 0;
 }
 
 hipError_t launch_prefill_w4(const GemmArgs &a, hipStream_t s) {

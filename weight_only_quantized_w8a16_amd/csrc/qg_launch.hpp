@@ -34,7 +34,8 @@ hipError_t set_lds_limit_once(Kern kern, int bytes, std::atomic<uint64_t> &done)
 // problem is ignored for that problem.
 enum { kPathAuto = 0, kPathDecode = 1, kPathPrefill = 2 };
 // Prefill tiles (prefill.hip), in the order qg_set_override names them.
-enum PrefillTile { kX, kD8, kD8N, kD64, kD128, kL, kM, kS };
+// kP256 .. kP64: the dense tiles of the dequantize-then-dense path.
+enum PrefillTile { kX, kD8, kD8N, kD64, kD128, kL, kM, kS, kP256, kP128, kP64 };
 // W8A8 tiles (w8a8.hip), in the order qg_set_override names them.
 enum W8A8Tile { kT256, kT256N, kT128, kT64 };
 struct Override {
