@@ -91,9 +91,18 @@ __device__ __forceinline__ void w8a8_tile(int id, int tiles_m, int tiles_n, int 
   tn = in / gsz;
 }
 
+// The two LDS stages of each operand are separate objects: with one array
+// and a stage index the compiler's wait-count pass cannot tell the stage
+// being read from the one being loaded, and made every step wait for the
+// next step's direct loads before its first fragment read.
+struct W8Lds {
+  char *a[2];
+  char *b[2];
+};
+
 template <class Cfg, int OUT, bool SPLIT>
 __device__ __forceinline__ void w8a8_tile_gemm(const W8A8Problem &p, int tiles_m, int tiles_n,
-                                               char (*a_st)[Cfg::BM * 128], char (*b_st)[Cfg::BN * 128]) {
+                                               const W8Lds &L) {
   constexpr int TM = Cfg::TM, TN = Cfg::TN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
@@ -131,8 +140,8 @@ __device__ __forceinline__ void w8a8_tile_gemm(const W8A8Problem &p, int tiles_m
     b_voff[i] = static_cast<uint32_t>(min(col_lo + r, col_last)) * static_cast<uint32_t>(K) + c * 16;
   }
   auto issue = [&](int step, int st) {
-    char *da = a_st[st] + wave * Cfg::A_DMA * 1024;
-    char *db = b_st[st] + wave * Cfg::B_DMA * 1024;
+    char *da = L.a[st] + wave * Cfg::A_DMA * 1024;
+    char *db = L.b[st] + wave * Cfg::B_DMA * 1024;
 #pragma unroll
     for (int i = 0; i < Cfg::A_DMA; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -197,7 +206,7 @@ __device__ __forceinline__ void w8a8_tile_gemm(const W8A8Problem &p, int tiles_m
     constexpr int I = decltype(Ic)::value;
     if (step + 1 < s1) issue(step + 1, 1 - I);
     __builtin_amdgcn_sched_barrier(0);
-    const char *As = a_st[I], *Bs = b_st[I];
+    const char *As = L.a[I], *Bs = L.b[I];
     Frags f0, f1;
     fread(As, Bs, 0, f0);
     fread(As, Bs, 1, f1);
@@ -283,9 +292,11 @@ __device__ __forceinline__ void w8a8_tile_gemm(const W8A8Problem &p, int tiles_m
 
 template <class Cfg, int OUT, bool SPLIT>
 __global__ __launch_bounds__(Cfg::NTHR) void k_w8a8(W8A8Problem p, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(16))) char a_st[2][Cfg::BM * 128];
-  __shared__ __attribute__((aligned(16))) char b_st[2][Cfg::BN * 128];
-  w8a8_tile_gemm<Cfg, OUT, SPLIT>(p, tiles_m, tiles_n, a_st, b_st);
+  __shared__ __attribute__((aligned(16))) char a0[Cfg::BM * 128];
+  __shared__ __attribute__((aligned(16))) char a1[Cfg::BM * 128];
+  __shared__ __attribute__((aligned(16))) char b0[Cfg::BN * 128];
+  __shared__ __attribute__((aligned(16))) char b1[Cfg::BN * 128];
+  w8a8_tile_gemm<Cfg, OUT, SPLIT>(p, tiles_m, tiles_n, W8Lds{{a0, a1}, {b0, b1}});
 }
 
 // Split-K: C = RNE_out(float(sum of the slices' int32 partials) * scales);
