@@ -328,18 +328,6 @@ hipError_t run_dma(const GemmArgs &a, hipStream_t s, const Split &sp = Split{}) 
   return reduce_split<ACT, WBITS, GS8>(a, sp, s);
 }
 
-// Compute units of the current device (cached per device; 256 if unknown).
-int device_cus() {
-  static std::atomic<int> cus[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int c = cus[dev].load(std::memory_order_relaxed);
-  if (c == 0) {
-    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
-    cus[dev].store(c, std::memory_order_relaxed);
-  }
-  return c;
-}
 
 // Tile shapes.  Choice, from on-device sweeps at K = 2048 and 3584 (M from
 // 32 to 4096): the direct-load tiles once there are enough of them to keep

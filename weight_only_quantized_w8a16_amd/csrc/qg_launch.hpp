@@ -29,6 +29,19 @@ hipError_t set_lds_limit_once(Kern kern, int bytes, std::atomic<uint64_t> &done)
   return e;
 }
 
+// Compute units of the current device (cached per device; 256 if unknown).
+inline int device_cus() {
+  static std::atomic<int> cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int c = cus[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0) c = 256;
+    cus[dev].store(c, std::memory_order_relaxed);
+  }
+  return c;
+}
+
 // Dispatch override (qg_set_override): forced choices, or the automatic
 // ones (kPathAuto, -1, 0, false).  A forced tile or path that does not fit a
 // problem is ignored for that problem.

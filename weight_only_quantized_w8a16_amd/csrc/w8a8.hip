@@ -26,6 +26,7 @@
 // source side.  Rows past the end of A or B are read from the last valid row
 // (a direct load cannot be masked); their outputs are never stored.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "qg_common.hpp"
@@ -48,9 +49,10 @@ struct W8A8Problem {
   int kseg;              // 128-k steps per K slice (split-K)
 };
 
-template <int BM_, int BN_, int WM_, int WN_>
+// NS LDS stages, loads issued NS - 1 steps ahead.
+template <int BM_, int BN_, int WM_, int WN_, int NS_ = 2>
 struct W8Cfg {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NS = NS_;
   static constexpr int NTHR = 64 * WM * WN;
   static constexpr int WTM = BM / WM, WTN = BN / WN;   // wave tile
   static constexpr int TM = WTM / 32, TN = WTN / 32;   // 32x32 accumulators per wave
@@ -58,6 +60,7 @@ struct W8Cfg {
   static constexpr int B_DMA = BN * 8 / NTHR;
   static_assert(NTHR == 512, "eight waves");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0 && A_DMA >= 1 && B_DMA >= 1, "tile shape");
+  static_assert(NS >= 2 && NS <= 4 && NS * (BM + BN) * 128 <= 160 * 1024, "LDS stages");
 };
 
 // Output element conversion.
@@ -96,8 +99,8 @@ __device__ __forceinline__ void w8a8_tile(int id, int tiles_m, int tiles_n, int 
 // being read from the one being loaded, and made every step wait for the
 // next step's direct loads before its first fragment read.
 struct W8Lds {
-  char *a[2];
-  char *b[2];
+  char *a[4];
+  char *b[4];
 };
 
 template <class Cfg, int OUT, bool SPLIT>
@@ -139,17 +142,22 @@ __device__ __forceinline__ void w8a8_tile_gemm(const W8A8Problem &p, int tiles_m
     const int r = q >> 3, c = (q & 7) ^ ((r >> 1) & 7);
     b_voff[i] = static_cast<uint32_t>(min(col_lo + r, col_last)) * static_cast<uint32_t>(K) + c * 16;
   }
-  auto issue = [&](int step, int st) {
-    char *da = L.a[st] + wave * Cfg::A_DMA * 1024;
-    char *db = L.b[st] + wave * Cfg::B_DMA * 1024;
+  // Step `step` into stage ST; past the slice's last step its last step is
+  // loaded again (into a stage no later step reads), so every step issues
+  // the same number of loads and one wait count fits all.
+  auto issue = [&](auto STc, int step) {
+    constexpr int ST = decltype(STc)::value;
+    const int sk = min(step, s1 - 1) * 128;
+    char *da = L.a[ST] + wave * Cfg::A_DMA * 1024;
+    char *db = L.b[ST] + wave * Cfg::B_DMA * 1024;
 #pragma unroll
     for (int i = 0; i < Cfg::A_DMA; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rA, (__attribute__((address_space(3))) void *)(da + i * 1024), 16, a_voff[i], step * 128, 0, 0);
+          rA, (__attribute__((address_space(3))) void *)(da + i * 1024), 16, a_voff[i], sk, 0, 0);
 #pragma unroll
     for (int i = 0; i < Cfg::B_DMA; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rB, (__attribute__((address_space(3))) void *)(db + i * 1024), 16, b_voff[i], step * 128, 0, 0);
+          rB, (__attribute__((address_space(3))) void *)(db + i * 1024), 16, b_voff[i], sk, 0, 0);
   };
 
   // Fragments: sub-step ks covers k bytes 32 ks .. 32 ks + 31; lane reads
@@ -197,14 +205,19 @@ __device__ __forceinline__ void w8a8_tile_gemm(const W8A8Problem &p, int tiles_m
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  constexpr int WAIT_ALL = 7 << 4;   // vmcnt(0) lgkmcnt(0)
+  constexpr int NS = Cfg::NS;
+  // vmcnt: after a step's issue the next step's loads are the oldest but
+  // those of the NS - 2 steps after it; lgkmcnt(0).
+  constexpr int NWAIT = (NS - 2) * (Cfg::A_DMA + Cfg::B_DMA);
+  constexpr int WAIT_NEXT = (NWAIT & 15) | ((NWAIT >> 4) << 14) | (7 << 4);
 
-  // Step s on stage I: issue step s + 1 into the other stage (last read in
-  // step s - 1, before the barrier that ended it), run the four sub-steps,
-  // wait for this wave's loads, meet the other waves.
+  // Step s on stage I = (s - s0) % NS: issue step s + NS - 1 into stage
+  // (I - 1) % NS (last read in step s - 1, before the barrier that ended it),
+  // run the four sub-steps, wait for this wave's loads of step s + 1, meet
+  // the other waves.
   auto body = [&](auto Ic, int step) {
     constexpr int I = decltype(Ic)::value;
-    if (step + 1 < s1) issue(step + 1, 1 - I);
+    issue(std::integral_constant<int, (I + NS - 1) % NS>{}, step + NS - 1);
     __builtin_amdgcn_sched_barrier(0);
     const char *As = L.a[I], *Bs = L.b[I];
     Frags f0, f1;
@@ -226,21 +239,33 @@ __device__ __forceinline__ void w8a8_tile_gemm(const W8A8Problem &p, int tiles_m
     __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(WAIT_ALL);
+    __builtin_amdgcn_s_waitcnt(WAIT_NEXT);
     barrier();
   };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
 
-  issue(s0, 0);
-  __builtin_amdgcn_s_waitcnt(WAIT_ALL);
+  issue(S0{}, s0);
+  if constexpr (NS > 2) issue(S1{}, s0 + 1);
+  if constexpr (NS > 3) issue(S2{}, s0 + 2);
+  __builtin_amdgcn_s_waitcnt(WAIT_NEXT);
   barrier();
   int step = s0;
-  for (; step + 2 <= s1; step += 2) {
-    body(I0{}, step);
-    body(I1{}, step + 1);
+  for (; step + NS <= s1; step += NS) {
+    body(S0{}, step);
+    body(S1{}, step + 1);
+    if constexpr (NS > 2) body(S2{}, step + 2);
+    if constexpr (NS > 3) body(S3{}, step + 3);
   }
-  if (step < s1) body(I0{}, step);
+  if (step < s1) body(S0{}, step);
+  if (step + 1 < s1) body(S1{}, step + 1);
+  if constexpr (NS > 2)
+    if (step + 2 < s1) body(S2{}, step + 2);
+  // The re-issued loads of the last steps land before the workgroup (and its
+  // LDS) ends.
+  __builtin_amdgcn_s_waitcnt(7 << 4);
 
   // Epilogue: value v of acc[i][j] is C[row][col], row = wave tile row +
   // 32 i + lane % 32, col = wave tile column + 32 j + 8 (v / 4) +
@@ -292,11 +317,16 @@ __device__ __forceinline__ void w8a8_tile_gemm(const W8A8Problem &p, int tiles_m
 
 template <class Cfg, int OUT, bool SPLIT>
 __global__ __launch_bounds__(Cfg::NTHR) void k_w8a8(W8A8Problem p, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(16))) char a0[Cfg::BM * 128];
-  __shared__ __attribute__((aligned(16))) char a1[Cfg::BM * 128];
-  __shared__ __attribute__((aligned(16))) char b0[Cfg::BN * 128];
-  __shared__ __attribute__((aligned(16))) char b1[Cfg::BN * 128];
-  w8a8_tile_gemm<Cfg, OUT, SPLIT>(p, tiles_m, tiles_n, W8Lds{{a0, a1}, {b0, b1}});
+  constexpr int SA = Cfg::BM * 128, SB = Cfg::BN * 128;
+  __shared__ __attribute__((aligned(16))) char a0[SA];
+  __shared__ __attribute__((aligned(16))) char a1[SA];
+  __shared__ __attribute__((aligned(16))) char a2[Cfg::NS > 2 ? SA : 16];
+  __shared__ __attribute__((aligned(16))) char a3[Cfg::NS > 3 ? SA : 16];
+  __shared__ __attribute__((aligned(16))) char b0[SB];
+  __shared__ __attribute__((aligned(16))) char b1[SB];
+  __shared__ __attribute__((aligned(16))) char b2[Cfg::NS > 2 ? SB : 16];
+  __shared__ __attribute__((aligned(16))) char b3[Cfg::NS > 3 ? SB : 16];
+  w8a8_tile_gemm<Cfg, OUT, SPLIT>(p, tiles_m, tiles_n, W8Lds{{a0, a1, a2, a3}, {b0, b1, b2, b3}});
 }
 
 // Split-K: C = RNE_out(float(sum of the slices' int32 partials) * scales);
@@ -383,10 +413,15 @@ __global__ __launch_bounds__(NT == 1 ? 1024 : 512) void k_w8a8_decode(W8A8Proble
 
 namespace {
 
-using T256x256 = W8Cfg<256, 256, 2, 4>;   // waves of 128 x 64
-using T256x128 = W8Cfg<256, 128, 4, 2>;   // waves of 64 x 64
-using T128x128 = W8Cfg<128, 128, 2, 4>;   // waves of 64 x 32
-using T64x128 = W8Cfg<64, 128, 2, 4>;     // waves of 32 x 32
+// Stages (the LDS holds two of the 256 x 256 tile's, three of the 256 x 128
+// tile's, four of the smaller ones'), measured at K = 3584 against two:
+// 128 x 128 with four, m = 1024, n = 3584: 29.6 -> 22.3 us, m = 512: 24.7 ->
+// 16.2 us; 256 x 128 with three, m = 2048, n = 3584: 38.9 -> 34.3 us;
+// 64 x 128 with four 5-10 % slower, so it keeps two.
+using T256x256 = W8Cfg<256, 256, 2, 4>;      // waves of 128 x 64
+using T256x128 = W8Cfg<256, 128, 4, 2, 3>;   // waves of 64 x 64
+using T128x128 = W8Cfg<128, 128, 2, 4, 4>;   // waves of 64 x 32
+using T64x128 = W8Cfg<64, 128, 2, 4>;        // waves of 32 x 32
 
 struct W8A8Plan {
   int tile;
@@ -396,28 +431,52 @@ struct W8A8Plan {
 
 int tiles_of(int M, int N, int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); }
 
-// Tile by problem size: the largest tile that still gives most CUs work,
-// then K slices when even the smallest tile leaves the chip mostly idle,
-// enough for about one workgroup per CU, each slice at least two steps
-// (measured at K = 3584, m = 128, n = 3584: 56 tiles, 4-5 slices 15 us,
-// unsplit 28 us, 8-10 slices 18-21 us).  The dispatch override's w8a8_split
-// asks for n slices (tests and tuning).
+
+// Tile by problem size (below), then K slices when the tiles leave the chip
+// mostly idle, each slice at least two steps.  The dispatch override's
+// w8a8_split asks for n slices (tests and tuning).
 W8A8Plan plan_w8a8(int M, int N, int K) {
   W8A8Plan pl{kT64, 0, 1, 0};
-  // The 256 x 256 tile when its tiles fill the CUs in one round or in many
-  // (a second, partly filled round of large tiles costs more than smaller
-  // tiles: K = 3584, m = 1024, n = 18944, 296 tiles: 132 us, 128 x 128: 108).
-  const int t256 = tiles_of(M, N, 256, 256);
-  // The 256 x 128 tile was never the fastest in those sweeps (m 128 to 4096);
-  // it stays available through the dispatch override.
-  if (M > 128 && t256 >= 192 && (t256 <= 256 || t256 >= 768)) pl.tile = kT256;
-  else if (M > 64 && tiles_of(M, N, 128, 128) >= 128) pl.tile = kT128;
-  else pl.tile = kT64;
+  // Above 64 rows: each of these tiles holds a CU alone, so a launch takes
+  // ceil(tiles / CUs) rounds of one tile's time; the tile with the fewest
+  // round-weighted tile times wins, ties to the larger tile.  Relative tile
+  // times, measured at K = 3584 in one round: 256 x 256 1, 256 x 128 0.63,
+  // 128 x 128 0.41.  Against every tile forced, m = 128 .. 4096, n = 3584 and
+  // 18944, this picks the fastest (m = 2048, n = 18944: 166.8 us on
+  // 256 x 256 where the earlier rule took 128 x 128 at 209.8; m = 256,
+  // n = 18944: 33.8 on 256 x 128 against 44.3; m = 512, n = 3584: 20.9 on
+  // 128 x 128 against 24.4 on 64 x 128).  Up to 64 rows: 128 x 128 when
+  // its tiles fill half the CUs unsplit (four stages beat the smaller
+  // tile's two: m = 32, n = 18944, 148 tiles: 18.4 against 26.5 us), else
+  // 64 x 128 in K slices (m = 32, n = 3584: 12.3 against 14.9).
+  if (M <= 64) {
+    if (2 * tiles_of(M, N, 128, 128) >= device_cus()) pl.tile = kT128;
+  } else {
+    const int cus = device_cus();
+    auto cost = [&](int bm, int bn, int w) {
+      const long t = tiles_of(M, N, bm, bn);
+      return ((t + cus - 1) / cus) * static_cast<long>(w);
+    };
+    const long c256 = cost(256, 256, 100), c256n = cost(256, 128, 63), c128 = cost(128, 128, 41);
+    pl.tile = kT256;
+    long best = c256;
+    if (c256n < best) { pl.tile = kT256N; best = c256n; }
+    if (c128 < best) pl.tile = kT128;
+  }
   const int bm = pl.tile == kT64 ? 64 : pl.tile == kT128 ? 128 : 256;
   const int bn = pl.tile == kT256 ? 256 : 128;
   const int tiles = tiles_of(M, N, bm, bn), nsteps = K / 128;
   int want = 1;
-  if (tiles < 128 && nsteps >= 4) want = std::min((256 + tiles - 1) / tiles, std::min(nsteps / 2, 16));
+  // K slices for launches with few tiles: the 64 x 128 tile (two stages)
+  // below 128 tiles, for about 256 workgroups; the larger tiles (three or
+  // four stages, faster per step) only below 48 tiles, for about 128 (at
+  // m = 512, n = 3584, 112 tiles of 128 x 128: unsplit 20.9 us, three
+  // slices 29.6; m = 128, 28 tiles: five slices 15.7, ten 22.6).
+  if (pl.tile == kT64) {
+    if (tiles < 128 && nsteps >= 4) want = std::min((256 + tiles - 1) / tiles, std::min(nsteps / 2, 16));
+  } else if (tiles < 48 && nsteps >= 4) {
+    want = std::min((128 + tiles - 1) / tiles, std::min(nsteps / 2, 16));
+  }
   if (const int o = dispatch_override().w8a8_split; o > 0) want = std::min(o, nsteps);   // tuning
   {
     if (want >= 2) {
