@@ -38,6 +38,11 @@ def test_captured_calls_replay_bit_exact():
     ws = torch.empty(max(qg.gemm_workspace_size(128, 3072, K, 64, 4), 256), dtype=torch.uint8,
                      device=dev)
     assert qg.gemm_workspace_size(128, 3072, K, 64, 4) > 0
+    # prefill on the dequantize-then-dense path (M = 512: the weight dequantized
+    # into the workspace, then the dense tile)
+    a512 = to_dev(si.activations(512, K, 6), BF16)
+    wsd = torch.empty(qg.gemm_workspace_size(512, 3072, K, 64, 4), dtype=torch.uint8, device=dev)
+    assert wsd.numel() == 3072 * K * 2
     # W8A8
     p8 = si.w8a8_problem(64, 1024, 1024, True, True, tag="g-w8a8")
     A8, B8 = torch.from_numpy(p8.A).to(dev), torch.from_numpy(p8.B).to(dev)
@@ -55,6 +60,7 @@ def test_captured_calls_replay_bit_exact():
         "g_small": torch.empty((1, 3072), dtype=torch.bfloat16, device=dev),
         "g_wide": torch.empty((1, 13312), dtype=torch.bfloat16, device=dev),
         "pre": torch.empty((128, 3072), dtype=torch.bfloat16, device=dev),
+        "dense": torch.empty((512, 3072), dtype=torch.bfloat16, device=dev),
         "w8a8": torch.empty((64, 1024), dtype=torch.float16, device=dev),
     }
     state = {}
@@ -64,6 +70,7 @@ def test_captured_calls_replay_bit_exact():
         qg.gemm_w4a16(a1, w_wide[0], w_wide[1], w_wide[2], None, 64, out=outs["g_wide"])
         state["emb"] = qg.embed_w4(ids, w_wide[0], w_wide[1], w_wide[2], 64)
         qg.gemm_w4a16(a128, wp[0], wp[1], wp[2], wp[3], 64, out=outs["pre"], workspace=ws)
+        qg.gemm_w4a16(a512, wp[0], wp[1], wp[2], wp[3], 64, out=outs["dense"], workspace=wsd)
         qg.gemm_w8a8(A8, B8, r8, c8, out=outs["w8a8"], workspace=ws8)
         state["moe"] = qg.moe_grouped(mx, ml, w1, s1, z1, w2, s2, z2, 2, 64, workspace=mws)
 
