@@ -335,7 +335,7 @@ def test_prefill_tiles_integer_exact(tile, m):
     assert np.array_equal(got, _exact_expected(Cref, BF16))
 
 
-@pytest.mark.parametrize("tile", ["X", "L", "M", "S", "P256", "P128", "P64"])
+@pytest.mark.parametrize("tile", ["X", "L", "M", "S", "P256", "P128", "P64", "W256", "W256N", "W128", "W64"])
 def test_prefill_tiles_w8_integer_exact(tile):
     p = si.w8_exact_problem(200, 256, 576, seed=9, dtype=FP16, bias_dtype=FP16)
     Cref = oracle.gemm_w8(p.A, p.codes, p.scale, -1, FP16, p.bias, FP16)
@@ -356,7 +356,8 @@ def test_prefill_dma_tile_integer_exact(tile, group, m, n, k, dtype):
     assert np.array_equal(got, _exact_expected(Cref, dtype))
 
 
-@pytest.mark.parametrize("tile", ["D8", "D8N", "D64", "D128", "X", "P256", "P128", "P64"])
+@pytest.mark.parametrize("tile", ["D8", "D8N", "D64", "D128", "X", "P256", "P128", "P64", "W256", "W256N", "W128",
+                                  "W64"])
 def test_prefill_dma_tile_w8_integer_exact(tile):
     p = si.w8_exact_problem(300, 512, 576, seed=4, dtype=FP16, bias_dtype=FP16)
     Cref = oracle.gemm_w8(p.A, p.codes, p.scale, -1, FP16, p.bias, FP16)
@@ -428,6 +429,40 @@ def test_dense_path_taken_by_size_equals_forced_tile(m, n, k, group, tile):
     rows, cols = rng.integers(0, m, 128), rng.integers(0, n, 128)
     ref = oracle.gemm_w4_at(p.A, p.packed, p.scale, p.zero, group, rows, cols, BF16, p.bias, BF16)
     assert np.abs(C[rows, cols] - ref).max() / np.abs(ref).max() <= TOL[BF16]
+
+
+@pytest.mark.parametrize("tile", ["W256", "W256N", "W128", "W64"])
+@pytest.mark.parametrize("dtype", [FP16, BF16])
+@pytest.mark.parametrize("m,k", [(130, 1152), (300, 576), (1, 128)])
+def test_w8_code_tile_equals_fused_tile_bitwise(tile, dtype, m, k):
+    # int8 codes direct-loaded into LDS and converted after the read: the same
+    # exact codes, accumulated in the same order as the fused tile, with the
+    # channel scale and bias applied the same way -- identical bits.
+    p = si.w8_problem(m, 768, k, group=-1, tag="w8dir", dtype=dtype, bias_dtype=FP16)
+    qg.set_override(prefill_tile="D8")
+    fused = _run_w8(p, "prefill")
+    qg.set_override(prefill_tile=tile)
+    direct = _run_w8(p, "prefill")
+    assert torch.equal(fused.view(torch.int16), direct.view(torch.int16))
+
+
+@pytest.mark.parametrize("m,n,tile", [(512, 3584, "W64"), (1024, 3584, "W128"), (128, 18944, "W128")])
+def test_w8_code_tile_taken_by_size(m, n, tile):
+    # int8 per channel, one round of 64 x 128 or 128 x 128 tiles: the automatic
+    # choice is the code-converting tile (no workspace), bit-equal to it forced;
+    # sampled outputs within the fp16 tolerance of the oracle.
+    k = 3584
+    p = si.w8_problem(m, n, k, group=-1, tag="w8dir-auto", dtype=FP16, bias_dtype=FP16)
+    assert qg.gemm_workspace_size(m, n, k, -1, 8) == 0
+    auto = _run_w8(p, "prefill")
+    qg.set_override(prefill_tile=tile)
+    forced = _run_w8(p, "prefill")
+    assert torch.equal(auto.view(torch.int16), forced.view(torch.int16))
+    C = auto.float().cpu().numpy()
+    rng = np.random.default_rng(m + n)
+    rows, cols = rng.integers(0, m, 96), rng.integers(0, n, 96)
+    ref = oracle.gemm_w8_at(p.A, p.codes, p.scale, rows, cols, -1, FP16, p.bias, FP16)
+    assert np.abs(C[rows, cols] - ref).max() / np.abs(ref).max() <= TOL[FP16]
 
 
 @pytest.mark.parametrize("tile", DENSE_TILES)

@@ -54,9 +54,10 @@ bool parse(const char *spec, Override &o) {
       else if (v == "prefill") o.path = kPathPrefill;
       else return false;
     } else if (k == "prefill_tile") {
-      static const char *names[] = {"X", "D8", "D8N", "D64", "D128", "L", "M", "S", "P256", "P128", "P64"};
+      static const char *names[] = {"X", "D8", "D8N", "D64", "D128", "L", "M", "S", "P256", "P128", "P64",
+                                    "W256", "W256N", "W128", "W64"};
       int t = -1;
-      for (int i = 0; i < 11; ++i)
+      for (int i = 0; i < 15; ++i)
         if (v == names[i]) t = i;
       if (t < 0 && v != "auto") return false;
       o.prefill_tile = t;

@@ -13,6 +13,7 @@
 #include "qg_launch.hpp"
 #include "tile_big.hpp"
 #include "tile_dense.hpp"
+#include "tile_w8dir.hpp"
 #include "tile_gemm.hpp"
 
 namespace qg {
@@ -231,6 +232,24 @@ __global__ __launch_bounds__(Cfg::NTHR) void k_dense(DenseProblem p, int tiles_n
   dense_tile_gemm<Cfg, ACT>(p, tm, tn, L);
 }
 
+// int8 codes with one scale per channel, converted after the LDS read.
+template <class Cfg, int ACT>
+__global__ __launch_bounds__(Cfg::NTHR) void k_w8dir(W8DirProblem p, int tiles_n) {
+  constexpr int SA = Cfg::STAGE_A, SB = Cfg::STAGE_B;
+  __shared__ __attribute__((aligned(16))) char a0[SA];
+  __shared__ __attribute__((aligned(16))) char a1[SA];
+  __shared__ __attribute__((aligned(16))) char a2[Cfg::NS > 2 ? SA : 16];
+  __shared__ __attribute__((aligned(16))) char a3[Cfg::NS > 3 ? SA : 16];
+  __shared__ __attribute__((aligned(16))) char b0[SB];
+  __shared__ __attribute__((aligned(16))) char b1[SB];
+  __shared__ __attribute__((aligned(16))) char b2[Cfg::NS > 2 ? SB : 16];
+  __shared__ __attribute__((aligned(16))) char b3[Cfg::NS > 3 ? SB : 16];
+  const W8DirLds L{{a0, a1, a2, a3}, {b0, b1, b2, b3}};
+  int tm, tn;
+  grouped_tile(xcd_linear_id(), gridDim.x / tiles_n, tiles_n, tm, tn);
+  w8dir_tile_gemm<Cfg, ACT>(p, tm, tn, L);
+}
+
 namespace {
 
 using CfgX = TileCfg<256, 256, 2, 4>;   // 8 waves, 128x64 per wave
@@ -251,6 +270,11 @@ using CfgS = TileCfg<64, 64, 2, 2, 2>;
 using CfgP256 = DenseCfg<256, 256, 2, 4, 2>;   // 8 waves of 128 x 64, 2 stages
 using CfgP128 = DenseCfg<128, 128, 2, 4, 4>;   // 8 waves of 64 x 32, 4 stages
 using CfgP64 = DenseCfg<64, 128, 2, 4, 4>;     // 8 waves of 32 x 32, 4 stages
+// int8 per-channel tiles with the codes converted after the LDS read.
+using CfgW256 = W8DirCfg<256, 256, 2, 4, 3>;   // 8 waves of 128 x 64, 3 stages
+using CfgW256N = W8DirCfg<256, 128, 4, 2, 3>;  // 8 waves of 64 x 64, 3 stages
+using CfgW128 = W8DirCfg<128, 128, 2, 4, 4>;   // 8 waves of 64 x 32, 4 stages
+using CfgW64 = W8DirCfg<64, 128, 2, 4, 4>;     // 8 waves of 32 x 32, 4 stages
 
 // K slices of one launch: partials in `part` (nullptr: no split).
 struct Split {
@@ -510,8 +534,60 @@ hipError_t run_dense(int tile, const GemmArgs &a, hipStream_t s) {
   }
 }
 
+// int8 per channel, codes converted after the LDS read: the tile, or -1 for
+// the other tiles.  The operands must fit 32-bit buffer offsets.  By size:
+// up to 1024 rows, the 64 x 128 tile when its tiles number between half and
+// all of the CUs (one round, most CUs busy), else the 128 x 128 tile on the
+// same condition.  Measured on MI355X at K = 3584 (fp16, weights streamed),
+// against the other tiles' choice: m = 512, n = 3584 33.5 -> 26.0 us
+// (64 x 128); m = 1024, n = 3584 44.4 -> 38.8 us, m = 128, n = 18944
+// 52.8 -> 34.4 us (128 x 128); m = 32 / 64, n = 18944 31.1 / 32.9 -> 22.7 /
+// 25.5 us (64 x 128).  With fewer tiles (no K slices here: m <= 256,
+// n = 3584, 16-21 against 21-30 us) or more than a round of them (m = 256
+// and 512, n = 18944; m >= 2048) the other tiles are faster.
+int choose_w8dir_tile(const GemmArgs &a) {
+  const uint64_t lim = uint64_t(1) << 31;
+  if (uint64_t(a.M) * a.K * 2 >= lim || uint64_t(a.N) * a.K >= lim) return -1;
+  switch (dispatch_override().prefill_tile) {
+    case kW256: return a.N % 256 == 0 ? kW256 : -1;
+    case kW256N: return a.N % 128 == 0 ? kW256N : -1;
+    case kW128: return a.N % 128 == 0 ? kW128 : -1;
+    case kW64: return a.N % 128 == 0 ? kW64 : -1;
+    case -1: break;
+    default: return -1;   // another tile is forced
+  }
+  if (a.N % 128 != 0 || a.M > 1024) return -1;
+  const int cus = device_cus();
+  const long t64 = static_cast<long>((a.M + 63) / 64) * (a.N / 128);
+  const long t128 = static_cast<long>((a.M + 127) / 128) * (a.N / 128);
+  if (2 * t64 >= cus && t64 <= cus) return kW64;
+  if (2 * t128 >= cus && t128 <= cus) return kW128;
+  return -1;
+}
+
+template <class Cfg, int ACT>
+hipError_t launch_w8dir(const GemmArgs &a, hipStream_t s) {
+  const W8DirProblem p{a.A, static_cast<const uint8_t *>(a.B), a.S, a.bias, a.bias_dt, a.C, a.M, a.N, a.K};
+  const int tm = (a.M + Cfg::BM - 1) / Cfg::BM, tn = a.N / Cfg::BN;
+  hipLaunchKernelGGL((k_w8dir<Cfg, ACT>), dim3(tm * tn), dim3(Cfg::NTHR), 0, s, p, tn);
+  return hipGetLastError();
+}
+
+template <int ACT>
+hipError_t run_w8dir(int tile, const GemmArgs &a, hipStream_t s) {
+  switch (tile) {
+    case kW256: return launch_w8dir<CfgW256, ACT>(a, s);
+    case kW256N: return launch_w8dir<CfgW256N, ACT>(a, s);
+    case kW128: return launch_w8dir<CfgW128, ACT>(a, s);
+    default: return launch_w8dir<CfgW64, ACT>(a, s);
+  }
+}
+
 template <int ACT, int WBITS, bool GS8 = false, bool PC = false>
 hipError_t dispatch(const GemmArgs &a, hipStream_t s) {
+  if constexpr (WBITS == 8 && !GS8) {
+    if (const int w = choose_w8dir_tile(a); w >= 0) return run_w8dir<ACT>(w, a, s);
+  }
   Plan pl = plan_prefill(a, WBITS, GS8);
   if (is_dense(pl.tile)) {
     if (a.ws && a.ws_bytes >= pl.bytes) return run_dense<ACT, WBITS, GS8>(pl.tile, a, s);
@@ -531,6 +607,7 @@ hipError_t dispatch(const GemmArgs &a, hipStream_t s) {
 }  // namespace
 
 size_t prefill_workspace_bytes(const GemmArgs &a, int wbits) {
+  if (wbits == 8 && a.group == 0 && choose_w8dir_tile(a) >= 0) return 0;
   const Plan pl = plan_prefill(a, wbits, wbits == 8 && a.group > 0);
   return (pl.split.nsplit > 1 || is_dense(pl.tile)) ? pl.bytes : 0;
 }
