@@ -198,6 +198,15 @@ __device__ __forceinline__ void w8dir_tile_gemm(const W8DirProblem &p, int tm, i
     read_a(As, 3, a1);
     mma(H1{}, a0, b0);   // ks 2
     mma(H1{}, a1, b1);   // ks 3
+    // Fragment reads one sub-step ahead of the matrix instructions.
+    constexpr int NM = TM * TN;
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * (TM + TN), 0);   // reads: ks 0, 1 (codes for all four)
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);              // MFMA ks 0
+    __builtin_amdgcn_sched_group_barrier(0x100, TM, 0);              // reads ks 2
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);              // MFMA ks 1
+    __builtin_amdgcn_sched_group_barrier(0x100, TM, 0);              // reads ks 3
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);              // MFMA ks 2
+    __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);              // MFMA ks 3
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(WAIT_NEXT);
     barrier();
