@@ -88,9 +88,8 @@ int qg_version(void);
  *   prefill_tile=auto|X|D8|D8N|D64|D128|L|M|S|P256|P128|P64|W256|W256N|W128|W64
  *                                   the prefill tile (P: dequantize-then-
  *                                   dense, which needs n * k * 2 bytes of
- *                                   workspace; W: int8 with one scale per
- *                                   channel, codes converted after the LDS
- *                                   read)
+ *                                   workspace; W: int8, codes converted
+ *                                   after the LDS read)
  *   splitk=<n>                      prefill K slices (1: none), n >= 1
  *   moe_tile=auto|S                 S: the MoE on the 128 x 128 tile
  *   w8a8_tile=auto|T256|T256N|T128|T64   the W8A8 tile (also for m <= 16)

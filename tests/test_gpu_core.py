@@ -206,7 +206,8 @@ def test_w8_grouped_integer_exact(m, n, k, group, path, dtype):
     assert bad.size == 0, f"{len(bad)} mismatches, first at {bad[:4].tolist()}"
 
 
-@pytest.mark.parametrize("tile", ["D8", "D8N", "D64", "D128", "X", "L", "M", "S", "P256", "P128", "P64"])
+@pytest.mark.parametrize("tile", ["D8", "D8N", "D64", "D128", "X", "L", "M", "S", "P256", "P128", "P64",
+                                  "W256", "W256N", "W128", "W64"])
 @pytest.mark.parametrize("group", [64, 128])
 def test_prefill_tiles_w8_grouped_integer_exact(tile, group):
     p = si.w8_exact_problem(300, 512, 1024, seed=group, dtype=BF16, bias_dtype=FP16, group=group)
@@ -434,11 +435,15 @@ def test_dense_path_taken_by_size_equals_forced_tile(m, n, k, group, tile):
 @pytest.mark.parametrize("tile", ["W256", "W256N", "W128", "W64"])
 @pytest.mark.parametrize("dtype", [FP16, BF16])
 @pytest.mark.parametrize("m,k", [(130, 1152), (300, 576), (1, 128)])
-def test_w8_code_tile_equals_fused_tile_bitwise(tile, dtype, m, k):
+@pytest.mark.parametrize("group", [-1, 64, 128])
+def test_w8_code_tile_equals_fused_tile_bitwise(tile, dtype, m, k, group):
     # int8 codes direct-loaded into LDS and converted after the read: the same
-    # exact codes, accumulated in the same order as the fused tile, with the
-    # channel scale and bias applied the same way -- identical bits.
-    p = si.w8_problem(m, 768, k, group=-1, tag="w8dir", dtype=dtype, bias_dtype=FP16)
+    # weights (exact codes, or q * s rounded once for group scales),
+    # accumulated in the same order as the fused tile, with the channel scale
+    # and bias applied the same way -- identical bits.
+    if k % group:
+        pytest.skip("k is not a multiple of the group")
+    p = si.w8_problem(m, 768, k, group=group, tag="w8dir", dtype=dtype, bias_dtype=FP16)
     qg.set_override(prefill_tile="D8")
     fused = _run_w8(p, "prefill")
     qg.set_override(prefill_tile=tile)

@@ -232,8 +232,8 @@ __global__ __launch_bounds__(Cfg::NTHR) void k_dense(DenseProblem p, int tiles_n
   dense_tile_gemm<Cfg, ACT>(p, tm, tn, L);
 }
 
-// int8 codes with one scale per channel, converted after the LDS read.
-template <class Cfg, int ACT>
+// int8 codes, converted after the LDS read (GS: group scales).
+template <class Cfg, int ACT, bool GS>
 __global__ __launch_bounds__(Cfg::NTHR) void k_w8dir(W8DirProblem p, int tiles_n) {
   constexpr int SA = Cfg::STAGE_A, SB = Cfg::STAGE_B;
   __shared__ __attribute__((aligned(16))) char a0[SA];
@@ -247,7 +247,7 @@ __global__ __launch_bounds__(Cfg::NTHR) void k_w8dir(W8DirProblem p, int tiles_n
   const W8DirLds L{{a0, a1, a2, a3}, {b0, b1, b2, b3}};
   int tm, tn;
   grouped_tile(xcd_linear_id(), gridDim.x / tiles_n, tiles_n, tm, tn);
-  w8dir_tile_gemm<Cfg, ACT>(p, tm, tn, L);
+  w8dir_tile_gemm<Cfg, ACT, GS>(p, tm, tn, L);
 }
 
 namespace {
@@ -270,7 +270,7 @@ using CfgS = TileCfg<64, 64, 2, 2, 2>;
 using CfgP256 = DenseCfg<256, 256, 2, 4, 2>;   // 8 waves of 128 x 64, 2 stages
 using CfgP128 = DenseCfg<128, 128, 2, 4, 4>;   // 8 waves of 64 x 32, 4 stages
 using CfgP64 = DenseCfg<64, 128, 2, 4, 4>;     // 8 waves of 32 x 32, 4 stages
-// int8 per-channel tiles with the codes converted after the LDS read.
+// int8 tiles with the codes converted after the LDS read.
 using CfgW256 = W8DirCfg<256, 256, 2, 4, 3>;   // 8 waves of 128 x 64, 3 stages
 using CfgW256N = W8DirCfg<256, 128, 4, 2, 3>;  // 8 waves of 64 x 64, 3 stages
 using CfgW128 = W8DirCfg<128, 128, 2, 4, 4>;   // 8 waves of 64 x 32, 4 stages
@@ -534,8 +534,9 @@ hipError_t run_dense(int tile, const GemmArgs &a, hipStream_t s) {
   }
 }
 
-// int8 per channel, codes converted after the LDS read: the tile, or -1 for
-// the other tiles.  The operands must fit 32-bit buffer offsets.  By size:
+// int8 (channel or group scales), codes converted after the LDS read: the
+// tile, or -1 for the other tiles.  The operands must fit 32-bit buffer
+// offsets.  By size:
 // up to 1024 rows, the 64 x 128 tile when its tiles number between half and
 // all of the CUs (one round, most CUs busy), else the 128 x 128 tile on the
 // same condition.  Measured on MI355X at K = 3584 (fp16, weights streamed),
@@ -556,7 +557,10 @@ int choose_w8dir_tile(const GemmArgs &a) {
     case -1: break;
     default: return -1;   // another tile is forced
   }
-  if (a.N % 128 != 0 || a.M > 1024) return -1;
+  // Group scales (q s rounded per fragment: about 2.5x the conversion work)
+  // measured slower than the dequantize-then-dense path at m = 1024,
+  // n = 3584, group 128 (44.8 against 41.8 us): forced only.
+  if (a.group > 0 || a.N % 128 != 0 || a.M > 1024) return -1;
   const int cus = device_cus();
   const long t64 = static_cast<long>((a.M + 63) / 64) * (a.N / 128);
   const long t128 = static_cast<long>((a.M + 127) / 128) * (a.N / 128);
@@ -565,28 +569,29 @@ int choose_w8dir_tile(const GemmArgs &a) {
   return -1;
 }
 
-template <class Cfg, int ACT>
+template <class Cfg, int ACT, bool GS>
 hipError_t launch_w8dir(const GemmArgs &a, hipStream_t s) {
-  const W8DirProblem p{a.A, static_cast<const uint8_t *>(a.B), a.S, a.bias, a.bias_dt, a.C, a.M, a.N, a.K};
+  const W8DirProblem p{a.A, static_cast<const uint8_t *>(a.B), a.S, a.bias, a.bias_dt, a.C,
+                       a.M, a.N, a.K, GS ? a.group : 0};
   const int tm = (a.M + Cfg::BM - 1) / Cfg::BM, tn = a.N / Cfg::BN;
-  hipLaunchKernelGGL((k_w8dir<Cfg, ACT>), dim3(tm * tn), dim3(Cfg::NTHR), 0, s, p, tn);
+  hipLaunchKernelGGL((k_w8dir<Cfg, ACT, GS>), dim3(tm * tn), dim3(Cfg::NTHR), 0, s, p, tn);
   return hipGetLastError();
 }
 
-template <int ACT>
+template <int ACT, bool GS>
 hipError_t run_w8dir(int tile, const GemmArgs &a, hipStream_t s) {
   switch (tile) {
-    case kW256: return launch_w8dir<CfgW256, ACT>(a, s);
-    case kW256N: return launch_w8dir<CfgW256N, ACT>(a, s);
-    case kW128: return launch_w8dir<CfgW128, ACT>(a, s);
-    default: return launch_w8dir<CfgW64, ACT>(a, s);
+    case kW256: return launch_w8dir<CfgW256, ACT, GS>(a, s);
+    case kW256N: return launch_w8dir<CfgW256N, ACT, GS>(a, s);
+    case kW128: return launch_w8dir<CfgW128, ACT, GS>(a, s);
+    default: return launch_w8dir<CfgW64, ACT, GS>(a, s);
   }
 }
 
 template <int ACT, int WBITS, bool GS8 = false, bool PC = false>
 hipError_t dispatch(const GemmArgs &a, hipStream_t s) {
-  if constexpr (WBITS == 8 && !GS8) {
-    if (const int w = choose_w8dir_tile(a); w >= 0) return run_w8dir<ACT>(w, a, s);
+  if constexpr (WBITS == 8) {
+    if (const int w = choose_w8dir_tile(a); w >= 0) return run_w8dir<ACT, GS8>(w, a, s);
   }
   Plan pl = plan_prefill(a, WBITS, GS8);
   if (is_dense(pl.tile)) {
@@ -607,7 +612,7 @@ hipError_t dispatch(const GemmArgs &a, hipStream_t s) {
 }  // namespace
 
 size_t prefill_workspace_bytes(const GemmArgs &a, int wbits) {
-  if (wbits == 8 && a.group == 0 && choose_w8dir_tile(a) >= 0) return 0;
+  if (wbits == 8 && choose_w8dir_tile(a) >= 0) return 0;
   const Plan pl = plan_prefill(a, wbits, wbits == 8 && a.group > 0);
   return (pl.split.nsplit > 1 || is_dense(pl.tile)) ? pl.bytes : 0;
 }

@@ -1,9 +1,13 @@
-// tile_w8dir.hpp -- W8A16 with one scale per output channel on gfx950: the
+// tile_w8dir.hpp -- W8A16 on gfx950 (one scale per output channel, or per
+// channel and 64- or 128-k group): the
 // int8 weight codes go from their tiled layout straight into LDS (buffer_load
 // ... lds, one 1 KiB block of 16 rows x 64 k per load instruction, no VGPRs),
 // and each wave turns the code fragments it reads into exact 16-bit operands
-// in registers (the codes are small integers, so nothing is rounded); the
-// channel scale is applied to the finished sum.  Against the fused tiles,
+// in registers (the codes are small integers, so nothing is rounded); a
+// channel scale is applied to the finished sum, a group scale during the
+// conversion (q s rounded once, as the fused tiles do: a lane's 8 codes lie
+// in one group, so one scale per row and step, loaded with the step's
+// direct loads into a register ring).  Against the fused tiles,
 // which convert every code once per workgroup and stage the 16-bit weights
 // in LDS, the weight bytes in LDS halve and the conversion's LDS writes go
 // away, at the price of converting each code once per wave row.
@@ -28,17 +32,19 @@
 #include <type_traits>
 
 #include "qg_common.hpp"
+#include "tile_gemm.hpp"
 
 namespace qg {
 
 struct W8DirProblem {
   const uint16_t *A;          // [M, K]
   const uint8_t *B;           // tiled int8 codes (offset binary), [N, K]
-  const uint16_t *S;          // [N] channel scales, A's type
+  const uint16_t *S;          // [N] channel scales or [N, K / group] group scales, A's type
   const uint16_t *bias;       // [N] or null
   int bias_dt;
   uint16_t *C;                // [M, N]
   int M, N, K;
+  int group;                  // 64 or 128 (group scales), 0 (channel scales)
 };
 
 template <int BM_, int BN_, int WM_, int WN_, int NS_>
@@ -55,7 +61,7 @@ struct W8DirCfg {
   static_assert(NTHR == 512, "eight waves");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0 && A_DMA >= 1 && B_DMA >= 1, "tile shape");
   static_assert(NS >= 2 && NS <= 4 && NS * (STAGE_A + STAGE_B) <= 160 * 1024, "LDS stages");
-  static_assert((NS - 2) * (A_DMA + B_DMA) < 64, "vmcnt field");
+  static_assert((NS - 2) * (A_DMA + B_DMA + TN) < 64, "vmcnt field");
 };
 
 struct W8DirLds {
@@ -66,7 +72,7 @@ struct W8DirLds {
 // s_waitcnt with vmcnt(n), lgkmcnt(0), expcnt untouched.
 constexpr int w8dir_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
 
-template <class Cfg, int ACT>
+template <class Cfg, int ACT, bool GS>
 __device__ __forceinline__ void w8dir_tile_gemm(const W8DirProblem &p, int tm, int tn,
                                                 const W8DirLds &L) {
   constexpr int TM = Cfg::TM, TN = Cfg::TN, NS = Cfg::NS;
@@ -101,6 +107,9 @@ __device__ __forceinline__ void w8dir_tile_gemm(const W8DirProblem &p, int tm, i
     const int blk = wave * Cfg::B_DMA + i;
     b_voff[i] = static_cast<uint32_t>(col_lo / 16 + blk) * static_cast<uint32_t>(K / 64) * 1024u + lane * 16;
   }
+  // Group scales: stage ST's scale of row block j of this lane's rows.
+  [[maybe_unused]] uint16_t sreg[NS][TN];
+  [[maybe_unused]] const int kg = GS ? K / p.group : 1;
   // Step `step` into stage ST; past the last step the last one is loaded
   // again (into a stage no later step reads), so every step issues the same
   // number of loads and one wait count fits all.
@@ -117,6 +126,13 @@ __device__ __forceinline__ void w8dir_tile_gemm(const W8DirProblem &p, int tm, i
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rB, (__attribute__((address_space(3))) void *)(L.b[ST] + (wave * Cfg::B_DMA + i) * Cfg::BLK_PITCH),
           16, b_voff[i], s * 1024, 0, 0);
+    if constexpr (GS) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int n = col_lo + wn * Cfg::WTN + 32 * j + (lane & 31);
+        sreg[ST][j] = p.S[static_cast<size_t>(n) * kg + (s * 64) / p.group];
+      }
+    }
   };
 
   // Fragments: sub-step ks covers k 16 ks .. 16 ks + 15 of the step; lane
@@ -157,12 +173,14 @@ __device__ __forceinline__ void w8dir_tile_gemm(const W8DirProblem &p, int tm, i
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
   // Sub-step on activation fragments a and the code slots b: the slots'
   // first (HI = 0) or last 8 bytes.
-  auto mma = [&](auto HIc, const u32x4 (&a)[TM], const u32x4 (&b)[TN]) {
-    constexpr int HI = decltype(HIc)::value;
+  auto mma = [&](auto HIc, auto STc, const u32x4 (&a)[TM], const u32x4 (&b)[TN]) {
+    constexpr int HI = decltype(HIc)::value, ST = decltype(STc)::value;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const uint32_t lo = b[j][2 * HI], hi = b[j][2 * HI + 1];
-      const u32x4 w = (ACT == kFP16) ? w8_run_to_f16(lo, hi) : w8_run_to_bf16(lo, hi);
+      u32x4 w;
+      if constexpr (GS) w = dequant_run_w8<ACT>(lo, hi, bits_to_f32<ACT>(sreg[ST][j]));
+      else w = (ACT == kFP16) ? w8_run_to_f16(lo, hi) : w8_run_to_bf16(lo, hi);
 #pragma unroll
       for (int i = 0; i < TM; ++i) acc[i][j] = mfma32x32x16<ACT>(w, a[i], acc[i][j]);
     }
@@ -176,7 +194,7 @@ __device__ __forceinline__ void w8dir_tile_gemm(const W8DirProblem &p, int tm, i
   };
   // After a step's issue, the loads of the next step are the oldest but
   // those of the NS - 2 steps after it.
-  constexpr int WAIT_NEXT = w8dir_wait((NS - 2) * (Cfg::A_DMA + Cfg::B_DMA));
+  constexpr int WAIT_NEXT = w8dir_wait((NS - 2) * (Cfg::A_DMA + Cfg::B_DMA + (GS ? TN : 0)));
 
   // Step s on stage I = s % NS: issue step s + NS - 1 into stage
   // (s - 1) % NS (last read in step s - 1, before the barrier that ended
@@ -192,12 +210,12 @@ __device__ __forceinline__ void w8dir_tile_gemm(const W8DirProblem &p, int tm, i
     read_b(Bs, 0, b0);
     read_a(As, 1, a1);
     read_b(Bs, 1, b1);
-    mma(H0{}, a0, b0);   // ks 0
+    mma(H0{}, Ic, a0, b0);   // ks 0
     read_a(As, 2, a0);
-    mma(H0{}, a1, b1);   // ks 1
+    mma(H0{}, Ic, a1, b1);   // ks 1
     read_a(As, 3, a1);
-    mma(H1{}, a0, b0);   // ks 2
-    mma(H1{}, a1, b1);   // ks 3
+    mma(H1{}, Ic, a0, b0);   // ks 2
+    mma(H1{}, Ic, a1, b1);   // ks 3
     // Fragment reads one sub-step ahead of the matrix instructions.
     constexpr int NM = TM * TN;
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * (TM + TN), 0);   // reads: ks 0, 1 (codes for all four)
@@ -250,7 +268,7 @@ __device__ __forceinline__ void w8dir_tile_gemm(const W8DirProblem &p, int tm, i
       for (int e = 0; e < 4; ++e) {
         const int col = col_lo + wn * Cfg::WTN + 32 * j + 8 * q + 4 * khalf + e;
         add[j][q][e] = p.bias ? bits_to_f32_dyn(p.bias[col], p.bias_dt) : 0.0f;
-        mul[j][q][e] = bits_to_f32<ACT>(p.S[col]);
+        mul[j][q][e] = GS ? 1.0f : bits_to_f32<ACT>(p.S[col]);
       }
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
