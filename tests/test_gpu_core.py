@@ -470,6 +470,20 @@ def test_w8_code_tile_taken_by_size(m, n, tile):
     assert np.abs(C[rows, cols] - ref).max() / np.abs(ref).max() <= TOL[FP16]
 
 
+@pytest.mark.parametrize("tile", ["P256", "P128", "P64", "W256", "W128", "W64"])
+def test_forced_wide_tile_ignored_when_n_does_not_fit(tile):
+    # n = 272 (17 channel tiles of 16) fits none of these tiles' widths: the
+    # forced choice is ignored and the call runs as if nothing were forced.
+    p8 = si.w8_problem(300, 272, 576, group=-1, tag="w8-odd-n", dtype=FP16, bias_dtype=FP16)
+    p4 = si.w4_problem(300, 272, 640, 64, tag="w4-odd-n", bias_dtype=BF16)
+    auto8, auto4 = _run_w8(p8, "prefill"), _run_w4(p4, "prefill")
+    qg.set_override(prefill_tile=tile)
+    assert qg.gemm_workspace_size(300, 272, 640, 64, 4) == 0
+    forced8, forced4 = _run_w8(p8, "prefill"), _run_w4(p4, "prefill")
+    assert torch.equal(auto8.view(torch.int16), forced8.view(torch.int16))
+    assert torch.equal(auto4.view(torch.int16), forced4.view(torch.int16))
+
+
 @pytest.mark.parametrize("tile", DENSE_TILES)
 def test_dense_path_workspace_size_and_fallback(tile):
     # The dense path asks for n * k 16-bit values of workspace; with less the
