@@ -199,7 +199,7 @@ def test_workspace_query_and_alignment():
     # bytes, at 512 .. 1024 rows with few 256 x 256 tiles (256 CUs assumed
     # without a device)
     for args in [(512, 3072, 2048, 64, 4), (1024, 3072, 2048, 128, 4), (512, 4096, 2048, -1, 4),
-                 (700, 3584, 3584, 64, 8), (1024, 3584, 3584, 128, 8)]:
+                 (1024, 2048, 2048, 64, 4), (700, 3584, 3584, 64, 8), (1024, 3584, 3584, 128, 8)]:
         assert L.qgemm_workspace_size(*args) == args[1] * args[2] * 2, args
     # int8 per channel at those sizes: the tiles that convert codes after the
     # LDS read, no workspace

@@ -409,7 +409,8 @@ int choose_fused_tile(const GemmArgs &a) {
 // caller's workspace (N K 16-bit values), then a dense tile; the operands
 // must fit its 32-bit buffer offsets.  Taken when forced, and by size where
 // the fused tiles would re-dequantize every weight for many row tiles while
-// leaving most CUs idle: 512 to 1024 rows, at least 3072 columns, fewer
+// leaving most CUs idle: 512 to 1024 rows, at least 3072 columns (2048
+// above 512 rows: M = 1024, N = 2048 28.9 -> 25.0 us; M = 512 equal), fewer
 // 256 x 256 tiles than a quarter of the CUs.  Measured on MI355X (dequant + dense
 // tile against the fused choice): W4A16 K = 2048, N = 3072: M = 512
 // 28.4 -> 21.5 us (64 x 128 tile), M = 1024 31.0 -> 27.1 us (128 x 128);
@@ -428,7 +429,8 @@ int choose_dense_tile(const GemmArgs &a) {
     default: return -1;   // a fused tile is forced
   }
   const long t8 = static_cast<long>((a.M + 255) / 256) * (a.N / 256);
-  if (a.M >= 512 && a.M <= 1024 && a.N >= 3072 && a.N % 128 == 0 && 4 * t8 < device_cus())
+  if (a.M >= 512 && a.M <= 1024 && (a.N >= 3072 || (a.N >= 2048 && a.M > 512)) && a.N % 128 == 0 &&
+      4 * t8 < device_cus())
     return a.M <= 512 ? kP64 : kP128;
   return -1;
 }
