@@ -85,11 +85,13 @@ int qg_version(void);
  * spec is a comma-separated list of key=value pairs:
  *   path=auto|decode|prefill        the GEMM path (else by m: decode for
  *                                   m <= 16)
- *   prefill_tile=auto|X|D8|D8N|D64|D128|L|M|S|P256|P128|P64|W256|W256N|W128|W64
+ *   prefill_tile=auto|X|D8|D8N|D64|D128|L|M|S|P256|P128|P64|W256|W256N|W128|W64|WX
  *                                   the prefill tile (P: dequantize-then-
  *                                   dense, which needs n * k * 2 bytes of
  *                                   workspace; W: int8, codes converted
- *                                   after the LDS read)
+ *                                   after the LDS read; WX: 256 x 256 tiles
+ *                                   and 128 x 128 quarters in one launch,
+ *                                   forced: half the large tiles each)
  *   splitk=<n>                      prefill K slices (1: none), n >= 1
  *   moe_tile=auto|S                 S: the MoE on the 128 x 128 tile
  *   w8a8_tile=auto|T256|T256N|T128|T64   the W8A8 tile (also for m <= 16)

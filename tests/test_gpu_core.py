@@ -207,7 +207,7 @@ def test_w8_grouped_integer_exact(m, n, k, group, path, dtype):
 
 
 @pytest.mark.parametrize("tile", ["D8", "D8N", "D64", "D128", "X", "L", "M", "S", "P256", "P128", "P64",
-                                  "W256", "W256N", "W128", "W64"])
+                                  "W256", "W256N", "W128", "W64", "WX"])
 @pytest.mark.parametrize("group", [64, 128])
 def test_prefill_tiles_w8_grouped_integer_exact(tile, group):
     p = si.w8_exact_problem(300, 512, 1024, seed=group, dtype=BF16, bias_dtype=FP16, group=group)
@@ -336,7 +336,8 @@ def test_prefill_tiles_integer_exact(tile, m):
     assert np.array_equal(got, _exact_expected(Cref, BF16))
 
 
-@pytest.mark.parametrize("tile", ["X", "L", "M", "S", "P256", "P128", "P64", "W256", "W256N", "W128", "W64"])
+@pytest.mark.parametrize("tile", ["X", "L", "M", "S", "P256", "P128", "P64", "W256", "W256N", "W128", "W64",
+                                  "WX"])
 def test_prefill_tiles_w8_integer_exact(tile):
     p = si.w8_exact_problem(200, 256, 576, seed=9, dtype=FP16, bias_dtype=FP16)
     Cref = oracle.gemm_w8(p.A, p.codes, p.scale, -1, FP16, p.bias, FP16)
@@ -358,7 +359,7 @@ def test_prefill_dma_tile_integer_exact(tile, group, m, n, k, dtype):
 
 
 @pytest.mark.parametrize("tile", ["D8", "D8N", "D64", "D128", "X", "P256", "P128", "P64", "W256", "W256N", "W128",
-                                  "W64"])
+                                  "W64", "WX"])
 def test_prefill_dma_tile_w8_integer_exact(tile):
     p = si.w8_exact_problem(300, 512, 576, seed=4, dtype=FP16, bias_dtype=FP16)
     Cref = oracle.gemm_w8(p.A, p.codes, p.scale, -1, FP16, p.bias, FP16)
@@ -451,11 +452,29 @@ def test_w8_code_tile_equals_fused_tile_bitwise(tile, dtype, m, k, group):
     assert torch.equal(fused.view(torch.int16), direct.view(torch.int16))
 
 
-@pytest.mark.parametrize("m,n,tile", [(512, 3584, "W64"), (1024, 3584, "W128"), (128, 18944, "W128")])
+@pytest.mark.parametrize("dtype", [FP16, BF16])
+@pytest.mark.parametrize("m,n,k", [(520, 2048, 1152), (700, 2048, 576), (1024, 4096, 640)])
+@pytest.mark.parametrize("group", [-1, 64])
+def test_w8_mixed_tile_equals_fused_tile_bitwise(dtype, m, n, k, group):
+    # 256 x 256 tiles for the first half of the large tiles, 128 x 128
+    # quarters for the rest (those below the last row skipped), one launch:
+    # the fused tile's bits (m = 520: a quarter row past the end).
+    p = si.w8_problem(m, n, k, group=group, tag="w8mix", dtype=dtype, bias_dtype=FP16)
+    qg.set_override(prefill_tile="D8")
+    fused = _run_w8(p, "prefill")
+    qg.set_override(prefill_tile="WX")
+    mixed = _run_w8(p, "prefill")
+    assert torch.equal(fused.view(torch.int16), mixed.view(torch.int16))
+
+
+@pytest.mark.parametrize("m,n,tile", [(512, 3584, "W64"), (1024, 3584, "W128"), (128, 18944, "W128"),
+                                      (1024, 18944, "WX")])
 def test_w8_code_tile_taken_by_size(m, n, tile):
-    # int8 per channel, one round of 64 x 128 or 128 x 128 tiles: the automatic
-    # choice is the code-converting tile (no workspace), bit-equal to it forced;
-    # sampled outputs within the fp16 tolerance of the oracle.
+    # int8 per channel, one round of 64 x 128 or 128 x 128 tiles, or whole
+    # rounds of 256 x 256 tiles with at most a quarter-round left: the automatic
+    # choice is the code-converting tile (no workspace), bit-equal to it forced
+    # (WX forced splits the large tiles differently: same bits); sampled
+    # outputs within the fp16 tolerance of the oracle.
     k = 3584
     p = si.w8_problem(m, n, k, group=-1, tag="w8dir-auto", dtype=FP16, bias_dtype=FP16)
     assert qg.gemm_workspace_size(m, n, k, -1, 8) == 0

@@ -55,9 +55,9 @@ bool parse(const char *spec, Override &o) {
       else return false;
     } else if (k == "prefill_tile") {
       static const char *names[] = {"X", "D8", "D8N", "D64", "D128", "L", "M", "S", "P256", "P128", "P64",
-                                    "W256", "W256N", "W128", "W64"};
+                                    "W256", "W256N", "W128", "W64", "WX"};
       int t = -1;
-      for (int i = 0; i < 15; ++i)
+      for (int i = 0; i < static_cast<int>(sizeof(names) / sizeof(names[0])); ++i)
         if (v == names[i]) t = i;
       if (t < 0 && v != "auto") return false;
       o.prefill_tile = t;

@@ -21,12 +21,12 @@ namespace qg {
 // Hardware sends workgroup b to XCD b % 8.  Renumber so each XCD walks a
 // contiguous run of tiles in M-major order: neighbours on one XCD share their
 // activation rows in that XCD's L2.
-__device__ __forceinline__ int xcd_linear_id() {
-  const int bid = blockIdx.x, nblk = gridDim.x;
+__device__ __forceinline__ int xcd_id(int bid, int nblk) {
   const int xcd = bid & 7, loc = bid >> 3;
   const int per = nblk >> 3, rem = nblk & 7;
   return (xcd < rem) ? xcd * (per + 1) + loc : rem * (per + 1) + (xcd - rem) * per + loc;
 }
+__device__ __forceinline__ int xcd_linear_id() { return xcd_id(blockIdx.x, gridDim.x); }
 
 // Tile of linear position `id` (after the XCD renumbering): groups of up to
 // four rows of tiles, walked column by column, so the weight tile of one
@@ -248,6 +248,42 @@ __global__ __launch_bounds__(Cfg::NTHR) void k_w8dir(W8DirProblem p, int tiles_n
   int tm, tn;
   grouped_tile(xcd_linear_id(), gridDim.x / tiles_n, tiles_n, tm, tn);
   w8dir_tile_gemm<Cfg, ACT, GS>(p, tm, tn, L);
+}
+
+// One launch, two tile sizes (int8 codes converted after the LDS read): the
+// first `big` workgroups (whole rounds of the CUs, a multiple of 8) take the
+// first `big` of the 256 x 256 tiles, the rest each take a 128 x 128
+// quarter of the remaining ones, so the last, partial round is four times
+// as finely cut and ends about when a quarter tile would.  Both sizes share
+// the three LDS stages (a quarter tile's stage fits in the front of a large
+// one's, each stage still a separate object) and give the fused tiles' bits.
+struct CfgWXBig : W8DirCfg<256, 256, 2, 4, 3> {};
+struct CfgWXSmall : W8DirCfg<128, 128, 2, 4, 3> {};
+
+template <int ACT, bool GS>
+__global__ __launch_bounds__(512) void k_w8dir_mixed(W8DirProblem p, int tiles_n, int tiles, int big) {
+  constexpr int SA = CfgWXBig::STAGE_A, SB = CfgWXBig::STAGE_B;
+  static_assert(CfgWXSmall::STAGE_A <= SA && CfgWXSmall::STAGE_B <= SB && CfgWXSmall::NS <= CfgWXBig::NS,
+                "quarter-tile stages inside the large ones");
+  __shared__ __attribute__((aligned(16))) char a0[SA];
+  __shared__ __attribute__((aligned(16))) char a1[SA];
+  __shared__ __attribute__((aligned(16))) char a2[SA];
+  __shared__ __attribute__((aligned(16))) char b0[SB];
+  __shared__ __attribute__((aligned(16))) char b1[SB];
+  __shared__ __attribute__((aligned(16))) char b2[SB];
+  const W8DirLds L{{a0, a1, a2, a2}, {b0, b1, b2, b2}};
+  const int bid = blockIdx.x;
+  int tm, tn;
+  if (bid < big) {
+    grouped_tile(xcd_id(bid, big), tiles / tiles_n, tiles_n, tm, tn);
+    w8dir_tile_gemm<CfgWXBig, ACT, GS>(p, tm, tn, L);
+    return;
+  }
+  const int u = xcd_id(bid - big, gridDim.x - big);
+  grouped_tile(big + u / 4, tiles / tiles_n, tiles_n, tm, tn);
+  const int sm = 2 * tm + ((u >> 1) & 1), sn = 2 * tn + (u & 1);
+  if (sm * CfgWXSmall::BM >= p.M) return;   // quarter below the last row
+  w8dir_tile_gemm<CfgWXSmall, ACT, GS>(p, sm, sn, L);
 }
 
 namespace {
@@ -547,7 +583,13 @@ hipError_t run_dense(int tile, const GemmArgs &a, hipStream_t s) {
 // 52.8 -> 34.4 us (128 x 128); m = 32 / 64, n = 18944 31.1 / 32.9 -> 22.7 /
 // 25.5 us (64 x 128).  With fewer tiles (no K slices here: m <= 256,
 // n = 3584, 16-21 against 21-30 us) or more than a round of them (m = 256
-// and 512, n = 18944; m >= 2048) the other tiles are faster.
+// and 512, n = 18944; m >= 2048) the other tiles are faster -- except where
+// whole rounds of 256 x 256 tiles leave at most a quarter-round of them
+// over: then the mixed launch, whose leftover quarters end the last round
+// early (m = 1024, k = 3584: n = 18944 180.0 -> 143.9 us, n = 16640
+// 177.9 -> 136.7 us against the fused 256 x 256 tile; with more left over,
+// m = 1280 or 2048, n = 18944, or n = 22016, and with group scales it
+// measured 1-8 % slower than the other tiles' choice).
 int choose_w8dir_tile(const GemmArgs &a) {
   const uint64_t lim = uint64_t(1) << 31;
   if (uint64_t(a.M) * a.K * 2 >= lim || uint64_t(a.N) * a.K >= lim) return -1;
@@ -556,14 +598,21 @@ int choose_w8dir_tile(const GemmArgs &a) {
     case kW256N: return a.N % 128 == 0 ? kW256N : -1;
     case kW128: return a.N % 128 == 0 ? kW128 : -1;
     case kW64: return a.N % 128 == 0 ? kW64 : -1;
+    case kWX: return a.N % 256 == 0 ? kWX : -1;
     case -1: break;
     default: return -1;   // another tile is forced
   }
   // Group scales (q s rounded per fragment: about 2.5x the conversion work)
   // measured slower than the dequantize-then-dense path at m = 1024,
   // n = 3584, group 128 (44.8 against 41.8 us): forced only.
-  if (a.group > 0 || a.N % 128 != 0 || a.M > 1024) return -1;
+  if (a.group > 0 || a.N % 128 != 0) return -1;
   const int cus = device_cus();
+  if (a.N % 256 == 0) {
+    const long t256 = static_cast<long>((a.M + 255) / 256) * (a.N / 256);
+    const long full = t256 / cus * cus, rest = t256 - full;
+    if (full >= cus && full <= 4L * cus && rest > 0 && 4 * rest <= cus) return kWX;
+  }
+  if (a.M > 1024) return -1;
   const long t64 = static_cast<long>((a.M + 63) / 64) * (a.N / 128);
   const long t128 = static_cast<long>((a.M + 127) / 128) * (a.N / 128);
   if (2 * t64 >= cus && t64 <= cus) return kW64;
@@ -580,9 +629,24 @@ hipError_t launch_w8dir(const GemmArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The mixed launch: whole rounds of 256 x 256 tiles when chosen by size,
+// half the large tiles (rounded down to a multiple of 8) when forced.
+template <int ACT, bool GS>
+hipError_t launch_w8dir_mixed(const GemmArgs &a, hipStream_t s) {
+  const W8DirProblem p{a.A, static_cast<const uint8_t *>(a.B), a.S, a.bias, a.bias_dt, a.C,
+                       a.M, a.N, a.K, GS ? a.group : 0};
+  const int tiles_n = a.N / 256, tiles = ((a.M + 255) / 256) * tiles_n;
+  const int cus = device_cus();
+  const int big = dispatch_override().prefill_tile == kWX ? tiles / 2 / 8 * 8 : tiles / cus * cus;
+  hipLaunchKernelGGL((k_w8dir_mixed<ACT, GS>), dim3(big + 4 * (tiles - big)), dim3(512), 0, s, p, tiles_n,
+                     tiles, big);
+  return hipGetLastError();
+}
+
 template <int ACT, bool GS>
 hipError_t run_w8dir(int tile, const GemmArgs &a, hipStream_t s) {
   switch (tile) {
+    case kWX: return launch_w8dir_mixed<ACT, GS>(a, s);
     case kW256: return launch_w8dir<CfgW256, ACT, GS>(a, s);
     case kW256N: return launch_w8dir<CfgW256N, ACT, GS>(a, s);
     case kW128: return launch_w8dir<CfgW128, ACT, GS>(a, s);
