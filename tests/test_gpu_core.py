@@ -207,7 +207,7 @@ def test_w8_grouped_integer_exact(m, n, k, group, path, dtype):
 
 
 @pytest.mark.parametrize("tile", ["D8", "D8N", "D64", "D128", "X", "L", "M", "S", "P256", "P128", "P64",
-                                  "W256", "W256N", "W128", "W64", "WX"])
+                                  "W256", "W256N", "W128", "W64", "WX", "DX"])
 @pytest.mark.parametrize("group", [64, 128])
 def test_prefill_tiles_w8_grouped_integer_exact(tile, group):
     p = si.w8_exact_problem(300, 512, 1024, seed=group, dtype=BF16, bias_dtype=FP16, group=group)
@@ -337,7 +337,7 @@ def test_prefill_tiles_integer_exact(tile, m):
 
 
 @pytest.mark.parametrize("tile", ["X", "L", "M", "S", "P256", "P128", "P64", "W256", "W256N", "W128", "W64",
-                                  "WX"])
+                                  "WX", "DX"])
 def test_prefill_tiles_w8_integer_exact(tile):
     p = si.w8_exact_problem(200, 256, 576, seed=9, dtype=FP16, bias_dtype=FP16)
     Cref = oracle.gemm_w8(p.A, p.codes, p.scale, -1, FP16, p.bias, FP16)
@@ -348,7 +348,7 @@ def test_prefill_tiles_w8_integer_exact(tile):
 
 @pytest.mark.parametrize("m,n,k", [(1, 256, 128), (300, 512, 640), (513, 768, 2048), (256, 256, 384)])
 @pytest.mark.parametrize("dtype", [BF16, FP16])
-@pytest.mark.parametrize("tile", ["D8", "D8N", "D64", "D128", "X", "P256", "P128", "P64"])
+@pytest.mark.parametrize("tile", ["D8", "D8N", "D64", "D128", "X", "P256", "P128", "P64", "DX"])
 @pytest.mark.parametrize("group", [64, 128])
 def test_prefill_dma_tile_integer_exact(tile, group, m, n, k, dtype):
     p = si.w4_exact_problem(m, n, k, group, seed=m + k, dtype=dtype, bias_dtype=FP16)
@@ -359,7 +359,7 @@ def test_prefill_dma_tile_integer_exact(tile, group, m, n, k, dtype):
 
 
 @pytest.mark.parametrize("tile", ["D8", "D8N", "D64", "D128", "X", "P256", "P128", "P64", "W256", "W256N", "W128",
-                                  "W64", "WX"])
+                                  "W64", "WX", "DX"])
 def test_prefill_dma_tile_w8_integer_exact(tile):
     p = si.w8_exact_problem(300, 512, 576, seed=4, dtype=FP16, bias_dtype=FP16)
     Cref = oracle.gemm_w8(p.A, p.codes, p.scale, -1, FP16, p.bias, FP16)
@@ -465,6 +465,46 @@ def test_w8_mixed_tile_equals_fused_tile_bitwise(dtype, m, n, k, group):
     qg.set_override(prefill_tile="WX")
     mixed = _run_w8(p, "prefill")
     assert torch.equal(fused.view(torch.int16), mixed.view(torch.int16))
+
+
+@pytest.mark.parametrize("dtype", [FP16, BF16])
+@pytest.mark.parametrize("m,n,k", [(520, 2048, 1280), (1024, 4096, 512)])
+@pytest.mark.parametrize("form", ["w4g64", "w4pc", "w8g128"])
+def test_fused_mixed_tile_equals_fused_tile_bitwise(dtype, m, n, k, form):
+    # Fused 256 x 256 tiles for the first half of the large tiles, 256 x 128
+    # halves for the rest, one launch: the 256 x 256 tile's bits.  (K holds an
+    # even number of groups, as the direct-load tiles need.)
+    if form == "w8g128":
+        p = si.w8_problem(m, n, k, group=128, tag="dmix", dtype=dtype, bias_dtype=FP16)
+        run = _run_w8
+    else:
+        g = 64 if form == "w4g64" else -1
+        p = si.w4_problem(m, n, k, g, tag="dmix", dtype=dtype, bias_dtype=FP16)
+        run = _run_w4
+    qg.set_override(prefill_tile="D8")
+    fused = run(p, "prefill")
+    qg.set_override(prefill_tile="DX")
+    mixed = run(p, "prefill")
+    assert torch.equal(fused.view(torch.int16), mixed.view(torch.int16))
+
+
+def test_fused_mixed_tile_taken_by_size():
+    # int8 group 128, m = 1024, n = 18944, k = 3584: one round of 256 x 256
+    # tiles plus one of halves; no workspace; the forced form (another split
+    # of the large tiles) gives the same bits; sampled outputs within the fp16
+    # tolerance of the oracle.
+    m, n, k = 1024, 18944, 3584
+    p = si.w8_problem(m, n, k, group=128, tag="dmix-auto", dtype=FP16, bias_dtype=FP16)
+    assert qg.gemm_workspace_size(m, n, k, 128, 8) == 0
+    auto = _run_w8(p, "prefill")
+    qg.set_override(prefill_tile="DX")
+    forced = _run_w8(p, "prefill")
+    assert torch.equal(auto.view(torch.int16), forced.view(torch.int16))
+    C = auto.float().cpu().numpy()
+    rng = np.random.default_rng(m + n)
+    rows, cols = rng.integers(0, m, 96), rng.integers(0, n, 96)
+    ref = oracle.gemm_w8_at(p.A, p.codes, p.scale, rows, cols, 128, FP16, p.bias, FP16)
+    assert np.abs(C[rows, cols] - ref).max() / np.abs(ref).max() <= TOL[FP16]
 
 
 @pytest.mark.parametrize("m,n,tile", [(512, 3584, "W64"), (1024, 3584, "W128"), (128, 18944, "W128"),

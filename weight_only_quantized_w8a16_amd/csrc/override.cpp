@@ -55,7 +55,7 @@ bool parse(const char *spec, Override &o) {
       else return false;
     } else if (k == "prefill_tile") {
       static const char *names[] = {"X", "D8", "D8N", "D64", "D128", "L", "M", "S", "P256", "P128", "P64",
-                                    "W256", "W256N", "W128", "W64", "WX"};
+                                    "W256", "W256N", "W128", "W64", "WX", "DX"};
       int t = -1;
       for (int i = 0; i < static_cast<int>(sizeof(names) / sizeof(names[0])); ++i)
         if (v == names[i]) t = i;

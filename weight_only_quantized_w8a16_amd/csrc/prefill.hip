@@ -250,6 +250,41 @@ __global__ __launch_bounds__(Cfg::NTHR) void k_w8dir(W8DirProblem p, int tiles_n
   w8dir_tile_gemm<Cfg, ACT, GS>(p, tm, tn, L);
 }
 
+// One launch, two fused direct-load tile sizes: the first `big` workgroups
+// (whole rounds of the CUs, a multiple of 8) take the first `big` of the
+// 256 x 256 tiles, the rest each take a 256 x 128 half of the remaining
+// ones, so a last round of large tiles that would leave many CUs idle is cut
+// in two.  The halves' stages and scale windows fit in the large tile's LDS
+// objects; both sizes give the same bits (same k order and arithmetic).
+struct CfgDXBig : DmaCfg<2, 4> {};
+struct CfgDXHalf : DmaCfg<4, 2, 128> {};
+
+template <int ACT, int WBITS, bool GS8, bool PC>
+__global__ __launch_bounds__(512) void k_prefill_dma_mixed(TileProblem p, int tiles_n, int tiles, int big) {
+  using Big = CfgDXBig;
+  using Half = CfgDXHalf;
+  static_assert(Half::STAGE_A <= Big::STAGE_A && Half::STAGE_B <= Big::STAGE_B && Half::SC_WIN <= Big::SC_WIN &&
+                    Half::BN <= Big::BN && Half::NTHR == Big::NTHR && Big::NTHR == 512,
+                "half-tile LDS inside the large tile's");
+  __shared__ __attribute__((aligned(16))) char a0[Big::STAGE_A];
+  __shared__ __attribute__((aligned(16))) char a1[Big::STAGE_A];
+  __shared__ __attribute__((aligned(16))) char b0[Big::STAGE_B];
+  __shared__ __attribute__((aligned(16))) char b1[Big::STAGE_B];
+  __shared__ __attribute__((aligned(16))) char sc[2 * Big::SC_WIN];
+  __shared__ __attribute__((aligned(16))) char ep[2 * Big::BN * 2];
+  const DmaLds L{{a0, a1}, {b0, b1}, sc, ep};
+  const int bid = blockIdx.x;
+  int tm, tn;
+  if (bid < big) {
+    grouped_tile(xcd_id(bid, big), tiles / tiles_n, tiles_n, tm, tn);
+    tile_gemm_dma<Big, ACT, WBITS, kDense, GS8, false, PC>(p, tm, tn, L, 0);
+    return;
+  }
+  const int u = xcd_id(bid - big, gridDim.x - big);
+  grouped_tile(big + u / 2, tiles / tiles_n, tiles_n, tm, tn);
+  tile_gemm_dma<Half, ACT, WBITS, kDense, GS8, false, PC>(p, tm, 2 * tn + (u & 1), L, 0);
+}
+
 // One launch, two tile sizes (int8 codes converted after the LDS read): the
 // first `big` workgroups (whole rounds of the CUs, a multiple of 8) take the
 // first `big` of the 256 x 256 tiles, the rest each take a 128 x 128
@@ -654,11 +689,46 @@ hipError_t run_w8dir(int tile, const GemmArgs &a, hipStream_t s) {
   }
 }
 
+// The mixed fused launch (256 x 256 tiles for whole rounds, 256 x 128
+// halves for the rest): the number of large-tile workgroups, or -1 when not
+// taken.  By size, where its cost in the tile-choice model (a round of large
+// tiles 100, of halves 62) undercuts either tile alone: m = 1024, n = 18944,
+// one round of each against three of halves.  Measured on MI355X against
+// the 256 x 128 tile: int8 group 128, k = 3584: n = 18944 189.7 -> 176.0 us,
+// n = 16640 181.6 -> 173.5; int4 g64, k = 2048: n = 18944 111.5 -> 99.9,
+// n = 16640 105.6 -> 97.3; int4 per channel n = 18944 105.9 -> 97.5; where
+// the model says no (m = 2048, n = 13312) it measured 8 % slower.  Forced:
+// half the large tiles.  Never with forced K slices.
+int dma_mixed_big(const GemmArgs &a) {
+  const auto &o = dispatch_override();
+  const bool forced = o.prefill_tile == kDX;
+  if ((!forced && o.prefill_tile != -1) || o.splitk > 1 || a.N % 256 != 0) return -1;
+  const long t8 = static_cast<long>((a.M + 255) / 256) * (a.N / 256);
+  if (forced) return static_cast<int>(t8 / 2 / 8 * 8);
+  const int cus = device_cus();
+  const long full = t8 / cus * cus, rest = t8 - full;
+  if (full < cus || rest == 0) return -1;
+  const long rounds8 = (t8 + cus - 1) / cus, rounds8n = (2 * t8 + cus - 1) / cus;
+  const long mixed = full / cus * 100 + (2 * rest + cus - 1) / cus * 62;
+  return mixed < std::min(rounds8 * 100, rounds8n * 62) ? static_cast<int>(full) : -1;
+}
+
+template <int ACT, int WBITS, bool GS8, bool PC>
+hipError_t run_dma_mixed(const GemmArgs &a, int big, hipStream_t s) {
+  const TileProblem p = dense_problem(a, Split{});
+  const int tiles_n = a.N / 256, tiles = ((a.M + 255) / 256) * tiles_n;
+  hipLaunchKernelGGL((k_prefill_dma_mixed<ACT, WBITS, GS8, PC>), dim3(big + 2 * (tiles - big)), dim3(512), 0, s,
+                     p, tiles_n, tiles, big);
+  return hipGetLastError();
+}
+
 template <int ACT, int WBITS, bool GS8 = false, bool PC = false>
 hipError_t dispatch(const GemmArgs &a, hipStream_t s) {
   if constexpr (WBITS == 8) {
     if (const int w = choose_w8dir_tile(a); w >= 0) return run_w8dir<ACT, GS8>(w, a, s);
   }
+  if (const int big = dma_mixed_big(a); big >= 0 && dma_ok<WBITS, GS8, PC>(a))
+    return run_dma_mixed<ACT, WBITS, GS8, PC>(a, big, s);
   Plan pl = plan_prefill(a, WBITS, GS8);
   if (is_dense(pl.tile)) {
     if (a.ws && a.ws_bytes >= pl.bytes) return run_dense<ACT, WBITS, GS8>(pl.tile, a, s);

@@ -49,8 +49,9 @@ enum { kPathAuto = 0, kPathDecode = 1, kPathPrefill = 2 };
 // Prefill tiles (prefill.hip), in the order qg_set_override names them.
 // kP256 .. kP64: the dense tiles of the dequantize-then-dense path.
 // kW256 .. kW64: the int8 per-channel tiles that convert codes after the LDS read;
-// kWX: 256 x 256 ones for whole rounds of the CUs, 128 x 128 quarters for the rest.
-enum PrefillTile { kX, kD8, kD8N, kD64, kD128, kL, kM, kS, kP256, kP128, kP64, kW256, kW256N, kW128, kW64, kWX };
+// kWX: 256 x 256 ones for whole rounds of the CUs, 128 x 128 quarters for the rest;
+// kDX: fused 256 x 256 tiles for whole rounds, 256 x 128 halves for the rest.
+enum PrefillTile { kX, kD8, kD8N, kD64, kD128, kL, kM, kS, kP256, kP128, kP64, kW256, kW256N, kW128, kW64, kWX, kDX };
 // W8A8 tiles (w8a8.hip), in the order qg_set_override names them.
 enum W8A8Tile { kT256, kT256N, kT128, kT64 };
 struct Override {
