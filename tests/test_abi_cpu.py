@@ -192,9 +192,15 @@ def test_quantize_validation(kw, status):
 
 def test_workspace_query_and_alignment():
     L = qg.lib()
-    # split-K partials: two fp32 [m, n] slices where the plan splits K
+    # split-K partials: fp32 [m, n] slices where the plan splits K -- two on
+    # the fused 64 x 64 tile (int4 here); int8 per channel at up to 128 rows
+    # with few 64 x 128 code-converting tiles: about one workgroup per CU
+    # (256 CUs assumed without a device), slices of a multiple of 8 steps
+    # (K = 3584: 56 steps; m = 128: 56 tiles, four slices of 16, 16, 16, 8;
+    # m = 64: 28 tiles, seven slices of 8)
     assert L.qgemm_workspace_size(128, 3072, 2048, 64, 4) == 2 * 128 * 3072 * 4
-    assert L.qgemm_workspace_size(128, 3584, 3584, -1, 8) == 2 * 128 * 3584 * 4
+    assert L.qgemm_workspace_size(128, 3584, 3584, -1, 8) == 4 * 128 * 3584 * 4
+    assert L.qgemm_workspace_size(64, 3584, 3584, -1, 8) == 7 * 64 * 3584 * 4
     # dequantize-then-dense: the whole weight in the activation type, n * k * 2
     # bytes, at 512 .. 1024 rows with few 256 x 256 tiles (256 CUs assumed
     # without a device)

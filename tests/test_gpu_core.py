@@ -507,17 +507,37 @@ def test_fused_mixed_tile_taken_by_size():
     assert np.abs(C[rows, cols] - ref).max() / np.abs(ref).max() <= TOL[FP16]
 
 
-@pytest.mark.parametrize("m,n,tile", [(512, 3584, "W64"), (1024, 3584, "W128"), (128, 18944, "W128"),
-                                      (1024, 18944, "WX")])
-def test_w8_code_tile_taken_by_size(m, n, tile):
+@pytest.mark.parametrize("dtype", [FP16, BF16])
+@pytest.mark.parametrize("m", [130, 64])
+@pytest.mark.parametrize("group,nsplit", [(-1, 2), (-1, 3), (-1, 4), (128, 2)])
+def test_w8_code_tile_k_slices_equal_fused_k_slices_bitwise(dtype, m, group, nsplit):
+    # K slices on the code-converting 64 x 128 tile and on the fused 64-row
+    # direct-load tile, sliced alike (K = 2048: 16 or 8 steps a slice): the
+    # same fp32 partials, so the same reduced bits.
+    n, k = 512, 2048
+    p = si.w8_problem(m, n, k, group=group, tag="w8dir-split", dtype=dtype, bias_dtype=FP16)
+    qg.set_override(prefill_tile="D64", splitk=nsplit)
+    fused = _run_w8(p, "prefill")
+    qg.set_override(prefill_tile="W64", splitk=nsplit)
+    direct = _run_w8(p, "prefill")
+    qg.set_override(splitk=None)
+    assert torch.equal(fused.view(torch.int16), direct.view(torch.int16))
+
+
+@pytest.mark.parametrize("m,n,tile,nsplit", [(512, 3584, "W64", 1), (1024, 3584, "W128", 1),
+                                             (128, 18944, "W128", 1), (1024, 18944, "WX", 1),
+                                             (128, 3584, "W64", 4), (64, 3584, "W64", 7)])
+def test_w8_code_tile_taken_by_size(m, n, tile, nsplit):
     # int8 per channel, one round of 64 x 128 or 128 x 128 tiles, or whole
-    # rounds of 256 x 256 tiles with at most a quarter-round left: the automatic
-    # choice is the code-converting tile (no workspace), bit-equal to it forced
-    # (WX forced splits the large tiles differently: same bits); sampled
-    # outputs within the fp16 tolerance of the oracle.
+    # rounds of 256 x 256 tiles with at most a quarter-round left, or (up to
+    # 128 rows, few 64 x 128 tiles) 64 x 128 tiles in K slices: the automatic
+    # choice is the code-converting tile (workspace only for the slices'
+    # partials), bit-equal to it forced (WX forced splits the large tiles
+    # differently: same bits); sampled outputs within the fp16 tolerance of
+    # the oracle.
     k = 3584
     p = si.w8_problem(m, n, k, group=-1, tag="w8dir-auto", dtype=FP16, bias_dtype=FP16)
-    assert qg.gemm_workspace_size(m, n, k, -1, 8) == 0
+    assert qg.gemm_workspace_size(m, n, k, -1, 8) == (0 if nsplit == 1 else nsplit * m * n * 4)
     auto = _run_w8(p, "prefill")
     qg.set_override(prefill_tile=tile)
     forced = _run_w8(p, "prefill")

@@ -233,7 +233,7 @@ __global__ __launch_bounds__(Cfg::NTHR) void k_dense(DenseProblem p, int tiles_n
 }
 
 // int8 codes, converted after the LDS read (GS: group scales).
-template <class Cfg, int ACT, bool GS>
+template <class Cfg, int ACT, bool GS, bool SPLIT = false>
 __global__ __launch_bounds__(Cfg::NTHR) void k_w8dir(W8DirProblem p, int tiles_n) {
   constexpr int SA = Cfg::STAGE_A, SB = Cfg::STAGE_B;
   __shared__ __attribute__((aligned(16))) char a0[SA];
@@ -246,8 +246,17 @@ __global__ __launch_bounds__(Cfg::NTHR) void k_w8dir(W8DirProblem p, int tiles_n
   __shared__ __attribute__((aligned(16))) char b3[Cfg::NS > 3 ? SB : 16];
   const W8DirLds L{{a0, a1, a2, a3}, {b0, b1, b2, b3}};
   int tm, tn;
-  grouped_tile(xcd_linear_id(), gridDim.x / tiles_n, tiles_n, tm, tn);
-  w8dir_tile_gemm<Cfg, ACT, GS>(p, tm, tn, L);
+  if constexpr (SPLIT) {
+    // nsplit copies of the tile grid, slice-major.
+    const int nsplit = (p.K / 64 + p.kseg - 1) / p.kseg;
+    const int per = gridDim.x / nsplit, id = xcd_linear_id();
+    const int slice = id / per;
+    grouped_tile(id - slice * per, per / tiles_n, tiles_n, tm, tn);
+    w8dir_tile_gemm<Cfg, ACT, GS, true>(p, tm, tn, L, slice);
+  } else {
+    grouped_tile(xcd_linear_id(), gridDim.x / tiles_n, tiles_n, tm, tn);
+    w8dir_tile_gemm<Cfg, ACT, GS>(p, tm, tn, L);
+  }
 }
 
 // One launch, two fused direct-load tile sizes: the first `big` workgroups
@@ -607,6 +616,38 @@ hipError_t run_dense(int tile, const GemmArgs &a, hipStream_t s) {
   }
 }
 
+// K slices for the code-converting 64 x 128 tile: 64-k steps per slice, or
+// 0 for none.  Forced by the dispatch override's splitk (64 x 128 and
+// 128 x 128 tiles); by size for one scale per channel when the 64 x 128
+// tiles fill less than half the CUs (up to 128 rows): about one workgroup
+// per CU, slices of at least 8 steps, a multiple of 8 (the fused tiles'
+// slicing, so that both give the same partials).  Measured on MI355X,
+// k = 3584, n = 3584, against the fused 64 x 64 tile in two slices:
+// m = 128 18.1 -> 15.8 us (four slices), m = 64 16.5 -> 13.6, m = 32
+// 16.2 -> 11.3 (seven); with group scales four slices measured 18.7 against
+// 20.7 us at m = 128 but two or seven slower, so those take them only when
+// forced.
+int w8dir_kseg(const GemmArgs &a, int tile) {
+  const int nsteps = a.K / 64;
+  int want = 1;
+  if (const int o = dispatch_override().splitk; o > 0) {
+    want = (tile == kW64 || tile == kW128) ? o : 1;
+  } else if (tile == kW64 && a.group <= 0 && a.M <= 128) {
+    const int cus = device_cus();
+    const long t64 = static_cast<long>((a.M + 63) / 64) * (a.N / 128);
+    if (2 * t64 < cus) want = static_cast<int>(std::min<long>(cus / t64, nsteps / 8));
+  }
+  if (want <= 1) return 0;
+  int kseg = (nsteps + want - 1) / want;
+  kseg = (kseg + 7) / 8 * 8;
+  return (nsteps + kseg - 1) / kseg >= 2 ? kseg : 0;
+}
+size_t w8dir_bytes(const GemmArgs &a, int kseg) {
+  if (kseg <= 0) return 0;
+  const int nsplit = (a.K / 64 + kseg - 1) / kseg;
+  return static_cast<size_t>(nsplit) * a.M * a.N * sizeof(float);
+}
+
 // int8 (channel or group scales), codes converted after the LDS read: the
 // tile, or -1 for the other tiles.  The operands must fit 32-bit buffer
 // offsets.  By size:
@@ -652,14 +693,25 @@ int choose_w8dir_tile(const GemmArgs &a) {
   const long t128 = static_cast<long>((a.M + 127) / 128) * (a.N / 128);
   if (2 * t64 >= cus && t64 <= cus) return kW64;
   if (2 * t128 >= cus && t128 <= cus) return kW128;
+  if (a.M <= 128 && 2 * t64 < cus && w8dir_kseg(a, kW64) > 0) return kW64;   // in K slices
   return -1;
 }
 
+// K slices (kseg > 0, given the workspace): the partials, then the split-K
+// reduction (channel scale and bias applied there).
 template <class Cfg, int ACT, bool GS>
-hipError_t launch_w8dir(const GemmArgs &a, hipStream_t s) {
-  const W8DirProblem p{a.A, static_cast<const uint8_t *>(a.B), a.S, a.bias, a.bias_dt, a.C,
-                       a.M, a.N, a.K, GS ? a.group : 0};
+hipError_t launch_w8dir(const GemmArgs &a, hipStream_t s, int kseg = 0) {
+  W8DirProblem p{a.A, static_cast<const uint8_t *>(a.B), a.S, a.bias, a.bias_dt, a.C,
+                 a.M, a.N, a.K, GS ? a.group : 0, nullptr, 0};
   const int tm = (a.M + Cfg::BM - 1) / Cfg::BM, tn = a.N / Cfg::BN;
+  if (kseg > 0 && a.ws && a.ws_bytes >= w8dir_bytes(a, kseg)) {
+    p.part = static_cast<float *>(a.ws);
+    p.kseg = kseg;
+    const int nsplit = (a.K / 64 + kseg - 1) / kseg;
+    hipLaunchKernelGGL((k_w8dir<Cfg, ACT, GS, true>), dim3(tm * tn * nsplit), dim3(Cfg::NTHR), 0, s, p, tn);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    return reduce_split<ACT, 8, GS>(a, Split{p.part, kseg, nsplit}, s);
+  }
   hipLaunchKernelGGL((k_w8dir<Cfg, ACT, GS>), dim3(tm * tn), dim3(Cfg::NTHR), 0, s, p, tn);
   return hipGetLastError();
 }
@@ -669,7 +721,7 @@ hipError_t launch_w8dir(const GemmArgs &a, hipStream_t s) {
 template <int ACT, bool GS>
 hipError_t launch_w8dir_mixed(const GemmArgs &a, hipStream_t s) {
   const W8DirProblem p{a.A, static_cast<const uint8_t *>(a.B), a.S, a.bias, a.bias_dt, a.C,
-                       a.M, a.N, a.K, GS ? a.group : 0};
+                       a.M, a.N, a.K, GS ? a.group : 0, nullptr, 0};
   const int tiles_n = a.N / 256, tiles = ((a.M + 255) / 256) * tiles_n;
   const int cus = device_cus();
   const int big = dispatch_override().prefill_tile == kWX ? tiles / 2 / 8 * 8 : tiles / cus * cus;
@@ -684,8 +736,8 @@ hipError_t run_w8dir(int tile, const GemmArgs &a, hipStream_t s) {
     case kWX: return launch_w8dir_mixed<ACT, GS>(a, s);
     case kW256: return launch_w8dir<CfgW256, ACT, GS>(a, s);
     case kW256N: return launch_w8dir<CfgW256N, ACT, GS>(a, s);
-    case kW128: return launch_w8dir<CfgW128, ACT, GS>(a, s);
-    default: return launch_w8dir<CfgW64, ACT, GS>(a, s);
+    case kW128: return launch_w8dir<CfgW128, ACT, GS>(a, s, w8dir_kseg(a, kW128));
+    default: return launch_w8dir<CfgW64, ACT, GS>(a, s, w8dir_kseg(a, kW64));
   }
 }
 
@@ -748,7 +800,8 @@ hipError_t dispatch(const GemmArgs &a, hipStream_t s) {
 }  // namespace
 
 size_t prefill_workspace_bytes(const GemmArgs &a, int wbits) {
-  if (wbits == 8 && choose_w8dir_tile(a) >= 0) return 0;
+  if (wbits == 8)
+    if (const int w = choose_w8dir_tile(a); w >= 0) return w8dir_bytes(a, w8dir_kseg(a, w));
   const Plan pl = plan_prefill(a, wbits, wbits == 8 && a.group > 0);
   return (pl.split.nsplit > 1 || is_dense(pl.tile)) ? pl.bytes : 0;
 }

@@ -45,6 +45,8 @@ struct W8DirProblem {
   uint16_t *C;                // [M, N]
   int M, N, K;
   int group;                  // 64 or 128 (group scales), 0 (channel scales)
+  float *part;                // K slices: fp32 partials [nsplit][M][N], else null
+  int kseg;                   // K slices: 64-k steps per slice
 };
 
 template <int BM_, int BN_, int WM_, int WN_, int NS_>
@@ -72,13 +74,17 @@ struct W8DirLds {
 // s_waitcnt with vmcnt(n), lgkmcnt(0), expcnt untouched.
 constexpr int w8dir_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
 
-template <class Cfg, int ACT, bool GS>
+// SPLIT: the tile covers 64-k steps slice * kseg .. + kseg - 1 (fewer in the
+// last slice) and stores its unscaled fp32 sums as that slice's partials.
+template <class Cfg, int ACT, bool GS, bool SPLIT = false>
 __device__ __forceinline__ void w8dir_tile_gemm(const W8DirProblem &p, int tm, int tn,
-                                                const W8DirLds &L) {
+                                                const W8DirLds &L, int slice = 0) {
   constexpr int TM = Cfg::TM, TN = Cfg::TN, NS = Cfg::NS;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
-  const int K = p.K, nsteps = K / 64;
+  const int K = p.K;
+  const int k0 = SPLIT ? slice * p.kseg : 0;                        // first step
+  const int nsteps = SPLIT ? min(K / 64 - k0, p.kseg) : K / 64;     // steps walked
   const int row_lo = tm * Cfg::BM, row_last = min(p.M, row_lo + Cfg::BM) - 1;
   const int col_lo = tn * Cfg::BN;
 
@@ -115,7 +121,7 @@ __device__ __forceinline__ void w8dir_tile_gemm(const W8DirProblem &p, int tm, i
   // number of loads and one wait count fits all.
   auto issue = [&](auto STc, int step) {
     constexpr int ST = decltype(STc)::value;
-    const int s = min(step, nsteps - 1);
+    const int s = k0 + min(step, nsteps - 1);
     char *da = L.a[ST] + wave * Cfg::A_DMA * 1024;
 #pragma unroll
     for (int i = 0; i < Cfg::A_DMA; ++i)
@@ -258,7 +264,24 @@ __device__ __forceinline__ void w8dir_tile_gemm(const W8DirProblem &p, int tm, i
   // Epilogue: value v of acc[i][j] is C[row][col], row = wave tile row +
   // 32 i + lane % 32, col = wave tile column + 32 j + 8 (v / 4) +
   // 4 (lane / 32) + v % 4; C = RNE(acc * channel scale + bias), the fused
-  // tiles' expression.
+  // tiles' expression.  K slices: the sums as they are, 16 bytes a store.
+  if constexpr (SPLIT) {
+    float *P = p.part + static_cast<size_t>(slice) * p.M * p.N;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int r = row_lo + wm * Cfg::WTM + 32 * i + (lane & 31);
+      if (r > row_last) continue;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = col_lo + wn * Cfg::WTN + 32 * j + 8 * q + 4 * khalf;
+          *reinterpret_cast<f32x4 *>(P + static_cast<size_t>(r) * p.N + col) =
+              f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        }
+    }
+    return;
+  }
   float add[TN][4][4], mul[TN][4][4];
 #pragma unroll
   for (int j = 0; j < TN; ++j)
