@@ -217,8 +217,10 @@ qg_status qdequant_w8(const int8_t *B_tiled, const void *scales, void *W_out, in
  *   m is any value >= 0.  Accumulation is fp32; C = RNE(acc + bias).
  *   workspace: optional device scratch, 256-byte aligned.  When it holds at
  *   least qgemm_workspace_size() bytes (> 0 only for problems the prefill
- *   path splits along K -- today the 64 x 64 tile at m <= 128 with k >= 2048
- *   -- or runs dequantize-then-dense) the K slices write fp32 partials
+ *   path splits along K -- today the 64 x 64 tile at m <= 128 with k >= 2048,
+ *   and for int8 with one scale per channel the code-converting 64 x 128
+ *   tile at m <= 128 when its tiles fill less than half the CUs -- or runs
+ *   dequantize-then-dense) the K slices write fp32 partials
  *   [slices, m, n] there and one more launch sums them in slice order, then
  *   scales, adds bias and rounds; or the whole weight is dequantized there
  *   (n x k values in the activation type, vllm-omni cpu_int4.py: the int4

@@ -657,8 +657,9 @@ size_t w8dir_bytes(const GemmArgs &a, int kseg) {
 // against the other tiles' choice: m = 512, n = 3584 33.5 -> 26.0 us
 // (64 x 128); m = 1024, n = 3584 44.4 -> 38.8 us, m = 128, n = 18944
 // 52.8 -> 34.4 us (128 x 128); m = 32 / 64, n = 18944 31.1 / 32.9 -> 22.7 /
-// 25.5 us (64 x 128).  With fewer tiles (no K slices here: m <= 256,
-// n = 3584, 16-21 against 21-30 us) or more than a round of them (m = 256
+// 25.5 us (64 x 128).  With fewer tiles up to 128 rows, the 64 x 128 tile
+// in K slices (below); unsliced, with fewer tiles (m <= 256, n = 3584,
+// 16-21 against 21-30 us) or more than a round of them (m = 256
 // and 512, n = 18944; m >= 2048) the other tiles are faster -- except where
 // whole rounds of 256 x 256 tiles leave at most a quarter-round of them
 // over: then the mixed launch, whose leftover quarters end the last round

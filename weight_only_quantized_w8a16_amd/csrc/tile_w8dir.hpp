@@ -10,7 +10,9 @@
 // direct loads into a register ring).  Against the fused tiles,
 // which convert every code once per workgroup and stage the 16-bit weights
 // in LDS, the weight bytes in LDS halve and the conversion's LDS writes go
-// away, at the price of converting each code once per wave row.
+// away, at the price of converting each code once per wave row.  A tile can
+// also cover one K slice and store its unscaled fp32 sums as partials for
+// the split-K reduction.
 //
 // Per 64-k step a workgroup moves its BM activation rows (128 bytes each)
 // and its BN / 16 code blocks into one of NS LDS stages, NS - 1 steps ahead;
