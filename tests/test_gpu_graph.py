@@ -3,7 +3,8 @@
 The entry points only enqueue kernels on the caller's stream (no allocation,
 no memset, no host synchronization), so a serving loop can capture them.  A
 captured decode step (W4A16 GEMVs and the tied-table lookup), a prefill GEMM
-with split-K partials in a workspace, a W8A8 GEMM and the MoE are replayed
+with split-K partials in a workspace, W8A16 GEMMs (K-sliced and mixed-size
+launches), a W8A8 GEMM and the MoE are replayed
 several times, with eager work and synchronizations in between, and every
 replay must equal the eager result bit for bit (the kernels are
 deterministic: fixed summation orders, split-K slices summed in order)."""
@@ -43,6 +44,20 @@ def test_captured_calls_replay_bit_exact():
     a512 = to_dev(si.activations(512, K, 6), BF16)
     wsd = torch.empty(qg.gemm_workspace_size(512, 3072, K, 64, 4), dtype=torch.uint8, device=dev)
     assert wsd.numel() == 3072 * K * 2
+    # W8A16 (K = 3584): M = 128 on the code-converting tile in K slices (its
+    # partials in a workspace), M = 1024 on the mixed 256 / 128 launch (one
+    # scale per channel) and on the mixed fused 256 x 256 / 256 x 128 launch
+    # (group 128)
+    K8 = 3584
+    c8a, s8a, _ = si.w8_weights(3584, K8, -1, si.seed_of("g-w8a", K8))
+    c8b, s8b, _ = si.w8_weights(18944, K8, -1, si.seed_of("g-w8b", K8))
+    c8c, s8c, _ = si.w8_weights(18944, K8, 128, si.seed_of("g-w8c", K8))
+    b8a, b8b, b8c = (qg.repack_w8(to_dev(c)) for c in (c8a, c8b, c8c))
+    s8a, s8b, s8c = (to_dev(x, FP16) for x in (s8a, s8b, s8c))
+    a8_128 = to_dev(si.activations(128, K8, 8, FP16), FP16)
+    a8_1024 = to_dev(si.activations(1024, K8, 9, FP16), FP16)
+    ws8s = torch.empty(qg.gemm_workspace_size(128, 3584, K8, -1, 8), dtype=torch.uint8, device=dev)
+    assert ws8s.numel() == 4 * 128 * 3584 * 4
     # W8A8
     p8 = si.w8a8_problem(64, 1024, 1024, True, True, tag="g-w8a8")
     A8, B8 = torch.from_numpy(p8.A).to(dev), torch.from_numpy(p8.B).to(dev)
@@ -62,6 +77,9 @@ def test_captured_calls_replay_bit_exact():
         "pre": torch.empty((128, 3072), dtype=torch.bfloat16, device=dev),
         "dense": torch.empty((512, 3072), dtype=torch.bfloat16, device=dev),
         "w8a8": torch.empty((64, 1024), dtype=torch.float16, device=dev),
+        "w8_split": torch.empty((128, 3584), dtype=torch.float16, device=dev),
+        "w8_wx": torch.empty((1024, 18944), dtype=torch.float16, device=dev),
+        "w8_dx": torch.empty((1024, 18944), dtype=torch.float16, device=dev),
     }
     state = {}
 
@@ -71,6 +89,9 @@ def test_captured_calls_replay_bit_exact():
         state["emb"] = qg.embed_w4(ids, w_wide[0], w_wide[1], w_wide[2], 64)
         qg.gemm_w4a16(a128, wp[0], wp[1], wp[2], wp[3], 64, out=outs["pre"], workspace=ws)
         qg.gemm_w4a16(a512, wp[0], wp[1], wp[2], wp[3], 64, out=outs["dense"], workspace=wsd)
+        qg.gemm_w8a16(a8_128, b8a, s8a, None, -1, out=outs["w8_split"], workspace=ws8s)
+        qg.gemm_w8a16(a8_1024, b8b, s8b, None, -1, out=outs["w8_wx"])
+        qg.gemm_w8a16(a8_1024, b8c, s8c, None, 128, out=outs["w8_dx"])
         qg.gemm_w8a8(A8, B8, r8, c8, out=outs["w8a8"], workspace=ws8)
         state["moe"] = qg.moe_grouped(mx, ml, w1, s1, z1, w2, s2, z2, 2, 64, workspace=mws)
 
