@@ -57,11 +57,14 @@ def test_w8a8_integer_sums_bit_exact(tile, m, n, k):
 @pytest.mark.parametrize("m,n,k", [(1, 16, 128), (1, 528, 384), (5, 144, 1024), (16, 8192, 896), (1, 8192, 768),
                                    (9, 3584, 3584), (16, 18944, 1024),
                                    # one tile per workgroup, 17 and 15 chunks over up to 16 waves
-                                   (2, 48, 2176), (3, 32, 1920)])
+                                   (2, 48, 2176), (3, 32, 1920),
+                                   # from 8 rows the weight chunks go through LDS
+                                   (8, 8192, 1280), (12, 64, 384), (8, 48, 2176)])
 def test_w8a8_decode_kernel_bit_exact(m, n, k):
     # m <= 16 runs the streaming decode kernel (one or two 16-channel tiles
-    # per workgroup, waves over 128-k chunks); unit and power-of-two scales
-    # keep the fp32 output exact.
+    # per workgroup, waves over 128- or 256-k chunks; from 8 rows each chunk
+    # staged through the wave's LDS area); unit and power-of-two scales keep
+    # the fp32 output exact.
     p = si.w8a8_problem(m, n, k, False, False, scales=[1.0])
     acc, _ = ref(p)
     if np.abs(acc).max() < 2 ** 24:

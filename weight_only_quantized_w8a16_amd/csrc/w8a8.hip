@@ -359,9 +359,9 @@ __global__ __launch_bounds__(256) void k_w8a8_reduce(W8A8Problem p, int nsplit) 
 // fragment does not matter.  The waves' int32 sums meet in LDS (exact), then
 // one pass scales and stores.
 // ---------------------------------------------------------------------------
-template <int OUT, int NT, int KC>
+template <int OUT, int NT, int KC, bool STAGED>
 __global__ __launch_bounds__(NT == 1 ? 1024 : 512) void k_w8a8_decode(W8A8Problem p) {
-  extern __shared__ int red[];   // [waves][NT][256]
+  extern __shared__ int red[];   // [waves][NT][256], then (STAGED) [waves][NT][KC / 64][1 KiB]
   constexpr int NP = KC / 64;    // pieces per lane per chunk
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
   const int nl = lane & 15, j = lane >> 4;
@@ -372,15 +372,45 @@ __global__ __launch_bounds__(NT == 1 ? 1024 : 512) void k_w8a8_decode(W8A8Proble
   i32x4 acc[NT];
 #pragma unroll
   for (int i = 0; i < NT; ++i) acc[i] = i32x4{0, 0, 0, 0};
+  // STAGED: the weight chunk goes through this wave's LDS area (NT x 16 rows
+  // x KC bytes), loaded as RPI = 1024 / KC rows of KC contiguous bytes per
+  // direct-load instruction (lane l: row l / (KC / 16), bytes
+  // 16 (l % (KC / 16)), landing in lane order), then read back in the matrix
+  // instruction's lane layout; else each load reads 64 bytes of each of 16
+  // rows straight into registers.
+  constexpr int RPI = 1024 / KC, LPR = KC / 16;
+  [[maybe_unused]] char *stage = reinterpret_cast<char *>(red) + nwaves * NT * 256 * 4 + wave * NT * NP * 1024;
+  [[maybe_unused]] const auto rB = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t *>(p.B), 0, static_cast<int>(static_cast<uint32_t>(p.N) * K), 0x00020000);
+  [[maybe_unused]] const uint32_t lrow = lane / LPR, lbyte = 16 * (lane % LPR);
   for (int c = wave; c < nchunks; c += nwaves) {
     const int k0 = c * KC;
     i32x4 w[NT][NP];
+    if constexpr (STAGED) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's reads of the last chunk are done
 #pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      const i32x4 *src = reinterpret_cast<const i32x4 *>(
-          p.B + static_cast<size_t>((nt0 + i) * 16 + nl) * K + k0 + 16 * j);
+      for (int i = 0; i < NT; ++i)
 #pragma unroll
-      for (int t = 0; t < NP; ++t) w[i][t] = src[4 * t];
+        for (int q = 0; q < NP; ++q)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rB, (__attribute__((address_space(3))) void *)(stage + (i * NP + q) * 1024), 16,
+              (static_cast<uint32_t>((nt0 + i) * 16 + q * RPI) + lrow) * static_cast<uint32_t>(K) + k0 + lbyte, 0,
+              0, 0);
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the chunk is in LDS
+#pragma unroll
+      for (int i = 0; i < NT; ++i)
+#pragma unroll
+        for (int t = 0; t < NP; ++t)
+          w[i][t] = *reinterpret_cast<const i32x4 *>(
+              stage + (i * NP + nl / RPI) * 1024 + ((nl % RPI) * LPR + 4 * t + j) * 16);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        const i32x4 *src = reinterpret_cast<const i32x4 *>(
+            p.B + static_cast<size_t>((nt0 + i) * 16 + nl) * K + k0 + 16 * j);
+#pragma unroll
+        for (int t = 0; t < NP; ++t) w[i][t] = src[4 * t];
+      }
     }
     i32x4 a[NP];
 #pragma unroll
@@ -534,6 +564,10 @@ size_t w8a8_workspace_bytes(int m, int n, int k) {
 // one tile per workgroup up to 16 waves share K (half the chunks per wave,
 // each a memory round trip): N = 3584, m = 1 5.9 -> 4.9 us, m = 16
 // 6.3 -> 6.2 us; the two-tile form stays at 8 (16 measured 9-11 % slower).
+// From 8 rows (weights under 2 GiB) the weight chunks go through LDS as
+// whole 256- or 128-byte row pieces: m = 16, n = 18944 19.9 -> 17.6 us,
+// n = 3584 6.2 -> 5.9, bit-equal; at m = 1 no faster (15.9 / 15.8 us at
+// n = 18944, 4.9 -> 5.1 at n = 3584), so fewer rows keep the direct loads.
 template <int OUT>
 hipError_t launch_w8a8_decode(const W8A8Problem &p, hipStream_t s) {
   const int ntiles = p.N >> 4;
@@ -541,11 +575,17 @@ hipError_t launch_w8a8_decode(const W8A8Problem &p, hipStream_t s) {
   const int nchunks = wide ? p.K >> 8 : p.K >> 7;
   const int maxw = wide ? 8 : 16;
   const int waves = nchunks < maxw ? nchunks : maxw;
-  const size_t lds = static_cast<size_t>(waves) * (wide ? 2 : 1) * 256 * sizeof(int);
-  if (wide)
-    hipLaunchKernelGGL((k_w8a8_decode<OUT, 2, 256>), dim3(ntiles / 2), dim3(64 * waves), lds, s, p);
+  const bool staged = p.M >= 8 && uint64_t(p.N) * p.K < (uint64_t(1) << 31);
+  const size_t lds = static_cast<size_t>(waves) * (wide ? 2 : 1) *
+                     (256 * sizeof(int) + (staged ? (wide ? 4 : 2) * 1024 : 0));
+  if (wide && staged)
+    hipLaunchKernelGGL((k_w8a8_decode<OUT, 2, 256, true>), dim3(ntiles / 2), dim3(64 * waves), lds, s, p);
+  else if (wide)
+    hipLaunchKernelGGL((k_w8a8_decode<OUT, 2, 256, false>), dim3(ntiles / 2), dim3(64 * waves), lds, s, p);
+  else if (staged)
+    hipLaunchKernelGGL((k_w8a8_decode<OUT, 1, 128, true>), dim3(ntiles), dim3(64 * waves), lds, s, p);
   else
-    hipLaunchKernelGGL((k_w8a8_decode<OUT, 1, 128>), dim3(ntiles), dim3(64 * waves), lds, s, p);
+    hipLaunchKernelGGL((k_w8a8_decode<OUT, 1, 128, false>), dim3(ntiles), dim3(64 * waves), lds, s, p);
   return hipGetLastError();
 }
 
